@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Benchmark: one gated tile-sparse attention layer on one MI355X.
+
+A step is one pass of the whole device path over one batch of synthetic
+input already resident in HBM:
+    g = bf16(x . W_gate^T)                  (vsa_gate_proj)
+    tile means, coarse scores, top-k,
+    coarse attention                        (vsa_coarse_topk)
+    fine block-sparse attention + g*O_coarse (vsa_sparse_attn_fwd)
+The tile plan is a pure function of the shape and is built once (cached), as
+the method does.
+
+Prints ONE JSON line. `value` is effective TFLOP/s: the kept-pair FLOPs of the
+fine pass (4*D per real query-row x real key-row pair, prefix and kept video
+tiles only) divided by the layer time; `ms_per_step` is ms per layer.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "ms/layer + effective TFLOP/s (% bf16 MFMA peak) for tile-sparse attn at ~100k tok"
+BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (vendor figure)
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E (vendor figure)
+
+
+def effective_fine_flops(plan, keep_idx: np.ndarray, heads: int, head_dim: int) -> float:
+    """4*D * sum over heads and query tiles of rows_i * (real key rows it attends)."""
+    bl = plan.block_len.astype(np.int64)
+    P = plan.P
+    all_rows = int(bl.sum())
+    prefix_rows = int(bl[:P].sum())
+    pairs = heads * prefix_rows * all_rows
+    kept = bl[keep_idx].sum(-1) if keep_idx.size else np.zeros((heads, plan.n_v), np.int64)
+    pairs += int((bl[P:][None, :] * (prefix_rows + kept)).sum())
+    return 4.0 * head_dim * float(pairs)
+
+
+def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops):
+    """The oracle, as it stands, on a bounded sample of this layer, scaled to one layer."""
+    import oracle
+    Qb, Kb, Vb = (workloads.bf16_bits(t) for t in (q, k, v))
+    xb, wb = workloads.bf16_bits(x), workloads.bf16_bits(w)
+    pl = oracle.plan(wl.prefix_segments, wl.grid, wl.tile)
+    scale = wl.head_dim ** -0.5
+    t0 = time.perf_counter()
+    hr = oracle.head(Qb, Kb, Vb, 0, pl, kk, scale)          # pool, scores, top-k, O_coarse
+    t_head = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    vid = rng.choice(np.arange(pl.S)[pl.untile // pl.B >= pl.P], size=64, replace=False)
+    pre = rng.choice(np.arange(pl.S)[pl.untile // pl.B < pl.P], size=min(32, wl.prefix_tokens),
+                     replace=False) if wl.prefix_tokens else np.zeros(0, np.int64)
+    t0 = time.perf_counter()
+    oracle.fine_tokens(Qb, Kb, Vb, 0, pl, hr.keep, kk, scale, vid)
+    t_vid = (time.perf_counter() - t0) / len(vid)
+    t_pre = 0.0
+    if len(pre):
+        t0 = time.perf_counter()
+        oracle.fine_tokens(Qb, Kb, Vb, 0, pl, hr.keep, kk, scale, pre)
+        t_pre = (time.perf_counter() - t0) / len(pre)
+    gt = rng.choice(pl.S, size=16, replace=False)
+    t0 = time.perf_counter()
+    oracle.gate_proj(xb, wb, gt)
+    t_gate = (time.perf_counter() - t0) / len(gt)
+    n_video_tok = pl.S - wl.prefix_tokens
+    layer_s = (wl.heads * (t_head + n_video_tok * t_vid + wl.prefix_tokens * t_pre)
+               + pl.S * t_gate)
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return {
+        "value": fine_flops / layer_s / 1e12,
+        "unit": "TFLOP/s",
+        "ms_per_layer": layer_s * 1e3,
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"head 0 of {wl.heads}: tile means, all coarse scores, top-k and O_coarse "
+                   f"({t_head:.2f} s); fine attention of {len(vid)} video and {len(pre)} prefix "
+                   f"query tokens; gate projection of {len(gt)} tokens; scaled to all heads "
+                   f"and tokens of one layer"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="h3", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the layer shards by head with no exchange; see the design notes)", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    import tile_sparse_video_amd as tsv
+
+    wl = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {wl.name} inputs ({wl.tokens} tokens)", file=sys.stderr, flush=True)
+    q, k, v = workloads.make_qkv(wl)
+    x, w = workloads.make_x(wl), workloads.make_w_gate(wl)
+    qd, kd, vd, xd, wd = (t.to(dev) for t in (q, k, v, x, w))
+    att = tsv.TileSparseAttention(wl.prefix_segments, wl.grid, wl.tile, wl.heads, wl.head_dim,
+                                  sparsity=wl.sparsity, keep_k=wl.keep_k, device=dev)
+    g = torch.empty((wl.tokens, wl.heads * wl.head_dim), dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        tsv.vsa_gate_proj(xd, wd, g, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        att.coarse(qd, kd, vd, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        att.fine(qd, g, out, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    parts = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)]
+                      for i in range(args.steps)])
+    layer_ms = float(evs[0][0].elapsed_time(evs[-1][3])) / args.steps
+    gate_ms, coarse_ms, fine_ms = (float(x) for x in parts.mean(0))
+
+    keep_host = att.keep_idx.cpu().numpy()
+    fine_flops = effective_fine_flops(att.plan, keep_host, wl.heads, wl.head_dim)
+    tflops = fine_flops / (layer_ms * 1e-3) / 1e12
+    fine_tflops = fine_flops / (fine_ms * 1e-3) / 1e12
+    frac_pairs = tsv.vsa_tile_pair_fraction(att.plan.info, att.k)
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(layer_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: {wl.note}",
+            "heads": wl.heads, "head_dim": wl.head_dim, "hidden": wl.hidden,
+            "tokens": wl.tokens, "prefix_segments": list(wl.prefix_segments),
+            "grid": list(wl.grid), "tile": list(wl.tile), "keep_k": att.k,
+            "parallelism": "single GPU",
+        },
+        "ms_per_layer": round(layer_ms, 4),
+        "pct_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
+        "breakdown_ms": {"gate_proj": round(gate_ms, 4), "coarse_topk": round(coarse_ms, 4),
+                         "sparse_attn_fwd": round(fine_ms, 4)},
+        "ms_per_layer_attention_only": round(coarse_ms + fine_ms, 4),
+        "tile_pair_fraction": round(frac_pairs, 4),
+        "effective_fine_tflop": round(fine_flops / 1e12, 3),
+        "wall_s": round(wall, 3),
+        "roofline": {
+            "kernel": "fine_attn_kernel (vsa_sparse_attn_fwd)",
+            "bound": "mfma",
+            "achieved": round(fine_tflops, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(fine_tflops / BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, x, w, att.plan, att.k, fine_flops)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

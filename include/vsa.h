@@ -1,0 +1,234 @@
+/*
+ * vsa.h -- C ABI of libvsa: gated, tile-sparse video attention for one
+ * video-DiT layer on AMD Instinct MI355X (gfx950).
+ *
+ * The method (web pages cited by title and section):
+ *   [SnackOnAI] "ComfyUI-Ref2VA-VSA proves a sparse attention gate can be
+ *               transplanted ..." -- "The Architecture, Unpacked", "The Code,
+ *               Annotated" (snippets one and two), "It In Action".
+ *   [News]      "Ref2VA VSA: Sparse Attention Node for H3 Reference-to-Video"
+ *               -- "The two-tier attention patch".
+ *   [Veda]      "Veda Sparse Attention" news item -- "ComfyUI node" inputs.
+ *
+ * Video tokens are regrouped into 3D spatio-temporal tiles behind a prefix of
+ * segment-pure text / reference tiles. A coarse pass mean-pools Q, K and V per
+ * tile, scores video tiles against each other and keeps, per head and video
+ * query tile, the top-k video key tiles; prefix key tiles are always kept and
+ * prefix query tiles attend densely. A fine pass runs block-sparse softmax
+ * attention over the kept tiles, and the output is
+ *     out = O_fine + g (elementwise) O_coarse[tile of the token],
+ * where g = x . W_gate^T is a bias-free linear gate projection of the layer
+ * input and O_coarse is tile-level attention over the pooled Q, K, V.
+ *
+ * Conventions for every function:
+ *  - Returns VSA_OK (0) or a negative status; vsa_last_error() then holds a
+ *    thread-local message. All arguments are checked before any GPU work is
+ *    enqueued, so a failed call enqueues nothing. There is no fallback path.
+ *  - "host" pointers are CPU memory; "device" pointers are HIP device memory
+ *    on the current device. The caller owns every buffer and the stream; the
+ *    library allocates no device memory and keeps no pointer after returning.
+ *  - GPU functions only enqueue work on `stream` (a hipStream_t; NULL = the
+ *    null stream). Results are valid once the stream has completed.
+ *  - Tensors are bf16 (raw 16-bit patterns) unless stated. Natural token
+ *    order = prefix segments in order, then the video flattened t-major, then
+ *    h, then w. [S][H][D] means token-major, then head, then head_dim.
+ *  - Supported on device: head_dim in {64, 128}; tile rows B in {64, 128}.
+ */
+#ifndef VSA_H
+#define VSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ status -- */
+#define VSA_OK 0
+#define VSA_ERR_ARG (-1)          /* null pointer, bad size, k out of range, NaN, ...  */
+#define VSA_ERR_UNSUPPORTED (-2)  /* head_dim / tile rows / device not supported        */
+#define VSA_ERR_PLAN (-3)         /* plan arrays inconsistent or untile map not injective */
+#define VSA_ERR_DEVICE (-4)       /* a HIP runtime or launch error                      */
+
+/* Short description of a status code (static string). */
+const char *vsa_status_string(int status);
+/* Detail of the last failing call on this thread ("" if none). */
+const char *vsa_last_error(void);
+
+/* ------------------------------------------------------------- plan -- */
+typedef struct vsa_plan_info {
+    int32_t grid[3];         /* video latent grid (T, H, W)                       */
+    int32_t tile[3];         /* tile shape (t, h, w)                              */
+    int32_t tile_rows;       /* B = tile[0] * tile[1] * tile[2]                   */
+    int32_t n_prefix_tiles;  /* P: tiles [0, P) hold the prefix segments          */
+    int32_t n_video_tiles;   /* n_v: tiles [P, n_t) hold the video                */
+    int32_t n_tiles;         /* n_t = P + n_v                                     */
+    int64_t rows_real;       /* S: number of tokens                               */
+    int64_t rows_padded;     /* S_pad = n_t * B                                   */
+    int64_t prefix_rows;     /* tokens in the prefix segments                     */
+} vsa_plan_info;
+
+/*
+ * vsa_plan_tiles -- the tile plan ("geometry"), computed on the host.
+ * [SnackOnAI] "The Code, Annotated", snippet one; "The Architecture,
+ * Unpacked" (segment-pure prefix tiles); [News] "The two-tier attention
+ * patch", item 1.
+ *
+ * Each prefix segment (text, reference image, reference audio, ...) starts
+ * a new tile and fills tiles of B rows; its last tile may be short. The video
+ * (grid T x H x W, flattened t-major) is cut into tiles of tile_t x tile_h x
+ * tile_w, enumerated t-major then h then w, with partial tiles at the grid
+ * edges. Inside a tile, real tokens take rows 0.. in (dt, dy, dx) order and
+ * padding rows come last.
+ *
+ * prefix_seg_lens: host [n_prefix_segs] token counts (>= 0; zero adds no
+ *   tile; may be NULL if n_prefix_segs == 0).
+ * info: out, always filled on success.
+ * untile_index: out host int32 [S]: padded row of each token, or NULL.
+ * row_src: out host int32 [S_pad]: token of each padded row, -1 = padding, or NULL.
+ * block_len: out host int32 [n_t]: real rows per tile, or NULL.
+ * Pass all three arrays as NULL to query sizes first.
+ * Errors: VSA_ERR_ARG (non-positive grid/tile, negative segment, S_pad >= 2^31).
+ */
+int vsa_plan_tiles(const int64_t *prefix_seg_lens, int32_t n_prefix_segs,
+                   int32_t grid_t, int32_t grid_h, int32_t grid_w,
+                   int32_t tile_t, int32_t tile_h, int32_t tile_w,
+                   vsa_plan_info *info, int32_t *untile_index, int32_t *row_src,
+                   int32_t *block_len);
+
+/*
+ * vsa_plan_validate -- checks host plan arrays against `info` before they are
+ * trusted: untile is injective and is the inverse of row_src, every tile has
+ * 1..B real rows packed first, block_len sums to S, and no tile mixes two
+ * prefix segments or prefix and video ([SnackOnAI] snippet one: a mis-tiling
+ * must fail loudly, never scramble tokens).
+ * prefix_seg_lens as for vsa_plan_tiles. Returns VSA_OK or VSA_ERR_PLAN.
+ */
+int vsa_plan_validate(const vsa_plan_info *info, const int64_t *prefix_seg_lens,
+                      int32_t n_prefix_segs, const int32_t *untile_index,
+                      const int32_t *row_src, const int32_t *block_len);
+
+/*
+ * vsa_keep_count -- number k of video key tiles kept per video query tile.
+ * [SnackOnAI] snippet two: keep ratio = clamp(1 - sparsity, 0, 1);
+ * [Veda] "ComfyUI node": an integer keeps exactly that many key tiles.
+ * keep_k >= 0: k = keep_k (VSA_ERR_ARG if keep_k > n_v).
+ * keep_k < 0: k = floor(clamp(1 - sparsity, 0, 1) * n_v + 0.5)
+ *             (VSA_ERR_ARG if sparsity is NaN).
+ */
+int vsa_keep_count(const vsa_plan_info *info, double sparsity, int64_t keep_k, int32_t *k_out);
+
+/*
+ * vsa_tile_pair_fraction -- share of the n_t^2 dense tile pairs that the sparse
+ * pass computes: n_v query tiles see P + k key tiles, P prefix query tiles see
+ * all n_t ([SnackOnAI] "It In Action", step three). Host only.
+ */
+int vsa_tile_pair_fraction(const vsa_plan_info *info, int32_t k, double *fraction);
+
+/* ------------------------------------------------------- workspace -- */
+/*
+ * The workspace (device memory, caller-owned) holds what the coarse pass
+ * produces for the fine pass; it must survive between vsa_coarse_topk and
+ * vsa_sparse_attn_fwd. Byte offsets (each 256-byte aligned):
+ *   k_tiled, v_tiled: bf16 K and V in tile order, [H][n_t][B/64] blocks of
+ *     64 rows, each block stored as (D/16)*2 fragments of 64 lanes x 8 bf16:
+ *       K block, fragment f = kb*(D/16) + c (kb in {0,1}, c < D/16): lane l,
+ *         element e = K[row 32*kb + l%32][d = 16*c + 8*(l/32) + e];
+ *       V block, fragment f = db*4 + c (db < D/32, c < 4): lane l, element e =
+ *         V[row 16*c + (e<4 ? 4*(l/32) + e : 8 + 4*(l/32) + e-4)][d = 32*db + l%32].
+ *     Padding rows are zero.
+ *   q_mean, k_mean, v_mean: fp32 [H][n_t][D] tile means over real rows.
+ *   scores: fp32 [H][n_v][n_v] coarse scores of video query tile i (row) vs
+ *     video key tile j (column).
+ */
+typedef struct vsa_ws_layout {
+    size_t k_tiled, v_tiled, q_mean, k_mean, v_mean, scores;
+    size_t total_bytes;
+} vsa_ws_layout;
+
+int vsa_workspace_layout(const vsa_plan_info *info, int32_t heads, int32_t head_dim,
+                         vsa_ws_layout *layout);
+
+/* ------------------------------------------------------ coarse pass -- */
+/*
+ * vsa_coarse_topk -- coarse stage: tile means, coarse scores, top-k video key
+ * tiles, and the coarse attention output. Enqueued on `stream`.
+ *
+ *  1. Tile means ("mean-pooled Q/K", plus V for the coarse output) over the
+ *     real rows of every tile: a sequential fp32 sum over rows in ascending
+ *     row order from +0, then one fp32 division by block_len. K and V are
+ *     also written in tile order to the workspace for the fine pass.
+ *  2. Coarse score of video key tile j for video query tile i: the unscaled
+ *     dot product of their mean Q and K, as a chain of fp32 fused
+ *     multiply-adds over ascending d from +0.
+ *  3. Top-k ([News] "The two-tier attention patch", item 2: only video key
+ *     tiles are pruned): per head and video query tile, the k video key tiles
+ *     with the largest score; equal scores keep the lower tile index; -0 and
+ *     +0 are equal. keep_idx[h][i][0..k) holds them as ascending global tile
+ *     ids (P + j). Scores must be finite.
+ *  4. O_coarse[h][i] = sum_j softmax_j(scale * qmean_i . kmean_j) vmean_j over
+ *     all n_t key tiles, for every tile i (prefix and video).
+ *
+ * info: host plan (as filled by vsa_plan_tiles).
+ * row_src_dev, block_len_dev: device copies of the plan arrays.
+ * heads (H), head_dim (D in {64,128}).
+ * sparsity / keep_k: as vsa_keep_count. scale <= 0 means D^-1/2.
+ * q, k, v: device bf16 [S][H][D].
+ * workspace: device, >= vsa_workspace_layout().total_bytes, 256-byte aligned.
+ * keep_idx_dev: out device int32 [H][n_v][k] (may be NULL when k == 0).
+ * o_coarse_dev: out device fp32 [H][n_t][D].
+ * Errors: VSA_ERR_ARG, VSA_ERR_UNSUPPORTED, VSA_ERR_DEVICE.
+ */
+int vsa_coarse_topk(const vsa_plan_info *info, const int32_t *row_src_dev,
+                    const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                    double sparsity, int64_t keep_k, float scale,
+                    const void *q, const void *k, const void *v,
+                    void *workspace, size_t workspace_bytes,
+                    int32_t *keep_idx_dev, float *o_coarse_dev, void *stream);
+
+/* -------------------------------------------------------- fine pass -- */
+/*
+ * vsa_sparse_attn_fwd -- fine block-sparse attention plus the gated coarse
+ * term, written in natural token order. Enqueued on `stream`.
+ * [SnackOnAI] snippet two: prefix key tiles are always kept (sink blocks
+ * [0, P)); prefix query tiles attend to every tile (sink queries [0, P));
+ * block_len keeps padding rows out of the softmax; scale = D^-1/2.
+ *
+ * For each head h and real token t in tile i:
+ *   keys(i)  = real rows of all tiles            if i < P,
+ *            = real rows of tiles [0, P) and keep_idx[h][i-P][0..k)  otherwise;
+ *   O_fine   = sum_u softmax_u(scale * q_t . k_u) v_u   (bf16 inputs, fp32 accumulation);
+ *   out[t][h][:] = bf16_rne(O_fine + g[t][h][:] * o_coarse[h][i][:]).
+ *
+ * workspace: as filled by vsa_coarse_topk for the same plan, heads, head_dim
+ *   and K/V (only k_tiled / v_tiled are read).
+ * k: keep count used by vsa_coarse_topk; keep_idx_dev: its output.
+ * q: device bf16 [S][H][D]. gate: device bf16 [S][H*D] (g, natural order).
+ * out: device bf16 [S][H][D]; only real tokens are written.
+ * Errors: VSA_ERR_ARG (also: empty key set, i.e. P == 0 and k == 0),
+ * VSA_ERR_UNSUPPORTED, VSA_ERR_DEVICE.
+ */
+int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row_src_dev,
+                        const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                        int32_t k, float scale, const void *q,
+                        const void *workspace, size_t workspace_bytes,
+                        const int32_t *keep_idx_dev, const float *o_coarse_dev,
+                        const void *gate, void *out, void *stream);
+
+/* -------------------------------------------------- gate projection -- */
+/*
+ * vsa_gate_proj -- g = bf16_rne(x . W_gate^T), the bias-free gate projection
+ * ([SnackOnAI] snippets two and three: to_gate_compress is an nn.Linear
+ * without bias, weight [heads*head_dim][hidden]). bf16 inputs, fp32 accumulation.
+ * x: device bf16 [rows][hidden]; w_gate: device bf16 [out_features][hidden];
+ * g: out device bf16 [rows][out_features]. hidden and out_features must be
+ * multiples of 64. Errors: VSA_ERR_ARG, VSA_ERR_UNSUPPORTED, VSA_ERR_DEVICE.
+ */
+int vsa_gate_proj(const void *x, const void *w_gate, int64_t rows, int32_t hidden,
+                  int32_t out_features, void *g, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VSA_H */

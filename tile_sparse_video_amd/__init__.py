@@ -1,0 +1,327 @@
+"""Gated, tile-sparse video attention for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libvsa.so`` (hand-written HIP kernels behind the
+C ABI in ``include/vsa.h``). Functions carry the C names; this module only
+marshals arguments: every step of the computation runs in the library's
+kernels. PyTorch supplies device memory and streams.
+
+There is no fallback: if ``libvsa.so`` is missing, importing this package
+raises. Build it with ``python tile_sparse_video_amd/build.py`` (or
+``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvsa.so")
+
+VSA_OK = 0
+VSA_ERR_ARG = -1
+VSA_ERR_UNSUPPORTED = -2
+VSA_ERR_PLAN = -3
+VSA_ERR_DEVICE = -4
+
+EXPORTED = (
+    "vsa_status_string", "vsa_last_error", "vsa_plan_tiles", "vsa_plan_validate",
+    "vsa_keep_count", "vsa_tile_pair_fraction", "vsa_workspace_layout", "vsa_coarse_topk",
+    "vsa_sparse_attn_fwd", "vsa_gate_proj",
+)
+
+
+class VsaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {detail} (status {status})")
+        self.status = status
+
+
+class vsa_plan_info(ctypes.Structure):
+    _fields_ = [
+        ("grid", ctypes.c_int32 * 3), ("tile", ctypes.c_int32 * 3), ("tile_rows", ctypes.c_int32),
+        ("n_prefix_tiles", ctypes.c_int32), ("n_video_tiles", ctypes.c_int32),
+        ("n_tiles", ctypes.c_int32), ("rows_real", ctypes.c_int64),
+        ("rows_padded", ctypes.c_int64), ("prefix_rows", ctypes.c_int64),
+    ]
+
+
+class vsa_ws_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("k_tiled", "v_tiled", "q_mean", "k_mean", "v_mean", "scores", "total_bytes")]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run tile_sparse_video_amd/build.py "
+                          "(the HIP library is required: there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32, F64, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                 ctypes.c_double, ctypes.c_size_t)
+    info_p = ctypes.POINTER(vsa_plan_info)
+    sig = {
+        "vsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "vsa_last_error": ([], ctypes.c_char_p),
+        "vsa_plan_tiles": ([P, I32, I32, I32, I32, I32, I32, I32, info_p, P, P, P], ctypes.c_int),
+        "vsa_plan_validate": ([info_p, P, I32, P, P, P], ctypes.c_int),
+        "vsa_keep_count": ([info_p, F64, I64, ctypes.POINTER(I32)], ctypes.c_int),
+        "vsa_tile_pair_fraction": ([info_p, I32, ctypes.POINTER(F64)], ctypes.c_int),
+        "vsa_workspace_layout": ([info_p, I32, I32, ctypes.POINTER(vsa_ws_layout)], ctypes.c_int),
+        "vsa_coarse_topk": ([info_p, P, P, I32, I32, F64, I64, F32, P, P, P, P, SZ, P, P, P],
+                            ctypes.c_int),
+        "vsa_sparse_attn_fwd": ([info_p, P, P, I32, I32, I32, F32, P, P, SZ, P, P, P, P, P],
+                                ctypes.c_int),
+        "vsa_gate_proj": ([P, P, I64, I32, I32, P, P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int, where: str) -> None:
+    if status != VSA_OK:
+        raise VsaError(status, where, _lib.vsa_last_error().decode() or
+                       _lib.vsa_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+# ------------------------------------------------------------------ plan --
+
+@dataclass
+class Plan:
+    """Host plan (vsa_plan_tiles) plus the arguments it was built from."""
+    info: vsa_plan_info
+    prefix_segments: tuple
+    untile: np.ndarray      # int32 [S]
+    row_src: np.ndarray     # int32 [S_pad], -1 = padding
+    block_len: np.ndarray   # int32 [n_t]
+
+    @property
+    def P(self) -> int:
+        return self.info.n_prefix_tiles
+
+    @property
+    def n_v(self) -> int:
+        return self.info.n_video_tiles
+
+    @property
+    def n_t(self) -> int:
+        return self.info.n_tiles
+
+    @property
+    def B(self) -> int:
+        return self.info.tile_rows
+
+    @property
+    def S(self) -> int:
+        return self.info.rows_real
+
+    @property
+    def S_pad(self) -> int:
+        return self.info.rows_padded
+
+
+def _segs(prefix_segments: Sequence[int]) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(list(prefix_segments), dtype=np.int64).reshape(-1))
+
+
+def vsa_plan_tiles(prefix_segments: Sequence[int], grid: Sequence[int], tile: Sequence[int]) -> Plan:
+    segs = _segs(prefix_segments)
+    info = vsa_plan_info()
+    seg_p = segs.ctypes.data if segs.size else None
+    _check(_lib.vsa_plan_tiles(seg_p, segs.size, *map(int, grid), *map(int, tile),
+                               ctypes.byref(info), None, None, None), "vsa_plan_tiles")
+    untile = np.empty(info.rows_real, dtype=np.int32)
+    row_src = np.empty(info.rows_padded, dtype=np.int32)
+    block_len = np.empty(info.n_tiles, dtype=np.int32)
+    _check(_lib.vsa_plan_tiles(seg_p, segs.size, *map(int, grid), *map(int, tile),
+                               ctypes.byref(info), untile.ctypes.data, row_src.ctypes.data,
+                               block_len.ctypes.data), "vsa_plan_tiles")
+    return Plan(info, tuple(int(s) for s in segs), untile, row_src, block_len)
+
+
+def vsa_plan_validate(plan: Plan, untile=None, row_src=None, block_len=None) -> None:
+    segs = _segs(plan.prefix_segments)
+    u = np.ascontiguousarray(plan.untile if untile is None else untile, dtype=np.int32)
+    r = np.ascontiguousarray(plan.row_src if row_src is None else row_src, dtype=np.int32)
+    b = np.ascontiguousarray(plan.block_len if block_len is None else block_len, dtype=np.int32)
+    _check(_lib.vsa_plan_validate(ctypes.byref(plan.info), segs.ctypes.data if segs.size else None,
+                                  segs.size, u.ctypes.data, r.ctypes.data, b.ctypes.data),
+           "vsa_plan_validate")
+
+
+def vsa_keep_count(info: vsa_plan_info, sparsity: Optional[float] = None,
+                   keep_k: Optional[int] = None) -> int:
+    k = ctypes.c_int32(0)
+    _check(_lib.vsa_keep_count(ctypes.byref(info), float("nan") if sparsity is None else float(sparsity),
+                               -1 if keep_k is None else int(keep_k), ctypes.byref(k)),
+           "vsa_keep_count")
+    return int(k.value)
+
+
+def vsa_tile_pair_fraction(info: vsa_plan_info, k: int) -> float:
+    f = ctypes.c_double(0)
+    _check(_lib.vsa_tile_pair_fraction(ctypes.byref(info), int(k), ctypes.byref(f)),
+           "vsa_tile_pair_fraction")
+    return float(f.value)
+
+
+def vsa_workspace_layout(info: vsa_plan_info, heads: int, head_dim: int) -> vsa_ws_layout:
+    lay = vsa_ws_layout()
+    _check(_lib.vsa_workspace_layout(ctypes.byref(info), int(heads), int(head_dim), ctypes.byref(lay)),
+           "vsa_workspace_layout")
+    return lay
+
+
+# ------------------------------------------------------------ GPU calls --
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def vsa_coarse_topk(info: vsa_plan_info, row_src_dev: torch.Tensor, block_len_dev: torch.Tensor,
+                    heads: int, head_dim: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    workspace: torch.Tensor, keep_idx: Optional[torch.Tensor], o_coarse: torch.Tensor,
+                    sparsity: Optional[float] = None, keep_k: Optional[int] = None,
+                    scale: float = 0.0, stream=None) -> None:
+    S = info.rows_real
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, (S, heads, head_dim))
+    _need(row_src_dev, "row_src", torch.int32, (info.rows_padded,))
+    _need(block_len_dev, "block_len", torch.int32, (info.n_tiles,))
+    _need(workspace, "workspace", torch.uint8)
+    _need(o_coarse, "o_coarse", torch.float32, (heads, info.n_tiles, head_dim))
+    if keep_idx is not None:
+        _need(keep_idx, "keep_idx", torch.int32)
+    _check(_lib.vsa_coarse_topk(ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev), heads,
+                                head_dim, float("nan") if sparsity is None else float(sparsity),
+                                -1 if keep_k is None else int(keep_k), float(scale), _ptr(q),
+                                _ptr(k), _ptr(v), _ptr(workspace), workspace.numel(),
+                                _ptr(keep_idx), _ptr(o_coarse), _stream(stream)),
+           "vsa_coarse_topk")
+
+
+def vsa_sparse_attn_fwd(info: vsa_plan_info, row_src_dev: torch.Tensor, block_len_dev: torch.Tensor,
+                        heads: int, head_dim: int, k: int, q: torch.Tensor, workspace: torch.Tensor,
+                        keep_idx: Optional[torch.Tensor], o_coarse: torch.Tensor, gate: torch.Tensor,
+                        out: torch.Tensor, scale: float = 0.0, stream=None) -> None:
+    S = info.rows_real
+    _need(q, "q", torch.bfloat16, (S, heads, head_dim))
+    _need(gate, "gate", torch.bfloat16)
+    if gate.numel() != S * heads * head_dim:
+        raise ValueError("gate must hold [S][heads*head_dim] values")
+    _need(out, "out", torch.bfloat16, (S, heads, head_dim))
+    _need(row_src_dev, "row_src", torch.int32, (info.rows_padded,))
+    _need(block_len_dev, "block_len", torch.int32, (info.n_tiles,))
+    _need(workspace, "workspace", torch.uint8)
+    _need(o_coarse, "o_coarse", torch.float32, (heads, info.n_tiles, head_dim))
+    if keep_idx is not None:
+        _need(keep_idx, "keep_idx", torch.int32, (heads, info.n_video_tiles, k))
+    _check(_lib.vsa_sparse_attn_fwd(ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev), heads,
+                                    head_dim, int(k), float(scale), _ptr(q), _ptr(workspace),
+                                    workspace.numel(), _ptr(keep_idx), _ptr(o_coarse), _ptr(gate),
+                                    _ptr(out), _stream(stream)),
+           "vsa_sparse_attn_fwd")
+
+
+def vsa_gate_proj(x: torch.Tensor, w_gate: torch.Tensor, g: torch.Tensor, stream=None) -> None:
+    _need(x, "x", torch.bfloat16)
+    _need(w_gate, "w_gate", torch.bfloat16)
+    _need(g, "g", torch.bfloat16)
+    rows, hidden = x.shape
+    out_f = w_gate.shape[0]
+    if w_gate.shape[1] != hidden or tuple(g.shape) != (rows, out_f):
+        raise ValueError("shapes: x [rows][hidden], w_gate [out][hidden], g [rows][out]")
+    _check(_lib.vsa_gate_proj(_ptr(x), _ptr(w_gate), rows, hidden, out_f, _ptr(g), _stream(stream)),
+           "vsa_gate_proj")
+
+
+# ---------------------------------------------------------- convenience --
+
+_PLAN_CACHE: dict = {}
+
+
+def cached_plan(prefix_segments, grid, tile) -> Plan:
+    """The plan is a pure function of the shape: build and validate it once per shape."""
+    key = (tuple(int(s) for s in prefix_segments), tuple(int(g) for g in grid), tuple(int(t) for t in tile))
+    pl = _PLAN_CACHE.get(key)
+    if pl is None:
+        pl = vsa_plan_tiles(*key)
+        vsa_plan_validate(pl)
+        _PLAN_CACHE[key] = pl
+    return pl
+
+
+class TileSparseAttention:
+    """One layer's gated tile-sparse attention with its device-side state.
+
+    Holds the cached plan (copied to the device once), the workspace, and the
+    keep-index / coarse-output buffers, so each call only enqueues kernels."""
+
+    def __init__(self, prefix_segments, grid, tile, heads: int, head_dim: int,
+                 sparsity: Optional[float] = None, keep_k: Optional[int] = None,
+                 scale: float = 0.0, device="cuda"):
+        self.plan = cached_plan(prefix_segments, grid, tile)
+        info = self.plan.info
+        self.heads, self.head_dim, self.scale = int(heads), int(head_dim), float(scale)
+        self.sparsity, self.keep_k = sparsity, keep_k
+        self.k = vsa_keep_count(info, sparsity, keep_k)
+        self.layout = vsa_workspace_layout(info, heads, head_dim)
+        dev = torch.device(device)
+        self.row_src = torch.from_numpy(self.plan.row_src).to(dev)
+        self.block_len = torch.from_numpy(self.plan.block_len).to(dev)
+        self.workspace = torch.empty(self.layout.total_bytes, dtype=torch.uint8, device=dev)
+        self.keep_idx = torch.empty((heads, info.n_video_tiles, self.k), dtype=torch.int32, device=dev)
+        self.o_coarse = torch.empty((heads, info.n_tiles, head_dim), dtype=torch.float32, device=dev)
+
+    def coarse(self, q, k, v, stream=None) -> None:
+        vsa_coarse_topk(self.plan.info, self.row_src, self.block_len, self.heads, self.head_dim,
+                        q, k, v, self.workspace, self.keep_idx if self.k > 0 else None,
+                        self.o_coarse, sparsity=self.sparsity, keep_k=self.keep_k,
+                        scale=self.scale, stream=stream)
+
+    def fine(self, q, gate, out, stream=None) -> None:
+        vsa_sparse_attn_fwd(self.plan.info, self.row_src, self.block_len, self.heads,
+                            self.head_dim, self.k, q, self.workspace,
+                            self.keep_idx if self.k > 0 else None, self.o_coarse, gate, out,
+                            scale=self.scale, stream=stream)
+
+    def __call__(self, q, k, v, gate, out=None, stream=None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty_like(q)
+        self.coarse(q, k, v, stream)
+        self.fine(q, gate, out, stream)
+        return out
+
+    def workspace_view(self, name: str, dtype, shape) -> torch.Tensor:
+        """A typed view of one workspace region (tests read means and scores)."""
+        off = getattr(self.layout, name)
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        return self.workspace[off:off + n].view(dtype).view(*shape)

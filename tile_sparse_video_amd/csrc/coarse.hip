@@ -1,0 +1,471 @@
+// Coarse stage of gated, tile-sparse video attention on gfx950:
+//   gather_pool  -- tile means of Q, K, V (canonical fp32 order) and K/V in tile
+//                   order, fragment layout, for the fine pass (HBM-bound);
+//   video_scores -- coarse score of every (video query tile, video key tile)
+//                   pair as an fp32 fused-multiply-add chain (VALU);
+//   coarse_attn  -- tile-level softmax attention over the pooled Q, K, V (VALU);
+//   topk         -- per (head, video query tile) top-k by radix select, lowest
+//                   index first on ties, ascending output (one wavefront per row).
+//
+// Method: SnackOnAI analysis of ComfyUI-Ref2VA-VSA ("The Code, Annotated",
+// snippet two: block_len masks padding; "References": coarse tile selection
+// from pooled Q/K as in the VSA paper) and the Ref2VA VSA news item ("The
+// two-tier attention patch": only video key tiles are pruned).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "common.h"
+#include "device.h"
+
+namespace vsa {
+
+// ------------------------------------------------------------ device check --
+
+int check_device()
+{
+    static std::mutex mu;
+    static int verdict[64];  // 0 unknown, 1 ok, -1 not gfx950
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(VSA_ERR_DEVICE, "hipGetDevice failed");
+    if (dev < 0 || dev >= 64) return fail(VSA_ERR_DEVICE, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (verdict[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return fail(VSA_ERR_DEVICE, "hipGetDeviceProperties failed");
+        verdict[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        if (verdict[dev] < 0)
+            return fail(VSA_ERR_UNSUPPORTED, "device %d is %s; libvsa is built for gfx950", dev,
+                        prop.gcnArchName);
+    }
+    if (verdict[dev] < 0) return fail(VSA_ERR_UNSUPPORTED, "device %d is not a gfx950", dev);
+    return VSA_OK;
+}
+
+namespace {
+
+// ------------------------------------------------------------- gather/pool --
+//
+// One block per (tile, group of 256/D heads, tensor). The tile's real rows for
+// those heads are staged in LDS (padding rows zero), each thread then owns one
+// (head, d) column and sums it over the real rows in ascending row order from
+// +0 (fp32 adds), dividing once by block_len. For K and V the block also
+// writes the staged tile to the workspace in the MFMA fragment layout the fine
+// pass streams (see vsa.h).
+template <int D, int B>
+__global__ __launch_bounds__(256) void gather_pool_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ row_src, const int32_t *__restrict__ block_len, int H, int n_t,
+    float *__restrict__ qmean, float *__restrict__ kmean, float *__restrict__ vmean,
+    uint16_t *__restrict__ kt, uint16_t *__restrict__ vt)
+{
+    constexpr int HPB = 256 / D;          // heads per block
+    constexpr int ROW = HPB * D + 8;      // LDS row stride in bf16 (pad: 16 bytes)
+    constexpr int CH = HPB * D / 8;       // 16-byte chunks per staged row
+    constexpr int FR = D / 8;             // fragments per 64-row block and head
+    constexpr int SUB = B / 64;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[B * ROW];
+    __shared__ int32_t toks[B];
+
+    const int tile = blockIdx.x;
+    const int h0 = blockIdx.y * HPB;
+    const int which = blockIdx.z;  // 0 = Q, 1 = K, 2 = V
+    const uint16_t *X = which == 0 ? q : (which == 1 ? k : v);
+    const int nh = min(HPB, H - h0);
+    const int n = block_len[tile];
+    const int tid = threadIdx.x;
+
+    if (tid < B) toks[tid] = row_src[size_t(tile) * B + tid];
+    __syncthreads();
+
+    for (int idx = tid; idx < B * CH; idx += 256) {
+        const int r = idx / CH, c = idx % CH;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (r < n && c / (D / 8) < nh)
+            val = *reinterpret_cast<const uint4 *>(X + (size_t(toks[r]) * H + h0) * D + c * 8);
+        *reinterpret_cast<uint4 *>(&lds[r * ROW + c * 8]) = val;
+    }
+    __syncthreads();
+
+    {
+        const int hl = tid / D, d = tid % D;
+        if (hl < nh) {
+            float acc = 0.0f;
+            for (int r = 0; r < n; ++r) acc = acc + bf16_to_f32(lds[r * ROW + tid]);
+            float *mean = which == 0 ? qmean : (which == 1 ? kmean : vmean);
+            mean[(size_t(h0 + hl) * n_t + tile) * D + d] = acc / float(n);
+        }
+    }
+    if (which == 0) return;
+
+    uint16_t *dst = which == 1 ? kt : vt;
+    const int total = nh * SUB * FR * kWave;
+    for (int idx = tid; idx < total; idx += 256) {
+        const int lane = idx % kWave;
+        const int f = (idx / kWave) % FR;
+        const int sub = (idx / (kWave * FR)) % SUB;
+        const int hl = idx / (kWave * FR * SUB);
+        const int half = lane / 32, l32 = lane % 32;
+        uint16_t e8[8];
+        if (which == 1) {
+            // K fragment f = kb*(D/16) + c: row 32kb + l32, d = 16c + 8*half + e.
+            const int kb = f / (D / 16), c = f % (D / 16);
+            const int row = 64 * sub + 32 * kb + l32;
+            const uint16_t *src = &lds[row * ROW + hl * D + 16 * c + 8 * half];
+            *reinterpret_cast<uint4 *>(e8) = *reinterpret_cast<const uint4 *>(src);
+        } else {
+            // V fragment f = db*4 + c: d = 32db + l32, row 16c + {4h..4h+3, 8+4h..8+4h+3}.
+            const int db = f / 4, c = f % 4;
+            const int col = hl * D + 32 * db + l32;
+            const int r0 = 64 * sub + 16 * c + 4 * half;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                e8[e] = lds[(r0 + e) * ROW + col];
+                e8[4 + e] = lds[(r0 + 8 + e) * ROW + col];
+            }
+        }
+        const size_t frag = ((size_t(h0 + hl) * n_t + tile) * SUB + sub) * FR + f;
+        *reinterpret_cast<uint4 *>(dst + frag * 512 + lane * 8) = *reinterpret_cast<uint4 *>(e8);
+    }
+}
+
+// ------------------------------------------------------------ video scores --
+//
+// scores[h][i][j] = fma-chain over ascending d of qmean[P+i][d] * kmean[P+j][d],
+// from +0. A block computes a 64 x 64 tile of (i, j) pairs from LDS copies of
+// the means; each thread owns 4 x 4 pairs and walks d in order, so every pair
+// is the same sequential chain of correctly rounded fused multiply-adds.
+template <int D>
+__global__ __launch_bounds__(256) void video_scores_kernel(const float *__restrict__ qmean,
+                                                          const float *__restrict__ kmean, int n_t,
+                                                          int P, int n_v, float *__restrict__ scores)
+{
+    constexpr int T = 64, ROW = D + 4;
+    __shared__ __attribute__((aligned(16))) float qs[T * ROW];
+    __shared__ __attribute__((aligned(16))) float ks[T * ROW];
+    const int h = blockIdx.z;
+    const int i0 = blockIdx.y * T, j0 = blockIdx.x * T;
+    const int tid = threadIdx.x;
+    const float *qh = qmean + (size_t(h) * n_t + P) * D;
+    const float *kh = kmean + (size_t(h) * n_t + P) * D;
+    for (int idx = tid; idx < T * D / 4; idx += 256) {
+        const int r = idx / (D / 4), c = idx % (D / 4);
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+        if (i0 + r < n_v) a = *reinterpret_cast<const float4 *>(qh + size_t(i0 + r) * D + 4 * c);
+        if (j0 + r < n_v) b = *reinterpret_cast<const float4 *>(kh + size_t(j0 + r) * D + 4 * c);
+        *reinterpret_cast<float4 *>(&qs[r * ROW + 4 * c]) = a;
+        *reinterpret_cast<float4 *>(&ks[r * ROW + 4 * c]) = b;
+    }
+    __syncthreads();
+    const int ty = tid / 16, tx = tid % 16;
+    float acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+    for (int d = 0; d < D; d += 4) {
+        float4 qv[4], kv[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) qv[a] = *reinterpret_cast<const float4 *>(&qs[(4 * ty + a) * ROW + d]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) kv[b] = *reinterpret_cast<const float4 *>(&ks[(tx + 16 * b) * ROW + d]);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                acc[a][b] = __builtin_fmaf(qv[a].x, kv[b].x, acc[a][b]);
+                acc[a][b] = __builtin_fmaf(qv[a].y, kv[b].y, acc[a][b]);
+                acc[a][b] = __builtin_fmaf(qv[a].z, kv[b].z, acc[a][b]);
+                acc[a][b] = __builtin_fmaf(qv[a].w, kv[b].w, acc[a][b]);
+            }
+    }
+    float *out = scores + size_t(h) * n_v * n_v;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int i = i0 + 4 * ty + a;
+        if (i >= n_v) continue;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int j = j0 + tx + 16 * b;
+            if (j < n_v) out[size_t(i) * n_v + j] = acc[a][b];
+        }
+    }
+}
+
+// ------------------------------------------------------- coarse attention --
+//
+// O_coarse[h][i] = sum_j softmax_j(scale * qmean_i . kmean_j) vmean_j over all
+// n_t key tiles, for 32 query tiles per block, streaming 64 key tiles at a time
+// through LDS with an online (running max / running sum) softmax in fp32.
+// A group of 8 consecutive lanes owns one query tile.
+template <int D>
+__global__ __launch_bounds__(256) void coarse_attn_kernel(const float *__restrict__ qmean,
+                                                         const float *__restrict__ kmean,
+                                                         const float *__restrict__ vmean, int n_t,
+                                                         float scale_log2e, float *__restrict__ o_coarse)
+{
+    constexpr int TI = 32, TJ = 64, ROW = D + 4, DPT = D / 8;
+    __shared__ __attribute__((aligned(16))) float qs[TI * ROW];
+    __shared__ __attribute__((aligned(16))) float ks[TJ * ROW];
+    __shared__ __attribute__((aligned(16))) float vs[TJ * ROW];
+    __shared__ float ps[TI * (TJ + 1)];
+    const int h = blockIdx.y, i0 = blockIdx.x * TI, tid = threadIdx.x;
+    const size_t hb = size_t(h) * n_t * D;
+    for (int idx = tid; idx < TI * D / 4; idx += 256) {
+        const int r = idx / (D / 4), c = idx % (D / 4);
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i0 + r < n_t) a = *reinterpret_cast<const float4 *>(qmean + hb + size_t(i0 + r) * D + 4 * c);
+        *reinterpret_cast<float4 *>(&qs[r * ROW + 4 * c]) = a;
+    }
+    const int qi = tid / 8, sub = tid % 8;  // query tile qi; lane-in-group sub
+    float m = -INFINITY, l = 0.0f, o[DPT];
+#pragma unroll
+    for (int c = 0; c < DPT; ++c) o[c] = 0.0f;
+
+    for (int j0 = 0; j0 < n_t; j0 += TJ) {
+        __syncthreads();
+        for (int idx = tid; idx < TJ * D / 4; idx += 256) {
+            const int r = idx / (D / 4), c = idx % (D / 4);
+            float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+            if (j0 + r < n_t) {
+                a = *reinterpret_cast<const float4 *>(kmean + hb + size_t(j0 + r) * D + 4 * c);
+                b = *reinterpret_cast<const float4 *>(vmean + hb + size_t(j0 + r) * D + 4 * c);
+            }
+            *reinterpret_cast<float4 *>(&ks[r * ROW + 4 * c]) = a;
+            *reinterpret_cast<float4 *>(&vs[r * ROW + 4 * c]) = b;
+        }
+        __syncthreads();
+        float z[TJ / 8];
+        float zmax = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < TJ / 8; ++b) {
+            const int j = sub + 8 * b;
+            float acc = 0.0f;
+            for (int d = 0; d < D; d += 4) {
+                const float4 qv = *reinterpret_cast<const float4 *>(&qs[qi * ROW + d]);
+                const float4 kv = *reinterpret_cast<const float4 *>(&ks[j * ROW + d]);
+                acc = __builtin_fmaf(qv.x, kv.x, acc);
+                acc = __builtin_fmaf(qv.y, kv.y, acc);
+                acc = __builtin_fmaf(qv.z, kv.z, acc);
+                acc = __builtin_fmaf(qv.w, kv.w, acc);
+            }
+            z[b] = (j0 + j < n_t) ? acc * scale_log2e : -INFINITY;
+            zmax = fmaxf(zmax, z[b]);
+        }
+        zmax = fmaxf(zmax, __shfl_xor(zmax, 1));
+        zmax = fmaxf(zmax, __shfl_xor(zmax, 2));
+        zmax = fmaxf(zmax, __shfl_xor(zmax, 4));
+        const float m_new = fmaxf(m, zmax);  // finite: every chunk has >= 1 real key tile
+        const float alpha = exp2f(m - m_new);
+        float psum = 0.0f;
+#pragma unroll
+        for (int b = 0; b < TJ / 8; ++b) {
+            const float p = exp2f(z[b] - m_new);
+            psum += p;
+            ps[qi * (TJ + 1) + sub + 8 * b] = p;
+        }
+        psum += __shfl_xor(psum, 1);
+        psum += __shfl_xor(psum, 2);
+        psum += __shfl_xor(psum, 4);
+        l = l * alpha + psum;
+        m = m_new;
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < DPT; ++c) {
+            const int d = sub + 8 * c;
+            float acc = 0.0f;
+            for (int j = 0; j < TJ; ++j) acc = __builtin_fmaf(ps[qi * (TJ + 1) + j], vs[j * ROW + d], acc);
+            o[c] = o[c] * alpha + acc;
+        }
+    }
+    if (i0 + qi < n_t) {
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int c = 0; c < DPT; ++c) o_coarse[hb + size_t(i0 + qi) * D + sub + 8 * c] = o[c] * inv;
+    }
+}
+
+// ------------------------------------------------------------------- top-k --
+//
+// One wavefront per (head, video query tile) row of n_v scores. A four-pass
+// 8-bit radix select over order-preserving keys finds the k-th largest key T
+// and how many keys equal to T are needed; a final pass in ascending index
+// order keeps every key > T and the lowest-index keys == T, writing their
+// global tile ids (P + j) in ascending order. Counts are exact integers, so
+// the result does not depend on the order of the LDS atomics.
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ scores, int n_rows,
+                                                   int n_v, int k, int P, int32_t *__restrict__ keep)
+{
+    __shared__ uint32_t hist[4][256];
+    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int row = blockIdx.x * 4 + w;
+    const bool live = row < n_rows;
+    const float *s = scores + size_t(live ? row : 0) * n_v;
+    int32_t *out = keep + size_t(live ? row : 0) * k;
+
+    if (k == n_v) {  // uniform across the launch
+        if (live)
+            for (int j = lane; j < n_v; j += kWave) out[j] = P + j;
+        return;
+    }
+    uint32_t prefix = 0, mask = 0;
+    int krem = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) hist[w][4 * lane + b] = 0;
+        __syncthreads();
+        if (live)
+            for (int j = lane; j < n_v; j += kWave) {
+                const uint32_t key = score_key(s[j]);
+                if ((key & mask) == prefix) atomicAdd(&hist[w][(key >> shift) & 255u], 1u);
+            }
+        __syncthreads();
+        // Lane L owns digits 255-4L .. 252-4L (descending); an inclusive scan over
+        // lanes gives the number of matching keys at or above each lane's digits.
+        uint32_t c[4], local = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            c[b] = hist[w][255 - 4 * lane - b];
+            local += c[b];
+        }
+        uint32_t incl = local;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const uint32_t t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
+        }
+        const uint32_t excl = incl - local;
+        const bool mine = excl < uint32_t(krem) && uint32_t(krem) <= incl;
+        int digit = 0;
+        uint32_t above = excl;
+        if (mine) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                if (above + c[b] >= uint32_t(krem)) {
+                    digit = 255 - 4 * lane - b;
+                    break;
+                }
+                above += c[b];
+            }
+        }
+        const uint64_t who = __ballot(mine);
+        const int src = who ? __ffsll((unsigned long long)who) - 1 : 0;
+        digit = __shfl(digit, src);
+        above = __shfl(above, src);
+        krem -= int(above);
+        prefix |= uint32_t(digit) << shift;
+        mask |= 255u << shift;
+        __syncthreads();
+    }
+    if (!live || k == 0) return;
+    // prefix is the k-th largest key; keep krem of the keys equal to it.
+    int base = 0, eq_seen = 0;
+    for (int j0 = 0; j0 < n_v; j0 += kWave) {
+        const int j = j0 + lane;
+        const bool valid = j < n_v;
+        const uint32_t key = valid ? score_key(s[j]) : 0u;
+        const bool gt = valid && key > prefix;
+        const bool eq = valid && key == prefix;
+        const uint64_t eq_mask = __ballot(eq);
+        const int eq_before = __popcll(eq_mask & lanes_below(lane));
+        const bool sel = gt || (eq && eq_seen + eq_before < krem);
+        const uint64_t sel_mask = __ballot(sel);
+        const int pos = base + __popcll(sel_mask & lanes_below(lane));
+        if (sel && pos < k) out[pos] = P + j;  // exactly k are selected; the bound is a guard
+        base += __popcll(sel_mask);
+        eq_seen += __popcll(eq_mask);
+    }
+}
+
+template <int D, int B>
+void launch_gather_pool(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *row_src,
+                        const int32_t *block_len, int H, int n_t, float *qm, float *km, float *vm,
+                        uint16_t *kt, uint16_t *vt, hipStream_t st)
+{
+    constexpr int HPB = 256 / D;
+    dim3 grid(n_t, (H + HPB - 1) / HPB, 3);
+    hipLaunchKernelGGL((gather_pool_kernel<D, B>), grid, dim3(256), 0, st, q, k, v, row_src,
+                       block_len, H, n_t, qm, km, vm, kt, vt);
+}
+
+template <int D>
+void launch_coarse(const vsa_plan_info &info, int H, float scale, const float *qm, const float *km,
+                   const float *vm, float *scores, float *o_coarse, hipStream_t st)
+{
+    const int n_t = info.n_tiles, n_v = info.n_video_tiles, P = info.n_prefix_tiles;
+    if (n_v > 0) {
+        dim3 grid((n_v + 63) / 64, (n_v + 63) / 64, H);
+        hipLaunchKernelGGL((video_scores_kernel<D>), grid, dim3(256), 0, st, qm, km, n_t, P, n_v, scores);
+    }
+    dim3 grid2((n_t + 31) / 32, H);
+    hipLaunchKernelGGL((coarse_attn_kernel<D>), grid2, dim3(256), 0, st, qm, km, vm, n_t,
+                       scale * 1.4426950408889634f, o_coarse);
+}
+
+}  // namespace
+}  // namespace vsa
+
+using namespace vsa;
+
+extern "C" int vsa_coarse_topk(const vsa_plan_info *info, const int32_t *row_src_dev,
+                               const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                               double sparsity, int64_t keep_k, float scale, const void *q,
+                               const void *k, const void *v, void *workspace, size_t workspace_bytes,
+                               int32_t *keep_idx_dev, float *o_coarse_dev, void *stream)
+{
+    clear_error();
+    if (int st = check_info(info)) return st;
+    if (heads <= 0) return fail(VSA_ERR_ARG, "heads = %d", heads);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(VSA_ERR_UNSUPPORTED, "head_dim = %d; supported: 64, 128", head_dim);
+    if (!row_src_dev || !block_len_dev || !q || !k || !v || !workspace || !o_coarse_dev)
+        return fail(VSA_ERR_ARG, "null device pointer");
+    if (!(std::isfinite(scale)) ) return fail(VSA_ERR_ARG, "scale is not finite");
+    int32_t kk = 0;
+    if (int st = vsa_keep_count(info, sparsity, keep_k, &kk)) return st;
+    if (kk > 0 && !keep_idx_dev) return fail(VSA_ERR_ARG, "keep_idx is null with k = %d", kk);
+    vsa_ws_layout L;
+    compute_layout(*info, heads, head_dim, &L);
+    if (workspace_bytes < L.total_bytes)
+        return fail(VSA_ERR_ARG, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(VSA_ERR_ARG, "workspace must be 256-byte aligned");
+    if (int st = check_device()) return st;
+
+    const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(float(head_dim));
+    char *ws = static_cast<char *>(workspace);
+    auto *qm = reinterpret_cast<float *>(ws + L.q_mean);
+    auto *km = reinterpret_cast<float *>(ws + L.k_mean);
+    auto *vm = reinterpret_cast<float *>(ws + L.v_mean);
+    auto *kt = reinterpret_cast<uint16_t *>(ws + L.k_tiled);
+    auto *vt = reinterpret_cast<uint16_t *>(ws + L.v_tiled);
+    auto *sc_buf = reinterpret_cast<float *>(ws + L.scores);
+    auto *qq = static_cast<const uint16_t *>(q);
+    auto *kk_ = static_cast<const uint16_t *>(k);
+    auto *vv = static_cast<const uint16_t *>(v);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int n_t = info->n_tiles, B = info->tile_rows;
+
+    (void)hipGetLastError();
+    if (head_dim == 128) {
+        if (B == 64) launch_gather_pool<128, 64>(qq, kk_, vv, row_src_dev, block_len_dev, heads, n_t, qm, km, vm, kt, vt, st);
+        else launch_gather_pool<128, 128>(qq, kk_, vv, row_src_dev, block_len_dev, heads, n_t, qm, km, vm, kt, vt, st);
+        launch_coarse<128>(*info, heads, sc, qm, km, vm, sc_buf, o_coarse_dev, st);
+    } else {
+        if (B == 64) launch_gather_pool<64, 64>(qq, kk_, vv, row_src_dev, block_len_dev, heads, n_t, qm, km, vm, kt, vt, st);
+        else launch_gather_pool<64, 128>(qq, kk_, vv, row_src_dev, block_len_dev, heads, n_t, qm, km, vm, kt, vt, st);
+        launch_coarse<64>(*info, heads, sc, qm, km, vm, sc_buf, o_coarse_dev, st);
+    }
+    const int n_v = info->n_video_tiles;
+    if (n_v > 0 && kk > 0) {
+        const int rows = heads * n_v;
+        hipLaunchKernelGGL(topk_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, sc_buf, rows, n_v,
+                           int(kk), info->n_prefix_tiles, keep_idx_dev);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(VSA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    return VSA_OK;
+}

@@ -1,0 +1,28 @@
+// Internal helpers shared by the libvsa translation units (not part of the ABI).
+#pragma once
+
+#include <cstdarg>
+#include <cstddef>
+#include <cstdint>
+
+#include "vsa.h"
+
+namespace vsa {
+
+// Records a formatted message in the thread-local error slot and returns `status`.
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Re-derives every field of `info` from grid/tile/prefix fields and checks it is
+// consistent and supported on the device path (B in {64,128}, S_pad < 2^31).
+int check_info(const vsa_plan_info *info);
+
+// Fills `layout` for a checked plan (see vsa.h for the meaning of each region).
+void compute_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_ws_layout *layout);
+
+// Checks that the current HIP device is a gfx950; caches the answer per device.
+int check_device();
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace vsa
