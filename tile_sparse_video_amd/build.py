@@ -4,6 +4,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -17,7 +18,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # Bit-exact stages (tile means, fused-multiply-add score chains) rely on no
     # implicit contraction and IEEE fp32 division with denormals kept.
     "-ffp-contract=off",
@@ -27,25 +27,39 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# Per-source extras. The fine kernel rescales its O accumulators with VALU
+# ops; MFMA accumulators in VGPRs avoid bouncing them through AGPRs.
+PER_SOURCE = {
+    "fine.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    out = (res.stdout + res.stderr)
     # hipcc's host pass does not know the packed-fp32 feature; that warning is harmless.
     noise = "is not a recognized feature for this target"
-    msgs = "\n".join(ln for ln in out.splitlines() if noise not in ln)
+    msgs = "\n".join(ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs, file=sys.stderr)
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    objs = [os.path.join(objdir, src + ".o") for src in SOURCES]
+    cmds = [[hipcc, *HIPCC_FLAGS, *PER_SOURCE.get(src, []), *extra_flags, *inc, "-c",
+             os.path.join(CSRC, src), "-o", obj] for src, obj in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(max_workers=len(cmds)) as pool:
+        for f in [pool.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

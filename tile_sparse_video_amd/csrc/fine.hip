@@ -48,15 +48,25 @@ struct FineArgs {
     float scale_log2e;
 };
 
-template <int D>
-struct Frags {
-    bf16x8_t x[2][D / 16];  // [32-row block][16-wide reduction chunk]
-};
-
 __device__ __forceinline__ bf16x8_t load_frag(const uint16_t *p)
 {
     return *reinterpret_cast<const bf16x8_t *>(p);
 }
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((address_space(4))) const int32_t cint32_t;
+
+__device__ __forceinline__ const cint32_t *to_const(const int32_t *p)
+{
+    return reinterpret_cast<const cint32_t *>(reinterpret_cast<uintptr_t>(p));
+}
+constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+// Word 3 of a raw buffer resource (32-bit data format) for gfx9-family parts.
+constexpr int kRsrcWord3 = 0x00020000;
+
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+constexpr float kLazy = 8.0f;  // log2-domain slack before the running max moves
 
 template <int D, int B>
 __global__ __launch_bounds__(64) void fine_attn_kernel(FineArgs a)
@@ -64,7 +74,8 @@ __global__ __launch_bounds__(64) void fine_attn_kernel(FineArgs a)
     constexpr int SUB = B / 64;   // 64-row blocks per tile
     constexpr int NC = D / 16;    // reduction chunks of S = K.Q^T
     constexpr int DB = D / 32;    // 32-row blocks of O^T (over d)
-    constexpr int FR = D / 8;     // fragments per 64-row block
+    constexpr int FR = D / 8;     // 1 KB fragments per 64-row block
+    constexpr int HPU = 2 * SUB;  // 32-key halves per key tile
     const int lane = threadIdx.x;
     const int l32 = lane & 31, half = lane >> 5;
 
@@ -86,12 +97,13 @@ __global__ __launch_bounds__(64) void fine_attn_kernel(FineArgs a)
     }
     const bool dense = tile < a.P;
     const int n_key_tiles = dense ? a.n_t : a.P + a.k;
-    const int32_t *keep_row = dense ? nullptr : a.keep + (size_t(h) * a.n_v + (tile - a.P)) * a.k;
 
     // ---- query fragments (B operand of S^T = K . Q^T): lane -> query 32qb + l32,
-    // reduction slot e of chunk c -> d = 16c + 8*half + e.
+    // reduction slot e of chunk c -> d = 16c + 8*half + e. They are staged once
+    // in LDS (16 KB per wave) and re-read for every S product, which keeps their
+    // 64 VGPRs free for the K/V stream.
+    __shared__ __attribute__((aligned(16))) bf16x8_t q_lds[2][NC][kWave];
     int tok[2];
-    Frags<D> Qf;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         tok[qb] = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
@@ -100,17 +112,52 @@ __global__ __launch_bounds__(64) void fine_attn_kernel(FineArgs a)
         for (int c = 0; c < NC; ++c) {
             bf16x8_t v = load_frag(qrow + 16 * c);
             if (tok[qb] < 0) v = bf16x8_t{};
-            Qf.x[qb][c] = v;
+            q_lds[qb][c][lane] = v;
         }
     }
+    __syncthreads();
 
-    // Kept tiles come from the coarse stage; clamping only guards against a
-    // foreign keep list addressing outside the workspace.
-    auto key_tile = [&](int n) -> int {
-        return (dense || n < a.P) ? n : min(max(keep_row[n - a.P], 0), a.n_t - 1);
+    // ---- key list. Kept tiles come from the coarse stage; clamping only guards
+    // against a foreign keep list. The list and block_len are read-only and read
+    // at wave-uniform addresses, so they go through the constant address space:
+    // scalar loads, whose waits do not drain the in-flight K/V vector loads.
+    const cint32_t *keep_s =
+        to_const(dense ? a.keep : a.keep + (size_t(h) * a.n_v + (tile - a.P)) * a.k);
+    const cint32_t *bl_s = to_const(a.block_len);
+    auto half_tile = [&](int v) -> int {
+        const int n = v / HPU;
+        return (dense || n < a.P) ? n : min(max(keep_s[n - a.P], 0), a.n_t - 1);
     };
-    auto frag_base = [&](const uint16_t *t, int kt_id, int s) -> const uint16_t * {
-        return t + ((size_t(h) * a.n_t + kt_id) * SUB + s) * FR * 512 + lane * 8;
+
+    // ---- K/V stream: one buffer resource per head (SGPRs); a fragment is read
+    // with an SGPR byte offset plus the lane's 16-byte slot, fully coalesced.
+    // Reads outside the head's region return zero instead of faulting.
+    const uint32_t head_bytes = uint32_t(a.n_t) * B * D * 2;
+    const size_t head_elems = size_t(h) * a.n_t * B * D;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(a.kt + head_elems), (short)0, head_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(a.vt + head_elems), (short)0, head_bytes, kRsrcWord3);
+    const int vlane = lane * 16;
+    // Half v covers rows 32*(v % 2) .. +31 of 64-row block (v % HPU) / 2 of its tile.
+    auto half_base = [&](int v) -> uint32_t {
+        const int u = v % HPU;
+        return (uint32_t(half_tile(v)) * SUB + uint32_t(u >> 1)) * FR * 1024u;
+    };
+    auto load_k = [&](int v, bf16x8_t (&Kb)[NC]) {
+        const uint32_t base = half_base(v) + uint32_t(v & 1) * NC * 1024u;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            Kb[c] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rk, vlane, base + c * 1024u, 0));
+    };
+    auto load_v = [&](int v, bf16x8_t (&Vb)[2 * DB]) {
+        const uint32_t base = half_base(v) + uint32_t(v & 1) * 2 * 1024u;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+                Vb[2 * db + cc] = as_bf16x8(
+                    __builtin_amdgcn_raw_buffer_load_b128(rv, vlane, base + (4 * db + cc) * 1024u, 0));
     };
 
     f32x16_t O[DB][2];
@@ -118,118 +165,115 @@ __global__ __launch_bounds__(64) void fine_attn_kernel(FineArgs a)
     for (int db = 0; db < DB; ++db) O[db][0] = O[db][1] = f32x16_t{};
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
     const float c2 = a.scale_log2e;
+    const int n_half = n_key_tiles * HPU;  // always even
 
-    const int n_units = n_key_tiles * SUB;
-    int cur_tile = key_tile(0);
-    Frags<D> Kf;
-    {
-        const uint16_t *kp = frag_base(a.kt, cur_tile, 0);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int c = 0; c < NC; ++c) Kf.x[kb][c] = load_frag(kp + (kb * NC + c) * 512);
-    }
+    // One 32-key half: S = K.Q^T, online softmax, O += V.P; then refill the
+    // buffers with half v + 2 (two halves in flight while this one computes).
+    // The body is straight-line on purpose: halves with no real key are masked
+    // rather than skipped, and the last two refills re-read a valid half, so
+    // the ring registers never merge values from different control paths.
+    auto step = [&](int v, bf16x8_t (&Kb)[NC], bf16x8_t (&Vb)[2 * DB]) {
+        const int real = min(32, bl_s[half_tile(v)] - 32 * (v % HPU));
+        const int next = v + 2 < n_half ? v + 2 : v;
 
-    for (int u = 0; u < n_units; ++u) {
-        const int s = u % SUB;
-        const int real = min(64, a.block_len[cur_tile] - 64 * s);
-
-        // V of this unit: A operand of O^T += V^T . P^T (fragment f = db*4 + c).
-        bf16x8_t Vf[DB][4];
-        {
-            const uint16_t *vp = frag_base(a.vt, cur_tile, s);
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) Vf[db][c] = load_frag(vp + (db * 4 + c) * 512);
-        }
-
-        // S^T[kb][qb]: rows = keys 32kb + 8i + 4*half + j (acc 4i + j), col = query.
-        f32x16_t S[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                f32x16_t acc = f32x16_t{};
-#pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Kf.x[kb][c], Qf.x[qb][c], acc, 0, 0, 0);
-                S[kb][qb] = acc;
-            }
-
-        // Prefetch the next unit's K while the softmax and P.V of this one run.
-        const int nu = u + 1;
-        int next_tile = cur_tile;
-        if (nu < n_units) {
-            next_tile = (nu % SUB == 0) ? key_tile(nu / SUB) : cur_tile;
-            const uint16_t *kp = frag_base(a.kt, next_tile, nu % SUB);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int c = 0; c < NC; ++c) Kf.x[kb][c] = load_frag(kp + (kb * NC + c) * 512);
-        }
-
-        // Mask padding keys, then the online softmax per query column.
-        if (real < 64) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (32 * kb + 8 * i + 4 * half + j >= real) {
-                            S[kb][0][4 * i + j] = -INFINITY;
-                            S[kb][1][4 * i + j] = -INFINITY;
-                        }
-        }
-        bf16x8_t Pf[2][4];
+        // S^T[qb]: rows = keys 8i + 4*half + j of this half (acc 4i + j), col = query.
+        // The Q fragments are re-read from LDS each half: the empty asm makes the
+        // lane index opaque so the reads are not hoisted into 64 live VGPRs.
+        int ql = lane;
+        asm volatile("" : "+v"(ql));
+        f32x16_t S[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            float mx = -INFINITY;
+            f32x16_t acc = f32x16_t{};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int c = 0; c < NC; ++c)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Kb[c], q_lds[qb][c][ql], acc, 0, 0, 0);
+            S[qb] = acc;
+        }
+        load_k(next, Kb);
+        // Padding keys (partial tiles only: a wave-uniform branch) never score.
+        if (__builtin_expect(real < 32, 0)) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[kb][qb][e]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m[qb], mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = exp2f((m[qb] - m_use) * c2);
-            const float moff = -m_use * c2;
-            float rs = 0.f;
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                uint16_t pb[16];
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float p = exp2f(__builtin_fmaf(S[kb][qb][e], c2, moff));
-                    rs += p;
-                    pb[e] = f32_to_bf16(p);
-                }
-                // chunk c = 2kb + half16 holds acc elements 8*half16 .. 8*half16 + 7
-                Pf[qb][2 * kb + 0] = *reinterpret_cast<bf16x8_t *>(&pb[0]);
-                Pf[qb][2 * kb + 1] = *reinterpret_cast<bf16x8_t *>(&pb[8]);
-            }
-            rs += __shfl_xor(rs, 32);
-            l[qb] = l[qb] * alpha + rs;
-            m[qb] = m_new;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) O[db][qb][e] *= alpha;
+                for (int j = 0; j < 4; ++j)
+                    if (8 * i + 4 * half + j >= real) {
+                        S[0][4 * i + j] = -INFINITY;
+                        S[1][4 * i + j] = -INFINITY;
+                    }
         }
 
-        // O^T[db][qb] += V^T[db] . P^T[qb] over the four 16-key chunks.
+        // Online softmax per query column, rescaling lazily: the running max m
+        // only moves (and O, l are rescaled) when some row's new max exceeds it
+        // by more than kLazy in log2 units, so p <= 2^kLazy stays safe in fp32
+        // and bf16 while most halves skip the rescale entirely.
+        float mx[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float t = S[qb][0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) t = fmaxf(t, S[qb][e]);
+            mx[qb] = fmaxf(t, __shfl_xor(t, 32));
+        }
+        const bool grow = (mx[0] * c2 > m[0] * c2 + kLazy) || (mx[1] * c2 > m[1] * c2 + kLazy);
+        if (__ballot(grow) != 0) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const float m_new = fmaxf(m[qb], mx[qb]);
+                const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m[qb] - m_new) * c2);
+                l[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) O[db][qb][e] *= alpha;
+                m[qb] = m_new;
+            }
+        }
+        bf16x8_t Pf[2][2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const float moff = m[qb] == -INFINITY ? 0.f : -m[qb] * c2;
+            float rs = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                u32x4_t w;
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][8 * cc + e], c2, moff));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][8 * cc + e + 1], c2, moff));
+                    const bf16x2_t pp = {(__bf16)p0, (__bf16)p1};
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, rs, false);
+                    w[e / 2] = __builtin_bit_cast(uint32_t, pp);
+                }
+                // 16-key chunk cc of this half = acc elements 8cc .. 8cc + 7
+                Pf[qb][cc] = as_bf16x8(w);
+            }
+            rs += __shfl_xor(rs, 32);
+            l[qb] += rs;
+        }
+
+        // O^T[db][qb] += V^T[db] . P^T[qb] over the half's two 16-key chunks.
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 f32x16_t acc = O[db][qb];
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Vf[db][c], Pf[qb][c], acc, 0, 0, 0);
+                for (int cc = 0; cc < 2; ++cc)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Vb[2 * db + cc], Pf[qb][cc], acc, 0, 0, 0);
                 O[db][qb] = acc;
             }
-        cur_tile = next_tile;
+        load_v(next, Vb);
+    };
+
+    bf16x8_t K0[NC], V0[2 * DB], K1[NC], V1[2 * DB];
+    load_k(0, K0);
+    load_v(0, V0);
+    load_k(1, K1);
+    load_v(1, V1);
+    for (int v = 0; v < n_half; v += 2) {
+        step(v, K0, V0);
+        step(v + 1, K1, V1);
     }
 
     // ---- epilogue: out = bf16(O_fine + g * O_coarse[tile]), natural token order.
@@ -253,9 +297,10 @@ __global__ __launch_bounds__(64) void fine_attn_kernel(FineArgs a)
                 const float r1 = O[db][qb][4 * i + 1] * inv + g1 * ocv.y;
                 const float r2 = O[db][qb][4 * i + 2] * inv + g2 * ocv.z;
                 const float r3 = O[db][qb][4 * i + 3] * inv + g3 * ocv.w;
+                const bf16x2_t w0 = {(__bf16)r0, (__bf16)r1}, w1 = {(__bf16)r2, (__bf16)r3};
                 uint2 w;
-                w.x = uint32_t(f32_to_bf16(r0)) | (uint32_t(f32_to_bf16(r1)) << 16);
-                w.y = uint32_t(f32_to_bf16(r2)) | (uint32_t(f32_to_bf16(r3)) << 16);
+                w.x = *reinterpret_cast<const uint32_t *>(&w0);
+                w.y = *reinterpret_cast<const uint32_t *>(&w1);
                 *reinterpret_cast<uint2 *>(a.out + base + d0) = w;
             }
     }
