@@ -141,9 +141,16 @@ int vsa_tile_pair_fraction(const vsa_plan_info *info, int32_t k, double *fractio
  *   q_mean, k_mean, v_mean: fp32 [H][n_t][D] tile means over real rows.
  *   scores: fp32 [H][n_v][n_v] coarse scores of video query tile i (row) vs
  *     video key tile j (column).
+ *   part_o, part_ml: scratch for the fine pass when it splits each key list
+ *     into C chunks (by tile id modulo C, C = 8 for heads whose K and V exceed
+ *     16 MiB): per chunk, the unnormalised output and the running max / sum
+ *     of every 64 query rows. Zero bytes when C = 1.
+ * The layout depends on the split count, so query it after any
+ * vsa_set_split_chunks call.
  */
 typedef struct vsa_ws_layout {
     size_t k_tiled, v_tiled, q_mean, k_mean, v_mean, scores;
+    size_t part_o, part_ml;  /* fine-pass chunk partials (empty when not split) */
     size_t total_bytes;
 } vsa_ws_layout;
 
@@ -215,6 +222,15 @@ int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row_src_dev,
                         const void *workspace, size_t workspace_bytes,
                         const int32_t *keep_idx_dev, const float *o_coarse_dev,
                         const void *gate, void *out, void *stream);
+
+/*
+ * vsa_set_split_chunks -- tuning override for the fine pass: split every key
+ * list into `chunks` parts (1 = never split; 0 = automatic, the default).
+ * Process-wide; affects vsa_workspace_layout and vsa_sparse_attn_fwd calls
+ * made afterwards. The result does not depend on it beyond fp32 rounding.
+ * Errors: VSA_ERR_ARG if chunks is outside [0, 64].
+ */
+int vsa_set_split_chunks(int32_t chunks);
 
 /* -------------------------------------------------- gate projection -- */
 /*

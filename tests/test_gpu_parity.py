@@ -277,3 +277,21 @@ def test_full_size_sampled(name):
     check_layer(inp, run, heads, toks)
     del run
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------ split fine pass --
+
+@pytest.mark.parametrize("chunks", [3, 8])
+@pytest.mark.parametrize("name", ["ragged64", "ragged128", "d64", "no_prefix", "k0", "one_tile"])
+def test_split_key_lists_every_token(name, chunks):
+    """The fine pass split into chunks (partials + merge) gives the same layer."""
+    import tile_sparse_video_amd as tsv
+    wl = CUSTOM[name]
+    print(f"[gpu] split {name} chunks={chunks}", flush=True)
+    inp = parity.make_inputs(wl)
+    tsv.vsa_set_split_chunks(chunks)
+    try:
+        run = parity.run_gpu(inp)
+        check_layer(inp, run, range(wl.heads), np.arange(wl.tokens))
+    finally:
+        tsv.vsa_set_split_chunks(0)

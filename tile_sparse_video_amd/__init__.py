@@ -31,7 +31,7 @@ VSA_ERR_DEVICE = -4
 EXPORTED = (
     "vsa_status_string", "vsa_last_error", "vsa_plan_tiles", "vsa_plan_validate",
     "vsa_keep_count", "vsa_tile_pair_fraction", "vsa_workspace_layout", "vsa_coarse_topk",
-    "vsa_sparse_attn_fwd", "vsa_gate_proj",
+    "vsa_sparse_attn_fwd", "vsa_gate_proj", "vsa_set_split_chunks",
 )
 
 
@@ -52,7 +52,8 @@ class vsa_plan_info(ctypes.Structure):
 
 class vsa_ws_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("k_tiled", "v_tiled", "q_mean", "k_mean", "v_mean", "scores", "total_bytes")]
+                ("k_tiled", "v_tiled", "q_mean", "k_mean", "v_mean", "scores", "part_o",
+                 "part_ml", "total_bytes")]
 
 
 def _load() -> ctypes.CDLL:
@@ -76,6 +77,7 @@ def _load() -> ctypes.CDLL:
         "vsa_sparse_attn_fwd": ([info_p, P, P, I32, I32, I32, F32, P, P, SZ, P, P, P, P, P],
                                 ctypes.c_int),
         "vsa_gate_proj": ([P, P, I64, I32, I32, P, P], ctypes.c_int),
+        "vsa_set_split_chunks": ([I32], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -261,6 +263,11 @@ def vsa_gate_proj(x: torch.Tensor, w_gate: torch.Tensor, g: torch.Tensor, stream
         raise ValueError("shapes: x [rows][hidden], w_gate [out][hidden], g [rows][out]")
     _check(_lib.vsa_gate_proj(_ptr(x), _ptr(w_gate), rows, hidden, out_f, _ptr(g), _stream(stream)),
            "vsa_gate_proj")
+
+
+def vsa_set_split_chunks(chunks: int) -> None:
+    """Tuning override for the fine pass key-list split (0 = automatic)."""
+    _check(_lib.vsa_set_split_chunks(int(chunks)), "vsa_set_split_chunks")
 
 
 # ---------------------------------------------------------- convenience --

@@ -20,6 +20,9 @@ int check_info(const vsa_plan_info *info);
 // Fills `layout` for a checked plan (see vsa.h for the meaning of each region).
 void compute_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_ws_layout *layout);
 
+// Number of key chunks the fine pass splits each key list into (1 = no split).
+int split_chunks(const vsa_plan_info &info, int head_dim);
+
 // Checks that the current HIP device is a gfx950; caches the answer per device.
 int check_device();
 

@@ -11,27 +11,47 @@
 //
 // Design (CDNA4):
 //  - One wavefront per (head, 64 query rows of a tile). The wave holds the 64
-//    query rows as MFMA B-operand fragments for the whole key list, so the
-//    K/V of a key tile is consumed by exactly one wave and never has to be
-//    shared through LDS: K and V arrive from L2/HBM as fully coalesced 1 KB
-//    fragments (the layout written by the coarse stage) straight into VGPRs.
+//    query rows for its whole key list, so the K/V of a key tile is consumed
+//    by exactly one wave and never has to be shared through LDS: K and V arrive
+//    as fully coalesced 1 KB fragments (the layout the coarse stage writes)
+//    straight into VGPRs through bounds-checked buffer loads.
 //  - S^T = K . Q^T and O^T += V^T . P^T on v_mfma_f32_32x32x16_bf16 with fp32
 //    accumulation. With keys as rows of S^T, each lane owns one query column,
 //    so the running max / sum and the O rescale are per lane (plus one
 //    cross-half exchange), and the S accumulator already has the register
 //    layout of the P^T operand of the second product.
-//  - The next key tile's K is fetched while P.V of the current one runs, and
-//    the current V while S is computed (register double buffering).
-//  - Heavy work first: prefix query tiles (dense over all n_t tiles) are
-//    dispatched before the video query tiles (prefix + k tiles).
+//  - The key list is walked in 32-key halves; K of the next half is fetched
+//    as soon as S is formed and V once P.V is issued. 256 VGPRs per wave give
+//    two waves per SIMD, which cover each other's memory waits.
+//  - With random keep-sets the kernel is bound by the traffic beyond L2, so
+//    for large heads the key list is split into C chunks by tile id modulo C,
+//    and chunk c is dispatched to XCD c (workgroups are spread round-robin
+//    over the 8 XCDs): each XCD's L2 then serves only 1/C of a head's K/V,
+//    swept in ascending order by all its waves. Each chunk writes a partial
+//    (O, running max, running sum); a merge kernel combines the chunks and
+//    applies the gated epilogue. Small heads (C = 1) finish in the epilogue.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 
 #include "common.h"
 #include "device.h"
 
 namespace vsa {
+
+static std::atomic<int> g_split_override{0};
+
+// Number of key chunks for the fine pass: split when the K and V of one head
+// are large enough that L2 reuse across query tiles matters.
+int split_chunks(const vsa_plan_info &info, int head_dim)
+{
+    const int forced = g_split_override.load();
+    if (forced > 0) return forced;
+    const double head_kv = 2.0 * double(info.rows_padded) * head_dim * 2.0;
+    return head_kv >= 16.0 * (1 << 20) ? 8 : 1;
+}
+
 namespace {
 
 struct FineArgs {
@@ -44,32 +64,44 @@ struct FineArgs {
     const float *o_coarse;      // [H][n_t][D]
     const uint16_t *gate;       // [S][H*D]
     uint16_t *out;              // [S][H][D]
-    int H, P, n_v, n_t, k;
+    float *part_o;              // split: [items][C][DB][2][64][16] unnormalised O
+    float *part_ml;             // split: [items][C][2 (m, l)][2][32]
+    int H, P, n_v, n_t, k, chunks;
     float scale_log2e;
 };
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 __device__ __forceinline__ bf16x8_t load_frag(const uint16_t *p)
 {
     return *reinterpret_cast<const bf16x8_t *>(p);
 }
 
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
-typedef __attribute__((address_space(4))) const int32_t cint32_t;
-
-__device__ __forceinline__ const cint32_t *to_const(const int32_t *p)
-{
-    return reinterpret_cast<const cint32_t *>(reinterpret_cast<uintptr_t>(p));
-}
 constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
-// Word 3 of a raw buffer resource (32-bit data format) for gfx9-family parts.
-constexpr int kRsrcWord3 = 0x00020000;
+constexpr float kLazy = 8.0f;   // log2-domain slack before the running max moves
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource word 3, 32-bit data (gfx9 family)
+constexpr int kListCap = 896;   // key-list entries staged in LDS per segment
 
-typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
-constexpr float kLazy = 8.0f;  // log2-domain slack before the running max moves
+// out[t][h][d0..d0+3] = bf16(o * inv + g * oc) for four consecutive d.
+__device__ __forceinline__ void store4(uint16_t *out, const uint16_t *gate, size_t base, int d0,
+                                       float4 oc, float o0, float o1, float o2, float o3, float inv)
+{
+    const uint2 graw = *reinterpret_cast<const uint2 *>(gate + base + d0);
+    const float g0 = __uint_as_float(graw.x << 16), g1 = __uint_as_float(graw.x & 0xffff0000u);
+    const float g2 = __uint_as_float(graw.y << 16), g3 = __uint_as_float(graw.y & 0xffff0000u);
+    const bf16x2_t w0 = {(__bf16)(o0 * inv + g0 * oc.x), (__bf16)(o1 * inv + g1 * oc.y)};
+    const bf16x2_t w1 = {(__bf16)(o2 * inv + g2 * oc.z), (__bf16)(o3 * inv + g3 * oc.w)};
+    uint2 w;
+    w.x = __builtin_bit_cast(uint32_t, w0);
+    w.y = __builtin_bit_cast(uint32_t, w1);
+    *reinterpret_cast<uint2 *>(out + base + d0) = w;
+}
 
-template <int D, int B>
-__global__ __launch_bounds__(64) void fine_attn_kernel(FineArgs a)
+template <int D, int B, bool SPLIT>
+__global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
 {
     constexpr int SUB = B / 64;   // 64-row blocks per tile
     constexpr int NC = D / 16;    // reduction chunks of S = K.Q^T
@@ -79,30 +111,25 @@ __global__ __launch_bounds__(64) void fine_attn_kernel(FineArgs a)
     const int lane = threadIdx.x;
     const int l32 = lane & 31, half = lane >> 5;
 
-    // ---- work item: prefix query tiles first (heavy), then video query tiles.
-    const int item = blockIdx.x;
-    const int prefix_items = a.H * a.P * SUB;
-    int h, tile, qsub;
-    if (item < prefix_items) {
-        h = item / (a.P * SUB);
-        const int r = item % (a.P * SUB);
-        tile = r / SUB;
-        qsub = r % SUB;
-    } else {
-        const int it = item - prefix_items;
-        h = it / (a.n_v * SUB);
-        const int r = it % (a.n_v * SUB);
-        tile = a.P + r / SUB;
-        qsub = r % SUB;
+    // ---- work item. Split: chunk = block % C, so with C = 8 chunk c always runs
+    // on XCD c. Then head-major, so the K/V in flight belong to one or two heads.
+    int rest = blockIdx.x, chunk = 0;
+    if (SPLIT) {
+        chunk = rest % a.chunks;
+        rest /= a.chunks;
     }
+    const int item = rest;  // = (h * n_t + tile) * SUB + qsub
+    const int h = item / (a.n_t * SUB);
+    const int r = item % (a.n_t * SUB);
+    const int tile = r / SUB, qsub = r % SUB;
     const bool dense = tile < a.P;
-    const int n_key_tiles = dense ? a.n_t : a.P + a.k;
+    const int n_list = dense ? a.n_t : a.P + a.k;
 
     // ---- query fragments (B operand of S^T = K . Q^T): lane -> query 32qb + l32,
-    // reduction slot e of chunk c -> d = 16c + 8*half + e. They are staged once
-    // in LDS (16 KB per wave) and re-read for every S product, which keeps their
-    // 64 VGPRs free for the K/V stream.
+    // reduction slot e of chunk c -> d = 16c + 8*half + e. Staged once in LDS
+    // (16 KB per wave) and re-read for every S product.
     __shared__ __attribute__((aligned(16))) bf16x8_t q_lds[2][NC][kWave];
+    __shared__ uint32_t list_lds[kListCap];  // tile | (block_len - 1) << 25
     int tok[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -115,18 +142,34 @@ __global__ __launch_bounds__(64) void fine_attn_kernel(FineArgs a)
             q_lds[qb][c][lane] = v;
         }
     }
-    __syncthreads();
 
-    // ---- key list. Kept tiles come from the coarse stage; clamping only guards
-    // against a foreign keep list. The list and block_len are read-only and read
-    // at wave-uniform addresses, so they go through the constant address space:
-    // scalar loads, whose waits do not drain the in-flight K/V vector loads.
-    const cint32_t *keep_s =
-        to_const(dense ? a.keep : a.keep + (size_t(h) * a.n_v + (tile - a.P)) * a.k);
-    const cint32_t *bl_s = to_const(a.block_len);
-    auto half_tile = [&](int v) -> int {
-        const int n = v / HPU;
-        return (dense || n < a.P) ? n : min(max(keep_s[n - a.P], 0), a.n_t - 1);
+    // ---- key list source: position n -> tile n (prefix, or all tiles for a dense
+    // query tile) or the n-P-th kept tile (clamped: only guards a foreign list).
+    const int32_t *keep_row = dense ? a.keep : a.keep + (size_t(h) * a.n_v + (tile - a.P)) * a.k;
+    auto tile_at = [&](int n) -> int {
+        return (dense || n < a.P) ? n : min(max(keep_row[n - a.P], 0), a.n_t - 1);
+    };
+    // The wave stages the next segment of its key list (tiles of this chunk)
+    // into LDS with block_len packed alongside, 64 list positions at a time.
+    int scan = 0;
+    auto fill = [&]() -> int {
+        int count = 0;
+        while (scan < n_list) {
+            const int n = scan + lane;
+            const int t = n < n_list ? tile_at(n) : -1;
+            const bool match = t >= 0 && (!SPLIT || t % a.chunks == chunk);
+            const uint64_t mask = __ballot(match);
+            const int take = __popcll(mask);
+            if (count + take > kListCap) break;  // next segment
+            if (match) {
+                const int bl = a.block_len[t];
+                list_lds[count + __popcll(mask & lanes_below(lane))] = uint32_t(t) | uint32_t(bl - 1) << 25;
+            }
+            count += take;
+            scan += kWave;
+        }
+        __syncthreads();
+        return count;
     };
 
     // ---- K/V stream: one buffer resource per head (SGPRs); a fragment is read
@@ -139,10 +182,13 @@ __global__ __launch_bounds__(64) void fine_attn_kernel(FineArgs a)
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc((void *)(a.vt + head_elems), (short)0, head_bytes, kRsrcWord3);
     const int vlane = lane * 16;
+    auto entry = [&](int v) -> uint32_t {  // wave-uniform LDS read
+        return __builtin_amdgcn_readfirstlane(list_lds[v / HPU]);
+    };
     // Half v covers rows 32*(v % 2) .. +31 of 64-row block (v % HPU) / 2 of its tile.
     auto half_base = [&](int v) -> uint32_t {
-        const int u = v % HPU;
-        return (uint32_t(half_tile(v)) * SUB + uint32_t(u >> 1)) * FR * 1024u;
+        const uint32_t t = entry(v) & 0x1ffffffu;
+        return (t * SUB + uint32_t((v % HPU) >> 1)) * FR * 1024u;
     };
     auto load_k = [&](int v, bf16x8_t (&Kb)[NC]) {
         const uint32_t base = half_base(v) + uint32_t(v & 1) * NC * 1024u;
@@ -165,16 +211,15 @@ __global__ __launch_bounds__(64) void fine_attn_kernel(FineArgs a)
     for (int db = 0; db < DB; ++db) O[db][0] = O[db][1] = f32x16_t{};
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
     const float c2 = a.scale_log2e;
-    const int n_half = n_key_tiles * HPU;  // always even
 
-    // One 32-key half: S = K.Q^T, online softmax, O += V.P; then refill the
-    // buffers with half v + 2 (two halves in flight while this one computes).
-    // The body is straight-line on purpose: halves with no real key are masked
-    // rather than skipped, and the last two refills re-read a valid half, so
-    // the ring registers never merge values from different control paths.
-    auto step = [&](int v, bf16x8_t (&Kb)[NC], bf16x8_t (&Vb)[2 * DB]) {
-        const int real = min(32, bl_s[half_tile(v)] - 32 * (v % HPU));
-        const int next = v + 2 < n_half ? v + 2 : v;
+    // One 32-key half: S = K.Q^T, online softmax, O += V.P. K of the next half
+    // is fetched as soon as S is formed, V of the next half once P.V has been
+    // issued. The body is straight-line on purpose: halves with no real key are
+    // masked rather than skipped, and the last refill re-reads a valid half, so
+    // the K/V registers never merge values from different control paths.
+    auto step = [&](int v, int n_half, bf16x8_t (&Kb)[NC], bf16x8_t (&Vb)[2 * DB]) {
+        const int real = min(32, int(entry(v) >> 25) + 1 - 32 * (v % HPU));
+        const int next = v + 1 < n_half ? v + 1 : v;
 
         // S^T[qb]: rows = keys 8i + 4*half + j of this half (acc 4i + j), col = query.
         // The Q fragments are re-read from LDS each half: the empty asm makes the
@@ -266,14 +311,42 @@ __global__ __launch_bounds__(64) void fine_attn_kernel(FineArgs a)
         load_v(next, Vb);
     };
 
-    bf16x8_t K0[NC], V0[2 * DB], K1[NC], V1[2 * DB];
-    load_k(0, K0);
-    load_v(0, V0);
-    load_k(1, K1);
-    load_v(1, V1);
-    for (int v = 0; v < n_half; v += 2) {
-        step(v, K0, V0);
-        step(v + 1, K1, V1);
+    bf16x8_t Kb[NC], Vb[2 * DB];
+    while (true) {
+        const int count = fill();
+        if (count > 0) {
+            const int n_half = count * HPU;
+            load_k(0, Kb);
+            load_v(0, Vb);
+            for (int v = 0; v < n_half; ++v) step(v, n_half, Kb, Vb);
+        }
+        if (scan >= n_list) break;
+        __syncthreads();  // every lane has read the list before it is refilled
+    }
+
+    if (SPLIT) {
+        // ---- partial: unnormalised O in register order, plus (m, l) per query.
+        const size_t pidx = size_t(item) * a.chunks + chunk;
+        float *po = a.part_o + pidx * (64 * D);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                float4 *dst = reinterpret_cast<float4 *>(po + ((db * 2 + qb) * 64 + lane) * 16);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    dst[q4] = make_float4(O[db][qb][4 * q4], O[db][qb][4 * q4 + 1], O[db][qb][4 * q4 + 2],
+                                          O[db][qb][4 * q4 + 3]);
+            }
+        if (lane < 32) {
+            float *pml = a.part_ml + pidx * 128;
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                pml[qb * 32 + lane] = m[qb];
+                pml[64 + qb * 32 + lane] = l[qb];
+            }
+        }
+        return;
     }
 
     // ---- epilogue: out = bf16(O_fine + g * O_coarse[tile]), natural token order.
@@ -289,19 +362,82 @@ __global__ __launch_bounds__(64) void fine_attn_kernel(FineArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int d0 = 32 * db + 8 * i + 4 * half;
-                const float4 ocv = *reinterpret_cast<const float4 *>(oc + d0);
-                const uint2 graw = *reinterpret_cast<const uint2 *>(a.gate + base + d0);
-                const float g0 = __uint_as_float(graw.x << 16), g1 = __uint_as_float(graw.x & 0xffff0000u);
-                const float g2 = __uint_as_float(graw.y << 16), g3 = __uint_as_float(graw.y & 0xffff0000u);
-                const float r0 = O[db][qb][4 * i + 0] * inv + g0 * ocv.x;
-                const float r1 = O[db][qb][4 * i + 1] * inv + g1 * ocv.y;
-                const float r2 = O[db][qb][4 * i + 2] * inv + g2 * ocv.z;
-                const float r3 = O[db][qb][4 * i + 3] * inv + g3 * ocv.w;
-                const bf16x2_t w0 = {(__bf16)r0, (__bf16)r1}, w1 = {(__bf16)r2, (__bf16)r3};
-                uint2 w;
-                w.x = *reinterpret_cast<const uint32_t *>(&w0);
-                w.y = *reinterpret_cast<const uint32_t *>(&w1);
-                *reinterpret_cast<uint2 *>(a.out + base + d0) = w;
+                store4(a.out, a.gate, base, d0, *reinterpret_cast<const float4 *>(oc + d0),
+                       O[db][qb][4 * i], O[db][qb][4 * i + 1], O[db][qb][4 * i + 2], O[db][qb][4 * i + 3], inv);
+            }
+    }
+}
+
+// Combines the C chunk partials of one (head, 64 query rows) item:
+// M = max_c m_c, w_c = 2^((m_c - M) scale log2 e), O = sum_c w_c O_c,
+// l = sum_c w_c l_c, then the same gated epilogue as the direct path.
+// One wavefront per item, lanes laid out as in the fine kernel.
+template <int D, int B>
+__global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
+{
+    constexpr int SUB = B / 64, DB = D / 32;
+    const int lane = threadIdx.x % kWave;
+    const int item = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (item >= n_items) return;
+    const int l32 = lane & 31, half = lane >> 5;
+    const int h = item / (a.n_t * SUB);
+    const int r = item % (a.n_t * SUB);
+    const int tile = r / SUB, qsub = r % SUB;
+    const float c2 = a.scale_log2e;
+    const int C = a.chunks;
+    const size_t p0 = size_t(item) * C;
+
+    float M[2] = {-INFINITY, -INFINITY};
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) M[qb] = fmaxf(M[qb], a.part_ml[(p0 + c) * 128 + qb * 32 + l32]);
+    float L[2] = {0.f, 0.f};
+    float O[DB][2][16];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) O[db][qb][e] = 0.f;
+    for (int c = 0; c < C; ++c) {
+        const float *pml = a.part_ml + (p0 + c) * 128;
+        float w[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const float mc = pml[qb * 32 + l32];
+            w[qb] = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mc - M[qb]) * c2);
+            L[qb] += w[qb] * pml[64 + qb * 32 + l32];
+        }
+        const float *po = a.part_o + (p0 + c) * (64 * D);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const float4 *src = reinterpret_cast<const float4 *>(po + ((db * 2 + qb) * 64 + lane) * 16);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const float4 v = src[q4];
+                    O[db][qb][4 * q4 + 0] += w[qb] * v.x;
+                    O[db][qb][4 * q4 + 1] += w[qb] * v.y;
+                    O[db][qb][4 * q4 + 2] += w[qb] * v.z;
+                    O[db][qb][4 * q4 + 3] += w[qb] * v.w;
+                }
+            }
+    }
+    const float *oc = a.o_coarse + (size_t(h) * a.n_t + tile) * D;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int tok = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
+        if (tok < 0) continue;
+        const float inv = 1.0f / L[qb];
+        const size_t base = (size_t(tok) * a.H + h) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = 32 * db + 8 * i + 4 * half;
+                store4(a.out, a.gate, base, d0, *reinterpret_cast<const float4 *>(oc + d0),
+                       O[db][qb][4 * i], O[db][qb][4 * i + 1], O[db][qb][4 * i + 2], O[db][qb][4 * i + 3], inv);
             }
     }
 }
@@ -310,13 +446,26 @@ template <int D, int B>
 void launch_fine(const FineArgs &a, hipStream_t st)
 {
     const int items = a.H * a.n_t * (B / 64);
-    hipLaunchKernelGGL((fine_attn_kernel<D, B>), dim3(items), dim3(64), 0, st, a);
+    if (a.chunks > 1) {
+        hipLaunchKernelGGL((fine_attn_kernel<D, B, true>), dim3(items * a.chunks), dim3(64), 0, st, a);
+        hipLaunchKernelGGL((merge_kernel<D, B>), dim3((items + 3) / 4), dim3(256), 0, st, a, items);
+    } else {
+        hipLaunchKernelGGL((fine_attn_kernel<D, B, false>), dim3(items), dim3(64), 0, st, a);
+    }
 }
 
 }  // namespace
 }  // namespace vsa
 
 using namespace vsa;
+
+extern "C" int vsa_set_split_chunks(int32_t chunks)
+{
+    clear_error();
+    if (chunks < 0 || chunks > 64) return fail(VSA_ERR_ARG, "split chunks %d outside [0, 64]", chunks);
+    g_split_override.store(chunks);
+    return VSA_OK;
+}
 
 extern "C" int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row_src_dev,
                                    const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
@@ -344,9 +493,13 @@ extern "C" int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row
         return fail(VSA_ERR_ARG, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total_bytes);
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
         return fail(VSA_ERR_ARG, "workspace must be 256-byte aligned");
+    const int64_t items = int64_t(heads) * info->n_tiles * (info->tile_rows / 64);
+    const int chunks = split_chunks(*info, head_dim);
+    if (items * chunks >= (int64_t(1) << 31))
+        return fail(VSA_ERR_UNSUPPORTED, "too many work items (%lld)", (long long)(items * chunks));
     if (int st = check_device()) return st;
 
-    const char *ws = static_cast<const char *>(workspace);
+    char *ws = static_cast<char *>(const_cast<void *>(workspace));
     FineArgs a;
     a.q = static_cast<const uint16_t *>(q);
     a.kt = reinterpret_cast<const uint16_t *>(ws + L.k_tiled);
@@ -357,11 +510,14 @@ extern "C" int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row
     a.o_coarse = o_coarse_dev;
     a.gate = static_cast<const uint16_t *>(gate);
     a.out = static_cast<uint16_t *>(out);
+    a.part_o = reinterpret_cast<float *>(ws + L.part_o);
+    a.part_ml = reinterpret_cast<float *>(ws + L.part_ml);
     a.H = heads;
     a.P = info->n_prefix_tiles;
     a.n_v = info->n_video_tiles;
     a.n_t = info->n_tiles;
     a.k = k;
+    a.chunks = chunks;
     const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(float(head_dim));
     a.scale_log2e = sc * 1.4426950408889634f;
     hipStream_t st = static_cast<hipStream_t>(stream);
