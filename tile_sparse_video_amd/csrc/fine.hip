@@ -190,20 +190,18 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
         const uint32_t t = entry(v) & 0x1ffffffu;
         return (t * SUB + uint32_t((v % HPU) >> 1)) * FR * 1024u;
     };
-    auto load_k = [&](int v, bf16x8_t (&Kb)[NC]) {
+    auto load_k = [&](int v, u32x4_t (&Kb)[NC]) {
         const uint32_t base = half_base(v) + uint32_t(v & 1) * NC * 1024u;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-            Kb[c] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rk, vlane, base + c * 1024u, 0));
+        for (int c = 0; c < NC; ++c) Kb[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, vlane, base + c * 1024u, 0);
     };
-    auto load_v = [&](int v, bf16x8_t (&Vb)[2 * DB]) {
+    auto load_v = [&](int v, u32x4_t (&Vb)[2 * DB]) {
         const uint32_t base = half_base(v) + uint32_t(v & 1) * 2 * 1024u;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc)
-                Vb[2 * db + cc] = as_bf16x8(
-                    __builtin_amdgcn_raw_buffer_load_b128(rv, vlane, base + (4 * db + cc) * 1024u, 0));
+                Vb[2 * db + cc] = __builtin_amdgcn_raw_buffer_load_b128(rv, vlane, base + (4 * db + cc) * 1024u, 0);
     };
 
     f32x16_t O[DB][2];
@@ -217,54 +215,47 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
     // issued. The body is straight-line on purpose: halves with no real key are
     // masked rather than skipped, and the last refill re-reads a valid half, so
     // the K/V registers never merge values from different control paths.
-    auto step = [&](int v, int n_half, bf16x8_t (&Kb)[NC], bf16x8_t (&Vb)[2 * DB]) {
+    auto step = [&](int v, int n_half, u32x4_t (&Kb)[NC], u32x4_t (&Vb)[2 * DB]) {
         const int real = min(32, int(entry(v) >> 25) + 1 - 32 * (v % HPU));
         const int next = v + 1 < n_half ? v + 1 : v;
 
-        // S^T[qb]: rows = keys 8i + 4*half + j of this half (acc 4i + j), col = query.
-        // The Q fragments are re-read from LDS each half: the empty asm makes the
-        // lane index opaque so the reads are not hoisted into 64 live VGPRs.
-        int ql = lane;
-        asm volatile("" : "+v"(ql));
-        f32x16_t S[2];
+        // The two 32-query blocks are independent (each lane owns one query of
+        // each), so each block runs S, softmax and P.V on its own: only its S
+        // and P are live, and block 1's products can overlap block 0's softmax.
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            f32x16_t acc = f32x16_t{};
+            // S^T: rows = keys 8i + 4*half + j of this half (acc 4i + j), col = query.
+            // Q fragments come from LDS in one batch; the empty asm makes the lane
+            // index opaque so they are re-read rather than hoisted into VGPRs.
+            int ql = lane;
+            asm volatile("" : "+v"(ql));
+            bf16x8_t Qf[NC];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) Qf[c] = q_lds[qb][c][ql];
+            f32x16_t S = f32x16_t{};
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Kb[c], q_lds[qb][c][ql], acc, 0, 0, 0);
-            S[qb] = acc;
-        }
-        load_k(next, Kb);
-        // Padding keys (partial tiles only: a wave-uniform branch) never score.
-        if (__builtin_expect(real < 32, 0)) {
+                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Kb[c]), Qf[c], S, 0, 0, 0);
+            if (qb == 1) load_k(next, Kb);
+            // Padding keys (partial tiles only: a wave-uniform branch) never score.
+            if (__builtin_expect(real < 32, 0)) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (8 * i + 4 * half + j >= real) {
-                        S[0][4 * i + j] = -INFINITY;
-                        S[1][4 * i + j] = -INFINITY;
-                    }
-        }
+                    for (int j = 0; j < 4; ++j)
+                        if (8 * i + 4 * half + j >= real) S[4 * i + j] = -INFINITY;
+            }
 
-        // Online softmax per query column, rescaling lazily: the running max m
-        // only moves (and O, l are rescaled) when some row's new max exceeds it
-        // by more than kLazy in log2 units, so p <= 2^kLazy stays safe in fp32
-        // and bf16 while most halves skip the rescale entirely.
-        float mx[2];
+            // Online softmax per query column, rescaling lazily: the running max
+            // m only moves (and O, l are rescaled) when some row's new max exceeds
+            // it by more than kLazy in log2 units, so p <= 2^kLazy stays safe in
+            // fp32 and bf16 while most halves skip the rescale entirely.
+            float mx = S[0];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float t = S[qb][0];
-#pragma unroll
-            for (int e = 1; e < 16; ++e) t = fmaxf(t, S[qb][e]);
-            mx[qb] = fmaxf(t, __shfl_xor(t, 32));
-        }
-        const bool grow = (mx[0] * c2 > m[0] * c2 + kLazy) || (mx[1] * c2 > m[1] * c2 + kLazy);
-        if (__ballot(grow) != 0) {
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const float m_new = fmaxf(m[qb], mx[qb]);
+            for (int e = 1; e < 16; ++e) mx = fmaxf(mx, S[e]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (__ballot(mx * c2 > m[qb] * c2 + kLazy) != 0) {
+                const float m_new = fmaxf(m[qb], mx);
                 const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m[qb] - m_new) * c2);
                 l[qb] *= alpha;
 #pragma unroll
@@ -273,45 +264,40 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
                     for (int e = 0; e < 16; ++e) O[db][qb][e] *= alpha;
                 m[qb] = m_new;
             }
-        }
-        bf16x8_t Pf[2][2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
             const float moff = m[qb] == -INFINITY ? 0.f : -m[qb] * c2;
             float rs = 0.f;
+            bf16x8_t Pf[2];
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 u32x4_t w;
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][8 * cc + e], c2, moff));
-                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][8 * cc + e + 1], c2, moff));
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * cc + e], c2, moff));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * cc + e + 1], c2, moff));
                     const bf16x2_t pp = {(__bf16)p0, (__bf16)p1};
                     rs = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, rs, false);
                     w[e / 2] = __builtin_bit_cast(uint32_t, pp);
                 }
                 // 16-key chunk cc of this half = acc elements 8cc .. 8cc + 7
-                Pf[qb][cc] = as_bf16x8(w);
+                Pf[cc] = as_bf16x8(w);
             }
             rs += __shfl_xor(rs, 32);
             l[qb] += rs;
-        }
 
-        // O^T[db][qb] += V^T[db] . P^T[qb] over the half's two 16-key chunks.
+            // O^T[db][qb] += V^T[db] . P^T[qb] over the half's two 16-key chunks.
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
+            for (int db = 0; db < DB; ++db) {
                 f32x16_t acc = O[db][qb];
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc)
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Vb[2 * db + cc], Pf[qb][cc], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Vb[2 * db + cc]), Pf[cc], acc, 0, 0, 0);
                 O[db][qb] = acc;
             }
+        }
         load_v(next, Vb);
     };
 
-    bf16x8_t Kb[NC], Vb[2 * DB];
+    u32x4_t Kb[NC], Vb[2 * DB];
     while (true) {
         const int count = fill();
         if (count > 0) {
