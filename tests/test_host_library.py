@@ -1,0 +1,221 @@
+"""libvsa host side, on the CPU: exports, plan parity with the oracle, plan
+validation, keep-count, workspace layout, and argument checks of the GPU entry
+points (which must fail before any device work, so no GPU is touched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import tile_sparse_video_amd as tsv
+import workloads
+from tests.test_oracle_plan import _random_geometries
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "vsa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 11
+    lib = ctypes.CDLL(tsv.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in vsa.h but not exported"
+    assert set(tsv.EXPORTED) == set(names)
+
+
+@pytest.mark.parametrize("segs,grid,tile", _random_geometries(30, seed=3))
+def test_plan_matches_oracle(orc, segs, grid, tile):
+    pl = tsv.vsa_plan_tiles(segs, grid, tile)
+    o = orc.plan(segs, grid, tile)
+    assert (pl.P, pl.n_v, pl.n_t, pl.B, pl.S, pl.S_pad) == (o.P, o.n_v, o.n_t, o.B, o.S, o.S_pad)
+    assert np.array_equal(pl.untile, o.untile)
+    assert np.array_equal(pl.row_src, o.row_src)
+    assert np.array_equal(pl.block_len, o.block_len)
+    tsv.vsa_plan_validate(pl)
+
+
+@pytest.mark.parametrize("name", sorted(workloads.WORKLOADS))
+def test_workload_plans_and_keep_counts(orc, name):
+    wl = workloads.WORKLOADS[name]
+    pl = tsv.cached_plan(wl.prefix_segments, wl.grid, wl.tile)
+    o = orc.plan(wl.prefix_segments, wl.grid, wl.tile)
+    assert np.array_equal(pl.row_src, o.row_src) and np.array_equal(pl.block_len, o.block_len)
+    assert tsv.vsa_keep_count(pl.info, wl.sparsity, wl.keep_k) == \
+        orc.keep_count(o.n_v, wl.sparsity, wl.keep_k)
+    k = orc.keep_count(o.n_v, wl.sparsity, wl.keep_k)
+    assert tsv.vsa_tile_pair_fraction(pl.info, k) == pytest.approx(
+        orc.tile_pair_fraction(o.P, o.n_v, k), rel=1e-15)
+
+
+def test_keep_count_matches_oracle_grid(orc):
+    pl = tsv.vsa_plan_tiles([5], (4, 8, 12), (4, 4, 4))
+    for s in np.linspace(-0.5, 1.5, 41):
+        assert tsv.vsa_keep_count(pl.info, float(s)) == orc.keep_count(pl.n_v, float(s))
+    for k in range(pl.n_v + 1):
+        assert tsv.vsa_keep_count(pl.info, keep_k=k) == k
+    for bad in (dict(keep_k=pl.n_v + 1), dict(sparsity=float("nan"))):
+        with pytest.raises(tsv.VsaError) as e:
+            tsv.vsa_keep_count(pl.info, **bad)
+        assert e.value.status == tsv.VSA_ERR_ARG
+
+
+def _expect_plan_error(pl, **arrays):
+    with pytest.raises(tsv.VsaError) as e:
+        tsv.vsa_plan_validate(pl, **arrays)
+    assert e.value.status == tsv.VSA_ERR_PLAN
+
+
+def test_validate_rejects_corrupted_plans():
+    pl = tsv.vsa_plan_tiles([30, 70], (5, 6, 9), (4, 4, 4))
+    # non-injective untile map
+    u = pl.untile.copy()
+    u[3] = u[4]
+    _expect_plan_error(pl, untile=u)
+    # row_src not the inverse of untile
+    r = pl.row_src.copy()
+    a, b = pl.untile[0], pl.untile[1]
+    r[a], r[b] = r[b], r[a]
+    _expect_plan_error(pl, row_src=r)
+    # a tile whose real rows are not packed first (swap a real row with padding)
+    t = int(np.nonzero(pl.block_len < pl.B)[0][0])
+    r = pl.row_src.copy()
+    u = pl.untile.copy()
+    last = t * pl.B + pl.block_len[t] - 1
+    tok = r[last]
+    r[last], r[t * pl.B + pl.B - 1] = -1, tok
+    u[tok] = t * pl.B + pl.B - 1
+    _expect_plan_error(pl, row_src=r, untile=u)
+    # a tile mixing the prefix and the video (swap one prefix and one video token)
+    r = pl.row_src.copy()
+    u = pl.untile.copy()
+    pa, va = pl.untile[0], pl.untile[pl.S - 1]
+    r[pa], r[va] = r[va], r[pa]
+    u[r[pa]], u[r[va]] = pa, va
+    _expect_plan_error(pl, row_src=r, untile=u)
+    # wrong block_len
+    bl = pl.block_len.copy()
+    bl[0] -= 1
+    _expect_plan_error(pl, block_len=bl)
+
+
+def test_plan_argument_errors():
+    for args in (([4], (0, 4, 4), (4, 4, 4)), ([-1], (4, 4, 4), (4, 4, 4)),
+                 ([4], (4, 4, 4), (4, 0, 4))):
+        with pytest.raises(tsv.VsaError) as e:
+            tsv.vsa_plan_tiles(*args)
+        assert e.value.status == tsv.VSA_ERR_ARG
+    # padded rows must fit int32 indices
+    with pytest.raises(tsv.VsaError) as e:
+        tsv.vsa_plan_tiles([], (4096, 4096, 256), (4, 4, 4))
+    assert e.value.status == tsv.VSA_ERR_ARG
+
+
+def test_workspace_layout():
+    wl = workloads.WORKLOADS["h3"]
+    pl = tsv.cached_plan(wl.prefix_segments, wl.grid, wl.tile)
+    lay = tsv.vsa_workspace_layout(pl.info, wl.heads, wl.head_dim)
+    H, D, n_t, n_v = wl.heads, wl.head_dim, pl.n_t, pl.n_v
+    regions = [("k_tiled", H * pl.S_pad * D * 2), ("v_tiled", H * pl.S_pad * D * 2),
+               ("q_mean", H * n_t * D * 4), ("k_mean", H * n_t * D * 4),
+               ("v_mean", H * n_t * D * 4), ("scores", H * n_v * n_v * 4)]
+    end = 0
+    for name, size in regions:
+        off = getattr(lay, name)
+        assert off % 256 == 0 and off >= end
+        end = off + size
+    assert lay.part_o >= end and lay.total_bytes >= lay.part_ml
+    # a 50 MiB head splits its key lists: room for 8 chunk partials per 64 query rows
+    items = H * n_t
+    assert lay.part_ml - lay.part_o >= items * 8 * 64 * D * 4
+    # an override changes the layout, and 0 restores the automatic choice
+    tsv.vsa_set_split_chunks(1)
+    try:
+        assert tsv.vsa_workspace_layout(pl.info, H, D).total_bytes < lay.total_bytes
+    finally:
+        tsv.vsa_set_split_chunks(0)
+    assert tsv.vsa_workspace_layout(pl.info, H, D).total_bytes == lay.total_bytes
+    with pytest.raises(tsv.VsaError) as e:
+        tsv.vsa_set_split_chunks(65)
+    assert e.value.status == tsv.VSA_ERR_ARG
+
+
+def test_workspace_layout_unsupported():
+    pl = tsv.vsa_plan_tiles([10], (4, 4, 4), (4, 4, 4))
+    with pytest.raises(tsv.VsaError) as e:
+        tsv.vsa_workspace_layout(pl.info, 2, 96)
+    assert e.value.status == tsv.VSA_ERR_UNSUPPORTED
+    small = tsv.vsa_plan_tiles([10], (4, 4, 4), (2, 2, 2))   # 8-row tiles
+    with pytest.raises(tsv.VsaError) as e:
+        tsv.vsa_workspace_layout(small.info, 2, 64)
+    assert e.value.status == tsv.VSA_ERR_UNSUPPORTED
+
+
+# ---- GPU entry points: argument errors are reported before any device call.
+# Pointers below are never dereferenced: every case fails validation first.
+
+FAKE = 0x10000
+
+
+def _coarse(info, heads=2, head_dim=128, sparsity=float("nan"), keep_k=1, scale=0.0,
+            ptrs=(FAKE,) * 5, ws_bytes=1 << 40, keep=FAKE, oc=FAKE):
+    lib = tsv._lib
+    return lib.vsa_coarse_topk(ctypes.byref(info), ptrs[0], ptrs[1], heads, head_dim, sparsity,
+                               keep_k, scale, ptrs[2], ptrs[3], ptrs[4], FAKE * 2, ws_bytes, keep,
+                               oc, None)
+
+
+def _fine(info, heads=2, head_dim=128, k=1, scale=0.0, ws_bytes=1 << 40, keep=FAKE,
+          q=FAKE, gate=FAKE, out=FAKE):
+    lib = tsv._lib
+    return lib.vsa_sparse_attn_fwd(ctypes.byref(info), FAKE, FAKE, heads, head_dim, k, scale, q,
+                                   FAKE * 2, ws_bytes, keep, FAKE, gate, out, None)
+
+
+def test_gpu_entry_points_reject_bad_arguments():
+    pl = tsv.vsa_plan_tiles([20, 40], (4, 8, 8), (4, 4, 4))
+    info = pl.info
+    E = tsv
+    cases = [
+        (_coarse(info, head_dim=96), E.VSA_ERR_UNSUPPORTED),
+        (_coarse(info, heads=0), E.VSA_ERR_ARG),
+        (_coarse(info, keep_k=pl.n_v + 1), E.VSA_ERR_ARG),
+        (_coarse(info, keep_k=-1), E.VSA_ERR_ARG),                  # NaN sparsity
+        (_coarse(info, ptrs=(0, FAKE, FAKE, FAKE, FAKE)), E.VSA_ERR_ARG),
+        (_coarse(info, keep=0), E.VSA_ERR_ARG),                     # k > 0 needs keep_idx
+        (_coarse(info, ws_bytes=1024), E.VSA_ERR_ARG),
+        (_coarse(info, scale=float("inf")), E.VSA_ERR_ARG),
+        (_fine(info, head_dim=80), E.VSA_ERR_UNSUPPORTED),
+        (_fine(info, k=pl.n_v + 1), E.VSA_ERR_ARG),
+        (_fine(info, q=0), E.VSA_ERR_ARG),
+        (_fine(info, ws_bytes=1024), E.VSA_ERR_ARG),
+        (_fine(info, keep=0), E.VSA_ERR_ARG),
+    ]
+    for got, want in cases:
+        assert got == want, (got, want, tsv._lib.vsa_last_error())
+    # empty key set: no prefix tiles and k = 0
+    nopre = tsv.vsa_plan_tiles([], (4, 8, 8), (4, 4, 4))
+    assert _fine(nopre.info, k=0, keep=0) == E.VSA_ERR_ARG
+    assert b"empty key set" in tsv._lib.vsa_last_error()
+    # inconsistent plan info
+    bad = tsv.vsa_plan_info.from_buffer_copy(info)
+    bad.n_tiles += 1
+    assert _fine(bad) == E.VSA_ERR_PLAN
+    # gate projection shapes
+    lib = tsv._lib
+    assert lib.vsa_gate_proj(FAKE, FAKE, 10, 100, 64, FAKE, None) == E.VSA_ERR_UNSUPPORTED
+    assert lib.vsa_gate_proj(0, FAKE, 10, 128, 64, FAKE, None) == E.VSA_ERR_ARG
+    assert lib.vsa_gate_proj(FAKE, FAKE, -1, 128, 64, FAKE, None) == E.VSA_ERR_ARG
+
+
+def test_status_strings():
+    lib = tsv._lib
+    for code in (0, -1, -2, -3, -4):
+        assert lib.vsa_status_string(code)
+    assert lib.vsa_status_string(7) == b"unknown status"
