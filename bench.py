@@ -98,6 +98,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="h3", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-chunks", type=int, default=0,
+                    help="fine-pass key-list split (0 = the library's automatic choice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes (3 times), to scale "
                          "the FETCH_SIZE / WRITE_SIZE counters")
@@ -122,6 +124,7 @@ def main() -> int:
     import tile_sparse_video_amd as tsv
 
     wl = workloads.WORKLOADS[args.workload]
+    tsv.vsa_set_split_chunks(args.split_chunks)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating {wl.name} inputs ({wl.tokens} tokens)", file=sys.stderr, flush=True)
@@ -188,6 +191,7 @@ def main() -> int:
             "heads": wl.heads, "head_dim": wl.head_dim, "hidden": wl.hidden,
             "tokens": wl.tokens, "prefix_segments": list(wl.prefix_segments),
             "grid": list(wl.grid), "tile": list(wl.tile), "keep_k": att.k,
+            "split_chunks": args.split_chunks or "auto",
             "parallelism": "single GPU",
         },
         "ms_per_layer": round(layer_ms, 4),

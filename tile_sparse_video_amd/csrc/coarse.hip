@@ -3,7 +3,8 @@
 //                   order, fragment layout, for the fine pass (HBM-bound);
 //   video_scores -- coarse score of every (video query tile, video key tile)
 //                   pair as an fp32 fused-multiply-add chain (VALU);
-//   coarse_attn  -- tile-level softmax attention over the pooled Q, K, V (VALU);
+//   coarse_attn  -- tile-level softmax attention over the pooled Q, K, V (fp32
+//                   matrix cores);
 //   topk         -- per (head, video query tile) top-k by radix select, lowest
 //                   index first on ties, ascending output (one wavefront per row).
 //
@@ -198,94 +199,99 @@ __global__ __launch_bounds__(256) void video_scores_kernel(const float *__restri
 // ------------------------------------------------------- coarse attention --
 //
 // O_coarse[h][i] = sum_j softmax_j(scale * qmean_i . kmean_j) vmean_j over all
-// n_t key tiles, for 32 query tiles per block, streaming 64 key tiles at a time
-// through LDS with an online (running max / running sum) softmax in fp32.
-// A group of 8 consecutive lanes owns one query tile.
+// n_t key tiles, for every tile i. fp32 throughout, on the fp32 matrix cores
+// (v_mfma_f32_32x32x2_f32). A workgroup of 4 waves covers 128 query tiles of a
+// head; blocks of 32 key tiles (means of K and V) are staged in LDS once and
+// used by all 4 waves. Each wave: S^T = K.Q^T for its 32 query tiles (lane =
+// one query column), an online softmax per lane, then O^T += V^T.P^T.
+// Reduction slots: in S, product m pairs d = m (lane half 0) with d = D/2 + m
+// (half 1); in P.V, product m pairs keys 8(m/4) + 4*half + m%4, which are
+// exactly the S accumulator elements the lane already holds.
 template <int D>
 __global__ __launch_bounds__(256) void coarse_attn_kernel(const float *__restrict__ qmean,
                                                          const float *__restrict__ kmean,
                                                          const float *__restrict__ vmean, int n_t,
                                                          float scale_log2e, float *__restrict__ o_coarse)
 {
-    constexpr int TI = 32, TJ = 64, ROW = D + 4, DPT = D / 8;
-    __shared__ __attribute__((aligned(16))) float qs[TI * ROW];
-    __shared__ __attribute__((aligned(16))) float ks[TJ * ROW];
-    __shared__ __attribute__((aligned(16))) float vs[TJ * ROW];
-    __shared__ float ps[TI * (TJ + 1)];
-    const int h = blockIdx.y, i0 = blockIdx.x * TI, tid = threadIdx.x;
+    constexpr int KB = 32, ROW = D + 1, HD = D / 2, DB = D / 32;
+    __shared__ float ks[KB * ROW];
+    __shared__ float vs[KB * ROW];
+    const int h = blockIdx.y, wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int l32 = lane & 31, half = lane >> 5;
     const size_t hb = size_t(h) * n_t * D;
-    for (int idx = tid; idx < TI * D / 4; idx += 256) {
-        const int r = idx / (D / 4), c = idx % (D / 4);
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i0 + r < n_t) a = *reinterpret_cast<const float4 *>(qmean + hb + size_t(i0 + r) * D + 4 * c);
-        *reinterpret_cast<float4 *>(&qs[r * ROW + 4 * c]) = a;
-    }
-    const int qi = tid / 8, sub = tid % 8;  // query tile qi; lane-in-group sub
-    float m = -INFINITY, l = 0.0f, o[DPT];
-#pragma unroll
-    for (int c = 0; c < DPT; ++c) o[c] = 0.0f;
+    const int qi = blockIdx.x * 128 + wave * 32 + l32;
+    const bool qlive = qi < n_t;
 
-    for (int j0 = 0; j0 < n_t; j0 += TJ) {
+    float qv[HD];
+#pragma unroll
+    for (int m = 0; m < HD; ++m) qv[m] = qlive ? qmean[hb + size_t(qi) * D + HD * half + m] : 0.f;
+
+    f32x16_t O[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) O[db] = f32x16_t{};
+    float mrun = -INFINITY, lrun = 0.f;
+
+    for (int j0 = 0; j0 < n_t; j0 += KB) {
         __syncthreads();
-        for (int idx = tid; idx < TJ * D / 4; idx += 256) {
-            const int r = idx / (D / 4), c = idx % (D / 4);
-            float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-            if (j0 + r < n_t) {
-                a = *reinterpret_cast<const float4 *>(kmean + hb + size_t(j0 + r) * D + 4 * c);
-                b = *reinterpret_cast<const float4 *>(vmean + hb + size_t(j0 + r) * D + 4 * c);
+        for (int idx = threadIdx.x; idx < KB * D; idx += 256) {
+            const int r = idx / D, c = idx % D;
+            const bool live = j0 + r < n_t;
+            ks[r * ROW + c] = live ? kmean[hb + size_t(j0 + r) * D + c] : 0.f;
+            vs[r * ROW + c] = live ? vmean[hb + size_t(j0 + r) * D + c] : 0.f;
+        }
+        __syncthreads();
+
+        f32x16_t S = f32x16_t{};
+#pragma unroll
+        for (int m = 0; m < HD; ++m)
+            S = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[l32 * ROW + HD * half + m], qv[m], S, 0, 0, 0);
+        if (j0 + KB > n_t) {  // key tiles past the end never score
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (j0 + 8 * i + 4 * half + j >= n_t) S[4 * i + j] = -INFINITY;
+        }
+        float mx = S[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, S[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(mrun, mx);  // finite: every block has a real key tile
+        const float alpha = exp2f((mrun - m_new) * scale_log2e);
+        float p[16], rs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            p[e] = exp2f((S[e] - m_new) * scale_log2e);
+            rs += p[e];
+        }
+        rs += __shfl_xor(rs, 32);
+        lrun = lrun * alpha + rs;
+        mrun = m_new;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            f32x16_t acc = O[db];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[e] *= alpha;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const int key = 8 * (m / 4) + 4 * half + (m % 4);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * ROW + 32 * db + l32], p[m], acc, 0, 0, 0);
             }
-            *reinterpret_cast<float4 *>(&ks[r * ROW + 4 * c]) = a;
-            *reinterpret_cast<float4 *>(&vs[r * ROW + 4 * c]) = b;
-        }
-        __syncthreads();
-        float z[TJ / 8];
-        float zmax = -INFINITY;
-#pragma unroll
-        for (int b = 0; b < TJ / 8; ++b) {
-            const int j = sub + 8 * b;
-            float acc = 0.0f;
-            for (int d = 0; d < D; d += 4) {
-                const float4 qv = *reinterpret_cast<const float4 *>(&qs[qi * ROW + d]);
-                const float4 kv = *reinterpret_cast<const float4 *>(&ks[j * ROW + d]);
-                acc = __builtin_fmaf(qv.x, kv.x, acc);
-                acc = __builtin_fmaf(qv.y, kv.y, acc);
-                acc = __builtin_fmaf(qv.z, kv.z, acc);
-                acc = __builtin_fmaf(qv.w, kv.w, acc);
-            }
-            z[b] = (j0 + j < n_t) ? acc * scale_log2e : -INFINITY;
-            zmax = fmaxf(zmax, z[b]);
-        }
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 1));
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 2));
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 4));
-        const float m_new = fmaxf(m, zmax);  // finite: every chunk has >= 1 real key tile
-        const float alpha = exp2f(m - m_new);
-        float psum = 0.0f;
-#pragma unroll
-        for (int b = 0; b < TJ / 8; ++b) {
-            const float p = exp2f(z[b] - m_new);
-            psum += p;
-            ps[qi * (TJ + 1) + sub + 8 * b] = p;
-        }
-        psum += __shfl_xor(psum, 1);
-        psum += __shfl_xor(psum, 2);
-        psum += __shfl_xor(psum, 4);
-        l = l * alpha + psum;
-        m = m_new;
-        __syncthreads();
-#pragma unroll
-        for (int c = 0; c < DPT; ++c) {
-            const int d = sub + 8 * c;
-            float acc = 0.0f;
-            for (int j = 0; j < TJ; ++j) acc = __builtin_fmaf(ps[qi * (TJ + 1) + j], vs[j * ROW + d], acc);
-            o[c] = o[c] * alpha + acc;
+            O[db] = acc;
         }
     }
-    if (i0 + qi < n_t) {
-        const float inv = 1.0f / l;
+    if (!qlive) return;
+    // O^T[db] element 4i + j <-> d = 32db + 8i + 4*half + j, query column l32.
+    const float inv = 1.0f / lrun;
 #pragma unroll
-        for (int c = 0; c < DPT; ++c) o_coarse[hb + size_t(i0 + qi) * D + sub + 8 * c] = o[c] * inv;
-    }
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 32 * db + 8 * i + 4 * half;
+            *reinterpret_cast<float4 *>(o_coarse + hb + size_t(qi) * D + d0) =
+                make_float4(O[db][4 * i] * inv, O[db][4 * i + 1] * inv, O[db][4 * i + 2] * inv,
+                            O[db][4 * i + 3] * inv);
+        }
 }
 
 // ------------------------------------------------------------------- top-k --
@@ -400,7 +406,7 @@ void launch_coarse(const vsa_plan_info &info, int H, float scale, const float *q
         dim3 grid((n_v + 63) / 64, (n_v + 63) / 64, H);
         hipLaunchKernelGGL((video_scores_kernel<D>), grid, dim3(256), 0, st, qm, km, n_t, P, n_v, scores);
     }
-    dim3 grid2((n_t + 31) / 32, H);
+    dim3 grid2((n_t + 127) / 128, H);
     hipLaunchKernelGGL((coarse_attn_kernel<D>), grid2, dim3(256), 0, st, qm, km, vm, n_t,
                        scale * 1.4426950408889634f, o_coarse);
 }
