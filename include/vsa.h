@@ -142,9 +142,9 @@ int vsa_tile_pair_fraction(const vsa_plan_info *info, int32_t k, double *fractio
  *   scores: fp32 [H][n_v][n_v] coarse scores of video query tile i (row) vs
  *     video key tile j (column).
  *   part_o, part_ml: scratch for the fine pass when it splits each key list
- *     into C chunks (by tile id modulo C, C = 8 for heads whose K and V exceed
- *     16 MiB): per chunk, the unnormalised output and the running max / sum
- *     of every 64 query rows. Zero bytes when C = 1.
+ *     into C chunks (by tile id modulo C; C = 8 for heads whose K and V exceed
+ *     16 MiB, 8 * ceil(K+V / 96 MiB) beyond 96 MiB): per chunk, bf16 O / l and
+ *     the fp32 running max and sum of every 64 query rows. Zero when C = 1.
  * The layout depends on the split count, so query it after any
  * vsa_set_split_chunks call.
  */

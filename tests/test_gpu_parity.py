@@ -281,7 +281,7 @@ def test_full_size_sampled(name):
 
 # ------------------------------------------------ split fine pass --
 
-@pytest.mark.parametrize("chunks", [3, 8])
+@pytest.mark.parametrize("chunks", [3, 8, 16])
 @pytest.mark.parametrize("name", ["ragged64", "ragged128", "d64", "no_prefix", "k0", "one_tile"])
 def test_split_key_lists_every_token(name, chunks):
     """The fine pass split into chunks (partials + merge) gives the same layer."""

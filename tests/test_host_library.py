@@ -133,7 +133,7 @@ def test_workspace_layout():
     assert lay.part_o >= end and lay.total_bytes >= lay.part_ml
     # a 50 MiB head splits its key lists: room for 8 chunk partials per 64 query rows
     items = H * n_t
-    assert lay.part_ml - lay.part_o >= items * 8 * 64 * D * 4
+    assert lay.part_ml - lay.part_o >= items * 8 * 64 * D * 2
     # an override changes the layout, and 0 restores the automatic choice
     tsv.vsa_set_split_chunks(1)
     try:

@@ -28,8 +28,10 @@
 //    and chunk c is dispatched to XCD c (workgroups are spread round-robin
 //    over the 8 XCDs): each XCD's L2 then serves only 1/C of a head's K/V,
 //    swept in ascending order by all its waves. Each chunk writes a partial
-//    (O, running max, running sum); a merge kernel combines the chunks and
-//    applies the gated epilogue. Small heads (C = 1) finish in the epilogue.
+//    (O / l in bf16, running max and sum in fp32); a merge kernel combines the
+//    chunks and applies the gated epilogue. Small heads (C = 1) finish in the
+//    epilogue. Heads too large for the Infinity Cache use 8 * G chunks, taken
+//    in G phases per head.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -42,14 +44,20 @@ namespace vsa {
 
 static std::atomic<int> g_split_override{0};
 
-// Number of key chunks for the fine pass: split when the K and V of one head
-// are large enough that L2 reuse across query tiles matters.
+// Number of key chunks for the fine pass. Split (8 chunks, one per XCD) when
+// the K and V of one head are large enough that L2 reuse across query tiles
+// matters; beyond 96 MiB per head use 8 * G chunks taken in G phases, so the
+// K/V touched by one phase stays within what the Infinity Cache serves at
+// full speed.
 int split_chunks(const vsa_plan_info &info, int head_dim)
 {
     const int forced = g_split_override.load();
     if (forced > 0) return forced;
+    const double mib = 1024.0 * 1024.0;
     const double head_kv = 2.0 * double(info.rows_padded) * head_dim * 2.0;
-    return head_kv >= 16.0 * (1 << 20) ? 8 : 1;
+    if (head_kv < 16.0 * mib) return 1;
+    const int phases = int(std::ceil(head_kv / (96.0 * mib)));
+    return 8 * std::min(phases, 8);
 }
 
 namespace {
@@ -64,7 +72,7 @@ struct FineArgs {
     const float *o_coarse;      // [H][n_t][D]
     const uint16_t *gate;       // [S][H*D]
     uint16_t *out;              // [S][H][D]
-    float *part_o;              // split: [items][C][DB][2][64][16] unnormalised O
+    uint16_t *part_o;           // split: [items][C][DB][2][64][16] bf16 O / l
     float *part_ml;             // split: [items][C][2 (m, l)][2][32]
     int H, P, n_v, n_t, k, chunks;
     float scale_log2e;
@@ -111,16 +119,24 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
     const int lane = threadIdx.x;
     const int l32 = lane & 31, half = lane >> 5;
 
-    // ---- work item. Split: chunk = block % C, so with C = 8 chunk c always runs
-    // on XCD c. Then head-major, so the K/V in flight belong to one or two heads.
-    int rest = blockIdx.x, chunk = 0;
-    if (SPLIT) {
-        chunk = rest % a.chunks;
-        rest /= a.chunks;
+    // ---- work item, head-major so the K/V in flight belong to one or two heads.
+    // Split: the chunk's low three bits are block % 8, so chunk c always runs on
+    // XCD c % 8; with C = 8G the G phases of a head run one after another.
+    const int per_head = a.n_t * SUB;
+    int item, chunk = 0;
+    if (!SPLIT) {
+        item = blockIdx.x;  // = (h * n_t + tile) * SUB + qsub
+    } else if (a.chunks % 8 == 0) {
+        const int G = a.chunks / 8, rest = blockIdx.x / 8;
+        const int hh = rest / (G * per_head), g = (rest / per_head) % G;
+        item = hh * per_head + rest % per_head;
+        chunk = 8 * g + blockIdx.x % 8;
+    } else {
+        item = blockIdx.x / a.chunks;
+        chunk = blockIdx.x % a.chunks;
     }
-    const int item = rest;  // = (h * n_t + tile) * SUB + qsub
-    const int h = item / (a.n_t * SUB);
-    const int r = item % (a.n_t * SUB);
+    const int h = item / per_head;
+    const int r = item % per_head;
     const int tile = r / SUB, qsub = r % SUB;
     const bool dense = tile < a.P;
     const int n_list = dense ? a.n_t : a.P + a.k;
@@ -311,18 +327,25 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
     }
 
     if (SPLIT) {
-        // ---- partial: unnormalised O in register order, plus (m, l) per query.
+        // ---- partial: O / l in bf16 (register order), plus fp32 (m, l) per query.
         const size_t pidx = size_t(item) * a.chunks + chunk;
-        float *po = a.part_o + pidx * (64 * D);
+        uint16_t *po = a.part_o + pidx * (64 * D);
+        float inv[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) inv[qb] = l[qb] > 0.f ? 1.0f / l[qb] : 0.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                float4 *dst = reinterpret_cast<float4 *>(po + ((db * 2 + qb) * 64 + lane) * 16);
+                u32x4_t w[2];
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    dst[q4] = make_float4(O[db][qb][4 * q4], O[db][qb][4 * q4 + 1], O[db][qb][4 * q4 + 2],
-                                          O[db][qb][4 * q4 + 3]);
+                for (int e = 0; e < 16; e += 2) {
+                    const bf16x2_t pp = {(__bf16)(O[db][qb][e] * inv[qb]), (__bf16)(O[db][qb][e + 1] * inv[qb])};
+                    w[e / 8][(e % 8) / 2] = __builtin_bit_cast(uint32_t, pp);
+                }
+                u32x4_t *dst = reinterpret_cast<u32x4_t *>(po + ((db * 2 + qb) * 64 + lane) * 16);
+                dst[0] = w[0];
+                dst[1] = w[1];
             }
         if (lane < 32) {
             float *pml = a.part_ml + pidx * 128;
@@ -355,8 +378,8 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
 }
 
 // Combines the C chunk partials of one (head, 64 query rows) item:
-// M = max_c m_c, w_c = 2^((m_c - M) scale log2 e), O = sum_c w_c O_c,
-// l = sum_c w_c l_c, then the same gated epilogue as the direct path.
+// M = max_c m_c, w_c = l_c 2^((m_c - M) scale log2 e), O = sum_c w_c (O/l)_c,
+// L = sum_c w_c, then the same gated epilogue as the direct path.
 // One wavefront per item, lanes laid out as in the fine kernel.
 template <int D, int B>
 __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
@@ -391,22 +414,23 @@ __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const float mc = pml[qb * 32 + l32];
-            w[qb] = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mc - M[qb]) * c2);
-            L[qb] += w[qb] * pml[64 + qb * 32 + l32];
+            w[qb] = mc == -INFINITY ? 0.f : pml[64 + qb * 32 + l32] * __builtin_amdgcn_exp2f((mc - M[qb]) * c2);
+            L[qb] += w[qb];
         }
-        const float *po = a.part_o + (p0 + c) * (64 * D);
+        const uint16_t *po = a.part_o + (p0 + c) * (64 * D);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                const float4 *src = reinterpret_cast<const float4 *>(po + ((db * 2 + qb) * 64 + lane) * 16);
+                const u32x4_t *src = reinterpret_cast<const u32x4_t *>(po + ((db * 2 + qb) * 64 + lane) * 16);
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const float4 v = src[q4];
-                    O[db][qb][4 * q4 + 0] += w[qb] * v.x;
-                    O[db][qb][4 * q4 + 1] += w[qb] * v.y;
-                    O[db][qb][4 * q4 + 2] += w[qb] * v.z;
-                    O[db][qb][4 * q4 + 3] += w[qb] * v.w;
+                for (int h8 = 0; h8 < 2; ++h8) {
+                    const u32x4_t v = src[h8];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        O[db][qb][8 * h8 + 2 * q] += w[qb] * __uint_as_float(v[q] << 16);
+                        O[db][qb][8 * h8 + 2 * q + 1] += w[qb] * __uint_as_float(v[q] & 0xffff0000u);
+                    }
                 }
             }
     }
@@ -496,7 +520,7 @@ extern "C" int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row
     a.o_coarse = o_coarse_dev;
     a.gate = static_cast<const uint16_t *>(gate);
     a.out = static_cast<uint16_t *>(out);
-    a.part_o = reinterpret_cast<float *>(ws + L.part_o);
+    a.part_o = reinterpret_cast<uint16_t *>(ws + L.part_o);
     a.part_ml = reinterpret_cast<float *>(ws + L.part_ml);
     a.H = heads;
     a.P = info->n_prefix_tiles;

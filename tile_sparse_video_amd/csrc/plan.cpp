@@ -130,7 +130,7 @@ void compute_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_ws_l
     L->scores = take(H * n_v * n_v * 4);
     const size_t items = H * n_t * size_t(info.tile_rows / 64);
     const size_t C = size_t(split_chunks(info, head_dim));
-    L->part_o = take(C > 1 ? items * C * 64 * D * 4 : 0);
+    L->part_o = take(C > 1 ? items * C * 64 * D * 2 : 0);
     L->part_ml = take(C > 1 ? items * C * 128 * 4 : 0);
     L->total_bytes = off;
 }
