@@ -17,8 +17,10 @@ tiles only) divided by the layer time; `ms_per_step` is ms per layer.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -59,8 +61,8 @@ def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops):
     hr = oracle.head(Qb, Kb, Vb, 0, pl, kk, scale)          # pool, scores, top-k, O_coarse
     t_head = time.perf_counter() - t0
     rng = np.random.default_rng(0)
-    vid = rng.choice(np.arange(pl.S)[pl.untile // pl.B >= pl.P], size=64, replace=False)
-    pre = rng.choice(np.arange(pl.S)[pl.untile // pl.B < pl.P], size=min(32, wl.prefix_tokens),
+    vid = rng.choice(np.arange(pl.S)[pl.untile // pl.B >= pl.P], size=2048, replace=False)
+    pre = rng.choice(np.arange(pl.S)[pl.untile // pl.B < pl.P], size=min(256, wl.prefix_tokens),
                      replace=False) if wl.prefix_tokens else np.zeros(0, np.int64)
     t0 = time.perf_counter()
     oracle.fine_tokens(Qb, Kb, Vb, 0, pl, hr.keep, kk, scale, vid)
@@ -70,7 +72,7 @@ def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops):
         t0 = time.perf_counter()
         oracle.fine_tokens(Qb, Kb, Vb, 0, pl, hr.keep, kk, scale, pre)
         t_pre = (time.perf_counter() - t0) / len(pre)
-    gt = rng.choice(pl.S, size=16, replace=False)
+    gt = rng.choice(pl.S, size=512, replace=False)
     t0 = time.perf_counter()
     oracle.gate_proj(xb, wb, gt)
     t_gate = (time.perf_counter() - t0) / len(gt)
@@ -89,6 +91,35 @@ def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops):
                    f"query tokens; gate projection of {len(gt)} tokens; scaled to all heads "
                    f"and tokens of one layer"),
     }
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fine_attn_pmc_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "tile_sparse_video_amd", "csrc", f)
+                  for f in ("fine.hip", "device.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM-side bytes per fine-kernel launch from the committed PMC summary, or None
+    when it was taken on another workload or on a kernel source that has changed since."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1)).get(workload)
+    if not rec or rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec
 
 
 def main() -> int:
@@ -157,11 +188,18 @@ def main() -> int:
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    tsv.vsa_timing_enable(True)     # per-kernel events on the library's launch stream
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    tsv.vsa_timing_enable(False)
+    kernels = {}
+    for name in tsv.TIMED_KERNELS:
+        n, ms = tsv.vsa_timing_read(name)
+        if n:
+            kernels[name] = {"launches": n, "avg_ms": round(ms / n, 4)}
     parts = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)]
                       for i in range(args.steps)])
     layer_ms = float(evs[0][0].elapsed_time(evs[-1][3])) / args.steps
@@ -170,7 +208,9 @@ def main() -> int:
     keep_host = att.keep_idx.cpu().numpy()
     fine_flops = effective_fine_flops(att.plan, keep_host, wl.heads, wl.head_dim)
     tflops = fine_flops / (layer_ms * 1e-3) / 1e12
-    fine_tflops = fine_flops / (fine_ms * 1e-3) / 1e12
+    fine_kernel_ms = kernels["fine_attn"]["avg_ms"]
+    fine_tflops = fine_flops / (fine_kernel_ms * 1e-3) / 1e12
+    traffic = recorded_traffic(wl.name)
     frac_pairs = tsv.vsa_tile_pair_fraction(att.plan.info, att.k)
 
     result = {
@@ -198,18 +238,22 @@ def main() -> int:
         "pct_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
         "breakdown_ms": {"gate_proj": round(gate_ms, 4), "coarse_topk": round(coarse_ms, 4),
                          "sparse_attn_fwd": round(fine_ms, 4)},
+        "kernels": kernels,
         "ms_per_layer_attention_only": round(coarse_ms + fine_ms, 4),
         "tile_pair_fraction": round(frac_pairs, 4),
         "effective_fine_tflop": round(fine_flops / 1e12, 3),
         "wall_s": round(wall, 3),
         "roofline": {
-            "kernel": "fine_attn_kernel (vsa_sparse_attn_fwd)",
+            "kernel": "fine_attn_kernel (vsa_sparse_attn_fwd; its merge kernel is timed apart)",
             "bound": "mfma",
             "achieved": round(fine_tflops, 2),
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(fine_tflops / BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "algorithmic_tflop_per_launch": round(fine_flops / 1e12, 4),
+            "avg_launch_ms": fine_kernel_ms,
+            "traffic": None if traffic is None else traffic["bytes_per_launch"],
+            "traffic_detail": traffic,
         },
     }
     if not args.no_cpu_baseline:

@@ -244,6 +244,28 @@ int vsa_set_split_chunks(int32_t chunks);
 int vsa_gate_proj(const void *x, const void *w_gate, int64_t rows, int32_t hidden,
                   int32_t out_features, void *g, void *stream);
 
+/* ---------------------------------------------------- kernel timing -- */
+/*
+ * Measurement support, not part of the method: per-kernel device time of this
+ * library's own launches, for benchmarks that must report one kernel's time
+ * when an entry point launches several.
+ *
+ * vsa_timing_enable -- 1 clears earlier records and starts timing; 0 stops.
+ * While on, every kernel launch the library makes is bracketed by two HIP
+ * events recorded on the launch's own stream (events are created on first
+ * use and reused; they are never recorded into a stream being captured by
+ * design -- do not enable timing around graph capture). Process-wide.
+ *
+ * vsa_timing_read -- for the kernel named `kernel` (one of "gate_gemm",
+ * "gather_pool", "video_scores", "coarse_attn", "topk", "fine_attn",
+ * "merge"), waits for the recorded launches since the last enable and returns
+ * their number in *launches and their summed duration in *total_ms (host
+ * pointers). Errors: VSA_ERR_ARG for a null pointer or an unknown name,
+ * VSA_ERR_DEVICE if an event query fails.
+ */
+int vsa_timing_enable(int32_t enable);
+int vsa_timing_read(const char *kernel, int32_t *launches, double *total_ms);
+
 #ifdef __cplusplus
 }
 #endif

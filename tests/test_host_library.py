@@ -219,3 +219,25 @@ def test_status_strings():
     for code in (0, -1, -2, -3, -4):
         assert lib.vsa_status_string(code)
     assert lib.vsa_status_string(7) == b"unknown status"
+
+
+def test_kernel_timing_host_side():
+    lib = tsv._lib
+    tsv.vsa_timing_enable(True)
+    try:
+        for name in tsv.TIMED_KERNELS:
+            assert tsv.vsa_timing_read(name) == (0, 0.0)   # nothing launched since enable
+        with pytest.raises(tsv.VsaError) as e:
+            tsv.vsa_timing_read("not_a_kernel")
+        assert e.value.status == tsv.VSA_ERR_ARG
+        assert lib.vsa_timing_read(b"fine_attn", None, None) == tsv.VSA_ERR_ARG
+    finally:
+        tsv.vsa_timing_enable(False)
+    # failed launches (argument errors) record nothing
+    pl = tsv.vsa_plan_tiles([20, 40], (4, 8, 8), (4, 4, 4))
+    tsv.vsa_timing_enable(True)
+    try:
+        assert _fine(pl.info, head_dim=80) == tsv.VSA_ERR_UNSUPPORTED
+        assert tsv.vsa_timing_read("fine_attn") == (0, 0.0)
+    finally:
+        tsv.vsa_timing_enable(False)

@@ -31,8 +31,11 @@ VSA_ERR_DEVICE = -4
 EXPORTED = (
     "vsa_status_string", "vsa_last_error", "vsa_plan_tiles", "vsa_plan_validate",
     "vsa_keep_count", "vsa_tile_pair_fraction", "vsa_workspace_layout", "vsa_coarse_topk",
-    "vsa_sparse_attn_fwd", "vsa_gate_proj", "vsa_set_split_chunks",
+    "vsa_sparse_attn_fwd", "vsa_gate_proj", "vsa_set_split_chunks", "vsa_timing_enable",
+    "vsa_timing_read",
 )
+TIMED_KERNELS = ("gate_gemm", "gather_pool", "video_scores", "coarse_attn", "topk", "fine_attn",
+                 "merge")
 
 
 class VsaError(RuntimeError):
@@ -78,6 +81,9 @@ def _load() -> ctypes.CDLL:
                                 ctypes.c_int),
         "vsa_gate_proj": ([P, P, I64, I32, I32, P, P], ctypes.c_int),
         "vsa_set_split_chunks": ([I32], ctypes.c_int),
+        "vsa_timing_enable": ([I32], ctypes.c_int),
+        "vsa_timing_read": ([ctypes.c_char_p, ctypes.POINTER(I32), ctypes.POINTER(F64)],
+                            ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -268,6 +274,20 @@ def vsa_gate_proj(x: torch.Tensor, w_gate: torch.Tensor, g: torch.Tensor, stream
 def vsa_set_split_chunks(chunks: int) -> None:
     """Tuning override for the fine pass key-list split (0 = automatic)."""
     _check(_lib.vsa_set_split_chunks(int(chunks)), "vsa_set_split_chunks")
+
+
+def vsa_timing_enable(enable: bool) -> None:
+    """Start (clearing earlier records) or stop per-kernel timing of library launches."""
+    _check(_lib.vsa_timing_enable(1 if enable else 0), "vsa_timing_enable")
+
+
+def vsa_timing_read(kernel: str) -> tuple:
+    """(launches, total ms) of `kernel` since timing was last enabled; waits for them."""
+    n = ctypes.c_int32()
+    ms = ctypes.c_double()
+    _check(_lib.vsa_timing_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)),
+           "vsa_timing_read")
+    return n.value, ms.value
 
 
 # ---------------------------------------------------------- convenience --

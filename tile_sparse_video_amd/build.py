@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvsa.so")
-SOURCES = ["plan.cpp", "coarse.hip", "fine.hip", "gemm.hip"]
+SOURCES = ["plan.cpp", "timing.cpp", "coarse.hip", "fine.hip", "gemm.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -393,6 +393,7 @@ void launch_gather_pool(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 {
     constexpr int HPB = 256 / D;
     dim3 grid(n_t, (H + HPB - 1) / HPB, 3);
+    KernelTimer t(K_GATHER_POOL, st);
     hipLaunchKernelGGL((gather_pool_kernel<D, B>), grid, dim3(256), 0, st, q, k, v, row_src,
                        block_len, H, n_t, qm, km, vm, kt, vt);
 }
@@ -404,9 +405,11 @@ void launch_coarse(const vsa_plan_info &info, int H, float scale, const float *q
     const int n_t = info.n_tiles, n_v = info.n_video_tiles, P = info.n_prefix_tiles;
     if (n_v > 0) {
         dim3 grid((n_v + 63) / 64, (n_v + 63) / 64, H);
+        KernelTimer t(K_VIDEO_SCORES, st);
         hipLaunchKernelGGL((video_scores_kernel<D>), grid, dim3(256), 0, st, qm, km, n_t, P, n_v, scores);
     }
     dim3 grid2((n_t + 127) / 128, H);
+    KernelTimer t(K_COARSE_ATTN, st);
     hipLaunchKernelGGL((coarse_attn_kernel<D>), grid2, dim3(256), 0, st, qm, km, vm, n_t,
                        scale * 1.4426950408889634f, o_coarse);
 }
@@ -468,6 +471,7 @@ extern "C" int vsa_coarse_topk(const vsa_plan_info *info, const int32_t *row_src
     const int n_v = info->n_video_tiles;
     if (n_v > 0 && kk > 0) {
         const int rows = heads * n_v;
+        KernelTimer t(K_TOPK, st);
         hipLaunchKernelGGL(topk_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, sc_buf, rows, n_v,
                            int(kk), info->n_prefix_tiles, keep_idx_dev);
     }

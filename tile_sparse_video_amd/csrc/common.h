@@ -5,6 +5,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include <hip/hip_runtime_api.h>
+
 #include "vsa.h"
 
 namespace vsa {
@@ -25,6 +27,26 @@ int split_chunks(const vsa_plan_info &info, int head_dim);
 
 // Checks that the current HIP device is a gfx950; caches the answer per device.
 int check_device();
+
+// Kernels whose launches vsa_timing_read can report.
+enum KernelId {
+    K_GATE_GEMM, K_GATHER_POOL, K_VIDEO_SCORES, K_COARSE_ATTN, K_TOPK, K_FINE_ATTN, K_MERGE,
+    K_COUNT
+};
+
+// Scope guard around one launch: while timing is enabled it records an event
+// before the launch and one after it on `stream`; otherwise it does nothing.
+class KernelTimer {
+  public:
+    KernelTimer(KernelId id, hipStream_t stream);
+    ~KernelTimer();
+    KernelTimer(const KernelTimer &) = delete;
+    KernelTimer &operator=(const KernelTimer &) = delete;
+
+  private:
+    hipStream_t stream_;
+    long slot_;
+};
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -457,9 +457,14 @@ void launch_fine(const FineArgs &a, hipStream_t st)
 {
     const int items = a.H * a.n_t * (B / 64);
     if (a.chunks > 1) {
-        hipLaunchKernelGGL((fine_attn_kernel<D, B, true>), dim3(items * a.chunks), dim3(64), 0, st, a);
+        {
+            KernelTimer t(K_FINE_ATTN, st);
+            hipLaunchKernelGGL((fine_attn_kernel<D, B, true>), dim3(items * a.chunks), dim3(64), 0, st, a);
+        }
+        KernelTimer t(K_MERGE, st);
         hipLaunchKernelGGL((merge_kernel<D, B>), dim3((items + 3) / 4), dim3(256), 0, st, a, items);
     } else {
+        KernelTimer t(K_FINE_ATTN, st);
         hipLaunchKernelGGL((fine_attn_kernel<D, B, false>), dim3(items), dim3(64), 0, st, a);
     }
 }

@@ -135,10 +135,13 @@ extern "C" int vsa_gate_proj(const void *x, const void *w_gate, int64_t rows, in
     if (int st = check_device()) return st;
     if (rows == 0) return VSA_OK;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(gate_gemm_kernel, dim3(unsigned(blocks)), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const uint16_t *>(x),
-                       static_cast<const uint16_t *>(w_gate), rows, int(out_features), int(hidden),
-                       static_cast<uint16_t *>(g));
+    {
+        KernelTimer t(K_GATE_GEMM, static_cast<hipStream_t>(stream));
+        hipLaunchKernelGGL(gate_gemm_kernel, dim3(unsigned(blocks)), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), static_cast<const uint16_t *>(x),
+                           static_cast<const uint16_t *>(w_gate), rows, int(out_features), int(hidden),
+                           static_cast<uint16_t *>(g));
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(VSA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return VSA_OK;
