@@ -28,9 +28,11 @@ HIPCC_FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 # Per-source extras. The fine kernel rescales its O accumulators with VALU
-# ops; MFMA accumulators in VGPRs avoid bouncing them through AGPRs.
+# ops; MFMA accumulators in VGPRs avoid bouncing them through AGPRs. Its
+# scores and running maxima are never NaN (padding keys are -inf), so max
+# operations need no NaN-quieting canonicalisation.
 PER_SOURCE = {
-    "fine.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fine.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
 }
 
 
