@@ -61,6 +61,8 @@ def _load():
     lib.orc_tile_means.restype = None
     lib.orc_video_scores.argtypes = [_F32P, _F32P, i32, i32, i32, _I32P, i32, _F32P]
     lib.orc_video_scores.restype = None
+    lib.orc_all_scores.argtypes = [_F32P, _F32P, i32, i32, _I32P, i32, _F32P]
+    lib.orc_all_scores.restype = None
     lib.orc_topk_rows.argtypes = [_F32P, i32, i32, i32, i32, _I32P]
     lib.orc_topk_rows.restype = ctypes.c_int
     lib.orc_coarse_attn.argtypes = [_F32P, _F32P, _F32P, i32, i32, f64, _I32P, i32, _F64P]
@@ -68,6 +70,9 @@ def _load():
     lib.orc_fine_tokens.argtypes = [_U16P, _U16P, _U16P, i32, i32, i32, _I32P, _I32P, i32, i32,
                                     i32, _I32P, i32, f64, _I64P, i64, _F64P]
     lib.orc_fine_tokens.restype = ctypes.c_int
+    lib.orc_fine_tokens_lists.argtypes = [_U16P, _U16P, _U16P, i32, i32, i32, _I32P, _I32P, i32,
+                                          i32, _I32P, i32, f64, _I64P, i64, _F64P]
+    lib.orc_fine_tokens_lists.restype = ctypes.c_int
     lib.orc_combine.argtypes = [_F64P, _U16P, _F64P, i64, i32, _U16P]
     lib.orc_combine.restype = None
     lib.orc_gate_proj.argtypes = [_U16P, _U16P, i32, i32, _I64P, i64, _U16P]
@@ -242,6 +247,92 @@ def gate_proj(x: np.ndarray, W: np.ndarray, tokens: Optional[Iterable[int]] = No
 
 def tile_pair_fraction(P: int, n_v: int, k: int) -> float:
     return float(_load().orc_tile_pair_fraction(int(P), int(n_v), int(k)))
+
+
+# ------------------------------------------- reference-sparsity variant --
+#
+# [Veda] "ComfyUI node" inputs table: reference_sparsity applies the same top-k
+# setting to the reference tokens ("0 % = full attention"). Reading: the prefix
+# (reference) tiles stop being sinks; every query tile keeps its top-k_ref
+# prefix key tiles and its top-k_gen video key tiles by coarse score.
+
+def ref_keep_counts(pl: Plan, ref_sparsity=None, ref_keep_k=None, sparsity=None, keep_k=None):
+    """(k_ref over the P prefix tiles, k_gen over the n_v video tiles), same rule as O2."""
+    return keep_count(pl.P, ref_sparsity, ref_keep_k), keep_count(pl.n_v, sparsity, keep_k)
+
+
+def all_scores(qm: np.ndarray, km: np.ndarray, rows: Optional[Iterable[int]] = None) -> np.ndarray:
+    """fp32 [n_rows][n_t] FMA-chain scores of the given global query tiles against every tile."""
+    lib = _load()
+    n_t, D = qm.shape
+    r = np.arange(n_t, dtype=np.int32) if rows is None else np.asarray(list(rows), dtype=np.int32)
+    r = np.ascontiguousarray(r)
+    out = np.empty((r.size, n_t), dtype=np.float32)
+    lib.orc_all_scores(np.ascontiguousarray(qm, dtype=np.float32).reshape(-1),
+                       np.ascontiguousarray(km, dtype=np.float32).reshape(-1),
+                       int(n_t), int(D), r, int(r.size), out.reshape(-1))
+    return out
+
+
+def topk_ref(scores: np.ndarray, P: int, k_ref: int, k_gen: int) -> np.ndarray:
+    """Per row: the top k_ref of the prefix columns and the top k_gen of the video
+    columns (O5 on each group), as ascending global ids: int32 [n_rows][k_ref + k_gen]."""
+    pre = topk_rows(np.ascontiguousarray(scores[:, :P]), k_ref, 0)
+    vid = topk_rows(np.ascontiguousarray(scores[:, P:]), k_gen, P)
+    return np.concatenate([pre, vid], axis=1)
+
+
+def fine_tokens_lists(Q, K, V, h: int, pl: Plan, lists_h: np.ndarray, scale: float,
+                      tokens: Iterable[int]) -> np.ndarray:
+    """O_fine (fp64 [n_tok][D]) of the given tokens of head h with an explicit key
+    list per query tile: lists_h int32 [n_t][L] global tile ids."""
+    lib = _load()
+    S, H, D = Q.shape
+    toks = np.ascontiguousarray(np.asarray(list(tokens), dtype=np.int64))
+    lists_h = np.ascontiguousarray(lists_h, dtype=np.int32)
+    L = int(lists_h.shape[1])
+    flat = lists_h.reshape(-1) if lists_h.size else np.zeros(1, dtype=np.int32)
+    out = np.empty((toks.size, D), dtype=np.float64)
+    rc = lib.orc_fine_tokens_lists(np.ascontiguousarray(Q).reshape(-1),
+                                   np.ascontiguousarray(K).reshape(-1),
+                                   np.ascontiguousarray(V).reshape(-1), H, D, int(h), pl.untile,
+                                   pl.row_src, pl.n_t, pl.B, flat, L, float(scale), toks,
+                                   int(toks.size), out.reshape(-1))
+    if rc != 0:
+        raise OracleError("fine attention: a query has an empty or invalid key list")
+    return out
+
+
+def tile_pair_fraction_ref(n_t: int, k_ref: int, k_gen: int) -> float:
+    """Every query tile sees k_ref + k_gen key tiles out of n_t."""
+    return (k_ref + k_gen) / n_t
+
+
+def head_ref(Q, K, V, h: int, pl: Plan, k_ref: int, k_gen: int, scale: float,
+             score_rows: Optional[Iterable[int]] = None) -> "HeadResult":
+    """Pool, score (all tiles), select per group, coarse-attend one head."""
+    qm = tile_means(Q, h, pl)
+    km = tile_means(K, h, pl)
+    vm = tile_means(V, h, pl)
+    rows = (np.arange(pl.n_t, dtype=np.int32) if score_rows is None
+            else np.asarray(list(score_rows), dtype=np.int32))
+    sc = all_scores(qm, km, rows)
+    keep = topk_ref(sc, pl.P, k_ref, k_gen)
+    oc = coarse_attn(qm, km, vm, scale)
+    return HeadResult(qm, km, vm, sc, rows, keep, oc)
+
+
+def layer_tokens_ref(Q, K, V, g: np.ndarray, h: int, pl: Plan, hr: "HeadResult", scale: float,
+                     tokens: Iterable[int], g_is_rows: bool = False):
+    """Reference-sparsity outputs (bf16 bits [n_tok][D]) and O_fine of selected tokens.
+    hr must come from head_ref over all n_t query tiles."""
+    toks = np.asarray(list(tokens), dtype=np.int64)
+    D = Q.shape[2]
+    assert hr.keep.shape[0] == pl.n_t, "layer_tokens_ref needs the key lists of all tiles"
+    o_fine = fine_tokens_lists(Q, K, V, h, pl, hr.keep, scale, toks)
+    tiles = pl.untile[toks] // pl.B
+    g_rows = (g if g_is_rows else g[toks])[:, h * D:(h + 1) * D]
+    return combine(o_fine, np.ascontiguousarray(g_rows), hr.o_coarse[tiles]), o_fine
 
 
 # ------------------------------------------------------- the layer, in order --

@@ -229,6 +229,30 @@ void orc_video_scores(const float *qmean, const float *kmean, int32_t P, int32_t
     }
 }
 
+/*
+ * Reference-sparsity variant ([Veda] "ComfyUI node" inputs table: the
+ * reference_sparsity input applies the same top-k setting to the reference
+ * tokens). Reading: the reference (prefix) tiles lose their sink status; every
+ * query tile, prefix or video, is scored against every key tile with the same
+ * unscaled FMA chain as above, so the ranking within each key group uses one
+ * definition of the score. rows lists global query tile ids; scores is fp32
+ * [n_rows][n_t] over global key tile ids 0..n_t-1.
+ */
+void orc_all_scores(const float *qmean, const float *kmean, int32_t n_t, int32_t D,
+                    const int32_t *rows, int32_t n_rows, float *scores)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t r = 0; r < n_rows; ++r) {
+        const float *q = qmean + (int64_t)rows[r] * D;
+        for (int32_t j = 0; j < n_t; ++j) {
+            const float *k = kmean + (int64_t)j * D;
+            float acc = 0.0f;
+            for (int32_t d = 0; d < D; ++d) acc = fmaf(q[d], k[d], acc);
+            scores[(int64_t)r * n_t + j] = acc;
+        }
+    }
+}
+
 /* ----------------------------------------------------------- O5: top-k -- */
 /*
  * Kept video key tiles for one video query tile: the k largest coarse scores
@@ -355,6 +379,71 @@ int orc_fine_tokens(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int
         double zmax = -INFINITY;
         for (int32_t a = 0; a < n_keys_tiles; ++a) {
             int32_t j = (tile < P || a < P) ? a : keep[(int64_t)(tile - P) * k + (a - P)];
+            for (int32_t r = 0; r < B; ++r) {
+                int32_t u = row_src[(int64_t)j * B + r];
+                if (u < 0) continue;
+                double dot = 0.0;
+                for (int32_t d = 0; d < D; ++d)
+                    dot += q[d] * (double)bf16_to_float(K[((int64_t)u * H + h) * D + d]);
+                z[nk] = scale * dot;
+                u_of[nk] = u;
+                if (z[nk] > zmax) zmax = z[nk];
+                ++nk;
+            }
+        }
+        if (nk == 0) {
+            bad = 1;
+        } else {
+            double denom = 0.0;
+            for (int64_t a = 0; a < nk; ++a) {
+                z[a] = exp(z[a] - zmax);
+                denom += z[a];
+            }
+            for (int32_t d = 0; d < D; ++d) out[qi * D + d] = 0.0;
+            for (int64_t a = 0; a < nk; ++a) {
+                const uint16_t *v = V + (u_of[a] * H + h) * D;
+                for (int32_t d = 0; d < D; ++d) out[qi * D + d] += z[a] * (double)bf16_to_float(v[d]);
+            }
+            for (int32_t d = 0; d < D; ++d) out[qi * D + d] /= denom;
+        }
+        free(z);
+        free(u_of);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Reference-sparsity variant of O7: every query tile i has an explicit key
+ * list lists[i][0..L) of global tile ids (its kept reference tiles followed
+ * by its kept video tiles); a query token attends to the real rows of exactly
+ * those tiles. Padding never scores; scale and fp64 arithmetic as in O7.
+ * lists is int32 [n_t][L] for this head. out is fp64 [n_tok][D].
+ * Returns 0, or -1 if some query has no key (L = 0 or only empty tiles).
+ */
+int orc_fine_tokens_lists(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int32_t H,
+                          int32_t D, int32_t h, const int32_t *untile, const int32_t *row_src,
+                          int32_t n_t, int32_t B, const int32_t *lists, int32_t L, double scale,
+                          const int64_t *tokens, int64_t n_tok, double *out)
+{
+    if (D > 256) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t qi = 0; qi < n_tok; ++qi) {
+        int64_t t = tokens[qi];
+        int32_t tile = untile[t] / B;
+        double q[256];
+        for (int32_t d = 0; d < D; ++d) q[d] = (double)bf16_to_float(Q[(t * H + h) * D + d]);
+        size_t cap = (size_t)(L > 0 ? L : 1) * (size_t)B;
+        double *z = (double *)malloc(sizeof(double) * cap);
+        int64_t *u_of = (int64_t *)malloc(sizeof(int64_t) * cap);
+        int64_t nk = 0;
+        double zmax = -INFINITY;
+        for (int32_t a = 0; a < L; ++a) {
+            int32_t j = lists[(int64_t)tile * L + a];
+            if (j < 0 || j >= n_t) {
+                bad = 1;
+                continue;
+            }
             for (int32_t r = 0; r < B; ++r) {
                 int32_t u = row_src[(int64_t)j * B + r];
                 if (u < 0) continue;
