@@ -126,6 +126,24 @@ int vsa_keep_count(const vsa_plan_info *info, double sparsity, int64_t keep_k, i
  */
 int vsa_tile_pair_fraction(const vsa_plan_info *info, int32_t k, double *fraction);
 
+/*
+ * Reference sparsity. [Veda] "ComfyUI node" inputs table: reference_sparsity
+ * applies the same top-k setting to the reference tokens (0 % = full
+ * attention). Reading taken here: the prefix (reference) tiles stop being
+ * sinks; every query tile, prefix or video, keeps its k_ref highest-scoring
+ * prefix key tiles and its k_gen highest-scoring video key tiles.
+ *
+ * vsa_ref_keep_count -- k_ref over the P prefix tiles, by the vsa_keep_count
+ * rule: ref_keep_k >= 0 gives k_ref = ref_keep_k (VSA_ERR_ARG above P), else
+ * floor(clamp(1 - ref_sparsity, 0, 1) * P + 0.5) (VSA_ERR_ARG if NaN).
+ * vsa_tile_pair_fraction_ref -- (k_ref + k_gen) / n_t, the share of dense
+ * tile pairs computed in this mode. Both host only.
+ */
+int vsa_ref_keep_count(const vsa_plan_info *info, double ref_sparsity, int64_t ref_keep_k,
+                       int32_t *k_out);
+int vsa_tile_pair_fraction_ref(const vsa_plan_info *info, int32_t k_ref, int32_t k_gen,
+                               double *fraction);
+
 /* ------------------------------------------------------- workspace -- */
 /*
  * The workspace (device memory, caller-owned) holds what the coarse pass
@@ -139,8 +157,9 @@ int vsa_tile_pair_fraction(const vsa_plan_info *info, int32_t k, double *fractio
  *         V[row 16*c + (e<4 ? 4*(l/32) + e : 8 + 4*(l/32) + e-4)][d = 32*db + l%32].
  *     Padding rows are zero.
  *   q_mean, k_mean, v_mean: fp32 [H][n_t][D] tile means over real rows.
- *   scores: fp32 [H][n_v][n_v] coarse scores of video query tile i (row) vs
- *     video key tile j (column).
+ *   scores: fp32 coarse scores, [H][n_v][n_v] (video query tile i, video key
+ *     tile j) after vsa_coarse_topk, [H][n_t][n_t] (every query tile, every
+ *     key tile) after vsa_coarse_topk_ref; sized for the larger.
  *   part_o, part_ml: scratch for the fine pass when it splits each key list
  *     into C chunks (by tile id modulo C; C = 8 for heads whose K and V exceed
  *     16 MiB, 8 * ceil(K+V / 96 MiB) beyond 96 MiB): per chunk, bf16 O / l and
@@ -194,6 +213,27 @@ int vsa_coarse_topk(const vsa_plan_info *info, const int32_t *row_src_dev,
                     void *workspace, size_t workspace_bytes,
                     int32_t *keep_idx_dev, float *o_coarse_dev, void *stream);
 
+/*
+ * vsa_coarse_topk_ref -- the coarse stage with reference sparsity (see
+ * vsa_ref_keep_count). Steps 1 and 4 as vsa_coarse_topk; step 2 scores every
+ * query tile against every key tile (same FMA chain); step 3 selects, per
+ * head and query tile i (all n_t of them), the k_ref best prefix key tiles
+ * and the k_gen best video key tiles (ties to the lower index), written as
+ * keep_idx[h][i][0..k_ref) = prefix ids ascending, then
+ * keep_idx[h][i][k_ref..k_ref+k_gen) = video ids ascending.
+ * ref_sparsity / ref_keep_k: as vsa_ref_keep_count; sparsity / keep_k: as
+ * vsa_keep_count (for k_gen). keep_idx_dev: out device int32
+ * [H][n_t][k_ref + k_gen]; NULL allowed only when k_ref + k_gen == 0 (which
+ * vsa_sparse_attn_fwd_ref then rejects). Other arguments and errors as
+ * vsa_coarse_topk.
+ */
+int vsa_coarse_topk_ref(const vsa_plan_info *info, const int32_t *row_src_dev,
+                        const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                        double sparsity, int64_t keep_k, double ref_sparsity, int64_t ref_keep_k,
+                        float scale, const void *q, const void *k, const void *v,
+                        void *workspace, size_t workspace_bytes,
+                        int32_t *keep_idx_dev, float *o_coarse_dev, void *stream);
+
 /* -------------------------------------------------------- fine pass -- */
 /*
  * vsa_sparse_attn_fwd -- fine block-sparse attention plus the gated coarse
@@ -222,6 +262,21 @@ int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row_src_dev,
                         const void *workspace, size_t workspace_bytes,
                         const int32_t *keep_idx_dev, const float *o_coarse_dev,
                         const void *gate, void *out, void *stream);
+
+/*
+ * vsa_sparse_attn_fwd_ref -- the fine pass with reference sparsity: for each
+ * head h and real token t in tile i, keys(i) = the real rows of the tiles
+ * keep_idx[h][i][0..k_ref + k_gen) (as written by vsa_coarse_topk_ref), for
+ * prefix and video query tiles alike; O_fine and the gated output as
+ * vsa_sparse_attn_fwd. k_ref, k_gen: the counts used by vsa_coarse_topk_ref.
+ * Errors as vsa_sparse_attn_fwd; VSA_ERR_ARG also when k_ref + k_gen == 0.
+ */
+int vsa_sparse_attn_fwd_ref(const vsa_plan_info *info, const int32_t *row_src_dev,
+                            const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                            int32_t k_ref, int32_t k_gen, float scale, const void *q,
+                            const void *workspace, size_t workspace_bytes,
+                            const int32_t *keep_idx_dev, const float *o_coarse_dev,
+                            const void *gate, void *out, void *stream);
 
 /*
  * vsa_set_split_chunks -- tuning override for the fine pass: split every key

@@ -138,3 +138,25 @@ def sample_tokens(pl, n: int, seed: int) -> np.ndarray:
         picks = list(rng.choice(picks, size=n // 2, replace=False))
     rest = rng.choice(pl.S, size=max(0, n - len(picks)), replace=False)
     return np.unique(np.concatenate([np.asarray(picks, dtype=np.int64), rest.astype(np.int64)]))
+
+
+def run_gpu_ref(inp: Inputs, ref_sparsity=None, ref_keep_k=None, gate: Optional[torch.Tensor] = None,
+                dev="cuda") -> GpuRun:
+    """The layer in the reference-sparsity mode (every query tile keeps k_ref
+    prefix tiles and k_gen video tiles)."""
+    import tile_sparse_video_amd as tsv
+    wl = inp.wl
+    att = tsv.TileSparseAttention(wl.prefix_segments, wl.grid, wl.tile, wl.heads, wl.head_dim,
+                                  sparsity=wl.sparsity, keep_k=wl.keep_k, device=dev,
+                                  reference_sparsity=ref_sparsity, ref_keep_k=ref_keep_k)
+    qd, kd, vd = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    if gate is None:
+        xd, wd = inp.x.to(dev), inp.w.to(dev)
+        g = torch.empty((wl.tokens, wl.heads * wl.head_dim), dtype=torch.bfloat16, device=dev)
+        tsv.vsa_gate_proj(xd, wd, g)
+        del xd, wd
+    else:
+        g = gate.to(dev)
+    out = att(qd, kd, vd, g)
+    torch.cuda.synchronize()
+    return GpuRun(att, out, g)

@@ -241,3 +241,70 @@ def test_kernel_timing_host_side():
         assert tsv.vsa_timing_read("fine_attn") == (0, 0.0)
     finally:
         tsv.vsa_timing_enable(False)
+
+
+# ---- reference-sparsity mode: host-side checks
+
+def test_ref_keep_count_matches_oracle(orc):
+    for name in sorted(workloads.WORKLOADS):
+        wl = workloads.WORKLOADS[name]
+        pl = tsv.cached_plan(wl.prefix_segments, wl.grid, wl.tile)
+        o = orc.plan(wl.prefix_segments, wl.grid, wl.tile)
+        for s in (0.0, 0.5, 0.9, 1.0, -0.3):
+            k_ref, k_gen = orc.ref_keep_counts(o, s, None, s, None)
+            assert tsv.vsa_ref_keep_count(pl.info, s) == k_ref
+            assert tsv.vsa_tile_pair_fraction_ref(pl.info, k_ref, k_gen) == pytest.approx(
+                orc.tile_pair_fraction_ref(o.n_t, k_ref, k_gen), rel=1e-15)
+        assert tsv.vsa_ref_keep_count(pl.info, ref_keep_k=pl.P) == pl.P
+        with pytest.raises(tsv.VsaError) as e:
+            tsv.vsa_ref_keep_count(pl.info, ref_keep_k=pl.P + 1)
+        assert e.value.status == tsv.VSA_ERR_ARG
+    with pytest.raises(tsv.VsaError):
+        tsv.vsa_ref_keep_count(pl.info, float("nan"))
+    with pytest.raises(tsv.VsaError):
+        tsv.vsa_tile_pair_fraction_ref(pl.info, pl.P + 1, 0)
+
+
+def test_workspace_scores_region_holds_all_tile_pairs():
+    wl = workloads.WORKLOADS["h3"]
+    pl = tsv.cached_plan(wl.prefix_segments, wl.grid, wl.tile)
+    lay = tsv.vsa_workspace_layout(pl.info, wl.heads, wl.head_dim)
+    assert lay.part_o - lay.scores >= wl.heads * pl.n_t * pl.n_t * 4
+
+
+def test_ref_entry_points_reject_bad_arguments():
+    pl = tsv.vsa_plan_tiles([20, 40], (4, 8, 8), (4, 4, 4))
+    info = pl.info
+    lib = tsv._lib
+
+    def coarse(heads=2, head_dim=128, sparsity=0.5, keep_k=-1, rs=0.5, rk=-1, keep=FAKE,
+               ws_bytes=1 << 40, scale=0.0):
+        return lib.vsa_coarse_topk_ref(ctypes.byref(info), FAKE, FAKE, heads, head_dim, sparsity,
+                                       keep_k, rs, rk, scale, FAKE, FAKE, FAKE, FAKE * 2, ws_bytes,
+                                       keep, FAKE, None)
+
+    def fine(heads=2, head_dim=128, k_ref=1, k_gen=1, keep=FAKE, ws_bytes=1 << 40):
+        return lib.vsa_sparse_attn_fwd_ref(ctypes.byref(info), FAKE, FAKE, heads, head_dim, k_ref,
+                                           k_gen, 0.0, FAKE, FAKE * 2, ws_bytes, keep, FAKE, FAKE,
+                                           FAKE, None)
+
+    E = tsv
+    cases = [
+        (coarse(head_dim=96), E.VSA_ERR_UNSUPPORTED),
+        (coarse(heads=0), E.VSA_ERR_ARG),
+        (coarse(rk=pl.P + 1), E.VSA_ERR_ARG),
+        (coarse(rs=float("nan")), E.VSA_ERR_ARG),
+        (coarse(keep_k=pl.n_v + 1), E.VSA_ERR_ARG),
+        (coarse(keep=0), E.VSA_ERR_ARG),
+        (coarse(ws_bytes=4096), E.VSA_ERR_ARG),
+        (coarse(scale=float("nan")), E.VSA_ERR_ARG),
+        (fine(k_ref=0, k_gen=0, keep=0), E.VSA_ERR_ARG),   # empty key set
+        (fine(k_ref=pl.P + 1), E.VSA_ERR_ARG),
+        (fine(k_gen=pl.n_v + 1), E.VSA_ERR_ARG),
+        (fine(keep=0), E.VSA_ERR_ARG),
+        (fine(head_dim=80), E.VSA_ERR_UNSUPPORTED),
+        (fine(ws_bytes=4096), E.VSA_ERR_ARG),
+    ]
+    for got, want in cases:
+        assert got == want, (got, want, lib.vsa_last_error())
+    assert b"empty key set" in (fine(k_ref=0, k_gen=0, keep=0), lib.vsa_last_error())[1]

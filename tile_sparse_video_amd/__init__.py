@@ -32,7 +32,8 @@ EXPORTED = (
     "vsa_status_string", "vsa_last_error", "vsa_plan_tiles", "vsa_plan_validate",
     "vsa_keep_count", "vsa_tile_pair_fraction", "vsa_workspace_layout", "vsa_coarse_topk",
     "vsa_sparse_attn_fwd", "vsa_gate_proj", "vsa_set_split_chunks", "vsa_timing_enable",
-    "vsa_timing_read",
+    "vsa_timing_read", "vsa_ref_keep_count", "vsa_tile_pair_fraction_ref", "vsa_coarse_topk_ref",
+    "vsa_sparse_attn_fwd_ref",
 )
 TIMED_KERNELS = ("gate_gemm", "gather_pool", "video_scores", "coarse_attn", "topk", "fine_attn",
                  "merge")
@@ -81,6 +82,12 @@ def _load() -> ctypes.CDLL:
                                 ctypes.c_int),
         "vsa_gate_proj": ([P, P, I64, I32, I32, P, P], ctypes.c_int),
         "vsa_set_split_chunks": ([I32], ctypes.c_int),
+        "vsa_ref_keep_count": ([info_p, F64, I64, ctypes.POINTER(I32)], ctypes.c_int),
+        "vsa_tile_pair_fraction_ref": ([info_p, I32, I32, ctypes.POINTER(F64)], ctypes.c_int),
+        "vsa_coarse_topk_ref": ([info_p, P, P, I32, I32, F64, I64, F64, I64, F32, P, P, P, P, SZ,
+                                 P, P, P], ctypes.c_int),
+        "vsa_sparse_attn_fwd_ref": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, SZ, P, P, P, P,
+                                     P], ctypes.c_int),
         "vsa_timing_enable": ([I32], ctypes.c_int),
         "vsa_timing_read": ([ctypes.c_char_p, ctypes.POINTER(I32), ctypes.POINTER(F64)],
                             ctypes.c_int),
@@ -192,6 +199,24 @@ def vsa_tile_pair_fraction(info: vsa_plan_info, k: int) -> float:
     return float(f.value)
 
 
+def vsa_ref_keep_count(info: vsa_plan_info, ref_sparsity: Optional[float] = None,
+                       ref_keep_k: Optional[int] = None) -> int:
+    """Kept prefix (reference) tiles per query tile in the reference-sparsity mode."""
+    k = ctypes.c_int32(0)
+    _check(_lib.vsa_ref_keep_count(ctypes.byref(info),
+                                   float("nan") if ref_sparsity is None else float(ref_sparsity),
+                                   -1 if ref_keep_k is None else int(ref_keep_k), ctypes.byref(k)),
+           "vsa_ref_keep_count")
+    return int(k.value)
+
+
+def vsa_tile_pair_fraction_ref(info: vsa_plan_info, k_ref: int, k_gen: int) -> float:
+    f = ctypes.c_double(0)
+    _check(_lib.vsa_tile_pair_fraction_ref(ctypes.byref(info), int(k_ref), int(k_gen),
+                                           ctypes.byref(f)), "vsa_tile_pair_fraction_ref")
+    return float(f.value)
+
+
 def vsa_workspace_layout(info: vsa_plan_info, heads: int, head_dim: int) -> vsa_ws_layout:
     lay = vsa_ws_layout()
     _check(_lib.vsa_workspace_layout(ctypes.byref(info), int(heads), int(head_dim), ctypes.byref(lay)),
@@ -259,6 +284,58 @@ def vsa_sparse_attn_fwd(info: vsa_plan_info, row_src_dev: torch.Tensor, block_le
            "vsa_sparse_attn_fwd")
 
 
+def vsa_coarse_topk_ref(info: vsa_plan_info, row_src_dev: torch.Tensor,
+                        block_len_dev: torch.Tensor, heads: int, head_dim: int, q: torch.Tensor,
+                        k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor,
+                        keep_idx: Optional[torch.Tensor], o_coarse: torch.Tensor,
+                        sparsity: Optional[float] = None, keep_k: Optional[int] = None,
+                        ref_sparsity: Optional[float] = None, ref_keep_k: Optional[int] = None,
+                        scale: float = 0.0, stream=None) -> None:
+    S = info.rows_real
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, (S, heads, head_dim))
+    _need(row_src_dev, "row_src", torch.int32, (info.rows_padded,))
+    _need(block_len_dev, "block_len", torch.int32, (info.n_tiles,))
+    _need(workspace, "workspace", torch.uint8)
+    _need(o_coarse, "o_coarse", torch.float32, (heads, info.n_tiles, head_dim))
+    if keep_idx is not None:
+        _need(keep_idx, "keep_idx", torch.int32)
+        if keep_idx.dim() != 3 or tuple(keep_idx.shape[:2]) != (heads, info.n_tiles):
+            raise ValueError("keep_idx must be [heads][n_tiles][k_ref + k_gen]")
+    _check(_lib.vsa_coarse_topk_ref(
+        ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev), heads, head_dim,
+        float("nan") if sparsity is None else float(sparsity), -1 if keep_k is None else int(keep_k),
+        float("nan") if ref_sparsity is None else float(ref_sparsity),
+        -1 if ref_keep_k is None else int(ref_keep_k), float(scale), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(workspace), workspace.numel(), _ptr(keep_idx), _ptr(o_coarse), _stream(stream)),
+        "vsa_coarse_topk_ref")
+
+
+def vsa_sparse_attn_fwd_ref(info: vsa_plan_info, row_src_dev: torch.Tensor,
+                            block_len_dev: torch.Tensor, heads: int, head_dim: int, k_ref: int,
+                            k_gen: int, q: torch.Tensor, workspace: torch.Tensor,
+                            keep_idx: Optional[torch.Tensor], o_coarse: torch.Tensor,
+                            gate: torch.Tensor, out: torch.Tensor, scale: float = 0.0,
+                            stream=None) -> None:
+    S = info.rows_real
+    _need(q, "q", torch.bfloat16, (S, heads, head_dim))
+    _need(gate, "gate", torch.bfloat16)
+    if gate.numel() != S * heads * head_dim:
+        raise ValueError("gate must hold [S][heads*head_dim] values")
+    _need(out, "out", torch.bfloat16, (S, heads, head_dim))
+    _need(row_src_dev, "row_src", torch.int32, (info.rows_padded,))
+    _need(block_len_dev, "block_len", torch.int32, (info.n_tiles,))
+    _need(workspace, "workspace", torch.uint8)
+    _need(o_coarse, "o_coarse", torch.float32, (heads, info.n_tiles, head_dim))
+    if keep_idx is not None:
+        _need(keep_idx, "keep_idx", torch.int32, (heads, info.n_tiles, k_ref + k_gen))
+    _check(_lib.vsa_sparse_attn_fwd_ref(ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev),
+                                        heads, head_dim, int(k_ref), int(k_gen), float(scale),
+                                        _ptr(q), _ptr(workspace), workspace.numel(), _ptr(keep_idx),
+                                        _ptr(o_coarse), _ptr(gate), _ptr(out), _stream(stream)),
+           "vsa_sparse_attn_fwd_ref")
+
+
 def vsa_gate_proj(x: torch.Tensor, w_gate: torch.Tensor, g: torch.Tensor, stream=None) -> None:
     _need(x, "x", torch.bfloat16)
     _need(w_gate, "w_gate", torch.bfloat16)
@@ -314,31 +391,63 @@ class TileSparseAttention:
 
     def __init__(self, prefix_segments, grid, tile, heads: int, head_dim: int,
                  sparsity: Optional[float] = None, keep_k: Optional[int] = None,
-                 scale: float = 0.0, device="cuda"):
+                 scale: float = 0.0, device="cuda", reference_sparsity: Optional[float] = None,
+                 ref_keep_k: Optional[int] = None):
+        """reference_sparsity / ref_keep_k (either one) switch to the reference-sparsity
+        mode: every query tile keeps k_ref prefix tiles and k video tiles."""
         self.plan = cached_plan(prefix_segments, grid, tile)
         info = self.plan.info
         self.heads, self.head_dim, self.scale = int(heads), int(head_dim), float(scale)
         self.sparsity, self.keep_k = sparsity, keep_k
         self.k = vsa_keep_count(info, sparsity, keep_k)
+        self.ref = reference_sparsity is not None or ref_keep_k is not None
+        self.reference_sparsity, self.ref_keep_k = reference_sparsity, ref_keep_k
+        self.k_ref = vsa_ref_keep_count(info, reference_sparsity, ref_keep_k) if self.ref else 0
         self.layout = vsa_workspace_layout(info, heads, head_dim)
         dev = torch.device(device)
         self.row_src = torch.from_numpy(self.plan.row_src).to(dev)
         self.block_len = torch.from_numpy(self.plan.block_len).to(dev)
         self.workspace = torch.empty(self.layout.total_bytes, dtype=torch.uint8, device=dev)
-        self.keep_idx = torch.empty((heads, info.n_video_tiles, self.k), dtype=torch.int32, device=dev)
+        if self.ref:
+            shape = (heads, info.n_tiles, self.k_ref + self.k)
+        else:
+            shape = (heads, info.n_video_tiles, self.k)
+        self.keep_idx = torch.empty(shape, dtype=torch.int32, device=dev)
         self.o_coarse = torch.empty((heads, info.n_tiles, head_dim), dtype=torch.float32, device=dev)
 
+    @property
+    def list_len(self) -> int:
+        return self.keep_idx.shape[2]
+
     def coarse(self, q, k, v, stream=None) -> None:
-        vsa_coarse_topk(self.plan.info, self.row_src, self.block_len, self.heads, self.head_dim,
-                        q, k, v, self.workspace, self.keep_idx if self.k > 0 else None,
-                        self.o_coarse, sparsity=self.sparsity, keep_k=self.keep_k,
-                        scale=self.scale, stream=stream)
+        keep = self.keep_idx if self.list_len > 0 else None
+        if self.ref:
+            vsa_coarse_topk_ref(self.plan.info, self.row_src, self.block_len, self.heads,
+                                self.head_dim, q, k, v, self.workspace, keep, self.o_coarse,
+                                sparsity=self.sparsity, keep_k=self.keep_k,
+                                ref_sparsity=self.reference_sparsity, ref_keep_k=self.ref_keep_k,
+                                scale=self.scale, stream=stream)
+        else:
+            vsa_coarse_topk(self.plan.info, self.row_src, self.block_len, self.heads,
+                            self.head_dim, q, k, v, self.workspace, keep, self.o_coarse,
+                            sparsity=self.sparsity, keep_k=self.keep_k, scale=self.scale,
+                            stream=stream)
 
     def fine(self, q, gate, out, stream=None) -> None:
-        vsa_sparse_attn_fwd(self.plan.info, self.row_src, self.block_len, self.heads,
-                            self.head_dim, self.k, q, self.workspace,
-                            self.keep_idx if self.k > 0 else None, self.o_coarse, gate, out,
-                            scale=self.scale, stream=stream)
+        keep = self.keep_idx if self.list_len > 0 else None
+        if self.ref:
+            vsa_sparse_attn_fwd_ref(self.plan.info, self.row_src, self.block_len, self.heads,
+                                    self.head_dim, self.k_ref, self.k, q, self.workspace, keep,
+                                    self.o_coarse, gate, out, scale=self.scale, stream=stream)
+        else:
+            vsa_sparse_attn_fwd(self.plan.info, self.row_src, self.block_len, self.heads,
+                                self.head_dim, self.k, q, self.workspace, keep, self.o_coarse,
+                                gate, out, scale=self.scale, stream=stream)
+
+    def tile_pair_fraction(self) -> float:
+        if self.ref:
+            return vsa_tile_pair_fraction_ref(self.plan.info, self.k_ref, self.k)
+        return vsa_tile_pair_fraction(self.plan.info, self.k)
 
     def __call__(self, q, k, v, gate, out=None, stream=None) -> torch.Tensor:
         if out is None:

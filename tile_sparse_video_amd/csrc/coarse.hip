@@ -1,17 +1,21 @@
 // Coarse stage of gated, tile-sparse video attention on gfx950:
 //   gather_pool  -- tile means of Q, K, V (canonical fp32 order) and K/V in tile
 //                   order, fragment layout, for the fine pass (HBM-bound);
-//   video_scores -- coarse score of every (video query tile, video key tile)
-//                   pair as an fp32 fused-multiply-add chain (VALU);
+//   tile_scores  -- coarse score of every (query tile, key tile) pair of a tile
+//                   range (video x video, or all x all with reference
+//                   sparsity) as an fp32 fused-multiply-add chain (VALU);
 //   coarse_attn  -- tile-level softmax attention over the pooled Q, K, V (fp32
 //                   matrix cores);
-//   topk         -- per (head, video query tile) top-k by radix select, lowest
-//                   index first on ties, ascending output (one wavefront per row).
+//   topk         -- per score row and column group, top-k by a bitwise search
+//                   for the k-th largest key, lowest index first on ties,
+//                   ascending output (one wavefront per row, keys in registers).
 //
 // Method: SnackOnAI analysis of ComfyUI-Ref2VA-VSA ("The Code, Annotated",
 // snippet two: block_len masks padding; "References": coarse tile selection
-// from pooled Q/K as in the VSA paper) and the Ref2VA VSA news item ("The
-// two-tier attention patch": only video key tiles are pruned).
+// from pooled Q/K as in the VSA paper), the Ref2VA VSA news item ("The
+// two-tier attention patch": only video key tiles are pruned), and the Veda
+// news item ("ComfyUI node" inputs: reference_sparsity applies the same top-k
+// setting to the reference tokens).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -133,16 +137,16 @@ __global__ __launch_bounds__(256) void gather_pool_kernel(
     }
 }
 
-// ------------------------------------------------------------ video scores --
+// ------------------------------------------------------------- tile scores --
 //
-// scores[h][i][j] = fma-chain over ascending d of qmean[P+i][d] * kmean[P+j][d],
-// from +0. A block computes a 64 x 64 tile of (i, j) pairs from LDS copies of
+// scores[h][i][j] = fma-chain over ascending d of qmean[first+i][d] *
+// kmean[first+j][d], from +0, for i, j < n. A block computes a 64 x 64 tile of (i, j) pairs from LDS copies of
 // the means; each thread owns 4 x 4 pairs and walks d in order, so every pair
 // is the same sequential chain of correctly rounded fused multiply-adds.
 template <int D>
-__global__ __launch_bounds__(256) void video_scores_kernel(const float *__restrict__ qmean,
-                                                          const float *__restrict__ kmean, int n_t,
-                                                          int P, int n_v, float *__restrict__ scores)
+__global__ __launch_bounds__(256) void tile_scores_kernel(const float *__restrict__ qmean,
+                                                         const float *__restrict__ kmean, int n_t,
+                                                         int first, int n, float *__restrict__ scores)
 {
     constexpr int T = 64, ROW = D + 4;
     __shared__ __attribute__((aligned(16))) float qs[T * ROW];
@@ -150,13 +154,13 @@ __global__ __launch_bounds__(256) void video_scores_kernel(const float *__restri
     const int h = blockIdx.z;
     const int i0 = blockIdx.y * T, j0 = blockIdx.x * T;
     const int tid = threadIdx.x;
-    const float *qh = qmean + (size_t(h) * n_t + P) * D;
-    const float *kh = kmean + (size_t(h) * n_t + P) * D;
+    const float *qh = qmean + (size_t(h) * n_t + first) * D;
+    const float *kh = kmean + (size_t(h) * n_t + first) * D;
     for (int idx = tid; idx < T * D / 4; idx += 256) {
         const int r = idx / (D / 4), c = idx % (D / 4);
         float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-        if (i0 + r < n_v) a = *reinterpret_cast<const float4 *>(qh + size_t(i0 + r) * D + 4 * c);
-        if (j0 + r < n_v) b = *reinterpret_cast<const float4 *>(kh + size_t(j0 + r) * D + 4 * c);
+        if (i0 + r < n) a = *reinterpret_cast<const float4 *>(qh + size_t(i0 + r) * D + 4 * c);
+        if (j0 + r < n) b = *reinterpret_cast<const float4 *>(kh + size_t(j0 + r) * D + 4 * c);
         *reinterpret_cast<float4 *>(&qs[r * ROW + 4 * c]) = a;
         *reinterpret_cast<float4 *>(&ks[r * ROW + 4 * c]) = b;
     }
@@ -183,15 +187,15 @@ __global__ __launch_bounds__(256) void video_scores_kernel(const float *__restri
                 acc[a][b] = __builtin_fmaf(qv[a].w, kv[b].w, acc[a][b]);
             }
     }
-    float *out = scores + size_t(h) * n_v * n_v;
+    float *out = scores + size_t(h) * n * n;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int i = i0 + 4 * ty + a;
-        if (i >= n_v) continue;
+        if (i >= n) continue;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int j = j0 + tx + 16 * b;
-            if (j < n_v) out[size_t(i) * n_v + j] = acc[a][b];
+            if (j < n) out[size_t(i) * n + j] = acc[a][b];
         }
     }
 }
@@ -296,94 +300,146 @@ __global__ __launch_bounds__(256) void coarse_attn_kernel(const float *__restric
 
 // ------------------------------------------------------------------- top-k --
 //
-// One wavefront per (head, video query tile) row of n_v scores. A four-pass
-// 8-bit radix select over order-preserving keys finds the k-th largest key T
-// and how many keys equal to T are needed; a final pass in ascending index
-// order keeps every key > T and the lowest-index keys == T, writing their
-// global tile ids (P + j) in ascending order. Counts are exact integers, so
-// the result does not depend on the order of the LDS atomics.
+// One wavefront per score row: the k largest of n_cols scores (columns
+// col_first .. col_first + n_cols of the row), equal scores keeping the lower
+// column, written as ascending ids id_first + j to out[0..k).
+//
+// The row's order-preserving keys stay in registers (PL per lane, read once).
+// The k-th largest key T is found by a 32-step bitwise search: T is built from
+// the top bit down, keeping a bit whenever at least k keys are >= the
+// candidate; each count is a sum of ballot popcounts, so there are no atomics
+// and the result is exact. Then a pass in ascending column order keeps every
+// key > T and the first (k - #keys > T) keys equal to T.
+template <int PL>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ scores, int n_rows,
-                                                   int n_v, int k, int P, int32_t *__restrict__ keep)
+                                                   int row_len, int col_first, int n_cols, int k,
+                                                   int id_first, int32_t *__restrict__ keep,
+                                                   int keep_stride, int keep_first)
 {
-    __shared__ uint32_t hist[4][256];
-    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int row = blockIdx.x * 4 + w;
-    const bool live = row < n_rows;
-    const float *s = scores + size_t(live ? row : 0) * n_v;
-    int32_t *out = keep + size_t(live ? row : 0) * k;
-
-    if (k == n_v) {  // uniform across the launch
-        if (live)
-            for (int j = lane; j < n_v; j += kWave) out[j] = P + j;
+    const int lane = threadIdx.x % kWave;
+    const int row = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (row >= n_rows) return;  // wave-uniform
+    const float *s = scores + size_t(row) * row_len + col_first;
+    int32_t *out = keep + size_t(row) * keep_stride + keep_first;
+    if (k == n_cols) {
+        for (int j = lane; j < n_cols; j += kWave) out[j] = id_first + j;
         return;
     }
-    uint32_t prefix = 0, mask = 0;
-    int krem = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    if (k == 0) return;
+    uint32_t key[PL];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) hist[w][4 * lane + b] = 0;
-        __syncthreads();
-        if (live)
-            for (int j = lane; j < n_v; j += kWave) {
-                const uint32_t key = score_key(s[j]);
-                if ((key & mask) == prefix) atomicAdd(&hist[w][(key >> shift) & 255u], 1u);
-            }
-        __syncthreads();
-        // Lane L owns digits 255-4L .. 252-4L (descending); an inclusive scan over
-        // lanes gives the number of matching keys at or above each lane's digits.
-        uint32_t c[4], local = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            c[b] = hist[w][255 - 4 * lane - b];
-            local += c[b];
-        }
-        uint32_t incl = local;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const uint32_t t = __shfl_up(incl, off);
-            if (lane >= off) incl += t;
-        }
-        const uint32_t excl = incl - local;
-        const bool mine = excl < uint32_t(krem) && uint32_t(krem) <= incl;
-        int digit = 0;
-        uint32_t above = excl;
-        if (mine) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                if (above + c[b] >= uint32_t(krem)) {
-                    digit = 255 - 4 * lane - b;
-                    break;
-                }
-                above += c[b];
-            }
-        }
-        const uint64_t who = __ballot(mine);
-        const int src = who ? __ffsll((unsigned long long)who) - 1 : 0;
-        digit = __shfl(digit, src);
-        above = __shfl(above, src);
-        krem -= int(above);
-        prefix |= uint32_t(digit) << shift;
-        mask |= 255u << shift;
-        __syncthreads();
+    for (int e = 0; e < PL; ++e) {
+        const int j = kWave * e + lane;
+        key[e] = j < n_cols ? score_key(s[j]) : 0u;
     }
-    if (!live || k == 0) return;
-    // prefix is the k-th largest key; keep krem of the keys equal to it.
+    // Padding slots (j >= n_cols) hold key 0 and are excluded from every count.
+    auto count_ge = [&](uint32_t t) -> int {
+        int c = 0;
+#pragma unroll
+        for (int e = 0; e < PL; ++e) {
+            if (kWave * e >= n_cols) break;  // uniform
+            c += __popcll(__ballot(kWave * e + lane < n_cols && key[e] >= t));
+        }
+        return c;
+    };
+    uint32_t T = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = T | (1u << b);
+        if (count_ge(cand) >= k) T = cand;
+    }
+    // T is the k-th largest key: count(>= T) >= k > count(>= T + 1).
+    const int n_gt = T == 0xffffffffu ? 0 : count_ge(T + 1);
+    const int krem = k - n_gt;
     int base = 0, eq_seen = 0;
-    for (int j0 = 0; j0 < n_v; j0 += kWave) {
-        const int j = j0 + lane;
-        const bool valid = j < n_v;
-        const uint32_t key = valid ? score_key(s[j]) : 0u;
-        const bool gt = valid && key > prefix;
-        const bool eq = valid && key == prefix;
+#pragma unroll
+    for (int e = 0; e < PL; ++e) {
+        if (kWave * e >= n_cols) break;  // uniform
+        const int j = kWave * e + lane;
+        const bool valid = j < n_cols;
+        const bool gt = valid && key[e] > T;
+        const bool eq = valid && key[e] == T;
         const uint64_t eq_mask = __ballot(eq);
         const int eq_before = __popcll(eq_mask & lanes_below(lane));
         const bool sel = gt || (eq && eq_seen + eq_before < krem);
         const uint64_t sel_mask = __ballot(sel);
         const int pos = base + __popcll(sel_mask & lanes_below(lane));
-        if (sel && pos < k) out[pos] = P + j;  // exactly k are selected; the bound is a guard
+        if (sel && pos < k) out[pos] = id_first + j;  // exactly k are selected; the bound is a guard
         base += __popcll(sel_mask);
         eq_seen += __popcll(eq_mask);
     }
+}
+
+// Rows longer than the register-resident kernel holds: the same search, with
+// the keys re-read from memory (L2) for every count.
+__global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restrict__ scores,
+                                                          int n_rows, int row_len, int col_first,
+                                                          int n_cols, int k, int id_first,
+                                                          int32_t *__restrict__ keep, int keep_stride,
+                                                          int keep_first)
+{
+    const int lane = threadIdx.x % kWave;
+    const int row = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (row >= n_rows) return;  // wave-uniform
+    const float *s = scores + size_t(row) * row_len + col_first;
+    int32_t *out = keep + size_t(row) * keep_stride + keep_first;
+    if (k == n_cols) {
+        for (int j = lane; j < n_cols; j += kWave) out[j] = id_first + j;
+        return;
+    }
+    if (k == 0) return;
+    auto count_ge = [&](uint32_t t) -> int {
+        int c = 0;
+        for (int j0 = 0; j0 < n_cols; j0 += kWave) {
+            const int j = j0 + lane;
+            c += __popcll(__ballot(j < n_cols && score_key(s[j]) >= t));
+        }
+        return c;
+    };
+    uint32_t T = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = T | (1u << b);
+        if (count_ge(cand) >= k) T = cand;
+    }
+    const int n_gt = T == 0xffffffffu ? 0 : count_ge(T + 1);
+    const int krem = k - n_gt;
+    int base = 0, eq_seen = 0;
+    for (int j0 = 0; j0 < n_cols; j0 += kWave) {
+        const int j = j0 + lane;
+        const bool valid = j < n_cols;
+        const uint32_t key = valid ? score_key(s[j]) : 0u;
+        const bool gt = valid && key > T;
+        const bool eq = valid && key == T;
+        const uint64_t eq_mask = __ballot(eq);
+        const int eq_before = __popcll(eq_mask & lanes_below(lane));
+        const bool sel = gt || (eq && eq_seen + eq_before < krem);
+        const uint64_t sel_mask = __ballot(sel);
+        const int pos = base + __popcll(sel_mask & lanes_below(lane));
+        if (sel && pos < k) out[pos] = id_first + j;
+        base += __popcll(sel_mask);
+        eq_seen += __popcll(eq_mask);
+    }
+}
+
+// Top-k of one column group for n_rows rows (one wave per row).
+void launch_topk(const float *scores, int n_rows, int row_len, int col_first, int n_cols, int k,
+                 int id_first, int32_t *keep, int keep_stride, int keep_first, hipStream_t st)
+{
+    if (n_rows == 0 || n_cols == 0) return;
+    const dim3 grid((n_rows + 3) / 4), block(256);
+    KernelTimer t(K_TOPK, st);
+#define VSA_TOPK(PLV)                                                                              \
+    hipLaunchKernelGGL(topk_kernel<PLV>, grid, block, 0, st, scores, n_rows, row_len, col_first,    \
+                       n_cols, k, id_first, keep, keep_stride, keep_first)
+    if (n_cols <= 4 * kWave) VSA_TOPK(4);
+    else if (n_cols <= 8 * kWave) VSA_TOPK(8);
+    else if (n_cols <= 16 * kWave) VSA_TOPK(16);
+    else if (n_cols <= 32 * kWave) VSA_TOPK(32);
+    else if (n_cols <= 64 * kWave) VSA_TOPK(64);
+    else if (n_cols <= 96 * kWave) VSA_TOPK(96);
+    else
+        hipLaunchKernelGGL(topk_stream_kernel, grid, block, 0, st, scores, n_rows, row_len, col_first,
+                           n_cols, k, id_first, keep, keep_stride, keep_first);
+#undef VSA_TOPK
 }
 
 template <int D, int B>
@@ -398,15 +454,17 @@ void launch_gather_pool(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                        block_len, H, n_t, qm, km, vm, kt, vt);
 }
 
+// Scores over tiles [first, first + n) x [first, first + n), then the coarse
+// attention over all tiles.
 template <int D>
 void launch_coarse(const vsa_plan_info &info, int H, float scale, const float *qm, const float *km,
-                   const float *vm, float *scores, float *o_coarse, hipStream_t st)
+                   const float *vm, int first, int n, float *scores, float *o_coarse, hipStream_t st)
 {
-    const int n_t = info.n_tiles, n_v = info.n_video_tiles, P = info.n_prefix_tiles;
-    if (n_v > 0) {
-        dim3 grid((n_v + 63) / 64, (n_v + 63) / 64, H);
+    const int n_t = info.n_tiles;
+    if (n > 0) {
+        dim3 grid((n + 63) / 64, (n + 63) / 64, H);
         KernelTimer t(K_VIDEO_SCORES, st);
-        hipLaunchKernelGGL((video_scores_kernel<D>), grid, dim3(256), 0, st, qm, km, n_t, P, n_v, scores);
+        hipLaunchKernelGGL((tile_scores_kernel<D>), grid, dim3(256), 0, st, qm, km, n_t, first, n, scores);
     }
     dim3 grid2((n_t + 127) / 128, H);
     KernelTimer t(K_COARSE_ATTN, st);
@@ -414,34 +472,35 @@ void launch_coarse(const vsa_plan_info &info, int H, float scale, const float *q
                        scale * 1.4426950408889634f, o_coarse);
 }
 
-}  // namespace
-}  // namespace vsa
-
-using namespace vsa;
-
-extern "C" int vsa_coarse_topk(const vsa_plan_info *info, const int32_t *row_src_dev,
-                               const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
-                               double sparsity, int64_t keep_k, float scale, const void *q,
-                               const void *k, const void *v, void *workspace, size_t workspace_bytes,
-                               int32_t *keep_idx_dev, float *o_coarse_dev, void *stream)
+// Shared body of the two coarse entry points. ref: reference-sparsity mode
+// (scores over all tiles, two selections per query tile); otherwise the
+// default mode (video x video scores, k_gen video tiles per video query tile).
+int coarse_impl(const char *name, const vsa_plan_info *info, const int32_t *row_src_dev,
+                const int32_t *block_len_dev, int heads, int head_dim, bool ref, double sparsity,
+                int64_t keep_k, double ref_sparsity, int64_t ref_keep_k, float scale, const void *q,
+                const void *k, const void *v, void *workspace, size_t workspace_bytes,
+                int32_t *keep_idx_dev, float *o_coarse_dev, void *stream)
 {
-    clear_error();
     if (int st = check_info(info)) return st;
-    if (heads <= 0) return fail(VSA_ERR_ARG, "heads = %d", heads);
+    if (heads <= 0) return fail(VSA_ERR_ARG, "%s: heads = %d", name, heads);
     if (head_dim != 64 && head_dim != 128)
-        return fail(VSA_ERR_UNSUPPORTED, "head_dim = %d; supported: 64, 128", head_dim);
+        return fail(VSA_ERR_UNSUPPORTED, "%s: head_dim = %d; supported: 64, 128", name, head_dim);
     if (!row_src_dev || !block_len_dev || !q || !k || !v || !workspace || !o_coarse_dev)
-        return fail(VSA_ERR_ARG, "null device pointer");
-    if (!(std::isfinite(scale)) ) return fail(VSA_ERR_ARG, "scale is not finite");
-    int32_t kk = 0;
-    if (int st = vsa_keep_count(info, sparsity, keep_k, &kk)) return st;
-    if (kk > 0 && !keep_idx_dev) return fail(VSA_ERR_ARG, "keep_idx is null with k = %d", kk);
+        return fail(VSA_ERR_ARG, "%s: null device pointer", name);
+    if (!(std::isfinite(scale))) return fail(VSA_ERR_ARG, "%s: scale is not finite", name);
+    int32_t k_gen = 0, k_ref = 0;
+    if (int st = vsa_keep_count(info, sparsity, keep_k, &k_gen)) return st;
+    if (ref)
+        if (int st = vsa_ref_keep_count(info, ref_sparsity, ref_keep_k, &k_ref)) return st;
+    if (k_gen + k_ref > 0 && !keep_idx_dev)
+        return fail(VSA_ERR_ARG, "%s: keep_idx is null with %d kept tiles per row", name, k_gen + k_ref);
     vsa_ws_layout L;
     compute_layout(*info, heads, head_dim, &L);
     if (workspace_bytes < L.total_bytes)
-        return fail(VSA_ERR_ARG, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total_bytes);
+        return fail(VSA_ERR_ARG, "%s: workspace has %zu bytes, needs %zu", name, workspace_bytes,
+                    L.total_bytes);
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-        return fail(VSA_ERR_ARG, "workspace must be 256-byte aligned");
+        return fail(VSA_ERR_ARG, "%s: workspace must be 256-byte aligned", name);
     if (int st = check_device()) return st;
 
     const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(float(head_dim));
@@ -456,26 +515,58 @@ extern "C" int vsa_coarse_topk(const vsa_plan_info *info, const int32_t *row_src
     auto *kk_ = static_cast<const uint16_t *>(k);
     auto *vv = static_cast<const uint16_t *>(v);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int n_t = info->n_tiles, B = info->tile_rows;
+    const int n_t = info->n_tiles, B = info->tile_rows, P = info->n_prefix_tiles;
+    const int n_v = info->n_video_tiles;
+    const int first = ref ? 0 : P, n = ref ? n_t : n_v;
 
     (void)hipGetLastError();
     if (head_dim == 128) {
         if (B == 64) launch_gather_pool<128, 64>(qq, kk_, vv, row_src_dev, block_len_dev, heads, n_t, qm, km, vm, kt, vt, st);
         else launch_gather_pool<128, 128>(qq, kk_, vv, row_src_dev, block_len_dev, heads, n_t, qm, km, vm, kt, vt, st);
-        launch_coarse<128>(*info, heads, sc, qm, km, vm, sc_buf, o_coarse_dev, st);
+        launch_coarse<128>(*info, heads, sc, qm, km, vm, first, n, sc_buf, o_coarse_dev, st);
     } else {
         if (B == 64) launch_gather_pool<64, 64>(qq, kk_, vv, row_src_dev, block_len_dev, heads, n_t, qm, km, vm, kt, vt, st);
         else launch_gather_pool<64, 128>(qq, kk_, vv, row_src_dev, block_len_dev, heads, n_t, qm, km, vm, kt, vt, st);
-        launch_coarse<64>(*info, heads, sc, qm, km, vm, sc_buf, o_coarse_dev, st);
+        launch_coarse<64>(*info, heads, sc, qm, km, vm, first, n, sc_buf, o_coarse_dev, st);
     }
-    const int n_v = info->n_video_tiles;
-    if (n_v > 0 && kk > 0) {
-        const int rows = heads * n_v;
-        KernelTimer t(K_TOPK, st);
-        hipLaunchKernelGGL(topk_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, sc_buf, rows, n_v,
-                           int(kk), info->n_prefix_tiles, keep_idx_dev);
+    if (!ref) {
+        launch_topk(sc_buf, heads * n_v, n_v, 0, n_v, k_gen, P, keep_idx_dev, k_gen, 0, st);
+    } else {
+        const int Lk = k_ref + k_gen;
+        launch_topk(sc_buf, heads * n_t, n_t, 0, P, k_ref, 0, keep_idx_dev, Lk, 0, st);
+        launch_topk(sc_buf, heads * n_t, n_t, P, n_v, k_gen, P, keep_idx_dev, Lk, k_ref, st);
     }
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(VSA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(VSA_ERR_DEVICE, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
     return VSA_OK;
+}
+
+}  // namespace
+}  // namespace vsa
+
+using namespace vsa;
+
+extern "C" int vsa_coarse_topk(const vsa_plan_info *info, const int32_t *row_src_dev,
+                               const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                               double sparsity, int64_t keep_k, float scale, const void *q,
+                               const void *k, const void *v, void *workspace, size_t workspace_bytes,
+                               int32_t *keep_idx_dev, float *o_coarse_dev, void *stream)
+{
+    clear_error();
+    return coarse_impl("vsa_coarse_topk", info, row_src_dev, block_len_dev, heads, head_dim, false,
+                       sparsity, keep_k, 0.0, -1, scale, q, k, v, workspace, workspace_bytes,
+                       keep_idx_dev, o_coarse_dev, stream);
+}
+
+extern "C" int vsa_coarse_topk_ref(const vsa_plan_info *info, const int32_t *row_src_dev,
+                                   const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                                   double sparsity, int64_t keep_k, double ref_sparsity,
+                                   int64_t ref_keep_k, float scale, const void *q, const void *k,
+                                   const void *v, void *workspace, size_t workspace_bytes,
+                                   int32_t *keep_idx_dev, float *o_coarse_dev, void *stream)
+{
+    clear_error();
+    return coarse_impl("vsa_coarse_topk_ref", info, row_src_dev, block_len_dev, heads, head_dim, true,
+                       sparsity, keep_k, ref_sparsity, ref_keep_k, scale, q, k, v, workspace,
+                       workspace_bytes, keep_idx_dev, o_coarse_dev, stream);
 }

@@ -75,6 +75,8 @@ struct FineArgs {
     uint16_t *part_o;           // split: [items][C][DB][2][64][16] bf16 O / l
     float *part_ml;             // split: [items][C][2 (m, l)][2][32]
     int H, P, n_v, n_t, k, chunks;
+    int ref;                    // reference sparsity: every tile has an explicit list
+    int list_len;               // ref: entries per list (k_ref + k_gen), keep is [H][n_t][list_len]
     float scale_log2e;
 };
 
@@ -153,8 +155,8 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
     const int h = item / per_head;
     const int r = item % per_head;
     const int tile = r / SUB, qsub = r % SUB;
-    const bool dense = tile < a.P;
-    const int n_list = dense ? a.n_t : a.P + a.k;
+    const bool dense = !a.ref && tile < a.P;
+    const int n_list = a.ref ? a.list_len : dense ? a.n_t : a.P + a.k;
 
     // ---- query fragments (B operand of S^T = K . Q^T): lane -> query 32qb + l32,
     // reduction slot e of chunk c -> d = 16c + 8*half + e. Staged once in LDS
@@ -174,10 +176,15 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
         }
     }
 
-    // ---- key list source: position n -> tile n (prefix, or all tiles for a dense
-    // query tile) or the n-P-th kept tile (clamped: only guards a foreign list).
-    const int32_t *keep_row = dense ? a.keep : a.keep + (size_t(h) * a.n_v + (tile - a.P)) * a.k;
+    // ---- key list source. Default: position n -> tile n (prefix, or all tiles
+    // for a dense query tile) or the n-P-th kept tile. Reference sparsity: the
+    // n-th entry of the tile's own list. Entries are clamped (this only guards
+    // against a foreign list).
+    const int32_t *keep_row = a.ref ? a.keep + (size_t(h) * a.n_t + tile) * a.list_len
+                              : dense ? a.keep
+                                      : a.keep + (size_t(h) * a.n_v + (tile - a.P)) * a.k;
     auto tile_at = [&](int n) -> int {
+        if (a.ref) return min(max(keep_row[n], 0), a.n_t - 1);
         return (dense || n < a.P) ? n : min(max(keep_row[n - a.P], 0), a.n_t - 1);
     };
     // The wave stages the next segment of its key list (tiles of this chunk)
@@ -503,36 +510,44 @@ extern "C" int vsa_set_split_chunks(int32_t chunks)
     return VSA_OK;
 }
 
-extern "C" int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row_src_dev,
-                                   const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
-                                   int32_t k, float scale, const void *q, const void *workspace,
-                                   size_t workspace_bytes, const int32_t *keep_idx_dev,
-                                   const float *o_coarse_dev, const void *gate, void *out,
-                                   void *stream)
+namespace {
+
+// Shared body of the two fine entry points (ref: reference-sparsity lists).
+int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_src_dev,
+              const int32_t *block_len_dev, int heads, int head_dim, bool ref, int k, int k_ref,
+              float scale, const void *q, const void *workspace, size_t workspace_bytes,
+              const int32_t *keep_idx_dev, const float *o_coarse_dev, const void *gate, void *out,
+              void *stream)
 {
-    clear_error();
     if (int st = check_info(info)) return st;
-    if (heads <= 0) return fail(VSA_ERR_ARG, "heads = %d", heads);
+    if (heads <= 0) return fail(VSA_ERR_ARG, "%s: heads = %d", name, heads);
     if (head_dim != 64 && head_dim != 128)
-        return fail(VSA_ERR_UNSUPPORTED, "head_dim = %d; supported: 64, 128", head_dim);
+        return fail(VSA_ERR_UNSUPPORTED, "%s: head_dim = %d; supported: 64, 128", name, head_dim);
     if (k < 0 || k > info->n_video_tiles)
-        return fail(VSA_ERR_ARG, "k = %d outside [0, %d]", k, info->n_video_tiles);
-    if (info->n_prefix_tiles == 0 && k == 0 && info->n_video_tiles > 0)
-        return fail(VSA_ERR_ARG, "empty key set: no prefix tiles and k = 0");
+        return fail(VSA_ERR_ARG, "%s: k = %d outside [0, %d]", name, k, info->n_video_tiles);
+    if (ref && (k_ref < 0 || k_ref > info->n_prefix_tiles))
+        return fail(VSA_ERR_ARG, "%s: k_ref = %d outside [0, %d]", name, k_ref, info->n_prefix_tiles);
+    if (!ref && info->n_prefix_tiles == 0 && k == 0 && info->n_video_tiles > 0)
+        return fail(VSA_ERR_ARG, "%s: empty key set: no prefix tiles and k = 0", name);
+    if (ref && k + k_ref == 0)
+        return fail(VSA_ERR_ARG, "%s: empty key set: k_ref = k_gen = 0", name);
     if (!row_src_dev || !block_len_dev || !q || !workspace || !o_coarse_dev || !gate || !out)
-        return fail(VSA_ERR_ARG, "null device pointer");
-    if (k > 0 && !keep_idx_dev) return fail(VSA_ERR_ARG, "keep_idx is null with k = %d", k);
-    if (!std::isfinite(scale)) return fail(VSA_ERR_ARG, "scale is not finite");
+        return fail(VSA_ERR_ARG, "%s: null device pointer", name);
+    if ((ref ? k + k_ref : k) > 0 && !keep_idx_dev)
+        return fail(VSA_ERR_ARG, "%s: keep_idx is null", name);
+    if (!std::isfinite(scale)) return fail(VSA_ERR_ARG, "%s: scale is not finite", name);
     vsa_ws_layout L;
     compute_layout(*info, heads, head_dim, &L);
     if (workspace_bytes < L.total_bytes)
-        return fail(VSA_ERR_ARG, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total_bytes);
+        return fail(VSA_ERR_ARG, "%s: workspace has %zu bytes, needs %zu", name, workspace_bytes,
+                    L.total_bytes);
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-        return fail(VSA_ERR_ARG, "workspace must be 256-byte aligned");
+        return fail(VSA_ERR_ARG, "%s: workspace must be 256-byte aligned", name);
     const int64_t items = int64_t(heads) * info->n_tiles * (info->tile_rows / 64);
     const int chunks = split_chunks(*info, head_dim);
     if (items * chunks >= (int64_t(1) << 31))
-        return fail(VSA_ERR_UNSUPPORTED, "too many work items (%lld)", (long long)(items * chunks));
+        return fail(VSA_ERR_UNSUPPORTED, "%s: too many work items (%lld)", name,
+                    (long long)(items * chunks));
     if (int st = check_device()) return st;
 
     char *ws = static_cast<char *>(const_cast<void *>(workspace));
@@ -554,6 +569,8 @@ extern "C" int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row
     a.n_t = info->n_tiles;
     a.k = k;
     a.chunks = chunks;
+    a.ref = ref ? 1 : 0;
+    a.list_len = ref ? k + k_ref : 0;
     const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(float(head_dim));
     a.scale_log2e = sc * 1.4426950408889634f;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -567,6 +584,34 @@ extern "C" int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row
         else launch_fine<64, 128>(a, st);
     }
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(VSA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(VSA_ERR_DEVICE, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
     return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row_src_dev,
+                                   const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                                   int32_t k, float scale, const void *q, const void *workspace,
+                                   size_t workspace_bytes, const int32_t *keep_idx_dev,
+                                   const float *o_coarse_dev, const void *gate, void *out,
+                                   void *stream)
+{
+    clear_error();
+    return fine_impl("vsa_sparse_attn_fwd", info, row_src_dev, block_len_dev, heads, head_dim, false,
+                     k, 0, scale, q, workspace, workspace_bytes, keep_idx_dev, o_coarse_dev, gate,
+                     out, stream);
+}
+
+extern "C" int vsa_sparse_attn_fwd_ref(const vsa_plan_info *info, const int32_t *row_src_dev,
+                                       const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                                       int32_t k_ref, int32_t k_gen, float scale, const void *q,
+                                       const void *workspace, size_t workspace_bytes,
+                                       const int32_t *keep_idx_dev, const float *o_coarse_dev,
+                                       const void *gate, void *out, void *stream)
+{
+    clear_error();
+    return fine_impl("vsa_sparse_attn_fwd_ref", info, row_src_dev, block_len_dev, heads, head_dim,
+                     true, k_gen, k_ref, scale, q, workspace, workspace_bytes, keep_idx_dev,
+                     o_coarse_dev, gate, out, stream);
 }

@@ -127,7 +127,10 @@ void compute_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_ws_l
     L->q_mean = take(H * n_t * D * 4);
     L->k_mean = take(H * n_t * D * 4);
     L->v_mean = take(H * n_t * D * 4);
-    L->scores = take(H * n_v * n_v * 4);
+    // Coarse scores: [H][n_v][n_v] on the default path, [H][n_t][n_t] with
+    // reference sparsity (every query tile against every key tile).
+    (void)n_v;
+    L->scores = take(H * n_t * n_t * 4);
     const size_t items = H * n_t * size_t(info.tile_rows / 64);
     const size_t C = size_t(split_chunks(info, head_dim));
     L->part_o = take(C > 1 ? items * C * 64 * D * 2 : 0);
@@ -281,6 +284,38 @@ int vsa_keep_count(const vsa_plan_info *info, double sparsity, int64_t keep_k, i
     if (std::isnan(sparsity)) return fail(VSA_ERR_ARG, "sparsity is NaN");
     const double keep = std::min(1.0, std::max(0.0, 1.0 - sparsity));
     *k_out = int32_t(std::floor(keep * double(n_v) + 0.5));
+    return VSA_OK;
+}
+
+int vsa_ref_keep_count(const vsa_plan_info *info, double ref_sparsity, int64_t ref_keep_k,
+                       int32_t *k_out)
+{
+    clear_error();
+    if (!info || !k_out) return fail(VSA_ERR_ARG, "null argument");
+    const int64_t P = info->n_prefix_tiles;
+    if (P < 0) return fail(VSA_ERR_ARG, "negative prefix tile count");
+    if (ref_keep_k >= 0) {
+        if (ref_keep_k > P)
+            return fail(VSA_ERR_ARG, "reference keep count %lld exceeds %lld prefix tiles",
+                        (long long)ref_keep_k, (long long)P);
+        *k_out = int32_t(ref_keep_k);
+        return VSA_OK;
+    }
+    if (std::isnan(ref_sparsity)) return fail(VSA_ERR_ARG, "reference sparsity is NaN");
+    const double keep = std::min(1.0, std::max(0.0, 1.0 - ref_sparsity));
+    *k_out = int32_t(std::floor(keep * double(P) + 0.5));
+    return VSA_OK;
+}
+
+int vsa_tile_pair_fraction_ref(const vsa_plan_info *info, int32_t k_ref, int32_t k_gen,
+                               double *fraction)
+{
+    clear_error();
+    if (!info || !fraction) return fail(VSA_ERR_ARG, "null argument");
+    if (k_ref < 0 || k_ref > info->n_prefix_tiles || k_gen < 0 || k_gen > info->n_video_tiles)
+        return fail(VSA_ERR_ARG, "keep counts out of range");
+    if (info->n_tiles <= 0) return fail(VSA_ERR_ARG, "empty plan");
+    *fraction = (double(k_ref) + double(k_gen)) / double(info->n_tiles);
     return VSA_OK;
 }
 
