@@ -38,9 +38,16 @@ BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (vendor figure)
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E (vendor figure)
 
 
-def effective_fine_flops(plan, keep_idx: np.ndarray, heads: int, head_dim: int) -> float:
-    """4*D * sum over heads and query tiles of rows_i * (real key rows it attends)."""
+def effective_fine_flops(plan, keep_idx: np.ndarray, heads: int, head_dim: int,
+                         ref: bool = False) -> float:
+    """4*D * sum over heads and query tiles of rows_i * (real key rows it attends).
+    Default mode: keep_idx [H][n_v][k], prefix tiles are sinks and prefix queries
+    dense. Reference-sparsity mode: keep_idx [H][n_t][k_ref + k_gen], every list
+    explicit."""
     bl = plan.block_len.astype(np.int64)
+    if ref:
+        kept = bl[keep_idx].sum(-1) if keep_idx.shape[-1] else np.zeros(keep_idx.shape[:2], np.int64)
+        return 4.0 * head_dim * float((bl[None, :] * kept).sum())
     P = plan.P
     all_rows = int(bl.sum())
     prefix_rows = int(bl[:P].sum())
@@ -50,27 +57,37 @@ def effective_fine_flops(plan, keep_idx: np.ndarray, heads: int, head_dim: int) 
     return 4.0 * head_dim * float(pairs)
 
 
-def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops):
-    """The oracle, as it stands, on a bounded sample of this layer, scaled to one layer."""
+def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops, k_ref=None):
+    """The oracle, as it stands, on a bounded sample of this layer, scaled to one layer.
+    k_ref is not None in the reference-sparsity mode."""
     import oracle
     Qb, Kb, Vb = (workloads.bf16_bits(t) for t in (q, k, v))
     xb, wb = workloads.bf16_bits(x), workloads.bf16_bits(w)
     pl = oracle.plan(wl.prefix_segments, wl.grid, wl.tile)
     scale = wl.head_dim ** -0.5
     t0 = time.perf_counter()
-    hr = oracle.head(Qb, Kb, Vb, 0, pl, kk, scale)          # pool, scores, top-k, O_coarse
+    if k_ref is None:
+        hr = oracle.head(Qb, Kb, Vb, 0, pl, kk, scale)      # pool, scores, top-k, O_coarse
+
+        def fine(toks):
+            return oracle.fine_tokens(Qb, Kb, Vb, 0, pl, hr.keep, kk, scale, toks)
+    else:
+        hr = oracle.head_ref(Qb, Kb, Vb, 0, pl, k_ref, kk, scale)
+
+        def fine(toks):
+            return oracle.fine_tokens_lists(Qb, Kb, Vb, 0, pl, hr.keep, scale, toks)
     t_head = time.perf_counter() - t0
     rng = np.random.default_rng(0)
     vid = rng.choice(np.arange(pl.S)[pl.untile // pl.B >= pl.P], size=2048, replace=False)
     pre = rng.choice(np.arange(pl.S)[pl.untile // pl.B < pl.P], size=min(256, wl.prefix_tokens),
                      replace=False) if wl.prefix_tokens else np.zeros(0, np.int64)
     t0 = time.perf_counter()
-    oracle.fine_tokens(Qb, Kb, Vb, 0, pl, hr.keep, kk, scale, vid)
+    fine(vid)
     t_vid = (time.perf_counter() - t0) / len(vid)
     t_pre = 0.0
     if len(pre):
         t0 = time.perf_counter()
-        oracle.fine_tokens(Qb, Kb, Vb, 0, pl, hr.keep, kk, scale, pre)
+        fine(pre)
         t_pre = (time.perf_counter() - t0) / len(pre)
     gt = rng.choice(pl.S, size=512, replace=False)
     t0 = time.perf_counter()
@@ -129,6 +146,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="h3", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--reference-sparsity", type=float, default=None, metavar="S",
+                    help="run the reference-sparsity mode: every query tile keeps the top "
+                         "(1-S) of the prefix tiles as well as the top video tiles")
     ap.add_argument("--split-chunks", type=int, default=0,
                     help="fine-pass key-list split (0 = the library's automatic choice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -163,7 +183,8 @@ def main() -> int:
     x, w = workloads.make_x(wl), workloads.make_w_gate(wl)
     qd, kd, vd, xd, wd = (t.to(dev) for t in (q, k, v, x, w))
     att = tsv.TileSparseAttention(wl.prefix_segments, wl.grid, wl.tile, wl.heads, wl.head_dim,
-                                  sparsity=wl.sparsity, keep_k=wl.keep_k, device=dev)
+                                  sparsity=wl.sparsity, keep_k=wl.keep_k, device=dev,
+                                  reference_sparsity=args.reference_sparsity)
     g = torch.empty((wl.tokens, wl.heads * wl.head_dim), dtype=torch.bfloat16, device=dev)
     out = torch.empty_like(qd)
     stream = torch.cuda.current_stream()
@@ -206,12 +227,12 @@ def main() -> int:
     gate_ms, coarse_ms, fine_ms = (float(x) for x in parts.mean(0))
 
     keep_host = att.keep_idx.cpu().numpy()
-    fine_flops = effective_fine_flops(att.plan, keep_host, wl.heads, wl.head_dim)
+    fine_flops = effective_fine_flops(att.plan, keep_host, wl.heads, wl.head_dim, att.ref)
     tflops = fine_flops / (layer_ms * 1e-3) / 1e12
     fine_kernel_ms = kernels["fine_attn"]["avg_ms"]
     fine_tflops = fine_flops / (fine_kernel_ms * 1e-3) / 1e12
-    traffic = recorded_traffic(wl.name)
-    frac_pairs = tsv.vsa_tile_pair_fraction(att.plan.info, att.k)
+    traffic = None if att.ref else recorded_traffic(wl.name)
+    frac_pairs = att.tile_pair_fraction()
 
     result = {
         "metric": METRIC,
@@ -231,6 +252,8 @@ def main() -> int:
             "heads": wl.heads, "head_dim": wl.head_dim, "hidden": wl.hidden,
             "tokens": wl.tokens, "prefix_segments": list(wl.prefix_segments),
             "grid": list(wl.grid), "tile": list(wl.tile), "keep_k": att.k,
+            "reference_sparsity": args.reference_sparsity,
+            "ref_keep_k": att.k_ref if att.ref else None,
             "split_chunks": args.split_chunks or "auto",
             "parallelism": "single GPU",
         },
@@ -258,7 +281,8 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, x, w, att.plan, att.k, fine_flops)
+        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, x, w, att.plan, att.k, fine_flops,
+                                              att.k_ref if att.ref else None)
     print(json.dumps(result), flush=True)
     return 0
 

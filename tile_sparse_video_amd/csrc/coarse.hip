@@ -6,9 +6,10 @@
 //                   sparsity) as an fp32 fused-multiply-add chain (VALU);
 //   coarse_attn  -- tile-level softmax attention over the pooled Q, K, V (fp32
 //                   matrix cores);
-//   topk         -- per score row and column group, top-k by a bitwise search
-//                   for the k-th largest key, lowest index first on ties,
-//                   ascending output (one wavefront per row, keys in registers).
+//   topk         -- per score row and column group, top-k: a bitwise search for
+//                   the k-th largest key over register-resident keys (rows up to
+//                   2048), an 8-bit radix select beyond; lowest index first on
+//                   ties, ascending output (one wavefront per row).
 //
 // Method: SnackOnAI analysis of ComfyUI-Ref2VA-VSA ("The Code, Annotated",
 // snippet two: block_len masks padding; "References": coarse tile selection
@@ -332,14 +333,16 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
         const int j = kWave * e + lane;
         key[e] = j < n_cols ? score_key(s[j]) : 0u;
     }
-    // Padding slots (j >= n_cols) hold key 0 and are excluded from every count.
+    // Padding slots (j >= n_cols) hold key 0, which no count sees: every
+    // threshold searched below is >= 1, and finite scores have keys >= 1.
+    // A count is a per-lane compare-and-add over the registers, summed
+    // across the wave by a butterfly.
     auto count_ge = [&](uint32_t t) -> int {
         int c = 0;
 #pragma unroll
-        for (int e = 0; e < PL; ++e) {
-            if (kWave * e >= n_cols) break;  // uniform
-            c += __popcll(__ballot(kWave * e + lane < n_cols && key[e] >= t));
-        }
+        for (int e = 0; e < PL; ++e) c += key[e] >= t ? 1 : 0;
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off);
         return c;
     };
     uint32_t T = 0;
@@ -369,52 +372,89 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
     }
 }
 
-// Rows longer than the register-resident kernel holds: the same search, with
-// the keys re-read from memory (L2) for every count.
-__global__ __launch_bounds__(256) void topk_stream_kernel(const float *__restrict__ scores,
-                                                          int n_rows, int row_len, int col_first,
-                                                          int n_cols, int k, int id_first,
-                                                          int32_t *__restrict__ keep, int keep_stride,
-                                                          int keep_first)
+// Long rows: a four-pass 8-bit radix select over LDS histograms, re-reading
+// the row (from L2) in each pass, then the same ordered compaction.
+__global__ __launch_bounds__(256) void topk_radix_kernel(const float *__restrict__ scores,
+                                                         int n_rows, int row_len, int col_first,
+                                                         int n_cols, int k, int id_first,
+                                                         int32_t *__restrict__ keep, int keep_stride,
+                                                         int keep_first)
 {
-    const int lane = threadIdx.x % kWave;
-    const int row = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (row >= n_rows) return;  // wave-uniform
-    const float *s = scores + size_t(row) * row_len + col_first;
-    int32_t *out = keep + size_t(row) * keep_stride + keep_first;
-    if (k == n_cols) {
-        for (int j = lane; j < n_cols; j += kWave) out[j] = id_first + j;
+    __shared__ uint32_t hist[4][256];
+    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int row = blockIdx.x * 4 + w;
+    const bool live = row < n_rows;
+    const float *s = scores + size_t(live ? row : 0) * row_len + col_first;
+    int32_t *out = keep + size_t(live ? row : 0) * keep_stride + keep_first;
+    if (k == n_cols) {  // uniform across the launch
+        if (live)
+            for (int j = lane; j < n_cols; j += kWave) out[j] = id_first + j;
         return;
     }
-    if (k == 0) return;
-    auto count_ge = [&](uint32_t t) -> int {
-        int c = 0;
-        for (int j0 = 0; j0 < n_cols; j0 += kWave) {
-            const int j = j0 + lane;
-            c += __popcll(__ballot(j < n_cols && score_key(s[j]) >= t));
+    uint32_t prefix = 0, mask = 0;
+    int krem = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) hist[w][4 * lane + b] = 0;
+        __syncthreads();
+        if (live)
+            for (int j = lane; j < n_cols; j += kWave) {
+                const uint32_t key = score_key(s[j]);
+                if ((key & mask) == prefix) atomicAdd(&hist[w][(key >> shift) & 255u], 1u);
+            }
+        __syncthreads();
+        // Lane L owns digits 255-4L .. 252-4L (descending); an inclusive scan over
+        // lanes gives the number of matching keys at or above each lane's digits.
+        uint32_t c[4], local = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            c[b] = hist[w][255 - 4 * lane - b];
+            local += c[b];
         }
-        return c;
-    };
-    uint32_t T = 0;
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t cand = T | (1u << b);
-        if (count_ge(cand) >= k) T = cand;
+        uint32_t incl = local;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const uint32_t t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
+        }
+        const uint32_t excl = incl - local;
+        const bool mine = excl < uint32_t(krem) && uint32_t(krem) <= incl;
+        int digit = 0;
+        uint32_t above = excl;
+        if (mine) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                if (above + c[b] >= uint32_t(krem)) {
+                    digit = 255 - 4 * lane - b;
+                    break;
+                }
+                above += c[b];
+            }
+        }
+        const uint64_t who = __ballot(mine);
+        const int src = who ? __ffsll((unsigned long long)who) - 1 : 0;
+        digit = __shfl(digit, src);
+        above = __shfl(above, src);
+        krem -= int(above);
+        prefix |= uint32_t(digit) << shift;
+        mask |= 255u << shift;
+        __syncthreads();
     }
-    const int n_gt = T == 0xffffffffu ? 0 : count_ge(T + 1);
-    const int krem = k - n_gt;
+    if (!live || k == 0) return;
+    // prefix is the k-th largest key; keep krem of the keys equal to it.
     int base = 0, eq_seen = 0;
     for (int j0 = 0; j0 < n_cols; j0 += kWave) {
         const int j = j0 + lane;
         const bool valid = j < n_cols;
         const uint32_t key = valid ? score_key(s[j]) : 0u;
-        const bool gt = valid && key > T;
-        const bool eq = valid && key == T;
+        const bool gt = valid && key > prefix;
+        const bool eq = valid && key == prefix;
         const uint64_t eq_mask = __ballot(eq);
         const int eq_before = __popcll(eq_mask & lanes_below(lane));
         const bool sel = gt || (eq && eq_seen + eq_before < krem);
         const uint64_t sel_mask = __ballot(sel);
         const int pos = base + __popcll(sel_mask & lanes_below(lane));
-        if (sel && pos < k) out[pos] = id_first + j;
+        if (sel && pos < k) out[pos] = id_first + j;  // exactly k are selected; the bound is a guard
         base += __popcll(sel_mask);
         eq_seen += __popcll(eq_mask);
     }
@@ -432,12 +472,12 @@ void launch_topk(const float *scores, int n_rows, int row_len, int col_first, in
                        n_cols, k, id_first, keep, keep_stride, keep_first)
     if (n_cols <= 4 * kWave) VSA_TOPK(4);
     else if (n_cols <= 8 * kWave) VSA_TOPK(8);
+    else if (n_cols <= 12 * kWave) VSA_TOPK(12);
     else if (n_cols <= 16 * kWave) VSA_TOPK(16);
+    else if (n_cols <= 24 * kWave) VSA_TOPK(24);
     else if (n_cols <= 32 * kWave) VSA_TOPK(32);
-    else if (n_cols <= 64 * kWave) VSA_TOPK(64);
-    else if (n_cols <= 96 * kWave) VSA_TOPK(96);
     else
-        hipLaunchKernelGGL(topk_stream_kernel, grid, block, 0, st, scores, n_rows, row_len, col_first,
+        hipLaunchKernelGGL(topk_radix_kernel, grid, block, 0, st, scores, n_rows, row_len, col_first,
                            n_cols, k, id_first, keep, keep_stride, keep_first);
 #undef VSA_TOPK
 }
