@@ -436,6 +436,8 @@ __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) O[db][qb][e] = 0.f;
+    // Two chunks per iteration keep twice the partial loads in flight.
+#pragma unroll 2
     for (int c = 0; c < C; ++c) {
         const float *pml = a.part_ml + (p0 + c) * 128;
         float w[2];
