@@ -73,6 +73,10 @@ def _load():
     lib.orc_fine_tokens_lists.argtypes = [_U16P, _U16P, _U16P, i32, i32, i32, _I32P, _I32P, i32,
                                           i32, _I32P, i32, f64, _I64P, i64, _F64P]
     lib.orc_fine_tokens_lists.restype = ctypes.c_int
+    lib.orc_layer_bwd.argtypes = [_U16P, _U16P, _U16P, _U16P, _U16P, i32, i32, i32, _I32P, _I32P,
+                                  _I32P, i32, i32, _I32P, _I32P, _F32P, _F32P, _F32P, f64, _F64P,
+                                  _F64P, _F64P, _F64P]
+    lib.orc_layer_bwd.restype = ctypes.c_int
     lib.orc_combine.argtypes = [_F64P, _U16P, _F64P, i64, i32, _U16P]
     lib.orc_combine.restype = None
     lib.orc_gate_proj.argtypes = [_U16P, _U16P, i32, i32, _I64P, i64, _U16P]
@@ -333,6 +337,51 @@ def layer_tokens_ref(Q, K, V, g: np.ndarray, h: int, pl: Plan, hr: "HeadResult",
     tiles = pl.untile[toks] // pl.B
     g_rows = (g if g_is_rows else g[toks])[:, h * D:(h + 1) * D]
     return combine(o_fine, np.ascontiguousarray(g_rows), hr.o_coarse[tiles]), o_fine
+
+
+# ---------------------------------------------------------------- backward --
+
+def key_lists_default(pl: Plan, keep_h: np.ndarray):
+    """CSR key lists (off [n_t+1], ids) of the default mode for one head: prefix query
+    tiles see every tile; video query tile P+i sees [0, P) and keep_h[i]."""
+    lists = []
+    for i in range(pl.n_t):
+        if i < pl.P:
+            lists.append(np.arange(pl.n_t, dtype=np.int32))
+        else:
+            lists.append(np.concatenate([np.arange(pl.P, dtype=np.int32),
+                                         np.asarray(keep_h[i - pl.P], dtype=np.int32)]))
+    return _csr(lists)
+
+
+def key_lists_explicit(lists_h: np.ndarray):
+    """CSR key lists from the reference-sparsity [n_t][L] lists of one head."""
+    return _csr([np.asarray(r, dtype=np.int32) for r in lists_h])
+
+
+def _csr(lists):
+    off = np.zeros(len(lists) + 1, dtype=np.int32)
+    off[1:] = np.cumsum([len(x) for x in lists])
+    ids = np.concatenate(lists).astype(np.int32) if off[-1] else np.zeros(1, np.int32)
+    return off, np.ascontiguousarray(ids)
+
+
+def layer_bwd(Q, K, V, G, dOut, h: int, pl: Plan, csr, scale: float):
+    """Gradients of the layer for head h: dict of fp64 [S][D] arrays dq, dk, dv, dg.
+    G is the bf16 gate [S][H*D]; dOut is bf16 [S][H][D]; csr = (off, ids) key lists."""
+    lib = _load()
+    S, H, D = Q.shape
+    qm, km, vm = (tile_means(X, h, pl) for X in (Q, K, V))
+    off, ids = csr
+    outs = {n: np.zeros((S, D), dtype=np.float64) for n in ("dq", "dk", "dv", "dg")}
+    rc = lib.orc_layer_bwd(*(np.ascontiguousarray(X).reshape(-1) for X in (Q, K, V, G, dOut)),
+                           H, D, int(h), pl.untile, pl.row_src, pl.block_len, pl.n_t, pl.B,
+                           np.ascontiguousarray(off), ids, qm.reshape(-1), km.reshape(-1),
+                           vm.reshape(-1), float(scale), outs["dq"].reshape(-1),
+                           outs["dk"].reshape(-1), outs["dv"].reshape(-1), outs["dg"].reshape(-1))
+    if rc != 0:
+        raise OracleError("backward: a query has an empty key list")
+    return outs
 
 
 # ------------------------------------------------------- the layer, in order --

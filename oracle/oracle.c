@@ -477,6 +477,172 @@ int orc_fine_tokens_lists(const uint16_t *Q, const uint16_t *K, const uint16_t *
     return bad ? -1 : 0;
 }
 
+/* ------------------------------------------------------ backward (NEXT) -- */
+/*
+ * Gradient of the layer for one head. The method is trainable ([SnackOnAI]
+ * "References": VSA trains end to end with its sparse kernel); the keep sets
+ * come from a top-k and are held fixed, as a selection has no gradient.
+ * Forward, for a real token t in tile i (fp64 throughout):
+ *   O_fine[t]  = sum_{u in keys(i)} softmax_u(scale q_t.k_u) v_u
+ *   O_c[i]     = sum_j softmax_j(scale qm_i.km_j) vm_j  over all n_t tiles,
+ *                qm/km/vm the tile means of the real rows
+ *   out[t]     = O_fine[t] + g[t] * O_c[i]   (elementwise)
+ * Given dout (bf16), this returns (all fp64 [S][D] for head h):
+ *   dg[t]  = dout[t] * O_c[i]
+ *   dq, dk, dv = fine-attention gradients (chain rule through both softmaxes)
+ *                plus the coarse path: dO_c[i] = sum_{t in i} dout[t] * g[t],
+ *                back through the tile softmax to dqm/dkm/dvm, and each real
+ *                row t of tile i receives dqm_i / n_i (the mean's derivative).
+ * Key lists are given per query tile in CSR form: tiles lst[off[i]..off[i+1]).
+ * The tile means are the fp32 canonical ones (orc_tile_means) read as fp64,
+ * the same values the forward uses. Returns 0, or -1 on an empty key list.
+ */
+int orc_layer_bwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const uint16_t *G,
+                  const uint16_t *dOut, int32_t H, int32_t D, int32_t h, const int32_t *untile,
+                  const int32_t *row_src, const int32_t *block_len, int32_t n_t, int32_t B,
+                  const int32_t *off, const int32_t *lst, const float *qm, const float *km,
+                  const float *vm, double scale, double *dq, double *dk, double *dv, double *dg)
+{
+    if (D > 256) return -1;
+    (void)untile;
+    int64_t n_rows = (int64_t)n_t * B;
+#define X(A, t, d) ((double)bf16_to_float((A)[((int64_t)(t) * H + h) * D + (d)]))
+#define GV(t, d) ((double)bf16_to_float(G[(int64_t)(t) * H * D + (int64_t)h * D + (d)]))
+    /* ---- coarse forward and its gradient inputs */
+    double *Pc = (double *)malloc(sizeof(double) * (size_t)n_t * (size_t)n_t);
+    double *Oc = (double *)calloc((size_t)n_t * (size_t)D, sizeof(double));
+    double *dOc = (double *)calloc((size_t)n_t * (size_t)D, sizeof(double));
+    double *dqm = (double *)calloc((size_t)n_t * (size_t)D, sizeof(double));
+    double *dkm = (double *)calloc((size_t)n_t * (size_t)D, sizeof(double));
+    double *dvm = (double *)calloc((size_t)n_t * (size_t)D, sizeof(double));
+    for (int32_t i = 0; i < n_t; ++i) {
+        double zmax = -INFINITY;
+        for (int32_t j = 0; j < n_t; ++j) {
+            double dot = 0.0;
+            for (int32_t d = 0; d < D; ++d) dot += (double)qm[(int64_t)i * D + d] * (double)km[(int64_t)j * D + d];
+            Pc[(int64_t)i * n_t + j] = scale * dot;
+            if (scale * dot > zmax) zmax = scale * dot;
+        }
+        double den = 0.0;
+        for (int32_t j = 0; j < n_t; ++j) {
+            double e = exp(Pc[(int64_t)i * n_t + j] - zmax);
+            Pc[(int64_t)i * n_t + j] = e;
+            den += e;
+        }
+        for (int32_t j = 0; j < n_t; ++j) {
+            Pc[(int64_t)i * n_t + j] /= den;
+            for (int32_t d = 0; d < D; ++d) Oc[(int64_t)i * D + d] += Pc[(int64_t)i * n_t + j] * (double)vm[(int64_t)j * D + d];
+        }
+    }
+    /* dg and dO_c */
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int32_t t = row_src[r];
+        if (t < 0) continue;
+        int32_t i = (int32_t)(r / B);
+        for (int32_t d = 0; d < D; ++d) {
+            double go = X(dOut, t, d);
+            dg[(int64_t)t * D + d] = go * Oc[(int64_t)i * D + d];
+            dOc[(int64_t)i * D + d] += go * GV(t, d);
+        }
+    }
+    /* coarse backward: dZ_ij = Pc_ij (dOc_i . vm_j - Dc_i) */
+    for (int32_t i = 0; i < n_t; ++i) {
+        double Dc = 0.0;
+        for (int32_t d = 0; d < D; ++d) Dc += dOc[(int64_t)i * D + d] * Oc[(int64_t)i * D + d];
+        for (int32_t j = 0; j < n_t; ++j) {
+            double p = Pc[(int64_t)i * n_t + j];
+            double dp = 0.0;
+            for (int32_t d = 0; d < D; ++d) dp += dOc[(int64_t)i * D + d] * (double)vm[(int64_t)j * D + d];
+            double dz = p * (dp - Dc);
+            for (int32_t d = 0; d < D; ++d) {
+                dqm[(int64_t)i * D + d] += scale * dz * (double)km[(int64_t)j * D + d];
+                dkm[(int64_t)j * D + d] += scale * dz * (double)qm[(int64_t)i * D + d];
+                dvm[(int64_t)j * D + d] += p * dOc[(int64_t)i * D + d];
+            }
+        }
+    }
+    /* ---- fine attention: the mean-pooling gradient first, then the fine part */
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int32_t t = row_src[r];
+        if (t < 0) continue;
+        int32_t i = (int32_t)(r / B);
+        double inv = 1.0 / (double)block_len[i];
+        for (int32_t d = 0; d < D; ++d) {
+            dq[(int64_t)t * D + d] = dqm[(int64_t)i * D + d] * inv;
+            dk[(int64_t)t * D + d] = dkm[(int64_t)i * D + d] * inv;
+            dv[(int64_t)t * D + d] = dvm[(int64_t)i * D + d] * inv;
+        }
+    }
+    int bad = 0;
+    /* per query token: softmax over its keys, O_fine, D_t, then dS */
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int32_t t = row_src[r];
+        if (t < 0) continue;
+        int32_t i = (int32_t)(r / B);
+        int64_t nk = 0;
+        for (int32_t a = off[i]; a < off[i + 1]; ++a) nk += block_len[lst[a]];
+        if (nk == 0) {
+            bad = 1;
+            continue;
+        }
+        double *z = (double *)malloc(sizeof(double) * (size_t)nk);
+        int32_t *u_of = (int32_t *)malloc(sizeof(int32_t) * (size_t)nk);
+        int64_t n = 0;
+        double zmax = -INFINITY;
+        for (int32_t a = off[i]; a < off[i + 1]; ++a) {
+            int32_t j = lst[a];
+            for (int32_t rr = 0; rr < B; ++rr) {
+                int32_t u = row_src[(int64_t)j * B + rr];
+                if (u < 0) continue;
+                double dot = 0.0;
+                for (int32_t d = 0; d < D; ++d) dot += X(Q, t, d) * X(K, u, d);
+                z[n] = scale * dot;
+                u_of[n] = u;
+                if (z[n] > zmax) zmax = z[n];
+                ++n;
+            }
+        }
+        double den = 0.0;
+        for (int64_t a = 0; a < n; ++a) {
+            z[a] = exp(z[a] - zmax);
+            den += z[a];
+        }
+        double o[256], go[256];
+        for (int32_t d = 0; d < D; ++d) {
+            o[d] = 0.0;
+            go[d] = X(dOut, t, d);
+        }
+        for (int64_t a = 0; a < n; ++a) {
+            z[a] /= den;
+            for (int32_t d = 0; d < D; ++d) o[d] += z[a] * X(V, u_of[a], d);
+        }
+        double Dt = 0.0;
+        for (int32_t d = 0; d < D; ++d) Dt += go[d] * o[d];
+        for (int64_t a = 0; a < n; ++a) {
+            int32_t u = u_of[a];
+            double dp = 0.0;
+            for (int32_t d = 0; d < D; ++d) dp += go[d] * X(V, u, d);
+            double ds = z[a] * (dp - Dt);
+            for (int32_t d = 0; d < D; ++d) {
+                dq[(int64_t)t * D + d] += scale * ds * X(K, u, d);
+                dk[(int64_t)u * D + d] += scale * ds * X(Q, t, d);
+                dv[(int64_t)u * D + d] += z[a] * go[d];
+            }
+        }
+        free(z);
+        free(u_of);
+    }
+#undef X
+#undef GV
+    free(Pc);
+    free(Oc);
+    free(dOc);
+    free(dqm);
+    free(dkm);
+    free(dvm);
+    return bad ? -1 : 0;
+}
+
 /* ----------------------------------------------------------- O8: combine -- */
 /*
  * Layer output for individual (token, head) rows: out = O_fine + g * O_coarse
