@@ -278,6 +278,53 @@ int vsa_sparse_attn_fwd_ref(const vsa_plan_info *info, const int32_t *row_src_de
                             const int32_t *keep_idx_dev, const float *o_coarse_dev,
                             const void *gate, void *out, void *stream);
 
+/* --------------------------------------------------------- backward -- */
+/*
+ * Backward pass: the gradient of the layer with the keep sets held fixed (a
+ * top-k selection has no gradient; [SnackOnAI] "References": VSA trains end
+ * to end). For each head and real token t of tile i, with the forward above:
+ *   dg[t]   = dout[t] * O_coarse[i];
+ *   dO_c[i] = sum_{t in i} dout[t] * g[t], back through the tile softmax to
+ *             the tile means, and each real row of tile i receives the
+ *             mean's share (gradient / block_len);
+ *   dq, dk, dv also receive the fine attention's gradient over the same key
+ *             lists (log-sum-exp recomputed; the softmax-gradient row term
+ *             D_t = dout[t] . (out[t] - g[t] * O_coarse[i]) uses the bf16
+ *             output, P and dS are rounded to bf16 for the matrix products).
+ *
+ * vsa_bwd_layout -- scratch regions (device, caller-owned, 256-byte aligned):
+ * fragment copies (V rows, K / Q / dO columns), per-row log-sum-exp and D_t,
+ * the coarse-path gradients, and the transposed key lists ([H][n_t][n_t]).
+ */
+typedef struct vsa_bwd_layout {
+    size_t vrow, kcol, qcol, docol, lse, dt, doc, dqm, dkm, dvm, lsec, dcc, tlist, tcount;
+    size_t total_bytes;
+} vsa_bwd_layout;
+
+int vsa_bwd_workspace_layout(const vsa_plan_info *info, int32_t heads, int32_t head_dim,
+                             vsa_bwd_layout *layout);
+
+/*
+ * vsa_sparse_attn_bwd -- enqueues the backward pass on `stream`.
+ * k_ref < 0: the default mode (keep_idx [H][n_v][k_gen] from vsa_coarse_topk);
+ * k_ref >= 0: reference sparsity (keep_idx [H][n_t][k_ref + k_gen] from
+ * vsa_coarse_topk_ref). q, k, v, out, dout: device bf16 [S][H][D]; gate:
+ * device bf16 [S][H*D]; workspace / keep_idx / o_coarse: as left by the
+ * coarse pass for the same inputs (the tiled K and the tile means are read).
+ * bwd_workspace: >= vsa_bwd_workspace_layout().total_bytes.
+ * dq, dk, dv: out device fp32 [S][H][D]; dgate: out device fp32 [S][H*D].
+ * Errors: as vsa_sparse_attn_fwd(_ref), plus VSA_ERR_ARG for a small
+ * backward workspace.
+ */
+int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row_src_dev,
+                        const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                        int32_t k_ref, int32_t k_gen, float scale, const void *q, const void *k,
+                        const void *v, const void *gate, const void *out, const void *dout,
+                        const void *workspace, size_t workspace_bytes,
+                        const int32_t *keep_idx_dev, const float *o_coarse_dev,
+                        void *bwd_workspace, size_t bwd_workspace_bytes, float *dq, float *dk,
+                        float *dv, float *dgate, void *stream);
+
 /*
  * vsa_set_split_chunks -- tuning override for the fine pass: split every key
  * list into `chunks` parts (1 = never split; 0 = automatic, the default).
@@ -313,7 +360,8 @@ int vsa_gate_proj(const void *x, const void *w_gate, int64_t rows, int32_t hidde
  *
  * vsa_timing_read -- for the kernel named `kernel` (one of "gate_gemm",
  * "gather_pool", "video_scores", "coarse_attn", "topk", "fine_attn",
- * "merge"), waits for the recorded launches since the last enable and returns
+ * "merge", "bwd_gather", "bwd_prep", "bwd_coarse", "bwd_tlist", "bwd_dq",
+ * "bwd_dkdv"), waits for the recorded launches since the last enable and returns
  * their number in *launches and their summed duration in *total_ms (host
  * pointers). Errors: VSA_ERR_ARG for a null pointer or an unknown name,
  * VSA_ERR_DEVICE if an event query fails.

@@ -33,10 +33,10 @@ EXPORTED = (
     "vsa_keep_count", "vsa_tile_pair_fraction", "vsa_workspace_layout", "vsa_coarse_topk",
     "vsa_sparse_attn_fwd", "vsa_gate_proj", "vsa_set_split_chunks", "vsa_timing_enable",
     "vsa_timing_read", "vsa_ref_keep_count", "vsa_tile_pair_fraction_ref", "vsa_coarse_topk_ref",
-    "vsa_sparse_attn_fwd_ref",
+    "vsa_sparse_attn_fwd_ref", "vsa_bwd_workspace_layout", "vsa_sparse_attn_bwd",
 )
 TIMED_KERNELS = ("gate_gemm", "gather_pool", "video_scores", "coarse_attn", "topk", "fine_attn",
-                 "merge")
+                 "merge", "bwd_gather", "bwd_prep", "bwd_coarse", "bwd_tlist", "bwd_dq", "bwd_dkdv")
 
 
 class VsaError(RuntimeError):
@@ -58,6 +58,12 @@ class vsa_ws_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("k_tiled", "v_tiled", "q_mean", "k_mean", "v_mean", "scores", "part_o",
                  "part_ml", "total_bytes")]
+
+
+class vsa_bwd_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("vrow", "kcol", "qcol", "docol", "lse", "dt", "doc", "dqm", "dkm", "dvm", "lsec",
+                 "dcc", "tlist", "tcount", "total_bytes")]
 
 
 def _load() -> ctypes.CDLL:
@@ -88,6 +94,9 @@ def _load() -> ctypes.CDLL:
                                  P, P, P], ctypes.c_int),
         "vsa_sparse_attn_fwd_ref": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, SZ, P, P, P, P,
                                      P], ctypes.c_int),
+        "vsa_bwd_workspace_layout": ([info_p, I32, I32, ctypes.POINTER(vsa_bwd_layout)], ctypes.c_int),
+        "vsa_sparse_attn_bwd": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, P, P, P, P, P, SZ, P, P,
+                                 P, SZ, P, P, P, P, P], ctypes.c_int),
         "vsa_timing_enable": ([I32], ctypes.c_int),
         "vsa_timing_read": ([ctypes.c_char_p, ctypes.POINTER(I32), ctypes.POINTER(F64)],
                             ctypes.c_int),
@@ -336,6 +345,45 @@ def vsa_sparse_attn_fwd_ref(info: vsa_plan_info, row_src_dev: torch.Tensor,
            "vsa_sparse_attn_fwd_ref")
 
 
+def vsa_bwd_workspace_layout(info: vsa_plan_info, heads: int, head_dim: int) -> vsa_bwd_layout:
+    lay = vsa_bwd_layout()
+    _check(_lib.vsa_bwd_workspace_layout(ctypes.byref(info), int(heads), int(head_dim),
+                                         ctypes.byref(lay)), "vsa_bwd_workspace_layout")
+    return lay
+
+
+def vsa_sparse_attn_bwd(info: vsa_plan_info, row_src_dev: torch.Tensor, block_len_dev: torch.Tensor,
+                        heads: int, head_dim: int, k_ref: int, k_gen: int, q, k, v, gate, out, dout,
+                        workspace: torch.Tensor, keep_idx: Optional[torch.Tensor],
+                        o_coarse: torch.Tensor, bwd_workspace: torch.Tensor, dq, dk, dv, dgate,
+                        scale: float = 0.0, stream=None) -> None:
+    """Backward pass (k_ref < 0: default mode). Gradients are fp32."""
+    S = info.rows_real
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, (S, heads, head_dim))
+    _need(gate, "gate", torch.bfloat16)
+    if gate.numel() != S * heads * head_dim:
+        raise ValueError("gate must hold [S][heads*head_dim] values")
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, n, torch.float32, (S, heads, head_dim))
+    _need(dgate, "dgate", torch.float32)
+    if dgate.numel() != S * heads * head_dim:
+        raise ValueError("dgate must hold [S][heads*head_dim] values")
+    _need(row_src_dev, "row_src", torch.int32, (info.rows_padded,))
+    _need(block_len_dev, "block_len", torch.int32, (info.n_tiles,))
+    _need(workspace, "workspace", torch.uint8)
+    _need(bwd_workspace, "bwd_workspace", torch.uint8)
+    _need(o_coarse, "o_coarse", torch.float32, (heads, info.n_tiles, head_dim))
+    if keep_idx is not None:
+        _need(keep_idx, "keep_idx", torch.int32)
+    _check(_lib.vsa_sparse_attn_bwd(
+        ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev), heads, head_dim, int(k_ref),
+        int(k_gen), float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(out), _ptr(dout),
+        _ptr(workspace), workspace.numel(), _ptr(keep_idx), _ptr(o_coarse), _ptr(bwd_workspace),
+        bwd_workspace.numel(), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate), _stream(stream)),
+        "vsa_sparse_attn_bwd")
+
+
 def vsa_gate_proj(x: torch.Tensor, w_gate: torch.Tensor, g: torch.Tensor, stream=None) -> None:
     _need(x, "x", torch.bfloat16)
     _need(w_gate, "w_gate", torch.bfloat16)
@@ -443,6 +491,23 @@ class TileSparseAttention:
             vsa_sparse_attn_fwd(self.plan.info, self.row_src, self.block_len, self.heads,
                                 self.head_dim, self.k, q, self.workspace, keep, self.o_coarse,
                                 gate, out, scale=self.scale, stream=stream)
+
+    def backward(self, q, k, v, gate, out, dout, stream=None):
+        """Gradients (dq, dk, dv, dgate), fp32, of the last forward's layer with its
+        keep sets held fixed. Call after coarse() and fine() on the same inputs."""
+        if not hasattr(self, "bwd_workspace"):
+            lay = vsa_bwd_workspace_layout(self.plan.info, self.heads, self.head_dim)
+            self.bwd_layout = lay
+            self.bwd_workspace = torch.empty(lay.total_bytes, dtype=torch.uint8, device=q.device)
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+        dgate = torch.empty(gate.shape, dtype=torch.float32, device=q.device)
+        keep = self.keep_idx if self.list_len > 0 else None
+        vsa_sparse_attn_bwd(self.plan.info, self.row_src, self.block_len, self.heads, self.head_dim,
+                            self.k_ref if self.ref else -1, self.k, q, k, v, gate, out, dout,
+                            self.workspace, keep, self.o_coarse, self.bwd_workspace, dq, dk, dv,
+                            dgate, scale=self.scale, stream=stream)
+        return dq, dk, dv, dgate
 
     def tile_pair_fraction(self) -> float:
         if self.ref:

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvsa.so")
-SOURCES = ["plan.cpp", "timing.cpp", "coarse.hip", "fine.hip", "gemm.hip"]
+SOURCES = ["plan.cpp", "timing.cpp", "coarse.hip", "fine.hip", "gemm.hip", "backward.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -33,6 +33,7 @@ HIPCC_FLAGS = [
 # operations need no NaN-quieting canonicalisation.
 PER_SOURCE = {
     "fine.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+    "backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

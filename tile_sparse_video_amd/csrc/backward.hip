@@ -1,0 +1,930 @@
+// Backward pass of gated, tile-sparse video attention on gfx950: the gradient
+// of the layer with respect to Q, K, V and the gate, with the keep sets held
+// fixed (a top-k selection has no gradient).
+//
+// Method: SnackOnAI analysis of ComfyUI-Ref2VA-VSA, "References" (VSA trains
+// end to end with its sparse kernel) and "The Code, Annotated", snippet two
+// (the forward being differentiated: sink prefix tiles, block_len masking,
+// scale = D^-1/2); the Veda news item's reference_sparsity input for the
+// explicit-list variant.
+//
+// Forward, per head, for a real token t of tile i:
+//   O_fine[t] = sum_{u in keys(i)} softmax_u(scale q_t.k_u) v_u
+//   O_c[i]    = sum_j softmax_j(scale qm_i.km_j) vm_j   (tile means, all tiles)
+//   out[t]    = O_fine[t] + g[t] * O_c[i]
+// Kernels, in launch order:
+//   frag_gather  -- V in the row-fragment layout, K / Q / dO in the
+//                   column-fragment layout (the two MFMA operand layouts of
+//                   the forward's K and V copies), tile order, padding zero;
+//   bwd_prep     -- dg = dout * O_c, D_t = dout . (out - g * O_c) (the
+//                   softmax-gradient row term, from the bf16 output), and
+//                   dO_c[i] = sum_{t in i} dout * g;
+//   coarse_bwd   -- the tile-level attention's gradient to the tile means
+//                   (fp32, rows then columns);
+//   tlist        -- for every key tile, the ascending list of query tiles
+//                   whose key list holds it (the transpose of the keep sets);
+//   dq           -- query-major: the fine softmax statistics (log-sum-exp),
+//                   then dQ = scale dS K over the tile's key list, plus the
+//                   mean's share dqm / n;
+//   dkdv         -- key-major over the transposed lists: dV = P^T dO,
+//                   dK = scale dS^T Q, plus dkm / n and dvm / n.
+// S, dP, dV and dK run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation,
+// P and dS rounded to bf16 as the forward rounds P.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "common.h"
+#include "device.h"
+
+namespace vsa {
+namespace {
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource word 3, 32-bit data (gfx9 family)
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+// Packs fp32 values a[8 cc .. 8 cc + 7] into the bf16 B operand of one 16-row
+// chunk (the accumulator-to-operand order the forward uses for P).
+__device__ __forceinline__ bf16x8_t pack8(const f32x16_t &a, int cc)
+{
+    u32x4_t w;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const bf16x2_t pp = {(__bf16)a[8 * cc + e], (__bf16)a[8 * cc + e + 1]};
+        w[e / 2] = __builtin_bit_cast(uint32_t, pp);
+    }
+    return as_bf16x8(w);
+}
+
+// ----------------------------------------------------------- frag_gather --
+//
+// One block per (tile, group of 256/D heads). ROWS = 1: row layout, fragment
+// f = kb*(D/16) + c holds row 32kb + l32, d = 16c + 8*half + e. ROWS = 0:
+// column layout, fragment f = db*4 + c holds d = 32db + l32, rows 16c +
+// {4h..4h+3, 8+4h..8+4h+3}. The same two layouts the coarse stage writes for K
+// and V.
+template <int D, int B, int ROWS>
+__global__ __launch_bounds__(256) void frag_gather_kernel(const uint16_t *__restrict__ X,
+                                                         const int32_t *__restrict__ row_src,
+                                                         const int32_t *__restrict__ block_len,
+                                                         int H, int n_t, uint16_t *__restrict__ dst)
+{
+    constexpr int HPB = 256 / D, ROW = HPB * D + 8, CH = HPB * D / 8, FR = D / 8, SUB = B / 64;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[B * ROW];
+    __shared__ int32_t toks[B];
+    const int tile = blockIdx.x, h0 = blockIdx.y * HPB, tid = threadIdx.x;
+    const int nh = min(HPB, H - h0), n = block_len[tile];
+    if (tid < B) toks[tid] = row_src[size_t(tile) * B + tid];
+    __syncthreads();
+    for (int idx = tid; idx < B * CH; idx += 256) {
+        const int r = idx / CH, c = idx % CH;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (r < n && c / (D / 8) < nh)
+            val = *reinterpret_cast<const uint4 *>(X + (size_t(toks[r]) * H + h0) * D + c * 8);
+        *reinterpret_cast<uint4 *>(&lds[r * ROW + c * 8]) = val;
+    }
+    __syncthreads();
+    const int total = nh * SUB * FR * kWave;
+    for (int idx = tid; idx < total; idx += 256) {
+        const int lane = idx % kWave, f = (idx / kWave) % FR;
+        const int sub = (idx / (kWave * FR)) % SUB, hl = idx / (kWave * FR * SUB);
+        const int half = lane / 32, l32 = lane % 32;
+        uint16_t e8[8];
+        if (ROWS) {
+            const int kb = f / (D / 16), c = f % (D / 16);
+            const uint16_t *src = &lds[(64 * sub + 32 * kb + l32) * ROW + hl * D + 16 * c + 8 * half];
+            *reinterpret_cast<uint4 *>(e8) = *reinterpret_cast<const uint4 *>(src);
+        } else {
+            const int db = f / 4, c = f % 4;
+            const int col = hl * D + 32 * db + l32, r0 = 64 * sub + 16 * c + 4 * half;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                e8[e] = lds[(r0 + e) * ROW + col];
+                e8[4 + e] = lds[(r0 + 8 + e) * ROW + col];
+            }
+        }
+        const size_t frag = ((size_t(h0 + hl) * n_t + tile) * SUB + sub) * FR + f;
+        *reinterpret_cast<uint4 *>(dst + frag * 512 + lane * 8) = *reinterpret_cast<uint4 *>(e8);
+    }
+}
+
+// -------------------------------------------------------------- bwd_prep --
+//
+// One block (4 waves) per (tile, head); wave w takes the tile's real rows
+// w, w+4, ...; lane owns d = lane + 64p. Writes dg (fp32, natural order),
+// D_t (fp32 [H][S_pad], tile order; zero on padding rows) and dO_c.
+template <int D, int B>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t *__restrict__ dout,
+                                                      const uint16_t *__restrict__ out,
+                                                      const uint16_t *__restrict__ gate,
+                                                      const float *__restrict__ o_coarse,
+                                                      const int32_t *__restrict__ row_src,
+                                                      const int32_t *__restrict__ block_len, int H,
+                                                      int n_t, float *__restrict__ dgate,
+                                                      float *__restrict__ dt, float *__restrict__ doc)
+{
+    constexpr int PL = D / kWave;
+    __shared__ float red[4][D];
+    const int tile = blockIdx.x, h = blockIdx.y;
+    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int n = block_len[tile];
+    const size_t S_pad = size_t(n_t) * B;
+    float oc[PL], acc[PL];
+#pragma unroll
+    for (int p = 0; p < PL; ++p) {
+        oc[p] = o_coarse[(size_t(h) * n_t + tile) * D + lane + kWave * p];
+        acc[p] = 0.f;
+    }
+    for (int r = w; r < B; r += 4) {
+        float dsum = 0.f;
+        if (r < n) {
+            const int t = row_src[size_t(tile) * B + r];
+            const size_t base = (size_t(t) * H + h) * D;
+#pragma unroll
+            for (int p = 0; p < PL; ++p) {
+                const int d = lane + kWave * p;
+                const float go = bf16_to_f32(dout[base + d]);
+                const float o = bf16_to_f32(out[base + d]);
+                const float g = bf16_to_f32(gate[base + d]);
+                dgate[base + d] = go * oc[p];
+                dsum += go * (o - g * oc[p]);
+                acc[p] += go * g;
+            }
+        }
+        dsum = wave_sum(dsum);
+        if (lane == 0) dt[size_t(h) * S_pad + size_t(tile) * B + r] = dsum;
+    }
+#pragma unroll
+    for (int p = 0; p < PL; ++p) red[w][lane + kWave * p] = acc[p];
+    __syncthreads();
+    for (int d = threadIdx.x; d < D; d += 256)
+        doc[(size_t(h) * n_t + tile) * D + d] = red[0][d] + red[1][d] + red[2][d] + red[3][d];
+}
+
+// ------------------------------------------------------------ coarse_bwd --
+//
+// Tile-level attention gradient, fp32, natural-log softmax (as the forward).
+// Rows: block per (64 query tiles, head); four threads per query tile, each
+// owning D/4 of the dimension; key tiles stream through LDS in chunks of 32.
+// Writes the row log-sum-exp, Dc_i = dO_c[i] . O_c[i] and dqm_i.
+template <int D>
+__global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const float *__restrict__ qm,
+                                                             const float *__restrict__ km,
+                                                             const float *__restrict__ vm,
+                                                             const float *__restrict__ o_coarse,
+                                                             const float *__restrict__ doc, int n_t,
+                                                             float scale, float *__restrict__ lsec,
+                                                             float *__restrict__ dcc,
+                                                             float *__restrict__ dqm)
+{
+    constexpr int DQ = D / 4, KC = 32;
+    __shared__ float ks[KC][D], vs[KC][D];
+    const int h = blockIdx.y, tid = threadIdx.x;
+    const int i = blockIdx.x * 64 + tid / 4, part = tid % 4;
+    const bool live = i < n_t;
+    const size_t rowoff = (size_t(h) * n_t + (live ? i : 0)) * D + part * DQ;
+    float q[DQ], g[DQ], acc[DQ];
+    float dc = 0.f;
+#pragma unroll
+    for (int d = 0; d < DQ; ++d) {
+        q[d] = qm[rowoff + d];
+        g[d] = doc[rowoff + d];
+        dc += g[d] * o_coarse[rowoff + d];
+        acc[d] = 0.f;
+    }
+    dc += __shfl_xor(dc, 1);
+    dc += __shfl_xor(dc, 2);
+    const float *kh = km + size_t(h) * n_t * D, *vh = vm + size_t(h) * n_t * D;
+    // pass 1: log-sum-exp over all key tiles
+    float mx = -INFINITY, sum = 0.f;
+    for (int j0 = 0; j0 < n_t; j0 += KC) {
+        __syncthreads();
+        for (int idx = tid; idx < KC * D; idx += 256) {
+            const int r = idx / D, d = idx % D;
+            ks[r][d] = j0 + r < n_t ? kh[size_t(j0 + r) * D + d] : 0.f;
+        }
+        __syncthreads();
+        const int nj = min(KC, n_t - j0);
+        for (int r = 0; r < nj; ++r) {
+            float z = 0.f;
+#pragma unroll
+            for (int d = 0; d < DQ; ++d) z += q[d] * ks[r][part * DQ + d];
+            z += __shfl_xor(z, 1);
+            z += __shfl_xor(z, 2);
+            z *= scale;
+            if (z > mx) {
+                sum = sum * expf(mx - z) + 1.f;
+                mx = z;
+            } else {
+                sum += expf(z - mx);
+            }
+        }
+    }
+    const float lse = mx + logf(sum);
+    // pass 2: dZ_ij = P_ij (dO_c[i] . vm_j - Dc_i); dqm_i = scale sum_j dZ_ij km_j
+    for (int j0 = 0; j0 < n_t; j0 += KC) {
+        __syncthreads();
+        for (int idx = tid; idx < KC * D; idx += 256) {
+            const int r = idx / D, d = idx % D;
+            const bool in = j0 + r < n_t;
+            ks[r][d] = in ? kh[size_t(j0 + r) * D + d] : 0.f;
+            vs[r][d] = in ? vh[size_t(j0 + r) * D + d] : 0.f;
+        }
+        __syncthreads();
+        const int nj = min(KC, n_t - j0);
+        for (int r = 0; r < nj; ++r) {
+            float z = 0.f, dp = 0.f;
+#pragma unroll
+            for (int d = 0; d < DQ; ++d) {
+                z += q[d] * ks[r][part * DQ + d];
+                dp += g[d] * vs[r][part * DQ + d];
+            }
+            z += __shfl_xor(z, 1);
+            z += __shfl_xor(z, 2);
+            dp += __shfl_xor(dp, 1);
+            dp += __shfl_xor(dp, 2);
+            const float p = expf(z * scale - lse);
+            const float dz = p * (dp - dc) * scale;
+#pragma unroll
+            for (int d = 0; d < DQ; ++d) acc[d] += dz * ks[r][part * DQ + d];
+        }
+    }
+    if (!live) return;
+#pragma unroll
+    for (int d = 0; d < DQ; ++d) dqm[rowoff + d] = acc[d];
+    if (part == 0) {
+        lsec[size_t(h) * n_t + i] = lse;
+        dcc[size_t(h) * n_t + i] = dc;
+    }
+}
+
+// Columns: block per (64 key tiles, head); query tiles stream through LDS.
+// dkm_j = scale sum_i dZ_ij qm_i, dvm_j = sum_i P_ij dO_c[i].
+template <int D>
+__global__ __launch_bounds__(256) void coarse_bwd_cols_kernel(const float *__restrict__ qm,
+                                                             const float *__restrict__ km,
+                                                             const float *__restrict__ vm,
+                                                             const float *__restrict__ doc,
+                                                             const float *__restrict__ lsec,
+                                                             const float *__restrict__ dcc, int n_t,
+                                                             float scale, float *__restrict__ dkm,
+                                                             float *__restrict__ dvm)
+{
+    constexpr int DQ = D / 4, QC = 32;
+    __shared__ float qs[QC][D], gs[QC][D];
+    __shared__ float ls[QC], cs[QC];
+    const int h = blockIdx.y, tid = threadIdx.x;
+    const int j = blockIdx.x * 64 + tid / 4, part = tid % 4;
+    const bool live = j < n_t;
+    const size_t rowoff = (size_t(h) * n_t + (live ? j : 0)) * D + part * DQ;
+    float k[DQ], v[DQ], ak[DQ], av[DQ];
+#pragma unroll
+    for (int d = 0; d < DQ; ++d) {
+        k[d] = km[rowoff + d];
+        v[d] = vm[rowoff + d];
+        ak[d] = av[d] = 0.f;
+    }
+    const float *qh = qm + size_t(h) * n_t * D, *gh = doc + size_t(h) * n_t * D;
+    for (int i0 = 0; i0 < n_t; i0 += QC) {
+        __syncthreads();
+        for (int idx = tid; idx < QC * D; idx += 256) {
+            const int r = idx / D, d = idx % D;
+            const bool in = i0 + r < n_t;
+            qs[r][d] = in ? qh[size_t(i0 + r) * D + d] : 0.f;
+            gs[r][d] = in ? gh[size_t(i0 + r) * D + d] : 0.f;
+        }
+        if (tid < QC) {
+            const bool in = i0 + tid < n_t;
+            ls[tid] = in ? lsec[size_t(h) * n_t + i0 + tid] : 0.f;
+            cs[tid] = in ? dcc[size_t(h) * n_t + i0 + tid] : 0.f;
+        }
+        __syncthreads();
+        const int ni = min(QC, n_t - i0);
+        for (int r = 0; r < ni; ++r) {
+            float z = 0.f, dp = 0.f;
+#pragma unroll
+            for (int d = 0; d < DQ; ++d) {
+                z += qs[r][part * DQ + d] * k[d];
+                dp += gs[r][part * DQ + d] * v[d];
+            }
+            z += __shfl_xor(z, 1);
+            z += __shfl_xor(z, 2);
+            dp += __shfl_xor(dp, 1);
+            dp += __shfl_xor(dp, 2);
+            const float p = expf(z * scale - ls[r]);
+            const float dz = p * (dp - cs[r]) * scale;
+#pragma unroll
+            for (int d = 0; d < DQ; ++d) {
+                ak[d] += dz * qs[r][part * DQ + d];
+                av[d] += p * gs[r][part * DQ + d];
+            }
+        }
+    }
+    if (!live) return;
+#pragma unroll
+    for (int d = 0; d < DQ; ++d) {
+        dkm[rowoff + d] = ak[d];
+        dvm[rowoff + d] = av[d];
+    }
+}
+
+// ----------------------------------------------------------------- tlist --
+//
+// One wavefront per (key tile j, head): scans the query tiles in ascending
+// order and keeps those whose key list holds j (binary search in the sorted
+// keep row), compacting with ballots, so each list is ascending and the
+// result is deterministic.
+__device__ __forceinline__ bool sorted_has(const int32_t *row, int len, int j)
+{
+    int lo = 0, hi = len;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (row[mid] < j) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo < len && row[lo] == j;
+}
+
+__global__ __launch_bounds__(256) void tlist_kernel(const int32_t *__restrict__ keep, int ref, int P,
+                                                    int n_v, int n_t, int k, int list_len,
+                                                    int32_t *__restrict__ tlist,
+                                                    int32_t *__restrict__ tcount)
+{
+    const int h = blockIdx.y;
+    const int j = blockIdx.x * 4 + threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    if (j >= n_t) return;
+    int32_t *dst = tlist + (size_t(h) * n_t + j) * n_t;
+    int count = 0;
+    for (int i0 = 0; i0 < n_t; i0 += kWave) {
+        const int i = i0 + lane;
+        bool has = false;
+        if (i < n_t) {
+            if (ref) has = sorted_has(keep + (size_t(h) * n_t + i) * list_len, list_len, j);
+            else has = i < P || j < P || sorted_has(keep + (size_t(h) * n_v + (i - P)) * k, k, j);
+        }
+        const uint64_t m = __ballot(has);
+        if (has) dst[count + __popcll(m & lanes_below(lane))] = i;
+        count += __popcll(m);
+    }
+    if (lane == 0) tcount[size_t(h) * n_t + j] = count;
+}
+
+struct BwdArgs {
+    const uint16_t *q, *dout;       // natural [S][H][D]
+    const uint16_t *kt, *vt;        // forward workspace: K row fragments, V column fragments
+    const uint16_t *vrow, *kcol;    // V row fragments, K column fragments
+    const uint16_t *qcol, *docol;   // Q and dO column fragments
+    const uint16_t *kn, *vn;        // natural K and V
+    const int32_t *row_src, *block_len, *keep;
+    const int32_t *tlist, *tcount;
+    const float *dt;                // [H][S_pad]
+    float *lse;                     // [H][S_pad], log2 domain (+inf on padding rows)
+    const float *dqm, *dkm, *dvm;   // [H][n_t][D]
+    float *dq, *dk, *dv;            // natural [S][H][D]
+    int H, P, n_v, n_t, k, ref, list_len;
+    float scale, scale_log2e;
+};
+
+// -------------------------------------------------------------------- dq --
+//
+// One wavefront per (head, 64 query rows), as the forward: Q and dO fragments
+// staged in LDS, K / V / K^T fragments streamed as 1 KB coalesced buffer loads
+// per 32-key half. Pass 1 forms S^T = K Q^T and the per-query log-sum-exp
+// (written for the key-major kernel); pass 2 forms S^T, P^T, dP^T = V dO^T,
+// dS^T = P^T (dP^T - D) and dQ^T += K^T dS^T.
+template <int D, int B>
+__global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
+{
+    constexpr int SUB = B / 64, NC = D / 16, DB = D / 32, FR = D / 8, HPU = 2 * SUB;
+    constexpr int kListCap = 896;
+    const int lane = threadIdx.x, l32 = lane & 31, half = lane >> 5;
+    const int per_head = a.n_t * SUB;
+    const int item = blockIdx.x, h = item / per_head, r = item % per_head;
+    const int tile = r / SUB, qsub = r % SUB;
+    const bool dense = !a.ref && tile < a.P;
+    const int n_list = a.ref ? a.list_len : dense ? a.n_t : a.P + a.k;
+    const size_t S_pad = size_t(a.n_t) * B;
+
+    __shared__ __attribute__((aligned(16))) bf16x8_t q_lds[2][NC][kWave];
+    __shared__ __attribute__((aligned(16))) bf16x8_t o_lds[2][NC][kWave];
+    __shared__ uint32_t list_lds[kListCap];
+    int tok[2];
+    float dq_row[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int row = tile * B + 64 * qsub + 32 * qb + l32;
+        tok[qb] = a.row_src[row];
+        dq_row[qb] = a.dt[size_t(h) * S_pad + row];
+        const size_t base = (size_t(tok[qb] < 0 ? 0 : tok[qb]) * a.H + h) * D + 8 * half;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            bf16x8_t vq = *reinterpret_cast<const bf16x8_t *>(a.q + base + 16 * c);
+            bf16x8_t vo = *reinterpret_cast<const bf16x8_t *>(a.dout + base + 16 * c);
+            if (tok[qb] < 0) vq = vo = bf16x8_t{};
+            q_lds[qb][c][lane] = vq;
+            o_lds[qb][c][lane] = vo;
+        }
+    }
+    const int32_t *keep_row = a.ref ? a.keep + (size_t(h) * a.n_t + tile) * a.list_len
+                              : dense ? a.keep
+                                      : a.keep + (size_t(h) * a.n_v + (tile - a.P)) * a.k;
+    auto tile_at = [&](int n) -> int {
+        if (a.ref) return min(max(keep_row[n], 0), a.n_t - 1);
+        return (dense || n < a.P) ? n : min(max(keep_row[n - a.P], 0), a.n_t - 1);
+    };
+    const uint32_t head_bytes = uint32_t(a.n_t) * B * D * 2;
+    const size_t head_elems = size_t(h) * a.n_t * B * D;
+    auto rsrc = [&](const uint16_t *p) {
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(p + head_elems), (short)0, head_bytes, kRsrcWord3);
+    };
+    const __amdgpu_buffer_rsrc_t rk = rsrc(a.kt), rvr = rsrc(a.vrow), rkc = rsrc(a.kcol);
+    const int vlane = lane * 16;
+    const float c2 = a.scale_log2e;
+
+    // Walks the key list in segments staged in LDS; body(v, entry) per half.
+    auto walk = [&](auto &&body) {
+        int scan = 0;
+        while (true) {
+            int count = 0;
+            while (scan < n_list) {
+                const int n = scan + lane;
+                const int t = n < n_list ? tile_at(n) : -1;
+                const uint64_t mask = __ballot(t >= 0);
+                const int take = __popcll(mask);
+                if (count + take > kListCap) break;
+                if (t >= 0) list_lds[count + __popcll(mask & lanes_below(lane))] = uint32_t(t) | uint32_t(a.block_len[t] - 1) << 25;
+                count += take;
+                scan += kWave;
+            }
+            __syncthreads();
+            for (int v = 0; v < count * HPU; ++v) body(v, __builtin_amdgcn_readfirstlane(list_lds[v / HPU]));
+            if (scan >= n_list) break;
+            __syncthreads();
+        }
+    };
+    auto half_base = [&](int v, uint32_t ent) -> uint32_t {
+        return ((ent & 0x1ffffffu) * SUB + uint32_t((v % HPU) >> 1)) * FR * 1024u;
+    };
+    // A . B^T with A = 32 key rows (fragments in registers) and B = the Q (or dO)
+    // rows of query block qb from LDS; the lane index is made opaque so the LDS
+    // operands are re-read rather than hoisted into VGPRs.
+    auto s_block = [&](int qb, const u32x4_t (&Kb)[NC], bool use_do) {
+        int ql = lane;
+        asm volatile("" : "+v"(ql));
+        f32x16_t S = f32x16_t{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const bf16x8_t bq = use_do ? o_lds[qb][c][ql] : q_lds[qb][c][ql];
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Kb[c]), bq, S, 0, 0, 0);
+        }
+        return S;
+    };
+    auto mask_pad = [&](f32x16_t &S, int real) {
+        if (real < 32) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (8 * i + 4 * half + j >= real) S[4 * i + j] = -INFINITY;
+        }
+    };
+
+    // ---- pass 1: log-sum-exp (log2 domain) of every query row
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    walk([&](int v, uint32_t ent) {
+        const int real = min(32, int(ent >> 25) + 1 - 32 * (v % HPU));
+        const uint32_t base = half_base(v, ent) + uint32_t(v & 1) * NC * 1024u;
+        u32x4_t Kb[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) Kb[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, vlane, base + c * 1024u, 0);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            f32x16_t S = s_block(qb, Kb, false);
+            mask_pad(S, real);
+            float mx = S[0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) mx = fmaxf(mx, S[e]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mn = fmaxf(m[qb], mx);
+            if (mn > -INFINITY) {
+                float s = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) s += __builtin_amdgcn_exp2f((S[e] - mn) * c2);
+                s += __shfl_xor(s, 32);
+                l[qb] = l[qb] * (m[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m[qb] - mn) * c2)) + s;
+                m[qb] = mn;
+            }
+        }
+    });
+    float lse[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        lse[qb] = tok[qb] < 0 ? INFINITY : m[qb] * c2 + __log2f(l[qb]);
+        if (half == 0) a.lse[size_t(h) * S_pad + tile * B + 64 * qsub + 32 * qb + l32] = lse[qb];
+    }
+
+    // ---- pass 2: dQ^T = K^T dS^T
+    f32x16_t G[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) G[db][0] = G[db][1] = f32x16_t{};
+    walk([&](int v, uint32_t ent) {
+        const int real = min(32, int(ent >> 25) + 1 - 32 * (v % HPU));
+        const uint32_t hb = half_base(v, ent);
+        const uint32_t kbase = hb + uint32_t(v & 1) * NC * 1024u;
+        const uint32_t cbase = hb + uint32_t(v & 1) * 2 * 1024u;
+        u32x4_t Kb[NC], Vr[NC], Kc[2 * DB];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            Kb[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, vlane, kbase + c * 1024u, 0);
+            Vr[c] = __builtin_amdgcn_raw_buffer_load_b128(rvr, vlane, kbase + c * 1024u, 0);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+                Kc[2 * db + cc] = __builtin_amdgcn_raw_buffer_load_b128(rkc, vlane, cbase + (4 * db + cc) * 1024u, 0);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            f32x16_t S = s_block(qb, Kb, false);
+            mask_pad(S, real);
+            const f32x16_t dP = s_block(qb, Vr, true);
+            f32x16_t dS;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float p = __builtin_amdgcn_exp2f(S[e] * c2 - lse[qb]);
+                dS[e] = p * (dP[e] - dq_row[qb]);
+            }
+            const bf16x8_t d0 = pack8(dS, 0), d1 = pack8(dS, 1);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                G[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Kc[2 * db]), d0, G[db][qb], 0, 0, 0);
+                G[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Kc[2 * db + 1]), d1, G[db][qb], 0, 0, 0);
+            }
+        }
+    });
+
+    // ---- epilogue: dq = scale dQ_fine + dqm / n (fp32, natural order)
+    const float inv_n = 1.0f / float(a.block_len[tile]);
+    const float *gm = a.dqm + (size_t(h) * a.n_t + tile) * D;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        if (tok[qb] < 0) continue;
+        float *dst = a.dq + (size_t(tok[qb]) * a.H + h) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = 32 * db + 8 * i + 4 * half;
+                const float4 mm = *reinterpret_cast<const float4 *>(gm + d0);
+                float4 o;
+                o.x = a.scale * G[db][qb][4 * i] + mm.x * inv_n;
+                o.y = a.scale * G[db][qb][4 * i + 1] + mm.y * inv_n;
+                o.z = a.scale * G[db][qb][4 * i + 2] + mm.z * inv_n;
+                o.w = a.scale * G[db][qb][4 * i + 3] + mm.w * inv_n;
+                *reinterpret_cast<float4 *>(dst + d0) = o;
+            }
+    }
+}
+
+// ------------------------------------------------------------------ dkdv --
+//
+// One wavefront per (head, key tile, 32 key rows). The wave holds its keys'
+// K^T and V^T operand fragments (natural rows) and the dK^T, dV^T
+// accumulators (lane = key column), and walks the query tiles of the key
+// tile's transposed list, 32 query rows at a time:
+//   S = Q K^T, P = exp2(S c2 - lse), dP = dO V^T, dS = P (dP - D),
+//   dV^T += dO^T P, dK^T += Q^T dS.
+template <int D, int B>
+__global__ __launch_bounds__(64, 1) void dkdv_kernel(BwdArgs a)
+{
+    constexpr int SUB = B / 64, NC = D / 16, DB = D / 32, FR = D / 8, KB = B / 32;
+    const int lane = threadIdx.x, l32 = lane & 31, half = lane >> 5;
+    const int per_head = a.n_t * KB;
+    const int h = blockIdx.x / per_head, r = blockIdx.x % per_head;
+    const int tile = r / KB, kb = r % KB;
+    const size_t S_pad = size_t(a.n_t) * B;
+
+    // Own keys as B operands: lane -> key 32kb + l32 of the tile, slots d = 16c + 8 half + e.
+    const int krow = tile * B + 32 * kb + l32;
+    const int ktok = a.row_src[krow];
+    bf16x8_t Kt[NC], Vt[NC];
+    {
+        const size_t base = (size_t(ktok < 0 ? 0 : ktok) * a.H + h) * D + 8 * half;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            Kt[c] = *reinterpret_cast<const bf16x8_t *>(a.kn + base + 16 * c);
+            Vt[c] = *reinterpret_cast<const bf16x8_t *>(a.vn + base + 16 * c);
+            if (ktok < 0) Kt[c] = Vt[c] = bf16x8_t{};
+        }
+    }
+    f32x16_t GK[DB], GV[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) GK[db] = GV[db] = f32x16_t{};
+    const float c2 = a.scale_log2e;
+    const size_t head_frag = size_t(h) * a.n_t * SUB;  // 64-row blocks before this head
+
+    const int cnt = a.tcount[size_t(h) * a.n_t + tile];
+    const int32_t *lst = a.tlist + (size_t(h) * a.n_t + tile) * a.n_t;
+    for (int x = 0; x < cnt; ++x) {
+        const int qt = __builtin_amdgcn_readfirstlane(lst[x]);
+        for (int qs = 0; qs < SUB; ++qs) {
+            const size_t blk = (head_frag + size_t(qt) * SUB + qs) * FR;  // fragment index of the block
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int q0 = qt * B + 64 * qs + 32 * qb;  // first query row of this 32-row block
+                // A operands: query rows q0 + l32 (natural Q / dO rows), slots d.
+                const int qtok = a.row_src[q0 + l32];
+                const size_t qbase = (size_t(qtok < 0 ? 0 : qtok) * a.H + h) * D + 8 * half;
+                bf16x8_t Qr[NC], Or[NC];
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    Qr[c] = *reinterpret_cast<const bf16x8_t *>(a.q + qbase + 16 * c);
+                    Or[c] = *reinterpret_cast<const bf16x8_t *>(a.dout + qbase + 16 * c);
+                    if (qtok < 0) Qr[c] = Or[c] = bf16x8_t{};
+                }
+                // Row statistics of the accumulator rows 8i + 4 half + j.
+                float4 L4[4], D4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const size_t off = size_t(h) * S_pad + q0 + 8 * i + 4 * half;
+                    L4[i] = *reinterpret_cast<const float4 *>(a.lse + off);
+                    D4[i] = *reinterpret_cast<const float4 *>(a.dt + off);
+                }
+                f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qr[c], Kt[c], S, 0, 0, 0);
+                    dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Or[c], Vt[c], dP, 0, 0, 0);
+                }
+                f32x16_t Pm, dS;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float lv[4] = {L4[i].x, L4[i].y, L4[i].z, L4[i].w};
+                    const float dv[4] = {D4[i].x, D4[i].y, D4[i].z, D4[i].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float p = __builtin_amdgcn_exp2f(S[4 * i + j] * c2 - lv[j]);
+                        Pm[4 * i + j] = p;
+                        dS[4 * i + j] = p * (dP[4 * i + j] - dv[j]);
+                    }
+                }
+                const bf16x8_t p0 = pack8(Pm, 0), p1 = pack8(Pm, 1);
+                const bf16x8_t s0 = pack8(dS, 0), s1 = pack8(dS, 1);
+                // Column-fragment A operands of this 32-row block: chunks 2qb, 2qb+1.
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const size_t f0 = (blk + 4 * db + 2 * qb) * 512 + lane * 8;
+                    const bf16x8_t o0 = *reinterpret_cast<const bf16x8_t *>(a.docol + f0);
+                    const bf16x8_t o1 = *reinterpret_cast<const bf16x8_t *>(a.docol + f0 + 512);
+                    const bf16x8_t q0f = *reinterpret_cast<const bf16x8_t *>(a.qcol + f0);
+                    const bf16x8_t q1f = *reinterpret_cast<const bf16x8_t *>(a.qcol + f0 + 512);
+                    GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, p0, GV[db], 0, 0, 0);
+                    GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, p1, GV[db], 0, 0, 0);
+                    GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q0f, s0, GK[db], 0, 0, 0);
+                    GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q1f, s1, GK[db], 0, 0, 0);
+                }
+            }
+        }
+    }
+    if (ktok < 0) return;
+    // dk = scale dK_fine + dkm / n, dv = dV_fine + dvm / n; acc 4i + j <-> d = 32db + 8i + 4 half + j.
+    const float inv_n = 1.0f / float(a.block_len[tile]);
+    const float *gk = a.dkm + (size_t(h) * a.n_t + tile) * D;
+    const float *gv = a.dvm + (size_t(h) * a.n_t + tile) * D;
+    float *dk = a.dk + (size_t(ktok) * a.H + h) * D;
+    float *dv = a.dv + (size_t(ktok) * a.H + h) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 32 * db + 8 * i + 4 * half;
+            const float4 mk = *reinterpret_cast<const float4 *>(gk + d0);
+            const float4 mv = *reinterpret_cast<const float4 *>(gv + d0);
+            float4 ok, ov;
+            ok.x = a.scale * GK[db][4 * i] + mk.x * inv_n;
+            ok.y = a.scale * GK[db][4 * i + 1] + mk.y * inv_n;
+            ok.z = a.scale * GK[db][4 * i + 2] + mk.z * inv_n;
+            ok.w = a.scale * GK[db][4 * i + 3] + mk.w * inv_n;
+            ov.x = GV[db][4 * i] + mv.x * inv_n;
+            ov.y = GV[db][4 * i + 1] + mv.y * inv_n;
+            ov.z = GV[db][4 * i + 2] + mv.z * inv_n;
+            ov.w = GV[db][4 * i + 3] + mv.w * inv_n;
+            *reinterpret_cast<float4 *>(dk + d0) = ok;
+            *reinterpret_cast<float4 *>(dv + d0) = ov;
+        }
+}
+
+}  // namespace
+}  // namespace vsa
+
+namespace vsa {
+
+void compute_bwd_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_bwd_layout *L)
+{
+    const size_t H = size_t(heads), D = size_t(head_dim), n_t = size_t(info.n_tiles);
+    const size_t S_pad = size_t(info.rows_padded);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    L->vrow = take(H * S_pad * D * 2);
+    L->kcol = take(H * S_pad * D * 2);
+    L->qcol = take(H * S_pad * D * 2);
+    L->docol = take(H * S_pad * D * 2);
+    L->lse = take(H * S_pad * 4);
+    L->dt = take(H * S_pad * 4);
+    L->doc = take(H * n_t * D * 4);
+    L->dqm = take(H * n_t * D * 4);
+    L->dkm = take(H * n_t * D * 4);
+    L->dvm = take(H * n_t * D * 4);
+    L->lsec = take(H * n_t * 4);
+    L->dcc = take(H * n_t * 4);
+    L->tlist = take(H * n_t * n_t * 4);
+    L->tcount = take(H * n_t * 4);
+    L->total_bytes = off;
+}
+
+namespace {
+
+template <int D, int B>
+void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, const uint16_t *v,
+                const uint16_t *q, const uint16_t *dout, const uint16_t *out, const uint16_t *gate,
+                const float *o_coarse, const float *qm, const float *km, const float *vm,
+                const vsa_bwd_layout &L, char *bw, float *dgate, hipStream_t st)
+{
+    constexpr int HPB = 256 / D;
+    const int H = a.H, n_t = a.n_t;
+    const dim3 gg(n_t, (H + HPB - 1) / HPB);
+    {
+        KernelTimer t(K_BWD_GATHER, st);
+        hipLaunchKernelGGL((frag_gather_kernel<D, B, 1>), gg, dim3(256), 0, st, v, a.row_src, a.block_len,
+                           H, n_t, reinterpret_cast<uint16_t *>(bw + L.vrow));
+        hipLaunchKernelGGL((frag_gather_kernel<D, B, 0>), gg, dim3(256), 0, st, k, a.row_src, a.block_len,
+                           H, n_t, reinterpret_cast<uint16_t *>(bw + L.kcol));
+        hipLaunchKernelGGL((frag_gather_kernel<D, B, 0>), gg, dim3(256), 0, st, q, a.row_src, a.block_len,
+                           H, n_t, reinterpret_cast<uint16_t *>(bw + L.qcol));
+        hipLaunchKernelGGL((frag_gather_kernel<D, B, 0>), gg, dim3(256), 0, st, dout, a.row_src,
+                           a.block_len, H, n_t, reinterpret_cast<uint16_t *>(bw + L.docol));
+    }
+    auto *dt = reinterpret_cast<float *>(bw + L.dt);
+    auto *doc = reinterpret_cast<float *>(bw + L.doc);
+    {
+        KernelTimer t(K_BWD_PREP, st);
+        hipLaunchKernelGGL((bwd_prep_kernel<D, B>), dim3(n_t, H), dim3(256), 0, st, dout, out, gate,
+                           o_coarse, a.row_src, a.block_len, H, n_t, dgate, dt, doc);
+    }
+    {
+        KernelTimer t(K_BWD_COARSE, st);
+        const dim3 gc((n_t + 63) / 64, H);
+        hipLaunchKernelGGL((coarse_bwd_rows_kernel<D>), gc, dim3(256), 0, st, qm, km, vm, o_coarse, doc,
+                           n_t, a.scale, reinterpret_cast<float *>(bw + L.lsec),
+                           reinterpret_cast<float *>(bw + L.dcc), reinterpret_cast<float *>(bw + L.dqm));
+        hipLaunchKernelGGL((coarse_bwd_cols_kernel<D>), gc, dim3(256), 0, st, qm, km, vm, doc,
+                           reinterpret_cast<const float *>(bw + L.lsec),
+                           reinterpret_cast<const float *>(bw + L.dcc), n_t, a.scale,
+                           reinterpret_cast<float *>(bw + L.dkm), reinterpret_cast<float *>(bw + L.dvm));
+    }
+    {
+        KernelTimer t(K_BWD_TLIST, st);
+        hipLaunchKernelGGL(tlist_kernel, dim3((n_t + 3) / 4, H), dim3(256), 0, st, a.keep, a.ref, a.P,
+                           a.n_v, n_t, a.k, a.list_len, reinterpret_cast<int32_t *>(bw + L.tlist),
+                           reinterpret_cast<int32_t *>(bw + L.tcount));
+    }
+    {
+        KernelTimer t(K_BWD_DQ, st);
+        hipLaunchKernelGGL((dq_kernel<D, B>), dim3(H * n_t * (B / 64)), dim3(64), 0, st, a);
+    }
+    {
+        KernelTimer t(K_BWD_DKDV, st);
+        hipLaunchKernelGGL((dkdv_kernel<D, B>), dim3(H * n_t * (B / 32)), dim3(64), 0, st, a);
+    }
+}
+
+}  // namespace
+}  // namespace vsa
+
+using namespace vsa;
+
+extern "C" int vsa_bwd_workspace_layout(const vsa_plan_info *info, int32_t heads, int32_t head_dim,
+                                        vsa_bwd_layout *layout)
+{
+    clear_error();
+    if (!layout) return fail(VSA_ERR_ARG, "layout is null");
+    if (int st = check_info(info)) return st;
+    if (heads <= 0) return fail(VSA_ERR_ARG, "heads = %d", heads);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(VSA_ERR_UNSUPPORTED, "head_dim = %d; supported: 64, 128", head_dim);
+    compute_bwd_layout(*info, heads, head_dim, layout);
+    return VSA_OK;
+}
+
+extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row_src_dev,
+                                   const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                                   int32_t k_ref, int32_t k_gen, float scale, const void *q,
+                                   const void *k, const void *v, const void *gate, const void *out,
+                                   const void *dout, const void *workspace, size_t workspace_bytes,
+                                   const int32_t *keep_idx_dev, const float *o_coarse_dev,
+                                   void *bwd_workspace, size_t bwd_workspace_bytes, float *dq,
+                                   float *dk, float *dv, float *dgate, void *stream)
+{
+    clear_error();
+    const char *name = "vsa_sparse_attn_bwd";
+    if (int st = check_info(info)) return st;
+    const bool ref = k_ref >= 0;
+    if (heads <= 0) return fail(VSA_ERR_ARG, "%s: heads = %d", name, heads);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(VSA_ERR_UNSUPPORTED, "%s: head_dim = %d; supported: 64, 128", name, head_dim);
+    if (k_gen < 0 || k_gen > info->n_video_tiles)
+        return fail(VSA_ERR_ARG, "%s: k_gen = %d outside [0, %d]", name, k_gen, info->n_video_tiles);
+    if (ref && k_ref > info->n_prefix_tiles)
+        return fail(VSA_ERR_ARG, "%s: k_ref = %d outside [0, %d]", name, k_ref, info->n_prefix_tiles);
+    if (!ref && info->n_prefix_tiles == 0 && k_gen == 0 && info->n_video_tiles > 0)
+        return fail(VSA_ERR_ARG, "%s: empty key set: no prefix tiles and k = 0", name);
+    if (ref && k_ref + k_gen == 0) return fail(VSA_ERR_ARG, "%s: empty key set: k_ref = k_gen = 0", name);
+    if (!row_src_dev || !block_len_dev || !q || !k || !v || !gate || !out || !dout || !workspace ||
+        !o_coarse_dev || !bwd_workspace || !dq || !dk || !dv || !dgate)
+        return fail(VSA_ERR_ARG, "%s: null device pointer", name);
+    if ((ref ? k_ref + k_gen : k_gen) > 0 && !keep_idx_dev) return fail(VSA_ERR_ARG, "%s: keep_idx is null", name);
+    if (!std::isfinite(scale)) return fail(VSA_ERR_ARG, "%s: scale is not finite", name);
+    vsa_ws_layout L;
+    compute_layout(*info, heads, head_dim, &L);
+    if (workspace_bytes < L.total_bytes)
+        return fail(VSA_ERR_ARG, "%s: workspace has %zu bytes, needs %zu", name, workspace_bytes, L.total_bytes);
+    vsa_bwd_layout BL;
+    compute_bwd_layout(*info, heads, head_dim, &BL);
+    if (bwd_workspace_bytes < BL.total_bytes)
+        return fail(VSA_ERR_ARG, "%s: backward workspace has %zu bytes, needs %zu", name,
+                    bwd_workspace_bytes, BL.total_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0 || reinterpret_cast<uintptr_t>(bwd_workspace) % 256 != 0)
+        return fail(VSA_ERR_ARG, "%s: workspaces must be 256-byte aligned", name);
+    if (int64_t(heads) * info->n_tiles * (info->tile_rows / 32) >= (int64_t(1) << 31))
+        return fail(VSA_ERR_UNSUPPORTED, "%s: too many work items", name);
+    if (int st = check_device()) return st;
+
+    const char *ws = static_cast<const char *>(workspace);
+    char *bw = static_cast<char *>(bwd_workspace);
+    BwdArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.dout = static_cast<const uint16_t *>(dout);
+    a.kt = reinterpret_cast<const uint16_t *>(ws + L.k_tiled);
+    a.vt = reinterpret_cast<const uint16_t *>(ws + L.v_tiled);
+    a.vrow = reinterpret_cast<const uint16_t *>(bw + BL.vrow);
+    a.kcol = reinterpret_cast<const uint16_t *>(bw + BL.kcol);
+    a.qcol = reinterpret_cast<const uint16_t *>(bw + BL.qcol);
+    a.docol = reinterpret_cast<const uint16_t *>(bw + BL.docol);
+    a.kn = static_cast<const uint16_t *>(k);
+    a.vn = static_cast<const uint16_t *>(v);
+    a.row_src = row_src_dev;
+    a.block_len = block_len_dev;
+    a.keep = keep_idx_dev;
+    a.tlist = reinterpret_cast<const int32_t *>(bw + BL.tlist);
+    a.tcount = reinterpret_cast<const int32_t *>(bw + BL.tcount);
+    a.dt = reinterpret_cast<const float *>(bw + BL.dt);
+    a.lse = reinterpret_cast<float *>(bw + BL.lse);
+    a.dqm = reinterpret_cast<const float *>(bw + BL.dqm);
+    a.dkm = reinterpret_cast<const float *>(bw + BL.dkm);
+    a.dvm = reinterpret_cast<const float *>(bw + BL.dvm);
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.H = heads;
+    a.P = info->n_prefix_tiles;
+    a.n_v = info->n_video_tiles;
+    a.n_t = info->n_tiles;
+    a.k = k_gen;
+    a.ref = ref ? 1 : 0;
+    a.list_len = ref ? k_ref + k_gen : 0;
+    a.scale = scale > 0.f ? scale : 1.0f / std::sqrt(float(head_dim));
+    a.scale_log2e = a.scale * 1.4426950408889634f;
+    const auto *qm = reinterpret_cast<const float *>(ws + L.q_mean);
+    const auto *km = reinterpret_cast<const float *>(ws + L.k_mean);
+    const auto *vm = reinterpret_cast<const float *>(ws + L.v_mean);
+    const auto *kk = static_cast<const uint16_t *>(k), *vv = static_cast<const uint16_t *>(v);
+    const auto *qq = static_cast<const uint16_t *>(q), *dd = static_cast<const uint16_t *>(dout);
+    const auto *oo = static_cast<const uint16_t *>(out), *gg = static_cast<const uint16_t *>(gate);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const int B = info->tile_rows;
+    if (head_dim == 128) {
+        if (B == 64) launch_bwd<128, 64>(*info, a, kk, vv, qq, dd, oo, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
+        else launch_bwd<128, 128>(*info, a, kk, vv, qq, dd, oo, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
+    } else {
+        if (B == 64) launch_bwd<64, 64>(*info, a, kk, vv, qq, dd, oo, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
+        else launch_bwd<64, 128>(*info, a, kk, vv, qq, dd, oo, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(VSA_ERR_DEVICE, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
+    return VSA_OK;
+}

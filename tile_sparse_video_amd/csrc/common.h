@@ -21,6 +21,7 @@ int check_info(const vsa_plan_info *info);
 
 // Fills `layout` for a checked plan (see vsa.h for the meaning of each region).
 void compute_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_ws_layout *layout);
+void compute_bwd_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_bwd_layout *layout);
 
 // Number of key chunks the fine pass splits each key list into (1 = no split).
 int split_chunks(const vsa_plan_info &info, int head_dim);
@@ -31,6 +32,7 @@ int check_device();
 // Kernels whose launches vsa_timing_read can report.
 enum KernelId {
     K_GATE_GEMM, K_GATHER_POOL, K_VIDEO_SCORES, K_COARSE_ATTN, K_TOPK, K_FINE_ATTN, K_MERGE,
+    K_BWD_GATHER, K_BWD_PREP, K_BWD_COARSE, K_BWD_TLIST, K_BWD_DQ, K_BWD_DKDV,
     K_COUNT
 };
 
