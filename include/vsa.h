@@ -288,9 +288,9 @@ int vsa_sparse_attn_fwd_ref(const vsa_plan_info *info, const int32_t *row_src_de
  *             the tile means, and each real row of tile i receives the
  *             mean's share (gradient / block_len);
  *   dq, dk, dv also receive the fine attention's gradient over the same key
- *             lists (log-sum-exp recomputed; the softmax-gradient row term
- *             D_t = dout[t] . (out[t] - g[t] * O_coarse[i]) uses the bf16
- *             output, P and dS are rounded to bf16 for the matrix products).
+ *             lists (the fine forward is recomputed for the log-sum-exp and
+ *             the softmax-gradient row term D_t = dout[t] . O_fine[t]; P and
+ *             dS are rounded to bf16 for the matrix products).
  *
  * vsa_bwd_layout -- scratch regions (device, caller-owned, 256-byte aligned):
  * fragment copies (V rows, K / Q / dO columns), per-row log-sum-exp and D_t,
@@ -308,7 +308,7 @@ int vsa_bwd_workspace_layout(const vsa_plan_info *info, int32_t heads, int32_t h
  * vsa_sparse_attn_bwd -- enqueues the backward pass on `stream`.
  * k_ref < 0: the default mode (keep_idx [H][n_v][k_gen] from vsa_coarse_topk);
  * k_ref >= 0: reference sparsity (keep_idx [H][n_t][k_ref + k_gen] from
- * vsa_coarse_topk_ref). q, k, v, out, dout: device bf16 [S][H][D]; gate:
+ * vsa_coarse_topk_ref). q, k, v, dout: device bf16 [S][H][D]; gate:
  * device bf16 [S][H*D]; workspace / keep_idx / o_coarse: as left by the
  * coarse pass for the same inputs (the tiled K and the tile means are read).
  * bwd_workspace: >= vsa_bwd_workspace_layout().total_bytes.
@@ -319,7 +319,7 @@ int vsa_bwd_workspace_layout(const vsa_plan_info *info, int32_t heads, int32_t h
 int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row_src_dev,
                         const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
                         int32_t k_ref, int32_t k_gen, float scale, const void *q, const void *k,
-                        const void *v, const void *gate, const void *out, const void *dout,
+                        const void *v, const void *gate, const void *dout,
                         const void *workspace, size_t workspace_bytes,
                         const int32_t *keep_idx_dev, const float *o_coarse_dev,
                         void *bwd_workspace, size_t bwd_workspace_bytes, float *dq, float *dk,

@@ -77,6 +77,10 @@ def _load():
                                   _I32P, i32, i32, _I32P, _I32P, _F32P, _F32P, _F32P, f64, _F64P,
                                   _F64P, _F64P, _F64P]
     lib.orc_layer_bwd.restype = ctypes.c_int
+    lib.orc_dq_tokens.argtypes = [_U16P, _U16P, _U16P, _U16P, _U16P, i32, i32, i32, _I32P, _I32P,
+                                  _I32P, i32, i32, _I32P, _I32P, _F32P, _F32P, _F32P, f64, _I64P,
+                                  i64, _F64P]
+    lib.orc_dq_tokens.restype = ctypes.c_int
     lib.orc_combine.argtypes = [_F64P, _U16P, _F64P, i64, i32, _U16P]
     lib.orc_combine.restype = None
     lib.orc_gate_proj.argtypes = [_U16P, _U16P, i32, i32, _I64P, i64, _U16P]
@@ -382,6 +386,24 @@ def layer_bwd(Q, K, V, G, dOut, h: int, pl: Plan, csr, scale: float):
     if rc != 0:
         raise OracleError("backward: a query has an empty key list")
     return outs
+
+
+def dq_tokens(Q, K, V, G, dOut, h: int, pl: Plan, csr, scale: float, tokens, means=None):
+    """dq (fp64 [n_tok][D]) of the given query tokens of head h, as layer_bwd."""
+    lib = _load()
+    S, H, D = Q.shape
+    qm, km, vm = means if means is not None else (tile_means(X, h, pl) for X in (Q, K, V))
+    off, ids = csr
+    toks = np.ascontiguousarray(np.asarray(list(tokens), dtype=np.int64))
+    out = np.zeros((toks.size, D), dtype=np.float64)
+    rc = lib.orc_dq_tokens(*(np.ascontiguousarray(X).reshape(-1) for X in (Q, K, V, G, dOut)),
+                           H, D, int(h), pl.untile, pl.row_src, pl.block_len, pl.n_t, pl.B,
+                           np.ascontiguousarray(off), ids, np.ascontiguousarray(qm).reshape(-1),
+                           np.ascontiguousarray(km).reshape(-1), np.ascontiguousarray(vm).reshape(-1),
+                           float(scale), toks, int(toks.size), out.reshape(-1))
+    if rc != 0:
+        raise OracleError("dq: a query has an empty key list")
+    return out
 
 
 # ------------------------------------------------------- the layer, in order --

@@ -643,6 +643,112 @@ int orc_layer_bwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const
     return bad ? -1 : 0;
 }
 
+/*
+ * dq of selected query tokens only (the same gradient as orc_layer_bwd, for
+ * checks at full size): the fine part needs only the token's own keys, and
+ * the mean's share needs only its tile's row of the coarse attention
+ * (dO_c[i] from the tile's real rows). dq is fp64 [n_tok][D].
+ */
+int orc_dq_tokens(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const uint16_t *G,
+                  const uint16_t *dOut, int32_t H, int32_t D, int32_t h, const int32_t *untile,
+                  const int32_t *row_src, const int32_t *block_len, int32_t n_t, int32_t B,
+                  const int32_t *off, const int32_t *lst, const float *qm, const float *km,
+                  const float *vm, double scale, const int64_t *tokens, int64_t n_tok, double *dq)
+{
+    if (D > 256) return -1;
+    int bad = 0;
+#define X(A, t, d) ((double)bf16_to_float((A)[((int64_t)(t) * H + h) * D + (d)]))
+#define GV(t, d) ((double)bf16_to_float(G[(int64_t)(t) * H * D + (int64_t)h * D + (d)]))
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t qi = 0; qi < n_tok; ++qi) {
+        const int64_t t = tokens[qi];
+        const int32_t i = untile[t] / B;
+        double *res = dq + qi * D;
+        /* coarse row i: Pc_ij, O_c[i], dO_c[i], Dc_i, then dqm_i */
+        double *pc = (double *)malloc(sizeof(double) * (size_t)n_t);
+        double zmax = -INFINITY, den = 0.0;
+        for (int32_t j = 0; j < n_t; ++j) {
+            double dot = 0.0;
+            for (int32_t d = 0; d < D; ++d) dot += (double)qm[(int64_t)i * D + d] * (double)km[(int64_t)j * D + d];
+            pc[j] = scale * dot;
+            if (pc[j] > zmax) zmax = pc[j];
+        }
+        for (int32_t j = 0; j < n_t; ++j) {
+            pc[j] = exp(pc[j] - zmax);
+            den += pc[j];
+        }
+        double oc[256], doc[256], dqm[256];
+        for (int32_t d = 0; d < D; ++d) oc[d] = doc[d] = dqm[d] = 0.0;
+        for (int32_t j = 0; j < n_t; ++j) {
+            pc[j] /= den;
+            for (int32_t d = 0; d < D; ++d) oc[d] += pc[j] * (double)vm[(int64_t)j * D + d];
+        }
+        for (int32_t r = 0; r < B; ++r) {
+            int32_t u = row_src[(int64_t)i * B + r];
+            if (u < 0) continue;
+            for (int32_t d = 0; d < D; ++d) doc[d] += X(dOut, u, d) * GV(u, d);
+        }
+        double Dc = 0.0;
+        for (int32_t d = 0; d < D; ++d) Dc += doc[d] * oc[d];
+        for (int32_t j = 0; j < n_t; ++j) {
+            double dp = 0.0;
+            for (int32_t d = 0; d < D; ++d) dp += doc[d] * (double)vm[(int64_t)j * D + d];
+            double dz = pc[j] * (dp - Dc);
+            for (int32_t d = 0; d < D; ++d) dqm[d] += scale * dz * (double)km[(int64_t)j * D + d];
+        }
+        free(pc);
+        for (int32_t d = 0; d < D; ++d) res[d] = dqm[d] / (double)block_len[i];
+        /* fine part over the token's own keys */
+        int64_t nk = 0;
+        for (int32_t a = off[i]; a < off[i + 1]; ++a) nk += block_len[lst[a]];
+        if (nk == 0) {
+            bad = 1;
+            continue;
+        }
+        double *z = (double *)malloc(sizeof(double) * (size_t)nk);
+        int32_t *u_of = (int32_t *)malloc(sizeof(int32_t) * (size_t)nk);
+        int64_t n = 0;
+        zmax = -INFINITY;
+        for (int32_t a = off[i]; a < off[i + 1]; ++a) {
+            int32_t j = lst[a];
+            for (int32_t rr = 0; rr < B; ++rr) {
+                int32_t u = row_src[(int64_t)j * B + rr];
+                if (u < 0) continue;
+                double dot = 0.0;
+                for (int32_t d = 0; d < D; ++d) dot += X(Q, t, d) * X(K, u, d);
+                z[n] = scale * dot;
+                u_of[n] = u;
+                if (z[n] > zmax) zmax = z[n];
+                ++n;
+            }
+        }
+        den = 0.0;
+        for (int64_t a = 0; a < n; ++a) {
+            z[a] = exp(z[a] - zmax);
+            den += z[a];
+        }
+        double o[256];
+        for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+        for (int64_t a = 0; a < n; ++a) {
+            z[a] /= den;
+            for (int32_t d = 0; d < D; ++d) o[d] += z[a] * X(V, u_of[a], d);
+        }
+        double Dt = 0.0;
+        for (int32_t d = 0; d < D; ++d) Dt += X(dOut, t, d) * o[d];
+        for (int64_t a = 0; a < n; ++a) {
+            double dp = 0.0;
+            for (int32_t d = 0; d < D; ++d) dp += X(dOut, t, d) * X(V, u_of[a], d);
+            double ds = z[a] * (dp - Dt);
+            for (int32_t d = 0; d < D; ++d) res[d] += scale * ds * X(K, u_of[a], d);
+        }
+        free(z);
+        free(u_of);
+    }
+#undef X
+#undef GV
+    return bad ? -1 : 0;
+}
+
 /* ----------------------------------------------------------- O8: combine -- */
 /*
  * Layer output for individual (token, head) rows: out = O_fine + g * O_coarse

@@ -113,3 +113,19 @@ def test_backward_zero_and_gate_cases(orc):
     oc = hr.o_coarse[pl.untile // pl.B]
     assert np.allclose(g0["dg"], orc.bf16_value(dO)[:, 0, :] * oc, rtol=1e-12, atol=1e-14)
     assert np.allclose(g0["dv"].sum(0), orc.bf16_value(dO)[:, 0, :].sum(0), rtol=1e-10, atol=1e-9)
+
+
+def test_dq_tokens_matches_full_backward(orc):
+    segs, grid, tile = (5, 70), (5, 6, 9), (4, 4, 4)
+    pl = orc.plan(segs, grid, tile)
+    H, D = 2, 32
+    Q, K, V = (rand_bf16((pl.S, H, D), s) for s in (61, 62, 63))
+    G = rand_bf16((pl.S, H * D), 64)
+    dO = rand_bf16((pl.S, H, D), 65)
+    for h in range(H):
+        hr = orc.head(Q, K, V, h, pl, 3, D ** -0.5)
+        csr = orc.key_lists_default(pl, hr.keep)
+        full = orc.layer_bwd(Q, K, V, G, dO, h, pl, csr, D ** -0.5)
+        toks = np.array([0, 3, 11, pl.S - 1, pl.S // 2])
+        got = orc.dq_tokens(Q, K, V, G, dO, h, pl, csr, D ** -0.5, toks)
+        assert np.allclose(got, full["dq"][toks], rtol=1e-12, atol=1e-13)

@@ -95,7 +95,7 @@ def _load() -> ctypes.CDLL:
         "vsa_sparse_attn_fwd_ref": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, SZ, P, P, P, P,
                                      P], ctypes.c_int),
         "vsa_bwd_workspace_layout": ([info_p, I32, I32, ctypes.POINTER(vsa_bwd_layout)], ctypes.c_int),
-        "vsa_sparse_attn_bwd": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, P, P, P, P, P, SZ, P, P,
+        "vsa_sparse_attn_bwd": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, P, P, P, P, SZ, P, P,
                                  P, SZ, P, P, P, P, P], ctypes.c_int),
         "vsa_timing_enable": ([I32], ctypes.c_int),
         "vsa_timing_read": ([ctypes.c_char_p, ctypes.POINTER(I32), ctypes.POINTER(F64)],
@@ -353,13 +353,13 @@ def vsa_bwd_workspace_layout(info: vsa_plan_info, heads: int, head_dim: int) -> 
 
 
 def vsa_sparse_attn_bwd(info: vsa_plan_info, row_src_dev: torch.Tensor, block_len_dev: torch.Tensor,
-                        heads: int, head_dim: int, k_ref: int, k_gen: int, q, k, v, gate, out, dout,
+                        heads: int, head_dim: int, k_ref: int, k_gen: int, q, k, v, gate, dout,
                         workspace: torch.Tensor, keep_idx: Optional[torch.Tensor],
                         o_coarse: torch.Tensor, bwd_workspace: torch.Tensor, dq, dk, dv, dgate,
                         scale: float = 0.0, stream=None) -> None:
     """Backward pass (k_ref < 0: default mode). Gradients are fp32."""
     S = info.rows_real
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _need(t, n, torch.bfloat16, (S, heads, head_dim))
     _need(gate, "gate", torch.bfloat16)
     if gate.numel() != S * heads * head_dim:
@@ -378,7 +378,7 @@ def vsa_sparse_attn_bwd(info: vsa_plan_info, row_src_dev: torch.Tensor, block_le
         _need(keep_idx, "keep_idx", torch.int32)
     _check(_lib.vsa_sparse_attn_bwd(
         ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev), heads, head_dim, int(k_ref),
-        int(k_gen), float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(out), _ptr(dout),
+        int(k_gen), float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(dout),
         _ptr(workspace), workspace.numel(), _ptr(keep_idx), _ptr(o_coarse), _ptr(bwd_workspace),
         bwd_workspace.numel(), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate), _stream(stream)),
         "vsa_sparse_attn_bwd")
@@ -492,7 +492,7 @@ class TileSparseAttention:
                                 self.head_dim, self.k, q, self.workspace, keep, self.o_coarse,
                                 gate, out, scale=self.scale, stream=stream)
 
-    def backward(self, q, k, v, gate, out, dout, stream=None):
+    def backward(self, q, k, v, gate, dout, stream=None):
         """Gradients (dq, dk, dv, dgate), fp32, of the last forward's layer with its
         keep sets held fixed. Call after coarse() and fine() on the same inputs."""
         if not hasattr(self, "bwd_workspace"):
@@ -504,7 +504,7 @@ class TileSparseAttention:
         dgate = torch.empty(gate.shape, dtype=torch.float32, device=q.device)
         keep = self.keep_idx if self.list_len > 0 else None
         vsa_sparse_attn_bwd(self.plan.info, self.row_src, self.block_len, self.heads, self.head_dim,
-                            self.k_ref if self.ref else -1, self.k, q, k, v, gate, out, dout,
+                            self.k_ref if self.ref else -1, self.k, q, k, v, gate, dout,
                             self.workspace, keep, self.o_coarse, self.bwd_workspace, dq, dk, dv,
                             dgate, scale=self.scale, stream=stream)
         return dq, dk, dv, dgate

@@ -16,14 +16,13 @@
 //   frag_gather  -- V in the row-fragment layout, K / Q / dO in the
 //                   column-fragment layout (the two MFMA operand layouts of
 //                   the forward's K and V copies), tile order, padding zero;
-//   bwd_prep     -- dg = dout * O_c, D_t = dout . (out - g * O_c) (the
-//                   softmax-gradient row term, from the bf16 output), and
-//                   dO_c[i] = sum_{t in i} dout * g;
+//   bwd_prep     -- dg = dout * O_c and dO_c[i] = sum_{t in i} dout * g;
 //   coarse_bwd   -- the tile-level attention's gradient to the tile means
 //                   (fp32, rows then columns);
 //   tlist        -- for every key tile, the ascending list of query tiles
 //                   whose key list holds it (the transpose of the keep sets);
-//   dq           -- query-major: the fine softmax statistics (log-sum-exp),
+//   dq           -- query-major: the fine forward again (log-sum-exp, O_fine
+//                   and the softmax-gradient row term D_t = dout . O_fine),
 //                   then dQ = scale dS K over the tile's key list, plus the
 //                   mean's share dqm / n;
 //   dkdv         -- key-major over the transposed lists: dV = P^T dO,
@@ -121,48 +120,39 @@ __global__ __launch_bounds__(256) void frag_gather_kernel(const uint16_t *__rest
 // -------------------------------------------------------------- bwd_prep --
 //
 // One block (4 waves) per (tile, head); wave w takes the tile's real rows
-// w, w+4, ...; lane owns d = lane + 64p. Writes dg (fp32, natural order),
-// D_t (fp32 [H][S_pad], tile order; zero on padding rows) and dO_c.
+// w, w+4, ...; lane owns d = lane + 64p. Writes dg (fp32, natural order) and
+// dO_c[i] = sum over the tile's rows of dout * g.
 template <int D, int B>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t *__restrict__ dout,
-                                                      const uint16_t *__restrict__ out,
                                                       const uint16_t *__restrict__ gate,
                                                       const float *__restrict__ o_coarse,
                                                       const int32_t *__restrict__ row_src,
                                                       const int32_t *__restrict__ block_len, int H,
                                                       int n_t, float *__restrict__ dgate,
-                                                      float *__restrict__ dt, float *__restrict__ doc)
+                                                      float *__restrict__ doc)
 {
     constexpr int PL = D / kWave;
     __shared__ float red[4][D];
     const int tile = blockIdx.x, h = blockIdx.y;
     const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int n = block_len[tile];
-    const size_t S_pad = size_t(n_t) * B;
     float oc[PL], acc[PL];
 #pragma unroll
     for (int p = 0; p < PL; ++p) {
         oc[p] = o_coarse[(size_t(h) * n_t + tile) * D + lane + kWave * p];
         acc[p] = 0.f;
     }
-    for (int r = w; r < B; r += 4) {
-        float dsum = 0.f;
-        if (r < n) {
-            const int t = row_src[size_t(tile) * B + r];
-            const size_t base = (size_t(t) * H + h) * D;
+    for (int r = w; r < n; r += 4) {
+        const int t = row_src[size_t(tile) * B + r];
+        const size_t base = (size_t(t) * H + h) * D;
 #pragma unroll
-            for (int p = 0; p < PL; ++p) {
-                const int d = lane + kWave * p;
-                const float go = bf16_to_f32(dout[base + d]);
-                const float o = bf16_to_f32(out[base + d]);
-                const float g = bf16_to_f32(gate[base + d]);
-                dgate[base + d] = go * oc[p];
-                dsum += go * (o - g * oc[p]);
-                acc[p] += go * g;
-            }
+        for (int p = 0; p < PL; ++p) {
+            const int d = lane + kWave * p;
+            const float go = bf16_to_f32(dout[base + d]);
+            const float g = bf16_to_f32(gate[base + d]);
+            dgate[base + d] = go * oc[p];
+            acc[p] += go * g;
         }
-        dsum = wave_sum(dsum);
-        if (lane == 0) dt[size_t(h) * S_pad + size_t(tile) * B + r] = dsum;
     }
 #pragma unroll
     for (int p = 0; p < PL; ++p) red[w][lane + kWave * p] = acc[p];
@@ -387,7 +377,8 @@ struct BwdArgs {
     const uint16_t *kn, *vn;        // natural K and V
     const int32_t *row_src, *block_len, *keep;
     const int32_t *tlist, *tcount;
-    const float *dt;                // [H][S_pad]
+    const float *dt;                // [H][S_pad] D_t, written by the dq kernel (dt_out)
+    float *dt_out;
     float *lse;                     // [H][S_pad], log2 domain (+inf on padding rows)
     const float *dqm, *dkm, *dvm;   // [H][n_t][D]
     float *dq, *dk, *dv;            // natural [S][H][D]
@@ -424,7 +415,6 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
     for (int qb = 0; qb < 2; ++qb) {
         const int row = tile * B + 64 * qsub + 32 * qb + l32;
         tok[qb] = a.row_src[row];
-        dq_row[qb] = a.dt[size_t(h) * S_pad + row];
         const size_t base = (size_t(tok[qb] < 0 ? 0 : tok[qb]) * a.H + h) * D + 8 * half;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
@@ -499,14 +489,27 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
         }
     };
 
-    // ---- pass 1: log-sum-exp (log2 domain) of every query row
+    // ---- pass 1: the fine forward again -- running max, sum and O^T = V^T P^T
+    // -- giving the log-sum-exp (log2 domain) and D_t = dout . O_fine, both
+    // written for the key-major kernel.
+    const __amdgpu_buffer_rsrc_t rv = rsrc(a.vt);
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    f32x16_t O[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) O[db][0] = O[db][1] = f32x16_t{};
     walk([&](int v, uint32_t ent) {
         const int real = min(32, int(ent >> 25) + 1 - 32 * (v % HPU));
-        const uint32_t base = half_base(v, ent) + uint32_t(v & 1) * NC * 1024u;
-        u32x4_t Kb[NC];
+        const uint32_t hb = half_base(v, ent);
+        const uint32_t base = hb + uint32_t(v & 1) * NC * 1024u;
+        const uint32_t cbase = hb + uint32_t(v & 1) * 2 * 1024u;
+        u32x4_t Kb[NC], Vc[2 * DB];
 #pragma unroll
         for (int c = 0; c < NC; ++c) Kb[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, vlane, base + c * 1024u, 0);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+                Vc[2 * db + cc] = __builtin_amdgcn_raw_buffer_load_b128(rv, vlane, cbase + (4 * db + cc) * 1024u, 0);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             f32x16_t S = s_block(qb, Kb, false);
@@ -516,21 +519,59 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
             for (int e = 1; e < 16; ++e) mx = fmaxf(mx, S[e]);
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float mn = fmaxf(m[qb], mx);
-            if (mn > -INFINITY) {
-                float s = 0.f;
+            if (mn > m[qb]) {  // per query column; VALU only
+                const float alpha = m[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m[qb] - mn) * c2);
+                l[qb] *= alpha;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) s += __builtin_amdgcn_exp2f((S[e] - mn) * c2);
-                s += __shfl_xor(s, 32);
-                l[qb] = l[qb] * (m[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m[qb] - mn) * c2)) + s;
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) O[db][qb][e] *= alpha;
                 m[qb] = mn;
+            }
+            // A column with no real key yet (all -inf) takes P = 0, not NaN.
+            const float mref = mn == -INFINITY ? 0.f : mn;
+            f32x16_t Pm;
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                Pm[e] = __builtin_amdgcn_exp2f((S[e] - mref) * c2);
+                s += Pm[e];
+            }
+            l[qb] += s + __shfl_xor(s, 32);
+            const bf16x8_t p0 = pack8(Pm, 0), p1 = pack8(Pm, 1);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Vc[2 * db]), p0, O[db][qb], 0, 0, 0);
+                O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Vc[2 * db + 1]), p1, O[db][qb], 0, 0, 0);
             }
         }
     });
     float lse[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
+        const size_t row = size_t(h) * S_pad + tile * B + 64 * qsub + 32 * qb + l32;
+        // D_t = sum_d dout[d] O_fine[d]; O^T acc 4i + j <-> d = 32db + 8i + 4 half + j.
+        float part = 0.f;
+        if (tok[qb] >= 0) {
+            const uint16_t *go = a.dout + (size_t(tok[qb]) * a.H + h) * D;
+            const float inv = 1.0f / l[qb];
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint2 raw = *reinterpret_cast<const uint2 *>(go + 32 * db + 8 * i + 4 * half);
+                    part += __uint_as_float(raw.x << 16) * O[db][qb][4 * i] * inv;
+                    part += __uint_as_float(raw.x & 0xffff0000u) * O[db][qb][4 * i + 1] * inv;
+                    part += __uint_as_float(raw.y << 16) * O[db][qb][4 * i + 2] * inv;
+                    part += __uint_as_float(raw.y & 0xffff0000u) * O[db][qb][4 * i + 3] * inv;
+                }
+        }
+        dq_row[qb] = part + __shfl_xor(part, 32);
         lse[qb] = tok[qb] < 0 ? INFINITY : m[qb] * c2 + __log2f(l[qb]);
-        if (half == 0) a.lse[size_t(h) * S_pad + tile * B + 64 * qsub + 32 * qb + l32] = lse[qb];
+        if (half == 0) {
+            a.lse[row] = lse[qb];
+            a.dt_out[row] = dq_row[qb];
+        }
     }
 
     // ---- pass 2: dQ^T = K^T dS^T
@@ -760,7 +801,7 @@ namespace {
 
 template <int D, int B>
 void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, const uint16_t *v,
-                const uint16_t *q, const uint16_t *dout, const uint16_t *out, const uint16_t *gate,
+                const uint16_t *q, const uint16_t *dout, const uint16_t *gate,
                 const float *o_coarse, const float *qm, const float *km, const float *vm,
                 const vsa_bwd_layout &L, char *bw, float *dgate, hipStream_t st)
 {
@@ -778,12 +819,11 @@ void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, 
         hipLaunchKernelGGL((frag_gather_kernel<D, B, 0>), gg, dim3(256), 0, st, dout, a.row_src,
                            a.block_len, H, n_t, reinterpret_cast<uint16_t *>(bw + L.docol));
     }
-    auto *dt = reinterpret_cast<float *>(bw + L.dt);
     auto *doc = reinterpret_cast<float *>(bw + L.doc);
     {
         KernelTimer t(K_BWD_PREP, st);
-        hipLaunchKernelGGL((bwd_prep_kernel<D, B>), dim3(n_t, H), dim3(256), 0, st, dout, out, gate,
-                           o_coarse, a.row_src, a.block_len, H, n_t, dgate, dt, doc);
+        hipLaunchKernelGGL((bwd_prep_kernel<D, B>), dim3(n_t, H), dim3(256), 0, st, dout, gate,
+                           o_coarse, a.row_src, a.block_len, H, n_t, dgate, doc);
     }
     {
         KernelTimer t(K_BWD_COARSE, st);
@@ -833,7 +873,7 @@ extern "C" int vsa_bwd_workspace_layout(const vsa_plan_info *info, int32_t heads
 extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row_src_dev,
                                    const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
                                    int32_t k_ref, int32_t k_gen, float scale, const void *q,
-                                   const void *k, const void *v, const void *gate, const void *out,
+                                   const void *k, const void *v, const void *gate,
                                    const void *dout, const void *workspace, size_t workspace_bytes,
                                    const int32_t *keep_idx_dev, const float *o_coarse_dev,
                                    void *bwd_workspace, size_t bwd_workspace_bytes, float *dq,
@@ -853,7 +893,7 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
     if (!ref && info->n_prefix_tiles == 0 && k_gen == 0 && info->n_video_tiles > 0)
         return fail(VSA_ERR_ARG, "%s: empty key set: no prefix tiles and k = 0", name);
     if (ref && k_ref + k_gen == 0) return fail(VSA_ERR_ARG, "%s: empty key set: k_ref = k_gen = 0", name);
-    if (!row_src_dev || !block_len_dev || !q || !k || !v || !gate || !out || !dout || !workspace ||
+    if (!row_src_dev || !block_len_dev || !q || !k || !v || !gate || !dout || !workspace ||
         !o_coarse_dev || !bwd_workspace || !dq || !dk || !dv || !dgate)
         return fail(VSA_ERR_ARG, "%s: null device pointer", name);
     if ((ref ? k_ref + k_gen : k_gen) > 0 && !keep_idx_dev) return fail(VSA_ERR_ARG, "%s: keep_idx is null", name);
@@ -892,6 +932,7 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
     a.tlist = reinterpret_cast<const int32_t *>(bw + BL.tlist);
     a.tcount = reinterpret_cast<const int32_t *>(bw + BL.tcount);
     a.dt = reinterpret_cast<const float *>(bw + BL.dt);
+    a.dt_out = reinterpret_cast<float *>(bw + BL.dt);
     a.lse = reinterpret_cast<float *>(bw + BL.lse);
     a.dqm = reinterpret_cast<const float *>(bw + BL.dqm);
     a.dkm = reinterpret_cast<const float *>(bw + BL.dkm);
@@ -913,16 +954,16 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
     const auto *vm = reinterpret_cast<const float *>(ws + L.v_mean);
     const auto *kk = static_cast<const uint16_t *>(k), *vv = static_cast<const uint16_t *>(v);
     const auto *qq = static_cast<const uint16_t *>(q), *dd = static_cast<const uint16_t *>(dout);
-    const auto *oo = static_cast<const uint16_t *>(out), *gg = static_cast<const uint16_t *>(gate);
+    const auto *gg = static_cast<const uint16_t *>(gate);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     const int B = info->tile_rows;
     if (head_dim == 128) {
-        if (B == 64) launch_bwd<128, 64>(*info, a, kk, vv, qq, dd, oo, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
-        else launch_bwd<128, 128>(*info, a, kk, vv, qq, dd, oo, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
+        if (B == 64) launch_bwd<128, 64>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
+        else launch_bwd<128, 128>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
     } else {
-        if (B == 64) launch_bwd<64, 64>(*info, a, kk, vv, qq, dd, oo, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
-        else launch_bwd<64, 128>(*info, a, kk, vv, qq, dd, oo, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
+        if (B == 64) launch_bwd<64, 64>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
+        else launch_bwd<64, 128>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(VSA_ERR_DEVICE, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
