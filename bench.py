@@ -139,6 +139,115 @@ def recorded_traffic(workload: str):
     return rec
 
 
+def bench_backward(args, wl, tsv, att, qd, kd, vd, xd, wd, g, out, stream, host_inputs) -> int:
+    """Training step of one layer: forward (gate projection, coarse, fine) then the
+    backward pass; effective FLOPs = 4 D (forward) + 10 D (backward: S, dP, dV, dK,
+    dQ) per kept (query row, key row) pair."""
+    gen = torch.Generator().manual_seed(4242)
+    dout = torch.randn(wl.tokens, wl.heads, wl.head_dim, generator=gen).to(torch.bfloat16).to(qd.device)
+    grads = {}
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        tsv.vsa_gate_proj(xd, wd, g, stream=stream)
+        att.coarse(qd, kd, vd, stream=stream)
+        att.fine(qd, g, out, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        grads["g"] = att.backward(qd, kd, vd, g, dout, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    print("[bench] warmup (training step)", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    tsv.vsa_timing_enable(True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tsv.vsa_timing_enable(False)
+    kernels = {}
+    for name in tsv.TIMED_KERNELS:
+        n, ms = tsv.vsa_timing_read(name)
+        if n:
+            kernels[name] = {"launches": n, "avg_ms": round(ms / n, 4)}
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    layer_ms = float(evs[0][0].elapsed_time(evs[-1][2])) / args.steps
+    keep_host = att.keep_idx.cpu().numpy()
+    fwd_flops = effective_fine_flops(att.plan, keep_host, wl.heads, wl.head_dim, att.ref)
+    bwd_flops = 2.5 * fwd_flops
+    dkdv_flops = 2.0 * fwd_flops       # S, dP, dV, dK: 8 D per pair
+    dkdv_ms = kernels["bwd_dkdv"]["avg_ms"]
+    dkdv_tf = dkdv_flops / (dkdv_ms * 1e-3) / 1e12
+    result = {
+        "metric": "ms/layer fwd+bwd + effective TFLOP/s (fine: 4D fwd + 10D bwd per kept pair)",
+        "value": round((fwd_flops + bwd_flops) / (layer_ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(layer_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.note}", "heads": wl.heads, "head_dim": wl.head_dim,
+                   "tokens": wl.tokens, "keep_k": att.k,
+                   "reference_sparsity": args.reference_sparsity,
+                   "ref_keep_k": att.k_ref if att.ref else None, "mode": "training step",
+                   "parallelism": "single GPU"},
+        "breakdown_ms": {"forward": round(fwd_ms, 4), "backward": round(bwd_ms, 4)},
+        "kernels": kernels,
+        "effective_tflop": {"forward": round(fwd_flops / 1e12, 3),
+                            "backward": round(bwd_flops / 1e12, 3)},
+        "wall_s": round(wall, 3),
+        "roofline": {
+            "kernel": "dkdv_kernel (vsa_sparse_attn_bwd)", "bound": "mfma",
+            "achieved": round(dkdv_tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(dkdv_tf / BF16_PEAK_TFLOPS, 4),
+            "algorithmic_tflop_per_launch": round(dkdv_flops / 1e12, 4),
+            "avg_launch_ms": dkdv_ms, "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_backward(wl, host_inputs, att, dout, g,
+                                                        fwd_flops + bwd_flops)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline_backward(wl, host_inputs, att, dout, g, flops):
+    """The oracle's backward on a bounded sample: dq of sampled tokens of head 0
+    (each token's own keys plus its tile's coarse row), scaled by 3 (dk and dv
+    cost the same per pair) to all tokens and heads."""
+    import oracle
+    q, k, v, x, w = host_inputs
+    Qb, Kb, Vb = (workloads.bf16_bits(t) for t in (q, k, v))
+    pl = oracle.plan(wl.prefix_segments, wl.grid, wl.tile)
+    scale = wl.head_dim ** -0.5
+    if att.ref:
+        hr = oracle.head_ref(Qb, Kb, Vb, 0, pl, att.k_ref, att.k, scale)
+        csr = oracle.key_lists_explicit(hr.keep)
+    else:
+        hr = oracle.head(Qb, Kb, Vb, 0, pl, att.k, scale)
+        csr = oracle.key_lists_default(pl, hr.keep)
+    g_bits = workloads.bf16_bits(g.cpu())
+    d_bits = workloads.bf16_bits(dout.cpu())
+    toks = np.random.default_rng(0).choice(pl.S, size=512, replace=False)
+    t0 = time.perf_counter()
+    oracle.dq_tokens(Qb, Kb, Vb, g_bits, d_bits, 0, pl, csr, scale, toks,
+                     means=(hr.qm, hr.km, hr.vm))
+    per_tok = (time.perf_counter() - t0) / len(toks)
+    layer_s = 3.0 * per_tok * pl.S * wl.heads
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return {"value": flops / layer_s / 1e12, "unit": "TFLOP/s", "ms_per_layer": layer_s * 1e3,
+            "cores": threads, "kind": "oracle",
+            "sample": f"dq of {len(toks)} tokens of head 0 ({per_tok * 1e3:.2f} ms per token), "
+                      f"times 3 for dk and dv, scaled to all tokens and heads (backward only)"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +258,9 @@ def main() -> int:
     ap.add_argument("--reference-sparsity", type=float, default=None, metavar="S",
                     help="run the reference-sparsity mode: every query tile keeps the top "
                          "(1-S) of the prefix tiles as well as the top video tiles")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the layer's training step instead: forward plus the backward "
+                         "pass (gradients of q, k, v and the gate)")
     ap.add_argument("--split-chunks", type=int, default=0,
                     help="fine-pass key-list split (0 = the library's automatic choice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -201,6 +313,10 @@ def main() -> int:
         att.fine(qd, g, out, stream=stream)
         if ev is not None:
             ev[3].record(stream)
+
+    if args.backward:
+        return bench_backward(args, wl, tsv, att, qd, kd, vd, xd, wd, g, out, stream,
+                              (q, k, v, x, w))
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

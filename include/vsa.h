@@ -293,11 +293,12 @@ int vsa_sparse_attn_fwd_ref(const vsa_plan_info *info, const int32_t *row_src_de
  *             dS are rounded to bf16 for the matrix products).
  *
  * vsa_bwd_layout -- scratch regions (device, caller-owned, 256-byte aligned):
- * fragment copies (V rows, K / Q / dO columns), per-row log-sum-exp and D_t,
+ * fragment copies (V / Q / dO rows, K / Q / dO columns), per-row log-sum-exp and D_t,
  * the coarse-path gradients, and the transposed key lists ([H][n_t][n_t]).
  */
 typedef struct vsa_bwd_layout {
-    size_t vrow, kcol, qcol, docol, lse, dt, doc, dqm, dkm, dvm, lsec, dcc, tlist, tcount;
+    size_t vrow, kcol, qcol, docol, qrow, dorow, lse, dt, doc, dqm, dkm, dvm, lsec, dcc, tlist,
+        tcount;
     size_t total_bytes;
 } vsa_bwd_layout;
 

@@ -62,8 +62,8 @@ class vsa_ws_layout(ctypes.Structure):
 
 class vsa_bwd_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("vrow", "kcol", "qcol", "docol", "lse", "dt", "doc", "dqm", "dkm", "dvm", "lsec",
-                 "dcc", "tlist", "tcount", "total_bytes")]
+                ("vrow", "kcol", "qcol", "docol", "qrow", "dorow", "lse", "dt", "doc", "dqm", "dkm",
+                 "dvm", "lsec", "dcc", "tlist", "tcount", "total_bytes")]
 
 
 def _load() -> ctypes.CDLL:

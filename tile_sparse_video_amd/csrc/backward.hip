@@ -13,7 +13,7 @@
 //   O_c[i]    = sum_j softmax_j(scale qm_i.km_j) vm_j   (tile means, all tiles)
 //   out[t]    = O_fine[t] + g[t] * O_c[i]
 // Kernels, in launch order:
-//   frag_gather  -- V in the row-fragment layout, K / Q / dO in the
+//   frag_gather  -- V / Q / dO in the row-fragment layout, K / Q / dO in the
 //                   column-fragment layout (the two MFMA operand layouts of
 //                   the forward's K and V copies), tile order, padding zero;
 //   bwd_prep     -- dg = dout * O_c and dO_c[i] = sum_{t in i} dout * g;
@@ -374,6 +374,7 @@ struct BwdArgs {
     const uint16_t *kt, *vt;        // forward workspace: K row fragments, V column fragments
     const uint16_t *vrow, *kcol;    // V row fragments, K column fragments
     const uint16_t *qcol, *docol;   // Q and dO column fragments
+    const uint16_t *qrow, *dorow;   // Q and dO row fragments
     const uint16_t *kn, *vn;        // natural K and V
     const int32_t *row_src, *block_len, *keep;
     const int32_t *tlist, *tcount;
@@ -441,8 +442,12 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
     const int vlane = lane * 16;
     const float c2 = a.scale_log2e;
 
-    // Walks the key list in segments staged in LDS; body(v, entry) per half.
-    auto walk = [&](auto &&body) {
+    // Walks the key list in segments staged in LDS. Per 32-key half v:
+    // fetch(v, entry, regs) issues its operand loads, body(v, entry, regs)
+    // uses them; the next half's loads are in flight while the current half
+    // is computed (two register sets; a segment always has an even number of
+    // halves).
+    auto walk = [&](auto &&fetch, auto &&body, auto &regA, auto &regB) {
         int scan = 0;
         while (true) {
             int count = 0;
@@ -457,7 +462,15 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
                 scan += kWave;
             }
             __syncthreads();
-            for (int v = 0; v < count * HPU; ++v) body(v, __builtin_amdgcn_readfirstlane(list_lds[v / HPU]));
+            const int n_half = count * HPU;
+            auto ent = [&](int v) { return __builtin_amdgcn_readfirstlane(list_lds[v / HPU]); };
+            if (n_half > 0) fetch(0, ent(0), regA);
+            for (int v = 0; v < n_half; v += 2) {
+                fetch(v + 1, ent(v + 1), regB);
+                body(v, ent(v), regA);
+                if (v + 2 < n_half) fetch(v + 2, ent(v + 2), regA);
+                body(v + 1, ent(v + 1), regB);
+            }
             if (scan >= n_list) break;
             __syncthreads();
         }
@@ -497,22 +510,26 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
     f32x16_t O[DB][2];
 #pragma unroll
     for (int db = 0; db < DB; ++db) O[db][0] = O[db][1] = f32x16_t{};
-    walk([&](int v, uint32_t ent) {
-        const int real = min(32, int(ent >> 25) + 1 - 32 * (v % HPU));
+    struct Regs1 {
+        u32x4_t Kb[NC], Vc[2 * DB];
+    };
+    auto fetch1 = [&](int v, uint32_t ent, Regs1 &g) {
         const uint32_t hb = half_base(v, ent);
         const uint32_t base = hb + uint32_t(v & 1) * NC * 1024u;
         const uint32_t cbase = hb + uint32_t(v & 1) * 2 * 1024u;
-        u32x4_t Kb[NC], Vc[2 * DB];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) Kb[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, vlane, base + c * 1024u, 0);
+        for (int c = 0; c < NC; ++c) g.Kb[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, vlane, base + c * 1024u, 0);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc)
-                Vc[2 * db + cc] = __builtin_amdgcn_raw_buffer_load_b128(rv, vlane, cbase + (4 * db + cc) * 1024u, 0);
+                g.Vc[2 * db + cc] = __builtin_amdgcn_raw_buffer_load_b128(rv, vlane, cbase + (4 * db + cc) * 1024u, 0);
+    };
+    auto body1 = [&](int v, uint32_t ent, const Regs1 &g) {
+        const int real = min(32, int(ent >> 25) + 1 - 32 * (v % HPU));
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            f32x16_t S = s_block(qb, Kb, false);
+            f32x16_t S = s_block(qb, g.Kb, false);
             mask_pad(S, real);
             float mx = S[0];
 #pragma unroll
@@ -541,11 +558,15 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
             const bf16x8_t p0 = pack8(Pm, 0), p1 = pack8(Pm, 1);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Vc[2 * db]), p0, O[db][qb], 0, 0, 0);
-                O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Vc[2 * db + 1]), p1, O[db][qb], 0, 0, 0);
+                O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(g.Vc[2 * db]), p0, O[db][qb], 0, 0, 0);
+                O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(g.Vc[2 * db + 1]), p1, O[db][qb], 0, 0, 0);
             }
         }
-    });
+    };
+    {
+        Regs1 ga, gb;
+        walk(fetch1, body1, ga, gb);
+    }
     float lse[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -578,27 +599,31 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
     f32x16_t G[DB][2];
 #pragma unroll
     for (int db = 0; db < DB; ++db) G[db][0] = G[db][1] = f32x16_t{};
-    walk([&](int v, uint32_t ent) {
-        const int real = min(32, int(ent >> 25) + 1 - 32 * (v % HPU));
+    struct Regs2 {
+        u32x4_t Kb[NC], Vr[NC], Kc[2 * DB];
+    };
+    auto fetch2 = [&](int v, uint32_t ent, Regs2 &g) {
         const uint32_t hb = half_base(v, ent);
         const uint32_t kbase = hb + uint32_t(v & 1) * NC * 1024u;
         const uint32_t cbase = hb + uint32_t(v & 1) * 2 * 1024u;
-        u32x4_t Kb[NC], Vr[NC], Kc[2 * DB];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            Kb[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, vlane, kbase + c * 1024u, 0);
-            Vr[c] = __builtin_amdgcn_raw_buffer_load_b128(rvr, vlane, kbase + c * 1024u, 0);
+            g.Kb[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, vlane, kbase + c * 1024u, 0);
+            g.Vr[c] = __builtin_amdgcn_raw_buffer_load_b128(rvr, vlane, kbase + c * 1024u, 0);
         }
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc)
-                Kc[2 * db + cc] = __builtin_amdgcn_raw_buffer_load_b128(rkc, vlane, cbase + (4 * db + cc) * 1024u, 0);
+                g.Kc[2 * db + cc] = __builtin_amdgcn_raw_buffer_load_b128(rkc, vlane, cbase + (4 * db + cc) * 1024u, 0);
+    };
+    auto body2 = [&](int v, uint32_t ent, const Regs2 &g) {
+        const int real = min(32, int(ent >> 25) + 1 - 32 * (v % HPU));
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            f32x16_t S = s_block(qb, Kb, false);
+            f32x16_t S = s_block(qb, g.Kb, false);
             mask_pad(S, real);
-            const f32x16_t dP = s_block(qb, Vr, true);
+            const f32x16_t dP = s_block(qb, g.Vr, true);
             f32x16_t dS;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -608,11 +633,15 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
             const bf16x8_t d0 = pack8(dS, 0), d1 = pack8(dS, 1);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                G[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Kc[2 * db]), d0, G[db][qb], 0, 0, 0);
-                G[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Kc[2 * db + 1]), d1, G[db][qb], 0, 0, 0);
+                G[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(g.Kc[2 * db]), d0, G[db][qb], 0, 0, 0);
+                G[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(g.Kc[2 * db + 1]), d1, G[db][qb], 0, 0, 0);
             }
         }
-    });
+    };
+    {
+        Regs2 ga, gb;
+        walk(fetch2, body2, ga, gb);
+    }
 
     // ---- epilogue: dq = scale dQ_fine + dqm / n (fp32, natural order)
     const float inv_n = 1.0f / float(a.block_len[tile]);
@@ -639,20 +668,25 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
 
 // ------------------------------------------------------------------ dkdv --
 //
-// One wavefront per (head, key tile, 32 key rows). The wave holds its keys'
-// K^T and V^T operand fragments (natural rows) and the dK^T, dV^T
+// One wavefront per (head, key tile, 32 key rows), the key tile's waves in one
+// workgroup. The wave holds its keys' K^T and V^T operand fragments (natural rows) and the dK^T, dV^T
 // accumulators (lane = key column), and walks the query tiles of the key
-// tile's transposed list, 32 query rows at a time:
+// tile's transposed list, 32 query rows (one "block") at a time:
 //   S = Q K^T, P = exp2(S c2 - lse), dP = dO V^T, dS = P (dP - D),
 //   dV^T += dO^T P, dK^T += Q^T dS.
+// Every operand is a coalesced 1 KB fragment of the tile-ordered copies; the
+// row-layout operands and row statistics of the next block are fetched while
+// the current one is computed (two register sets, the loop unrolled by two).
 template <int D, int B>
-__global__ __launch_bounds__(64, 1) void dkdv_kernel(BwdArgs a)
+__global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
 {
-    constexpr int SUB = B / 64, NC = D / 16, DB = D / 32, FR = D / 8, KB = B / 32;
-    const int lane = threadIdx.x, l32 = lane & 31, half = lane >> 5;
-    const int per_head = a.n_t * KB;
-    const int h = blockIdx.x / per_head, r = blockIdx.x % per_head;
-    const int tile = r / KB, kb = r % KB;
+    constexpr int SUB = B / 64, NC = D / 16, DB = D / 32, FR = D / 8;
+    // One workgroup per (head, key tile): wave kb owns key rows 32kb..32kb+31.
+    // The waves walk the same query list in step, so the second wave's
+    // fragment reads are served by the CU's L1.
+    const int lane = threadIdx.x % kWave, l32 = lane & 31, half = lane >> 5;
+    const int kb = threadIdx.x / kWave;
+    const int h = blockIdx.x / a.n_t, tile = blockIdx.x % a.n_t;
     const size_t S_pad = size_t(a.n_t) * B;
 
     // Own keys as B operands: lane -> key 32kb + l32 of the tile, slots d = 16c + 8 half + e.
@@ -672,69 +706,89 @@ __global__ __launch_bounds__(64, 1) void dkdv_kernel(BwdArgs a)
 #pragma unroll
     for (int db = 0; db < DB; ++db) GK[db] = GV[db] = f32x16_t{};
     const float c2 = a.scale_log2e;
-    const size_t head_frag = size_t(h) * a.n_t * SUB;  // 64-row blocks before this head
+    const size_t head_blk = size_t(h) * a.n_t * SUB;  // 64-row blocks before this head
 
     const int cnt = a.tcount[size_t(h) * a.n_t + tile];
     const int32_t *lst = a.tlist + (size_t(h) * a.n_t + tile) * a.n_t;
-    for (int x = 0; x < cnt; ++x) {
-        const int qt = __builtin_amdgcn_readfirstlane(lst[x]);
-        for (int qs = 0; qs < SUB; ++qs) {
-            const size_t blk = (head_frag + size_t(qt) * SUB + qs) * FR;  // fragment index of the block
+    const int n_blocks = cnt * SUB * 2;  // 32-row query blocks (even)
+
+    // Operands of block b: query tile lst[b / (2 SUB)], 64-row block (b / 2) % SUB, half b % 2.
+    struct RowOps {
+        u32x4_t Qr[NC], Or[NC];
+        float4 L4[4], D4[4];
+    };
+    auto frag_base = [&](int b) -> size_t {
+        const int qt = __builtin_amdgcn_readfirstlane(lst[b / (2 * SUB)]);
+        return (head_blk + size_t(qt) * SUB + (b / 2) % SUB) * FR;
+    };
+    auto row0 = [&](int b) -> size_t {
+        const int qt = __builtin_amdgcn_readfirstlane(lst[b / (2 * SUB)]);
+        return size_t(h) * S_pad + size_t(qt) * B + 64 * ((b / 2) % SUB) + 32 * (b % 2);
+    };
+    auto fetch = [&](int b, RowOps &o) {
+        const size_t fb = frag_base(b), r0 = row0(b);
+        const int qb = b % 2;
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int q0 = qt * B + 64 * qs + 32 * qb;  // first query row of this 32-row block
-                // A operands: query rows q0 + l32 (natural Q / dO rows), slots d.
-                const int qtok = a.row_src[q0 + l32];
-                const size_t qbase = (size_t(qtok < 0 ? 0 : qtok) * a.H + h) * D + 8 * half;
-                bf16x8_t Qr[NC], Or[NC];
+        for (int c = 0; c < NC; ++c) {
+            const size_t f = (fb + qb * NC + c) * 512 + lane * 8;   // row fragment qb*(D/16) + c
+            o.Qr[c] = *reinterpret_cast<const u32x4_t *>(a.qrow + f);
+            o.Or[c] = *reinterpret_cast<const u32x4_t *>(a.dorow + f);
+        }
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    Qr[c] = *reinterpret_cast<const bf16x8_t *>(a.q + qbase + 16 * c);
-                    Or[c] = *reinterpret_cast<const bf16x8_t *>(a.dout + qbase + 16 * c);
-                    if (qtok < 0) Qr[c] = Or[c] = bf16x8_t{};
-                }
-                // Row statistics of the accumulator rows 8i + 4 half + j.
-                float4 L4[4], D4[4];
+        for (int i = 0; i < 4; ++i) {
+            o.L4[i] = *reinterpret_cast<const float4 *>(a.lse + r0 + 8 * i + 4 * half);
+            o.D4[i] = *reinterpret_cast<const float4 *>(a.dt + r0 + 8 * i + 4 * half);
+        }
+    };
+    auto compute = [&](int b, const RowOps &o) {
+        const size_t fb = frag_base(b);
+        const int qb = b % 2;
+        f32x16_t S = f32x16_t{}, dP = f32x16_t{};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const size_t off = size_t(h) * S_pad + q0 + 8 * i + 4 * half;
-                    L4[i] = *reinterpret_cast<const float4 *>(a.lse + off);
-                    D4[i] = *reinterpret_cast<const float4 *>(a.dt + off);
-                }
-                f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+        for (int c = 0; c < NC; ++c) {
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(o.Qr[c]), Kt[c], S, 0, 0, 0);
+            dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(o.Or[c]), Vt[c], dP, 0, 0, 0);
+        }
+        // Column-fragment A operands of this 32-row block: chunks 2qb, 2qb+1.
+        u32x4_t Oc[2 * DB], Qc[2 * DB];
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Qr[c], Kt[c], S, 0, 0, 0);
-                    dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Or[c], Vt[c], dP, 0, 0, 0);
-                }
-                f32x16_t Pm, dS;
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float lv[4] = {L4[i].x, L4[i].y, L4[i].z, L4[i].w};
-                    const float dv[4] = {D4[i].x, D4[i].y, D4[i].z, D4[i].w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float p = __builtin_amdgcn_exp2f(S[4 * i + j] * c2 - lv[j]);
-                        Pm[4 * i + j] = p;
-                        dS[4 * i + j] = p * (dP[4 * i + j] - dv[j]);
-                    }
-                }
-                const bf16x8_t p0 = pack8(Pm, 0), p1 = pack8(Pm, 1);
-                const bf16x8_t s0 = pack8(dS, 0), s1 = pack8(dS, 1);
-                // Column-fragment A operands of this 32-row block: chunks 2qb, 2qb+1.
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const size_t f0 = (blk + 4 * db + 2 * qb) * 512 + lane * 8;
-                    const bf16x8_t o0 = *reinterpret_cast<const bf16x8_t *>(a.docol + f0);
-                    const bf16x8_t o1 = *reinterpret_cast<const bf16x8_t *>(a.docol + f0 + 512);
-                    const bf16x8_t q0f = *reinterpret_cast<const bf16x8_t *>(a.qcol + f0);
-                    const bf16x8_t q1f = *reinterpret_cast<const bf16x8_t *>(a.qcol + f0 + 512);
-                    GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o0, p0, GV[db], 0, 0, 0);
-                    GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o1, p1, GV[db], 0, 0, 0);
-                    GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q0f, s0, GK[db], 0, 0, 0);
-                    GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q1f, s1, GK[db], 0, 0, 0);
-                }
+            for (int cc = 0; cc < 2; ++cc) {
+                const size_t f = (fb + 4 * db + 2 * qb + cc) * 512 + lane * 8;
+                Oc[2 * db + cc] = *reinterpret_cast<const u32x4_t *>(a.docol + f);
+                Qc[2 * db + cc] = *reinterpret_cast<const u32x4_t *>(a.qcol + f);
             }
+        f32x16_t Pm, dS;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lv[4] = {o.L4[i].x, o.L4[i].y, o.L4[i].z, o.L4[i].w};
+            const float dv[4] = {o.D4[i].x, o.D4[i].y, o.D4[i].z, o.D4[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float p = __builtin_amdgcn_exp2f(S[4 * i + j] * c2 - lv[j]);
+                Pm[4 * i + j] = p;
+                dS[4 * i + j] = p * (dP[4 * i + j] - dv[j]);
+            }
+        }
+        const bf16x8_t p0 = pack8(Pm, 0), p1 = pack8(Pm, 1);
+        const bf16x8_t s0 = pack8(dS, 0), s1 = pack8(dS, 1);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Oc[2 * db]), p0, GV[db], 0, 0, 0);
+            GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Oc[2 * db + 1]), p1, GV[db], 0, 0, 0);
+            GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Qc[2 * db]), s0, GK[db], 0, 0, 0);
+            GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Qc[2 * db + 1]), s1, GK[db], 0, 0, 0);
+        }
+    };
+    if (n_blocks > 0) {
+        RowOps A, Bo;
+        fetch(0, A);
+        for (int b = 0; b < n_blocks; b += 2) {
+            fetch(b + 1, Bo);
+            compute(b, A);
+            if (b + 2 < n_blocks) fetch(b + 2, A);
+            compute(b + 1, Bo);
         }
     }
     if (ktok < 0) return;
@@ -784,6 +838,8 @@ void compute_bwd_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_
     L->kcol = take(H * S_pad * D * 2);
     L->qcol = take(H * S_pad * D * 2);
     L->docol = take(H * S_pad * D * 2);
+    L->qrow = take(H * S_pad * D * 2);
+    L->dorow = take(H * S_pad * D * 2);
     L->lse = take(H * S_pad * 4);
     L->dt = take(H * S_pad * 4);
     L->doc = take(H * n_t * D * 4);
@@ -818,6 +874,10 @@ void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, 
                            H, n_t, reinterpret_cast<uint16_t *>(bw + L.qcol));
         hipLaunchKernelGGL((frag_gather_kernel<D, B, 0>), gg, dim3(256), 0, st, dout, a.row_src,
                            a.block_len, H, n_t, reinterpret_cast<uint16_t *>(bw + L.docol));
+        hipLaunchKernelGGL((frag_gather_kernel<D, B, 1>), gg, dim3(256), 0, st, q, a.row_src, a.block_len,
+                           H, n_t, reinterpret_cast<uint16_t *>(bw + L.qrow));
+        hipLaunchKernelGGL((frag_gather_kernel<D, B, 1>), gg, dim3(256), 0, st, dout, a.row_src,
+                           a.block_len, H, n_t, reinterpret_cast<uint16_t *>(bw + L.dorow));
     }
     auto *doc = reinterpret_cast<float *>(bw + L.doc);
     {
@@ -848,7 +908,7 @@ void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, 
     }
     {
         KernelTimer t(K_BWD_DKDV, st);
-        hipLaunchKernelGGL((dkdv_kernel<D, B>), dim3(H * n_t * (B / 32)), dim3(64), 0, st, a);
+        hipLaunchKernelGGL((dkdv_kernel<D, B>), dim3(H * n_t), dim3(B * 2), 0, st, a);
     }
 }
 
@@ -924,6 +984,8 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
     a.kcol = reinterpret_cast<const uint16_t *>(bw + BL.kcol);
     a.qcol = reinterpret_cast<const uint16_t *>(bw + BL.qcol);
     a.docol = reinterpret_cast<const uint16_t *>(bw + BL.docol);
+    a.qrow = reinterpret_cast<const uint16_t *>(bw + BL.qrow);
+    a.dorow = reinterpret_cast<const uint16_t *>(bw + BL.dorow);
     a.kn = static_cast<const uint16_t *>(k);
     a.vn = static_cast<const uint16_t *>(v);
     a.row_src = row_src_dev;
