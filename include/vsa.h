@@ -294,11 +294,12 @@ int vsa_sparse_attn_fwd_ref(const vsa_plan_info *info, const int32_t *row_src_de
  *
  * vsa_bwd_layout -- scratch regions (device, caller-owned, 256-byte aligned):
  * fragment copies (V / Q / dO rows, K / Q / dO columns), per-row log-sum-exp and D_t,
- * the coarse-path gradients, and the transposed key lists ([H][n_t][n_t]).
+ * the coarse-path gradients, the transposed key lists ([H][n_t][n_t]), and,
+ * when the forward splits its key lists, fp32 dQ partials of 8 key chunks.
  */
 typedef struct vsa_bwd_layout {
     size_t vrow, kcol, qcol, docol, qrow, dorow, lse, dt, doc, dqm, dkm, dvm, lsec, dcc, tlist,
-        tcount;
+        tcount, part_dq;
     size_t total_bytes;
 } vsa_bwd_layout;
 
@@ -362,7 +363,7 @@ int vsa_gate_proj(const void *x, const void *w_gate, int64_t rows, int32_t hidde
  * vsa_timing_read -- for the kernel named `kernel` (one of "gate_gemm",
  * "gather_pool", "video_scores", "coarse_attn", "topk", "fine_attn",
  * "merge", "bwd_gather", "bwd_prep", "bwd_coarse", "bwd_tlist", "bwd_dq",
- * "bwd_dkdv"), waits for the recorded launches since the last enable and returns
+ * "bwd_dkdv", "bwd_stats"), waits for the recorded launches since the last enable and returns
  * their number in *launches and their summed duration in *total_ms (host
  * pointers). Errors: VSA_ERR_ARG for a null pointer or an unknown name,
  * VSA_ERR_DEVICE if an event query fails.

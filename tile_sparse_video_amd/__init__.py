@@ -36,7 +36,8 @@ EXPORTED = (
     "vsa_sparse_attn_fwd_ref", "vsa_bwd_workspace_layout", "vsa_sparse_attn_bwd",
 )
 TIMED_KERNELS = ("gate_gemm", "gather_pool", "video_scores", "coarse_attn", "topk", "fine_attn",
-                 "merge", "bwd_gather", "bwd_prep", "bwd_coarse", "bwd_tlist", "bwd_dq", "bwd_dkdv")
+                 "merge", "bwd_gather", "bwd_prep", "bwd_coarse", "bwd_tlist", "bwd_dq", "bwd_dkdv",
+                 "bwd_stats")
 
 
 class VsaError(RuntimeError):
@@ -63,7 +64,7 @@ class vsa_ws_layout(ctypes.Structure):
 class vsa_bwd_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("vrow", "kcol", "qcol", "docol", "qrow", "dorow", "lse", "dt", "doc", "dqm", "dkm",
-                 "dvm", "lsec", "dcc", "tlist", "tcount", "total_bytes")]
+                 "dvm", "lsec", "dcc", "tlist", "tcount", "part_dq", "total_bytes")]
 
 
 def _load() -> ctypes.CDLL:

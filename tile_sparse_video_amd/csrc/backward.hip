@@ -383,6 +383,7 @@ struct BwdArgs {
     float *lse;                     // [H][S_pad], log2 domain (+inf on padding rows)
     const float *dqm, *dkm, *dvm;   // [H][n_t][D]
     float *dq, *dk, *dv;            // natural [S][H][D]
+    float *part_dq;                 // split dq: [items][8][D/32][2][64][16] fp32
     int H, P, n_v, n_t, k, ref, list_len;
     float scale, scale_log2e;
 };
@@ -394,14 +395,19 @@ struct BwdArgs {
 // per 32-key half. Pass 1 forms S^T = K Q^T and the per-query log-sum-exp
 // (written for the key-major kernel); pass 2 forms S^T, P^T, dP^T = V dO^T,
 // dS^T = P^T (dP^T - D) and dQ^T += K^T dS^T.
-template <int D, int B>
+template <int D, int B, bool SPLIT>
 __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
 {
     constexpr int SUB = B / 64, NC = D / 16, DB = D / 32, FR = D / 8, HPU = 2 * SUB;
     constexpr int kListCap = 896;
     const int lane = threadIdx.x, l32 = lane & 31, half = lane >> 5;
     const int per_head = a.n_t * SUB;
-    const int item = blockIdx.x, h = item / per_head, r = item % per_head;
+    // Split: 8 chunks by key tile id mod 8, chunk = block % 8 so that chunk c
+    // runs on XCD c (as the forward); the log-sum-exp and D_t come from the
+    // statistics pass and each chunk writes a partial dQ.
+    const int item = SPLIT ? int(blockIdx.x / 8) : int(blockIdx.x);
+    const int chunk = SPLIT ? int(blockIdx.x % 8) : 0;
+    const int h = item / per_head, r = item % per_head;
     const int tile = r / SUB, qsub = r % SUB;
     const bool dense = !a.ref && tile < a.P;
     const int n_list = a.ref ? a.list_len : dense ? a.n_t : a.P + a.k;
@@ -453,7 +459,8 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
             int count = 0;
             while (scan < n_list) {
                 const int n = scan + lane;
-                const int t = n < n_list ? tile_at(n) : -1;
+                int t = n < n_list ? tile_at(n) : -1;
+                if (SPLIT && t % 8 != chunk) t = -1;
                 const uint64_t mask = __ballot(t >= 0);
                 const int take = __popcll(mask);
                 if (count + take > kListCap) break;
@@ -563,13 +570,20 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
             }
         }
     };
-    {
+    float lse[2];
+    if (SPLIT) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const size_t row = size_t(h) * S_pad + tile * B + 64 * qsub + 32 * qb + l32;
+            lse[qb] = a.lse[row];
+            dq_row[qb] = a.dt[row];
+        }
+    } else {
         Regs1 ga, gb;
         walk(fetch1, body1, ga, gb);
     }
-    float lse[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < 2 && !SPLIT; ++qb) {
         const size_t row = size_t(h) * S_pad + tile * B + 64 * qsub + 32 * qb + l32;
         // D_t = sum_d dout[d] O_fine[d]; O^T acc 4i + j <-> d = 32db + 8i + 4 half + j.
         float part = 0.f;
@@ -643,6 +657,21 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
         walk(fetch2, body2, ga, gb);
     }
 
+    if (SPLIT) {
+        // partial dQ^T of this chunk, fp32 in register order: [item][8][DB][2][64][16]
+        float *pd = a.part_dq + (size_t(item) * 8 + chunk) * (DB * 2 * kWave * 16);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                float4 *dst = reinterpret_cast<float4 *>(pd + ((db * 2 + qb) * kWave + lane) * 16);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    dst[q4] = make_float4(G[db][qb][4 * q4], G[db][qb][4 * q4 + 1], G[db][qb][4 * q4 + 2],
+                                          G[db][qb][4 * q4 + 3]);
+            }
+        return;
+    }
     // ---- epilogue: dq = scale dQ_fine + dqm / n (fp32, natural order)
     const float inv_n = 1.0f / float(a.block_len[tile]);
     const float *gm = a.dqm + (size_t(h) * a.n_t + tile) * D;
@@ -663,6 +692,54 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
                 o.w = a.scale * G[db][qb][4 * i + 3] + mm.w * inv_n;
                 *reinterpret_cast<float4 *>(dst + d0) = o;
             }
+    }
+}
+
+// Sums the 8 chunk partials of one item (in chunk order) and writes
+// dq = scale dQ_fine + dqm / n. One wavefront per item, lanes as the dq kernel.
+template <int D, int B>
+__global__ __launch_bounds__(256) void dq_merge_kernel(BwdArgs a, int n_items)
+{
+    constexpr int SUB = B / 64, DB = D / 32;
+    const int lane = threadIdx.x % kWave, half = lane >> 5, l32 = lane & 31;
+    const int item = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (item >= n_items) return;
+    const int h = item / (a.n_t * SUB), r = item % (a.n_t * SUB);
+    const int tile = r / SUB, qsub = r % SUB;
+    const float inv_n = 1.0f / float(a.block_len[tile]);
+    const float *gm = a.dqm + (size_t(h) * a.n_t + tile) * D;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int tok = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
+        if (tok < 0) continue;
+        float *dst = a.dq + (size_t(tok) * a.H + h) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            float acc[16] = {};
+            for (int c = 0; c < 8; ++c) {
+                const float4 *src = reinterpret_cast<const float4 *>(
+                    a.part_dq + (size_t(item) * 8 + c) * (DB * 2 * kWave * 16) + ((db * 2 + qb) * kWave + lane) * 16);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const float4 v = src[q4];
+                    acc[4 * q4] += v.x;
+                    acc[4 * q4 + 1] += v.y;
+                    acc[4 * q4 + 2] += v.z;
+                    acc[4 * q4 + 3] += v.w;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = 32 * db + 8 * i + 4 * half;
+                const float4 mm = *reinterpret_cast<const float4 *>(gm + d0);
+                float4 o;
+                o.x = a.scale * acc[4 * i] + mm.x * inv_n;
+                o.y = a.scale * acc[4 * i + 1] + mm.y * inv_n;
+                o.z = a.scale * acc[4 * i + 2] + mm.z * inv_n;
+                o.w = a.scale * acc[4 * i + 3] + mm.w * inv_n;
+                *reinterpret_cast<float4 *>(dst + d0) = o;
+            }
+        }
     }
 }
 
@@ -850,6 +927,9 @@ void compute_bwd_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_
     L->dcc = take(H * n_t * 4);
     L->tlist = take(H * n_t * n_t * 4);
     L->tcount = take(H * n_t * 4);
+    // Split dq partials, only when the forward splits its key lists.
+    const size_t items = H * n_t * size_t(info.tile_rows / 64);
+    L->part_dq = take(split_chunks(info, head_dim) > 1 ? items * 8 * 64 * D * 4 : 0);
     L->total_bytes = off;
 }
 
@@ -859,7 +939,7 @@ template <int D, int B>
 void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, const uint16_t *v,
                 const uint16_t *q, const uint16_t *dout, const uint16_t *gate,
                 const float *o_coarse, const float *qm, const float *km, const float *vm,
-                const vsa_bwd_layout &L, char *bw, float *dgate, hipStream_t st)
+                const vsa_bwd_layout &L, char *bw, float *dgate, bool split, hipStream_t st)
 {
     constexpr int HPB = 256 / D;
     const int H = a.H, n_t = a.n_t;
@@ -902,9 +982,14 @@ void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, 
                            a.n_v, n_t, a.k, a.list_len, reinterpret_cast<int32_t *>(bw + L.tlist),
                            reinterpret_cast<int32_t *>(bw + L.tcount));
     }
-    {
+    const int items = H * n_t * (B / 64);
+    if (split) {
         KernelTimer t(K_BWD_DQ, st);
-        hipLaunchKernelGGL((dq_kernel<D, B>), dim3(H * n_t * (B / 64)), dim3(64), 0, st, a);
+        hipLaunchKernelGGL((dq_kernel<D, B, true>), dim3(items * 8), dim3(64), 0, st, a);
+        hipLaunchKernelGGL((dq_merge_kernel<D, B>), dim3((items + 3) / 4), dim3(256), 0, st, a, items);
+    } else {
+        KernelTimer t(K_BWD_DQ, st);
+        hipLaunchKernelGGL((dq_kernel<D, B, false>), dim3(items), dim3(64), 0, st, a);
     }
     {
         KernelTimer t(K_BWD_DKDV, st);
@@ -1017,15 +1102,27 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
     const auto *kk = static_cast<const uint16_t *>(k), *vv = static_cast<const uint16_t *>(v);
     const auto *qq = static_cast<const uint16_t *>(q), *dd = static_cast<const uint16_t *>(dout);
     const auto *gg = static_cast<const uint16_t *>(gate);
+    a.part_dq = reinterpret_cast<float *>(bw + BL.part_dq);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
+    // Large heads: the log-sum-exp and D_t come from the forward's split kernel
+    // and a statistics merge, and dQ is split the same way; small heads
+    // recompute them inside the dq kernel.
+    bool split = false;
+    if (split_chunks(*info, head_dim) > 1) {
+        const int stv = fine_stats(*info, row_src_dev, block_len_dev, heads, head_dim, ref, k_gen,
+                                   ref ? k_ref : 0, a.scale, q, workspace, keep_idx_dev, dout,
+                                   reinterpret_cast<float *>(bw + BL.lse),
+                                   reinterpret_cast<float *>(bw + BL.dt), st);
+        split = stv == VSA_OK;
+    }
     const int B = info->tile_rows;
     if (head_dim == 128) {
-        if (B == 64) launch_bwd<128, 64>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
-        else launch_bwd<128, 128>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
+        if (B == 64) launch_bwd<128, 64>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, st);
+        else launch_bwd<128, 128>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, st);
     } else {
-        if (B == 64) launch_bwd<64, 64>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
-        else launch_bwd<64, 128>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, st);
+        if (B == 64) launch_bwd<64, 64>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, st);
+        else launch_bwd<64, 128>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, st);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(VSA_ERR_DEVICE, "%s: kernel launch failed: %s", name, hipGetErrorString(e));

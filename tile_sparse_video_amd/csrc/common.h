@@ -26,13 +26,22 @@ void compute_bwd_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_
 // Number of key chunks the fine pass splits each key list into (1 = no split).
 int split_chunks(const vsa_plan_info &info, int head_dim);
 
+// Backward support: runs the fine pass with split key lists and a merge that
+// writes the per-row log-sum-exp (log2 domain) and D_t = dout . O_fine
+// ([H][S_pad], tile order). Returns VSA_ERR_UNSUPPORTED when the heads are
+// too small to split (the caller then recomputes the statistics itself).
+int fine_stats(const vsa_plan_info &info, const int32_t *row_src, const int32_t *block_len, int heads,
+               int head_dim, bool ref, int k, int k_ref, float scale, const void *q,
+               const void *workspace, const int32_t *keep_idx, const void *dout, float *lse_out,
+               float *dt_out, hipStream_t st);
+
 // Checks that the current HIP device is a gfx950; caches the answer per device.
 int check_device();
 
 // Kernels whose launches vsa_timing_read can report.
 enum KernelId {
     K_GATE_GEMM, K_GATHER_POOL, K_VIDEO_SCORES, K_COARSE_ATTN, K_TOPK, K_FINE_ATTN, K_MERGE,
-    K_BWD_GATHER, K_BWD_PREP, K_BWD_COARSE, K_BWD_TLIST, K_BWD_DQ, K_BWD_DKDV,
+    K_BWD_GATHER, K_BWD_PREP, K_BWD_COARSE, K_BWD_TLIST, K_BWD_DQ, K_BWD_DKDV, K_BWD_STATS,
     K_COUNT
 };
 

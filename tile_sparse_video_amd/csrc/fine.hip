@@ -77,6 +77,10 @@ struct FineArgs {
     int H, P, n_v, n_t, k, chunks;
     int ref;                    // reference sparsity: every tile has an explicit list
     int list_len;               // ref: entries per list (k_ref + k_gen), keep is [H][n_t][list_len]
+    // Statistics merge (backward support): per tile-order row, the log2-domain
+    // log-sum-exp and D_t = dout . O_fine instead of the gated output.
+    const uint16_t *dout;       // [S][H][D]
+    float *lse_out, *dt_out;    // [H][S_pad]
     float scale_log2e;
 };
 
@@ -409,7 +413,7 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
 // M = max_c m_c, w_c = l_c 2^((m_c - M) scale log2 e), O = sum_c w_c (O/l)_c,
 // L = sum_c w_c, then the same gated epilogue as the direct path.
 // One wavefront per item, lanes laid out as in the fine kernel.
-template <int D, int B>
+template <int D, int B, bool STATS>
 __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
 {
     constexpr int SUB = B / 64, DB = D / 32;
@@ -464,6 +468,36 @@ __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
                 }
             }
     }
+    if (STATS) {
+        // lse (log2 domain) and D_t = dout . O_fine per row; +inf / 0 on padding rows.
+        const size_t S_pad = size_t(a.n_t) * B;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int row = tile * B + 64 * qsub + 32 * qb + l32;
+            const int tok = a.row_src[row];
+            float part = 0.f;
+            if (tok >= 0) {
+                const uint16_t *go = a.dout + (size_t(tok) * a.H + h) * D;
+                const float inv = 1.0f / L[qb];
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint2 raw = *reinterpret_cast<const uint2 *>(go + 32 * db + 8 * i + 4 * half);
+                        part += __uint_as_float(raw.x << 16) * O[db][qb][4 * i] * inv;
+                        part += __uint_as_float(raw.x & 0xffff0000u) * O[db][qb][4 * i + 1] * inv;
+                        part += __uint_as_float(raw.y << 16) * O[db][qb][4 * i + 2] * inv;
+                        part += __uint_as_float(raw.y & 0xffff0000u) * O[db][qb][4 * i + 3] * inv;
+                    }
+            }
+            part = xhalf_sum(part);  // both halves hold the full sum
+            if (half == 0) {
+                a.lse_out[size_t(h) * S_pad + row] = tok < 0 ? INFINITY : M[qb] * c2 + __log2f(L[qb]);
+                a.dt_out[size_t(h) * S_pad + row] = tok < 0 ? 0.f : part;
+            }
+        }
+        return;
+    }
     const float *oc = a.o_coarse + (size_t(h) * a.n_t + tile) * D;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -492,14 +526,69 @@ void launch_fine(const FineArgs &a, hipStream_t st)
             hipLaunchKernelGGL((fine_attn_kernel<D, B, true>), dim3(items * a.chunks), dim3(64), 0, st, a);
         }
         KernelTimer t(K_MERGE, st);
-        hipLaunchKernelGGL((merge_kernel<D, B>), dim3((items + 3) / 4), dim3(256), 0, st, a, items);
+        hipLaunchKernelGGL((merge_kernel<D, B, false>), dim3((items + 3) / 4), dim3(256), 0, st, a, items);
     } else {
         KernelTimer t(K_FINE_ATTN, st);
         hipLaunchKernelGGL((fine_attn_kernel<D, B, false>), dim3(items), dim3(64), 0, st, a);
     }
 }
 
+// Statistics pass for the backward (key lists split into C > 1 chunks): the
+// forward's split kernel, then a merge that writes lse and D_t per row.
+template <int D, int B>
+void launch_fine_stats(const FineArgs &a, hipStream_t st)
+{
+    const int items = a.H * a.n_t * (B / 64);
+    {
+        KernelTimer t(K_BWD_STATS, st);
+        hipLaunchKernelGGL((fine_attn_kernel<D, B, true>), dim3(items * a.chunks), dim3(64), 0, st, a);
+        hipLaunchKernelGGL((merge_kernel<D, B, true>), dim3((items + 3) / 4), dim3(256), 0, st, a, items);
+    }
+}
+
 }  // namespace
+
+int fine_stats(const vsa_plan_info &info, const int32_t *row_src, const int32_t *block_len, int heads,
+               int head_dim, bool ref, int k, int k_ref, float scale, const void *q,
+               const void *workspace, const int32_t *keep_idx, const void *dout, float *lse_out,
+               float *dt_out, hipStream_t st)
+{
+    vsa_ws_layout L;
+    compute_layout(info, heads, head_dim, &L);
+    const char *ws = static_cast<const char *>(workspace);
+    FineArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.kt = reinterpret_cast<const uint16_t *>(ws + L.k_tiled);
+    a.vt = reinterpret_cast<const uint16_t *>(ws + L.v_tiled);
+    a.row_src = row_src;
+    a.block_len = block_len;
+    a.keep = keep_idx;
+    a.part_o = reinterpret_cast<uint16_t *>(const_cast<char *>(ws) + L.part_o);
+    a.part_ml = reinterpret_cast<float *>(const_cast<char *>(ws) + L.part_ml);
+    a.H = heads;
+    a.P = info.n_prefix_tiles;
+    a.n_v = info.n_video_tiles;
+    a.n_t = info.n_tiles;
+    a.k = k;
+    a.chunks = split_chunks(info, head_dim);
+    a.ref = ref ? 1 : 0;
+    a.list_len = ref ? k + k_ref : 0;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    a.dout = static_cast<const uint16_t *>(dout);
+    a.lse_out = lse_out;
+    a.dt_out = dt_out;
+    if (a.chunks < 2) return VSA_ERR_UNSUPPORTED;  // small heads: the caller recomputes instead
+    const int B = info.tile_rows;
+    if (head_dim == 128) {
+        if (B == 64) launch_fine_stats<128, 64>(a, st);
+        else launch_fine_stats<128, 128>(a, st);
+    } else {
+        if (B == 64) launch_fine_stats<64, 64>(a, st);
+        else launch_fine_stats<64, 128>(a, st);
+    }
+    return VSA_OK;
+}
+
 }  // namespace vsa
 
 using namespace vsa;
