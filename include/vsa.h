@@ -295,11 +295,12 @@ int vsa_sparse_attn_fwd_ref(const vsa_plan_info *info, const int32_t *row_src_de
  * vsa_bwd_layout -- scratch regions (device, caller-owned, 256-byte aligned):
  * fragment copies (V / Q / dO rows, K / Q / dO columns), per-row log-sum-exp and D_t,
  * the coarse-path gradients, the transposed key lists ([H][n_t][n_t]), and,
- * when the forward splits its key lists, fp32 dQ partials of 8 key chunks.
+ * when the forward splits its key lists, fp32 dQ partials of 8 key chunks
+ * and fp32 dK / dV partials of 8 query chunks.
  */
 typedef struct vsa_bwd_layout {
     size_t vrow, kcol, qcol, docol, qrow, dorow, lse, dt, doc, dqm, dkm, dvm, lsec, dcc, tlist,
-        tcount, part_dq;
+        tcount, part_dq, part_dkv;
     size_t total_bytes;
 } vsa_bwd_layout;
 

@@ -64,7 +64,7 @@ class vsa_ws_layout(ctypes.Structure):
 class vsa_bwd_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("vrow", "kcol", "qcol", "docol", "qrow", "dorow", "lse", "dt", "doc", "dqm", "dkm",
-                 "dvm", "lsec", "dcc", "tlist", "tcount", "part_dq", "total_bytes")]
+                 "dvm", "lsec", "dcc", "tlist", "tcount", "part_dq", "part_dkv", "total_bytes")]
 
 
 def _load() -> ctypes.CDLL:

@@ -384,6 +384,7 @@ struct BwdArgs {
     const float *dqm, *dkm, *dvm;   // [H][n_t][D]
     float *dq, *dk, *dv;            // natural [S][H][D]
     float *part_dq;                 // split dq: [items][8][D/32][2][64][16] fp32
+    float *part_dkv;                // split dk/dv: [H][n_t][8][B/32][2][D/32][64][16] fp32
     int H, P, n_v, n_t, k, ref, list_len;
     float scale, scale_log2e;
 };
@@ -754,16 +755,22 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdArgs a, int n_items)
 // Every operand is a coalesced 1 KB fragment of the tile-ordered copies; the
 // row-layout operands and row statistics of the next block are fetched while
 // the current one is computed (two register sets, the loop unrolled by two).
-template <int D, int B>
+template <int D, int B, bool SPLIT>
 __global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
 {
-    constexpr int SUB = B / 64, NC = D / 16, DB = D / 32, FR = D / 8;
+    constexpr int SUB = B / 64, NC = D / 16, DB = D / 32, FR = D / 8, KB = B / 32;
+    constexpr int kListCap = 4096;
     // One workgroup per (head, key tile): wave kb owns key rows 32kb..32kb+31.
     // The waves walk the same query list in step, so the second wave's
-    // fragment reads are served by the CU's L1.
+    // fragment reads are served by the CU's L1. Split: 8 workgroups per key
+    // tile, chunk c = block % 8 (so on XCD c) taking the query tiles with id
+    // = c mod 8, each writing partial dK, dV.
     const int lane = threadIdx.x % kWave, l32 = lane & 31, half = lane >> 5;
     const int kb = threadIdx.x / kWave;
-    const int h = blockIdx.x / a.n_t, tile = blockIdx.x % a.n_t;
+    const int ht = SPLIT ? int(blockIdx.x / 8) : int(blockIdx.x);
+    const int chunk = SPLIT ? int(blockIdx.x % 8) : 0;
+    const int h = ht / a.n_t, tile = ht % a.n_t;
+    __shared__ int32_t flist[SPLIT ? kListCap : 1];
     const size_t S_pad = size_t(a.n_t) * B;
 
     // Own keys as B operands: lane -> key 32kb + l32 of the tile, slots d = 16c + 8 half + e.
@@ -785,8 +792,26 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
     const float c2 = a.scale_log2e;
     const size_t head_blk = size_t(h) * a.n_t * SUB;  // 64-row blocks before this head
 
-    const int cnt = a.tcount[size_t(h) * a.n_t + tile];
+    int cnt = a.tcount[size_t(h) * a.n_t + tile];
     const int32_t *lst = a.tlist + (size_t(h) * a.n_t + tile) * a.n_t;
+    if (SPLIT) {
+        // This chunk's query tiles, compacted in order into LDS by wave 0.
+        if (kb == 0) {
+            int n = 0;
+            for (int x0 = 0; x0 < cnt; x0 += kWave) {
+                const int x = x0 + lane;
+                const int qt = x < cnt ? lst[x] : -1;
+                const bool m = qt >= 0 && qt % 8 == chunk;
+                const uint64_t bal = __ballot(m);
+                if (m) flist[n + __popcll(bal & lanes_below(lane))] = qt;
+                n += __popcll(bal);
+            }
+            if (lane == 0) flist[kListCap - 1] = n;
+        }
+        __syncthreads();
+        cnt = flist[kListCap - 1];
+        lst = flist;
+    }
     const int n_blocks = cnt * SUB * 2;  // 32-row query blocks (even)
 
     // Operands of block b: query tile lst[b / (2 SUB)], 64-row block (b / 2) % SUB, half b % 2.
@@ -868,6 +893,21 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
             compute(b + 1, Bo);
         }
     }
+    if (SPLIT) {
+        // partial dK^T, dV^T, fp32 in register order: [H][n_t][8][KB][2][DB][64][16]
+        float *pd = a.part_dkv + ((size_t(ht) * 8 + chunk) * KB + kb) * (2 * DB * kWave * 16);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            float4 *dk4 = reinterpret_cast<float4 *>(pd + (db * kWave + lane) * 16);
+            float4 *dv4 = reinterpret_cast<float4 *>(pd + ((DB + db) * kWave + lane) * 16);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                dk4[q4] = make_float4(GK[db][4 * q4], GK[db][4 * q4 + 1], GK[db][4 * q4 + 2], GK[db][4 * q4 + 3]);
+                dv4[q4] = make_float4(GV[db][4 * q4], GV[db][4 * q4 + 1], GV[db][4 * q4 + 2], GV[db][4 * q4 + 3]);
+            }
+        }
+        return;
+    }
     if (ktok < 0) return;
     // dk = scale dK_fine + dkm / n, dv = dV_fine + dvm / n; acc 4i + j <-> d = 32db + 8i + 4 half + j.
     const float inv_n = 1.0f / float(a.block_len[tile]);
@@ -896,10 +936,71 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
         }
 }
 
+// Sums the 8 chunk partials of one (head, key tile, 32 key rows) in chunk
+// order and writes dk = scale dK + dkm / n, dv = dV + dvm / n for real keys.
+template <int D, int B>
+__global__ __launch_bounds__(256) void dkdv_merge_kernel(BwdArgs a, int n_units)
+{
+    constexpr int DB = D / 32, KB = B / 32;
+    const int lane = threadIdx.x % kWave, half = lane >> 5, l32 = lane & 31;
+    const int unit = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (unit >= n_units) return;
+    const int ht = unit / KB, kb = unit % KB;
+    const int h = ht / a.n_t, tile = ht % a.n_t;
+    const int ktok = a.row_src[size_t(tile) * B + 32 * kb + l32];
+    if (ktok < 0) return;
+    const float inv_n = 1.0f / float(a.block_len[tile]);
+    const float *gk = a.dkm + (size_t(h) * a.n_t + tile) * D;
+    const float *gv = a.dvm + (size_t(h) * a.n_t + tile) * D;
+    float *dk = a.dk + (size_t(ktok) * a.H + h) * D;
+    float *dv = a.dv + (size_t(ktok) * a.H + h) * D;
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            float acc[16] = {};
+            for (int c = 0; c < 8; ++c) {
+                const float4 *src = reinterpret_cast<const float4 *>(
+                    a.part_dkv + ((size_t(ht) * 8 + c) * KB + kb) * (2 * DB * kWave * 16) +
+                    ((kv * DB + db) * kWave + lane) * 16);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const float4 v = src[q4];
+                    acc[4 * q4] += v.x;
+                    acc[4 * q4 + 1] += v.y;
+                    acc[4 * q4 + 2] += v.z;
+                    acc[4 * q4 + 3] += v.w;
+                }
+            }
+            const float sc = kv == 0 ? a.scale : 1.0f;
+            const float *gm = kv == 0 ? gk : gv;
+            float *dst = kv == 0 ? dk : dv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = 32 * db + 8 * i + 4 * half;
+                const float4 mm = *reinterpret_cast<const float4 *>(gm + d0);
+                float4 o;
+                o.x = sc * acc[4 * i] + mm.x * inv_n;
+                o.y = sc * acc[4 * i + 1] + mm.y * inv_n;
+                o.z = sc * acc[4 * i + 2] + mm.z * inv_n;
+                o.w = sc * acc[4 * i + 3] + mm.w * inv_n;
+                *reinterpret_cast<float4 *>(dst + d0) = o;
+            }
+        }
+}
+
 }  // namespace
 }  // namespace vsa
 
 namespace vsa {
+
+// The dK/dV pass splits its query lists into 8 XCD-affine chunks when the
+// heads are large (as the forward) and the fp32 partials stay within 64 GiB.
+bool dkdv_split(const vsa_plan_info &info, int heads, int head_dim)
+{
+    const double bytes = double(heads) * info.n_tiles * 8 * (info.tile_rows / 32) * 2 * 32 * head_dim * 4;
+    return split_chunks(info, head_dim) > 1 && info.n_tiles <= 4095 && bytes <= 64.0 * (1 << 30);
+}
 
 void compute_bwd_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_bwd_layout *L)
 {
@@ -930,6 +1031,7 @@ void compute_bwd_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_
     // Split dq partials, only when the forward splits its key lists.
     const size_t items = H * n_t * size_t(info.tile_rows / 64);
     L->part_dq = take(split_chunks(info, head_dim) > 1 ? items * 8 * 64 * D * 4 : 0);
+    L->part_dkv = take(dkdv_split(info, heads, head_dim) ? H * n_t * 8 * size_t(info.tile_rows / 32) * 2 * 32 * D * 4 : 0);
     L->total_bytes = off;
 }
 
@@ -993,7 +1095,13 @@ void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, 
     }
     {
         KernelTimer t(K_BWD_DKDV, st);
-        hipLaunchKernelGGL((dkdv_kernel<D, B>), dim3(H * n_t), dim3(B * 2), 0, st, a);
+        if (dkdv_split(info, H, D)) {
+            hipLaunchKernelGGL((dkdv_kernel<D, B, true>), dim3(H * n_t * 8), dim3(B * 2), 0, st, a);
+            const int units = H * n_t * (B / 32);
+            hipLaunchKernelGGL((dkdv_merge_kernel<D, B>), dim3((units + 3) / 4), dim3(256), 0, st, a, units);
+        } else {
+            hipLaunchKernelGGL((dkdv_kernel<D, B, false>), dim3(H * n_t), dim3(B * 2), 0, st, a);
+        }
     }
 }
 
@@ -1103,6 +1211,7 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
     const auto *qq = static_cast<const uint16_t *>(q), *dd = static_cast<const uint16_t *>(dout);
     const auto *gg = static_cast<const uint16_t *>(gate);
     a.part_dq = reinterpret_cast<float *>(bw + BL.part_dq);
+    a.part_dkv = reinterpret_cast<float *>(bw + BL.part_dkv);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     // Large heads: the log-sum-exp and D_t come from the forward's split kernel
