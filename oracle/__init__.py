@@ -27,6 +27,7 @@ _lib = None
 _I32P = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 _I64P = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
 _U16P = np.ctypeslib.ndpointer(dtype=np.uint16, flags="C_CONTIGUOUS")
+_I8P = np.ctypeslib.ndpointer(dtype=np.int8, flags="C_CONTIGUOUS")
 _F32P = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
 _F64P = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 
@@ -73,6 +74,11 @@ def _load():
     lib.orc_fine_tokens_lists.argtypes = [_U16P, _U16P, _U16P, i32, i32, i32, _I32P, _I32P, i32,
                                           i32, _I32P, i32, f64, _I64P, i64, _F64P]
     lib.orc_fine_tokens_lists.restype = ctypes.c_int
+    lib.orc_quant_blocks_i8.argtypes = [_U16P, i32, i32, i32, _I32P, i32, i32, _I8P, _F32P]
+    lib.orc_quant_blocks_i8.restype = ctypes.c_int
+    lib.orc_fine_tokens_i8.argtypes = [_U16P, _U16P, _U16P, i32, i32, i32, _I32P, _I32P, i32, i32,
+                                       _I32P, _I32P, f64, _I64P, i64, _F64P]
+    lib.orc_fine_tokens_i8.restype = ctypes.c_int
     lib.orc_layer_bwd.argtypes = [_U16P, _U16P, _U16P, _U16P, _U16P, i32, i32, i32, _I32P, _I32P,
                                   _I32P, i32, i32, _I32P, _I32P, _F32P, _F32P, _F32P, f64, _F64P,
                                   _F64P, _F64P, _F64P]
@@ -341,6 +347,38 @@ def layer_tokens_ref(Q, K, V, g: np.ndarray, h: int, pl: Plan, hr: "HeadResult",
     tiles = pl.untile[toks] // pl.B
     g_rows = (g if g_is_rows else g[toks])[:, h * D:(h + 1) * D]
     return combine(o_fine, np.ascontiguousarray(g_rows), hr.o_coarse[tiles]), o_fine
+
+
+# ------------------------------------------------------------ INT8 fine pass --
+
+def quant_blocks_i8(X, h: int, pl: Plan):
+    """Symmetric INT8 codes of head h's rows in tiled order, one fp32 scale per
+    64-row block: (codes int8 [n_t*B][D], scales fp32 [n_t*B/64])."""
+    lib = _load()
+    S, H, D = X.shape
+    codes = np.zeros((pl.S_pad, D), dtype=np.int8)
+    scales = np.zeros(pl.S_pad // 64, dtype=np.float32)
+    rc = lib.orc_quant_blocks_i8(np.ascontiguousarray(X).reshape(-1), H, D, int(h), pl.row_src,
+                                 pl.n_t, pl.B, codes.reshape(-1), scales)
+    if rc != 0:
+        raise OracleError("INT8 blocks need B to be a multiple of 64")
+    return codes, scales
+
+
+def fine_tokens_i8(Q, K, V, h: int, pl: Plan, csr, scale: float, tokens) -> np.ndarray:
+    """O_fine (fp64 [n_tok][D]) with INT8 scores over CSR key lists (off, ids)."""
+    lib = _load()
+    S, H, D = Q.shape
+    off, ids = csr
+    toks = np.ascontiguousarray(np.asarray(list(tokens), dtype=np.int64))
+    out = np.empty((toks.size, D), dtype=np.float64)
+    rc = lib.orc_fine_tokens_i8(*(np.ascontiguousarray(X).reshape(-1) for X in (Q, K, V)), H, D,
+                                int(h), pl.untile, pl.row_src, pl.n_t, pl.B,
+                                np.ascontiguousarray(off, dtype=np.int32), ids, float(scale), toks,
+                                int(toks.size), out.reshape(-1))
+    if rc != 0:
+        raise OracleError("INT8 fine attention: an empty or invalid key list")
+    return out
 
 
 # ---------------------------------------------------------------- backward --

@@ -477,6 +477,136 @@ int orc_fine_tokens_lists(const uint16_t *Q, const uint16_t *K, const uint16_t *
     return bad ? -1 : 0;
 }
 
+/* ------------------------------------------------- INT8 fine pass (NEXT) -- */
+/*
+ * [Veda] "How Veda works" and its performance table: the tile-skip kernel
+ * computes attention in INT8. The pages give no scheme; the reading taken
+ * here is the plain symmetric one: Q and K of a head are quantised in blocks
+ * of 64 rows of the tiled layout (padding rows are zero), one fp32 scale per
+ * block, and only the score product q.k uses the INT8 codes; the softmax and
+ * the P.V product keep full precision.
+ *
+ * Block quantisation, all in fp32:
+ *   a     = max over the block of |x|           (exact: a bf16 is an fp32)
+ *   scale = a / 127                             (0 when a == 0)
+ *   code  = round-half-even(x * (127 / a)), clamped to [-127, 127]
+ *                                               (0 when a == 0)
+ * codes: int8 [n_t * B][D] in tiled row order; scales: fp32 [n_t * B / 64].
+ * Returns 0, or -1 if B is not a multiple of 64.
+ */
+int orc_quant_blocks_i8(const uint16_t *X, int32_t H, int32_t D, int32_t h, const int32_t *row_src,
+                        int32_t n_t, int32_t B, int8_t *codes, float *scales)
+{
+    if (B % 64 != 0) return -1;
+    const int64_t n_blocks = (int64_t)n_t * B / 64;
+    for (int64_t b = 0; b < n_blocks; ++b) {
+        float a = 0.0f;
+        for (int32_t r = 0; r < 64; ++r) {
+            int32_t u = row_src[b * 64 + r];
+            if (u < 0) continue;
+            for (int32_t d = 0; d < D; ++d) {
+                float x = fabsf(bf16_to_float(X[((int64_t)u * H + h) * D + d]));
+                if (x > a) a = x;
+            }
+        }
+        float inv = a > 0.0f ? 127.0f / a : 0.0f;
+        scales[b] = a > 0.0f ? a / 127.0f : 0.0f;
+        for (int32_t r = 0; r < 64; ++r) {
+            int32_t u = row_src[b * 64 + r];
+            int8_t *c = codes + (b * 64 + r) * D;
+            for (int32_t d = 0; d < D; ++d) {
+                float y = u < 0 ? 0.0f : rintf(bf16_to_float(X[((int64_t)u * H + h) * D + d]) * inv);
+                if (y > 127.0f) y = 127.0f;
+                if (y < -127.0f) y = -127.0f;
+                c[d] = (int8_t)y;
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * O_fine with INT8 scores, for the given query tokens of head h over CSR key
+ * lists (tiles lst[off[i]..off[i+1]) for query tile i): for a query in block
+ * bq and a key in block bk,
+ *   z = scale * sq[bq] * sk[bk] * (integer dot product of their codes),
+ * then softmax and P.V in fp64 as O7. Returns 0, or -1 on an empty key list
+ * or a bad argument.
+ */
+int orc_fine_tokens_i8(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int32_t H, int32_t D,
+                       int32_t h, const int32_t *untile, const int32_t *row_src, int32_t n_t, int32_t B,
+                       const int32_t *off, const int32_t *lst, double scale, const int64_t *tokens,
+                       int64_t n_tok, double *out)
+{
+    if (D > 256 || B % 64 != 0) return -1;
+    const int64_t rows = (int64_t)n_t * B;
+    int8_t *cq = (int8_t *)malloc((size_t)rows * (size_t)D);
+    int8_t *ck = (int8_t *)malloc((size_t)rows * (size_t)D);
+    float *sq = (float *)malloc(sizeof(float) * (size_t)(rows / 64));
+    float *sk = (float *)malloc(sizeof(float) * (size_t)(rows / 64));
+    int bad = 0;
+    if (!cq || !ck || !sq || !sk) {
+        bad = 1;
+        goto done;
+    }
+    orc_quant_blocks_i8(Q, H, D, h, row_src, n_t, B, cq, sq);
+    orc_quant_blocks_i8(K, H, D, h, row_src, n_t, B, ck, sk);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t qi = 0; qi < n_tok; ++qi) {
+        const int64_t rq = untile[tokens[qi]];
+        const int32_t tile = (int32_t)(rq / B);
+        const int8_t *a = cq + rq * D;
+        const int32_t n_keys_tiles = off[tile + 1] - off[tile];
+        size_t cap = (size_t)(n_keys_tiles > 0 ? n_keys_tiles : 1) * (size_t)B;
+        double *z = (double *)malloc(sizeof(double) * cap);
+        int64_t *u_of = (int64_t *)malloc(sizeof(int64_t) * cap);
+        int64_t nk = 0;
+        double zmax = -INFINITY;
+        for (int32_t e = off[tile]; e < off[tile + 1]; ++e) {
+            const int32_t j = lst[e];
+            if (j < 0 || j >= n_t) {
+                bad = 1;
+                continue;
+            }
+            for (int32_t r = 0; r < B; ++r) {
+                const int64_t rk = (int64_t)j * B + r;
+                const int32_t u = row_src[rk];
+                if (u < 0) continue;
+                const int8_t *b = ck + rk * D;
+                int64_t dot = 0;
+                for (int32_t d = 0; d < D; ++d) dot += (int64_t)a[d] * (int64_t)b[d];
+                z[nk] = scale * (double)sq[rq / 64] * (double)sk[rk / 64] * (double)dot;
+                u_of[nk] = u;
+                if (z[nk] > zmax) zmax = z[nk];
+                ++nk;
+            }
+        }
+        if (nk == 0) {
+            bad = 1;
+        } else {
+            double denom = 0.0;
+            for (int64_t x = 0; x < nk; ++x) {
+                z[x] = exp(z[x] - zmax);
+                denom += z[x];
+            }
+            for (int32_t d = 0; d < D; ++d) out[qi * D + d] = 0.0;
+            for (int64_t x = 0; x < nk; ++x) {
+                const uint16_t *v = V + (u_of[x] * H + h) * D;
+                for (int32_t d = 0; d < D; ++d) out[qi * D + d] += z[x] * (double)bf16_to_float(v[d]);
+            }
+            for (int32_t d = 0; d < D; ++d) out[qi * D + d] /= denom;
+        }
+        free(z);
+        free(u_of);
+    }
+done:
+    free(cq);
+    free(ck);
+    free(sq);
+    free(sk);
+    return bad ? -1 : 0;
+}
+
 /* ------------------------------------------------------ backward (NEXT) -- */
 /*
  * Gradient of the layer for one head. The method is trainable ([SnackOnAI]
