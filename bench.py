@@ -36,6 +36,10 @@ import workloads  # noqa: E402
 METRIC = "ms/layer + effective TFLOP/s (% bf16 MFMA peak) for tile-sparse attn at ~100k tok"
 BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (vendor figure)
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E (vendor figure)
+INT8_PEAK_TOPS = 5033.2     # MI355X dense int8 MFMA (vendor figure)
+# INT8 fine pass: per kept pair 2D int8 ops (scores) at the int8 peak and 2D bf16
+# flops (P.V) at the bf16 peak, so 4D operations take 2D/INT8 + 2D/BF16 at best.
+MIXED_PEAK_TOPS = 2.0 / (1.0 / INT8_PEAK_TOPS + 1.0 / BF16_PEAK_TFLOPS)
 
 
 def effective_fine_flops(plan, keep_idx: np.ndarray, heads: int, head_dim: int,
@@ -57,9 +61,9 @@ def effective_fine_flops(plan, keep_idx: np.ndarray, heads: int, head_dim: int,
     return 4.0 * head_dim * float(pairs)
 
 
-def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops, k_ref=None):
+def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops, k_ref=None, int8=False):
     """The oracle, as it stands, on a bounded sample of this layer, scaled to one layer.
-    k_ref is not None in the reference-sparsity mode."""
+    k_ref is not None in the reference-sparsity mode; int8 times the INT8 fine pass."""
     import oracle
     Qb, Kb, Vb = (workloads.bf16_bits(t) for t in (q, k, v))
     xb, wb = workloads.bf16_bits(x), workloads.bf16_bits(w)
@@ -76,6 +80,12 @@ def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops, k_ref=None):
 
         def fine(toks):
             return oracle.fine_tokens_lists(Qb, Kb, Vb, 0, pl, hr.keep, scale, toks)
+    if int8:
+        csr = (oracle.key_lists_default(pl, hr.keep) if k_ref is None
+               else oracle.key_lists_explicit(hr.keep))
+
+        def fine(toks):
+            return oracle.fine_tokens_i8(Qb, Kb, Vb, 0, pl, csr, scale, toks)
     t_head = time.perf_counter() - t0
     rng = np.random.default_rng(0)
     vid = rng.choice(np.arange(pl.S)[pl.untile // pl.B >= pl.P], size=2048, replace=False)
@@ -258,6 +268,8 @@ def main() -> int:
     ap.add_argument("--reference-sparsity", type=float, default=None, metavar="S",
                     help="run the reference-sparsity mode: every query tile keeps the top "
                          "(1-S) of the prefix tiles as well as the top video tiles")
+    ap.add_argument("--int8", action="store_true",
+                    help="run the fine pass with INT8 scores (vsa_sparse_attn_fwd_i8)")
     ap.add_argument("--backward", action="store_true",
                     help="time the layer's training step instead: forward plus the backward "
                          "pass (gradients of q, k, v and the gate)")
@@ -276,6 +288,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
         return 0
+    if args.int8 and args.backward:
+        print("--int8 times the forward only; the backward pass is bf16", file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
               "(the layer shards by head with no exchange; see the design notes)", file=sys.stderr)
@@ -296,7 +311,7 @@ def main() -> int:
     qd, kd, vd, xd, wd = (t.to(dev) for t in (q, k, v, x, w))
     att = tsv.TileSparseAttention(wl.prefix_segments, wl.grid, wl.tile, wl.heads, wl.head_dim,
                                   sparsity=wl.sparsity, keep_k=wl.keep_k, device=dev,
-                                  reference_sparsity=args.reference_sparsity)
+                                  reference_sparsity=args.reference_sparsity, int8=args.int8)
     g = torch.empty((wl.tokens, wl.heads * wl.head_dim), dtype=torch.bfloat16, device=dev)
     out = torch.empty_like(qd)
     stream = torch.cuda.current_stream()
@@ -347,7 +362,8 @@ def main() -> int:
     tflops = fine_flops / (layer_ms * 1e-3) / 1e12
     fine_kernel_ms = kernels["fine_attn"]["avg_ms"]
     fine_tflops = fine_flops / (fine_kernel_ms * 1e-3) / 1e12
-    traffic = None if att.ref else recorded_traffic(wl.name)
+    traffic = None if (att.ref or args.int8) else recorded_traffic(wl.name)
+    peak = MIXED_PEAK_TOPS if args.int8 else BF16_PEAK_TFLOPS
     frac_pairs = att.tile_pair_fraction()
 
     result = {
@@ -361,10 +377,11 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "int8 scores, bf16 P.V" if args.int8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: {wl.note}",
+            "int8": args.int8,
             "heads": wl.heads, "head_dim": wl.head_dim, "hidden": wl.hidden,
             "tokens": wl.tokens, "prefix_segments": list(wl.prefix_segments),
             "grid": list(wl.grid), "tile": list(wl.tile), "keep_k": att.k,
@@ -383,12 +400,14 @@ def main() -> int:
         "effective_fine_tflop": round(fine_flops / 1e12, 3),
         "wall_s": round(wall, 3),
         "roofline": {
-            "kernel": "fine_attn_kernel (vsa_sparse_attn_fwd; its merge kernel is timed apart)",
+            "kernel": ("fine_attn_kernel, INT8 scores (vsa_sparse_attn_fwd_i8; peak mixes the "
+                       "int8 and bf16 MFMA peaks per kept pair)" if args.int8 else
+                       "fine_attn_kernel (vsa_sparse_attn_fwd; its merge kernel is timed apart)"),
             "bound": "mfma",
             "achieved": round(fine_tflops, 2),
-            "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(fine_tflops / BF16_PEAK_TFLOPS, 4),
+            "peak": round(peak, 1),
+            "unit": "TOP/s" if args.int8 else "TFLOP/s",
+            "frac": round(fine_tflops / peak, 4),
             "algorithmic_tflop_per_launch": round(fine_flops / 1e12, 4),
             "avg_launch_ms": fine_kernel_ms,
             "traffic": None if traffic is None else traffic["bytes_per_launch"],
@@ -398,7 +417,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, q, k, v, x, w, att.plan, att.k, fine_flops,
-                                              att.k_ref if att.ref else None)
+                                              att.k_ref if att.ref else None, args.int8)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -164,12 +164,15 @@ int vsa_tile_pair_fraction_ref(const vsa_plan_info *info, int32_t k_ref, int32_t
  *     into C chunks (by tile id modulo C; C = 8 for heads whose K and V exceed
  *     16 MiB, 8 * ceil(K+V / 96 MiB) beyond 96 MiB): per chunk, bf16 O / l and
  *     the fp32 running max and sum of every 64 query rows. Zero when C = 1.
+ *   k_i8, k_scale: INT8 K codes and fp32 block scales written by
+ *     vsa_sparse_attn_fwd_i8 (layout there).
  * The layout depends on the split count, so query it after any
  * vsa_set_split_chunks call.
  */
 typedef struct vsa_ws_layout {
     size_t k_tiled, v_tiled, q_mean, k_mean, v_mean, scores;
     size_t part_o, part_ml;  /* fine-pass chunk partials (empty when not split) */
+    size_t k_i8, k_scale;    /* INT8 fine pass: K codes and block scales */
     size_t total_bytes;
 } vsa_ws_layout;
 
@@ -278,6 +281,35 @@ int vsa_sparse_attn_fwd_ref(const vsa_plan_info *info, const int32_t *row_src_de
                             const int32_t *keep_idx_dev, const float *o_coarse_dev,
                             const void *gate, void *out, void *stream);
 
+/*
+ * vsa_sparse_attn_fwd_i8 -- the fine pass with INT8 scores. [Veda] "How Veda
+ * works" and its performance table: the tile-skip kernel computes attention
+ * in INT8; the pages give no scheme, and the one below is this library's
+ * reading. Q and K of each head are quantised in blocks of 64 rows of the
+ * tiled layout (padding rows are zero), all in fp32:
+ *   a = max |x| over the block, scale = a / 127,
+ *   code = round-half-even(x * (127 / a)) clamped to [-127, 127]
+ *   (a block with a = 0 has scale 0 and zero codes).
+ * For a query in block bq and a key in block bk the score is
+ *   scale_attn * s_q[bq] * s_k[bk] * (exact integer dot product of the codes);
+ * the softmax, P.V (P in bf16, fp32 accumulation) and the gated combination
+ * are those of vsa_sparse_attn_fwd.
+ * k_ref < 0: default mode (key sets as vsa_sparse_attn_fwd with k = k_gen);
+ * k_ref >= 0: reference-sparsity mode (key sets as vsa_sparse_attn_fwd_ref).
+ * The K codes and scales are first written to the workspace regions k_i8
+ * (int8 [H][n_t][B/64] blocks of 2*(D/32) fragments of 64 lanes x 16 codes:
+ * fragment f = kb*(D/32) + c, lane l, byte e = code of K[row 32*kb + l%32]
+ * [d = 32*c + 16*(l/32) + e]) and k_scale (fp32 [H][n_t][B/64]) from
+ * k_tiled, so the workspace is written here; Q is quantised inside the
+ * fine kernel. Other arguments and errors as vsa_sparse_attn_fwd(_ref).
+ */
+int vsa_sparse_attn_fwd_i8(const vsa_plan_info *info, const int32_t *row_src_dev,
+                           const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                           int32_t k_ref, int32_t k_gen, float scale, const void *q,
+                           void *workspace, size_t workspace_bytes,
+                           const int32_t *keep_idx_dev, const float *o_coarse_dev,
+                           const void *gate, void *out, void *stream);
+
 /* --------------------------------------------------------- backward -- */
 /*
  * Backward pass: the gradient of the layer with the keep sets held fixed (a
@@ -364,7 +396,7 @@ int vsa_gate_proj(const void *x, const void *w_gate, int64_t rows, int32_t hidde
  * vsa_timing_read -- for the kernel named `kernel` (one of "gate_gemm",
  * "gather_pool", "video_scores", "coarse_attn", "topk", "fine_attn",
  * "merge", "bwd_gather", "bwd_prep", "bwd_coarse", "bwd_tlist", "bwd_dq",
- * "bwd_dkdv", "bwd_stats"), waits for the recorded launches since the last enable and returns
+ * "bwd_dkdv", "bwd_stats", "quant_k"), waits for the recorded launches since the last enable and returns
  * their number in *launches and their summed duration in *total_ms (host
  * pointers). Errors: VSA_ERR_ARG for a null pointer or an unknown name,
  * VSA_ERR_DEVICE if an event query fails.

@@ -308,3 +308,39 @@ def test_ref_entry_points_reject_bad_arguments():
     for got, want in cases:
         assert got == want, (got, want, lib.vsa_last_error())
     assert b"empty key set" in (fine(k_ref=0, k_gen=0, keep=0), lib.vsa_last_error())[1]
+
+
+def test_i8_entry_point_rejects_bad_arguments():
+    pl = tsv.vsa_plan_tiles([20, 40], (4, 8, 8), (4, 4, 4))
+    info = pl.info
+    lib = tsv._lib
+
+    def fine(heads=2, head_dim=128, k_ref=-1, k_gen=1, keep=FAKE, ws_bytes=1 << 40, q=FAKE,
+             scale=0.0):
+        return lib.vsa_sparse_attn_fwd_i8(ctypes.byref(info), FAKE, FAKE, heads, head_dim, k_ref,
+                                          k_gen, scale, q, FAKE * 2, ws_bytes, keep, FAKE, FAKE,
+                                          FAKE, None)
+
+    E = tsv
+    cases = [
+        (fine(head_dim=96), E.VSA_ERR_UNSUPPORTED),
+        (fine(heads=0), E.VSA_ERR_ARG),
+        (fine(k_gen=pl.n_v + 1), E.VSA_ERR_ARG),
+        (fine(k_ref=pl.P + 1), E.VSA_ERR_ARG),                 # ref mode: k_ref beyond P
+        (fine(k_ref=0, k_gen=0), E.VSA_ERR_ARG),               # ref mode: empty key set
+        (fine(q=0), E.VSA_ERR_ARG),
+        (fine(keep=0), E.VSA_ERR_ARG),
+        (fine(ws_bytes=1024), E.VSA_ERR_ARG),
+        (fine(scale=float("nan")), E.VSA_ERR_ARG),
+    ]
+    for got, want in cases:
+        assert got == want, (got, want, lib.vsa_last_error())
+    assert b"vsa_sparse_attn_fwd_i8" in lib.vsa_last_error()
+    # the INT8 regions: one byte per K element and one scale per 64-row block
+    wl = workloads.WORKLOADS["h3"]
+    big = tsv.cached_plan(wl.prefix_segments, wl.grid, wl.tile)
+    lay = tsv.vsa_workspace_layout(big.info, wl.heads, wl.head_dim)
+    assert lay.k_i8 % 256 == 0 and lay.k_scale % 256 == 0
+    assert lay.k_scale - lay.k_i8 >= wl.heads * big.S_pad * wl.head_dim
+    assert lay.total_bytes - lay.k_scale >= wl.heads * big.S_pad // 64 * 4
+    assert lay.k_i8 >= lay.part_ml

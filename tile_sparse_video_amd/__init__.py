@@ -34,10 +34,11 @@ EXPORTED = (
     "vsa_sparse_attn_fwd", "vsa_gate_proj", "vsa_set_split_chunks", "vsa_timing_enable",
     "vsa_timing_read", "vsa_ref_keep_count", "vsa_tile_pair_fraction_ref", "vsa_coarse_topk_ref",
     "vsa_sparse_attn_fwd_ref", "vsa_bwd_workspace_layout", "vsa_sparse_attn_bwd",
+    "vsa_sparse_attn_fwd_i8",
 )
 TIMED_KERNELS = ("gate_gemm", "gather_pool", "video_scores", "coarse_attn", "topk", "fine_attn",
                  "merge", "bwd_gather", "bwd_prep", "bwd_coarse", "bwd_tlist", "bwd_dq", "bwd_dkdv",
-                 "bwd_stats")
+                 "bwd_stats", "quant_k")
 
 
 class VsaError(RuntimeError):
@@ -58,7 +59,7 @@ class vsa_plan_info(ctypes.Structure):
 class vsa_ws_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("k_tiled", "v_tiled", "q_mean", "k_mean", "v_mean", "scores", "part_o",
-                 "part_ml", "total_bytes")]
+                 "part_ml", "k_i8", "k_scale", "total_bytes")]
 
 
 class vsa_bwd_layout(ctypes.Structure):
@@ -95,6 +96,8 @@ def _load() -> ctypes.CDLL:
                                  P, P, P], ctypes.c_int),
         "vsa_sparse_attn_fwd_ref": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, SZ, P, P, P, P,
                                      P], ctypes.c_int),
+        "vsa_sparse_attn_fwd_i8": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, SZ, P, P, P, P,
+                                    P], ctypes.c_int),
         "vsa_bwd_workspace_layout": ([info_p, I32, I32, ctypes.POINTER(vsa_bwd_layout)], ctypes.c_int),
         "vsa_sparse_attn_bwd": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, P, P, P, P, SZ, P, P,
                                  P, SZ, P, P, P, P, P], ctypes.c_int),
@@ -346,6 +349,35 @@ def vsa_sparse_attn_fwd_ref(info: vsa_plan_info, row_src_dev: torch.Tensor,
            "vsa_sparse_attn_fwd_ref")
 
 
+def vsa_sparse_attn_fwd_i8(info: vsa_plan_info, row_src_dev: torch.Tensor,
+                           block_len_dev: torch.Tensor, heads: int, head_dim: int, k_ref: int,
+                           k_gen: int, q: torch.Tensor, workspace: torch.Tensor,
+                           keep_idx: Optional[torch.Tensor], o_coarse: torch.Tensor,
+                           gate: torch.Tensor, out: torch.Tensor, scale: float = 0.0,
+                           stream=None) -> None:
+    """The fine pass with INT8 scores; k_ref < 0 selects the default mode
+    (keep_idx [H][n_v][k_gen]), k_ref >= 0 the reference-sparsity mode."""
+    S = info.rows_real
+    _need(q, "q", torch.bfloat16, (S, heads, head_dim))
+    _need(gate, "gate", torch.bfloat16)
+    if gate.numel() != S * heads * head_dim:
+        raise ValueError("gate must hold [S][heads*head_dim] values")
+    _need(out, "out", torch.bfloat16, (S, heads, head_dim))
+    _need(row_src_dev, "row_src", torch.int32, (info.rows_padded,))
+    _need(block_len_dev, "block_len", torch.int32, (info.n_tiles,))
+    _need(workspace, "workspace", torch.uint8)
+    _need(o_coarse, "o_coarse", torch.float32, (heads, info.n_tiles, head_dim))
+    if keep_idx is not None:
+        shape = ((heads, info.n_video_tiles, k_gen) if k_ref < 0
+                 else (heads, info.n_tiles, k_ref + k_gen))
+        _need(keep_idx, "keep_idx", torch.int32, shape)
+    _check(_lib.vsa_sparse_attn_fwd_i8(ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev),
+                                       heads, head_dim, int(k_ref), int(k_gen), float(scale),
+                                       _ptr(q), _ptr(workspace), workspace.numel(), _ptr(keep_idx),
+                                       _ptr(o_coarse), _ptr(gate), _ptr(out), _stream(stream)),
+           "vsa_sparse_attn_fwd_i8")
+
+
 def vsa_bwd_workspace_layout(info: vsa_plan_info, heads: int, head_dim: int) -> vsa_bwd_layout:
     lay = vsa_bwd_layout()
     _check(_lib.vsa_bwd_workspace_layout(ctypes.byref(info), int(heads), int(head_dim),
@@ -441,9 +473,11 @@ class TileSparseAttention:
     def __init__(self, prefix_segments, grid, tile, heads: int, head_dim: int,
                  sparsity: Optional[float] = None, keep_k: Optional[int] = None,
                  scale: float = 0.0, device="cuda", reference_sparsity: Optional[float] = None,
-                 ref_keep_k: Optional[int] = None):
+                 ref_keep_k: Optional[int] = None, int8: bool = False):
         """reference_sparsity / ref_keep_k (either one) switch to the reference-sparsity
-        mode: every query tile keeps k_ref prefix tiles and k video tiles."""
+        mode: every query tile keeps k_ref prefix tiles and k video tiles. int8 runs
+        the fine pass with INT8 scores (vsa_sparse_attn_fwd_i8)."""
+        self.int8 = bool(int8)
         self.plan = cached_plan(prefix_segments, grid, tile)
         info = self.plan.info
         self.heads, self.head_dim, self.scale = int(heads), int(head_dim), float(scale)
@@ -484,7 +518,12 @@ class TileSparseAttention:
 
     def fine(self, q, gate, out, stream=None) -> None:
         keep = self.keep_idx if self.list_len > 0 else None
-        if self.ref:
+        if self.int8:
+            vsa_sparse_attn_fwd_i8(self.plan.info, self.row_src, self.block_len, self.heads,
+                                   self.head_dim, self.k_ref if self.ref else -1, self.k, q,
+                                   self.workspace, keep, self.o_coarse, gate, out,
+                                   scale=self.scale, stream=stream)
+        elif self.ref:
             vsa_sparse_attn_fwd_ref(self.plan.info, self.row_src, self.block_len, self.heads,
                                     self.head_dim, self.k_ref, self.k, q, self.workspace, keep,
                                     self.o_coarse, gate, out, scale=self.scale, stream=stream)

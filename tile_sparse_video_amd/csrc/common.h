@@ -42,6 +42,7 @@ int check_device();
 enum KernelId {
     K_GATE_GEMM, K_GATHER_POOL, K_VIDEO_SCORES, K_COARSE_ATTN, K_TOPK, K_FINE_ATTN, K_MERGE,
     K_BWD_GATHER, K_BWD_PREP, K_BWD_COARSE, K_BWD_TLIST, K_BWD_DQ, K_BWD_DKDV, K_BWD_STATS,
+    K_QUANT_K,
     K_COUNT
 };
 

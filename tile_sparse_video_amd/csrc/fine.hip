@@ -81,11 +81,17 @@ struct FineArgs {
     // log-sum-exp and D_t = dout . O_fine instead of the gated output.
     const uint16_t *dout;       // [S][H][D]
     float *lse_out, *dt_out;    // [H][S_pad]
+    // INT8 scores: K codes in tile order [H][n_t][B/64][2][D/32][64][16] and one
+    // scale per 64-row block [H][n_t][B/64].
+    const uint8_t *k8;
+    const float *k_scale;
     float scale_log2e;
 };
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -129,11 +135,13 @@ __device__ __forceinline__ void store4(uint16_t *out, const uint16_t *gate, size
     *reinterpret_cast<uint2 *>(out + base + d0) = w;
 }
 
-template <int D, int B, bool SPLIT>
+template <int D, int B, bool SPLIT, bool I8 = false>
 __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
 {
     constexpr int SUB = B / 64;   // 64-row blocks per tile
     constexpr int NC = D / 16;    // reduction chunks of S = K.Q^T
+    constexpr int NC8 = D / 32;   // INT8: reduction chunks of 32 codes
+    constexpr int KN = I8 ? NC8 : NC;  // K registers (16 bytes each) per 32-key half
     constexpr int DB = D / 32;    // 32-row blocks of O^T (over d)
     constexpr int FR = D / 8;     // 1 KB fragments per 64-row block
     constexpr int HPU = 2 * SUB;  // 32-key halves per key tile
@@ -167,17 +175,71 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
     // (16 KB per wave) and re-read for every S product.
     __shared__ __attribute__((aligned(16))) bf16x8_t q_lds[2][NC][kWave];
     __shared__ uint32_t list_lds[kListCap];  // tile | (block_len - 1) << 25
+    __shared__ float list_sk[I8 ? kListCap * SUB : 1];  // INT8: K block scales of the entries
     int tok[2];
+    float sq = 0.f;  // INT8: the scale of this 64-row query block
+    if constexpr (!I8) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        tok[qb] = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
-        const uint16_t *qrow = a.q + (size_t(tok[qb] < 0 ? 0 : tok[qb]) * a.H + h) * D + 8 * half;
+        for (int qb = 0; qb < 2; ++qb) {
+            tok[qb] = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
+            const uint16_t *qrow = a.q + (size_t(tok[qb] < 0 ? 0 : tok[qb]) * a.H + h) * D + 8 * half;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            bf16x8_t v = load_frag(qrow + 16 * c);
-            if (tok[qb] < 0) v = bf16x8_t{};
-            q_lds[qb][c][lane] = v;
+            for (int c = 0; c < NC; ++c) {
+                bf16x8_t v = load_frag(qrow + 16 * c);
+                if (tok[qb] < 0) v = bf16x8_t{};
+                q_lds[qb][c][lane] = v;
+            }
         }
+    } else {
+        // INT8 B operand: lane -> query 32qb + l32, code slot e of chunk c ->
+        // d = 32c + 16*half + e (the K codes use the same slots). The block's
+        // scale is max|q| / 127 over its 64 rows (padding rows are zero); the
+        // codes are round-half-even(q * (127 / max|q|)), all in fp32.
+        u32x4_t raw[2][NC8][2];
+        float amax = 0.f;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            tok[qb] = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
+            const uint16_t *qrow = a.q + (size_t(tok[qb] < 0 ? 0 : tok[qb]) * a.H + h) * D + 16 * half;
+#pragma unroll
+            for (int c = 0; c < NC8; ++c)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    u32x4_t v = *reinterpret_cast<const u32x4_t *>(qrow + 32 * c + 8 * j);
+                    if (tok[qb] < 0) v = u32x4_t{};
+                    raw[qb][c][j] = v;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(v[w] << 16)),
+                                                 fabsf(__uint_as_float(v[w] & 0xffff0000u))));
+                }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        amax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(amax)));
+        const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+        sq = amax > 0.f ? amax / 127.0f : 0.f;
+        auto code = [&](float x) -> uint32_t {
+            const float y = fminf(fmaxf(__builtin_rintf(x * inv), -127.f), 127.f);
+            return uint32_t(int(y)) & 0xffu;
+        };
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int c = 0; c < NC8; ++c) {
+                u32x4_t w;
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int t2 = 0; t2 < 2; ++t2) {
+                        const uint32_t r0 = raw[qb][c][j][2 * t2], r1 = raw[qb][c][j][2 * t2 + 1];
+                        w[2 * j + t2] = code(__uint_as_float(r0 << 16)) |
+                                        code(__uint_as_float(r0 & 0xffff0000u)) << 8 |
+                                        code(__uint_as_float(r1 << 16)) << 16 |
+                                        code(__uint_as_float(r1 & 0xffff0000u)) << 24;
+                    }
+                q_lds[qb][c][lane] = as_bf16x8(w);
+            }
     }
 
     // ---- key list source. Default: position n -> tile n (prefix, or all tiles
@@ -205,7 +267,13 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
             if (count + take > kListCap) break;  // next segment
             if (match) {
                 const int bl = a.block_len[t];
-                list_lds[count + __popcll(mask & lanes_below(lane))] = uint32_t(t) | uint32_t(bl - 1) << 25;
+                const int at = count + __popcll(mask & lanes_below(lane));
+                list_lds[at] = uint32_t(t) | uint32_t(bl - 1) << 25;
+                if constexpr (I8) {
+#pragma unroll
+                    for (int sb = 0; sb < SUB; ++sb)
+                        list_sk[at * SUB + sb] = a.k_scale[(size_t(h) * a.n_t + t) * SUB + sb];
+                }
             }
             count += take;
             scan += kWave;
@@ -219,8 +287,9 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
     // Reads outside the head's region return zero instead of faulting.
     const uint32_t head_bytes = uint32_t(a.n_t) * B * D * 2;
     const size_t head_elems = size_t(h) * a.n_t * B * D;
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(a.kt + head_elems), (short)0, head_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rk = I8
+        ? __builtin_amdgcn_make_buffer_rsrc((void *)(a.k8 + head_elems), (short)0, head_bytes / 2, kRsrcWord3)
+        : __builtin_amdgcn_make_buffer_rsrc((void *)(a.kt + head_elems), (short)0, head_bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc((void *)(a.vt + head_elems), (short)0, head_bytes, kRsrcWord3);
     const int vlane = lane * 16;
@@ -232,10 +301,11 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
         const uint32_t t = entry(v) & 0x1ffffffu;
         return (t * SUB + uint32_t((v % HPU) >> 1)) * FR * 1024u;
     };
-    auto load_k = [&](int v, u32x4_t (&Kb)[NC]) {
-        const uint32_t base = half_base(v) + uint32_t(v & 1) * NC * 1024u;
+    // INT8 codes: a 64-row block is 2 * D/32 fragments of 1 KB (half the bf16 size).
+    auto load_k = [&](int v, u32x4_t (&Kb)[KN]) {
+        const uint32_t base = (I8 ? half_base(v) / 2 : half_base(v)) + uint32_t(v & 1) * KN * 1024u;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) Kb[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, vlane, base + c * 1024u, 0);
+        for (int c = 0; c < KN; ++c) Kb[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, vlane, base + c * 1024u, 0);
     };
     auto load_v = [&](int v, u32x4_t (&Vb)[2 * DB]) {
         const uint32_t base = half_base(v) + uint32_t(v & 1) * 2 * 1024u;
@@ -261,9 +331,19 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
     // issued. The body is straight-line on purpose: halves with no real key are
     // masked rather than skipped, and the last refill re-reads a valid half, so
     // the K/V registers never merge values from different control paths.
-    auto step = [&](int v, int n_half, u32x4_t (&Kb)[NC], u32x4_t (&Vb)[2 * DB]) {
+    auto step = [&](int v, int n_half, u32x4_t (&Kb)[KN], u32x4_t (&Vb)[2 * DB]) {
         const int real = min(32, int(entry(v) >> 25) + 1 - 32 * (v % HPU));
         const int next = v + 1 < n_half ? v + 1 : v;
+        // INT8: score = (integer product) * qk with qk = s_q * s_k of the two
+        // blocks; the exponent folds qk into c2. Clamping qk and c2 * qk to the
+        // least normal keeps masked keys at -inf (an all-zero block gives
+        // integer products of 0, so its scores stay exactly 0).
+        float qk = 1.f, c2s = c2;
+        if constexpr (I8) {
+            const float sk = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(list_sk[v >> 1])));
+            qk = fmaxf(sq * sk, 1.17549435e-38f);
+            c2s = fmaxf(c2 * qk, 1.17549435e-38f);
+        }
 
         // The two 32-query blocks are independent (each lane owns one query of
         // each), so each block runs S, softmax and P.V on its own: only its S
@@ -275,13 +355,26 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
             // index opaque so they are re-read rather than hoisted into VGPRs.
             int ql = lane;
             asm volatile("" : "+v"(ql));
-            bf16x8_t Qf[NC];
+            f32x16_t S;
+            if constexpr (!I8) {
+                bf16x8_t Qf[NC];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) Qf[c] = q_lds[qb][c][ql];
-            f32x16_t S = f32x16_t{};
+                for (int c = 0; c < NC; ++c) Qf[c] = q_lds[qb][c][ql];
+                S = f32x16_t{};
 #pragma unroll
-            for (int c = 0; c < NC; ++c)
-                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Kb[c]), Qf[c], S, 0, 0, 0);
+                for (int c = 0; c < NC; ++c)
+                    S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Kb[c]), Qf[c], S, 0, 0, 0);
+            } else {
+                i32x4_t Qf[NC8];
+#pragma unroll
+                for (int c = 0; c < NC8; ++c) Qf[c] = __builtin_bit_cast(i32x4_t, q_lds[qb][c][ql]);
+                i32x16_t Si = i32x16_t{};
+#pragma unroll
+                for (int c = 0; c < NC8; ++c)
+                    Si = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, Kb[c]), Qf[c], Si, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) S[e] = float(Si[e]);
+            }
             if (qb == 1) load_k(next, Kb);
             // Padding keys (partial tiles only: a wave-uniform branch) never score.
             if (__builtin_expect(real < 32, 0)) {
@@ -302,6 +395,7 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
             for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, S[e]), S[e + 1]);
             mx = fmaxf(mx, S[15]);
             mx = xhalf_max(mx);
+            if constexpr (I8) mx *= qk;  // integer units -> score units (qk > 0)
             if (__ballot(mx > thr[qb]) != 0) {
                 const float m_new = fmaxf(m[qb], mx);
                 const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m[qb] - m_new) * c2);
@@ -321,8 +415,8 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
                 u32x4_t w;
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * cc + e], c2, moff[qb]));
-                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * cc + e + 1], c2, moff[qb]));
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * cc + e], c2s, moff[qb]));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * cc + e + 1], c2s, moff[qb]));
                     const bf16x2_t pp = {(__bf16)p0, (__bf16)p1};
                     rs = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, rs, false);
                     w[e / 2] = __builtin_bit_cast(uint32_t, pp);
@@ -345,7 +439,7 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
         load_v(next, Vb);
     };
 
-    u32x4_t Kb[NC], Vb[2 * DB];
+    u32x4_t Kb[KN], Vb[2 * DB];
     while (true) {
         const int count = fill();
         if (count > 0) {
@@ -516,20 +610,84 @@ __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
     }
 }
 
-template <int D, int B>
+// INT8 K codes for the fine pass, one wave per 64-row block of the tiled K:
+// scale = max|k| / 127 over the block (padding rows are zero), codes =
+// round-half-even(k * (127 / max|k|)) clamped to [-127, 127], in fp32; a
+// block with max|k| = 0 gets scale 0 and zero codes. Lane l of fragment
+// (kb, c) holds the 16 codes of row 32kb + l%32, d = 32c + 16*(l/32) + e; they
+// come from the bf16 fragment 2c + l/32 of the same rows, whose lanes l%32
+// and l%32 + 32 hold d .. d+7 and d+8 .. d+15.
+template <int D>
+__global__ __launch_bounds__(256) void quant_k_kernel(const uint16_t *__restrict__ kt, int64_t n_blocks,
+                                                     uint8_t *__restrict__ k8, float *__restrict__ k_scale)
+{
+    constexpr int NC8 = D / 32, NC = D / 16;
+    const int lane = threadIdx.x % kWave, l32 = lane & 31, half = lane >> 5;
+    const int64_t blk = int64_t(blockIdx.x) * 4 + threadIdx.x / kWave;
+    if (blk >= n_blocks) return;
+    const uint16_t *src = kt + blk * (D / 8) * 512;
+    u32x4_t raw[2][NC8][2];
+    float amax = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < NC8; ++c)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(
+                    src + (kb * NC + 2 * c + half) * 512 + (l32 + 32 * j) * 8);
+                raw[kb][c][j] = v;
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(v[w] << 16)),
+                                             fabsf(__uint_as_float(v[w] & 0xffff0000u))));
+            }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+    if (lane == 0) k_scale[blk] = amax > 0.f ? amax / 127.0f : 0.f;
+    auto code = [&](float x) -> uint32_t {
+        const float y = fminf(fmaxf(__builtin_rintf(x * inv), -127.f), 127.f);
+        return uint32_t(int(y)) & 0xffu;
+    };
+    uint8_t *dst = k8 + blk * (64 * D);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < NC8; ++c) {
+            u32x4_t w;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) {
+                    const uint32_t r0 = raw[kb][c][j][2 * t2], r1 = raw[kb][c][j][2 * t2 + 1];
+                    w[2 * j + t2] = code(__uint_as_float(r0 << 16)) | code(__uint_as_float(r0 & 0xffff0000u)) << 8 |
+                                    code(__uint_as_float(r1 << 16)) << 16 |
+                                    code(__uint_as_float(r1 & 0xffff0000u)) << 24;
+                }
+            *reinterpret_cast<u32x4_t *>(dst + (kb * NC8 + c) * 1024 + lane * 16) = w;
+        }
+}
+
+template <int D, int B, bool I8 = false>
 void launch_fine(const FineArgs &a, hipStream_t st)
 {
     const int items = a.H * a.n_t * (B / 64);
+    if (I8) {
+        KernelTimer t(K_QUANT_K, st);
+        hipLaunchKernelGGL((quant_k_kernel<D>), dim3((items + 3) / 4), dim3(256), 0, st, a.kt, int64_t(items),
+                           const_cast<uint8_t *>(a.k8), const_cast<float *>(a.k_scale));
+    }
     if (a.chunks > 1) {
         {
             KernelTimer t(K_FINE_ATTN, st);
-            hipLaunchKernelGGL((fine_attn_kernel<D, B, true>), dim3(items * a.chunks), dim3(64), 0, st, a);
+            hipLaunchKernelGGL((fine_attn_kernel<D, B, true, I8>), dim3(items * a.chunks), dim3(64), 0, st, a);
         }
         KernelTimer t(K_MERGE, st);
         hipLaunchKernelGGL((merge_kernel<D, B, false>), dim3((items + 3) / 4), dim3(256), 0, st, a, items);
     } else {
         KernelTimer t(K_FINE_ATTN, st);
-        hipLaunchKernelGGL((fine_attn_kernel<D, B, false>), dim3(items), dim3(64), 0, st, a);
+        hipLaunchKernelGGL((fine_attn_kernel<D, B, false, I8>), dim3(items), dim3(64), 0, st, a);
     }
 }
 
@@ -605,7 +763,7 @@ namespace {
 
 // Shared body of the two fine entry points (ref: reference-sparsity lists).
 int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_src_dev,
-              const int32_t *block_len_dev, int heads, int head_dim, bool ref, int k, int k_ref,
+              const int32_t *block_len_dev, int heads, int head_dim, bool ref, bool i8, int k, int k_ref,
               float scale, const void *q, const void *workspace, size_t workspace_bytes,
               const int32_t *keep_idx_dev, const float *o_coarse_dev, const void *gate, void *out,
               void *stream)
@@ -654,6 +812,8 @@ int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_sr
     a.out = static_cast<uint16_t *>(out);
     a.part_o = reinterpret_cast<uint16_t *>(ws + L.part_o);
     a.part_ml = reinterpret_cast<float *>(ws + L.part_ml);
+    a.k8 = reinterpret_cast<const uint8_t *>(ws + L.k_i8);
+    a.k_scale = reinterpret_cast<const float *>(ws + L.k_scale);
     a.H = heads;
     a.P = info->n_prefix_tiles;
     a.n_v = info->n_video_tiles;
@@ -668,11 +828,11 @@ int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_sr
     (void)hipGetLastError();
     const int B = info->tile_rows;
     if (head_dim == 128) {
-        if (B == 64) launch_fine<128, 64>(a, st);
-        else launch_fine<128, 128>(a, st);
+        if (B == 64) i8 ? launch_fine<128, 64, true>(a, st) : launch_fine<128, 64>(a, st);
+        else i8 ? launch_fine<128, 128, true>(a, st) : launch_fine<128, 128>(a, st);
     } else {
-        if (B == 64) launch_fine<64, 64>(a, st);
-        else launch_fine<64, 128>(a, st);
+        if (B == 64) i8 ? launch_fine<64, 64, true>(a, st) : launch_fine<64, 64>(a, st);
+        else i8 ? launch_fine<64, 128, true>(a, st) : launch_fine<64, 128>(a, st);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(VSA_ERR_DEVICE, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
@@ -690,7 +850,7 @@ extern "C" int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row
 {
     clear_error();
     return fine_impl("vsa_sparse_attn_fwd", info, row_src_dev, block_len_dev, heads, head_dim, false,
-                     k, 0, scale, q, workspace, workspace_bytes, keep_idx_dev, o_coarse_dev, gate,
+                     false, k, 0, scale, q, workspace, workspace_bytes, keep_idx_dev, o_coarse_dev, gate,
                      out, stream);
 }
 
@@ -703,6 +863,19 @@ extern "C" int vsa_sparse_attn_fwd_ref(const vsa_plan_info *info, const int32_t 
 {
     clear_error();
     return fine_impl("vsa_sparse_attn_fwd_ref", info, row_src_dev, block_len_dev, heads, head_dim,
-                     true, k_gen, k_ref, scale, q, workspace, workspace_bytes, keep_idx_dev,
+                     true, false, k_gen, k_ref, scale, q, workspace, workspace_bytes, keep_idx_dev,
                      o_coarse_dev, gate, out, stream);
+}
+
+extern "C" int vsa_sparse_attn_fwd_i8(const vsa_plan_info *info, const int32_t *row_src_dev,
+                                      const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                                      int32_t k_ref, int32_t k_gen, float scale, const void *q,
+                                      void *workspace, size_t workspace_bytes,
+                                      const int32_t *keep_idx_dev, const float *o_coarse_dev,
+                                      const void *gate, void *out, void *stream)
+{
+    clear_error();
+    return fine_impl("vsa_sparse_attn_fwd_i8", info, row_src_dev, block_len_dev, heads, head_dim,
+                     k_ref >= 0, true, k_gen, k_ref < 0 ? 0 : k_ref, scale, q, workspace,
+                     workspace_bytes, keep_idx_dev, o_coarse_dev, gate, out, stream);
 }

@@ -135,6 +135,10 @@ void compute_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_ws_l
     const size_t C = size_t(split_chunks(info, head_dim));
     L->part_o = take(C > 1 ? items * C * 64 * D * 2 : 0);
     L->part_ml = take(C > 1 ? items * C * 128 * 4 : 0);
+    // INT8 fine pass: K codes in tile order (one byte per element) and one fp32
+    // scale per 64-row block.
+    L->k_i8 = take(H * S_pad * D);
+    L->k_scale = take(items * 4);
     L->total_bytes = off;
 }
 

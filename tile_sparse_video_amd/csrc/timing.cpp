@@ -15,7 +15,7 @@ namespace {
 const char *const kNames[K_COUNT] = {"gate_gemm",  "gather_pool", "video_scores", "coarse_attn",
                                      "topk",       "fine_attn",   "merge",        "bwd_gather",
                                      "bwd_prep",   "bwd_coarse",  "bwd_tlist",    "bwd_dq",
-                                     "bwd_dkdv",   "bwd_stats"};
+                                     "bwd_dkdv",   "bwd_stats",   "quant_k"};
 
 struct Record {
     hipEvent_t start, stop;
