@@ -310,6 +310,65 @@ int vsa_sparse_attn_fwd_i8(const vsa_plan_info *info, const int32_t *row_src_dev
                            const int32_t *keep_idx_dev, const float *o_coarse_dev,
                            const void *gate, void *out, void *stream);
 
+/* ------------------------------------------------ per-head tile shapes -- */
+/*
+ * [Veda] "How Veda works": tile shapes are chosen per layer and per head, so
+ * that heads that mix mostly within a frame and heads that mix mostly across
+ * frames each get a suitable tile within the same budget. Here a layer's
+ * heads are split into groups of consecutive heads, each group with its own
+ * tile plan (any tile shape the single-plan path supports); a group runs the
+ * single-plan path (vsa_coarse_topk(_ref) then vsa_sparse_attn_fwd(_ref|_i8))
+ * on its heads, so for every head h of group i the output is exactly what the
+ * single-plan path computes for head h with plan i.
+ *
+ * vsa_head_group (host struct; the pointers in it are device pointers unless
+ * marked host):
+ *   info                 host: the group's plan (vsa_plan_tiles); all groups
+ *                        plan the same token count S.
+ *   row_src_dev, block_len_dev: the plan's arrays on the device.
+ *   head_first, heads    the group's heads [head_first, head_first + heads) of
+ *                        the heads_total heads of each token row; groups must
+ *                        not overlap (heads no group covers are not written).
+ *   sparsity, keep_k     keep rule for video key tiles (vsa_keep_count).
+ *   ref, ref_sparsity, ref_keep_k: ref != 0 selects reference sparsity with
+ *                        k_ref from vsa_ref_keep_count.
+ *   int8                 != 0: the fine pass with INT8 scores (vsa_sparse_attn_fwd_i8).
+ *   workspace, workspace_bytes: vsa_workspace_layout(info, heads, head_dim).
+ *   keep_idx_dev         int32 [heads][n_v][k] (default) or [heads][n_t][k_ref + k]
+ *                        (reference sparsity); may be null when that is empty.
+ *   o_coarse_dev         fp32 [heads][n_t][head_dim].
+ * All of these stay owned by the caller.
+ */
+typedef struct vsa_head_group {
+    const vsa_plan_info *info;
+    const int32_t *row_src_dev, *block_len_dev;
+    int32_t head_first, heads;
+    double sparsity;
+    int64_t keep_k;
+    int32_t ref, int8;
+    double ref_sparsity;
+    int64_t ref_keep_k;
+    void *workspace;
+    size_t workspace_bytes;
+    int32_t *keep_idx_dev;
+    float *o_coarse_dev;
+} vsa_head_group;
+
+/*
+ * vsa_layer_fwd_groups -- the layer with per-head tile shapes, enqueued on
+ * `stream`, group after group. q, k, v: device bf16 [S][heads_total][head_dim];
+ * gate: device bf16 [S][heads_total * head_dim]; out: device bf16
+ * [S][heads_total][head_dim] (each group writes its own heads). scale <= 0
+ * means head_dim^-1/2. Every group is validated before anything is enqueued
+ * (VSA_ERR_ARG for no groups, a head range outside [0, heads_total) or shared
+ * by two groups, plans of different token counts, or a bad keep rule); errors
+ * of a group's own stages name the group. VSA_ERR_UNSUPPORTED, VSA_ERR_DEVICE
+ * as the single-plan entry points.
+ */
+int vsa_layer_fwd_groups(const vsa_head_group *groups, int32_t n_groups, int32_t heads_total,
+                         int32_t head_dim, float scale, const void *q, const void *k,
+                         const void *v, const void *gate, void *out, void *stream);
+
 /* --------------------------------------------------------- backward -- */
 /*
  * Backward pass: the gradient of the layer with the keep sets held fixed (a

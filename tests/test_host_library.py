@@ -344,3 +344,44 @@ def test_i8_entry_point_rejects_bad_arguments():
     assert lay.k_scale - lay.k_i8 >= wl.heads * big.S_pad * wl.head_dim
     assert lay.total_bytes - lay.k_scale >= wl.heads * big.S_pad // 64 * 4
     assert lay.k_i8 >= lay.part_ml
+
+
+def test_group_entry_point_rejects_bad_arguments():
+    """vsa_layer_fwd_groups validates every group before enqueuing anything."""
+    lib = tsv._lib
+    a = tsv.vsa_plan_tiles([20, 40], (4, 8, 8), (4, 4, 4))
+    b = tsv.vsa_plan_tiles([20, 40], (4, 8, 8), (1, 8, 8))
+    other = tsv.vsa_plan_tiles([20, 41], (4, 8, 8), (4, 4, 4))   # one token more
+
+    def group(pl, first, heads, keep_k=1, ws=FAKE, ref=0, ref_keep_k=-1):
+        g = tsv.vsa_head_group()
+        g.info = ctypes.pointer(pl.info)
+        g.row_src_dev = g.block_len_dev = FAKE
+        g.head_first, g.heads = first, heads
+        g.sparsity, g.keep_k = float("nan"), keep_k
+        g.ref, g.int8, g.ref_sparsity, g.ref_keep_k = ref, 0, float("nan"), ref_keep_k
+        g.workspace, g.workspace_bytes = ws, 1 << 40
+        g.keep_idx_dev = g.o_coarse_dev = FAKE
+        return g
+
+    def call(groups, heads_total=4, head_dim=128):
+        arr = (tsv.vsa_head_group * max(1, len(groups)))(*groups)
+        return lib.vsa_layer_fwd_groups(arr, len(groups), heads_total, head_dim, 0.0, FAKE, FAKE,
+                                        FAKE, FAKE, FAKE, None)
+
+    E = tsv
+    assert call([]) == E.VSA_ERR_ARG
+    assert call([group(a, 0, 2), group(b, 1, 2)]) == E.VSA_ERR_ARG        # head 1 twice
+    assert b"more than one group" in lib.vsa_last_error()
+    assert call([group(a, 0, 2), group(b, 2, 3)]) == E.VSA_ERR_ARG        # beyond heads_total
+    assert call([group(a, -1, 2)]) == E.VSA_ERR_ARG
+    assert call([group(a, 0, 2), group(other, 2, 2)]) == E.VSA_ERR_ARG    # token counts differ
+    assert b"tokens" in lib.vsa_last_error()
+    assert call([group(a, 0, 2), group(b, 2, 2, keep_k=10 ** 6)]) == E.VSA_ERR_ARG
+    assert b"group 1" in lib.vsa_last_error()
+    assert call([group(a, 0, 2, ref=1, ref_keep_k=a.P + 1)]) == E.VSA_ERR_ARG
+    # pointers and workspaces are checked up front too (null workspace in group 1)
+    assert call([group(a, 0, 2), group(b, 2, 2, ws=0)]) == E.VSA_ERR_ARG
+    assert b"group 1" in lib.vsa_last_error()
+    assert call([group(a, 0, 2), group(b, 2, 2, ws=FAKE + 8)]) == E.VSA_ERR_ARG   # misaligned
+    assert call([group(a, 0, 2)], head_dim=96) == E.VSA_ERR_UNSUPPORTED

@@ -34,7 +34,7 @@ EXPORTED = (
     "vsa_sparse_attn_fwd", "vsa_gate_proj", "vsa_set_split_chunks", "vsa_timing_enable",
     "vsa_timing_read", "vsa_ref_keep_count", "vsa_tile_pair_fraction_ref", "vsa_coarse_topk_ref",
     "vsa_sparse_attn_fwd_ref", "vsa_bwd_workspace_layout", "vsa_sparse_attn_bwd",
-    "vsa_sparse_attn_fwd_i8",
+    "vsa_sparse_attn_fwd_i8", "vsa_layer_fwd_groups",
 )
 TIMED_KERNELS = ("gate_gemm", "gather_pool", "video_scores", "coarse_attn", "topk", "fine_attn",
                  "merge", "bwd_gather", "bwd_prep", "bwd_coarse", "bwd_tlist", "bwd_dq", "bwd_dkdv",
@@ -60,6 +60,18 @@ class vsa_ws_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("k_tiled", "v_tiled", "q_mean", "k_mean", "v_mean", "scores", "part_o",
                  "part_ml", "k_i8", "k_scale", "total_bytes")]
+
+
+class vsa_head_group(ctypes.Structure):
+    _fields_ = [
+        ("info", ctypes.POINTER(vsa_plan_info)), ("row_src_dev", ctypes.c_void_p),
+        ("block_len_dev", ctypes.c_void_p), ("head_first", ctypes.c_int32),
+        ("heads", ctypes.c_int32), ("sparsity", ctypes.c_double), ("keep_k", ctypes.c_int64),
+        ("ref", ctypes.c_int32), ("int8", ctypes.c_int32), ("ref_sparsity", ctypes.c_double),
+        ("ref_keep_k", ctypes.c_int64), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t), ("keep_idx_dev", ctypes.c_void_p),
+        ("o_coarse_dev", ctypes.c_void_p),
+    ]
 
 
 class vsa_bwd_layout(ctypes.Structure):
@@ -98,6 +110,8 @@ def _load() -> ctypes.CDLL:
                                      P], ctypes.c_int),
         "vsa_sparse_attn_fwd_i8": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, SZ, P, P, P, P,
                                     P], ctypes.c_int),
+        "vsa_layer_fwd_groups": ([ctypes.POINTER(vsa_head_group), I32, I32, I32, F32, P, P, P, P,
+                                  P, P], ctypes.c_int),
         "vsa_bwd_workspace_layout": ([info_p, I32, I32, ctypes.POINTER(vsa_bwd_layout)], ctypes.c_int),
         "vsa_sparse_attn_bwd": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, P, P, P, P, SZ, P, P,
                                  P, SZ, P, P, P, P, P], ctypes.c_int),
@@ -566,3 +580,61 @@ class TileSparseAttention:
         off = getattr(self.layout, name)
         n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
         return self.workspace[off:off + n].view(dtype).view(*shape)
+
+
+class HeadGroupAttention:
+    """One layer whose heads are split into groups of consecutive heads, each with
+    its own tile shape (per-head tile shapes); one vsa_layer_fwd_groups call runs
+    every group on the shared q, k, v, gate and out.
+
+    groups: sequence of dicts with keys "tile" and "heads" (required) and optional
+    "sparsity", "keep_k", "reference_sparsity", "ref_keep_k", "int8"; the groups
+    take the heads in order."""
+
+    def __init__(self, prefix_segments, grid, groups, head_dim: int, scale: float = 0.0,
+                 device="cuda", heads_total: Optional[int] = None):
+        """heads_total: heads per token row of the tensors (default: the groups' sum;
+        heads beyond the groups are left untouched)."""
+        self.head_dim, self.scale = int(head_dim), float(scale)
+        self.layers, first = [], 0
+        for g in groups:
+            att = TileSparseAttention(prefix_segments, grid, g["tile"], g["heads"], head_dim,
+                                      sparsity=g.get("sparsity"), keep_k=g.get("keep_k"),
+                                      scale=scale, device=device,
+                                      reference_sparsity=g.get("reference_sparsity"),
+                                      ref_keep_k=g.get("ref_keep_k"), int8=g.get("int8", False))
+            self.layers.append((first, att))
+            first += int(g["heads"])
+        self.heads_total = first if heads_total is None else int(heads_total)
+        arr = (vsa_head_group * len(self.layers))()
+        for i, (h0, att) in enumerate(self.layers):
+            e = arr[i]
+            e.info = ctypes.pointer(att.plan.info)
+            e.row_src_dev, e.block_len_dev = _ptr(att.row_src), _ptr(att.block_len)
+            e.head_first, e.heads = h0, att.heads
+            e.sparsity = float("nan") if att.sparsity is None else float(att.sparsity)
+            e.keep_k = -1 if att.keep_k is None else int(att.keep_k)
+            e.ref, e.int8 = int(att.ref), int(att.int8)
+            e.ref_sparsity = (float("nan") if att.reference_sparsity is None
+                              else float(att.reference_sparsity))
+            e.ref_keep_k = -1 if att.ref_keep_k is None else int(att.ref_keep_k)
+            e.workspace, e.workspace_bytes = _ptr(att.workspace), att.workspace.numel()
+            e.keep_idx_dev = _ptr(att.keep_idx) if att.list_len > 0 else None
+            e.o_coarse_dev = _ptr(att.o_coarse)
+        self.groups = arr
+
+    def __call__(self, q, k, v, gate, out=None, stream=None) -> torch.Tensor:
+        S = self.layers[0][1].plan.info.rows_real
+        H, D = self.heads_total, self.head_dim
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            _need(t, n, torch.bfloat16, (S, H, D))
+        _need(gate, "gate", torch.bfloat16)
+        if gate.numel() != S * H * D:
+            raise ValueError("gate must hold [S][heads*head_dim] values")
+        if out is None:
+            out = torch.empty_like(q)
+        _need(out, "out", torch.bfloat16, (S, H, D))
+        _check(_lib.vsa_layer_fwd_groups(self.groups, len(self.layers), H, D, self.scale, _ptr(q),
+                                         _ptr(k), _ptr(v), _ptr(gate), _ptr(out), _stream(stream)),
+               "vsa_layer_fwd_groups")
+        return out

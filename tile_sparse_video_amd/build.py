@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvsa.so")
-SOURCES = ["plan.cpp", "timing.cpp", "coarse.hip", "fine.hip", "gemm.hip", "backward.hip"]
+SOURCES = ["plan.cpp", "timing.cpp", "groups.cpp", "coarse.hip", "fine.hip", "gemm.hip",
+           "backward.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -64,7 +64,7 @@ namespace {
 template <int D, int B>
 __global__ __launch_bounds__(256) void gather_pool_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const int32_t *__restrict__ row_src, const int32_t *__restrict__ block_len, int H, int n_t,
+    const int32_t *__restrict__ row_src, const int32_t *__restrict__ block_len, int H, int ld, int n_t,
     float *__restrict__ qmean, float *__restrict__ kmean, float *__restrict__ vmean,
     uint16_t *__restrict__ kt, uint16_t *__restrict__ vt)
 {
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void gather_pool_kernel(
         const int r = idx / CH, c = idx % CH;
         uint4 val = make_uint4(0, 0, 0, 0);
         if (r < n && c / (D / 8) < nh)
-            val = *reinterpret_cast<const uint4 *>(X + (size_t(toks[r]) * H + h0) * D + c * 8);
+            val = *reinterpret_cast<const uint4 *>(X + (size_t(toks[r]) * ld + h0) * D + c * 8);
         *reinterpret_cast<uint4 *>(&lds[r * ROW + c * 8]) = val;
     }
     __syncthreads();
@@ -484,14 +484,14 @@ void launch_topk(const float *scores, int n_rows, int row_len, int col_first, in
 
 template <int D, int B>
 void launch_gather_pool(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *row_src,
-                        const int32_t *block_len, int H, int n_t, float *qm, float *km, float *vm,
+                        const int32_t *block_len, int H, int ld, int n_t, float *qm, float *km, float *vm,
                         uint16_t *kt, uint16_t *vt, hipStream_t st)
 {
     constexpr int HPB = 256 / D;
     dim3 grid(n_t, (H + HPB - 1) / HPB, 3);
     KernelTimer t(K_GATHER_POOL, st);
     hipLaunchKernelGGL((gather_pool_kernel<D, B>), grid, dim3(256), 0, st, q, k, v, row_src,
-                       block_len, H, n_t, qm, km, vm, kt, vt);
+                       block_len, H, ld, n_t, qm, km, vm, kt, vt);
 }
 
 // Scores over tiles [first, first + n) x [first, first + n), then the coarse
@@ -512,17 +512,20 @@ void launch_coarse(const vsa_plan_info &info, int H, float scale, const float *q
                        scale * 1.4426950408889634f, o_coarse);
 }
 
-// Shared body of the two coarse entry points. ref: reference-sparsity mode
+}  // namespace
+
+// Shared body of the coarse entry points. ref: reference-sparsity mode
 // (scores over all tiles, two selections per query tile); otherwise the
 // default mode (video x video scores, k_gen video tiles per video query tile).
+// ld: heads per token row of q, k, v (the pointers address the first head).
 int coarse_impl(const char *name, const vsa_plan_info *info, const int32_t *row_src_dev,
-                const int32_t *block_len_dev, int heads, int head_dim, bool ref, double sparsity,
+                const int32_t *block_len_dev, int heads, int ld, int head_dim, bool ref, double sparsity,
                 int64_t keep_k, double ref_sparsity, int64_t ref_keep_k, float scale, const void *q,
                 const void *k, const void *v, void *workspace, size_t workspace_bytes,
                 int32_t *keep_idx_dev, float *o_coarse_dev, void *stream)
 {
     if (int st = check_info(info)) return st;
-    if (heads <= 0) return fail(VSA_ERR_ARG, "%s: heads = %d", name, heads);
+    if (heads <= 0 || ld < heads) return fail(VSA_ERR_ARG, "%s: heads = %d (row stride %d)", name, heads, ld);
     if (head_dim != 64 && head_dim != 128)
         return fail(VSA_ERR_UNSUPPORTED, "%s: head_dim = %d; supported: 64, 128", name, head_dim);
     if (!row_src_dev || !block_len_dev || !q || !k || !v || !workspace || !o_coarse_dev)
@@ -561,12 +564,12 @@ int coarse_impl(const char *name, const vsa_plan_info *info, const int32_t *row_
 
     (void)hipGetLastError();
     if (head_dim == 128) {
-        if (B == 64) launch_gather_pool<128, 64>(qq, kk_, vv, row_src_dev, block_len_dev, heads, n_t, qm, km, vm, kt, vt, st);
-        else launch_gather_pool<128, 128>(qq, kk_, vv, row_src_dev, block_len_dev, heads, n_t, qm, km, vm, kt, vt, st);
+        if (B == 64) launch_gather_pool<128, 64>(qq, kk_, vv, row_src_dev, block_len_dev, heads, ld, n_t, qm, km, vm, kt, vt, st);
+        else launch_gather_pool<128, 128>(qq, kk_, vv, row_src_dev, block_len_dev, heads, ld, n_t, qm, km, vm, kt, vt, st);
         launch_coarse<128>(*info, heads, sc, qm, km, vm, first, n, sc_buf, o_coarse_dev, st);
     } else {
-        if (B == 64) launch_gather_pool<64, 64>(qq, kk_, vv, row_src_dev, block_len_dev, heads, n_t, qm, km, vm, kt, vt, st);
-        else launch_gather_pool<64, 128>(qq, kk_, vv, row_src_dev, block_len_dev, heads, n_t, qm, km, vm, kt, vt, st);
+        if (B == 64) launch_gather_pool<64, 64>(qq, kk_, vv, row_src_dev, block_len_dev, heads, ld, n_t, qm, km, vm, kt, vt, st);
+        else launch_gather_pool<64, 128>(qq, kk_, vv, row_src_dev, block_len_dev, heads, ld, n_t, qm, km, vm, kt, vt, st);
         launch_coarse<64>(*info, heads, sc, qm, km, vm, first, n, sc_buf, o_coarse_dev, st);
     }
     if (!ref) {
@@ -581,7 +584,6 @@ int coarse_impl(const char *name, const vsa_plan_info *info, const int32_t *row_
     return VSA_OK;
 }
 
-}  // namespace
 }  // namespace vsa
 
 using namespace vsa;
@@ -593,7 +595,7 @@ extern "C" int vsa_coarse_topk(const vsa_plan_info *info, const int32_t *row_src
                                int32_t *keep_idx_dev, float *o_coarse_dev, void *stream)
 {
     clear_error();
-    return coarse_impl("vsa_coarse_topk", info, row_src_dev, block_len_dev, heads, head_dim, false,
+    return coarse_impl("vsa_coarse_topk", info, row_src_dev, block_len_dev, heads, heads, head_dim, false,
                        sparsity, keep_k, 0.0, -1, scale, q, k, v, workspace, workspace_bytes,
                        keep_idx_dev, o_coarse_dev, stream);
 }
@@ -606,7 +608,7 @@ extern "C" int vsa_coarse_topk_ref(const vsa_plan_info *info, const int32_t *row
                                    int32_t *keep_idx_dev, float *o_coarse_dev, void *stream)
 {
     clear_error();
-    return coarse_impl("vsa_coarse_topk_ref", info, row_src_dev, block_len_dev, heads, head_dim, true,
+    return coarse_impl("vsa_coarse_topk_ref", info, row_src_dev, block_len_dev, heads, heads, head_dim, true,
                        sparsity, keep_k, ref_sparsity, ref_keep_k, scale, q, k, v, workspace,
                        workspace_bytes, keep_idx_dev, o_coarse_dev, stream);
 }

@@ -75,6 +75,7 @@ struct FineArgs {
     uint16_t *part_o;           // split: [items][C][DB][2][64][16] bf16 O / l
     float *part_ml;             // split: [items][C][2 (m, l)][2][32]
     int H, P, n_v, n_t, k, chunks;
+    int ld;                     // heads per token row of q, gate, out and dout (>= H)
     int ref;                    // reference sparsity: every tile has an explicit list
     int list_len;               // ref: entries per list (k_ref + k_gen), keep is [H][n_t][list_len]
     // Statistics merge (backward support): per tile-order row, the log2-domain
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             tok[qb] = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
-            const uint16_t *qrow = a.q + (size_t(tok[qb] < 0 ? 0 : tok[qb]) * a.H + h) * D + 8 * half;
+            const uint16_t *qrow = a.q + (size_t(tok[qb] < 0 ? 0 : tok[qb]) * a.ld + h) * D + 8 * half;
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 bf16x8_t v = load_frag(qrow + 16 * c);
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             tok[qb] = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
-            const uint16_t *qrow = a.q + (size_t(tok[qb] < 0 ? 0 : tok[qb]) * a.H + h) * D + 16 * half;
+            const uint16_t *qrow = a.q + (size_t(tok[qb] < 0 ? 0 : tok[qb]) * a.ld + h) * D + 16 * half;
 #pragma unroll
             for (int c = 0; c < NC8; ++c)
 #pragma unroll
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
     for (int qb = 0; qb < 2; ++qb) {
         if (tok[qb] < 0) continue;
         const float inv = 1.0f / l[qb];
-        const size_t base = (size_t(tok[qb]) * a.H + h) * D;
+        const size_t base = (size_t(tok[qb]) * a.ld + h) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -571,7 +572,7 @@ __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
             const int tok = a.row_src[row];
             float part = 0.f;
             if (tok >= 0) {
-                const uint16_t *go = a.dout + (size_t(tok) * a.H + h) * D;
+                const uint16_t *go = a.dout + (size_t(tok) * a.ld + h) * D;
                 const float inv = 1.0f / L[qb];
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
@@ -598,7 +599,7 @@ __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
         const int tok = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
         if (tok < 0) continue;
         const float inv = 1.0f / L[qb];
-        const size_t base = (size_t(tok) * a.H + h) * D;
+        const size_t base = (size_t(tok) * a.ld + h) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -724,6 +725,7 @@ int fine_stats(const vsa_plan_info &info, const int32_t *row_src, const int32_t 
     a.part_o = reinterpret_cast<uint16_t *>(const_cast<char *>(ws) + L.part_o);
     a.part_ml = reinterpret_cast<float *>(const_cast<char *>(ws) + L.part_ml);
     a.H = heads;
+    a.ld = heads;
     a.P = info.n_prefix_tiles;
     a.n_v = info.n_video_tiles;
     a.n_t = info.n_tiles;
@@ -759,17 +761,19 @@ extern "C" int vsa_set_split_chunks(int32_t chunks)
     return VSA_OK;
 }
 
-namespace {
+namespace vsa {
 
-// Shared body of the two fine entry points (ref: reference-sparsity lists).
+// Shared body of the fine entry points (ref: reference-sparsity lists; i8:
+// INT8 scores). ld: heads per token row of q, gate and out (the pointers
+// address the first head).
 int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_src_dev,
-              const int32_t *block_len_dev, int heads, int head_dim, bool ref, bool i8, int k, int k_ref,
+              const int32_t *block_len_dev, int heads, int ld, int head_dim, bool ref, bool i8, int k, int k_ref,
               float scale, const void *q, const void *workspace, size_t workspace_bytes,
               const int32_t *keep_idx_dev, const float *o_coarse_dev, const void *gate, void *out,
               void *stream)
 {
     if (int st = check_info(info)) return st;
-    if (heads <= 0) return fail(VSA_ERR_ARG, "%s: heads = %d", name, heads);
+    if (heads <= 0 || ld < heads) return fail(VSA_ERR_ARG, "%s: heads = %d (row stride %d)", name, heads, ld);
     if (head_dim != 64 && head_dim != 128)
         return fail(VSA_ERR_UNSUPPORTED, "%s: head_dim = %d; supported: 64, 128", name, head_dim);
     if (k < 0 || k > info->n_video_tiles)
@@ -815,6 +819,7 @@ int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_sr
     a.k8 = reinterpret_cast<const uint8_t *>(ws + L.k_i8);
     a.k_scale = reinterpret_cast<const float *>(ws + L.k_scale);
     a.H = heads;
+    a.ld = ld;
     a.P = info->n_prefix_tiles;
     a.n_v = info->n_video_tiles;
     a.n_t = info->n_tiles;
@@ -839,7 +844,7 @@ int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_sr
     return VSA_OK;
 }
 
-}  // namespace
+}  // namespace vsa
 
 extern "C" int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row_src_dev,
                                    const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
@@ -849,7 +854,7 @@ extern "C" int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row
                                    void *stream)
 {
     clear_error();
-    return fine_impl("vsa_sparse_attn_fwd", info, row_src_dev, block_len_dev, heads, head_dim, false,
+    return fine_impl("vsa_sparse_attn_fwd", info, row_src_dev, block_len_dev, heads, heads, head_dim, false,
                      false, k, 0, scale, q, workspace, workspace_bytes, keep_idx_dev, o_coarse_dev, gate,
                      out, stream);
 }
@@ -862,7 +867,7 @@ extern "C" int vsa_sparse_attn_fwd_ref(const vsa_plan_info *info, const int32_t 
                                        const void *gate, void *out, void *stream)
 {
     clear_error();
-    return fine_impl("vsa_sparse_attn_fwd_ref", info, row_src_dev, block_len_dev, heads, head_dim,
+    return fine_impl("vsa_sparse_attn_fwd_ref", info, row_src_dev, block_len_dev, heads, heads, head_dim,
                      true, false, k_gen, k_ref, scale, q, workspace, workspace_bytes, keep_idx_dev,
                      o_coarse_dev, gate, out, stream);
 }
@@ -875,7 +880,7 @@ extern "C" int vsa_sparse_attn_fwd_i8(const vsa_plan_info *info, const int32_t *
                                       const void *gate, void *out, void *stream)
 {
     clear_error();
-    return fine_impl("vsa_sparse_attn_fwd_i8", info, row_src_dev, block_len_dev, heads, head_dim,
+    return fine_impl("vsa_sparse_attn_fwd_i8", info, row_src_dev, block_len_dev, heads, heads, head_dim,
                      k_ref >= 0, true, k_gen, k_ref < 0 ? 0 : k_ref, scale, q, workspace,
                      workspace_bytes, keep_idx_dev, o_coarse_dev, gate, out, stream);
 }
