@@ -385,3 +385,28 @@ def test_group_entry_point_rejects_bad_arguments():
     assert b"group 1" in lib.vsa_last_error()
     assert call([group(a, 0, 2), group(b, 2, 2, ws=FAKE + 8)]) == E.VSA_ERR_ARG   # misaligned
     assert call([group(a, 0, 2)], head_dim=96) == E.VSA_ERR_UNSUPPORTED
+
+
+def test_heads_beyond_4gib_are_rejected():
+    """A head's tile-ordered K is addressed through one 32-bit buffer resource."""
+    info = tsv.vsa_plan_info()
+    info.grid[:] = (256, 256, 256)
+    info.tile[:] = (4, 4, 4)
+    info.tile_rows, info.n_prefix_tiles = 64, 0
+    info.n_video_tiles = info.n_tiles = 64 * 64 * 64
+    info.rows_real = info.rows_padded = 256 ** 3      # 2^24 rows x 128 x 2 B = 4 GiB
+    info.prefix_rows = 0
+    lib = tsv._lib
+    rc = lib.vsa_sparse_attn_fwd(ctypes.byref(info), FAKE, FAKE, 1, 128, 1, 0.0, FAKE, FAKE * 2,
+                                 1 << 50, FAKE, FAKE, FAKE, FAKE, None)
+    assert rc == tsv.VSA_ERR_UNSUPPORTED, lib.vsa_last_error()
+    assert b"4 GiB" in lib.vsa_last_error()
+    rc = lib.vsa_sparse_attn_bwd(ctypes.byref(info), FAKE, FAKE, 1, 128, -1, 1, 0.0, FAKE, FAKE,
+                                 FAKE, FAKE, FAKE, FAKE * 2, 1 << 50, FAKE, FAKE, FAKE * 2, 1 << 50,
+                                 FAKE, FAKE, FAKE, FAKE, None)
+    assert rc == tsv.VSA_ERR_UNSUPPORTED, lib.vsa_last_error()
+    # head_dim 64 halves the bytes: the same plan passes this check (and fails later on the
+    # fake workspace size, still before any device work)
+    rc = lib.vsa_sparse_attn_fwd(ctypes.byref(info), FAKE, FAKE, 1, 64, 1, 0.0, FAKE, FAKE * 2,
+                                 1024, FAKE, FAKE, FAKE, FAKE, None)
+    assert rc == tsv.VSA_ERR_ARG and b"workspace" in lib.vsa_last_error()

@@ -31,10 +31,11 @@ HIPCC_FLAGS = [
 # Per-source extras. The fine kernel rescales its O accumulators with VALU
 # ops; MFMA accumulators in VGPRs avoid bouncing them through AGPRs. Its
 # scores and running maxima are never NaN (padding keys are -inf), so max
-# operations need no NaN-quieting canonicalisation.
+# operations need no NaN-quieting canonicalisation. The backward kernels keep
+# their long-lived dK/dV and dQ accumulators in AGPRs (the default form), which
+# leaves the VGPRs to the operands in flight.
 PER_SOURCE = {
     "fine.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
-    "backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

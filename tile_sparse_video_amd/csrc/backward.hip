@@ -755,6 +755,7 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdArgs a, int n_items)
 // Every operand is a coalesced 1 KB fragment of the tile-ordered copies; the
 // row-layout operands and row statistics of the next block are fetched while
 // the current one is computed (two register sets, the loop unrolled by two).
+// The dK^T, dV^T accumulators stay in AGPRs for the whole walk.
 template <int D, int B, bool SPLIT>
 __global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
 {
@@ -790,7 +791,6 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
 #pragma unroll
     for (int db = 0; db < DB; ++db) GK[db] = GV[db] = f32x16_t{};
     const float c2 = a.scale_log2e;
-    const size_t head_blk = size_t(h) * a.n_t * SUB;  // 64-row blocks before this head
 
     int cnt = a.tcount[size_t(h) * a.n_t + tile];
     const int32_t *lst = a.tlist + (size_t(h) * a.n_t + tile) * a.n_t;
@@ -819,31 +819,44 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
         u32x4_t Qr[NC], Or[NC];
         float4 L4[4], D4[4];
     };
-    auto frag_base = [&](int b) -> size_t {
-        const int qt = __builtin_amdgcn_readfirstlane(lst[b / (2 * SUB)]);
-        return (head_blk + size_t(qt) * SUB + (b / 2) % SUB) * FR;
+    // Operands are read through buffer resources based at the head's region:
+    // the lane's 16-byte slot is the VGPR offset and the block's fragment
+    // offset is uniform (SGPR), so no address arithmetic runs per load.
+    const uint32_t frag_bytes = uint32_t(S_pad) * D * 2;
+    const size_t head_elems = size_t(h) * S_pad * D;
+    auto rsrc = [&](const uint16_t *p) {
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(p + head_elems), (short)0, frag_bytes, kRsrcWord3);
     };
-    auto row0 = [&](int b) -> size_t {
+    const __amdgpu_buffer_rsrc_t rqr = rsrc(a.qrow), ror = rsrc(a.dorow), rqc = rsrc(a.qcol), roc = rsrc(a.docol);
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.lse + size_t(h) * S_pad), (short)0, uint32_t(S_pad) * 4, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.dt + size_t(h) * S_pad), (short)0, uint32_t(S_pad) * 4, kRsrcWord3);
+    const int vlane = lane * 16, vrow = (4 * half) * 4;
+    auto fbyte = [&](int b) -> uint32_t {
         const int qt = __builtin_amdgcn_readfirstlane(lst[b / (2 * SUB)]);
-        return size_t(h) * S_pad + size_t(qt) * B + 64 * ((b / 2) % SUB) + 32 * (b % 2);
+        return uint32_t(qt * SUB + (b / 2) % SUB) * FR * 1024u;
     };
     auto fetch = [&](int b, RowOps &o) {
-        const size_t fb = frag_base(b), r0 = row0(b);
-        const int qb = b % 2;
+        const int qt = __builtin_amdgcn_readfirstlane(lst[b / (2 * SUB)]);
+        const int sub = (b / 2) % SUB, qb = b % 2;
+        const uint32_t fb = uint32_t(qt * SUB + sub) * FR * 1024u;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const size_t f = (fb + qb * NC + c) * 512 + lane * 8;   // row fragment qb*(D/16) + c
-            o.Qr[c] = *reinterpret_cast<const u32x4_t *>(a.qrow + f);
-            o.Or[c] = *reinterpret_cast<const u32x4_t *>(a.dorow + f);
+            o.Qr[c] = __builtin_amdgcn_raw_buffer_load_b128(rqr, vlane, fb + (qb * NC + c) * 1024u, 0);
+            o.Or[c] = __builtin_amdgcn_raw_buffer_load_b128(ror, vlane, fb + (qb * NC + c) * 1024u, 0);
         }
+        const uint32_t r0 = uint32_t(qt * B + 64 * sub + 32 * qb) * 4u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            o.L4[i] = *reinterpret_cast<const float4 *>(a.lse + r0 + 8 * i + 4 * half);
-            o.D4[i] = *reinterpret_cast<const float4 *>(a.dt + r0 + 8 * i + 4 * half);
+            const u32x4_t l = __builtin_amdgcn_raw_buffer_load_b128(rl, vrow, r0 + 32u * i, 0);
+            const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(rd, vrow, r0 + 32u * i, 0);
+            o.L4[i] = make_float4(__uint_as_float(l[0]), __uint_as_float(l[1]), __uint_as_float(l[2]), __uint_as_float(l[3]));
+            o.D4[i] = make_float4(__uint_as_float(d[0]), __uint_as_float(d[1]), __uint_as_float(d[2]), __uint_as_float(d[3]));
         }
     };
     auto compute = [&](int b, const RowOps &o) {
-        const size_t fb = frag_base(b);
+        const uint32_t fb = fbyte(b);
         const int qb = b % 2;
         f32x16_t S = f32x16_t{}, dP = f32x16_t{};
 #pragma unroll
@@ -851,15 +864,14 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
             S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(o.Qr[c]), Kt[c], S, 0, 0, 0);
             dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(o.Or[c]), Vt[c], dP, 0, 0, 0);
         }
-        // Column-fragment A operands of this 32-row block: chunks 2qb, 2qb+1.
         u32x4_t Oc[2 * DB], Qc[2 * DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
-                const size_t f = (fb + 4 * db + 2 * qb + cc) * 512 + lane * 8;
-                Oc[2 * db + cc] = *reinterpret_cast<const u32x4_t *>(a.docol + f);
-                Qc[2 * db + cc] = *reinterpret_cast<const u32x4_t *>(a.qcol + f);
+                const uint32_t off = fb + (4 * db + 2 * qb + cc) * 1024u;
+                Oc[2 * db + cc] = __builtin_amdgcn_raw_buffer_load_b128(roc, vlane, off, 0);
+                Qc[2 * db + cc] = __builtin_amdgcn_raw_buffer_load_b128(rqc, vlane, off, 0);
             }
         f32x16_t Pm, dS;
 #pragma unroll
@@ -1151,6 +1163,9 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
         return fail(VSA_ERR_ARG, "%s: null device pointer", name);
     if ((ref ? k_ref + k_gen : k_gen) > 0 && !keep_idx_dev) return fail(VSA_ERR_ARG, "%s: keep_idx is null", name);
     if (!std::isfinite(scale)) return fail(VSA_ERR_ARG, "%s: scale is not finite", name);
+    if (int64_t(info->rows_padded) * head_dim * 2 >= (int64_t(1) << 32))
+        return fail(VSA_ERR_UNSUPPORTED, "%s: %lld padded rows x head_dim %d exceed 4 GiB per head", name,
+                    (long long)info->rows_padded, head_dim);
     vsa_ws_layout L;
     compute_layout(*info, heads, head_dim, &L);
     if (workspace_bytes < L.total_bytes)

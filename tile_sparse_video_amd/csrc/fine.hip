@@ -796,6 +796,10 @@ int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_sr
                     L.total_bytes);
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
         return fail(VSA_ERR_ARG, "%s: workspace must be 256-byte aligned", name);
+    // A head's tile-ordered K (or V) is addressed through one buffer resource.
+    if (int64_t(info->rows_padded) * head_dim * 2 >= (int64_t(1) << 32))
+        return fail(VSA_ERR_UNSUPPORTED, "%s: %lld padded rows x head_dim %d exceed 4 GiB per head", name,
+                    (long long)info->rows_padded, head_dim);
     const int64_t items = int64_t(heads) * info->n_tiles * (info->tile_rows / 64);
     const int chunks = split_chunks(*info, head_dim);
     if (items * chunks >= (int64_t(1) << 31))
