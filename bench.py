@@ -162,7 +162,7 @@ def bench_backward(args, wl, tsv, att, qd, kd, vd, xd, wd, g, out, stream, host_
             ev[0].record(stream)
         tsv.vsa_gate_proj(xd, wd, g, stream=stream)
         att.coarse(qd, kd, vd, stream=stream)
-        att.fine(qd, g, out, stream=stream)
+        att.fine_train(qd, g, out, stream=stream)   # also saves lse and O_fine for the backward
         if ev is not None:
             ev[1].record(stream)
         grads["g"] = att.backward(qd, kd, vd, g, dout, stream=stream)

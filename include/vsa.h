@@ -379,19 +379,21 @@ int vsa_layer_fwd_groups(const vsa_head_group *groups, int32_t n_groups, int32_t
  *             the tile means, and each real row of tile i receives the
  *             mean's share (gradient / block_len);
  *   dq, dk, dv also receive the fine attention's gradient over the same key
- *             lists (the fine forward is recomputed for the log-sum-exp and
- *             the softmax-gradient row term D_t = dout[t] . O_fine[t]; P and
- *             dS are rounded to bf16 for the matrix products).
+ *             lists (the log-sum-exp and the softmax-gradient row term
+ *             D_t = dout[t] . O_fine[t] come from the training forward when
+ *             it saved them, else the fine forward is recomputed for them; P
+ *             and dS are rounded to bf16 for the matrix products).
  *
  * vsa_bwd_layout -- scratch regions (device, caller-owned, 256-byte aligned):
  * fragment copies (V / Q / dO rows, K / Q / dO columns), per-row log-sum-exp and D_t,
  * the coarse-path gradients, the transposed key lists ([H][n_t][n_t]), and,
- * when the forward splits its key lists, fp32 dQ partials of 8 key chunks
- * and fp32 dK / dV partials of 8 query chunks.
+ * when the forward splits its key lists, fp32 dQ partials of 8 key chunks,
+ * fp32 dK / dV partials of 8 query chunks and the fp32 O_fine ([H][S_pad][D],
+ * tile order) that vsa_sparse_attn_fwd_train saves.
  */
 typedef struct vsa_bwd_layout {
     size_t vrow, kcol, qcol, docol, qrow, dorow, lse, dt, doc, dqm, dkm, dvm, lsec, dcc, tlist,
-        tcount, part_dq, part_dkv;
+        tcount, part_dq, part_dkv, ofine;
     size_t total_bytes;
 } vsa_bwd_layout;
 
@@ -407,6 +409,12 @@ int vsa_bwd_workspace_layout(const vsa_plan_info *info, int32_t heads, int32_t h
  * coarse pass for the same inputs (the tiled K and the tile means are read).
  * bwd_workspace: >= vsa_bwd_workspace_layout().total_bytes.
  * dq, dk, dv: out device fp32 [S][H][D]; dgate: out device fp32 [S][H*D].
+ * saved_stats != 0: bwd_workspace holds the lse and O_fine that
+ * vsa_sparse_attn_fwd_train wrote for this same forward (same inputs, keep
+ * lists and workspace); the backward then skips recomputing the fine forward.
+ * 0: they are recomputed. It has no effect on heads too small to split their
+ * key lists (those always recompute). The saved values stay valid until the
+ * next training forward on the same bwd_workspace.
  * Errors: as vsa_sparse_attn_fwd(_ref), plus VSA_ERR_ARG for a small
  * backward workspace.
  */
@@ -417,7 +425,26 @@ int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row_src_dev,
                         const void *workspace, size_t workspace_bytes,
                         const int32_t *keep_idx_dev, const float *o_coarse_dev,
                         void *bwd_workspace, size_t bwd_workspace_bytes, float *dq, float *dk,
-                        float *dv, float *dgate, void *stream);
+                        float *dv, float *dgate, int32_t saved_stats, void *stream);
+
+/*
+ * vsa_sparse_attn_fwd_train -- the fine pass of a training step: the same
+ * output as vsa_sparse_attn_fwd (k_ref < 0; keep_idx [H][n_v][k_gen]) or
+ * vsa_sparse_attn_fwd_ref (k_ref >= 0), and, for heads whose key lists are
+ * split, the per-row log-sum-exp (log2 domain) and the fp32 O_fine written to
+ * bwd_workspace (regions lse and ofine of vsa_bwd_workspace_layout) for a
+ * following vsa_sparse_attn_bwd(..., saved_stats = 1). Arguments as
+ * vsa_sparse_attn_fwd(_ref); bwd_workspace: device, >= the backward layout's
+ * total_bytes, 256-byte aligned. Errors: as vsa_sparse_attn_fwd(_ref), plus
+ * VSA_ERR_ARG for a small or misaligned bwd_workspace.
+ */
+int vsa_sparse_attn_fwd_train(const vsa_plan_info *info, const int32_t *row_src_dev,
+                              const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                              int32_t k_ref, int32_t k_gen, float scale, const void *q,
+                              const void *workspace, size_t workspace_bytes,
+                              const int32_t *keep_idx_dev, const float *o_coarse_dev,
+                              const void *gate, void *out, void *bwd_workspace,
+                              size_t bwd_workspace_bytes, void *stream);
 
 /*
  * vsa_set_split_chunks -- tuning override for the fine pass: split every key

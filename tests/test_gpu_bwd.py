@@ -31,8 +31,10 @@ def make_dout(wl, seed=99):
     return torch.randn(wl.tokens, wl.heads, wl.head_dim, generator=gen).to(torch.bfloat16)
 
 
-def run_case(wl, ref=None, heads=None):
-    """ref: None (default mode) or (ref_sparsity, ref_keep_k)."""
+def run_case(wl, ref=None, heads=None, train=False):
+    """ref: None (default mode) or (ref_sparsity, ref_keep_k). train: rerun the fine
+    pass as the training forward (its output must be bit-identical) so that the
+    backward uses the statistics it saved."""
     inp = parity.make_inputs(wl)
     pl = parity.oracle_plan(wl)
     g_bits = oracle.gate_proj(parity.bits(inp.x), parity.bits(inp.w))
@@ -44,6 +46,11 @@ def run_case(wl, ref=None, heads=None):
     dout = make_dout(wl)
     dev = run.out.device
     qd, kd, vd = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    if train:
+        out2 = torch.empty_like(run.out)
+        run.att.fine_train(qd, run.g, out2)
+        torch.cuda.synchronize()
+        assert torch.equal(out2.view(torch.int16), run.out.view(torch.int16)), "training forward output"
     dq, dk, dv, dg = run.att.backward(qd, kd, vd, run.g, dout.to(dev))
     torch.cuda.synchronize()
     got = {"dq": dq.cpu().numpy(), "dk": dk.cpu().numpy(), "dv": dv.cpu().numpy(),
@@ -84,6 +91,29 @@ def test_bwd_reference_sparsity(name, rs, rk):
     run_case(CUSTOM[name], ref=(rs, rk))
 
 
+@pytest.mark.parametrize("name", ["ragged64", "ragged128", "d64", "no_prefix", "k0"])
+def test_bwd_saved_stats_every_token(name):
+    """Key lists split into 8 chunks; the training forward saves lse and O_fine and the
+    backward uses them instead of recomputing the fine forward."""
+    import tile_sparse_video_amd as tsv
+    print(f"[gpu] bwd saved stats {name}", flush=True)
+    tsv.vsa_set_split_chunks(8)
+    try:
+        run_case(CUSTOM[name], train=True)
+    finally:
+        tsv.vsa_set_split_chunks(0)
+
+
+def test_bwd_saved_stats_reference_sparsity():
+    import tile_sparse_video_amd as tsv
+    print("[gpu] bwd saved stats ref", flush=True)
+    tsv.vsa_set_split_chunks(8)
+    try:
+        run_case(CUSTOM["ragged128"], ref=(0.5, None), train=True)
+    finally:
+        tsv.vsa_set_split_chunks(0)
+
+
 def test_bwd_tiny():
     print("[gpu] bwd tiny", flush=True)
     run_case(workloads.WORKLOADS["tiny"])
@@ -95,8 +125,8 @@ def test_bwd_mid_two_heads():
     run_case(wl, heads=[0, wl.heads - 1])
 
 
-@pytest.mark.parametrize("name", ["h3", "veda"])
-def test_bwd_full_size_sampled(name):
+@pytest.mark.parametrize("name,train", [("h3", False), ("veda", False), ("h3", True)])
+def test_bwd_full_size_sampled(name, train):
     """Full-size layers: dq on sampled tokens against the oracle, dg = dout * O_coarse
     on every token, and the identities sum(dv) = sum(dout * (1 + g)), sum(dk) = 0."""
     wl = workloads.WORKLOADS[name]
@@ -112,7 +142,13 @@ def test_bwd_full_size_sampled(name):
     run = parity.run_gpu(inp, gate=g)
     dout = make_dout(wl).to(dev)
     qd, kd, vd = (t.to(dev) for t in (inp.q, inp.k, inp.v))
-    print(f"[gpu] bwd full size {name}: backward", flush=True)
+    if train:
+        out2 = torch.empty_like(run.out)
+        run.att.fine_train(qd, run.g, out2)
+        torch.cuda.synchronize()
+        assert torch.equal(out2.view(torch.int16), run.out.view(torch.int16)), "training forward output"
+        del out2
+    print(f"[gpu] bwd full size {name}: backward (saved stats: {train})", flush=True)
     dq, dk, dv, dg = run.att.backward(qd, kd, vd, run.g, dout)
     torch.cuda.synchronize()
     oc = run.att.o_coarse                                           # [H][n_t][D]

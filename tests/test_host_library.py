@@ -403,10 +403,37 @@ def test_heads_beyond_4gib_are_rejected():
     assert b"4 GiB" in lib.vsa_last_error()
     rc = lib.vsa_sparse_attn_bwd(ctypes.byref(info), FAKE, FAKE, 1, 128, -1, 1, 0.0, FAKE, FAKE,
                                  FAKE, FAKE, FAKE, FAKE * 2, 1 << 50, FAKE, FAKE, FAKE * 2, 1 << 50,
-                                 FAKE, FAKE, FAKE, FAKE, None)
+                                 FAKE, FAKE, FAKE, FAKE, 0, None)
     assert rc == tsv.VSA_ERR_UNSUPPORTED, lib.vsa_last_error()
     # head_dim 64 halves the bytes: the same plan passes this check (and fails later on the
     # fake workspace size, still before any device work)
     rc = lib.vsa_sparse_attn_fwd(ctypes.byref(info), FAKE, FAKE, 1, 64, 1, 0.0, FAKE, FAKE * 2,
                                  1024, FAKE, FAKE, FAKE, FAKE, None)
     assert rc == tsv.VSA_ERR_ARG and b"workspace" in lib.vsa_last_error()
+
+
+def test_training_forward_rejects_bad_arguments():
+    pl = tsv.vsa_plan_tiles([20, 40], (4, 8, 8), (4, 4, 4))
+    info = pl.info
+    lib = tsv._lib
+
+    def call(bw=FAKE * 4, bw_bytes=1 << 40, heads=2, head_dim=128, k_gen=1):
+        return lib.vsa_sparse_attn_fwd_train(ctypes.byref(info), FAKE, FAKE, heads, head_dim, -1,
+                                             k_gen, 0.0, FAKE, FAKE * 2, 1 << 40, FAKE, FAKE, FAKE,
+                                             FAKE, bw, bw_bytes, None)
+
+    E = tsv
+    assert call(bw=0) == E.VSA_ERR_ARG
+    assert call(bw_bytes=1024) == E.VSA_ERR_ARG
+    assert b"backward workspace" in lib.vsa_last_error()
+    assert call(bw=FAKE * 4 + 8) == E.VSA_ERR_ARG                  # misaligned
+    assert call(head_dim=96) == E.VSA_ERR_UNSUPPORTED
+    assert call(k_gen=pl.n_v + 1) == E.VSA_ERR_ARG                 # checked by the forward body
+    assert b"vsa_sparse_attn_fwd_train" in lib.vsa_last_error()
+    # the O_fine region exists only for heads that split their key lists
+    wl = workloads.WORKLOADS["h3"]
+    big = tsv.cached_plan(wl.prefix_segments, wl.grid, wl.tile)
+    lay = tsv.vsa_bwd_workspace_layout(big.info, wl.heads, wl.head_dim)
+    assert lay.total_bytes - lay.ofine >= wl.heads * big.S_pad * wl.head_dim * 4
+    small = tsv.vsa_bwd_workspace_layout(info, 2, 128)
+    assert small.total_bytes == small.ofine

@@ -34,7 +34,7 @@ EXPORTED = (
     "vsa_sparse_attn_fwd", "vsa_gate_proj", "vsa_set_split_chunks", "vsa_timing_enable",
     "vsa_timing_read", "vsa_ref_keep_count", "vsa_tile_pair_fraction_ref", "vsa_coarse_topk_ref",
     "vsa_sparse_attn_fwd_ref", "vsa_bwd_workspace_layout", "vsa_sparse_attn_bwd",
-    "vsa_sparse_attn_fwd_i8", "vsa_layer_fwd_groups",
+    "vsa_sparse_attn_fwd_i8", "vsa_layer_fwd_groups", "vsa_sparse_attn_fwd_train",
 )
 TIMED_KERNELS = ("gate_gemm", "gather_pool", "video_scores", "coarse_attn", "topk", "fine_attn",
                  "merge", "bwd_gather", "bwd_prep", "bwd_coarse", "bwd_tlist", "bwd_dq", "bwd_dkdv",
@@ -77,7 +77,8 @@ class vsa_head_group(ctypes.Structure):
 class vsa_bwd_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("vrow", "kcol", "qcol", "docol", "qrow", "dorow", "lse", "dt", "doc", "dqm", "dkm",
-                 "dvm", "lsec", "dcc", "tlist", "tcount", "part_dq", "part_dkv", "total_bytes")]
+                 "dvm", "lsec", "dcc", "tlist", "tcount", "part_dq", "part_dkv", "ofine",
+                 "total_bytes")]
 
 
 def _load() -> ctypes.CDLL:
@@ -114,7 +115,9 @@ def _load() -> ctypes.CDLL:
                                   P, P], ctypes.c_int),
         "vsa_bwd_workspace_layout": ([info_p, I32, I32, ctypes.POINTER(vsa_bwd_layout)], ctypes.c_int),
         "vsa_sparse_attn_bwd": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, P, P, P, P, SZ, P, P,
-                                 P, SZ, P, P, P, P, P], ctypes.c_int),
+                                 P, SZ, P, P, P, P, I32, P], ctypes.c_int),
+        "vsa_sparse_attn_fwd_train": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, SZ, P, P, P, P,
+                                       P, SZ, P], ctypes.c_int),
         "vsa_timing_enable": ([I32], ctypes.c_int),
         "vsa_timing_read": ([ctypes.c_char_p, ctypes.POINTER(I32), ctypes.POINTER(F64)],
                             ctypes.c_int),
@@ -403,8 +406,9 @@ def vsa_sparse_attn_bwd(info: vsa_plan_info, row_src_dev: torch.Tensor, block_le
                         heads: int, head_dim: int, k_ref: int, k_gen: int, q, k, v, gate, dout,
                         workspace: torch.Tensor, keep_idx: Optional[torch.Tensor],
                         o_coarse: torch.Tensor, bwd_workspace: torch.Tensor, dq, dk, dv, dgate,
-                        scale: float = 0.0, stream=None) -> None:
-    """Backward pass (k_ref < 0: default mode). Gradients are fp32."""
+                        scale: float = 0.0, stream=None, saved_stats: bool = False) -> None:
+    """Backward pass (k_ref < 0: default mode). Gradients are fp32. saved_stats: the
+    bwd_workspace holds what vsa_sparse_attn_fwd_train saved for this forward."""
     S = info.rows_real
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _need(t, n, torch.bfloat16, (S, heads, head_dim))
@@ -427,8 +431,39 @@ def vsa_sparse_attn_bwd(info: vsa_plan_info, row_src_dev: torch.Tensor, block_le
         ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev), heads, head_dim, int(k_ref),
         int(k_gen), float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(dout),
         _ptr(workspace), workspace.numel(), _ptr(keep_idx), _ptr(o_coarse), _ptr(bwd_workspace),
-        bwd_workspace.numel(), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate), _stream(stream)),
+        bwd_workspace.numel(), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate), int(bool(saved_stats)),
+        _stream(stream)),
         "vsa_sparse_attn_bwd")
+
+
+def vsa_sparse_attn_fwd_train(info: vsa_plan_info, row_src_dev: torch.Tensor,
+                              block_len_dev: torch.Tensor, heads: int, head_dim: int, k_ref: int,
+                              k_gen: int, q: torch.Tensor, workspace: torch.Tensor,
+                              keep_idx: Optional[torch.Tensor], o_coarse: torch.Tensor,
+                              gate: torch.Tensor, out: torch.Tensor, bwd_workspace: torch.Tensor,
+                              scale: float = 0.0, stream=None) -> None:
+    """The fine pass of a training step (k_ref < 0: default mode): the forward's
+    output plus the lse and O_fine the backward needs, saved in bwd_workspace."""
+    S = info.rows_real
+    _need(q, "q", torch.bfloat16, (S, heads, head_dim))
+    _need(gate, "gate", torch.bfloat16)
+    if gate.numel() != S * heads * head_dim:
+        raise ValueError("gate must hold [S][heads*head_dim] values")
+    _need(out, "out", torch.bfloat16, (S, heads, head_dim))
+    _need(row_src_dev, "row_src", torch.int32, (info.rows_padded,))
+    _need(block_len_dev, "block_len", torch.int32, (info.n_tiles,))
+    _need(workspace, "workspace", torch.uint8)
+    _need(bwd_workspace, "bwd_workspace", torch.uint8)
+    _need(o_coarse, "o_coarse", torch.float32, (heads, info.n_tiles, head_dim))
+    if keep_idx is not None:
+        shape = ((heads, info.n_video_tiles, k_gen) if k_ref < 0
+                 else (heads, info.n_tiles, k_ref + k_gen))
+        _need(keep_idx, "keep_idx", torch.int32, shape)
+    _check(_lib.vsa_sparse_attn_fwd_train(
+        ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev), heads, head_dim, int(k_ref),
+        int(k_gen), float(scale), _ptr(q), _ptr(workspace), workspace.numel(), _ptr(keep_idx),
+        _ptr(o_coarse), _ptr(gate), _ptr(out), _ptr(bwd_workspace), bwd_workspace.numel(),
+        _stream(stream)), "vsa_sparse_attn_fwd_train")
 
 
 def vsa_gate_proj(x: torch.Tensor, w_gate: torch.Tensor, g: torch.Tensor, stream=None) -> None:
@@ -531,6 +566,7 @@ class TileSparseAttention:
                             stream=stream)
 
     def fine(self, q, gate, out, stream=None) -> None:
+        self._stats_saved = False
         keep = self.keep_idx if self.list_len > 0 else None
         if self.int8:
             vsa_sparse_attn_fwd_i8(self.plan.info, self.row_src, self.block_len, self.heads,
@@ -546,13 +582,31 @@ class TileSparseAttention:
                                 self.head_dim, self.k, q, self.workspace, keep, self.o_coarse,
                                 gate, out, scale=self.scale, stream=stream)
 
-    def backward(self, q, k, v, gate, dout, stream=None):
-        """Gradients (dq, dk, dv, dgate), fp32, of the last forward's layer with its
-        keep sets held fixed. Call after coarse() and fine() on the same inputs."""
+    def _bwd_workspace(self, device):
         if not hasattr(self, "bwd_workspace"):
             lay = vsa_bwd_workspace_layout(self.plan.info, self.heads, self.head_dim)
             self.bwd_layout = lay
-            self.bwd_workspace = torch.empty(lay.total_bytes, dtype=torch.uint8, device=q.device)
+            self.bwd_workspace = torch.empty(lay.total_bytes, dtype=torch.uint8, device=device)
+        return self.bwd_workspace
+
+    def fine_train(self, q, gate, out, stream=None) -> None:
+        """The fine pass of a training step: fine()'s output, plus the lse and O_fine
+        saved for the next backward() (bf16 path; not with int8)."""
+        if self.int8:
+            raise ValueError("the training forward is bf16; this layer runs the INT8 pass")
+        keep = self.keep_idx if self.list_len > 0 else None
+        vsa_sparse_attn_fwd_train(self.plan.info, self.row_src, self.block_len, self.heads,
+                                  self.head_dim, self.k_ref if self.ref else -1, self.k, q,
+                                  self.workspace, keep, self.o_coarse, gate, out,
+                                  self._bwd_workspace(q.device), scale=self.scale, stream=stream)
+        self._stats_saved = True
+
+    def backward(self, q, k, v, gate, dout, stream=None):
+        """Gradients (dq, dk, dv, dgate), fp32, of the last forward's layer with its
+        keep sets held fixed. Call after coarse() and fine() (or fine_train(), whose
+        saved statistics it then uses) on the same inputs."""
+        self._bwd_workspace(q.device)
+        saved = getattr(self, "_stats_saved", False)
         dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         dk, dv = torch.empty_like(dq), torch.empty_like(dq)
         dgate = torch.empty(gate.shape, dtype=torch.float32, device=q.device)
@@ -560,7 +614,7 @@ class TileSparseAttention:
         vsa_sparse_attn_bwd(self.plan.info, self.row_src, self.block_len, self.heads, self.head_dim,
                             self.k_ref if self.ref else -1, self.k, q, k, v, gate, dout,
                             self.workspace, keep, self.o_coarse, self.bwd_workspace, dq, dk, dv,
-                            dgate, scale=self.scale, stream=stream)
+                            dgate, scale=self.scale, stream=stream, saved_stats=saved)
         return dq, dk, dv, dgate
 
     def tile_pair_fraction(self) -> float:

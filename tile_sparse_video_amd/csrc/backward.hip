@@ -1044,10 +1044,47 @@ void compute_bwd_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_
     const size_t items = H * n_t * size_t(info.tile_rows / 64);
     L->part_dq = take(split_chunks(info, head_dim) > 1 ? items * 8 * 64 * D * 4 : 0);
     L->part_dkv = take(dkdv_split(info, heads, head_dim) ? H * n_t * 8 * size_t(info.tile_rows / 32) * 2 * 32 * D * 4 : 0);
+    // fp32 O_fine saved by a training forward, only when the key lists split.
+    L->ofine = take(split_chunks(info, head_dim) > 1 ? H * S_pad * D * 4 : 0);
     L->total_bytes = off;
 }
 
 namespace {
+
+// D_t = dout[t] . O_fine[t] per tile-order row of every head, from the fp32
+// O_fine a training forward saved (0 on padding rows); one thread per row,
+// d in ascending order.
+template <int D>
+__global__ __launch_bounds__(256) void dt_kernel(const uint16_t *__restrict__ dout, const float *__restrict__ ofine,
+                                                 const int32_t *__restrict__ row_src, int H, int64_t S_pad,
+                                                 float *__restrict__ dt)
+{
+    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= int64_t(H) * S_pad) return;
+    const int h = int(idx / S_pad);
+    const int64_t row = idx % S_pad;
+    const int tok = row_src[row];
+    float acc = 0.f;
+    if (tok >= 0) {
+        const uint16_t *g = dout + (size_t(tok) * H + h) * D;
+        const float *o = ofine + size_t(idx) * D;
+#pragma unroll 4
+        for (int d = 0; d < D; d += 8) {
+            const uint4 raw = *reinterpret_cast<const uint4 *>(g + d);
+            const float4 o0 = *reinterpret_cast<const float4 *>(o + d);
+            const float4 o1 = *reinterpret_cast<const float4 *>(o + d + 4);
+            acc += __uint_as_float(raw.x << 16) * o0.x;
+            acc += __uint_as_float(raw.x & 0xffff0000u) * o0.y;
+            acc += __uint_as_float(raw.y << 16) * o0.z;
+            acc += __uint_as_float(raw.y & 0xffff0000u) * o0.w;
+            acc += __uint_as_float(raw.z << 16) * o1.x;
+            acc += __uint_as_float(raw.z & 0xffff0000u) * o1.y;
+            acc += __uint_as_float(raw.w << 16) * o1.z;
+            acc += __uint_as_float(raw.w & 0xffff0000u) * o1.w;
+        }
+    }
+    dt[idx] = acc;
+}
 
 template <int D, int B>
 void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, const uint16_t *v,
@@ -1142,7 +1179,8 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
                                    const void *dout, const void *workspace, size_t workspace_bytes,
                                    const int32_t *keep_idx_dev, const float *o_coarse_dev,
                                    void *bwd_workspace, size_t bwd_workspace_bytes, float *dq,
-                                   float *dk, float *dv, float *dgate, void *stream)
+                                   float *dk, float *dv, float *dgate, int32_t saved_stats,
+                                   void *stream)
 {
     clear_error();
     const char *name = "vsa_sparse_attn_bwd";
@@ -1233,7 +1271,22 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
     // and a statistics merge, and dQ is split the same way; small heads
     // recompute them inside the dq kernel.
     bool split = false;
-    if (split_chunks(*info, head_dim) > 1) {
+    if (split_chunks(*info, head_dim) > 1 && saved_stats) {
+        // lse came with the training forward; D_t from its saved O_fine.
+        const int64_t rows = int64_t(heads) * info->rows_padded;
+        KernelTimer t(K_BWD_STATS, st);
+        auto *dtp = reinterpret_cast<float *>(bw + BL.dt);
+        auto *ofp = reinterpret_cast<const float *>(bw + BL.ofine);
+        if (head_dim == 128)
+            hipLaunchKernelGGL(dt_kernel<128>, dim3(unsigned((rows + 255) / 256)), dim3(256), 0, st,
+                               static_cast<const uint16_t *>(dout), ofp, row_src_dev, heads,
+                               int64_t(info->rows_padded), dtp);
+        else
+            hipLaunchKernelGGL(dt_kernel<64>, dim3(unsigned((rows + 255) / 256)), dim3(256), 0, st,
+                               static_cast<const uint16_t *>(dout), ofp, row_src_dev, heads,
+                               int64_t(info->rows_padded), dtp);
+        split = true;
+    } else if (split_chunks(*info, head_dim) > 1) {
         const int stv = fine_stats(*info, row_src_dev, block_len_dev, heads, head_dim, ref, k_gen,
                                    ref ? k_ref : 0, a.scale, q, workspace, keep_idx_dev, dout,
                                    reinterpret_cast<float *>(bw + BL.lse),
@@ -1251,4 +1304,33 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(VSA_ERR_DEVICE, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
     return VSA_OK;
+}
+
+extern "C" int vsa_sparse_attn_fwd_train(const vsa_plan_info *info, const int32_t *row_src_dev,
+                                         const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                                         int32_t k_ref, int32_t k_gen, float scale, const void *q,
+                                         const void *workspace, size_t workspace_bytes,
+                                         const int32_t *keep_idx_dev, const float *o_coarse_dev,
+                                         const void *gate, void *out, void *bwd_workspace,
+                                         size_t bwd_workspace_bytes, void *stream)
+{
+    clear_error();
+    const char *name = "vsa_sparse_attn_fwd_train";
+    if (int st = check_info(info)) return st;
+    if (heads <= 0) return fail(VSA_ERR_ARG, "%s: heads = %d", name, heads);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(VSA_ERR_UNSUPPORTED, "%s: head_dim = %d; supported: 64, 128", name, head_dim);
+    if (!bwd_workspace) return fail(VSA_ERR_ARG, "%s: null device pointer", name);
+    vsa_bwd_layout BL;
+    compute_bwd_layout(*info, heads, head_dim, &BL);
+    if (bwd_workspace_bytes < BL.total_bytes)
+        return fail(VSA_ERR_ARG, "%s: backward workspace has %zu bytes, needs %zu", name,
+                    bwd_workspace_bytes, BL.total_bytes);
+    if (reinterpret_cast<uintptr_t>(bwd_workspace) % 256 != 0)
+        return fail(VSA_ERR_ARG, "%s: workspaces must be 256-byte aligned", name);
+    char *bw = static_cast<char *>(bwd_workspace);
+    return fine_impl(name, info, row_src_dev, block_len_dev, heads, heads, head_dim, k_ref >= 0, false,
+                     k_gen, k_ref < 0 ? 0 : k_ref, scale, q, workspace, workspace_bytes, keep_idx_dev,
+                     o_coarse_dev, gate, out, stream, reinterpret_cast<float *>(bw + BL.lse),
+                     reinterpret_cast<float *>(bw + BL.ofine));
 }

@@ -63,6 +63,9 @@ class KernelTimer {
 // Bodies of the coarse and fine entry points, also driven per head group by
 // vsa_layer_fwd_groups. ld is the number of heads per token row of q, k, v,
 // gate and out (>= heads); the pointers address the first head processed.
+// fine_impl with lse_out and ofine_out set (a training forward) also writes,
+// when the key lists are split, the per-row lse and fp32 O_fine ([H][S_pad]
+// and [H][S_pad][D], tile order) for the backward.
 int coarse_impl(const char *name, const vsa_plan_info *info, const int32_t *row_src_dev,
                 const int32_t *block_len_dev, int heads, int ld, int head_dim, bool ref, double sparsity,
                 int64_t keep_k, double ref_sparsity, int64_t ref_keep_k, float scale, const void *q,
@@ -72,7 +75,7 @@ int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_sr
               const int32_t *block_len_dev, int heads, int ld, int head_dim, bool ref, bool i8, int k,
               int k_ref, float scale, const void *q, const void *workspace, size_t workspace_bytes,
               const int32_t *keep_idx_dev, const float *o_coarse_dev, const void *gate, void *out,
-              void *stream);
+              void *stream, float *lse_out, float *ofine_out);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -82,6 +82,9 @@ struct FineArgs {
     // log-sum-exp and D_t = dout . O_fine instead of the gated output.
     const uint16_t *dout;       // [S][H][D]
     float *lse_out, *dt_out;    // [H][S_pad]
+    // Training forward: the gated output plus, per tile-order row, the lse and
+    // the normalised fine output O_fine in fp32 ([H][S_pad][D]).
+    float *ofine_out;
     // INT8 scores: K codes in tile order [H][n_t][B/64][2][D/32][64][16] and one
     // scale per 64-row block [H][n_t][B/64].
     const uint8_t *k8;
@@ -508,7 +511,11 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
 // M = max_c m_c, w_c = l_c 2^((m_c - M) scale log2 e), O = sum_c w_c (O/l)_c,
 // L = sum_c w_c, then the same gated epilogue as the direct path.
 // One wavefront per item, lanes laid out as in the fine kernel.
-template <int D, int B, bool STATS>
+// MODE: kMergeOut = the gated output; kMergeStats = per-row lse and
+// D_t = dout . O_fine instead (backward support); kMergeTrain = the gated
+// output plus per-row lse and O_fine (a training forward).
+constexpr int kMergeOut = 0, kMergeStats = 1, kMergeTrain = 2;
+template <int D, int B, int MODE>
 __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
 {
     constexpr int SUB = B / 64, DB = D / 32;
@@ -563,7 +570,26 @@ __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
                 }
             }
     }
-    if (STATS) {
+    if (MODE == kMergeTrain) {
+        // lse (log2 domain, +inf on padding rows) and O_fine (0 on padding rows).
+        const size_t S_pad = size_t(a.n_t) * B;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int row = tile * B + 64 * qsub + 32 * qb + l32;
+            const bool real = a.row_src[row] >= 0;
+            const float inv = real ? 1.0f / L[qb] : 0.f;
+            float *orow = a.ofine_out + (size_t(h) * S_pad + row) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<float4 *>(orow + 32 * db + 8 * i + 4 * half) =
+                        make_float4(O[db][qb][4 * i] * inv, O[db][qb][4 * i + 1] * inv,
+                                    O[db][qb][4 * i + 2] * inv, O[db][qb][4 * i + 3] * inv);
+            if (half == 0) a.lse_out[size_t(h) * S_pad + row] = real ? M[qb] * c2 + __log2f(L[qb]) : INFINITY;
+        }
+    }
+    if (MODE == kMergeStats) {
         // lse (log2 domain) and D_t = dout . O_fine per row; +inf / 0 on padding rows.
         const size_t S_pad = size_t(a.n_t) * B;
 #pragma unroll
@@ -671,7 +697,7 @@ __global__ __launch_bounds__(256) void quant_k_kernel(const uint16_t *__restrict
 }
 
 template <int D, int B, bool I8 = false>
-void launch_fine(const FineArgs &a, hipStream_t st)
+void launch_fine(const FineArgs &a, hipStream_t st, bool train = false)
 {
     const int items = a.H * a.n_t * (B / 64);
     if (I8) {
@@ -685,7 +711,10 @@ void launch_fine(const FineArgs &a, hipStream_t st)
             hipLaunchKernelGGL((fine_attn_kernel<D, B, true, I8>), dim3(items * a.chunks), dim3(64), 0, st, a);
         }
         KernelTimer t(K_MERGE, st);
-        hipLaunchKernelGGL((merge_kernel<D, B, false>), dim3((items + 3) / 4), dim3(256), 0, st, a, items);
+        if (train)
+            hipLaunchKernelGGL((merge_kernel<D, B, kMergeTrain>), dim3((items + 3) / 4), dim3(256), 0, st, a, items);
+        else
+            hipLaunchKernelGGL((merge_kernel<D, B, kMergeOut>), dim3((items + 3) / 4), dim3(256), 0, st, a, items);
     } else {
         KernelTimer t(K_FINE_ATTN, st);
         hipLaunchKernelGGL((fine_attn_kernel<D, B, false, I8>), dim3(items), dim3(64), 0, st, a);
@@ -701,7 +730,7 @@ void launch_fine_stats(const FineArgs &a, hipStream_t st)
     {
         KernelTimer t(K_BWD_STATS, st);
         hipLaunchKernelGGL((fine_attn_kernel<D, B, true>), dim3(items * a.chunks), dim3(64), 0, st, a);
-        hipLaunchKernelGGL((merge_kernel<D, B, true>), dim3((items + 3) / 4), dim3(256), 0, st, a, items);
+        hipLaunchKernelGGL((merge_kernel<D, B, kMergeStats>), dim3((items + 3) / 4), dim3(256), 0, st, a, items);
     }
 }
 
@@ -770,7 +799,7 @@ int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_sr
               const int32_t *block_len_dev, int heads, int ld, int head_dim, bool ref, bool i8, int k, int k_ref,
               float scale, const void *q, const void *workspace, size_t workspace_bytes,
               const int32_t *keep_idx_dev, const float *o_coarse_dev, const void *gate, void *out,
-              void *stream)
+              void *stream, float *lse_out, float *ofine_out)
 {
     if (int st = check_info(info)) return st;
     if (heads <= 0 || ld < heads) return fail(VSA_ERR_ARG, "%s: heads = %d (row stride %d)", name, heads, ld);
@@ -820,6 +849,9 @@ int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_sr
     a.out = static_cast<uint16_t *>(out);
     a.part_o = reinterpret_cast<uint16_t *>(ws + L.part_o);
     a.part_ml = reinterpret_cast<float *>(ws + L.part_ml);
+    a.lse_out = lse_out;
+    a.ofine_out = ofine_out;
+    const bool train = lse_out && ofine_out && chunks > 1;
     a.k8 = reinterpret_cast<const uint8_t *>(ws + L.k_i8);
     a.k_scale = reinterpret_cast<const float *>(ws + L.k_scale);
     a.H = heads;
@@ -837,11 +869,11 @@ int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_sr
     (void)hipGetLastError();
     const int B = info->tile_rows;
     if (head_dim == 128) {
-        if (B == 64) i8 ? launch_fine<128, 64, true>(a, st) : launch_fine<128, 64>(a, st);
-        else i8 ? launch_fine<128, 128, true>(a, st) : launch_fine<128, 128>(a, st);
+        if (B == 64) i8 ? launch_fine<128, 64, true>(a, st, train) : launch_fine<128, 64>(a, st, train);
+        else i8 ? launch_fine<128, 128, true>(a, st, train) : launch_fine<128, 128>(a, st, train);
     } else {
-        if (B == 64) i8 ? launch_fine<64, 64, true>(a, st) : launch_fine<64, 64>(a, st);
-        else i8 ? launch_fine<64, 128, true>(a, st) : launch_fine<64, 128>(a, st);
+        if (B == 64) i8 ? launch_fine<64, 64, true>(a, st, train) : launch_fine<64, 64>(a, st, train);
+        else i8 ? launch_fine<64, 128, true>(a, st, train) : launch_fine<64, 128>(a, st, train);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(VSA_ERR_DEVICE, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
@@ -860,7 +892,7 @@ extern "C" int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row
     clear_error();
     return fine_impl("vsa_sparse_attn_fwd", info, row_src_dev, block_len_dev, heads, heads, head_dim, false,
                      false, k, 0, scale, q, workspace, workspace_bytes, keep_idx_dev, o_coarse_dev, gate,
-                     out, stream);
+                     out, stream, nullptr, nullptr);
 }
 
 extern "C" int vsa_sparse_attn_fwd_ref(const vsa_plan_info *info, const int32_t *row_src_dev,
@@ -873,7 +905,7 @@ extern "C" int vsa_sparse_attn_fwd_ref(const vsa_plan_info *info, const int32_t 
     clear_error();
     return fine_impl("vsa_sparse_attn_fwd_ref", info, row_src_dev, block_len_dev, heads, heads, head_dim,
                      true, false, k_gen, k_ref, scale, q, workspace, workspace_bytes, keep_idx_dev,
-                     o_coarse_dev, gate, out, stream);
+                     o_coarse_dev, gate, out, stream, nullptr, nullptr);
 }
 
 extern "C" int vsa_sparse_attn_fwd_i8(const vsa_plan_info *info, const int32_t *row_src_dev,
@@ -886,5 +918,5 @@ extern "C" int vsa_sparse_attn_fwd_i8(const vsa_plan_info *info, const int32_t *
     clear_error();
     return fine_impl("vsa_sparse_attn_fwd_i8", info, row_src_dev, block_len_dev, heads, heads, head_dim,
                      k_ref >= 0, true, k_gen, k_ref < 0 ? 0 : k_ref, scale, q, workspace,
-                     workspace_bytes, keep_idx_dev, o_coarse_dev, gate, out, stream);
+                     workspace_bytes, keep_idx_dev, o_coarse_dev, gate, out, stream, nullptr, nullptr);
 }

@@ -85,7 +85,7 @@ extern "C" int vsa_layer_fwd_groups(const vsa_head_group *groups, int32_t n_grou
         if (int st = fine_impl(name, g.info, g.row_src_dev, g.block_len_dev, g.heads, heads_total, head_dim,
                                g.ref != 0, g.int8 != 0, kk[size_t(i)], kr[size_t(i)], scale, at(q),
                                g.workspace, g.workspace_bytes, g.keep_idx_dev, g.o_coarse_dev, at(gate),
-                               static_cast<char *>(out) + first, stream))
+                               static_cast<char *>(out) + first, stream, nullptr, nullptr))
             return st;
     }
     return VSA_OK;
