@@ -746,6 +746,7 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdArgs a, int n_items)
 
 // ------------------------------------------------------------------ dkdv --
 //
+// Heads too small to split (the split ones use dkdv_ring_kernel below).
 // One wavefront per (head, key tile, 32 key rows), the key tile's waves in one
 // workgroup. The wave holds its keys' K^T and V^T operand fragments (natural rows) and the dK^T, dV^T
 // accumulators (lane = key column), and walks the query tiles of the key
@@ -756,22 +757,17 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdArgs a, int n_items)
 // row-layout operands and row statistics of the next block are fetched while
 // the current one is computed (two register sets, the loop unrolled by two).
 // The dK^T, dV^T accumulators stay in AGPRs for the whole walk.
-template <int D, int B, bool SPLIT>
+template <int D, int B>
 __global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
 {
-    constexpr int SUB = B / 64, NC = D / 16, DB = D / 32, FR = D / 8, KB = B / 32;
-    constexpr int kListCap = 4096;
+    constexpr int SUB = B / 64, NC = D / 16, DB = D / 32, FR = D / 8;
     // One workgroup per (head, key tile): wave kb owns key rows 32kb..32kb+31.
     // The waves walk the same query list in step, so the second wave's
-    // fragment reads are served by the CU's L1. Split: 8 workgroups per key
-    // tile, chunk c = block % 8 (so on XCD c) taking the query tiles with id
-    // = c mod 8, each writing partial dK, dV.
+    // fragment reads are served by the CU's L1.
     const int lane = threadIdx.x % kWave, l32 = lane & 31, half = lane >> 5;
     const int kb = threadIdx.x / kWave;
-    const int ht = SPLIT ? int(blockIdx.x / 8) : int(blockIdx.x);
-    const int chunk = SPLIT ? int(blockIdx.x % 8) : 0;
+    const int ht = int(blockIdx.x);
     const int h = ht / a.n_t, tile = ht % a.n_t;
-    __shared__ int32_t flist[SPLIT ? kListCap : 1];
     const size_t S_pad = size_t(a.n_t) * B;
 
     // Own keys as B operands: lane -> key 32kb + l32 of the tile, slots d = 16c + 8 half + e.
@@ -792,26 +788,8 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
     for (int db = 0; db < DB; ++db) GK[db] = GV[db] = f32x16_t{};
     const float c2 = a.scale_log2e;
 
-    int cnt = a.tcount[size_t(h) * a.n_t + tile];
+    const int cnt = a.tcount[size_t(h) * a.n_t + tile];
     const int32_t *lst = a.tlist + (size_t(h) * a.n_t + tile) * a.n_t;
-    if (SPLIT) {
-        // This chunk's query tiles, compacted in order into LDS by wave 0.
-        if (kb == 0) {
-            int n = 0;
-            for (int x0 = 0; x0 < cnt; x0 += kWave) {
-                const int x = x0 + lane;
-                const int qt = x < cnt ? lst[x] : -1;
-                const bool m = qt >= 0 && qt % 8 == chunk;
-                const uint64_t bal = __ballot(m);
-                if (m) flist[n + __popcll(bal & lanes_below(lane))] = qt;
-                n += __popcll(bal);
-            }
-            if (lane == 0) flist[kListCap - 1] = n;
-        }
-        __syncthreads();
-        cnt = flist[kListCap - 1];
-        lst = flist;
-    }
     const int n_blocks = cnt * SUB * 2;  // 32-row query blocks (even)
 
     // Operands of block b: query tile lst[b / (2 SUB)], 64-row block (b / 2) % SUB, half b % 2.
@@ -905,21 +883,6 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
             compute(b + 1, Bo);
         }
     }
-    if (SPLIT) {
-        // partial dK^T, dV^T, fp32 in register order: [H][n_t][8][KB][2][DB][64][16]
-        float *pd = a.part_dkv + ((size_t(ht) * 8 + chunk) * KB + kb) * (2 * DB * kWave * 16);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            float4 *dk4 = reinterpret_cast<float4 *>(pd + (db * kWave + lane) * 16);
-            float4 *dv4 = reinterpret_cast<float4 *>(pd + ((DB + db) * kWave + lane) * 16);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                dk4[q4] = make_float4(GK[db][4 * q4], GK[db][4 * q4 + 1], GK[db][4 * q4 + 2], GK[db][4 * q4 + 3]);
-                dv4[q4] = make_float4(GV[db][4 * q4], GV[db][4 * q4 + 1], GV[db][4 * q4 + 2], GV[db][4 * q4 + 3]);
-            }
-        }
-        return;
-    }
     if (ktok < 0) return;
     // dk = scale dK_fine + dkm / n, dv = dV_fine + dvm / n; acc 4i + j <-> d = 32db + 8i + 4 half + j.
     const float inv_n = 1.0f / float(a.block_len[tile]);
@@ -946,6 +909,234 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
             *reinterpret_cast<float4 *>(dk + d0) = ok;
             *reinterpret_cast<float4 *>(dv + d0) = ov;
         }
+}
+
+// ------------------------------------------------------------- dkdv ring --
+//
+// The dK/dV pass for split heads with the query-side operands shared through
+// LDS. A workgroup (one key tile, one chunk of its transposed list; wave kb
+// owns key rows 32kb..32kb+31 with their K^T, V^T in registers and dK^T, dV^T
+// in AGPRs) walks 32-row query blocks through a ring of NBUF LDS stages. A
+// stage holds the block's Q and dO row fragments, its Q and dO column
+// fragments (1 KB each, the tile-ordered copies) and the lse and D_t of its
+// rows. The waves fill a stage together with buffer-to-LDS loads (each wave a
+// fixed share of the fragments plus one row-statistics load: wave 0 the lse,
+// wave 1 the D_t, further waves a spare copy), so a fragment crosses from L2
+// once per workgroup and never occupies VGPRs in flight; a stage is refilled
+// NBUF - 1 blocks ahead of its use. Every wave issues the same number of
+// loads per block (past the end of the list it reloads the last block into
+// the free stage), so one wait on its own load counter, then a plain barrier,
+// makes the whole stage visible; a second barrier after the reads frees the
+// stage. Nothing else in the loop issues vector-memory loads, so the load
+// counter counts exactly the ring's loads.
+template <int D, int B>
+struct RingCfg {
+    static constexpr int NC = D / 16, DB = D / 32, KB = B / 32;
+    static constexpr int FRAGS = 2 * NC + 4 * DB;       // Qr, Or, Qc, Oc fragments per block
+    static constexpr int LPW = FRAGS / KB;              // fragment loads per wave per block
+    static constexpr int NBUF = B == 64 ? 2 : 3;        // stages (B = 64: two workgroups per CU)
+    static constexpr int STAGE = FRAGS * 1024 + KB * 256;  // + 64 lse, 64 D_t (+ spare areas)
+    static constexpr int LIST = 4096;                   // uint16 query-tile ids of the chunk
+    static constexpr size_t LDS = size_t(NBUF) * STAGE + LIST * 2;
+};
+
+// s_waitcnt immediate (gfx9 encoding) waiting until at most n vector-memory
+// loads are outstanding, with the export and LDS counters left alone.
+#define VSA_VMCNT(n) (((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+template <int D, int B>
+__global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
+{
+    using C = RingCfg<D, B>;
+    constexpr int SUB = B / 64, NC = C::NC, DB = C::DB, FR = D / 8, KB = C::KB;
+    constexpr int NBUF = C::NBUF, LPW = C::LPW, STAGE = C::STAGE;
+    extern __shared__ __attribute__((aligned(16))) char ring_lds[];
+    uint16_t *flist = reinterpret_cast<uint16_t *>(ring_lds + size_t(NBUF) * STAGE);
+    const int lane = threadIdx.x % kWave, l32 = lane & 31, half = lane >> 5;
+    const int kb = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+    const int ht = blockIdx.x / 8, chunk = blockIdx.x % 8;
+    const int h = ht / a.n_t, tile = ht % a.n_t;
+    const size_t S_pad = size_t(a.n_t) * B;
+
+    // Own keys as B operands: lane -> key 32kb + l32 of the tile, slots d = 16c + 8 half + e.
+    const int ktok = a.row_src[tile * B + 32 * kb + l32];
+    bf16x8_t Kt[NC], Vt[NC];
+    {
+        const size_t base = (size_t(ktok < 0 ? 0 : ktok) * a.H + h) * D + 8 * half;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            Kt[c] = *reinterpret_cast<const bf16x8_t *>(a.kn + base + 16 * c);
+            Vt[c] = *reinterpret_cast<const bf16x8_t *>(a.vn + base + 16 * c);
+            if (ktok < 0) Kt[c] = Vt[c] = bf16x8_t{};
+        }
+    }
+    f32x16_t GK[DB], GV[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) GK[db] = GV[db] = f32x16_t{};
+    const float c2 = a.scale_log2e;
+
+    // This chunk's query tiles (id % 8 == chunk), compacted in order by wave 0.
+    if (kb == 0) {
+        const int cnt_all = a.tcount[size_t(h) * a.n_t + tile];
+        const int32_t *lst = a.tlist + (size_t(h) * a.n_t + tile) * a.n_t;
+        int n = 0;
+        for (int x0 = 0; x0 < cnt_all; x0 += kWave) {
+            const int x = x0 + lane;
+            const int qt = x < cnt_all ? lst[x] : -1;
+            const bool m = qt >= 0 && qt % 8 == chunk;
+            const uint64_t bal = __ballot(m);
+            if (m) flist[n + __popcll(bal & lanes_below(lane))] = uint16_t(qt);
+            n += __popcll(bal);
+        }
+        if (lane == 0) flist[C::LIST - 1] = uint16_t(n);
+    }
+    __syncthreads();  // also orders the key loads above before the ring's load counting
+    const int n_blocks = int(flist[C::LIST - 1]) * SUB * 2;
+
+    const uint32_t frag_bytes = uint32_t(S_pad) * D * 2;
+    const size_t head_elems = size_t(h) * S_pad * D;
+    auto rsrc = [&](const uint16_t *p) {
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(p + head_elems), (short)0, frag_bytes, kRsrcWord3);
+    };
+    const __amdgpu_buffer_rsrc_t rqr = rsrc(a.qrow), ror = rsrc(a.dorow), rqc = rsrc(a.qcol), roc = rsrc(a.docol);
+    // Row statistics: wave 0 reads lse, the others D_t (only wave 1's copy is used).
+    const uint64_t stat_base = reinterpret_cast<uint64_t>((kb == 0 ? a.lse : a.dt) + size_t(h) * S_pad);
+    const uint64_t stat_uni = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(stat_base)))) |
+                              uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(stat_base >> 32)))) << 32;
+    const __amdgpu_buffer_rsrc_t rstat = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void *>(stat_uni), (short)0, uint32_t(S_pad) * 4, kRsrcWord3);
+
+    // Issue this wave's loads of block b into stage `slot`: fragments
+    // j = kb*LPW + t (Qr c, Or c, Qc (db, cc), Oc (db, cc)) and 64 row
+    // statistics from the block's first row (lanes 0-31 are the block's rows;
+    // rows past the head's end read as zero).
+    auto issue = [&](int b, int slot) {
+        const int qt = __builtin_amdgcn_readfirstlane(int(flist[b / (2 * SUB)]));
+        const int sub = (b / 2) % SUB, qb = b % 2;
+        const uint32_t fb = uint32_t(qt * SUB + sub) * FR * 1024u;
+        char *stage = ring_lds + slot * STAGE;
+#pragma unroll
+        for (int t = 0; t < LPW; ++t) {
+            const int j = kb * LPW + t;
+            __amdgpu_buffer_rsrc_t r;
+            uint32_t f;
+            if (j < NC) {
+                r = rqr;
+                f = qb * NC + j;
+            } else if (j < 2 * NC) {
+                r = ror;
+                f = qb * NC + (j - NC);
+            } else {
+                const int jj = (j - 2 * NC) % (2 * DB);
+                r = j < 2 * NC + 2 * DB ? rqc : roc;
+                f = 4 * (jj / 2) + 2 * qb + (jj % 2);
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void *)(stage + j * 1024), 16, lane * 16, fb + f * 1024u, 0, 0);
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rstat, (__attribute__((address_space(3))) void *)(stage + C::FRAGS * 1024 + kb * 256), 4, lane * 4,
+            uint32_t(qt * B + 64 * sub + 32 * qb) * 4u, 0, 0);
+    };
+    auto compute = [&](int b) {
+        const char *stage = ring_lds + (b % NBUF) * STAGE;
+        auto frag = [&](int j) { return *reinterpret_cast<const bf16x8_t *>(stage + j * 1024 + lane * 16); };
+        f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(c), Kt[c], S, 0, 0, 0);
+            dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(NC + c), Vt[c], dP, 0, 0, 0);
+        }
+        // Row statistics of the block: lse at rows 8i + 4 half + j (i, j < 4) and
+        // D_t 256 bytes further. Read in one asm block that also waits for the
+        // reads, so the compiler sees no LDS load it would order after a wait
+        // for every buffer-to-LDS load in flight (the next stage's included).
+        // The outputs are early-clobber: the address must not share a register
+        // with a result, since the later reads still use it.
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        f32x4_t L[4], Dv[4];
+        const uint32_t st_addr = uint32_t(reinterpret_cast<uintptr_t>(stage)) + C::FRAGS * 1024 + 16 * half;
+        asm volatile(
+            "ds_read_b128 %0, %8\n\t"
+            "ds_read_b128 %1, %8 offset:32\n\t"
+            "ds_read_b128 %2, %8 offset:64\n\t"
+            "ds_read_b128 %3, %8 offset:96\n\t"
+            "ds_read_b128 %4, %8 offset:256\n\t"
+            "ds_read_b128 %5, %8 offset:288\n\t"
+            "ds_read_b128 %6, %8 offset:320\n\t"
+            "ds_read_b128 %7, %8 offset:352\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(L[0]), "=&v"(L[1]), "=&v"(L[2]), "=&v"(L[3]), "=&v"(Dv[0]), "=&v"(Dv[1]), "=&v"(Dv[2]),
+              "=&v"(Dv[3])
+            : "v"(st_addr)
+            : "memory");
+        f32x16_t Pm, dS;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float l4[4] = {L[i].x, L[i].y, L[i].z, L[i].w}, d4[4] = {Dv[i].x, Dv[i].y, Dv[i].z, Dv[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * i + j], c2, -l4[j]));
+                Pm[4 * i + j] = p;
+                dS[4 * i + j] = p * (dP[4 * i + j] - d4[j]);
+            }
+        }
+        const bf16x8_t p0 = pack8(Pm, 0), p1 = pack8(Pm, 1);
+        const bf16x8_t s0 = pack8(dS, 0), s1 = pack8(dS, 1);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(2 * NC + 2 * DB + 2 * db), p0, GV[db], 0, 0, 0);
+            GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(2 * NC + 2 * DB + 2 * db + 1), p1, GV[db], 0, 0, 0);
+            GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(2 * NC + 2 * db), s0, GK[db], 0, 0, 0);
+            GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(2 * NC + 2 * db + 1), s1, GK[db], 0, 0, 0);
+        }
+    };
+    if (n_blocks > 0) {
+#pragma unroll
+        for (int b = 0; b < NBUF - 1; ++b) issue(min(b, n_blocks - 1), b);
+    }
+    for (int b = 0; b < n_blocks; ++b) {
+        // The empty asm statements keep the compiler from moving LDS accesses
+        // across the hand-placed waits and barriers (which carry no fence).
+        // Past the list's end the last block is reloaded into the free stage
+        // (never read), so the wait below is the same on every iteration.
+        const int nb = b + NBUF - 1;
+        issue(nb < n_blocks ? nb : n_blocks - 1, nb % NBUF);
+        __builtin_amdgcn_s_waitcnt(VSA_VMCNT((NBUF - 1) * (LPW + 1)));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();     // every wave's part of stage b % NBUF has landed
+        asm volatile("" ::: "memory");
+        compute(b);
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // LDS reads of the stage done (lgkmcnt 0)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();     // the stage may be refilled
+        asm volatile("" ::: "memory");
+    }
+    // partial dK^T, dV^T, fp32 in register order: [H][n_t][8][KB][2][DB][64][16]
+    float *pd = a.part_dkv + ((size_t(ht) * 8 + chunk) * KB + kb) * (2 * DB * kWave * 16);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        float4 *dk4 = reinterpret_cast<float4 *>(pd + (db * kWave + lane) * 16);
+        float4 *dv4 = reinterpret_cast<float4 *>(pd + ((DB + db) * kWave + lane) * 16);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            dk4[q4] = make_float4(GK[db][4 * q4], GK[db][4 * q4 + 1], GK[db][4 * q4 + 2], GK[db][4 * q4 + 3]);
+            dv4[q4] = make_float4(GV[db][4 * q4], GV[db][4 * q4 + 1], GV[db][4 * q4 + 2], GV[db][4 * q4 + 3]);
+        }
+    }
+}
+#undef VSA_VMCNT
+
+// Raises the dynamic-LDS limit of the ring kernel once per process.
+template <int D, int B>
+int ring_lds_attr()
+{
+    static const int status =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&dkdv_ring_kernel<D, B>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(RingCfg<D, B>::LDS)) == hipSuccess
+            ? int(VSA_OK)
+            : int(VSA_ERR_DEVICE);
+    return status;
 }
 
 // Sums the 8 chunk partials of one (head, key tile, 32 key rows) in chunk
@@ -1145,11 +1336,11 @@ void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, 
     {
         KernelTimer t(K_BWD_DKDV, st);
         if (dkdv_split(info, H, D)) {
-            hipLaunchKernelGGL((dkdv_kernel<D, B, true>), dim3(H * n_t * 8), dim3(B * 2), 0, st, a);
+            hipLaunchKernelGGL((dkdv_ring_kernel<D, B>), dim3(H * n_t * 8), dim3(B * 2), (RingCfg<D, B>::LDS), st, a);
             const int units = H * n_t * (B / 32);
             hipLaunchKernelGGL((dkdv_merge_kernel<D, B>), dim3((units + 3) / 4), dim3(256), 0, st, a, units);
         } else {
-            hipLaunchKernelGGL((dkdv_kernel<D, B, false>), dim3(H * n_t), dim3(B * 2), 0, st, a);
+            hipLaunchKernelGGL((dkdv_kernel<D, B>), dim3(H * n_t), dim3(B * 2), 0, st, a);
         }
     }
 }
@@ -1270,6 +1461,12 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
     // Large heads: the log-sum-exp and D_t come from the forward's split kernel
     // and a statistics merge, and dQ is split the same way; small heads
     // recompute them inside the dq kernel.
+    {
+        const int tb = info->tile_rows;
+        const int lds = head_dim == 128 ? (tb == 64 ? ring_lds_attr<128, 64>() : ring_lds_attr<128, 128>())
+                                        : (tb == 64 ? ring_lds_attr<64, 64>() : ring_lds_attr<64, 128>());
+        if (lds != VSA_OK) return fail(VSA_ERR_DEVICE, "%s: cannot raise the LDS limit of the dK/dV kernel", name);
+    }
     bool split = false;
     if (split_chunks(*info, head_dim) > 1 && saved_stats) {
         // lse came with the training forward; D_t from its saved O_fine.
