@@ -917,9 +917,10 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
 // LDS. A workgroup (one key tile, one chunk of its transposed list; wave kb
 // owns key rows 32kb..32kb+31 with their K^T, V^T in registers and dK^T, dV^T
 // in AGPRs) walks 32-row query blocks through a ring of NBUF LDS stages. A
-// stage holds the block's Q and dO row fragments, its Q and dO column
-// fragments (1 KB each, the tile-ordered copies) and the lse and D_t of its
-// rows. The waves fill a stage together with buffer-to-LDS loads (each wave a
+// stage holds the block's Q and dO row fragments (1 KB each, the tile-ordered
+// copies) and the lse and D_t of its rows; the column-layout operands of the
+// dV and dK products are read from the same row fragments with the LDS
+// transpose read (ds_read_b64_tr_b16), so Q and dO cross from L2 once. The waves fill a stage together with buffer-to-LDS loads (each wave a
 // fixed share of the fragments plus one row-statistics load: wave 0 the lse,
 // wave 1 the D_t, further waves a spare copy), so a fragment crosses from L2
 // once per workgroup and never occupies VGPRs in flight; a stage is refilled
@@ -932,9 +933,9 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
 template <int D, int B>
 struct RingCfg {
     static constexpr int NC = D / 16, DB = D / 32, KB = B / 32;
-    static constexpr int FRAGS = 2 * NC + 4 * DB;       // Qr, Or, Qc, Oc fragments per block
+    static constexpr int FRAGS = 2 * NC;                // Qr, Or fragments per block
     static constexpr int LPW = FRAGS / KB;              // fragment loads per wave per block
-    static constexpr int NBUF = B == 64 ? 2 : 3;        // stages (B = 64: two workgroups per CU)
+    static constexpr int NBUF = 4;                      // stages (B = 64: two workgroups per CU)
     static constexpr int STAGE = FRAGS * 1024 + KB * 256;  // + 64 lse, 64 D_t (+ spare areas)
     static constexpr int LIST = 4096;                   // uint16 query-tile ids of the chunk
     static constexpr size_t LDS = size_t(NBUF) * STAGE + LIST * 2;
@@ -998,7 +999,20 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
     auto rsrc = [&](const uint16_t *p) {
         return __builtin_amdgcn_make_buffer_rsrc((void *)(p + head_elems), (short)0, frag_bytes, kRsrcWord3);
     };
-    const __amdgpu_buffer_rsrc_t rqr = rsrc(a.qrow), ror = rsrc(a.dorow), rqc = rsrc(a.qcol), roc = rsrc(a.docol);
+    const __amdgpu_buffer_rsrc_t rqr = rsrc(a.qrow), ror = rsrc(a.dorow);
+    // Transposed reads. A row fragment chunk c holds, at byte 16 l + 2 e, the
+    // block's row l % 32, d = 16c + 8 (l / 32) + e. ds_read_b64_tr_b16 gives
+    // lane i of each 16-lane group the element i % 4 of the 8-byte segments
+    // that lanes i / 4 + 4k (k < 4) address. For the column fragment (db, cc)
+    // (lane L: d = 32 db + L % 32, rows 16 cc + 4 (L / 32) + {0..3} and
+    // + 8 + {0..3}) lane j of group g therefore addresses row
+    // 16 cc + 4 (g / 2) + j / 4 at d = 32 db + 16 (g % 2) + 4 (j % 4); the second
+    // read adds 8 rows. The per-lane part of that address is fixed.
+    const int tg = lane >> 4, ti = lane & 15;
+    const int t_d0 = 16 * (tg & 1) + 4 * (ti & 3);                    // d - 32 db
+    const uint32_t t_base = uint32_t(((t_d0 >> 4) * 1024) +                   // chunk 2 db + g % 2
+                                     ((4 * (tg >> 1) + (ti >> 2)) + 32 * ((t_d0 >> 3) & 1)) * 16 +
+                                     2 * (t_d0 & 7));
     // Row statistics: wave 0 reads lse, the others D_t (only wave 1's copy is used).
     const uint64_t stat_base = reinterpret_cast<uint64_t>((kb == 0 ? a.lse : a.dt) + size_t(h) * S_pad);
     const uint64_t stat_uni = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(stat_base)))) |
@@ -1007,7 +1021,7 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
         reinterpret_cast<void *>(stat_uni), (short)0, uint32_t(S_pad) * 4, kRsrcWord3);
 
     // Issue this wave's loads of block b into stage `slot`: fragments
-    // j = kb*LPW + t (Qr c, Or c, Qc (db, cc), Oc (db, cc)) and 64 row
+    // j = kb*LPW + t (Qr c for j < NC, then Or c) and 64 row
     // statistics from the block's first row (lanes 0-31 are the block's rows;
     // rows past the head's end read as zero).
     auto issue = [&](int b, int slot) {
@@ -1018,19 +1032,8 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
 #pragma unroll
         for (int t = 0; t < LPW; ++t) {
             const int j = kb * LPW + t;
-            __amdgpu_buffer_rsrc_t r;
-            uint32_t f;
-            if (j < NC) {
-                r = rqr;
-                f = qb * NC + j;
-            } else if (j < 2 * NC) {
-                r = ror;
-                f = qb * NC + (j - NC);
-            } else {
-                const int jj = (j - 2 * NC) % (2 * DB);
-                r = j < 2 * NC + 2 * DB ? rqc : roc;
-                f = 4 * (jj / 2) + 2 * qb + (jj % 2);
-            }
+            const __amdgpu_buffer_rsrc_t r = j < NC ? rqr : ror;
+            const uint32_t f = qb * NC + (j < NC ? j : j - NC);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 r, (__attribute__((address_space(3))) void *)(stage + j * 1024), 16, lane * 16, fb + f * 1024u, 0, 0);
         }
@@ -1083,12 +1086,26 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
         }
         const bf16x8_t p0 = pack8(Pm, 0), p1 = pack8(Pm, 1);
         const bf16x8_t s0 = pack8(dS, 0), s1 = pack8(dS, 1);
+        // Column fragment (db, cc) of the Q (first = 0) or dO (first = NC) chunks.
+        auto col = [&](int first, int db, int cc) -> bf16x8_t {
+            typedef short s16x4_t __attribute__((ext_vector_type(4)));
+            const char *p = stage + first * 1024 + t_base + 2048 * db + 256 * cc;
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t *)(p));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t *)(p + 128));
+            const u32x4_t w = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                               __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
+            return as_bf16x8(w);
+        };
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(2 * NC + 2 * DB + 2 * db), p0, GV[db], 0, 0, 0);
-            GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(2 * NC + 2 * DB + 2 * db + 1), p1, GV[db], 0, 0, 0);
-            GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(2 * NC + 2 * db), s0, GK[db], 0, 0, 0);
-            GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(2 * NC + 2 * db + 1), s1, GK[db], 0, 0, 0);
+            GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col(NC, db, 0), p0, GV[db], 0, 0, 0);
+            GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col(NC, db, 1), p1, GV[db], 0, 0, 0);
+            GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col(0, db, 0), s0, GK[db], 0, 0, 0);
+            GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col(0, db, 1), s1, GK[db], 0, 0, 0);
         }
     };
     if (n_blocks > 0) {
