@@ -501,7 +501,7 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
         return S;
     };
     auto mask_pad = [&](f32x16_t &S, int real) {
-        if (real < 32) {
+        if (__builtin_expect(real < 32, 0)) {  // partial tiles only: a wave-uniform branch
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -642,7 +642,7 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
             f32x16_t dS;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float p = __builtin_amdgcn_exp2f(S[e] * c2 - lse[qb]);
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], c2, -lse[qb]));
                 dS[e] = p * (dP[e] - dq_row[qb]);
             }
             const bf16x8_t d0 = pack8(dS, 0), d1 = pack8(dS, 1);
@@ -717,6 +717,7 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdArgs a, int n_items)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             float acc[16] = {};
+#pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const float4 *src = reinterpret_cast<const float4 *>(
                     a.part_dq + (size_t(item) * 8 + c) * (DB * 2 * kWave * 16) + ((db * 2 + qb) * kWave + lane) * 16);
@@ -1179,6 +1180,7 @@ __global__ __launch_bounds__(256) void dkdv_merge_kernel(BwdArgs a, int n_units)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             float acc[16] = {};
+#pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const float4 *src = reinterpret_cast<const float4 *>(
                     a.part_dkv + ((size_t(ht) * 8 + c) * KB + kb) * (2 * DB * kWave * 16) +
