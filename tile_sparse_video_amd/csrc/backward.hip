@@ -1042,15 +1042,21 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
             rstat, (__attribute__((address_space(3))) void *)(stage + C::FRAGS * 1024 + kb * 256), 4, lane * 4,
             uint32_t(qt * B + 64 * sub + 32 * qb) * 4u, 0, 0);
     };
-    auto compute = [&](int b) {
+    // Phase 1 of block b: S = Q K^T and dP = dO V^T from the row fragments.
+    auto phase1 = [&](int b, f32x16_t &S, f32x16_t &dP) {
         const char *stage = ring_lds + (b % NBUF) * STAGE;
         auto frag = [&](int j) { return *reinterpret_cast<const bf16x8_t *>(stage + j * 1024 + lane * 16); };
-        f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+        S = f32x16_t{};
+        dP = f32x16_t{};
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(c), Kt[c], S, 0, 0, 0);
             dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(NC + c), Vt[c], dP, 0, 0, 0);
         }
+    };
+    // Phase 2 of block b: P, dS and the dV, dK products.
+    auto phase2 = [&](int b, const f32x16_t &S, const f32x16_t &dP) {
+        const char *stage = ring_lds + (b % NBUF) * STAGE;
         // Row statistics of the block: lse at rows 8i + 4 half + j (i, j < 4) and
         // D_t 256 bytes further. Read in one asm block that also waits for the
         // reads, so the compiler sees no LDS load it would order after a wait
@@ -1109,26 +1115,39 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
             GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col(0, db, 1), s1, GK[db], 0, 0, 0);
         }
     };
+    // Software pipeline: block b + 1's S and dP products are issued before
+    // block b's softmax, so the matrix cores work while the VALU does. The
+    // empty asm statements keep the compiler from moving LDS accesses across
+    // the hand-placed waits and barriers (which carry no fence). Past the
+    // list's end the last block is reloaded into the free stage (never read),
+    // so every wait below is the same on every iteration.
+    auto step = [&](int b, const f32x16_t &S, const f32x16_t &dP, f32x16_t &Sn, f32x16_t &dPn) {
+        const int nb = b + NBUF - 1;
+        issue(nb < n_blocks ? nb : n_blocks - 1, nb % NBUF);  // into the stage freed by block b - 1
+        __builtin_amdgcn_s_waitcnt(VSA_VMCNT((NBUF - 2) * (LPW + 1)));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();     // every wave's part of stage (b + 1) % NBUF has landed
+        asm volatile("" ::: "memory");
+        if (b + 1 < n_blocks) phase1(b + 1, Sn, dPn);
+        phase2(b, S, dP);
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // LDS reads of stage b % NBUF done (lgkmcnt 0)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();     // stage b % NBUF may be refilled
+        asm volatile("" ::: "memory");
+    };
     if (n_blocks > 0) {
 #pragma unroll
         for (int b = 0; b < NBUF - 1; ++b) issue(min(b, n_blocks - 1), b);
-    }
-    for (int b = 0; b < n_blocks; ++b) {
-        // The empty asm statements keep the compiler from moving LDS accesses
-        // across the hand-placed waits and barriers (which carry no fence).
-        // Past the list's end the last block is reloaded into the free stage
-        // (never read), so the wait below is the same on every iteration.
-        const int nb = b + NBUF - 1;
-        issue(nb < n_blocks ? nb : n_blocks - 1, nb % NBUF);
-        __builtin_amdgcn_s_waitcnt(VSA_VMCNT((NBUF - 1) * (LPW + 1)));
+        __builtin_amdgcn_s_waitcnt(VSA_VMCNT((NBUF - 2) * (LPW + 1)));
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();     // every wave's part of stage b % NBUF has landed
+        __builtin_amdgcn_s_barrier();     // stage 0 has landed
         asm volatile("" ::: "memory");
-        compute(b);
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // LDS reads of the stage done (lgkmcnt 0)
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();     // the stage may be refilled
-        asm volatile("" ::: "memory");
+        f32x16_t Sa, dPa, Sb, dPb;
+        phase1(0, Sa, dPa);
+        for (int b = 0; b < n_blocks; b += 2) {  // n_blocks is even
+            step(b, Sa, dPa, Sb, dPb);
+            step(b + 1, Sb, dPb, Sa, dPa);
+        }
     }
     // partial dK^T, dV^T, fp32 in register order: [H][n_t][8][KB][2][DB][64][16]
     float *pd = a.part_dkv + ((size_t(ht) * 8 + chunk) * KB + kb) * (2 * DB * kWave * 16);
