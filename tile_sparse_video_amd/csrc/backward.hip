@@ -163,10 +163,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t *__restric
 
 // ------------------------------------------------------------ coarse_bwd --
 //
-// Tile-level attention gradient, fp32, natural-log softmax (as the forward).
-// Rows: block per (64 query tiles, head); four threads per query tile, each
-// owning D/4 of the dimension; key tiles stream through LDS in chunks of 32.
-// Writes the row log-sum-exp, Dc_i = dO_c[i] . O_c[i] and dqm_i.
+// Tile-level attention gradient in fp32 on the fp32 matrix cores
+// (v_mfma_f32_32x32x2_f32), laid out as the forward's coarse attention: a
+// workgroup of 4 waves covers 128 tiles of a head, blocks of 32 partner tiles
+// are staged in LDS, and each MFMA contracts the reduction index of lane half
+// h with the one of the other half. Softmax in the log2 domain: with
+// c = scale log2 e, P_ij = exp2(c qm_i.km_j - lse_i), lse_i = log2 sum_j
+// exp2(c qm_i.km_j) (stored in lsec in that domain).
+//
+// Rows: lane = query tile i. Pass 1: lse_i (online max and sum). Pass 2:
+// dZ_ij = scale P_ij (dO_c[i].vm_j - Dc_i) and dqm_i = sum_j dZ_ij km_j; also
+// Dc_i = dO_c[i] . O_c[i].
 template <int D>
 __global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const float *__restrict__ qm,
                                                              const float *__restrict__ km,
@@ -177,89 +184,122 @@ __global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const float *__res
                                                              float *__restrict__ dcc,
                                                              float *__restrict__ dqm)
 {
-    constexpr int DQ = D / 4, KC = 32;
-    __shared__ float ks[KC][D], vs[KC][D];
-    const int h = blockIdx.y, tid = threadIdx.x;
-    const int i = blockIdx.x * 64 + tid / 4, part = tid % 4;
-    const bool live = i < n_t;
-    const size_t rowoff = (size_t(h) * n_t + (live ? i : 0)) * D + part * DQ;
-    float q[DQ], g[DQ], acc[DQ];
+    constexpr int KB = 32, ROW = D + 1, HD = D / 2, DB = D / 32;
+    __shared__ float ks[KB * ROW];
+    __shared__ float vs[KB * ROW];
+    const int h = blockIdx.y, wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int l32 = lane & 31, half = lane >> 5;
+    const size_t hb = size_t(h) * n_t * D;
+    const int qi = blockIdx.x * 128 + wave * 32 + l32;
+    const bool qlive = qi < n_t;
+    const float c2 = scale * 1.4426950408889634f;
+
+    // B operands: lane -> query column l32, reduction slots d = HD half + m.
+    float qv[HD], gv[HD];
     float dc = 0.f;
 #pragma unroll
-    for (int d = 0; d < DQ; ++d) {
-        q[d] = qm[rowoff + d];
-        g[d] = doc[rowoff + d];
-        dc += g[d] * o_coarse[rowoff + d];
-        acc[d] = 0.f;
+    for (int m = 0; m < HD; ++m) {
+        const size_t at = hb + size_t(qlive ? qi : 0) * D + HD * half + m;
+        qv[m] = qlive ? qm[at] : 0.f;
+        gv[m] = qlive ? doc[at] : 0.f;
+        dc += gv[m] * (qlive ? o_coarse[at] : 0.f);
     }
-    dc += __shfl_xor(dc, 1);
-    dc += __shfl_xor(dc, 2);
-    const float *kh = km + size_t(h) * n_t * D, *vh = vm + size_t(h) * n_t * D;
-    // pass 1: log-sum-exp over all key tiles
-    float mx = -INFINITY, sum = 0.f;
-    for (int j0 = 0; j0 < n_t; j0 += KC) {
+    dc += __shfl_xor(dc, 32);
+
+    auto stage = [&](int j0, bool with_v) {
         __syncthreads();
-        for (int idx = tid; idx < KC * D; idx += 256) {
-            const int r = idx / D, d = idx % D;
-            ks[r][d] = j0 + r < n_t ? kh[size_t(j0 + r) * D + d] : 0.f;
+        for (int idx = threadIdx.x; idx < KB * D; idx += 256) {
+            const int r = idx / D, c = idx % D;
+            const bool live = j0 + r < n_t;
+            ks[r * ROW + c] = live ? km[hb + size_t(j0 + r) * D + c] : 0.f;
+            if (with_v) vs[r * ROW + c] = live ? vm[hb + size_t(j0 + r) * D + c] : 0.f;
         }
         __syncthreads();
-        const int nj = min(KC, n_t - j0);
-        for (int r = 0; r < nj; ++r) {
-            float z = 0.f;
+    };
+    // S^T = K . Q^T: rows = keys 8i + 4 half + j of the block (acc 4i + j), column = query.
+    auto scores = [&](int j0) {
+        f32x16_t S = f32x16_t{};
 #pragma unroll
-            for (int d = 0; d < DQ; ++d) z += q[d] * ks[r][part * DQ + d];
-            z += __shfl_xor(z, 1);
-            z += __shfl_xor(z, 2);
-            z *= scale;
-            if (z > mx) {
-                sum = sum * expf(mx - z) + 1.f;
-                mx = z;
-            } else {
-                sum += expf(z - mx);
+        for (int m = 0; m < HD; ++m)
+            S = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[l32 * ROW + HD * half + m], qv[m], S, 0, 0, 0);
+        if (j0 + KB > n_t) {  // key tiles past the end never score
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (j0 + 8 * i + 4 * half + j >= n_t) S[4 * i + j] = -INFINITY;
+        }
+        return S;
+    };
+
+    // pass 1: lse (log2 domain) over all key tiles
+    float mrun = -INFINITY, lrun = 0.f;
+    for (int j0 = 0; j0 < n_t; j0 += KB) {
+        stage(j0, false);
+        const f32x16_t S = scores(j0);
+        float mx = S[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, S[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(mrun, mx);  // finite: every block has a real key tile
+        float rs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) rs += __builtin_amdgcn_exp2f((S[e] - m_new) * c2);
+        rs += __shfl_xor(rs, 32);
+        lrun = lrun * __builtin_amdgcn_exp2f((mrun - m_new) * c2) + rs;
+        mrun = m_new;
+    }
+    const float lse = mrun * c2 + __log2f(lrun);
+
+    // pass 2: dQm^T += K^T dZ^T; product m pairs keys 8(m/4) + 4 half + m%4,
+    // the S accumulator elements the lane holds.
+    f32x16_t G[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) G[db] = f32x16_t{};
+    for (int j0 = 0; j0 < n_t; j0 += KB) {
+        stage(j0, true);
+        const f32x16_t S = scores(j0);
+        f32x16_t dP = f32x16_t{};
+#pragma unroll
+        for (int m = 0; m < HD; ++m)
+            dP = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[l32 * ROW + HD * half + m], gv[m], dP, 0, 0, 0);
+        float dz[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], c2, -lse));
+            dz[e] = p * (dP[e] - dc) * scale;
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            f32x16_t acc = G[db];
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const int key = 8 * (m / 4) + 4 * half + (m % 4);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[key * ROW + 32 * db + l32], dz[m], acc, 0, 0, 0);
             }
+            G[db] = acc;
         }
     }
-    const float lse = mx + logf(sum);
-    // pass 2: dZ_ij = P_ij (dO_c[i] . vm_j - Dc_i); dqm_i = scale sum_j dZ_ij km_j
-    for (int j0 = 0; j0 < n_t; j0 += KC) {
-        __syncthreads();
-        for (int idx = tid; idx < KC * D; idx += 256) {
-            const int r = idx / D, d = idx % D;
-            const bool in = j0 + r < n_t;
-            ks[r][d] = in ? kh[size_t(j0 + r) * D + d] : 0.f;
-            vs[r][d] = in ? vh[size_t(j0 + r) * D + d] : 0.f;
+    if (!qlive) return;
+    // G[db] element 4i + j <-> d = 32db + 8i + 4 half + j, query column l32.
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 32 * db + 8 * i + 4 * half;
+            *reinterpret_cast<float4 *>(dqm + hb + size_t(qi) * D + d0) =
+                make_float4(G[db][4 * i], G[db][4 * i + 1], G[db][4 * i + 2], G[db][4 * i + 3]);
         }
-        __syncthreads();
-        const int nj = min(KC, n_t - j0);
-        for (int r = 0; r < nj; ++r) {
-            float z = 0.f, dp = 0.f;
-#pragma unroll
-            for (int d = 0; d < DQ; ++d) {
-                z += q[d] * ks[r][part * DQ + d];
-                dp += g[d] * vs[r][part * DQ + d];
-            }
-            z += __shfl_xor(z, 1);
-            z += __shfl_xor(z, 2);
-            dp += __shfl_xor(dp, 1);
-            dp += __shfl_xor(dp, 2);
-            const float p = expf(z * scale - lse);
-            const float dz = p * (dp - dc) * scale;
-#pragma unroll
-            for (int d = 0; d < DQ; ++d) acc[d] += dz * ks[r][part * DQ + d];
-        }
-    }
-    if (!live) return;
-#pragma unroll
-    for (int d = 0; d < DQ; ++d) dqm[rowoff + d] = acc[d];
-    if (part == 0) {
-        lsec[size_t(h) * n_t + i] = lse;
-        dcc[size_t(h) * n_t + i] = dc;
+    if (half == 0) {
+        lsec[size_t(h) * n_t + qi] = lse;
+        dcc[size_t(h) * n_t + qi] = dc;
     }
 }
 
-// Columns: block per (64 key tiles, head); query tiles stream through LDS.
-// dkm_j = scale sum_i dZ_ij qm_i, dvm_j = sum_i P_ij dO_c[i].
+// Columns: lane = key tile j; blocks of 32 query tiles (means of Q and dO_c,
+// their lse and Dc) are staged in LDS. S = Q K^T and dP = dO_c V^T with rows =
+// queries 8i + 4 half + j (acc 4i + j); then dKm^T += Q^T dZ and dVm^T +=
+// dO_c^T P, product m pairing queries 8(m/4) + 4 half + m%4.
 template <int D>
 __global__ __launch_bounds__(256) void coarse_bwd_cols_kernel(const float *__restrict__ qm,
                                                              const float *__restrict__ km,
@@ -270,62 +310,78 @@ __global__ __launch_bounds__(256) void coarse_bwd_cols_kernel(const float *__res
                                                              float scale, float *__restrict__ dkm,
                                                              float *__restrict__ dvm)
 {
-    constexpr int DQ = D / 4, QC = 32;
-    __shared__ float qs[QC][D], gs[QC][D];
-    __shared__ float ls[QC], cs[QC];
-    const int h = blockIdx.y, tid = threadIdx.x;
-    const int j = blockIdx.x * 64 + tid / 4, part = tid % 4;
-    const bool live = j < n_t;
-    const size_t rowoff = (size_t(h) * n_t + (live ? j : 0)) * D + part * DQ;
-    float k[DQ], v[DQ], ak[DQ], av[DQ];
+    constexpr int QB = 32, ROW = D + 1, HD = D / 2, DB = D / 32;
+    __shared__ float qs[QB * ROW];
+    __shared__ float gs[QB * ROW];
+    __shared__ float ls[QB], cs[QB];
+    const int h = blockIdx.y, wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int l32 = lane & 31, half = lane >> 5;
+    const size_t hb = size_t(h) * n_t * D;
+    const int kj = blockIdx.x * 128 + wave * 32 + l32;
+    const bool klive = kj < n_t;
+    const float c2 = scale * 1.4426950408889634f;
+
+    float kv[HD], vv[HD];
 #pragma unroll
-    for (int d = 0; d < DQ; ++d) {
-        k[d] = km[rowoff + d];
-        v[d] = vm[rowoff + d];
-        ak[d] = av[d] = 0.f;
+    for (int m = 0; m < HD; ++m) {
+        const size_t at = hb + size_t(klive ? kj : 0) * D + HD * half + m;
+        kv[m] = klive ? km[at] : 0.f;
+        vv[m] = klive ? vm[at] : 0.f;
     }
-    const float *qh = qm + size_t(h) * n_t * D, *gh = doc + size_t(h) * n_t * D;
-    for (int i0 = 0; i0 < n_t; i0 += QC) {
+    f32x16_t GK[DB], GV[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) GK[db] = GV[db] = f32x16_t{};
+    for (int i0 = 0; i0 < n_t; i0 += QB) {
         __syncthreads();
-        for (int idx = tid; idx < QC * D; idx += 256) {
-            const int r = idx / D, d = idx % D;
-            const bool in = i0 + r < n_t;
-            qs[r][d] = in ? qh[size_t(i0 + r) * D + d] : 0.f;
-            gs[r][d] = in ? gh[size_t(i0 + r) * D + d] : 0.f;
+        for (int idx = threadIdx.x; idx < QB * D; idx += 256) {
+            const int r = idx / D, c = idx % D;
+            const bool live = i0 + r < n_t;
+            qs[r * ROW + c] = live ? qm[hb + size_t(i0 + r) * D + c] : 0.f;
+            gs[r * ROW + c] = live ? doc[hb + size_t(i0 + r) * D + c] : 0.f;
         }
-        if (tid < QC) {
-            const bool in = i0 + tid < n_t;
-            ls[tid] = in ? lsec[size_t(h) * n_t + i0 + tid] : 0.f;
-            cs[tid] = in ? dcc[size_t(h) * n_t + i0 + tid] : 0.f;
+        if (threadIdx.x < QB) {
+            const bool live = i0 + threadIdx.x < n_t;
+            ls[threadIdx.x] = live ? lsec[size_t(h) * n_t + i0 + threadIdx.x] : INFINITY;  // P = 0
+            cs[threadIdx.x] = live ? dcc[size_t(h) * n_t + i0 + threadIdx.x] : 0.f;
         }
         __syncthreads();
-        const int ni = min(QC, n_t - i0);
-        for (int r = 0; r < ni; ++r) {
-            float z = 0.f, dp = 0.f;
+        f32x16_t S = f32x16_t{}, dP = f32x16_t{};
 #pragma unroll
-            for (int d = 0; d < DQ; ++d) {
-                z += qs[r][part * DQ + d] * k[d];
-                dp += gs[r][part * DQ + d] * v[d];
-            }
-            z += __shfl_xor(z, 1);
-            z += __shfl_xor(z, 2);
-            dp += __shfl_xor(dp, 1);
-            dp += __shfl_xor(dp, 2);
-            const float p = expf(z * scale - ls[r]);
-            const float dz = p * (dp - cs[r]) * scale;
+        for (int m = 0; m < HD; ++m) {
+            S = __builtin_amdgcn_mfma_f32_32x32x2f32(qs[l32 * ROW + HD * half + m], kv[m], S, 0, 0, 0);
+            dP = __builtin_amdgcn_mfma_f32_32x32x2f32(gs[l32 * ROW + HD * half + m], vv[m], dP, 0, 0, 0);
+        }
+        float p[16], dz[16];
 #pragma unroll
-            for (int d = 0; d < DQ; ++d) {
-                ak[d] += dz * qs[r][part * DQ + d];
-                av[d] += p * gs[r][part * DQ + d];
+        for (int e = 0; e < 16; ++e) {
+            const int qr = 8 * (e / 4) + 4 * half + (e % 4);
+            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], c2, -ls[qr]));
+            dz[e] = p[e] * (dP[e] - cs[qr]) * scale;
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            f32x16_t ak = GK[db], av = GV[db];
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const int qr = 8 * (m / 4) + 4 * half + (m % 4);
+                ak = __builtin_amdgcn_mfma_f32_32x32x2f32(qs[qr * ROW + 32 * db + l32], dz[m], ak, 0, 0, 0);
+                av = __builtin_amdgcn_mfma_f32_32x32x2f32(gs[qr * ROW + 32 * db + l32], p[m], av, 0, 0, 0);
             }
+            GK[db] = ak;
+            GV[db] = av;
         }
     }
-    if (!live) return;
+    if (!klive) return;
 #pragma unroll
-    for (int d = 0; d < DQ; ++d) {
-        dkm[rowoff + d] = ak[d];
-        dvm[rowoff + d] = av[d];
-    }
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 32 * db + 8 * i + 4 * half;
+            *reinterpret_cast<float4 *>(dkm + hb + size_t(kj) * D + d0) =
+                make_float4(GK[db][4 * i], GK[db][4 * i + 1], GK[db][4 * i + 2], GK[db][4 * i + 3]);
+            *reinterpret_cast<float4 *>(dvm + hb + size_t(kj) * D + d0) =
+                make_float4(GV[db][4 * i], GV[db][4 * i + 1], GV[db][4 * i + 2], GV[db][4 * i + 3]);
+        }
 }
 
 // ----------------------------------------------------------------- tlist --
@@ -1347,7 +1403,7 @@ void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, 
     }
     {
         KernelTimer t(K_BWD_COARSE, st);
-        const dim3 gc((n_t + 63) / 64, H);
+        const dim3 gc((n_t + 127) / 128, H);
         hipLaunchKernelGGL((coarse_bwd_rows_kernel<D>), gc, dim3(256), 0, st, qm, km, vm, o_coarse, doc,
                            n_t, a.scale, reinterpret_cast<float *>(bw + L.lsec),
                            reinterpret_cast<float *>(bw + L.dcc), reinterpret_cast<float *>(bw + L.dqm));
