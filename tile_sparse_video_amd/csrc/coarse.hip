@@ -306,11 +306,15 @@ __global__ __launch_bounds__(256) void coarse_attn_kernel(const float *__restric
 // column, written as ascending ids id_first + j to out[0..k).
 //
 // The row's order-preserving keys stay in registers (PL per lane, read once).
-// The k-th largest key T is found by a 32-step bitwise search: T is built from
-// the top bit down, keeping a bit whenever at least k keys are >= the
-// candidate; each count is a sum of ballot popcounts, so there are no atomics
-// and the result is exact. Then a pass in ascending column order keeps every
-// key > T and the first (k - #keys > T) keys equal to T.
+// The k-th largest key T is found by a bitwise search: T is built from the top
+// bit down, keeping a bit whenever at least k keys are >= the candidate; each
+// count is a per-lane compare-and-add summed across the wave, so there are no
+// atomics and the result is exact. The bits above the highest bit in which
+// the row's largest and smallest keys differ are common to every key, so the
+// search starts below them; and as soon as exactly k keys are >= a candidate,
+// those k keys are the answer and the search stops. Then a pass in ascending
+// column order keeps every key > T and the first (k - #keys > T) keys equal to
+// T (or, after an early stop, every key >= the candidate).
 template <int PL>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ scores, int n_rows,
                                                    int row_len, int col_first, int n_cols, int k,
@@ -345,13 +349,35 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
         for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off);
         return c;
     };
-    uint32_t T = 0;
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t cand = T | (1u << b);
-        if (count_ge(cand) >= k) T = cand;
+    // Largest and smallest real key; their common leading bits are every key's.
+    uint32_t kmax = 0u, kmin = 0xffffffffu;
+#pragma unroll
+    for (int e = 0; e < PL; ++e) {
+        const bool valid = kWave * e + lane < n_cols;
+        kmax = max(kmax, key[e]);
+        kmin = min(kmin, valid ? key[e] : 0xffffffffu);
     }
-    // T is the k-th largest key: count(>= T) >= k > count(>= T + 1).
-    const int n_gt = T == 0xffffffffu ? 0 : count_ge(T + 1);
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), off)));
+        kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), off)));
+    }
+    const uint32_t diff = kmax ^ kmin;
+    const int top = diff == 0u ? -1 : 31 - __builtin_clz(diff);   // highest differing bit
+    uint32_t T = top < 0 ? kmax : kmax & ~((2u << top) - 1u);       // common prefix (2u << 31 wraps to 0)
+    bool exact = false;  // exactly k keys are >= T
+    for (int b = top; b >= 0; --b) {
+        const uint32_t cand = T | (1u << b);
+        const int c = count_ge(cand);
+        if (c >= k) T = cand;
+        if (c == k) {
+            exact = true;
+            break;
+        }
+    }
+    // Without an early stop T is the k-th largest key: count(>= T) >= k >
+    // count(>= T + 1); with one, the k keys >= T are the answer.
+    const int n_gt = exact ? k : (T == 0xffffffffu ? 0 : count_ge(T + 1));
     const int krem = k - n_gt;
     int base = 0, eq_seen = 0;
 #pragma unroll
@@ -359,8 +385,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
         if (kWave * e >= n_cols) break;  // uniform
         const int j = kWave * e + lane;
         const bool valid = j < n_cols;
-        const bool gt = valid && key[e] > T;
-        const bool eq = valid && key[e] == T;
+        const bool gt = valid && (exact ? key[e] >= T : key[e] > T);
+        const bool eq = valid && !exact && key[e] == T;
         const uint64_t eq_mask = __ballot(eq);
         const int eq_before = __popcll(eq_mask & lanes_below(lane));
         const bool sel = gt || (eq && eq_seen + eq_before < krem);
