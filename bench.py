@@ -61,6 +61,26 @@ def effective_fine_flops(plan, keep_idx: np.ndarray, heads: int, head_dim: int,
     return 4.0 * head_dim * float(pairs)
 
 
+def hbm_passes(wl, plan, kernels, k, k_ref=None):
+    """Achieved HBM bandwidth of the memory-bound coarse passes from their algorithmic bytes:
+    gather_pool reads Q, K, V once and writes the tile-ordered K, V and the three tile-mean
+    arrays; top-k reads the coarse score rows and writes the keep lists."""
+    H, D, S = wl.heads, wl.head_dim, wl.tokens
+    S_pad, n_t, n_v, P = plan.S_pad, plan.n_t, plan.n_v, plan.P
+    gather = 3 * S * H * D * 2 + 2 * S_pad * H * D * 2 + 3 * H * n_t * D * 4
+    if k_ref is None:
+        topk = H * n_v * n_v * 4 + H * n_v * k * 4
+    else:
+        topk = H * n_t * n_t * 4 + H * n_t * (k + k_ref) * 4
+    out = {}
+    for name, nbytes in (("gather_pool", gather), ("topk", topk)):
+        if name in kernels:
+            gbs = nbytes / (kernels[name]["avg_ms"] * 1e-3) / 1e9
+            out[name] = {"algorithmic_bytes": int(nbytes), "gb_s": round(gbs, 1),
+                         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops, k_ref=None, int8=False):
     """The oracle, as it stands, on a bounded sample of this layer, scaled to one layer.
     k_ref is not None in the reference-sparsity mode; int8 times the INT8 fine pass."""
@@ -88,7 +108,8 @@ def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops, k_ref=None, int8=False
             return oracle.fine_tokens_i8(Qb, Kb, Vb, 0, pl, csr, scale, toks)
     t_head = time.perf_counter() - t0
     rng = np.random.default_rng(0)
-    vid = rng.choice(np.arange(pl.S)[pl.untile // pl.B >= pl.P], size=2048, replace=False)
+    vid_all = np.arange(pl.S)[pl.untile // pl.B >= pl.P]
+    vid = rng.choice(vid_all, size=min(2048, vid_all.size), replace=False)
     pre = rng.choice(np.arange(pl.S)[pl.untile // pl.B < pl.P], size=min(256, wl.prefix_tokens),
                      replace=False) if wl.prefix_tokens else np.zeros(0, np.int64)
     t0 = time.perf_counter()
@@ -99,7 +120,7 @@ def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops, k_ref=None, int8=False
         t0 = time.perf_counter()
         fine(pre)
         t_pre = (time.perf_counter() - t0) / len(pre)
-    gt = rng.choice(pl.S, size=512, replace=False)
+    gt = rng.choice(pl.S, size=min(512, pl.S), replace=False)
     t0 = time.perf_counter()
     oracle.gate_proj(xb, wb, gt)
     t_gate = (time.perf_counter() - t0) / len(gt)
@@ -245,7 +266,7 @@ def cpu_baseline_backward(wl, host_inputs, att, dout, g, flops):
         csr = oracle.key_lists_default(pl, hr.keep)
     g_bits = workloads.bf16_bits(g.cpu())
     d_bits = workloads.bf16_bits(dout.cpu())
-    toks = np.random.default_rng(0).choice(pl.S, size=512, replace=False)
+    toks = np.random.default_rng(0).choice(pl.S, size=min(512, pl.S), replace=False)
     t0 = time.perf_counter()
     oracle.dq_tokens(Qb, Kb, Vb, g_bits, d_bits, 0, pl, csr, scale, toks,
                      means=(hr.qm, hr.km, hr.vm))
@@ -398,6 +419,7 @@ def main() -> int:
         "ms_per_layer_attention_only": round(coarse_ms + fine_ms, 4),
         "tile_pair_fraction": round(frac_pairs, 4),
         "effective_fine_tflop": round(fine_flops / 1e12, 3),
+        "hbm_passes": hbm_passes(wl, att.plan, kernels, att.k, att.k_ref if att.ref else None),
         "wall_s": round(wall, 3),
         "roofline": {
             "kernel": ("fine_attn_kernel, INT8 scores (vsa_sparse_attn_fwd_i8; peak mixes the "
