@@ -1,0 +1,82 @@
+"""GPU parity of the per-row top-k on long score rows (the multi-wave register
+path up to 16,384 columns, and the radix select beyond), with and without
+massive ties. Keep-sets and the scores they come from are compared bit for bit
+with the oracle on sampled rows.
+
+Selection rule (SnackOnAI analysis of ComfyUI-Ref2VA-VSA, "The Code, Annotated",
+snippet two and "References": the k key tiles of largest coarse score per video
+query tile; ties go to the lower tile index, ids ascending)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import parity
+from tests.conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a gfx950 GPU")]
+
+# (grid, keep_k): n_v = 2,080 / 3,500 / 5,544 / 6,300 / 8,464 video tiles of 4x4x4
+# take the multi-wave kernel with 2 / 3 / 4 / 5 / 6 waves of 24 keys per lane;
+# 16,900 is past it (radix select). keep_k spans 1, n_v - 1 and 1-25 %.
+CASES = {
+    "w2": ((4, 160, 208), 520),
+    "w3": ((4, 200, 280), 35),
+    "w4": ((4, 264, 336), 277),
+    "w5": ((4, 280, 360), 6299),
+    "w6": ((4, 368, 368), 1),
+    "radix": ((4, 520, 520), 845),
+}
+
+
+def _u32(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def _tie_keys(inp, pl, classes: int):
+    """K with every video tile a copy of one of `classes` tiles (by tile id mod
+    classes), so every score row holds only `classes` distinct values."""
+    K = inp.k.clone()
+    B = pl.B
+    base = [pl.row_src[(pl.P + c) * B:(pl.P + c + 1) * B] for c in range(classes)]
+    for t in range(pl.P + classes, pl.n_t):
+        rows = pl.row_src[t * B:(t + 1) * B]
+        src = base[(t - pl.P) % classes]
+        K[torch.from_numpy(rows.astype(np.int64))] = K[torch.from_numpy(src.astype(np.int64))]
+    return K
+
+
+@pytest.mark.parametrize("ties", [False, True])
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_topk_long_rows(name, ties):
+    import tile_sparse_video_amd as tsv
+    grid, keep_k = CASES[name]
+    wl = workloads.custom(f"topk_{name}", seed=31, heads=1, head_dim=64, hidden=64,
+                          prefix_segments=(70,), grid=grid, tile=(4, 4, 4), keep_k=keep_k)
+    print(f"[gpu] top-k rows {name} ties={ties}: inputs", flush=True)
+    inp = parity.make_inputs(wl)
+    pl = parity.oracle_plan(wl)
+    assert all(g % 4 == 0 for g in grid)  # full video tiles, so tied tiles have identical means
+    if ties:
+        inp.k = _tie_keys(inp, pl, 7)
+    att = tsv.TileSparseAttention(wl.prefix_segments, wl.grid, wl.tile, wl.heads, wl.head_dim,
+                                  keep_k=keep_k, device="cuda")
+    assert att.k == keep_k
+    print(f"[gpu] top-k rows {name} ties={ties}: n_v={pl.n_v}, k={keep_k}", flush=True)
+    att.coarse(inp.q.cuda(), inp.k.cuda(), inp.v.cuda())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, pl.n_v - 1], rng.choice(pl.n_v, 30, replace=False)]))
+    rows = rows.astype(np.int32)
+    qm = oracle.tile_means(inp.qb, 0, pl)
+    km = oracle.tile_means(inp.kb, 0, pl)
+    sc = oracle.video_scores(qm, km, pl.P, pl.n_v, rows)
+    keep_or = oracle.topk_rows(sc, keep_k, pl.P)
+    got_sc = att.workspace_view("scores", torch.float32, (1, pl.n_v, pl.n_v))[0].cpu().numpy()[rows]
+    assert np.array_equal(_u32(got_sc), _u32(sc))
+    if ties:
+        assert len(np.unique(sc[0])) <= 7 + 1
+    keep = att.keep_idx[0].cpu().numpy()[rows]
+    assert np.array_equal(keep, keep_or)

@@ -7,9 +7,10 @@
 //   coarse_attn  -- tile-level softmax attention over the pooled Q, K, V (fp32
 //                   matrix cores);
 //   topk         -- per score row and column group, top-k: a bitwise search for
-//                   the k-th largest key over register-resident keys (rows up to
-//                   2048), an 8-bit radix select beyond; lowest index first on
-//                   ties, ascending output (one wavefront per row).
+//                   the k-th largest key over register-resident keys (a wave
+//                   per row up to 2,048 columns, a workgroup up to 16,384), an
+//                   8-bit radix select beyond; lowest index first on ties,
+//                   ascending output.
 //
 // Method: SnackOnAI analysis of ComfyUI-Ref2VA-VSA ("The Code, Annotated",
 // snippet two: block_len masks padding; "References": coarse tile selection
@@ -301,20 +302,119 @@ __global__ __launch_bounds__(256) void coarse_attn_kernel(const float *__restric
 
 // ------------------------------------------------------------------- top-k --
 //
-// One wavefront per score row: the k largest of n_cols scores (columns
-// col_first .. col_first + n_cols of the row), equal scores keeping the lower
-// column, written as ascending ids id_first + j to out[0..k).
+// Per score row: the k largest of n_cols scores (columns col_first ..
+// col_first + n_cols of the row), equal scores keeping the lower column,
+// written as ascending ids id_first + j to out[0..k).
 //
-// The row's order-preserving keys stay in registers (PL per lane, read once).
-// The k-th largest key T is found by a bitwise search: T is built from the top
-// bit down, keeping a bit whenever at least k keys are >= the candidate; each
-// count is a per-lane compare-and-add summed across the wave, so there are no
-// atomics and the result is exact. The bits above the highest bit in which
-// the row's largest and smallest keys differ are common to every key, so the
-// search starts below them; and as soon as exactly k keys are >= a candidate,
-// those k keys are the answer and the search stops. Then a pass in ascending
-// column order keeps every key > T and the first (k - #keys > T) keys equal to
-// T (or, after an early stop, every key >= the candidate).
+// The row's order-preserving keys stay in registers (PL per lane, read once;
+// rows of up to 2,048 columns take one wave, longer ones a workgroup of up to
+// eight waves, each holding a contiguous slice of the row). The k-th largest
+// key T is found by a bitwise search: T is built from the top bit down,
+// keeping a bit whenever at least k keys are >= the candidate. A count is one
+// compare per register into a lane mask, the masks' population counts summed
+// on the scalar unit (wave-uniform, no atomics, exact), plus, for a
+// multi-wave row, a sum of the waves' counts through LDS. The bits above the
+// highest bit in which the row's largest and smallest keys differ are common
+// to every key, so the search starts below them; and as soon as exactly k
+// keys are >= a candidate, those k keys are the answer and the search stops.
+// Then a pass in ascending column order keeps every key > T and the first
+// (k - #keys > T) keys equal to T (after an early stop: every key >= T).
+
+// Loads the keys of columns c0 + 64 e + lane. Every load is issued
+// unconditionally (a clamped column for slots past the row), so all of them
+// are in flight at once; a guarded load would become a branch with its own
+// wait. Slots past the row hold key 0, which no count sees: every threshold
+// searched is >= 1, and finite scores have keys >= 1.
+template <int PL>
+__device__ __forceinline__ void topk_load(const float *s, int c0, int n_cols, int lane,
+                                          uint32_t (&key)[PL])
+{
+#pragma unroll
+    for (int e = 0; e < PL; ++e) {
+        const int j = c0 + kWave * e + lane;
+        const uint32_t kv = score_key(s[min(j, n_cols - 1)]);
+        key[e] = j < n_cols ? kv : 0u;
+    }
+}
+
+// Number of this wave's keys >= t (wave-uniform).
+template <int PL>
+__device__ __forceinline__ int topk_count_ge(const uint32_t (&key)[PL], uint32_t t)
+{
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < PL; ++e) c += __popcll(__ballot(key[e] >= t));
+    return c;
+}
+
+// This wave's largest and smallest real key (wave-uniform).
+template <int PL>
+__device__ __forceinline__ void topk_range(const uint32_t (&key)[PL], int c0, int n_cols, int lane,
+                                           uint32_t &kmax, uint32_t &kmin)
+{
+    kmax = 0u;
+    kmin = 0xffffffffu;
+#pragma unroll
+    for (int e = 0; e < PL; ++e) {
+        const bool valid = c0 + kWave * e + lane < n_cols;
+        kmax = max(kmax, key[e]);
+        kmin = min(kmin, valid ? key[e] : 0xffffffffu);
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), off)));
+        kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), off)));
+    }
+}
+
+// The common prefix of kmax and kmin and the bit the search starts at.
+__device__ __forceinline__ void topk_start(uint32_t kmax, uint32_t kmin, uint32_t &T, int &top)
+{
+    const uint32_t diff = kmax ^ kmin;
+    top = diff == 0u ? -1 : 31 - __builtin_clz(diff);   // highest differing bit
+    T = top < 0 ? kmax : kmax & ~((2u << top) - 1u);     // common prefix (2u << 31 wraps to 0)
+}
+
+// Writes this wave's selected columns in ascending order from position base.
+// exact: every key >= T is selected. Otherwise every key > T, and of the keys
+// equal to T the first krem of the row, eq_seen of which lie before this wave.
+template <int PL>
+__device__ __forceinline__ void topk_select(const uint32_t (&key)[PL], int c0, int n_cols, int lane,
+                                            uint32_t T, bool exact, int krem, int base, int eq_seen,
+                                            int k, int id_first, int32_t *out)
+{
+    if (exact) {
+#pragma unroll
+        for (int e = 0; e < PL; ++e) {
+            if (c0 + kWave * e >= n_cols) break;  // uniform
+            const int j = c0 + kWave * e + lane;
+            const bool sel = j < n_cols && key[e] >= T;
+            const uint64_t sel_mask = __ballot(sel);
+            const int pos = base + __popcll(sel_mask & lanes_below(lane));
+            if (sel && pos < k) out[pos] = id_first + j;  // exactly k are selected; the bound is a guard
+            base += __popcll(sel_mask);
+        }
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < PL; ++e) {
+        if (c0 + kWave * e >= n_cols) break;  // uniform
+        const int j = c0 + kWave * e + lane;
+        const bool valid = j < n_cols;
+        const bool gt = valid && key[e] > T;
+        const bool eq = valid && key[e] == T;
+        const uint64_t eq_mask = __ballot(eq);
+        const int eq_before = __popcll(eq_mask & lanes_below(lane));
+        const bool sel = gt || (eq && eq_seen + eq_before < krem);
+        const uint64_t sel_mask = __ballot(sel);
+        const int pos = base + __popcll(sel_mask & lanes_below(lane));
+        if (sel && pos < k) out[pos] = id_first + j;  // exactly k are selected; the bound is a guard
+        base += __popcll(sel_mask);
+        eq_seen += __popcll(eq_mask);
+    }
+}
+
+// Rows of up to 64 PL columns: one wavefront per row, four rows per workgroup.
 template <int PL>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ scores, int n_rows,
                                                    int row_len, int col_first, int n_cols, int k,
@@ -332,43 +432,15 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
     }
     if (k == 0) return;
     uint32_t key[PL];
-#pragma unroll
-    for (int e = 0; e < PL; ++e) {
-        const int j = kWave * e + lane;
-        key[e] = j < n_cols ? score_key(s[j]) : 0u;
-    }
-    // Padding slots (j >= n_cols) hold key 0, which no count sees: every
-    // threshold searched below is >= 1, and finite scores have keys >= 1.
-    // A count is a per-lane compare-and-add over the registers, summed
-    // across the wave by a butterfly.
-    auto count_ge = [&](uint32_t t) -> int {
-        int c = 0;
-#pragma unroll
-        for (int e = 0; e < PL; ++e) c += key[e] >= t ? 1 : 0;
-#pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off);
-        return c;
-    };
-    // Largest and smallest real key; their common leading bits are every key's.
-    uint32_t kmax = 0u, kmin = 0xffffffffu;
-#pragma unroll
-    for (int e = 0; e < PL; ++e) {
-        const bool valid = kWave * e + lane < n_cols;
-        kmax = max(kmax, key[e]);
-        kmin = min(kmin, valid ? key[e] : 0xffffffffu);
-    }
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-        kmax = max(kmax, uint32_t(__shfl_xor(int(kmax), off)));
-        kmin = min(kmin, uint32_t(__shfl_xor(int(kmin), off)));
-    }
-    const uint32_t diff = kmax ^ kmin;
-    const int top = diff == 0u ? -1 : 31 - __builtin_clz(diff);   // highest differing bit
-    uint32_t T = top < 0 ? kmax : kmax & ~((2u << top) - 1u);       // common prefix (2u << 31 wraps to 0)
+    topk_load<PL>(s, 0, n_cols, lane, key);
+    uint32_t kmax, kmin, T;
+    int top;
+    topk_range<PL>(key, 0, n_cols, lane, kmax, kmin);
+    topk_start(kmax, kmin, T, top);
     bool exact = false;  // exactly k keys are >= T
     for (int b = top; b >= 0; --b) {
         const uint32_t cand = T | (1u << b);
-        const int c = count_ge(cand);
+        const int c = topk_count_ge<PL>(key, cand);
         if (c >= k) T = cand;
         if (c == k) {
             exact = true;
@@ -377,29 +449,97 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
     }
     // Without an early stop T is the k-th largest key: count(>= T) >= k >
     // count(>= T + 1); with one, the k keys >= T are the answer.
-    const int n_gt = exact ? k : (T == 0xffffffffu ? 0 : count_ge(T + 1));
-    const int krem = k - n_gt;
-    int base = 0, eq_seen = 0;
-#pragma unroll
-    for (int e = 0; e < PL; ++e) {
-        if (kWave * e >= n_cols) break;  // uniform
-        const int j = kWave * e + lane;
-        const bool valid = j < n_cols;
-        const bool gt = valid && (exact ? key[e] >= T : key[e] > T);
-        const bool eq = valid && !exact && key[e] == T;
-        const uint64_t eq_mask = __ballot(eq);
-        const int eq_before = __popcll(eq_mask & lanes_below(lane));
-        const bool sel = gt || (eq && eq_seen + eq_before < krem);
-        const uint64_t sel_mask = __ballot(sel);
-        const int pos = base + __popcll(sel_mask & lanes_below(lane));
-        if (sel && pos < k) out[pos] = id_first + j;  // exactly k are selected; the bound is a guard
-        base += __popcll(sel_mask);
-        eq_seen += __popcll(eq_mask);
-    }
+    const int n_gt = exact ? k : (T == 0xffffffffu ? 0 : topk_count_ge<PL>(key, T + 1));
+    topk_select<PL>(key, 0, n_cols, lane, T, exact, k - n_gt, 0, 0, k, id_first, out);
 }
 
-// Long rows: a four-pass 8-bit radix select over LDS histograms, re-reading
-// the row (from L2) in each pass, then the same ordered compaction.
+constexpr int kTopkMaxWaves = 8;
+
+// Rows of up to 64 PL W columns: one workgroup of W = blockDim.x / 64 waves per
+// row, wave w holding columns [64 PL w, 64 PL (w + 1)). Counts are summed
+// across the waves through LDS, one barrier per search step (two buffers
+// alternate, so a buffer is rewritten only after every wave has passed the
+// barrier that follows its reads). Every branch taken on a count is uniform
+// over the workgroup.
+template <int PL>
+__global__ __launch_bounds__(kWave * kTopkMaxWaves) void topk_wide_kernel(
+    const float *__restrict__ scores, int n_rows, int row_len, int col_first, int n_cols, int k,
+    int id_first, int32_t *__restrict__ keep, int keep_stride, int keep_first)
+{
+    __shared__ int xs[2][kTopkMaxWaves];
+    __shared__ uint32_t xmax[kTopkMaxWaves], xmin[kTopkMaxWaves];
+    const int W = blockDim.x / kWave;
+    const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int row = blockIdx.x;
+    const float *s = scores + size_t(row) * row_len + col_first;
+    int32_t *out = keep + size_t(row) * keep_stride + keep_first;
+    if (k == n_cols) {
+        for (int j = threadIdx.x; j < n_cols; j += blockDim.x) out[j] = id_first + j;
+        return;
+    }
+    if (k == 0) return;
+    const int c0 = w * PL * kWave;
+    uint32_t key[PL];
+    topk_load<PL>(s, c0, n_cols, lane, key);
+    uint32_t kmax, kmin, T;
+    int top;
+    topk_range<PL>(key, c0, n_cols, lane, kmax, kmin);
+    if (lane == 0) {
+        xmax[w] = kmax;
+        xmin[w] = kmin;
+    }
+    __syncthreads();
+    for (int i = 0; i < W; ++i) {
+        kmax = max(kmax, xmax[i]);
+        kmin = min(kmin, xmin[i]);
+    }
+    topk_start(kmax, kmin, T, top);
+    // Publishes this wave's value v and returns the values' sum over the
+    // waves before this one (before) and over all waves.
+    int par = 0;
+    auto exchange = [&](int v, int &before) -> int {
+        if (lane == 0) xs[par][w] = v;
+        __syncthreads();
+        int all = 0;
+        before = 0;
+        for (int i = 0; i < W; ++i) {
+            const int x = xs[par][i];
+            before += i < w ? x : 0;
+            all += x;
+        }
+        par ^= 1;
+        return all;
+    };
+    int before;
+    bool exact = false;
+    for (int b = top; b >= 0; --b) {
+        const uint32_t cand = T | (1u << b);
+        const int c = exchange(topk_count_ge<PL>(key, cand), before);
+        if (c >= k) T = cand;
+        if (c == k) {
+            exact = true;
+            break;
+        }
+    }
+    if (exact) {
+        exchange(topk_count_ge<PL>(key, T), before);
+        topk_select<PL>(key, c0, n_cols, lane, T, true, 0, before, 0, k, id_first, out);
+        return;
+    }
+    // gt and eq counts packed in one word (each below 2^16: n_cols <= 16,384).
+    const int gt = T == 0xffffffffu ? 0 : topk_count_ge<PL>(key, T + 1);
+    const int ge = topk_count_ge<PL>(key, T);
+    const int all = exchange(gt | ((ge - gt) << 16), before);
+    const int krem = k - (all & 0xffff);
+    const int gt_before = before & 0xffff, eq_before = before >> 16;
+    topk_select<PL>(key, c0, n_cols, lane, T, false, krem, gt_before + min(eq_before, krem),
+                    eq_before, k, id_first, out);
+}
+
+// Rows beyond 16,384 columns: a four-pass 8-bit radix select over LDS
+// histograms, re-reading the row (from L2) in each pass in batches of
+// kRadixBatch loads per lane, then the same ordered compaction.
+constexpr int kRadixBatch = 8;
 __global__ __launch_bounds__(256) void topk_radix_kernel(const float *__restrict__ scores,
                                                          int n_rows, int row_len, int col_first,
                                                          int n_cols, int k, int id_first,
@@ -424,9 +564,15 @@ __global__ __launch_bounds__(256) void topk_radix_kernel(const float *__restrict
         for (int b = 0; b < 4; ++b) hist[w][4 * lane + b] = 0;
         __syncthreads();
         if (live)
-            for (int j = lane; j < n_cols; j += kWave) {
-                const uint32_t key = score_key(s[j]);
-                if ((key & mask) == prefix) atomicAdd(&hist[w][(key >> shift) & 255u], 1u);
+            for (int j0 = 0; j0 < n_cols; j0 += kRadixBatch * kWave) {
+                uint32_t kb[kRadixBatch];
+#pragma unroll
+                for (int u = 0; u < kRadixBatch; ++u)
+                    kb[u] = score_key(s[min(j0 + kWave * u + lane, n_cols - 1)]);
+#pragma unroll
+                for (int u = 0; u < kRadixBatch; ++u)
+                    if (j0 + kWave * u + lane < n_cols && (kb[u] & mask) == prefix)
+                        atomicAdd(&hist[w][(kb[u] >> shift) & 255u], 1u);
             }
         __syncthreads();
         // Lane L owns digits 255-4L .. 252-4L (descending); an inclusive scan over
@@ -469,43 +615,57 @@ __global__ __launch_bounds__(256) void topk_radix_kernel(const float *__restrict
     if (!live || k == 0) return;
     // prefix is the k-th largest key; keep krem of the keys equal to it.
     int base = 0, eq_seen = 0;
-    for (int j0 = 0; j0 < n_cols; j0 += kWave) {
-        const int j = j0 + lane;
-        const bool valid = j < n_cols;
-        const uint32_t key = valid ? score_key(s[j]) : 0u;
-        const bool gt = valid && key > prefix;
-        const bool eq = valid && key == prefix;
-        const uint64_t eq_mask = __ballot(eq);
-        const int eq_before = __popcll(eq_mask & lanes_below(lane));
-        const bool sel = gt || (eq && eq_seen + eq_before < krem);
-        const uint64_t sel_mask = __ballot(sel);
-        const int pos = base + __popcll(sel_mask & lanes_below(lane));
-        if (sel && pos < k) out[pos] = id_first + j;  // exactly k are selected; the bound is a guard
-        base += __popcll(sel_mask);
-        eq_seen += __popcll(eq_mask);
+    for (int j0 = 0; j0 < n_cols; j0 += kRadixBatch * kWave) {
+        uint32_t kb[kRadixBatch];
+#pragma unroll
+        for (int u = 0; u < kRadixBatch; ++u)
+            kb[u] = score_key(s[min(j0 + kWave * u + lane, n_cols - 1)]);
+#pragma unroll
+        for (int u = 0; u < kRadixBatch; ++u) {
+            const int j = j0 + kWave * u + lane;
+            const bool valid = j < n_cols;
+            const bool gt = valid && kb[u] > prefix;
+            const bool eq = valid && kb[u] == prefix;
+            const uint64_t eq_mask = __ballot(eq);
+            const int eq_before = __popcll(eq_mask & lanes_below(lane));
+            const bool sel = gt || (eq && eq_seen + eq_before < krem);
+            const uint64_t sel_mask = __ballot(sel);
+            const int pos = base + __popcll(sel_mask & lanes_below(lane));
+            if (sel && pos < k) out[pos] = id_first + j;  // exactly k are selected; the bound is a guard
+            base += __popcll(sel_mask);
+            eq_seen += __popcll(eq_mask);
+        }
     }
 }
 
-// Top-k of one column group for n_rows rows (one wave per row).
+// Top-k of one column group for n_rows rows.
 void launch_topk(const float *scores, int n_rows, int row_len, int col_first, int n_cols, int k,
                  int id_first, int32_t *keep, int keep_stride, int keep_first, hipStream_t st)
 {
     if (n_rows == 0 || n_cols == 0) return;
-    const dim3 grid((n_rows + 3) / 4), block(256);
     KernelTimer t(K_TOPK, st);
 #define VSA_TOPK(PLV)                                                                              \
-    hipLaunchKernelGGL(topk_kernel<PLV>, grid, block, 0, st, scores, n_rows, row_len, col_first,    \
-                       n_cols, k, id_first, keep, keep_stride, keep_first)
+    hipLaunchKernelGGL(topk_kernel<PLV>, dim3((n_rows + 3) / 4), dim3(256), 0, st, scores, n_rows, \
+                       row_len, col_first, n_cols, k, id_first, keep, keep_stride, keep_first)
+#define VSA_TOPK_WIDE(PLV)                                                                         \
+    hipLaunchKernelGGL(topk_wide_kernel<PLV>, dim3(n_rows),                                        \
+                       dim3(kWave * ((n_cols + kWave * (PLV)-1) / (kWave * (PLV)))), 0, st, scores, \
+                       n_rows, row_len, col_first, n_cols, k, id_first, keep, keep_stride,         \
+                       keep_first)
     if (n_cols <= 4 * kWave) VSA_TOPK(4);
     else if (n_cols <= 8 * kWave) VSA_TOPK(8);
     else if (n_cols <= 12 * kWave) VSA_TOPK(12);
     else if (n_cols <= 16 * kWave) VSA_TOPK(16);
     else if (n_cols <= 24 * kWave) VSA_TOPK(24);
     else if (n_cols <= 32 * kWave) VSA_TOPK(32);
+    else if (n_cols <= 24 * kWave * kTopkMaxWaves) VSA_TOPK_WIDE(24);
+    else if (n_cols <= 32 * kWave * kTopkMaxWaves) VSA_TOPK_WIDE(32);
     else
-        hipLaunchKernelGGL(topk_radix_kernel, grid, block, 0, st, scores, n_rows, row_len, col_first,
-                           n_cols, k, id_first, keep, keep_stride, keep_first);
+        hipLaunchKernelGGL(topk_radix_kernel, dim3((n_rows + 3) / 4), dim3(256), 0, st, scores,
+                           n_rows, row_len, col_first, n_cols, k, id_first, keep, keep_stride,
+                           keep_first);
 #undef VSA_TOPK
+#undef VSA_TOPK_WIDE
 }
 
 template <int D, int B>
