@@ -124,19 +124,44 @@ __device__ __forceinline__ float xhalf_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// out[t][h][d0..d0+3] = bf16(o * inv + g * oc) for four consecutive d.
-__device__ __forceinline__ void store4(uint16_t *out, const uint16_t *gate, size_t base, int d0,
-                                       float4 oc, float o0, float o1, float o2, float o3, float inv)
+// Gated epilogue of the query row that this lane holds in column qb of O^T
+// (element 4i + j of O[db][qb] <-> d = 32db + 8i + 4half + j):
+// out[base + d] = bf16(O[d] * inv + g[base + d] * oc[d]). Every gate and
+// O_coarse load is issued before the first store (the compiler cannot move a
+// load across a store to memory it cannot prove distinct), so the row's loads
+// are in flight together.
+template <int DB, typename OArr>
+__device__ __forceinline__ void gated_row(uint16_t *out, const uint16_t *gate, size_t base,
+                                          const float *oc, const OArr &O, int qb, float inv, int half)
 {
-    const uint2 graw = *reinterpret_cast<const uint2 *>(gate + base + d0);
-    const float g0 = __uint_as_float(graw.x << 16), g1 = __uint_as_float(graw.x & 0xffff0000u);
-    const float g2 = __uint_as_float(graw.y << 16), g3 = __uint_as_float(graw.y & 0xffff0000u);
-    const bf16x2_t w0 = {(__bf16)(o0 * inv + g0 * oc.x), (__bf16)(o1 * inv + g1 * oc.y)};
-    const bf16x2_t w1 = {(__bf16)(o2 * inv + g2 * oc.z), (__bf16)(o3 * inv + g3 * oc.w)};
-    uint2 w;
-    w.x = __builtin_bit_cast(uint32_t, w0);
-    w.y = __builtin_bit_cast(uint32_t, w1);
-    *reinterpret_cast<uint2 *>(out + base + d0) = w;
+    uint2 graw[DB][4];
+    float4 ocv[DB][4];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 32 * db + 8 * i + 4 * half;
+            graw[db][i] = *reinterpret_cast<const uint2 *>(gate + base + d0);
+            ocv[db][i] = *reinterpret_cast<const float4 *>(oc + d0);
+        }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 32 * db + 8 * i + 4 * half;
+            const uint2 g = graw[db][i];
+            const float4 c = ocv[db][i];
+            const float o0 = O[db][qb][4 * i], o1 = O[db][qb][4 * i + 1];
+            const float o2 = O[db][qb][4 * i + 2], o3 = O[db][qb][4 * i + 3];
+            const bf16x2_t w0 = {(__bf16)(o0 * inv + __uint_as_float(g.x << 16) * c.x),
+                                 (__bf16)(o1 * inv + __uint_as_float(g.x & 0xffff0000u) * c.y)};
+            const bf16x2_t w1 = {(__bf16)(o2 * inv + __uint_as_float(g.y << 16) * c.z),
+                                 (__bf16)(o3 * inv + __uint_as_float(g.y & 0xffff0000u) * c.w)};
+            uint2 w;
+            w.x = __builtin_bit_cast(uint32_t, w0);
+            w.y = __builtin_bit_cast(uint32_t, w1);
+            *reinterpret_cast<uint2 *>(out + base + d0) = w;
+        }
 }
 
 template <int D, int B, bool SPLIT, bool I8 = false>
@@ -495,15 +520,7 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
     for (int qb = 0; qb < 2; ++qb) {
         if (tok[qb] < 0) continue;
         const float inv = 1.0f / l[qb];
-        const size_t base = (size_t(tok[qb]) * a.ld + h) * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d0 = 32 * db + 8 * i + 4 * half;
-                store4(a.out, a.gate, base, d0, *reinterpret_cast<const float4 *>(oc + d0),
-                       O[db][qb][4 * i], O[db][qb][4 * i + 1], O[db][qb][4 * i + 2], O[db][qb][4 * i + 3], inv);
-            }
+        gated_row<DB>(a.out, a.gate, (size_t(tok[qb]) * a.ld + h) * D, oc, O, qb, inv, half);
     }
 }
 
@@ -529,11 +546,25 @@ __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
     const float c2 = a.scale_log2e;
     const int C = a.chunks;
     const size_t p0 = size_t(item) * C;
-
-    float M[2] = {-INFINITY, -INFINITY};
-    for (int c = 0; c < C; ++c)
+    int tok[2];  // the rows' tokens (-1: padding), read up front
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) M[qb] = fmaxf(M[qb], a.part_ml[(p0 + c) * 128 + qb * 32 + l32]);
+    for (int qb = 0; qb < 2; ++qb) tok[qb] = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
+
+    // The chunks' maxima, read eight chunks at a time (a clamped chunk index
+    // repeats a value, which leaves the max unchanged).
+    float M[2] = {-INFINITY, -INFINITY};
+    for (int c0 = 0; c0 < C; c0 += 8) {
+        float mv[8][2];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+                mv[u][qb] = a.part_ml[(p0 + min(c0 + u, C - 1)) * 128 + qb * 32 + l32];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) M[qb] = fmaxf(M[qb], mv[u][qb]);
+    }
     float L[2] = {0.f, 0.f};
     float O[DB][2][16];
 #pragma unroll
@@ -549,8 +580,8 @@ __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
         float w[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            const float mc = pml[qb * 32 + l32];
-            w[qb] = mc == -INFINITY ? 0.f : pml[64 + qb * 32 + l32] * __builtin_amdgcn_exp2f((mc - M[qb]) * c2);
+            const float mc = pml[qb * 32 + l32], lc = pml[64 + qb * 32 + l32];  // both loads unconditional
+            w[qb] = mc == -INFINITY ? 0.f : lc * __builtin_amdgcn_exp2f((mc - M[qb]) * c2);
             L[qb] += w[qb];
         }
         const uint16_t *po = a.part_o + (p0 + c) * (64 * D);
@@ -576,7 +607,7 @@ __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int row = tile * B + 64 * qsub + 32 * qb + l32;
-            const bool real = a.row_src[row] >= 0;
+            const bool real = tok[qb] >= 0;
             const float inv = real ? 1.0f / L[qb] : 0.f;
             float *orow = a.ofine_out + (size_t(h) * S_pad + row) * D;
 #pragma unroll
@@ -595,10 +626,9 @@ __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int row = tile * B + 64 * qsub + 32 * qb + l32;
-            const int tok = a.row_src[row];
             float part = 0.f;
-            if (tok >= 0) {
-                const uint16_t *go = a.dout + (size_t(tok) * a.ld + h) * D;
+            if (tok[qb] >= 0) {
+                const uint16_t *go = a.dout + (size_t(tok[qb]) * a.ld + h) * D;
                 const float inv = 1.0f / L[qb];
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
@@ -613,8 +643,8 @@ __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
             }
             part = xhalf_sum(part);  // both halves hold the full sum
             if (half == 0) {
-                a.lse_out[size_t(h) * S_pad + row] = tok < 0 ? INFINITY : M[qb] * c2 + __log2f(L[qb]);
-                a.dt_out[size_t(h) * S_pad + row] = tok < 0 ? 0.f : part;
+                a.lse_out[size_t(h) * S_pad + row] = tok[qb] < 0 ? INFINITY : M[qb] * c2 + __log2f(L[qb]);
+                a.dt_out[size_t(h) * S_pad + row] = tok[qb] < 0 ? 0.f : part;
             }
         }
         return;
@@ -622,18 +652,8 @@ __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
     const float *oc = a.o_coarse + (size_t(h) * a.n_t + tile) * D;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        const int tok = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
-        if (tok < 0) continue;
-        const float inv = 1.0f / L[qb];
-        const size_t base = (size_t(tok) * a.ld + h) * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d0 = 32 * db + 8 * i + 4 * half;
-                store4(a.out, a.gate, base, d0, *reinterpret_cast<const float4 *>(oc + d0),
-                       O[db][qb][4 * i], O[db][qb][4 * i + 1], O[db][qb][4 * i + 2], O[db][qb][4 * i + 3], inv);
-            }
+        if (tok[qb] < 0) continue;
+        gated_row<DB>(a.out, a.gate, (size_t(tok[qb]) * a.ld + h) * D, oc, O, qb, 1.0f / L[qb], half);
     }
 }
 
