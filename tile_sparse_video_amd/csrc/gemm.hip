@@ -8,11 +8,22 @@
 // Both operands are K-contiguous (x is [rows][hidden], W is [out][hidden]). A
 // workgroup computes a 256 x 256 tile of g with 4 waves (2 x 2), each wave a
 // 128 x 128 sub-tile = 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 accumulated in
-// fp32. 64-wide k-slices of both operands are staged in LDS (double buffered,
-// 144 KB): the next slice is fetched into registers with bounds-checked
-// buffer loads (rows past the end read as zero) while the current one is
-// multiplied, and within a slice the MFMA fragments of the next 16-wide step
-// are read from LDS while the current step's 16 products run.
+// fp32. 64-wide k-slices of both operands alternate between two LDS stages
+// (128 KB) filled by buffer-to-LDS loads: the data never passes through VGPRs
+// and no LDS store instructions are issued. The loads of slice ks + 1 are
+// spread over the four 16-wide k-steps of slice ks, a quarter before each
+// step's products, so they never hold up the matrix-core issue. A staged row
+// is 128 bytes (eight 16-byte chunks); chunk c of row r sits in slot
+// c ^ ((r ^ (r >> 3)) & 7), so that one load instruction still covers eight
+// whole rows (coalesced) while the MFMA fragment reads (32 rows, one chunk)
+// hit distinct LDS banks. After each slice every wave waits for its own loads
+// and a barrier (no fence: the compiler's own waits would hold back the
+// loads in flight) publishes the next slice and frees the current stage.
+//
+// Tile order: workgroups are dispatched to the 8 XCDs round robin (blockIdx %
+// 8); each XCD takes a contiguous range of logical tiles, and logical tiles
+// run over groups of 8 row blocks, row block fastest, so that the workgroups
+// resident on one XCD share x rows and W rows in its L2.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -21,26 +32,37 @@
 namespace vsa {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, LROW = BK + 8;  // LDS row: 144 bytes
-constexpr int KC = BK / 16;                                 // MFMA k-steps per slice
+constexpr int BM = 256, BN = 256, BK = 64, NS = 2;
+constexpr int RB = BK * 2;        // bytes per staged row
+constexpr int OPB = BM * RB;      // bytes per operand per stage (32 KB)
+constexpr int STAGE = 2 * OPB;    // 64 KB
+constexpr size_t kLdsBytes = size_t(NS) * STAGE;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource word 3, 32-bit data (gfx9 family)
 
-typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+// s_waitcnt immediate (gfx9 encoding): at most n vector-memory loads
+// outstanding, the export and LDS counters left alone.
+#define VSA_VMCNT(n) (((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+__device__ __forceinline__ int chunk_slot(int c, int r) { return c ^ ((r ^ (r >> 3)) & 7); }
 
 __global__ __launch_bounds__(256, 1) void gate_gemm_kernel(const uint16_t *__restrict__ x,
                                                           const uint16_t *__restrict__ w, int64_t M,
                                                           int N, int K, uint16_t *__restrict__ g)
 {
-    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    uint16_t *As = lds;                   // [2][BM][LROW]
-    uint16_t *Bs = lds + 2 * BM * LROW;   // [2][BN][LROW]
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    extern __shared__ __attribute__((aligned(16))) char ring[];
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wm = wave / 2, wn = wave % 2, l32 = lane & 31, half = lane >> 5;
-    // N-blocks of one row block are consecutive, so they share the x rows in cache.
     const int nblocks = (N + BN - 1) / BN;
-    const int mb = __builtin_amdgcn_readfirstlane(int(blockIdx.x) / nblocks);
+    const int total = int(gridDim.x);
+    const int b = int(blockIdx.x), x8 = b % 8, per = total / 8, rem = total % 8;
+    const int lb = x8 < rem ? x8 * (per + 1) + b / 8 : rem * (per + 1) + (x8 - rem) * per + b / 8;
+    const int mrows = int((M + BM - 1) / BM);
+    const int grp = lb / (8 * nblocks), gm0 = grp * 8, gsz = min(8, mrows - gm0);
+    const int in = lb - grp * 8 * nblocks;
+    const int mb = __builtin_amdgcn_readfirstlane(gm0 + in % gsz);
     const int64_t m0 = int64_t(mb) * BM;
-    const int n0 = __builtin_amdgcn_readfirstlane(int(blockIdx.x) - mb * nblocks) * BN;
+    const int n0 = __builtin_amdgcn_readfirstlane(in / gsz) * BN;
 
     // One buffer resource per operand, based at the tile's first row and sized
     // to the rows that exist, so loads past the last row return zero.
@@ -53,36 +75,38 @@ __global__ __launch_bounds__(256, 1) void gate_gemm_kernel(const uint16_t *__res
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(w + int64_t(n0) * K), (short)0, b_rows * row_bytes, kRsrcWord3);
 
-    // Each thread moves 8 chunks of 16 bytes of x and of W per k-slice: chunk
-    // idx = tid + 256 t covers row idx / 8, bytes 16 (idx % 8) of the slice.
-    u32x4_t pa[8], pb[8];
-    auto load_global = [&](int k0) {
+    // Load j (< 8) of this wave fills rows 8 (8 wave + j) .. +7 of an operand:
+    // lane -> row + lane / 8, LDS slot lane % 8 (the instruction writes lane l
+    // at its LDS base + 16 l), holding the row's chunk whose slot that is. The
+    // slice's k offset goes in the scalar offset. Part p (< 4) of a slice is
+    // loads 2p and 2p + 1 of both operands.
+    uint32_t voff[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int idx = tid + 256 * t;
-            const uint32_t off = uint32_t(idx / 8) * row_bytes + uint32_t(k0) * 2 + 16 * (idx % 8);
-            pa[t] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
-            pb[t] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+    for (int j = 0; j < 8; ++j) {
+        const int r = (8 * wave + j) * 8 + lane / 8;
+        voff[j] = uint32_t(r) * row_bytes + 16u * uint32_t(chunk_slot(lane % 8, r));
+    }
+    auto issue = [&](int ks, int stage, int p) {
+        char *st = ring + stage * STAGE;
+#pragma unroll
+        for (int j = 2 * p; j < 2 * p + 2; ++j) {
+            const int rbase = (8 * wave + j) * 8 * RB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (__attribute__((address_space(3))) void *)(st + rbase), 16, voff[j], ks * RB, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (__attribute__((address_space(3))) void *)(st + OPB + rbase), 16, voff[j], ks * RB, 0, 0);
         }
     };
-    auto store_lds = [&](int buf) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int idx = tid + 256 * t;
-            const int r = idx / 8, c = idx % 8;
-            *reinterpret_cast<u32x4_t *>(&As[(buf * BM + r) * LROW + 8 * c]) = pa[t];
-            *reinterpret_cast<u32x4_t *>(&Bs[(buf * BN + r) * LROW + 8 * c]) = pb[t];
-        }
-    };
-    // Fragments of k-step kc: lane -> row 32 i + l32 of the wave's 128 rows,
-    // reduction slots 16 kc + 8 half .. +7.
-    auto load_frags = [&](int buf, int kc, bf16x8_t (&af)[4], bf16x8_t (&bf)[4]) {
+    // Fragment of k-step kc (< 4) of row block i: row R = 128 w + 32 i + l32,
+    // chunk 2 kc + half, slot chunk ^ (l32 & 7) ^ (l32 >> 3) ^ 4 (i & 1).
+    const int fl = (l32 & 7) ^ (l32 >> 3);
+    const int a_row = (wm * 128 + l32) * RB, b_row = OPB + (wn * 128 + l32) * RB;
+    auto load_frags = [&](const char *st, int kc, bf16x8_t (&af)[4], bf16x8_t (&bf)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            af[i] = *reinterpret_cast<const bf16x8_t *>(
-                &As[(buf * BM + wm * 128 + 32 * i + l32) * LROW + 16 * kc + 8 * half]);
-            bf[i] = *reinterpret_cast<const bf16x8_t *>(
-                &Bs[(buf * BN + wn * 128 + 32 * i + l32) * LROW + 16 * kc + 8 * half]);
+            const int cs = 16 * ((2 * kc + half) ^ fl ^ (4 * (i & 1)));
+            af[i] = *reinterpret_cast<const bf16x8_t *>(st + a_row + 32 * i * RB + cs);
+            bf[i] = *reinterpret_cast<const bf16x8_t *>(st + b_row + 32 * i * RB + cs);
         }
     };
 
@@ -93,22 +117,21 @@ __global__ __launch_bounds__(256, 1) void gate_gemm_kernel(const uint16_t *__res
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
     const int nk = K / BK;
-    load_global(0);
-    store_lds(0);
-    __syncthreads();
-    for (int ks = 0; ks < nk; ++ks) {
-        const int buf = ks & 1;
-        if (ks + 1 < nk) load_global((ks + 1) * BK);
-        bf16x8_t af[2][4], bf[2][4];
-        load_frags(buf, 0, af[0], bf[0]);
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            // The next step's fragment reads are issued before this step's
-            // products (scheduling barriers keep them there), so their LDS
-            // latency hides behind 16 MFMAs.
-            if (kc + 1 < KC) load_frags(buf, kc + 1, af[(kc + 1) & 1], bf[(kc + 1) & 1]);
+    for (int p = 0; p < 4; ++p) issue(0, 0, p);
+    __builtin_amdgcn_s_waitcnt(VSA_VMCNT(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // slice 0 has landed
+    asm volatile("" ::: "memory");
+    for (int ks = 0; ks < nk; ++ks) {
+        const char *st = ring + (ks % NS) * STAGE;
+        bf16x8_t af[2][4], bf[2][4];
+        load_frags(st, 0, af[0], bf[0]);
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            if (kc + 1 < 4) load_frags(st, kc + 1, af[(kc + 1) & 1], bf[(kc + 1) & 1]);
+            if (ks + 1 < nk) issue(ks + 1, (ks + 1) % NS, kc);  // into the stage of slice ks - 1, consumed
             __builtin_amdgcn_sched_barrier(0);
-            // C^T blocks: rows = n (W rows), cols = m (x rows) -> a lane owns one m.
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -117,10 +140,11 @@ __global__ __launch_bounds__(256, 1) void gate_gemm_kernel(const uint16_t *__res
                                                                         acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (ks + 1 < nk) {
-            store_lds(buf ^ 1);
-            __syncthreads();
-        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);         // this slice's LDS reads are done
+        __builtin_amdgcn_s_waitcnt(VSA_VMCNT(0));   // slice ks + 1 has landed (own loads)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     }
     // acc[i][j] element 4r + e <-> n = n0 + wn*128 + 32j + 8r + 4*half + e, m = m0 + wm*128 + 32i + l32.
 #pragma unroll
@@ -141,7 +165,7 @@ __global__ __launch_bounds__(256, 1) void gate_gemm_kernel(const uint16_t *__res
     }
 }
 
-constexpr size_t kLdsBytes = size_t(2) * (BM + BN) * LROW * 2;
+#undef VSA_VMCNT
 
 }  // namespace
 }  // namespace vsa
