@@ -237,15 +237,37 @@ __global__ __launch_bounds__(256) void coarse_attn_kernel(const float *__restric
     for (int db = 0; db < DB; ++db) O[db] = f32x16_t{};
     float mrun = -INFINITY, lrun = 0.f;
 
+    // Key blocks are staged through registers: thread t holds float4 number
+    // t + 256 u (u < NT) of the block's K and V means. The next block's loads
+    // are issued right after the current block is in LDS, so they are in
+    // flight under its products; they read a clamped row (rows past the end
+    // are written to LDS as zeros), so no load sits behind a branch.
+    constexpr int C4 = D / 4, NT = KB * C4 / 256;
+    float4 kreg[NT], vreg[NT];
+    auto fetch = [&](int j0) {
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            const int idx = threadIdx.x + 256 * u, r = idx / C4, c4 = idx % C4;
+            const size_t off = hb + size_t(min(j0 + r, n_t - 1)) * D + 4 * c4;
+            kreg[u] = *reinterpret_cast<const float4 *>(kmean + off);
+            vreg[u] = *reinterpret_cast<const float4 *>(vmean + off);
+        }
+    };
+    fetch(0);
     for (int j0 = 0; j0 < n_t; j0 += KB) {
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < KB * D; idx += 256) {
-            const int r = idx / D, c = idx % D;
+        __syncthreads();  // every wave is done with the previous block
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            const int idx = threadIdx.x + 256 * u, r = idx / C4, c4 = idx % C4;
             const bool live = j0 + r < n_t;
-            ks[r * ROW + c] = live ? kmean[hb + size_t(j0 + r) * D + c] : 0.f;
-            vs[r * ROW + c] = live ? vmean[hb + size_t(j0 + r) * D + c] : 0.f;
+            const float4 k4 = live ? kreg[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 v4 = live ? vreg[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+            float *kd = &ks[r * ROW + 4 * c4], *vd = &vs[r * ROW + 4 * c4];
+            kd[0] = k4.x; kd[1] = k4.y; kd[2] = k4.z; kd[3] = k4.w;
+            vd[0] = v4.x; vd[1] = v4.y; vd[2] = v4.z; vd[3] = v4.w;
         }
         __syncthreads();
+        if (j0 + KB < n_t) fetch(j0 + KB);
 
         f32x16_t S = f32x16_t{};
 #pragma unroll
