@@ -142,15 +142,19 @@ __global__ __launch_bounds__(256) void gather_pool_kernel(
 // ------------------------------------------------------------- tile scores --
 //
 // scores[h][i][j] = fma-chain over ascending d of qmean[first+i][d] *
-// kmean[first+j][d], from +0, for i, j < n. A block computes a 64 x 64 tile of (i, j) pairs from LDS copies of
-// the means; each thread owns 4 x 4 pairs and walks d in order, so every pair
-// is the same sequential chain of correctly rounded fused multiply-adds.
+// kmean[first+j][d], from +0, for i, j < n. A block computes a 128 x 128 tile
+// of (i, j) pairs; each thread owns 8 x 8 pairs (rows 8 ty + a, columns
+// tx + 16 b) and walks d in order, so every pair is the same sequential chain
+// of correctly rounded fused multiply-adds. The means are staged in LDS 32
+// values of d at a time; the next chunk is loaded into registers (clamped
+// rows, unconditional loads) while the current one is used.
 template <int D>
-__global__ __launch_bounds__(256) void tile_scores_kernel(const float *__restrict__ qmean,
+__global__ __launch_bounds__(256, 2) void tile_scores_kernel(const float *__restrict__ qmean,
                                                          const float *__restrict__ kmean, int n_t,
                                                          int first, int n, float *__restrict__ scores)
 {
-    constexpr int T = 64, ROW = D + 4;
+    constexpr int T = 128, DC = 32, ROW = DC + 4, NCH = D / DC;
+    constexpr int NL = T * DC / 4 / 256;  // float4 loads per thread per operand per chunk (4)
     __shared__ __attribute__((aligned(16))) float qs[T * ROW];
     __shared__ __attribute__((aligned(16))) float ks[T * ROW];
     const int h = blockIdx.z;
@@ -158,48 +162,70 @@ __global__ __launch_bounds__(256) void tile_scores_kernel(const float *__restric
     const int tid = threadIdx.x;
     const float *qh = qmean + (size_t(h) * n_t + first) * D;
     const float *kh = kmean + (size_t(h) * n_t + first) * D;
-    for (int idx = tid; idx < T * D / 4; idx += 256) {
-        const int r = idx / (D / 4), c = idx % (D / 4);
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-        if (i0 + r < n) a = *reinterpret_cast<const float4 *>(qh + size_t(i0 + r) * D + 4 * c);
-        if (j0 + r < n) b = *reinterpret_cast<const float4 *>(kh + size_t(j0 + r) * D + 4 * c);
-        *reinterpret_cast<float4 *>(&qs[r * ROW + 4 * c]) = a;
-        *reinterpret_cast<float4 *>(&ks[r * ROW + 4 * c]) = b;
+    // load u of a chunk: row (tid + 256 u) / 8, float4 (tid + 256 u) % 8 of the chunk
+    const float *qrow[NL], *krow[NL];
+    int lds_off[NL];
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+        const int idx = tid + 256 * u, r = idx / (DC / 4), c4 = idx % (DC / 4);
+        qrow[u] = qh + size_t(min(i0 + r, n - 1)) * D + 4 * c4;
+        krow[u] = kh + size_t(min(j0 + r, n - 1)) * D + 4 * c4;
+        lds_off[u] = r * ROW + 4 * c4;
     }
-    __syncthreads();
+    f32x4_t qreg[NL], kreg[NL];
+#define VSA_SCORES_FETCH(c)                                                                 \
+    _Pragma("unroll") for (int u = 0; u < NL; ++u) {                                       \
+        qreg[u] = *reinterpret_cast<const f32x4_t *>(qrow[u] + DC * (c));                  \
+        kreg[u] = *reinterpret_cast<const f32x4_t *>(krow[u] + DC * (c));                  \
+    }
     const int ty = tid / 16, tx = tid % 16;
-    float acc[4][4];
+    float acc[8][8];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
-    for (int d = 0; d < D; d += 4) {
-        float4 qv[4], kv[4];
+        for (int b = 0; b < 8; ++b) acc[a][b] = 0.0f;
+    VSA_SCORES_FETCH(0)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) qv[a] = *reinterpret_cast<const float4 *>(&qs[(4 * ty + a) * ROW + d]);
+    for (int c = 0; c < NCH; ++c) {
+        __syncthreads();  // every thread is done with the previous chunk
 #pragma unroll
-        for (int b = 0; b < 4; ++b) kv[b] = *reinterpret_cast<const float4 *>(&ks[(tx + 16 * b) * ROW + d]);
+        for (int u = 0; u < NL; ++u) {
+            *reinterpret_cast<f32x4_t *>(&qs[lds_off[u]]) = qreg[u];
+            *reinterpret_cast<f32x4_t *>(&ks[lds_off[u]]) = kreg[u];
+        }
+        __syncthreads();
+        if (c + 1 < NCH) {
+            VSA_SCORES_FETCH(c + 1)
+        }
+        for (int d = 0; d < DC; d += 4) {
+            float4 qv[8], kv[8];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < 8; ++a) qv[a] = *reinterpret_cast<const float4 *>(&qs[(8 * ty + a) * ROW + d]);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                acc[a][b] = __builtin_fmaf(qv[a].x, kv[b].x, acc[a][b]);
-                acc[a][b] = __builtin_fmaf(qv[a].y, kv[b].y, acc[a][b]);
-                acc[a][b] = __builtin_fmaf(qv[a].z, kv[b].z, acc[a][b]);
-                acc[a][b] = __builtin_fmaf(qv[a].w, kv[b].w, acc[a][b]);
-            }
+            for (int b = 0; b < 8; ++b) kv[b] = *reinterpret_cast<const float4 *>(&ks[(tx + 16 * b) * ROW + d]);
+#pragma unroll
+            for (int a = 0; a < 8; ++a)
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    acc[a][b] = __builtin_fmaf(qv[a].x, kv[b].x, acc[a][b]);
+                    acc[a][b] = __builtin_fmaf(qv[a].y, kv[b].y, acc[a][b]);
+                    acc[a][b] = __builtin_fmaf(qv[a].z, kv[b].z, acc[a][b]);
+                    acc[a][b] = __builtin_fmaf(qv[a].w, kv[b].w, acc[a][b]);
+                }
+        }
     }
     float *out = scores + size_t(h) * n * n;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int i = i0 + 4 * ty + a;
+    for (int a = 0; a < 8; ++a) {
+        const int i = i0 + 8 * ty + a;
         if (i >= n) continue;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < 8; ++b) {
             const int j = j0 + tx + 16 * b;
             if (j < n) out[size_t(i) * n + j] = acc[a][b];
         }
     }
+#undef VSA_SCORES_FETCH
 }
 
 // ------------------------------------------------------- coarse attention --
@@ -710,7 +736,7 @@ void launch_coarse(const vsa_plan_info &info, int H, float scale, const float *q
 {
     const int n_t = info.n_tiles;
     if (n > 0) {
-        dim3 grid((n + 63) / 64, (n + 63) / 64, H);
+        dim3 grid((n + 127) / 128, (n + 127) / 128, H);
         KernelTimer t(K_VIDEO_SCORES, st);
         hipLaunchKernelGGL((tile_scores_kernel<D>), grid, dim3(256), 0, st, qm, km, n_t, first, n, scores);
     }
