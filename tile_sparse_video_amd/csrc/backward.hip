@@ -753,52 +753,47 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
 }
 
 // Sums the 8 chunk partials of one item (in chunk order) and writes
-// dq = scale dQ_fine + dqm / n. One wavefront per item, lanes as the dq kernel.
+// dq = scale dQ_fine + dqm / n. One wavefront per (item, 32-row half qb,
+// 32-column block db), lanes as the dq kernel: its 32 partial loads are
+// independent and in flight together, and the many small waves hide the
+// latency of one another.
 template <int D, int B>
 __global__ __launch_bounds__(256) void dq_merge_kernel(BwdArgs a, int n_items)
 {
     constexpr int SUB = B / 64, DB = D / 32;
     const int lane = threadIdx.x % kWave, half = lane >> 5, l32 = lane & 31;
-    const int item = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (item >= n_items) return;
+    const int wid = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (wid >= n_items * 2 * DB) return;
+    const int item = wid / (2 * DB), qb = (wid / DB) % 2, db = wid % DB;
     const int h = item / (a.n_t * SUB), r = item % (a.n_t * SUB);
     const int tile = r / SUB, qsub = r % SUB;
+    const int tok = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
     const float inv_n = 1.0f / float(a.block_len[tile]);
-    const float *gm = a.dqm + (size_t(h) * a.n_t + tile) * D;
+    const float *gm = a.dqm + (size_t(h) * a.n_t + tile) * D + 32 * db + 4 * half;
+    float acc[16] = {};
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int tok = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
-        if (tok < 0) continue;
-        float *dst = a.dq + (size_t(tok) * a.H + h) * D;
+    for (int c = 0; c < 8; ++c) {
+        const float4 *src = reinterpret_cast<const float4 *>(
+            a.part_dq + (size_t(item) * 8 + c) * (DB * 2 * kWave * 16) + ((db * 2 + qb) * kWave + lane) * 16);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            float acc[16] = {};
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const float4 *src = reinterpret_cast<const float4 *>(
-                    a.part_dq + (size_t(item) * 8 + c) * (DB * 2 * kWave * 16) + ((db * 2 + qb) * kWave + lane) * 16);
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const float4 v = src[q4];
-                    acc[4 * q4] += v.x;
-                    acc[4 * q4 + 1] += v.y;
-                    acc[4 * q4 + 2] += v.z;
-                    acc[4 * q4 + 3] += v.w;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d0 = 32 * db + 8 * i + 4 * half;
-                const float4 mm = *reinterpret_cast<const float4 *>(gm + d0);
-                float4 o;
-                o.x = a.scale * acc[4 * i] + mm.x * inv_n;
-                o.y = a.scale * acc[4 * i + 1] + mm.y * inv_n;
-                o.z = a.scale * acc[4 * i + 2] + mm.z * inv_n;
-                o.w = a.scale * acc[4 * i + 3] + mm.w * inv_n;
-                *reinterpret_cast<float4 *>(dst + d0) = o;
-            }
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 v = src[q4];
+            acc[4 * q4] += v.x;
+            acc[4 * q4 + 1] += v.y;
+            acc[4 * q4 + 2] += v.z;
+            acc[4 * q4 + 3] += v.w;
         }
     }
+    float4 mm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mm[i] = *reinterpret_cast<const float4 *>(gm + 8 * i);
+    if (tok < 0) return;
+    float *dst = a.dq + (size_t(tok) * a.H + h) * D + 32 * db + 4 * half;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4 *>(dst + 8 * i) =
+            make_float4(a.scale * acc[4 * i] + mm[i].x * inv_n, a.scale * acc[4 * i + 1] + mm[i].y * inv_n,
+                        a.scale * acc[4 * i + 2] + mm[i].z * inv_n, a.scale * acc[4 * i + 3] + mm[i].w * inv_n);
 }
 
 // ------------------------------------------------------------------ dkdv --
@@ -1234,56 +1229,46 @@ int ring_lds_attr()
 
 // Sums the 8 chunk partials of one (head, key tile, 32 key rows) in chunk
 // order and writes dk = scale dK + dkm / n, dv = dV + dvm / n for real keys.
+// One wavefront per (unit, dk or dv, 32-column block db): its 32 partial
+// loads are independent and in flight together.
 template <int D, int B>
 __global__ __launch_bounds__(256) void dkdv_merge_kernel(BwdArgs a, int n_units)
 {
     constexpr int DB = D / 32, KB = B / 32;
     const int lane = threadIdx.x % kWave, half = lane >> 5, l32 = lane & 31;
-    const int unit = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (unit >= n_units) return;
+    const int wid = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (wid >= n_units * 2 * DB) return;
+    const int unit = wid / (2 * DB), kv = (wid / DB) % 2, db = wid % DB;
     const int ht = unit / KB, kb = unit % KB;
     const int h = ht / a.n_t, tile = ht % a.n_t;
     const int ktok = a.row_src[size_t(tile) * B + 32 * kb + l32];
-    if (ktok < 0) return;
     const float inv_n = 1.0f / float(a.block_len[tile]);
-    const float *gk = a.dkm + (size_t(h) * a.n_t + tile) * D;
-    const float *gv = a.dvm + (size_t(h) * a.n_t + tile) * D;
-    float *dk = a.dk + (size_t(ktok) * a.H + h) * D;
-    float *dv = a.dv + (size_t(ktok) * a.H + h) * D;
+    const float *gm = (kv == 0 ? a.dkm : a.dvm) + (size_t(h) * a.n_t + tile) * D + 32 * db + 4 * half;
+    float acc[16] = {};
 #pragma unroll
-    for (int kv = 0; kv < 2; ++kv)
+    for (int c = 0; c < 8; ++c) {
+        const float4 *src = reinterpret_cast<const float4 *>(
+            a.part_dkv + ((size_t(ht) * 8 + c) * KB + kb) * (2 * DB * kWave * 16) + ((kv * DB + db) * kWave + lane) * 16);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            float acc[16] = {};
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const float4 *src = reinterpret_cast<const float4 *>(
-                    a.part_dkv + ((size_t(ht) * 8 + c) * KB + kb) * (2 * DB * kWave * 16) +
-                    ((kv * DB + db) * kWave + lane) * 16);
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const float4 v = src[q4];
-                    acc[4 * q4] += v.x;
-                    acc[4 * q4 + 1] += v.y;
-                    acc[4 * q4 + 2] += v.z;
-                    acc[4 * q4 + 3] += v.w;
-                }
-            }
-            const float sc = kv == 0 ? a.scale : 1.0f;
-            const float *gm = kv == 0 ? gk : gv;
-            float *dst = kv == 0 ? dk : dv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d0 = 32 * db + 8 * i + 4 * half;
-                const float4 mm = *reinterpret_cast<const float4 *>(gm + d0);
-                float4 o;
-                o.x = sc * acc[4 * i] + mm.x * inv_n;
-                o.y = sc * acc[4 * i + 1] + mm.y * inv_n;
-                o.z = sc * acc[4 * i + 2] + mm.z * inv_n;
-                o.w = sc * acc[4 * i + 3] + mm.w * inv_n;
-                *reinterpret_cast<float4 *>(dst + d0) = o;
-            }
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 v = src[q4];
+            acc[4 * q4] += v.x;
+            acc[4 * q4 + 1] += v.y;
+            acc[4 * q4 + 2] += v.z;
+            acc[4 * q4 + 3] += v.w;
         }
+    }
+    float4 mm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mm[i] = *reinterpret_cast<const float4 *>(gm + 8 * i);
+    if (ktok < 0) return;
+    const float sc = kv == 0 ? a.scale : 1.0f;
+    float *dst = (kv == 0 ? a.dk : a.dv) + (size_t(ktok) * a.H + h) * D + 32 * db + 4 * half;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4 *>(dst + 8 * i) =
+            make_float4(sc * acc[4 * i] + mm[i].x * inv_n, sc * acc[4 * i + 1] + mm[i].y * inv_n,
+                        sc * acc[4 * i + 2] + mm[i].z * inv_n, sc * acc[4 * i + 3] + mm[i].w * inv_n);
 }
 
 }  // namespace
@@ -1422,7 +1407,7 @@ void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, 
     if (split) {
         KernelTimer t(K_BWD_DQ, st);
         hipLaunchKernelGGL((dq_kernel<D, B, true>), dim3(items * 8), dim3(64), 0, st, a);
-        hipLaunchKernelGGL((dq_merge_kernel<D, B>), dim3((items + 3) / 4), dim3(256), 0, st, a, items);
+        hipLaunchKernelGGL((dq_merge_kernel<D, B>), dim3((items * 2 * (D / 32) + 3) / 4), dim3(256), 0, st, a, items);
     } else {
         KernelTimer t(K_BWD_DQ, st);
         hipLaunchKernelGGL((dq_kernel<D, B, false>), dim3(items), dim3(64), 0, st, a);
@@ -1432,7 +1417,7 @@ void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, 
         if (dkdv_split(info, H, D)) {
             hipLaunchKernelGGL((dkdv_ring_kernel<D, B>), dim3(H * n_t * 8), dim3(B * 2), (RingCfg<D, B>::LDS), st, a);
             const int units = H * n_t * (B / 32);
-            hipLaunchKernelGGL((dkdv_merge_kernel<D, B>), dim3((units + 3) / 4), dim3(256), 0, st, a, units);
+            hipLaunchKernelGGL((dkdv_merge_kernel<D, B>), dim3((units * 2 * (D / 32) + 3) / 4), dim3(256), 0, st, a, units);
         } else {
             hipLaunchKernelGGL((dkdv_kernel<D, B>), dim3(H * n_t), dim3(B * 2), 0, st, a);
         }
