@@ -88,12 +88,24 @@ __global__ __launch_bounds__(256) void gather_pool_kernel(
     if (tid < B) toks[tid] = row_src[size_t(tile) * B + tid];
     __syncthreads();
 
-    for (int idx = tid; idx < B * CH; idx += 256) {
-        const int r = idx / CH, c = idx % CH;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (r < n && c / (D / 8) < nh)
-            val = *reinterpret_cast<const uint4 *>(X + (size_t(toks[r]) * ld + h0) * D + c * 8);
-        *reinterpret_cast<uint4 *>(&lds[r * ROW + c * 8]) = val;
+    // Every load is issued unconditionally (from a clamped row, head and token,
+    // so always inside the input) and masked afterwards, so a thread's loads are
+    // all in flight together; a guarded load would become a branch with its own
+    // wait.
+    constexpr int NLD = B * CH / 256;
+    uint4 val[NLD];
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+        const int idx = tid + 256 * u, r = idx / CH, c = idx % CH;
+        const int rr = max(min(r, n - 1), 0), hh = min(c / (D / 8), nh - 1);
+        const int tok = max(toks[rr], 0);
+        val[u] = *reinterpret_cast<const uint4 *>(X + (size_t(tok) * ld + h0 + hh) * D + (c % (D / 8)) * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+        const int idx = tid + 256 * u, r = idx / CH, c = idx % CH;
+        const bool live = r < n && c / (D / 8) < nh;
+        *reinterpret_cast<uint4 *>(&lds[r * ROW + c * 8]) = live ? val[u] : make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
 
