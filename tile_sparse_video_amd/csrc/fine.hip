@@ -108,6 +108,7 @@ constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr float kLazy = 8.0f;   // log2-domain slack before the running max moves
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource word 3, 32-bit data (gfx9 family)
 constexpr int kListCap = 896;   // key-list entries staged in LDS per segment
+constexpr int kFillBatch = 4;   // 64-position blocks of the key list read per round
 
 // Max / sum of a value and its copy in the lane 32 apart (same query column of
 // the other row half): v_permlane32_swap exchanges the upper half of one
@@ -278,34 +279,71 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
     const int32_t *keep_row = a.ref ? a.keep + (size_t(h) * a.n_t + tile) * a.list_len
                               : dense ? a.keep
                                       : a.keep + (size_t(h) * a.n_v + (tile - a.P)) * a.k;
-    auto tile_at = [&](int n) -> int {
-        if (a.ref) return min(max(keep_row[n], 0), a.n_t - 1);
-        return (dense || n < a.P) ? n : min(max(keep_row[n - a.P], 0), a.n_t - 1);
+    // Tiles of list positions n (0 <= n < n_list). The list loads are issued for
+    // every lane (at clamped positions) whenever the wave's list has stored
+    // entries, all in one block, and the values are chosen afterwards, so no
+    // load sits behind a per-lane branch or waits for another.
+    const bool from_keep = a.ref || (!dense && a.k > 0);  // wave-uniform
+    auto tiles_at = [&](const int (&n)[kFillBatch], int (&t)[kFillBatch]) {
+        int kv[kFillBatch];
+#pragma unroll
+        for (int u = 0; u < kFillBatch; ++u) kv[u] = 0;
+        if (from_keep) {
+#pragma unroll
+            for (int u = 0; u < kFillBatch; ++u)
+                kv[u] = keep_row[a.ref ? min(n[u], a.list_len - 1) : min(max(n[u] - a.P, 0), a.k - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < kFillBatch; ++u) {
+            const int c = min(max(kv[u], 0), a.n_t - 1);
+            t[u] = a.ref ? c : ((dense || n[u] < a.P) ? n[u] : c);
+        }
     };
     // The wave stages the next segment of its key list (tiles of this chunk)
-    // into LDS with block_len packed alongside, 64 list positions at a time.
+    // into LDS with block_len packed alongside. Four blocks of 64 list
+    // positions are read per round: their entries, then their tiles' block
+    // lengths (and INT8 block scales), each batch in flight together.
     int scan = 0;
     auto fill = [&]() -> int {
         int count = 0;
-        while (scan < n_list) {
-            const int n = scan + lane;
-            const int t = n < n_list ? tile_at(n) : -1;
-            const bool match = t >= 0 && (!SPLIT || t % a.chunks == chunk);
-            const uint64_t mask = __ballot(match);
-            const int take = __popcll(mask);
-            if (count + take > kListCap) break;  // next segment
-            if (match) {
-                const int bl = a.block_len[t];
-                const int at = count + __popcll(mask & lanes_below(lane));
-                list_lds[at] = uint32_t(t) | uint32_t(bl - 1) << 25;
+        bool full = false;
+        while (!full && scan < n_list) {
+            int pos[kFillBatch], tt[kFillBatch], bl[kFillBatch];
+            float sk[I8 ? kFillBatch * SUB : 1];
+#pragma unroll
+            for (int u = 0; u < kFillBatch; ++u) pos[u] = min(scan + kWave * u + lane, n_list - 1);
+            tiles_at(pos, tt);
+#pragma unroll
+            for (int u = 0; u < kFillBatch; ++u) {
+                bl[u] = a.block_len[tt[u]];
                 if constexpr (I8) {
 #pragma unroll
                     for (int sb = 0; sb < SUB; ++sb)
-                        list_sk[at * SUB + sb] = a.k_scale[(size_t(h) * a.n_t + t) * SUB + sb];
+                        sk[u * SUB + sb] = a.k_scale[(size_t(h) * a.n_t + tt[u]) * SUB + sb];
                 }
             }
-            count += take;
-            scan += kWave;
+#pragma unroll
+            for (int u = 0; u < kFillBatch; ++u) {
+                if (full || scan >= n_list) break;  // uniform
+                const int n = scan + lane, t = tt[u];
+                const bool match = n < n_list && (!SPLIT || t % a.chunks == chunk);
+                const uint64_t mask = __ballot(match);
+                const int take = __popcll(mask);
+                if (count + take > kListCap) {  // next segment
+                    full = true;
+                    break;
+                }
+                if (match) {
+                    const int at = count + __popcll(mask & lanes_below(lane));
+                    list_lds[at] = uint32_t(t) | uint32_t(bl[u] - 1) << 25;
+                    if constexpr (I8) {
+#pragma unroll
+                        for (int sb = 0; sb < SUB; ++sb) list_sk[at * SUB + sb] = sk[u * SUB + sb];
+                    }
+                }
+                count += take;
+                scan += kWave;
+            }
         }
         __syncthreads();
         return count;
