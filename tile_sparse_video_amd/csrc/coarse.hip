@@ -154,19 +154,22 @@ __global__ __launch_bounds__(256) void gather_pool_kernel(
 // ------------------------------------------------------------- tile scores --
 //
 // scores[h][i][j] = fma-chain over ascending d of qmean[first+i][d] *
-// kmean[first+j][d], from +0, for i, j < n. A block computes a 128 x 128 tile
-// of (i, j) pairs; each thread owns 8 x 8 pairs (rows 8 ty + a, columns
-// tx + 16 b) and walks d in order, so every pair is the same sequential chain
-// of correctly rounded fused multiply-adds. The means are staged in LDS 32
-// values of d at a time; the next chunk is loaded into registers (clamped
-// rows, unconditional loads) while the current one is used.
-template <int D>
+// kmean[first+j][d], from +0, for i, j < n. A block computes a 16 TM x 16 TM
+// tile of (i, j) pairs; each thread owns TM x TM pairs (rows TM ty + a,
+// columns tx + 16 b) and walks d in order, so every pair is the same
+// sequential chain of correctly rounded fused multiply-adds. TM = 8 (128 x 128
+// tiles, 4x fewer LDS reads per FMA) for large grids, TM = 4 when that would
+// leave CUs idle. The means are staged in LDS 32 values of d at a time; the
+// next chunk is loaded into registers (clamped rows, unconditional loads)
+// while the current one is used.
+template <int D, int TM>
 __global__ __launch_bounds__(256, 2) void tile_scores_kernel(const float *__restrict__ qmean,
                                                          const float *__restrict__ kmean, int n_t,
                                                          int first, int n, float *__restrict__ scores)
 {
-    constexpr int T = 128, DC = 32, ROW = DC + 4, NCH = D / DC;
-    constexpr int NL = T * DC / 4 / 256;  // float4 loads per thread per operand per chunk (4)
+    constexpr int T = 16 * TM, DC = 32, ROW = DC + 4, NCH = D / DC;
+    constexpr int NL = T * DC / 4 / 256;  // float4 loads per thread per operand per chunk
+    constexpr int DUN = TM == 8 ? 1 : 2;  // d-step unrolling that keeps the LDS reads in registers
     __shared__ __attribute__((aligned(16))) float qs[T * ROW];
     __shared__ __attribute__((aligned(16))) float ks[T * ROW];
     const int h = blockIdx.z;
@@ -191,11 +194,11 @@ __global__ __launch_bounds__(256, 2) void tile_scores_kernel(const float *__rest
         kreg[u] = *reinterpret_cast<const f32x4_t *>(krow[u] + DC * (c));                  \
     }
     const int ty = tid / 16, tx = tid % 16;
-    float acc[8][8];
+    float acc[TM][TM];
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < 8; ++b) acc[a][b] = 0.0f;
+        for (int b = 0; b < TM; ++b) acc[a][b] = 0.0f;
     VSA_SCORES_FETCH(0)
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -209,16 +212,17 @@ __global__ __launch_bounds__(256, 2) void tile_scores_kernel(const float *__rest
         if (c + 1 < NCH) {
             VSA_SCORES_FETCH(c + 1)
         }
+#pragma unroll DUN
         for (int d = 0; d < DC; d += 4) {
-            float4 qv[8], kv[8];
+            float4 qv[TM], kv[TM];
 #pragma unroll
-            for (int a = 0; a < 8; ++a) qv[a] = *reinterpret_cast<const float4 *>(&qs[(8 * ty + a) * ROW + d]);
+            for (int a = 0; a < TM; ++a) qv[a] = *reinterpret_cast<const float4 *>(&qs[(TM * ty + a) * ROW + d]);
 #pragma unroll
-            for (int b = 0; b < 8; ++b) kv[b] = *reinterpret_cast<const float4 *>(&ks[(tx + 16 * b) * ROW + d]);
+            for (int b = 0; b < TM; ++b) kv[b] = *reinterpret_cast<const float4 *>(&ks[(tx + 16 * b) * ROW + d]);
 #pragma unroll
-            for (int a = 0; a < 8; ++a)
+            for (int a = 0; a < TM; ++a)
 #pragma unroll
-                for (int b = 0; b < 8; ++b) {
+                for (int b = 0; b < TM; ++b) {
                     acc[a][b] = __builtin_fmaf(qv[a].x, kv[b].x, acc[a][b]);
                     acc[a][b] = __builtin_fmaf(qv[a].y, kv[b].y, acc[a][b]);
                     acc[a][b] = __builtin_fmaf(qv[a].z, kv[b].z, acc[a][b]);
@@ -228,11 +232,11 @@ __global__ __launch_bounds__(256, 2) void tile_scores_kernel(const float *__rest
     }
     float *out = scores + size_t(h) * n * n;
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-        const int i = i0 + 8 * ty + a;
+    for (int a = 0; a < TM; ++a) {
+        const int i = i0 + TM * ty + a;
         if (i >= n) continue;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
+        for (int b = 0; b < TM; ++b) {
             const int j = j0 + tx + 16 * b;
             if (j < n) out[size_t(i) * n + j] = acc[a][b];
         }
@@ -748,9 +752,15 @@ void launch_coarse(const vsa_plan_info &info, int H, float scale, const float *q
 {
     const int n_t = info.n_tiles;
     if (n > 0) {
-        dim3 grid((n + 127) / 128, (n + 127) / 128, H);
         KernelTimer t(K_VIDEO_SCORES, st);
-        hipLaunchKernelGGL((tile_scores_kernel<D>), grid, dim3(256), 0, st, qm, km, n_t, first, n, scores);
+        const int64_t big = int64_t((n + 127) / 128) * ((n + 127) / 128) * H;
+        if (big >= 512) {
+            dim3 grid((n + 127) / 128, (n + 127) / 128, H);
+            hipLaunchKernelGGL((tile_scores_kernel<D, 8>), grid, dim3(256), 0, st, qm, km, n_t, first, n, scores);
+        } else {
+            dim3 grid((n + 63) / 64, (n + 63) / 64, H);
+            hipLaunchKernelGGL((tile_scores_kernel<D, 4>), grid, dim3(256), 0, st, qm, km, n_t, first, n, scores);
+        }
     }
     dim3 grid2((n_t + 127) / 128, H);
     KernelTimer t(K_COARSE_ATTN, st);
