@@ -40,6 +40,10 @@ INT8_PEAK_TOPS = 5033.2     # MI355X dense int8 MFMA (vendor figure)
 # INT8 fine pass: per kept pair 2D int8 ops (scores) at the int8 peak and 2D bf16
 # flops (P.V) at the bf16 peak, so 4D operations take 2D/INT8 + 2D/BF16 at best.
 MIXED_PEAK_TOPS = 2.0 / (1.0 / INT8_PEAK_TOPS + 1.0 / BF16_PEAK_TFLOPS)
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X fp32 matrix (vendor figure)
+# fp32 FMA on the vector ALUs without packed (two-wide) instructions, which this build leaves
+# off: 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz.
+FP32_VALU_FMA_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 
 
 def effective_fine_flops(plan, keep_idx: np.ndarray, heads: int, head_dim: int,
@@ -78,6 +82,27 @@ def hbm_passes(wl, plan, kernels, k, k_ref=None):
             gbs = nbytes / (kernels[name]["avg_ms"] * 1e-3) / 1e9
             out[name] = {"algorithmic_bytes": int(nbytes), "gb_s": round(gbs, 1),
                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
+
+
+def compute_passes(wl, plan, kernels, k_ref=None):
+    """Rates of the compute-bound side kernels against the peak of the unit each runs on:
+    the gate GEMM (2 * hidden FLOP per output, bf16 MFMA), the coarse scores (2 * D FLOP per
+    scored tile pair, fp32 FMA chains on the VALU) and the coarse attention (4 * D FLOP per
+    (query tile, key tile) pair, fp32 MFMA)."""
+    H, D, S = wl.heads, wl.head_dim, wl.tokens
+    n = plan.n_t if k_ref is not None else plan.n_v
+    work = {
+        "gate_gemm": (2.0 * S * wl.hidden * H * D, BF16_PEAK_TFLOPS, "bf16 MFMA"),
+        "video_scores": (2.0 * D * n * n * H, FP32_VALU_FMA_PEAK_TFLOPS, "fp32 VALU FMA"),
+        "coarse_attn": (4.0 * D * plan.n_t * plan.n_t * H, FP32_MFMA_PEAK_TFLOPS, "fp32 MFMA"),
+    }
+    out = {}
+    for name, (flops, peak, unit) in work.items():
+        if name in kernels and flops > 0:
+            tf = flops / (kernels[name]["avg_ms"] * 1e-3) / 1e12
+            out[name] = {"algorithmic_tflop": round(flops / 1e12, 4), "tflop_s": round(tf, 2),
+                         "peak": round(peak, 1), "unit": unit, "frac": round(tf / peak, 4)}
     return out
 
 
@@ -420,6 +445,7 @@ def main() -> int:
         "tile_pair_fraction": round(frac_pairs, 4),
         "effective_fine_tflop": round(fine_flops / 1e12, 3),
         "hbm_passes": hbm_passes(wl, att.plan, kernels, att.k, att.k_ref if att.ref else None),
+        "compute_passes": compute_passes(wl, att.plan, kernels, att.k_ref if att.ref else None),
         "wall_s": round(wall, 3),
         "roofline": {
             "kernel": ("fine_attn_kernel, INT8 scores (vsa_sparse_attn_fwd_i8; peak mixes the "
