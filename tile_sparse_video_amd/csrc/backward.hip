@@ -764,8 +764,11 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdArgs a, int n_items)
     const int lane = threadIdx.x % kWave, half = lane >> 5, l32 = lane & 31;
     const int wid = blockIdx.x * 4 + threadIdx.x / kWave;
     if (wid >= n_items * 2 * DB) return;
-    const int item = wid / (2 * DB), qb = (wid / DB) % 2, db = wid % DB;
-    const int h = item / (a.n_t * SUB), r = item % (a.n_t * SUB);
+    // Tile-major numbering (the heads of one 64-row block side by side): the
+    // fp32 dq rows that neighbouring waves write lie in the same token records.
+    const int grp = wid / (2 * DB), qb = (wid / DB) % 2, db = wid % DB;
+    const int h = grp % a.H, r = grp / a.H;
+    const int item = h * (a.n_t * SUB) + r;
     const int tile = r / SUB, qsub = r % SUB;
     const int tok = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
     const float inv_n = 1.0f / float(a.block_len[tile]);
@@ -1238,9 +1241,11 @@ __global__ __launch_bounds__(256) void dkdv_merge_kernel(BwdArgs a, int n_units)
     const int lane = threadIdx.x % kWave, half = lane >> 5, l32 = lane & 31;
     const int wid = blockIdx.x * 4 + threadIdx.x / kWave;
     if (wid >= n_units * 2 * DB) return;
-    const int unit = wid / (2 * DB), kv = (wid / DB) % 2, db = wid % DB;
-    const int ht = unit / KB, kb = unit % KB;
-    const int h = ht / a.n_t, tile = ht % a.n_t;
+    // Tile-major numbering, as in dq_merge_kernel.
+    const int grp = wid / (2 * DB), kv = (wid / DB) % 2, db = wid % DB;
+    const int h = grp % a.H, rest = grp / a.H;
+    const int tile = rest / KB, kb = rest % KB;
+    const int ht = h * a.n_t + tile;
     const int ktok = a.row_src[size_t(tile) * B + 32 * kb + l32];
     const float inv_n = 1.0f / float(a.block_len[tile]);
     const float *gm = (kv == 0 ? a.dkm : a.dvm) + (size_t(h) * a.n_t + tile) * D + 32 * db + 4 * half;

@@ -575,11 +575,15 @@ __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
 {
     constexpr int SUB = B / 64, DB = D / 32;
     const int lane = threadIdx.x % kWave;
-    const int item = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (item >= n_items) return;
+    // Waves are numbered tile-major (the heads of one 64-row block side by
+    // side), so neighbouring waves read and write adjacent slices of the same
+    // token records of g and out (1.7 % faster than head-major at 42 heads).
+    const int wi = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (wi >= n_items) return;
     const int l32 = lane & 31, half = lane >> 5;
-    const int h = item / (a.n_t * SUB);
-    const int r = item % (a.n_t * SUB);
+    const int h = wi % a.H;
+    const int r = wi / a.H;
+    const int item = h * (a.n_t * SUB) + r;
     const int tile = r / SUB, qsub = r % SUB;
     const float c2 = a.scale_log2e;
     const int C = a.chunks;
