@@ -384,6 +384,15 @@ __global__ __launch_bounds__(256) void coarse_attn_kernel(const float *__restric
 // Then a pass in ascending column order keeps every key > T and the first
 // (k - #keys > T) keys equal to T (after an early stop: every key >= T).
 
+// A lane mask of the wave's predicate (the compare's own result, no select).
+__device__ __forceinline__ uint64_t wave_mask(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// add + the number of set bits of mask in the lanes below this one (v_mbcnt).
+__device__ __forceinline__ int below_count(uint64_t mask, int add)
+{
+    return int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), uint32_t(add))));
+}
+
 // Loads the keys of columns c0 + 64 e + lane. Every load is issued
 // unconditionally (a clamped column for slots past the row), so all of them
 // are in flight at once; a guarded load would become a branch with its own
@@ -407,7 +416,7 @@ __device__ __forceinline__ int topk_count_ge(const uint32_t (&key)[PL], uint32_t
 {
     int c = 0;
 #pragma unroll
-    for (int e = 0; e < PL; ++e) c += __popcll(__ballot(key[e] >= t));
+    for (int e = 0; e < PL; ++e) c += __popcll(wave_mask(key[e] >= t));
     return c;
 }
 
@@ -458,8 +467,8 @@ __device__ __forceinline__ void topk_select(const uint32_t (&key)[PL], int c0, i
             if (c0 + kWave * e >= n_cols) break;  // uniform
             const int j = c0 + kWave * e + lane;
             const bool sel = j < n_cols && key[e] >= T;
-            const uint64_t sel_mask = __ballot(sel);
-            const int pos = base + __popcll(sel_mask & lanes_below(lane));
+            const uint64_t sel_mask = wave_mask(sel);
+            const int pos = below_count(sel_mask, base);
             if (sel && pos < k) out[pos] = id_first + j;  // exactly k are selected; the bound is a guard
             base += __popcll(sel_mask);
         }
@@ -472,11 +481,11 @@ __device__ __forceinline__ void topk_select(const uint32_t (&key)[PL], int c0, i
         const bool valid = j < n_cols;
         const bool gt = valid && key[e] > T;
         const bool eq = valid && key[e] == T;
-        const uint64_t eq_mask = __ballot(eq);
-        const int eq_before = __popcll(eq_mask & lanes_below(lane));
+        const uint64_t eq_mask = wave_mask(eq);
+        const int eq_before = below_count(eq_mask, 0);
         const bool sel = gt || (eq && eq_seen + eq_before < krem);
-        const uint64_t sel_mask = __ballot(sel);
-        const int pos = base + __popcll(sel_mask & lanes_below(lane));
+        const uint64_t sel_mask = wave_mask(sel);
+        const int pos = below_count(sel_mask, base);
         if (sel && pos < k) out[pos] = id_first + j;  // exactly k are selected; the bound is a guard
         base += __popcll(sel_mask);
         eq_seen += __popcll(eq_mask);
@@ -522,21 +531,111 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
     topk_select<PL>(key, 0, n_cols, lane, T, exact, k - n_gt, 0, 0, k, id_first, out);
 }
 
+// A threshold t >= 1 with at least r of the wave's sample registers sk (0 =
+// no sample) at or above it: the r-th largest sample, or any value at which
+// exactly r samples pass (the search stops there).
+template <int SR>
+__device__ __forceinline__ uint32_t topk_sample_threshold(const uint32_t (&sk)[SR], int r)
+{
+    uint32_t t = 0u;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = t | (1u << b);
+        const int c = topk_count_ge<SR>(sk, cand);
+        if (c >= r) t = cand;
+        if (c == r) break;
+    }
+    return t;
+}
+
+// One wave: the k largest of m <= 64 CR candidates (cand[0..m): key, column;
+// keys all >= tlo, in column order), written as ascending ids
+// id_first + column to out[0..k). Every key of the row above the k-th largest
+// is a candidate, so the candidates' counts are the row's.
+template <int CR>
+__device__ __forceinline__ void topk_finish(const uint2 *cand, int m, int k,
+                                            uint32_t tlo, int lane, int id_first, int32_t *out)
+{
+    uint32_t ck[CR];  // candidate 64 i + lane; 0 past m
+    uint32_t cmax = 0u;
+#pragma unroll
+    for (int i = 0; i < CR; ++i) {
+        const int g = kWave * i + lane;
+        const uint32_t v = cand[min(g, m - 1)].x;
+        ck[i] = g < m ? v : 0u;
+        cmax = max(cmax, ck[i]);
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) cmax = max(cmax, uint32_t(__shfl_xor(int(cmax), off)));
+    cmax = uint32_t(__builtin_amdgcn_readfirstlane(int(cmax)));
+    // tlo <= the k-th largest key <= cmax: the search starts below their common prefix.
+    uint32_t T;
+    int top;
+    topk_start(cmax, tlo, T, top);
+    bool exact = false;
+    for (int b = top; b >= 0; --b) {
+        const uint32_t cand = T | (1u << b);
+        const int c = topk_count_ge<CR>(ck, cand);
+        if (c >= k) T = cand;
+        if (c == k) {
+            exact = true;
+            break;
+        }
+    }
+    const int n_gt = exact ? k : (T == 0xffffffffu ? 0 : topk_count_ge<CR>(ck, T + 1));
+    const int krem = k - n_gt;
+    int obase = 0, eq_seen = 0;
+#pragma unroll
+    for (int i = 0; i < CR; ++i) {
+        if (kWave * i >= m) break;  // uniform
+        const int g = kWave * i + lane;
+        const bool valid = g < m;
+        const int col = int(cand[min(g, m - 1)].y);
+        const bool gt = valid && (exact ? ck[i] >= T : ck[i] > T);
+        const bool eq = valid && !exact && ck[i] == T;
+        const uint64_t eq_mask = wave_mask(eq);
+        const int eq_before = below_count(eq_mask, 0);
+        const bool sel = gt || (eq && eq_seen + eq_before < krem);
+        const uint64_t sel_mask = wave_mask(sel);
+        const int pos = below_count(sel_mask, obase);
+        if (sel && pos < k) out[pos] = id_first + col;  // exactly k are selected; the bound is a guard
+        obase += __popcll(sel_mask);
+        eq_seen += __popcll(eq_mask);
+    }
+}
+
 constexpr int kTopkMaxWaves = 8;
+constexpr int kTopkCand = 1024;  // candidate slots of the sampled path (16 per lane of one wave)
 
 // Rows of up to 64 PL W columns: one workgroup of W = blockDim.x / 64 waves per
-// row, wave w holding columns [64 PL w, 64 PL (w + 1)). Counts are summed
-// across the waves through LDS, one barrier per search step (two buffers
-// alternate, so a buffer is rewritten only after every wave has passed the
-// barrier that follows its reads). Every branch taken on a count is uniform
-// over the workgroup.
+// row, wave w holding columns [64 PL w, 64 PL (w + 1)).
+//
+// Sampled path (taken when it applies): a full-row bitwise search costs one
+// workgroup barrier and a count of every key per bit, and the kernel's time
+// follows the instructions it issues. So first a threshold t is taken from a
+// sample of 64 W keys (four registers of every wave, so the sample spans the
+// row): the r-th largest sample, with r above the sample's expected count of
+// keys >= the k-th largest by 2.5 standard deviations plus one. Then one
+// count of the keys >= t over the row; if there are m with k <= m <= 1,024
+// (else the full search below runs), the k-th largest key is among them: they
+// are compacted in column order into LDS and one wave finishes the exact
+// search and the ordered selection on them alone. The sample only decides how
+// much work is left, never the result.
+//
+// Full search: counts are summed across the waves through LDS, one barrier per
+// search step (two buffers alternate, so a buffer is rewritten only after every
+// wave has passed the barrier that follows its reads). Every branch taken on a
+// count is uniform over the workgroup.
 template <int PL>
 __global__ __launch_bounds__(kWave * kTopkMaxWaves) void topk_wide_kernel(
     const float *__restrict__ scores, int n_rows, int row_len, int col_first, int n_cols, int k,
     int id_first, int32_t *__restrict__ keep, int keep_stride, int keep_first)
 {
+    static_assert(PL % 4 == 0, "the sample takes four registers per wave");
     __shared__ int xs[2][kTopkMaxWaves];
     __shared__ uint32_t xmax[kTopkMaxWaves], xmin[kTopkMaxWaves];
+    __shared__ uint32_t samp[kTopkMaxWaves * kWave];
+    __shared__ uint2 cand[kTopkCand + kWave];  // (key, column); the last 64: discarded stores
+    __shared__ uint32_t s_tlo;
     const int W = blockDim.x / kWave;
     const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int row = blockIdx.x;
@@ -550,19 +649,6 @@ __global__ __launch_bounds__(kWave * kTopkMaxWaves) void topk_wide_kernel(
     const int c0 = w * PL * kWave;
     uint32_t key[PL];
     topk_load<PL>(s, c0, n_cols, lane, key);
-    uint32_t kmax, kmin, T;
-    int top;
-    topk_range<PL>(key, c0, n_cols, lane, kmax, kmin);
-    if (lane == 0) {
-        xmax[w] = kmax;
-        xmin[w] = kmin;
-    }
-    __syncthreads();
-    for (int i = 0; i < W; ++i) {
-        kmax = max(kmax, xmax[i]);
-        kmin = min(kmin, xmin[i]);
-    }
-    topk_start(kmax, kmin, T, top);
     // Publishes this wave's value v and returns the values' sum over the
     // waves before this one (before) and over all waves.
     int par = 0;
@@ -580,6 +666,90 @@ __global__ __launch_bounds__(kWave * kTopkMaxWaves) void topk_wide_kernel(
         return all;
     };
     int before;
+
+    // ---- Sampled path.
+    {
+        // Lane l offers register (l % 4) PL / 4: columns from all four quarters of the slice.
+        const int qr = lane & 3;
+        uint32_t sv = key[0];
+        sv = qr == 1 ? key[PL / 4] : sv;
+        sv = qr == 2 ? key[PL / 2] : sv;
+        sv = qr == 3 ? key[3 * PL / 4] : sv;
+        samp[w * kWave + lane] = sv;  // 0 past the row: never counted
+    }
+    __syncthreads();
+    if (w == 0) {
+        uint32_t sk[kTopkMaxWaves];
+        int ns = 0;
+#pragma unroll
+        for (int i = 0; i < kTopkMaxWaves; ++i) {
+            const uint32_t v = samp[min(i, W - 1) * kWave + lane];
+            sk[i] = i < W ? v : 0u;
+            ns += __popcll(wave_mask(sk[i] != 0u));
+        }
+        const float mu = float(k) * float(ns) / float(n_cols);
+        const int r = int(ceilf(mu + 2.5f * sqrtf(mu))) + 1;
+        uint32_t t = 0u;  // 0: no threshold (the full search runs)
+        if (r < ns) {
+            // Only the registers that hold samples are searched.
+            if (W <= 2) {
+                const uint32_t s2[2] = {sk[0], sk[1]};
+                t = topk_sample_threshold<2>(s2, r);
+            } else if (W <= 4) {
+                const uint32_t s4[4] = {sk[0], sk[1], sk[2], sk[3]};
+                t = topk_sample_threshold<4>(s4, r);
+            } else {
+                t = topk_sample_threshold<kTopkMaxWaves>(sk, r);
+            }
+        }
+        if (lane == 0) s_tlo = t;
+    }
+    __syncthreads();
+    const uint32_t tlo = uint32_t(__builtin_amdgcn_readfirstlane(int(s_tlo)));
+    if (tlo != 0u) {
+        const int m = __builtin_amdgcn_readfirstlane(exchange(topk_count_ge<PL>(key, tlo), before));
+        if (m >= k && m <= kTopkCand) {  // uniform over the workgroup
+            // Every key >= tlo, in column order (slots past the row hold 0 < tlo).
+            // Every lane stores (no branch around the store): the unselected
+            // ones into a slot of their own past the candidates.
+            int base = __builtin_amdgcn_readfirstlane(before);
+#pragma unroll
+            for (int e = 0; e < PL; ++e) {
+                const uint64_t msk = __builtin_amdgcn_uicmp(key[e], tlo, 35);  // 35: unsigned >=
+                const bool sel = key[e] >= tlo;
+                const int pos = below_count(msk, base);
+                cand[sel ? pos : kTopkCand + lane] = make_uint2(key[e], uint32_t(c0 + kWave * e + lane));
+                base += __popcll(msk);
+            }
+            __syncthreads();
+            if (w != 0) return;
+            // Registers for the candidates actually present (a uniform choice).
+            if (m <= 4 * kWave)
+                topk_finish<4>(cand, m, k, tlo, lane, id_first, out);
+            else if (m <= 8 * kWave)
+                topk_finish<8>(cand, m, k, tlo, lane, id_first, out);
+            else if (m <= 12 * kWave)
+                topk_finish<12>(cand, m, k, tlo, lane, id_first, out);
+            else
+                topk_finish<kTopkCand / kWave>(cand, m, k, tlo, lane, id_first, out);
+            return;
+        }
+    }
+
+    // ---- Full search.
+    uint32_t kmax, kmin, T;
+    int top;
+    topk_range<PL>(key, c0, n_cols, lane, kmax, kmin);
+    if (lane == 0) {
+        xmax[w] = kmax;
+        xmin[w] = kmin;
+    }
+    __syncthreads();
+    for (int i = 0; i < W; ++i) {
+        kmax = max(kmax, xmax[i]);
+        kmin = min(kmin, xmin[i]);
+    }
+    topk_start(kmax, kmin, T, top);
     bool exact = false;
     for (int b = top; b >= 0; --b) {
         const uint32_t cand = T | (1u << b);
@@ -672,7 +842,7 @@ __global__ __launch_bounds__(256) void topk_radix_kernel(const float *__restrict
                 above += c[b];
             }
         }
-        const uint64_t who = __ballot(mine);
+        const uint64_t who = wave_mask(mine);
         const int src = who ? __ffsll((unsigned long long)who) - 1 : 0;
         digit = __shfl(digit, src);
         above = __shfl(above, src);
@@ -695,11 +865,11 @@ __global__ __launch_bounds__(256) void topk_radix_kernel(const float *__restrict
             const bool valid = j < n_cols;
             const bool gt = valid && kb[u] > prefix;
             const bool eq = valid && kb[u] == prefix;
-            const uint64_t eq_mask = __ballot(eq);
-            const int eq_before = __popcll(eq_mask & lanes_below(lane));
+            const uint64_t eq_mask = wave_mask(eq);
+            const int eq_before = below_count(eq_mask, 0);
             const bool sel = gt || (eq && eq_seen + eq_before < krem);
-            const uint64_t sel_mask = __ballot(sel);
-            const int pos = base + __popcll(sel_mask & lanes_below(lane));
+            const uint64_t sel_mask = wave_mask(sel);
+            const int pos = below_count(sel_mask, base);
             if (sel && pos < k) out[pos] = id_first + j;  // exactly k are selected; the bound is a guard
             base += __popcll(sel_mask);
             eq_seen += __popcll(eq_mask);
