@@ -21,10 +21,16 @@ pytestmark = [pytest.mark.gpu,
 # (grid, keep_k): n_v = 2,080 / 3,500 / 5,544 / 6,300 / 8,464 video tiles of 4x4x4
 # take the multi-wave kernel with 2 / 3 / 4 / 5 / 6 waves of 24 keys per lane;
 # 16,900 is past it (radix select). keep_k spans 1, n_v - 1 and 1-25 %.
+# Paths of the multi-wave kernel: a sampled threshold with the candidates
+# compacted into LDS when k <= m <= 1,024 keys pass it (w3, w4, w6, and the
+# tied w4: m is the top classes' size), else the full search: k = n_v - 1
+# leaves no sample rank above the expected count (w5); 25 % of 5,544 keys
+# always passes more than 1,024 (w4q); at 25 % of 2,080 (w2) rows go either way.
 CASES = {
     "w2": ((4, 160, 208), 520),
     "w3": ((4, 200, 280), 35),
     "w4": ((4, 264, 336), 277),
+    "w4q": ((4, 264, 336), 1386),
     "w5": ((4, 280, 360), 6299),
     "w6": ((4, 368, 368), 1),
     "radix": ((4, 520, 520), 845),
