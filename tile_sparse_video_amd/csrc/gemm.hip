@@ -11,8 +11,9 @@
 // fp32. 64-wide k-slices of both operands alternate between two LDS stages
 // (128 KB) filled by buffer-to-LDS loads: the data never passes through VGPRs
 // and no LDS store instructions are issued. The loads of slice ks + 1 are
-// spread over the four 16-wide k-steps of slice ks, a quarter before each
-// step's products, so they never hold up the matrix-core issue. A staged row
+// spread over the four 16-wide k-steps of slice ks, a quarter in each step,
+// placed one after each product together with the next step's fragment reads,
+// so they never hold up the matrix-core issue. A staged row
 // is 128 bytes (eight 16-byte chunks); chunk c of row r sits in slot
 // c ^ ((r ^ (r >> 3)) & 7), so that one load instruction still covers eight
 // whole rows (coalesced) while the MFMA fragment reads (32 rows, one chunk)
@@ -129,15 +130,37 @@ __global__ __launch_bounds__(256, 1) void gate_gemm_kernel(const uint16_t *__res
         load_frags(st, 0, af[0], bf[0]);
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
-            if (kc + 1 < 4) load_frags(st, kc + 1, af[(kc + 1) & 1], bf[(kc + 1) & 1]);
-            if (ks + 1 < nk) issue(ks + 1, (ks + 1) % NS, kc);  // into the stage of slice ks - 1, consumed
             __builtin_amdgcn_sched_barrier(0);
+            if (kc + 1 < 4) load_frags(st, kc + 1, af[(kc + 1) & 1], bf[(kc + 1) & 1]);
+            // Into the stage of slice ks - 1, consumed. The last slice loads
+            // itself again (in bounds, never read): no branch, so the loads
+            // can be scheduled among the products.
+            issue(min(ks + 1, nk - 1), (ks + 1) % NS, kc);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[kc & 1][j], af[kc & 1][i],
                                                                         acc[i][j], 0, 0, 0);
+            // One fragment read, then one buffer-to-LDS load, after each
+            // product, so the matrix core is not left idle while a block of
+            // loads issues (+2 %).
+            if (kc + 1 < 4) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global read
+            }
+            if (kc + 1 < 4)
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            else
+                __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);         // this slice's LDS reads are done
