@@ -364,18 +364,18 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
         return __builtin_amdgcn_readfirstlane(list_lds[v / HPU]);
     };
     // Half v covers rows 32*(v % 2) .. +31 of 64-row block (v % HPU) / 2 of its tile.
-    auto half_base = [&](int v) -> uint32_t {
-        const uint32_t t = entry(v) & 0x1ffffffu;
+    auto half_base = [&](int v, uint32_t e) -> uint32_t {  // e = entry(v)
+        const uint32_t t = e & 0x1ffffffu;
         return (t * SUB + uint32_t((v % HPU) >> 1)) * FR * 1024u;
     };
     // INT8 codes: a 64-row block is 2 * D/32 fragments of 1 KB (half the bf16 size).
-    auto load_k = [&](int v, u32x4_t (&Kb)[KN]) {
-        const uint32_t base = (I8 ? half_base(v) / 2 : half_base(v)) + uint32_t(v & 1) * KN * 1024u;
+    auto load_k = [&](int v, uint32_t e, u32x4_t (&Kb)[KN]) {
+        const uint32_t base = (I8 ? half_base(v, e) / 2 : half_base(v, e)) + uint32_t(v & 1) * KN * 1024u;
 #pragma unroll
         for (int c = 0; c < KN; ++c) Kb[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, vlane, base + c * 1024u, 0);
     };
-    auto load_v = [&](int v, u32x4_t (&Vb)[2 * DB]) {
-        const uint32_t base = half_base(v) + uint32_t(v & 1) * 2 * 1024u;
+    auto load_v = [&](int v, uint32_t e, u32x4_t (&Vb)[2 * DB]) {
+        const uint32_t base = half_base(v, e) + uint32_t(v & 1) * 2 * 1024u;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -398,9 +398,12 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
     // issued. The body is straight-line on purpose: halves with no real key are
     // masked rather than skipped, and the last refill re-reads a valid half, so
     // the K/V registers never merge values from different control paths.
-    auto step = [&](int v, int n_half, u32x4_t (&Kb)[KN], u32x4_t (&Vb)[2 * DB]) {
-        const int real = min(32, int(entry(v) >> 25) + 1 - 32 * (v % HPU));
+    auto step = [&](int v, int n_half, uint32_t ecur, u32x4_t (&Kb)[KN], u32x4_t (&Vb)[2 * DB]) -> uint32_t {
+        const int real = min(32, int(ecur >> 25) + 1 - 32 * (v % HPU));
         const int next = v + 1 < n_half ? v + 1 : v;
+        // The next half's list entry is read here and handed to the next step,
+        // so no step opens with an LDS round trip before its Q reads (-1.5 %).
+        const uint32_t enext = entry(next);
         // INT8: score = (integer product) * qk with qk = s_q * s_k of the two
         // blocks; the exponent folds qk into c2. Clamping qk and c2 * qk to the
         // least normal keeps masked keys at -inf (an all-zero block gives
@@ -442,7 +445,7 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) S[e] = float(Si[e]);
             }
-            if (qb == 1) load_k(next, Kb);
+            if (qb == 1) load_k(next, enext, Kb);
             // Padding keys (partial tiles only: a wave-uniform branch) never score.
             if (__builtin_expect(real < 32, 0)) {
 #pragma unroll
@@ -503,7 +506,8 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
                 O[db][qb] = acc;
             }
         }
-        load_v(next, Vb);
+        load_v(next, enext, Vb);
+        return enext;
     };
 
     u32x4_t Kb[KN], Vb[2 * DB];
@@ -511,9 +515,10 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
         const int count = fill();
         if (count > 0) {
             const int n_half = count * HPU;
-            load_k(0, Kb);
-            load_v(0, Vb);
-            for (int v = 0; v < n_half; ++v) step(v, n_half, Kb, Vb);
+            uint32_t e = entry(0);
+            load_k(0, e, Kb);
+            load_v(0, e, Vb);
+            for (int v = 0; v < n_half; ++v) e = step(v, n_half, e, Kb, Vb);
         }
         if (scan >= n_list) break;
         __syncthreads();  // every lane has read the list before it is refilled
