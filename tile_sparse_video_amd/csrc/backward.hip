@@ -528,12 +528,18 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
             __syncthreads();
             const int n_half = count * HPU;
             auto ent = [&](int v) { return __builtin_amdgcn_readfirstlane(list_lds[v / HPU]); };
-            if (n_half > 0) fetch(0, ent(0), regA);
+            // Halves v (even) and v + 1 lie in one tile, so they share an entry;
+            // the next tile's entry is read before this pair's products, so no
+            // half waits on an LDS round trip.
+            uint32_t e = n_half > 0 ? ent(0) : 0u;
+            if (n_half > 0) fetch(0, e, regA);
             for (int v = 0; v < n_half; v += 2) {
-                fetch(v + 1, ent(v + 1), regB);
-                body(v, ent(v), regA);
-                if (v + 2 < n_half) fetch(v + 2, ent(v + 2), regA);
-                body(v + 1, ent(v + 1), regB);
+                fetch(v + 1, e, regB);
+                const uint32_t e2 = ent(min(v + 2, n_half - 1));
+                body(v, e, regA);
+                if (v + 2 < n_half) fetch(v + 2, e2, regA);
+                body(v + 1, e, regB);
+                e = e2;
             }
             if (scan >= n_list) break;
             __syncthreads();
