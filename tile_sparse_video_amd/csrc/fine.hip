@@ -72,7 +72,7 @@ struct FineArgs {
     const float *o_coarse;      // [H][n_t][D]
     const uint16_t *gate;       // [S][H*D]
     uint16_t *out;              // [S][H][D]
-    uint16_t *part_o;           // split: [items][C][DB][2][64][16] bf16 O / l
+    uint16_t *part_o;           // split: [items][C][DB][2][2][64][8] bf16 O / l
     float *part_ml;             // split: [items][C][2 (m, l)][2][32]
     int H, P, n_v, n_t, k, chunks;
     int ld;                     // heads per token row of q, gate, out and dout (>= H)
@@ -541,9 +541,11 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
                     const bf16x2_t pp = {(__bf16)(O[db][qb][e] * inv[qb]), (__bf16)(O[db][qb][e + 1] * inv[qb])};
                     w[e / 8][(e % 8) / 2] = __builtin_bit_cast(uint32_t, pp);
                 }
-                u32x4_t *dst = reinterpret_cast<u32x4_t *>(po + ((db * 2 + qb) * 64 + lane) * 16);
-                dst[0] = w[0];
-                dst[1] = w[1];
+                // Each 16-byte half of the lane's 32 bytes goes to its own 1 KB run
+                // (lane-contiguous stores and, in the merge, loads).
+#pragma unroll
+                for (int h8 = 0; h8 < 2; ++h8)
+                    *reinterpret_cast<u32x4_t *>(po + (((db * 2 + qb) * 2 + h8) * 64 + lane) * 8) = w[h8];
             }
         if (lane < 32) {
             float *pml = a.part_ml + pidx * 128;
@@ -636,10 +638,9 @@ __global__ __launch_bounds__(256) void merge_kernel(FineArgs a, int n_items)
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                const u32x4_t *src = reinterpret_cast<const u32x4_t *>(po + ((db * 2 + qb) * 64 + lane) * 16);
 #pragma unroll
                 for (int h8 = 0; h8 < 2; ++h8) {
-                    const u32x4_t v = src[h8];
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(po + (((db * 2 + qb) * 2 + h8) * 64 + lane) * 8);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         O[db][qb][8 * h8 + 2 * q] += w[qb] * __uint_as_float(v[q] << 16);
