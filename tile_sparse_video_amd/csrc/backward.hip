@@ -439,8 +439,8 @@ struct BwdArgs {
     float *lse;                     // [H][S_pad], log2 domain (+inf on padding rows)
     const float *dqm, *dkm, *dvm;   // [H][n_t][D]
     float *dq, *dk, *dv;            // natural [S][H][D]
-    float *part_dq;                 // split dq: [items][8][D/32][2][64][16] fp32
-    float *part_dkv;                // split dk/dv: [H][n_t][8][B/32][2][D/32][64][16] fp32
+    float *part_dq;                 // split dq: [items][8][D/32][2][4][64][4] fp32
+    float *part_dkv;                // split dk/dv: [H][n_t][8][B/32][2][D/32][4][64][4] fp32
     int H, P, n_v, n_t, k, ref, list_len;
     float scale, scale_log2e;
 };
@@ -721,16 +721,17 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
     }
 
     if (SPLIT) {
-        // partial dQ^T of this chunk, fp32 in register order: [item][8][DB][2][64][16]
+        // partial dQ^T of this chunk, fp32: [item][8][DB][2][4][64][4], register
+        // group q4 of every lane in one lane-contiguous 1 KB run.
         float *pd = a.part_dq + (size_t(item) * 8 + chunk) * (DB * 2 * kWave * 16);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                float4 *dst = reinterpret_cast<float4 *>(pd + ((db * 2 + qb) * kWave + lane) * 16);
+                float4 *dst = reinterpret_cast<float4 *>(pd + (db * 2 + qb) * kWave * 16);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
-                    dst[q4] = make_float4(G[db][qb][4 * q4], G[db][qb][4 * q4 + 1], G[db][qb][4 * q4 + 2],
+                    dst[q4 * kWave + lane] = make_float4(G[db][qb][4 * q4], G[db][qb][4 * q4 + 1], G[db][qb][4 * q4 + 2],
                                           G[db][qb][4 * q4 + 3]);
             }
         return;
@@ -783,10 +784,10 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdArgs a, int n_items)
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const float4 *src = reinterpret_cast<const float4 *>(
-            a.part_dq + (size_t(item) * 8 + c) * (DB * 2 * kWave * 16) + ((db * 2 + qb) * kWave + lane) * 16);
+            a.part_dq + (size_t(item) * 8 + c) * (DB * 2 * kWave * 16) + (db * 2 + qb) * kWave * 16);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 v = src[q4];
+            const float4 v = src[q4 * kWave + lane];
             acc[4 * q4] += v.x;
             acc[4 * q4 + 1] += v.y;
             acc[4 * q4 + 2] += v.z;
@@ -1209,16 +1210,17 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
             step(b + 1, Sb, dPb, Sa, dPa);
         }
     }
-    // partial dK^T, dV^T, fp32 in register order: [H][n_t][8][KB][2][DB][64][16]
+    // partial dK^T, dV^T, fp32: [H][n_t][8][KB][2][DB][4][64][4], register group
+    // q4 of every lane in one lane-contiguous 1 KB run.
     float *pd = a.part_dkv + ((size_t(ht) * 8 + chunk) * KB + kb) * (2 * DB * kWave * 16);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-        float4 *dk4 = reinterpret_cast<float4 *>(pd + (db * kWave + lane) * 16);
-        float4 *dv4 = reinterpret_cast<float4 *>(pd + ((DB + db) * kWave + lane) * 16);
+        float4 *dk4 = reinterpret_cast<float4 *>(pd + db * kWave * 16);
+        float4 *dv4 = reinterpret_cast<float4 *>(pd + (DB + db) * kWave * 16);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            dk4[q4] = make_float4(GK[db][4 * q4], GK[db][4 * q4 + 1], GK[db][4 * q4 + 2], GK[db][4 * q4 + 3]);
-            dv4[q4] = make_float4(GV[db][4 * q4], GV[db][4 * q4 + 1], GV[db][4 * q4 + 2], GV[db][4 * q4 + 3]);
+            dk4[q4 * kWave + lane] = make_float4(GK[db][4 * q4], GK[db][4 * q4 + 1], GK[db][4 * q4 + 2], GK[db][4 * q4 + 3]);
+            dv4[q4 * kWave + lane] = make_float4(GV[db][4 * q4], GV[db][4 * q4 + 1], GV[db][4 * q4 + 2], GV[db][4 * q4 + 3]);
         }
     }
 }
@@ -1259,10 +1261,10 @@ __global__ __launch_bounds__(256) void dkdv_merge_kernel(BwdArgs a, int n_units)
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const float4 *src = reinterpret_cast<const float4 *>(
-            a.part_dkv + ((size_t(ht) * 8 + c) * KB + kb) * (2 * DB * kWave * 16) + ((kv * DB + db) * kWave + lane) * 16);
+            a.part_dkv + ((size_t(ht) * 8 + c) * KB + kb) * (2 * DB * kWave * 16) + (kv * DB + db) * kWave * 16);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 v = src[q4];
+            const float4 v = src[q4 * kWave + lane];
             acc[4 * q4] += v.x;
             acc[4 * q4 + 1] += v.y;
             acc[4 * q4 + 2] += v.z;
