@@ -476,17 +476,35 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
     int tok[2];
     float dq_row[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int row = tile * B + 64 * qsub + 32 * qb + l32;
-        tok[qb] = a.row_src[row];
-        const size_t base = (size_t(tok[qb] < 0 ? 0 : tok[qb]) * a.H + h) * D + 8 * half;
+    for (int qb = 0; qb < 2; ++qb) tok[qb] = a.row_src[tile * B + 64 * qsub + 32 * qb + l32];
+    // The block's 64 Q and dO rows, D / 8 lanes per row (16 bytes each, so a
+    // load covers whole rows), stored to their fragment slots: piece p of row
+    // r is chunk p / 2, slot half p % 2, column r % 32 of block r / 32.
+    {
+        constexpr int PPR = D / 8, RPI = kWave / PPR, NG = 64 / RPI;
+        const int pr = lane / PPR, pp = lane % PPR;
+        size_t rbase[NG];
+        bool real[NG];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            bf16x8_t vq = *reinterpret_cast<const bf16x8_t *>(a.q + base + 16 * c);
-            bf16x8_t vo = *reinterpret_cast<const bf16x8_t *>(a.dout + base + 16 * c);
-            if (tok[qb] < 0) vq = vo = bf16x8_t{};
-            q_lds[qb][c][lane] = vq;
-            o_lds[qb][c][lane] = vo;
+        for (int g = 0; g < NG; ++g) {
+            const int tk = a.row_src[tile * B + 64 * qsub + RPI * g + pr];
+            real[g] = tk >= 0;
+            rbase[g] = (size_t(tk < 0 ? 0 : tk) * a.H + h) * D + 8 * pp;
+        }
+#pragma unroll
+        for (int src = 0; src < 2; ++src) {
+            const uint16_t *p = src == 0 ? a.q : a.dout;
+            bf16x8_t v[NG];
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(p + rbase[g]);
+                v[g] = real[g] ? x : bf16x8_t{};
+            }
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int r = RPI * g + pr;
+                (src == 0 ? q_lds : o_lds)[r >> 5][pp >> 1][(pp & 1) * 32 + (r & 31)] = v[g];
+            }
         }
     }
     const int32_t *keep_row = a.ref ? a.keep + (size_t(h) * a.n_t + tile) * a.list_len

@@ -210,15 +210,23 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
     float sq = 0.f;  // INT8: the scale of this 64-row query block
     if constexpr (!I8) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            tok[qb] = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
-            const uint16_t *qrow = a.q + (size_t(tok[qb] < 0 ? 0 : tok[qb]) * a.ld + h) * D + 8 * half;
+        for (int qb = 0; qb < 2; ++qb) tok[qb] = a.row_src[size_t(tile) * B + 64 * qsub + 32 * qb + l32];
+        // The block's 64 Q rows, D / 8 lanes per row (16 bytes each, so a load
+        // covers whole rows), then stored to their fragment slots: piece p of
+        // row r is chunk p / 2, slot half p % 2, column r % 32 of block r / 32.
+        constexpr int PPR = D / 8, RPI = kWave / PPR, NG = 64 / RPI;
+        const int pr = lane / PPR, pp = lane % PPR;
+        bf16x8_t qv[NG];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                bf16x8_t v = load_frag(qrow + 16 * c);
-                if (tok[qb] < 0) v = bf16x8_t{};
-                q_lds[qb][c][lane] = v;
-            }
+        for (int g = 0; g < NG; ++g) {
+            const int tk = a.row_src[size_t(tile) * B + 64 * qsub + RPI * g + pr];
+            const bf16x8_t v = load_frag(a.q + (size_t(tk < 0 ? 0 : tk) * a.ld + h) * D + 8 * pp);
+            qv[g] = tk < 0 ? bf16x8_t{} : v;
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const int r = RPI * g + pr;
+            q_lds[r >> 5][pp >> 1][(pp & 1) * 32 + (r & 31)] = qv[g];
         }
     } else {
         // INT8 B operand: lane -> query 32qb + l32, code slot e of chunk c ->
