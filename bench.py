@@ -41,8 +41,8 @@ INT8_PEAK_TOPS = 5033.2     # MI355X dense int8 MFMA (vendor figure)
 # flops (P.V) at the bf16 peak, so 4D operations take 2D/INT8 + 2D/BF16 at best.
 MIXED_PEAK_TOPS = 2.0 / (1.0 / INT8_PEAK_TOPS + 1.0 / BF16_PEAK_TFLOPS)
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X fp32 matrix (vendor figure)
-# fp32 FMA on the vector ALUs without packed (two-wide) instructions, which this build leaves
-# off: 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz.
+# fp32 FMA on the vector ALUs without packed (two-wide) instructions, which the library is
+# compiled without: 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz.
 FP32_VALU_FMA_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 
 
@@ -338,8 +338,8 @@ def main() -> int:
         print("--int8 times the forward only; the backward pass is bf16", file=sys.stderr)
         return 2
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the layer shards by head with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the library runs "
+              "on one GPU (the layer would shard by head with no exchange)", file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

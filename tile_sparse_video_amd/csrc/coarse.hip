@@ -34,21 +34,21 @@ namespace vsa {
 int check_device()
 {
     static std::mutex mu;
-    static int verdict[64];  // 0 unknown, 1 ok, -1 not gfx950
+    static int arch_ok[64];  // 0 unknown, 1 gfx950, -1 another architecture
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(VSA_ERR_DEVICE, "hipGetDevice failed");
     if (dev < 0 || dev >= 64) return fail(VSA_ERR_DEVICE, "device ordinal %d out of range", dev);
     std::lock_guard<std::mutex> lock(mu);
-    if (verdict[dev] == 0) {
+    if (arch_ok[dev] == 0) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
             return fail(VSA_ERR_DEVICE, "hipGetDeviceProperties failed");
-        verdict[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
-        if (verdict[dev] < 0)
+        arch_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        if (arch_ok[dev] < 0)
             return fail(VSA_ERR_UNSUPPORTED, "device %d is %s; libvsa is built for gfx950", dev,
                         prop.gcnArchName);
     }
-    if (verdict[dev] < 0) return fail(VSA_ERR_UNSUPPORTED, "device %d is not a gfx950", dev);
+    if (arch_ok[dev] < 0) return fail(VSA_ERR_UNSUPPORTED, "device %d is not a gfx950", dev);
     return VSA_OK;
 }
 
