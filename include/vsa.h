@@ -386,14 +386,15 @@ int vsa_layer_fwd_groups(const vsa_head_group *groups, int32_t n_groups, int32_t
  *
  * vsa_bwd_layout -- scratch regions (device, caller-owned, 256-byte aligned):
  * fragment copies (V / Q / dO rows, K / Q / dO columns), per-row log-sum-exp and D_t,
- * the coarse-path gradients, the transposed key lists ([H][n_t][n_t]), and,
+ * the coarse-path gradients, the transposed key lists ([H][n_t][n_t]) and the
+ * bit matrix they are built from ([H][n_t][ceil(n_t / 32)] words), and,
  * when the forward splits its key lists, fp32 dQ partials of 8 key chunks,
  * fp32 dK / dV partials of 8 query chunks and the fp32 O_fine ([H][S_pad][D],
  * tile order) that vsa_sparse_attn_fwd_train saves.
  */
 typedef struct vsa_bwd_layout {
     size_t vrow, kcol, qcol, docol, qrow, dorow, lse, dt, doc, dqm, dkm, dvm, lsec, dcc, tlist,
-        tcount, part_dq, part_dkv, ofine;
+        tcount, tbits, part_dq, part_dkv, ofine;
     size_t total_bytes;
 } vsa_bwd_layout;
 

@@ -77,7 +77,7 @@ class vsa_head_group(ctypes.Structure):
 class vsa_bwd_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("vrow", "kcol", "qcol", "docol", "qrow", "dorow", "lse", "dt", "doc", "dqm", "dkm",
-                 "dvm", "lsec", "dcc", "tlist", "tcount", "part_dq", "part_dkv", "ofine",
+                 "dvm", "lsec", "dcc", "tlist", "tcount", "tbits", "part_dq", "part_dkv", "ofine",
                  "total_bytes")]
 
 

@@ -386,41 +386,77 @@ __global__ __launch_bounds__(256) void coarse_bwd_cols_kernel(const float *__res
 
 // ----------------------------------------------------------------- tlist --
 //
-// One wavefront per (key tile j, head): scans the query tiles in ascending
-// order and keeps those whose key list holds j (binary search in the sorted
-// keep row), compacting with ballots, so each list is ascending and the
-// result is deterministic.
-__device__ __forceinline__ bool sorted_has(const int32_t *row, int len, int j)
+// The transpose of the key lists, in two passes over a bit matrix
+// bits[h][i][w] (W = ceil(n_t / 32) words per query tile i; bit j set when
+// query tile i's key list holds key tile j):
+//   tbits_kernel: one wavefront per (query tile, head) sets the bits of its
+//     list in an LDS row (prefix key tiles and dense rows as whole-word masks,
+//     kept tiles with LDS atomic ors, which commute) and stores the row;
+//   tlist_kernel: one wavefront per (key tile j, head) reads bit j of every
+//     row (independent loads, eight per lane in flight) and compacts the query
+//     tiles that have it with ballots, in ascending order.
+// Both are exact and deterministic; no step depends on the order of atomics.
+
+// Bits [32 w, 32 w + 32) of the range [0, n) as a word.
+__device__ __forceinline__ uint32_t range_word(int w, int n)
 {
-    int lo = 0, hi = len;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (row[mid] < j) lo = mid + 1;
-        else hi = mid;
-    }
-    return lo < len && row[lo] == j;
+    const int lo = 32 * w, left = n - lo;
+    return left <= 0 ? 0u : left >= 32 ? 0xffffffffu : (1u << left) - 1u;
 }
 
-__global__ __launch_bounds__(256) void tlist_kernel(const int32_t *__restrict__ keep, int ref, int P,
-                                                    int n_v, int n_t, int k, int list_len,
+__global__ __launch_bounds__(256) void tbits_kernel(const int32_t *__restrict__ keep, int ref, int P,
+                                                    int n_v, int n_t, int k, int list_len, int W,
+                                                    uint32_t *__restrict__ bits)
+{
+    extern __shared__ uint32_t rows[];  // [4][W]
+    const int h = blockIdx.y, wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int i = blockIdx.x * 4 + wave;
+    const bool live = i < n_t;  // no early return: the block's barriers stay uniform
+    uint32_t *row = rows + wave * W;
+    const bool dense = !ref && i < P;
+    // Initial words: a dense row holds every key tile; a default-mode row the
+    // prefix key tiles [0, P); a reference-mode row starts empty.
+    for (int w = lane; w < W; w += kWave) row[w] = !live ? 0u : dense ? range_word(w, n_t) : ref ? 0u : range_word(w, P);
+    __syncthreads();
+    if (live && !dense) {
+        const int len = ref ? list_len : k;
+        const int32_t *src = ref ? keep + (size_t(h) * n_t + i) * list_len : keep + (size_t(h) * n_v + (i - P)) * k;
+        for (int s = lane; s < len; s += kWave) {
+            const int j = min(max(src[s], 0), n_t - 1);
+            atomicOr(&row[j >> 5], 1u << (j & 31));
+        }
+    }
+    __syncthreads();
+    if (live)
+        for (int w = lane; w < W; w += kWave) bits[(size_t(h) * n_t + i) * W + w] = row[w];
+}
+
+constexpr int kTlistBatch = 8;  // rows read per lane before their ballots
+
+__global__ __launch_bounds__(256) void tlist_kernel(const uint32_t *__restrict__ bits, int n_t, int W,
                                                     int32_t *__restrict__ tlist,
                                                     int32_t *__restrict__ tcount)
 {
     const int h = blockIdx.y;
     const int j = blockIdx.x * 4 + threadIdx.x / kWave, lane = threadIdx.x % kWave;
     if (j >= n_t) return;
+    const uint32_t *col = bits + size_t(h) * n_t * W + (j >> 5);
+    const uint32_t bit = 1u << (j & 31);
     int32_t *dst = tlist + (size_t(h) * n_t + j) * n_t;
     int count = 0;
-    for (int i0 = 0; i0 < n_t; i0 += kWave) {
-        const int i = i0 + lane;
-        bool has = false;
-        if (i < n_t) {
-            if (ref) has = sorted_has(keep + (size_t(h) * n_t + i) * list_len, list_len, j);
-            else has = i < P || j < P || sorted_has(keep + (size_t(h) * n_v + (i - P)) * k, k, j);
+    for (int i0 = 0; i0 < n_t; i0 += kWave * kTlistBatch) {
+        uint32_t word[kTlistBatch];
+#pragma unroll
+        for (int u = 0; u < kTlistBatch; ++u)  // clamped rows: every load issued, none behind a branch
+            word[u] = col[size_t(min(i0 + kWave * u + lane, n_t - 1)) * W];
+#pragma unroll
+        for (int u = 0; u < kTlistBatch; ++u) {
+            const int i = i0 + kWave * u + lane;
+            const bool has = i < n_t && (word[u] & bit) != 0u;
+            const uint64_t m = __ballot(has);
+            if (has) dst[count + __popcll(m & lanes_below(lane))] = i;
+            count += __popcll(m);
         }
-        const uint64_t m = __ballot(has);
-        if (has) dst[count + __popcll(m & lanes_below(lane))] = i;
-        count += __popcll(m);
     }
     if (lane == 0) tcount[size_t(h) * n_t + j] = count;
 }
@@ -1341,6 +1377,7 @@ void compute_bwd_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_
     L->dcc = take(H * n_t * 4);
     L->tlist = take(H * n_t * n_t * 4);
     L->tcount = take(H * n_t * 4);
+    L->tbits = take(H * n_t * size_t((n_t + 31) / 32) * 4);
     // Split dq partials, only when the forward splits its key lists.
     const size_t items = H * n_t * size_t(info.tile_rows / 64);
     L->part_dq = take(split_chunks(info, head_dim) > 1 ? items * 8 * 64 * D * 4 : 0);
@@ -1430,9 +1467,12 @@ void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, 
     }
     {
         KernelTimer t(K_BWD_TLIST, st);
-        hipLaunchKernelGGL(tlist_kernel, dim3((n_t + 3) / 4, H), dim3(256), 0, st, a.keep, a.ref, a.P,
-                           a.n_v, n_t, a.k, a.list_len, reinterpret_cast<int32_t *>(bw + L.tlist),
-                           reinterpret_cast<int32_t *>(bw + L.tcount));
+        const int W = (n_t + 31) / 32;
+        uint32_t *tb = reinterpret_cast<uint32_t *>(bw + L.tbits);
+        hipLaunchKernelGGL(tbits_kernel, dim3((n_t + 3) / 4, H), dim3(256), size_t(4) * W * 4, st, a.keep,
+                           a.ref, a.P, a.n_v, n_t, a.k, a.list_len, W, tb);
+        hipLaunchKernelGGL(tlist_kernel, dim3((n_t + 3) / 4, H), dim3(256), 0, st, tb, n_t, W,
+                           reinterpret_cast<int32_t *>(bw + L.tlist), reinterpret_cast<int32_t *>(bw + L.tcount));
     }
     const int items = H * n_t * (B / 64);
     if (split) {
