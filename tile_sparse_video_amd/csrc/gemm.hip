@@ -11,9 +11,10 @@
 // fp32. 64-wide k-slices of both operands alternate between two LDS stages
 // (128 KB) filled by buffer-to-LDS loads: the data never passes through VGPRs
 // and no LDS store instructions are issued. The loads of slice ks + 1 are
-// spread over the four 16-wide k-steps of slice ks, a quarter in each step,
-// placed one after each product together with the next step's fragment reads,
-// so they never hold up the matrix-core issue. A staged row
+// spread over the first three 16-wide k-steps of slice ks (half, a quarter, a
+// quarter), placed one after each product together with the next step's
+// fragment reads, so they never hold up the matrix-core issue and have time
+// to land before the slice ends. A staged row
 // is 128 bytes (eight 16-byte chunks); chunk c of row r sits in slot
 // c ^ ((r ^ (r >> 3)) & 7), so that one load instruction still covers eight
 // whole rows (coalesced) while the MFMA fragment reads (32 rows, one chunk)
@@ -132,35 +133,35 @@ __global__ __launch_bounds__(256, 1) void gate_gemm_kernel(const uint16_t *__res
         for (int kc = 0; kc < 4; ++kc) {
             __builtin_amdgcn_sched_barrier(0);
             if (kc + 1 < 4) load_frags(st, kc + 1, af[(kc + 1) & 1], bf[(kc + 1) & 1]);
-            // Into the stage of slice ks - 1, consumed. The last slice loads
-            // itself again (in bounds, never read): no branch, so the loads
-            // can be scheduled among the products.
-            issue(min(ks + 1, nk - 1), (ks + 1) % NS, kc);
+            // The next slice's loads go into the stage of slice ks - 1, consumed:
+            // parts 0 and 1 in the first k-step, 2 and 3 in the second and third,
+            // none in the last, so every part has at least two k-steps to land
+            // before the slice's wait (-4.5 % against one part per step). The
+            // last slice loads itself again (in bounds, never read): no branch,
+            // so the loads can be scheduled among the products.
+            const int nks = min(ks + 1, nk - 1), nst = (ks + 1) % NS;
+            if (kc == 0) {
+                issue(nks, nst, 0);
+                issue(nks, nst, 1);
+            }
+            if (kc == 1) issue(nks, nst, 2);
+            if (kc == 2) issue(nks, nst, 3);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[kc & 1][j], af[kc & 1][i],
                                                                         acc[i][j], 0, 0, 0);
-            // One fragment read, then one buffer-to-LDS load, after each
-            // product, so the matrix core is not left idle while a block of
-            // loads issues (+2 %).
-            if (kc + 1 < 4) {
+            // After each product at most one fragment read and one
+            // buffer-to-LDS load, so the matrix core is not left idle while a
+            // block of loads issues.
+            const int n_vmem = kc == 0 ? 8 : kc < 3 ? 4 : 0;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                }
+            for (int t = 0; t < 16; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+                if (kc < 3 && t < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                if (t < n_vmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // global read
             }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global read
-            }
-            if (kc + 1 < 4)
-                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            else
-                __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);         // this slice's LDS reads are done
