@@ -605,6 +605,7 @@ __device__ __forceinline__ void topk_finish(const uint2 *cand, int m, int k,
 
 constexpr int kTopkMaxWaves = 8;
 constexpr int kTopkCand = 1024;  // candidate slots of the sampled path (16 per lane of one wave)
+constexpr int kIcmpUge = 35;     // the compare-predicate code of unsigned >= (v_cmp_ge_u32)
 
 // Rows of up to 64 PL W columns: one workgroup of W = blockDim.x / 64 waves per
 // row, wave w holding columns [64 PL w, 64 PL (w + 1)).
@@ -715,7 +716,7 @@ __global__ __launch_bounds__(kWave * kTopkMaxWaves) void topk_wide_kernel(
             int base = __builtin_amdgcn_readfirstlane(before);
 #pragma unroll
             for (int e = 0; e < PL; ++e) {
-                const uint64_t msk = __builtin_amdgcn_uicmp(key[e], tlo, 35);  // 35: unsigned >=
+                const uint64_t msk = __builtin_amdgcn_uicmp(key[e], tlo, kIcmpUge);  // the compare's own lane mask
                 const bool sel = key[e] >= tlo;
                 const int pos = below_count(msk, base);
                 cand[sel ? pos : kTopkCand + lane] = make_uint2(key[e], uint32_t(c0 + kWave * e + lane));
