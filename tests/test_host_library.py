@@ -437,3 +437,22 @@ def test_training_forward_rejects_bad_arguments():
     assert lay.total_bytes - lay.ofine >= wl.heads * big.S_pad * wl.head_dim * 4
     small = tsv.vsa_bwd_workspace_layout(info, 2, 128)
     assert small.total_bytes == small.ofine
+
+
+def test_bwd_layout_transposed_list_regions():
+    """The backward workspace holds the transposed key lists ([H][n_t][n_t] int32),
+    their counts, and the bit matrix they are built from ([H][n_t][ceil(n_t / 32)]
+    words), as disjoint 256-byte-aligned regions in that order."""
+    import tile_sparse_video_amd as tsv
+    for name in ("tiny", "h3", "page5"):
+        wl = workloads.WORKLOADS[name]
+        pl = tsv.cached_plan(wl.prefix_segments, wl.grid, wl.tile)
+        n_t = pl.info.n_tiles
+        lay = tsv.vsa_bwd_workspace_layout(pl.info, wl.heads, wl.head_dim)
+        words = (n_t + 31) // 32
+        assert lay.tcount - lay.tlist >= wl.heads * n_t * n_t * 4
+        assert lay.tbits - lay.tcount >= wl.heads * n_t * 4
+        assert lay.part_dq - lay.tbits >= wl.heads * n_t * words * 4
+        assert lay.part_dq - lay.tbits < wl.heads * n_t * words * 4 + 256
+        for off in (lay.tlist, lay.tcount, lay.tbits, lay.part_dq):
+            assert off % 256 == 0
