@@ -71,12 +71,14 @@ __device__ __forceinline__ bf16x8_t pack8(const f32x16_t &a, int cc)
 // f = kb*(D/16) + c holds row 32kb + l32, d = 16c + 8*half + e. ROWS = 0:
 // column layout, fragment f = db*4 + c holds d = 32db + l32, rows 16c +
 // {4h..4h+3, 8+4h..8+4h+3}. The same two layouts the coarse stage writes for K
-// and V.
+// and V. ROWS = 2: both, from one staged tile (dst: row layout, dst_col:
+// column layout), for the tensors the backward needs in both (Q, dO).
 template <int D, int B, int ROWS>
 __global__ __launch_bounds__(256) void frag_gather_kernel(const uint16_t *__restrict__ X,
                                                          const int32_t *__restrict__ row_src,
                                                          const int32_t *__restrict__ block_len,
-                                                         int H, int n_t, uint16_t *__restrict__ dst)
+                                                         int H, int n_t, uint16_t *__restrict__ dst,
+                                                         uint16_t *__restrict__ dst_col = nullptr)
 {
     constexpr int HPB = 256 / D, ROW = HPB * D + 8, CH = HPB * D / 8, FR = D / 8, SUB = B / 64;
     __shared__ __attribute__((aligned(16))) uint16_t lds[B * ROW];
@@ -98,12 +100,14 @@ __global__ __launch_bounds__(256) void frag_gather_kernel(const uint16_t *__rest
         const int lane = idx % kWave, f = (idx / kWave) % FR;
         const int sub = (idx / (kWave * FR)) % SUB, hl = idx / (kWave * FR * SUB);
         const int half = lane / 32, l32 = lane % 32;
-        uint16_t e8[8];
-        if (ROWS) {
+        const size_t frag = ((size_t(h0 + hl) * n_t + tile) * SUB + sub) * FR + f;
+        if (ROWS != 0) {
             const int kb = f / (D / 16), c = f % (D / 16);
             const uint16_t *src = &lds[(64 * sub + 32 * kb + l32) * ROW + hl * D + 16 * c + 8 * half];
-            *reinterpret_cast<uint4 *>(e8) = *reinterpret_cast<const uint4 *>(src);
-        } else {
+            *reinterpret_cast<uint4 *>(dst + frag * 512 + lane * 8) = *reinterpret_cast<const uint4 *>(src);
+        }
+        if (ROWS != 1) {
+            uint16_t e8[8];
             const int db = f / 4, c = f % 4;
             const int col = hl * D + 32 * db + l32, r0 = 64 * sub + 16 * c + 4 * half;
 #pragma unroll
@@ -111,9 +115,9 @@ __global__ __launch_bounds__(256) void frag_gather_kernel(const uint16_t *__rest
                 e8[e] = lds[(r0 + e) * ROW + col];
                 e8[4 + e] = lds[(r0 + 8 + e) * ROW + col];
             }
+            *reinterpret_cast<uint4 *>((ROWS == 2 ? dst_col : dst) + frag * 512 + lane * 8) =
+                *reinterpret_cast<uint4 *>(e8);
         }
-        const size_t frag = ((size_t(h0 + hl) * n_t + tile) * SUB + sub) * FR + f;
-        *reinterpret_cast<uint4 *>(dst + frag * 512 + lane * 8) = *reinterpret_cast<uint4 *>(e8);
     }
 }
 
@@ -1439,14 +1443,13 @@ void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, 
                            H, n_t, reinterpret_cast<uint16_t *>(bw + L.vrow));
         hipLaunchKernelGGL((frag_gather_kernel<D, B, 0>), gg, dim3(256), 0, st, k, a.row_src, a.block_len,
                            H, n_t, reinterpret_cast<uint16_t *>(bw + L.kcol));
-        hipLaunchKernelGGL((frag_gather_kernel<D, B, 0>), gg, dim3(256), 0, st, q, a.row_src, a.block_len,
-                           H, n_t, reinterpret_cast<uint16_t *>(bw + L.qcol));
-        hipLaunchKernelGGL((frag_gather_kernel<D, B, 0>), gg, dim3(256), 0, st, dout, a.row_src,
-                           a.block_len, H, n_t, reinterpret_cast<uint16_t *>(bw + L.docol));
-        hipLaunchKernelGGL((frag_gather_kernel<D, B, 1>), gg, dim3(256), 0, st, q, a.row_src, a.block_len,
-                           H, n_t, reinterpret_cast<uint16_t *>(bw + L.qrow));
-        hipLaunchKernelGGL((frag_gather_kernel<D, B, 1>), gg, dim3(256), 0, st, dout, a.row_src,
-                           a.block_len, H, n_t, reinterpret_cast<uint16_t *>(bw + L.dorow));
+        // Q and dO in both layouts from one read each.
+        hipLaunchKernelGGL((frag_gather_kernel<D, B, 2>), gg, dim3(256), 0, st, q, a.row_src, a.block_len,
+                           H, n_t, reinterpret_cast<uint16_t *>(bw + L.qrow),
+                           reinterpret_cast<uint16_t *>(bw + L.qcol));
+        hipLaunchKernelGGL((frag_gather_kernel<D, B, 2>), gg, dim3(256), 0, st, dout, a.row_src,
+                           a.block_len, H, n_t, reinterpret_cast<uint16_t *>(bw + L.dorow),
+                           reinterpret_cast<uint16_t *>(bw + L.docol));
     }
     auto *doc = reinterpret_cast<float *>(bw + L.doc);
     {
