@@ -19,8 +19,9 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a gfx950 GPU")]
 
 # (grid, keep_k): n_v = 2,080 / 3,500 / 5,544 / 6,300 / 8,464 video tiles of 4x4x4
-# take the multi-wave kernel with 2 / 3 / 4 / 5 / 6 waves of 24 keys per lane;
-# 16,900 is past it (radix select). keep_k spans 1, n_v - 1 and 1-25 %.
+# take the multi-wave kernel with 2 / 3 / 4 / 5 / 6 waves of 24 keys per lane,
+# 12,996 / 15,876 the one with 7 / 8 waves of 32; 16,900 is past it (radix
+# select). keep_k spans 1, n_v - 1 and 1-25 %.
 # Paths of the multi-wave kernel: a sampled threshold with the candidates
 # compacted into LDS when k <= m <= 1,024 keys pass it (w3, w4, w6, and the
 # tied w4: m is the top classes' size), else the full search: k = n_v - 1
@@ -33,6 +34,9 @@ CASES = {
     "w4q": ((4, 264, 336), 1386),
     "w5": ((4, 280, 360), 6299),
     "w6": ((4, 368, 368), 1),
+    # 12,996 and 15,876 columns: 32 keys per lane, 7 and 8 waves (sampled path).
+    "w7p32": ((4, 456, 456), 650),
+    "w8p32": ((4, 504, 504), 397),
     "radix": ((4, 520, 520), 845),
 }
 
