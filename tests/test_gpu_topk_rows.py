@@ -1,5 +1,5 @@
-"""GPU parity of the per-row top-k on long score rows (the multi-wave register
-path up to 16,384 columns, and the radix select beyond), with and without
+"""GPU parity of the per-row top-k on long score rows (the one-wave sampled path,
+the multi-wave register path up to 16,384 columns, and the radix select beyond), with and without
 massive ties. Keep-sets and the scores they come from are compared bit for bit
 with the oracle on sampled rows.
 
@@ -28,6 +28,10 @@ pytestmark = [pytest.mark.gpu,
 # leaves no sample rank above the expected count (w5); 25 % of 5,544 keys
 # always passes more than 1,024 (w4q); at 25 % of 2,080 (w2) rows go either way.
 CASES = {
+    # One wave per row, k a small share of the row: the one-wave sampled path
+    # (1,024 columns, 16 keys per lane; 1,936 columns, 32 keys per lane).
+    "o16": ((4, 128, 128), 60),
+    "o32": ((4, 176, 176), 97),
     "w2": ((4, 160, 208), 520),
     "w3": ((4, 200, 280), 35),
     "w4": ((4, 264, 336), 277),

@@ -492,45 +492,6 @@ __device__ __forceinline__ void topk_select(const uint32_t (&key)[PL], int c0, i
     }
 }
 
-// Rows of up to 64 PL columns: one wavefront per row, four rows per workgroup.
-template <int PL>
-__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ scores, int n_rows,
-                                                   int row_len, int col_first, int n_cols, int k,
-                                                   int id_first, int32_t *__restrict__ keep,
-                                                   int keep_stride, int keep_first)
-{
-    const int lane = threadIdx.x % kWave;
-    const int row = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (row >= n_rows) return;  // wave-uniform
-    const float *s = scores + size_t(row) * row_len + col_first;
-    int32_t *out = keep + size_t(row) * keep_stride + keep_first;
-    if (k == n_cols) {
-        for (int j = lane; j < n_cols; j += kWave) out[j] = id_first + j;
-        return;
-    }
-    if (k == 0) return;
-    uint32_t key[PL];
-    topk_load<PL>(s, 0, n_cols, lane, key);
-    uint32_t kmax, kmin, T;
-    int top;
-    topk_range<PL>(key, 0, n_cols, lane, kmax, kmin);
-    topk_start(kmax, kmin, T, top);
-    bool exact = false;  // exactly k keys are >= T
-    for (int b = top; b >= 0; --b) {
-        const uint32_t cand = T | (1u << b);
-        const int c = topk_count_ge<PL>(key, cand);
-        if (c >= k) T = cand;
-        if (c == k) {
-            exact = true;
-            break;
-        }
-    }
-    // Without an early stop T is the k-th largest key: count(>= T) >= k >
-    // count(>= T + 1); with one, the k keys >= T are the answer.
-    const int n_gt = exact ? k : (T == 0xffffffffu ? 0 : topk_count_ge<PL>(key, T + 1));
-    topk_select<PL>(key, 0, n_cols, lane, T, exact, k - n_gt, 0, 0, k, id_first, out);
-}
-
 // A threshold t >= 1 with at least r of the wave's sample registers sk (0 =
 // no sample) at or above it: the r-th largest sample, or any value at which
 // exactly r samples pass (the search stops there).
@@ -603,9 +564,90 @@ __device__ __forceinline__ void topk_finish(const uint2 *cand, int m, int k,
     }
 }
 
+constexpr int kTopkCand1 = 512;  // candidate slots per row of the one-wave sampled path
+constexpr int kIcmpUge = 35;     // the compare-predicate code of unsigned >= (v_cmp_ge_u32)
+
+// Rows of up to 64 PL columns: one wavefront per row, four rows per workgroup.
+// SAMPLED (chosen on the host when k is a small share of the row): first the
+// sampled path of the multi-wave kernel below, on one wave: a threshold from
+// the 64 keys of four spread registers, the keys at or above it compacted in
+// column order into the wave's own LDS slots (at most 512, else the full
+// search runs) and the exact search and ordered selection on those alone.
+template <int PL, bool SAMPLED>
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ scores, int n_rows,
+                                                   int row_len, int col_first, int n_cols, int k,
+                                                   int id_first, int32_t *__restrict__ keep,
+                                                   int keep_stride, int keep_first)
+{
+    __shared__ uint2 cand_all[SAMPLED ? 4 * (kTopkCand1 + kWave) : 1];  // per wave: candidates, then discards
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    const int row = blockIdx.x * 4 + wv;
+    if (row >= n_rows) return;  // wave-uniform; the block has no barrier
+    const float *s = scores + size_t(row) * row_len + col_first;
+    int32_t *out = keep + size_t(row) * keep_stride + keep_first;
+    if (k == n_cols) {
+        for (int j = lane; j < n_cols; j += kWave) out[j] = id_first + j;
+        return;
+    }
+    if (k == 0) return;
+    uint32_t key[PL];
+    topk_load<PL>(s, 0, n_cols, lane, key);
+    if constexpr (SAMPLED) {
+        static_assert(PL % 4 == 0, "the sample takes four registers");
+        const int qr = lane & 3;
+        uint32_t sv = key[0];
+        sv = qr == 1 ? key[PL / 4] : sv;
+        sv = qr == 2 ? key[PL / 2] : sv;
+        sv = qr == 3 ? key[3 * PL / 4] : sv;
+        const uint32_t s1[1] = {sv};
+        const int ns = __popcll(wave_mask(sv != 0u));
+        const float mu = float(k) * float(ns) / float(n_cols);
+        const int r = int(ceilf(mu + 2.5f * sqrtf(mu))) + 1;
+        if (r < ns) {  // uniform
+            const uint32_t tlo = topk_sample_threshold<1>(s1, r);
+            const int m = topk_count_ge<PL>(key, tlo);
+            if (m >= k && m <= kTopkCand1) {  // uniform
+                uint2 *cand = cand_all + wv * (kTopkCand1 + kWave);
+                int base = 0;
+#pragma unroll
+                for (int e = 0; e < PL; ++e) {
+                    const uint64_t msk = __builtin_amdgcn_uicmp(key[e], tlo, kIcmpUge);
+                    const bool sel = key[e] >= tlo;
+                    const int pos = below_count(msk, base);
+                    cand[sel ? pos : kTopkCand1 + lane] = make_uint2(key[e], uint32_t(kWave * e + lane));
+                    base += __popcll(msk);
+                }
+                // The wave reads back its own LDS stores: ordered by the LDS queue.
+                if (m <= 4 * kWave)
+                    topk_finish<4>(cand, m, k, tlo, lane, id_first, out);
+                else
+                    topk_finish<8>(cand, m, k, tlo, lane, id_first, out);
+                return;
+            }
+        }
+    }
+    uint32_t kmax, kmin, T;
+    int top;
+    topk_range<PL>(key, 0, n_cols, lane, kmax, kmin);
+    topk_start(kmax, kmin, T, top);
+    bool exact = false;  // exactly k keys are >= T
+    for (int b = top; b >= 0; --b) {
+        const uint32_t cand = T | (1u << b);
+        const int c = topk_count_ge<PL>(key, cand);
+        if (c >= k) T = cand;
+        if (c == k) {
+            exact = true;
+            break;
+        }
+    }
+    // Without an early stop T is the k-th largest key: count(>= T) >= k >
+    // count(>= T + 1); with one, the k keys >= T are the answer.
+    const int n_gt = exact ? k : (T == 0xffffffffu ? 0 : topk_count_ge<PL>(key, T + 1));
+    topk_select<PL>(key, 0, n_cols, lane, T, exact, k - n_gt, 0, 0, k, id_first, out);
+}
+
 constexpr int kTopkMaxWaves = 8;
 constexpr int kTopkCand = 1024;  // candidate slots of the sampled path (16 per lane of one wave)
-constexpr int kIcmpUge = 35;     // the compare-predicate code of unsigned >= (v_cmp_ge_u32)
 
 // Rows of up to 64 PL W columns: one workgroup of W = blockDim.x / 64 waves per
 // row, wave w holding columns [64 PL w, 64 PL (w + 1)).
@@ -884,9 +926,23 @@ void launch_topk(const float *scores, int n_rows, int row_len, int col_first, in
 {
     if (n_rows == 0 || n_cols == 0) return;
     KernelTimer t(K_TOPK, st);
-#define VSA_TOPK(PLV)                                                                              \
-    hipLaunchKernelGGL(topk_kernel<PLV>, dim3((n_rows + 3) / 4), dim3(256), 0, st, scores, n_rows, \
-                       row_len, col_first, n_cols, k, id_first, keep, keep_stride, keep_first)
+    // The one-wave sampled path pays when the candidates it expects (the
+    // sample rank it thresholds at, scaled to the row) fit its 512 slots with
+    // room to spare; otherwise the plain search runs.
+    const double mu = 64.0 * k / n_cols;
+    const bool sampled = n_cols >= 8 * kWave && k < n_cols &&
+                         (std::ceil(mu + 2.5 * std::sqrt(mu)) + 1.0) * n_cols / kWave <= 0.8 * kTopkCand1;
+#define VSA_TOPK(PLV)                                                                                  \
+    do {                                                                                               \
+        if (sampled && (PLV) % 4 == 0 && (PLV) >= 8)                                                   \
+            hipLaunchKernelGGL((topk_kernel<PLV, (PLV) % 4 == 0 && (PLV) >= 8>), dim3((n_rows + 3) / 4), \
+                               dim3(256), 0, st, scores, n_rows, row_len, col_first, n_cols, k,        \
+                               id_first, keep, keep_stride, keep_first);                               \
+        else                                                                                           \
+            hipLaunchKernelGGL((topk_kernel<PLV, false>), dim3((n_rows + 3) / 4), dim3(256), 0, st,     \
+                               scores, n_rows, row_len, col_first, n_cols, k, id_first, keep,          \
+                               keep_stride, keep_first);                                               \
+    } while (0)
 #define VSA_TOPK_WIDE(PLV)                                                                         \
     hipLaunchKernelGGL(topk_wide_kernel<PLV>, dim3(n_rows),                                        \
                        dim3(kWave * ((n_cols + kWave * (PLV)-1) / (kWave * (PLV)))), 0, st, scores, \
