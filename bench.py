@@ -220,16 +220,16 @@ def bench_backward(args, wl, tsv, att, qd, kd, vd, xd, wd, g, out, stream, host_
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    tsv.vsa_timing_enable(True)
+    tsv.vsa_timing_enable(True, stream)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    tsv.vsa_timing_enable(False)
+    tsv.vsa_timing_enable(False, stream)
     kernels = {}
     for name in tsv.TIMED_KERNELS:
-        n, ms = tsv.vsa_timing_read(name)
+        n, ms = tsv.vsa_timing_read(name, stream)
         if n:
             kernels[name] = {"launches": n, "avg_ms": round(ms / n, 4)}
     fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
@@ -348,7 +348,6 @@ def main() -> int:
     import tile_sparse_video_amd as tsv
 
     wl = workloads.WORKLOADS[args.workload]
-    tsv.vsa_set_split_chunks(args.split_chunks)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating {wl.name} inputs ({wl.tokens} tokens)", file=sys.stderr, flush=True)
@@ -357,7 +356,8 @@ def main() -> int:
     qd, kd, vd, xd, wd = (t.to(dev) for t in (q, k, v, x, w))
     att = tsv.TileSparseAttention(wl.prefix_segments, wl.grid, wl.tile, wl.heads, wl.head_dim,
                                   sparsity=wl.sparsity, keep_k=wl.keep_k, device=dev,
-                                  reference_sparsity=args.reference_sparsity, int8=args.int8)
+                                  reference_sparsity=args.reference_sparsity, int8=args.int8,
+                                  split_chunks=args.split_chunks)
     g = torch.empty((wl.tokens, wl.heads * wl.head_dim), dtype=torch.bfloat16, device=dev)
     out = torch.empty_like(qd)
     stream = torch.cuda.current_stream()
@@ -386,16 +386,16 @@ def main() -> int:
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    tsv.vsa_timing_enable(True)     # per-kernel events on the library's launch stream
+    tsv.vsa_timing_enable(True, stream)     # per-kernel events on the library's launch stream
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    tsv.vsa_timing_enable(False)
+    tsv.vsa_timing_enable(False, stream)
     kernels = {}
     for name in tsv.TIMED_KERNELS:
-        n, ms = tsv.vsa_timing_read(name)
+        n, ms = tsv.vsa_timing_read(name, stream)
         if n:
             kernels[name] = {"launches": n, "avg_ms": round(ms / n, 4)}
     parts = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)]
@@ -433,7 +433,7 @@ def main() -> int:
             "grid": list(wl.grid), "tile": list(wl.tile), "keep_k": att.k,
             "reference_sparsity": args.reference_sparsity,
             "ref_keep_k": att.k_ref if att.ref else None,
-            "split_chunks": args.split_chunks or "auto",
+            "split_chunks": att.split_chunks,
             "parallelism": "single GPU",
         },
         "ms_per_layer": round(layer_ms, 4),

@@ -160,24 +160,32 @@ int vsa_tile_pair_fraction_ref(const vsa_plan_info *info, int32_t k_ref, int32_t
  *   scores: fp32 coarse scores, [H][n_v][n_v] (video query tile i, video key
  *     tile j) after vsa_coarse_topk, [H][n_t][n_t] (every query tile, every
  *     key tile) after vsa_coarse_topk_ref; sized for the larger.
- *   part_o, part_ml: scratch for the fine pass when it splits each key list
- *     into C chunks (by tile id modulo C; C = 8 for heads whose K and V exceed
- *     16 MiB, 8 * ceil(K+V / 96 MiB) beyond 96 MiB): per chunk, bf16 O / l and
- *     the fp32 running max and sum of every 64 query rows. Zero when C = 1.
  *   k_i8, k_scale: INT8 K codes and fp32 block scales written by
  *     vsa_sparse_attn_fwd_i8 (layout there).
- * The layout depends on the split count, so query it after any
- * vsa_set_split_chunks call.
+ *   part_o, part_ml (last): scratch for the fine pass when it splits each key
+ *     list into C chunks by tile id modulo C: per chunk, bf16 O / l and the
+ *     fp32 running max and sum of every 64 query rows. Empty when C = 1.
+ * Everything before part_o is independent of C; the coarse stage needs only
+ * those `part_o` bytes, the fine stage the whole `total_bytes`.
+ *
+ * split_chunks (here and in every fine / backward entry point): the C a call
+ * uses; 0 = automatic (a function of the plan and head_dim only: 1 while one
+ * head's K and V fit in 16 MiB, else 8 * ceil(K+V / 96 MiB), at most 64),
+ * 1 = never split, 2..64 = that many chunks. It is a tuning choice: the
+ * result depends on it only through fp32 rounding. A workspace serves the
+ * fine calls made with the split count it was laid out for (or a smaller
+ * layout); there is no process-wide setting. VSA_ERR_ARG outside [0, 64].
  */
 typedef struct vsa_ws_layout {
     size_t k_tiled, v_tiled, q_mean, k_mean, v_mean, scores;
-    size_t part_o, part_ml;  /* fine-pass chunk partials (empty when not split) */
     size_t k_i8, k_scale;    /* INT8 fine pass: K codes and block scales */
+    size_t part_o, part_ml;  /* fine-pass chunk partials (empty when not split) */
     size_t total_bytes;
+    int32_t split_chunks;    /* the resolved C of this layout */
 } vsa_ws_layout;
 
 int vsa_workspace_layout(const vsa_plan_info *info, int32_t heads, int32_t head_dim,
-                         vsa_ws_layout *layout);
+                         int32_t split_chunks, vsa_ws_layout *layout);
 
 /* ------------------------------------------------------ coarse pass -- */
 /*
@@ -204,7 +212,7 @@ int vsa_workspace_layout(const vsa_plan_info *info, int32_t heads, int32_t head_
  * heads (H), head_dim (D in {64,128}).
  * sparsity / keep_k: as vsa_keep_count. scale <= 0 means D^-1/2.
  * q, k, v: device bf16 [S][H][D].
- * workspace: device, >= vsa_workspace_layout().total_bytes, 256-byte aligned.
+ * workspace: device, >= vsa_workspace_layout().part_o bytes, 256-byte aligned.
  * keep_idx_dev: out device int32 [H][n_v][k] (may be NULL when k == 0).
  * o_coarse_dev: out device fp32 [H][n_t][D].
  * Errors: VSA_ERR_ARG, VSA_ERR_UNSUPPORTED, VSA_ERR_DEVICE.
@@ -252,8 +260,11 @@ int vsa_coarse_topk_ref(const vsa_plan_info *info, const int32_t *row_src_dev,
  *   out[t][h][:] = bf16_rne(O_fine + g[t][h][:] * o_coarse[h][i][:]).
  *
  * workspace: as filled by vsa_coarse_topk for the same plan, heads, head_dim
- *   and K/V (only k_tiled / v_tiled are read).
+ *   and K/V (k_tiled / v_tiled are read), at least
+ *   vsa_workspace_layout(..., split_chunks).total_bytes long (the chunk
+ *   partials are written when the key lists split).
  * k: keep count used by vsa_coarse_topk; keep_idx_dev: its output.
+ * split_chunks: see the workspace section (0 = automatic).
  * q: device bf16 [S][H][D]. gate: device bf16 [S][H*D] (g, natural order).
  * out: device bf16 [S][H][D]; only real tokens are written.
  * Errors: VSA_ERR_ARG (also: empty key set, i.e. P == 0 and k == 0),
@@ -261,7 +272,7 @@ int vsa_coarse_topk_ref(const vsa_plan_info *info, const int32_t *row_src_dev,
  */
 int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row_src_dev,
                         const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
-                        int32_t k, float scale, const void *q,
+                        int32_t k, float scale, int32_t split_chunks, const void *q,
                         const void *workspace, size_t workspace_bytes,
                         const int32_t *keep_idx_dev, const float *o_coarse_dev,
                         const void *gate, void *out, void *stream);
@@ -276,7 +287,8 @@ int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row_src_dev,
  */
 int vsa_sparse_attn_fwd_ref(const vsa_plan_info *info, const int32_t *row_src_dev,
                             const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
-                            int32_t k_ref, int32_t k_gen, float scale, const void *q,
+                            int32_t k_ref, int32_t k_gen, float scale, int32_t split_chunks,
+                            const void *q,
                             const void *workspace, size_t workspace_bytes,
                             const int32_t *keep_idx_dev, const float *o_coarse_dev,
                             const void *gate, void *out, void *stream);
@@ -305,7 +317,8 @@ int vsa_sparse_attn_fwd_ref(const vsa_plan_info *info, const int32_t *row_src_de
  */
 int vsa_sparse_attn_fwd_i8(const vsa_plan_info *info, const int32_t *row_src_dev,
                            const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
-                           int32_t k_ref, int32_t k_gen, float scale, const void *q,
+                           int32_t k_ref, int32_t k_gen, float scale, int32_t split_chunks,
+                           const void *q,
                            void *workspace, size_t workspace_bytes,
                            const int32_t *keep_idx_dev, const float *o_coarse_dev,
                            const void *gate, void *out, void *stream);
@@ -333,7 +346,9 @@ int vsa_sparse_attn_fwd_i8(const vsa_plan_info *info, const int32_t *row_src_dev
  *   ref, ref_sparsity, ref_keep_k: ref != 0 selects reference sparsity with
  *                        k_ref from vsa_ref_keep_count.
  *   int8                 != 0: the fine pass with INT8 scores (vsa_sparse_attn_fwd_i8).
- *   workspace, workspace_bytes: vsa_workspace_layout(info, heads, head_dim).
+ *   split_chunks         the group's fine-pass split (0 = automatic).
+ *   workspace, workspace_bytes: vsa_workspace_layout(info, heads, head_dim,
+ *                        split_chunks).
  *   keep_idx_dev         int32 [heads][n_v][k] (default) or [heads][n_t][k_ref + k]
  *                        (reference sparsity); may be null when that is empty.
  *   o_coarse_dev         fp32 [heads][n_t][head_dim].
@@ -348,6 +363,7 @@ typedef struct vsa_head_group {
     int32_t ref, int8;
     double ref_sparsity;
     int64_t ref_keep_k;
+    int32_t split_chunks;
     void *workspace;
     size_t workspace_bytes;
     int32_t *keep_idx_dev;
@@ -396,10 +412,13 @@ typedef struct vsa_bwd_layout {
     size_t vrow, kcol, qcol, docol, qrow, dorow, lse, dt, doc, dqm, dkm, dvm, lsec, dcc, tlist,
         tcount, tbits, part_dq, part_dkv, ofine;
     size_t total_bytes;
+    int32_t split_chunks;    /* the resolved forward split of this layout */
 } vsa_bwd_layout;
 
+/* split_chunks: the forward's (as for vsa_workspace_layout); a backward with
+ * C > 1 also splits its dQ and dK/dV passes into 8 XCD-affine chunks. */
 int vsa_bwd_workspace_layout(const vsa_plan_info *info, int32_t heads, int32_t head_dim,
-                             vsa_bwd_layout *layout);
+                             int32_t split_chunks, vsa_bwd_layout *layout);
 
 /*
  * vsa_sparse_attn_bwd -- enqueues the backward pass on `stream`.
@@ -408,7 +427,8 @@ int vsa_bwd_workspace_layout(const vsa_plan_info *info, int32_t heads, int32_t h
  * vsa_coarse_topk_ref). q, k, v, dout: device bf16 [S][H][D]; gate:
  * device bf16 [S][H*D]; workspace / keep_idx / o_coarse: as left by the
  * coarse pass for the same inputs (the tiled K and the tile means are read).
- * bwd_workspace: >= vsa_bwd_workspace_layout().total_bytes.
+ * split_chunks: the forward's split (0 = automatic); the workspaces are laid
+ * out for it. bwd_workspace: >= vsa_bwd_workspace_layout().total_bytes.
  * dq, dk, dv: out device fp32 [S][H][D]; dgate: out device fp32 [S][H*D].
  * saved_stats != 0: bwd_workspace holds the lse and O_fine that
  * vsa_sparse_attn_fwd_train wrote for this same forward (same inputs, keep
@@ -421,8 +441,9 @@ int vsa_bwd_workspace_layout(const vsa_plan_info *info, int32_t heads, int32_t h
  */
 int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row_src_dev,
                         const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
-                        int32_t k_ref, int32_t k_gen, float scale, const void *q, const void *k,
-                        const void *v, const void *gate, const void *dout,
+                        int32_t k_ref, int32_t k_gen, float scale, int32_t split_chunks,
+                        const void *q, const void *k, const void *v, const void *gate,
+                        const void *dout,
                         const void *workspace, size_t workspace_bytes,
                         const int32_t *keep_idx_dev, const float *o_coarse_dev,
                         void *bwd_workspace, size_t bwd_workspace_bytes, float *dq, float *dk,
@@ -441,20 +462,11 @@ int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row_src_dev,
  */
 int vsa_sparse_attn_fwd_train(const vsa_plan_info *info, const int32_t *row_src_dev,
                               const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
-                              int32_t k_ref, int32_t k_gen, float scale, const void *q,
-                              const void *workspace, size_t workspace_bytes,
+                              int32_t k_ref, int32_t k_gen, float scale, int32_t split_chunks,
+                              const void *q, const void *workspace, size_t workspace_bytes,
                               const int32_t *keep_idx_dev, const float *o_coarse_dev,
                               const void *gate, void *out, void *bwd_workspace,
                               size_t bwd_workspace_bytes, void *stream);
-
-/*
- * vsa_set_split_chunks -- tuning override for the fine pass: split every key
- * list into `chunks` parts (1 = never split; 0 = automatic, the default).
- * Process-wide; affects vsa_workspace_layout and vsa_sparse_attn_fwd calls
- * made afterwards. The result does not depend on it beyond fp32 rounding.
- * Errors: VSA_ERR_ARG if chunks is outside [0, 64].
- */
-int vsa_set_split_chunks(int32_t chunks);
 
 /* -------------------------------------------------- gate projection -- */
 /*
@@ -474,22 +486,27 @@ int vsa_gate_proj(const void *x, const void *w_gate, int64_t rows, int32_t hidde
  * library's own launches, for benchmarks that must report one kernel's time
  * when an entry point launches several.
  *
- * vsa_timing_enable -- 1 clears earlier records and starts timing; 0 stops.
- * While on, every kernel launch the library makes is bracketed by two HIP
- * events recorded on the launch's own stream (events are created on first
- * use and reused; they are never recorded into a stream being captured by
- * design -- do not enable timing around graph capture). Process-wide.
+ * Timing is kept per stream: enabling it on one stream changes nothing for
+ * launches on any other stream.
+ *
+ * vsa_timing_enable -- for `stream` (a hipStream_t; NULL = the null stream):
+ * 1 clears its earlier records and starts timing; 0 stops. While on, every
+ * kernel launch the library makes on that stream is bracketed by two HIP
+ * events recorded on it (events are created on first use and reused; do not
+ * enable timing on a stream that is being captured into a graph).
  *
  * vsa_timing_read -- for the kernel named `kernel` (one of "gate_gemm",
  * "gather_pool", "video_scores", "coarse_attn", "topk", "fine_attn",
  * "merge", "bwd_gather", "bwd_prep", "bwd_coarse", "bwd_tlist", "bwd_dq",
- * "bwd_dkdv", "bwd_stats", "quant_k"), waits for the recorded launches since the last enable and returns
- * their number in *launches and their summed duration in *total_ms (host
- * pointers). Errors: VSA_ERR_ARG for a null pointer or an unknown name,
- * VSA_ERR_DEVICE if an event query fails.
+ * "bwd_dkdv", "bwd_stats", "quant_k"), waits for the launches recorded on
+ * `stream` since its last enable (call it after those entry points have
+ * returned) and returns their number in *launches and their summed duration
+ * in *total_ms (host pointers); 0 and 0.0 for a stream never timed.
+ * Errors: VSA_ERR_ARG for a null pointer or an unknown name, VSA_ERR_DEVICE
+ * if an event query fails.
  */
-int vsa_timing_enable(int32_t enable);
-int vsa_timing_read(const char *kernel, int32_t *launches, double *total_ms);
+int vsa_timing_enable(void *stream, int32_t enable);
+int vsa_timing_read(void *stream, const char *kernel, int32_t *launches, double *total_ms);
 
 #ifdef __cplusplus
 }

@@ -67,11 +67,13 @@ class GpuRun:
     g: torch.Tensor       # device bf16 [S][H*D]
 
 
-def run_gpu(inp: Inputs, gate: Optional[torch.Tensor] = None, dev="cuda") -> GpuRun:
+def run_gpu(inp: Inputs, gate: Optional[torch.Tensor] = None, dev="cuda",
+            split_chunks: int = 0) -> GpuRun:
     import tile_sparse_video_amd as tsv
     wl = inp.wl
     att = tsv.TileSparseAttention(wl.prefix_segments, wl.grid, wl.tile, wl.heads, wl.head_dim,
-                                  sparsity=wl.sparsity, keep_k=wl.keep_k, device=dev)
+                                  sparsity=wl.sparsity, keep_k=wl.keep_k, device=dev,
+                                  split_chunks=split_chunks)
     qd, kd, vd = (t.to(dev) for t in (inp.q, inp.k, inp.v))
     if gate is None:
         xd, wd = inp.x.to(dev), inp.w.to(dev)
@@ -141,14 +143,15 @@ def sample_tokens(pl, n: int, seed: int) -> np.ndarray:
 
 
 def run_gpu_ref(inp: Inputs, ref_sparsity=None, ref_keep_k=None, gate: Optional[torch.Tensor] = None,
-                dev="cuda") -> GpuRun:
+                dev="cuda", split_chunks: int = 0) -> GpuRun:
     """The layer in the reference-sparsity mode (every query tile keeps k_ref
     prefix tiles and k_gen video tiles)."""
     import tile_sparse_video_amd as tsv
     wl = inp.wl
     att = tsv.TileSparseAttention(wl.prefix_segments, wl.grid, wl.tile, wl.heads, wl.head_dim,
                                   sparsity=wl.sparsity, keep_k=wl.keep_k, device=dev,
-                                  reference_sparsity=ref_sparsity, ref_keep_k=ref_keep_k)
+                                  reference_sparsity=ref_sparsity, ref_keep_k=ref_keep_k,
+                                  split_chunks=split_chunks)
     qd, kd, vd = (t.to(dev) for t in (inp.q, inp.k, inp.v))
     if gate is None:
         xd, wd = inp.x.to(dev), inp.w.to(dev)

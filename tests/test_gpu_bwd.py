@@ -31,7 +31,7 @@ def make_dout(wl, seed=99):
     return torch.randn(wl.tokens, wl.heads, wl.head_dim, generator=gen).to(torch.bfloat16)
 
 
-def run_case(wl, ref=None, heads=None, train=False):
+def run_case(wl, ref=None, heads=None, train=False, split_chunks=0):
     """ref: None (default mode) or (ref_sparsity, ref_keep_k). train: rerun the fine
     pass as the training forward (its output must be bit-identical) so that the
     backward uses the statistics it saved."""
@@ -40,9 +40,9 @@ def run_case(wl, ref=None, heads=None, train=False):
     g_bits = oracle.gate_proj(parity.bits(inp.x), parity.bits(inp.w))
     g = torch.from_numpy(g_bits.view(np.int16)).view(torch.bfloat16)
     if ref is None:
-        run = parity.run_gpu(inp, gate=g)
+        run = parity.run_gpu(inp, gate=g, split_chunks=split_chunks)
     else:
-        run = parity.run_gpu_ref(inp, ref[0], ref[1], gate=g)
+        run = parity.run_gpu_ref(inp, ref[0], ref[1], gate=g, split_chunks=split_chunks)
     dout = make_dout(wl)
     dev = run.out.device
     qd, kd, vd = (t.to(dev) for t in (inp.q, inp.k, inp.v))
@@ -95,23 +95,13 @@ def test_bwd_reference_sparsity(name, rs, rk):
 def test_bwd_saved_stats_every_token(name):
     """Key lists split into 8 chunks; the training forward saves lse and O_fine and the
     backward uses them instead of recomputing the fine forward."""
-    import tile_sparse_video_amd as tsv
     print(f"[gpu] bwd saved stats {name}", flush=True)
-    tsv.vsa_set_split_chunks(8)
-    try:
-        run_case(CUSTOM[name], train=True)
-    finally:
-        tsv.vsa_set_split_chunks(0)
+    run_case(CUSTOM[name], train=True, split_chunks=8)
 
 
 def test_bwd_saved_stats_reference_sparsity():
-    import tile_sparse_video_amd as tsv
     print("[gpu] bwd saved stats ref", flush=True)
-    tsv.vsa_set_split_chunks(8)
-    try:
-        run_case(CUSTOM["ragged128"], ref=(0.5, None), train=True)
-    finally:
-        tsv.vsa_set_split_chunks(0)
+    run_case(CUSTOM["ragged128"], ref=(0.5, None), train=True, split_chunks=8)
 
 
 def test_bwd_tiny():

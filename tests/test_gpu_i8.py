@@ -29,12 +29,13 @@ pytestmark = [pytest.mark.gpu,
 EXACT_REL_L2 = 5e-2
 
 
-def run_gpu_i8(inp, ref_sparsity=None, ref_keep_k=None, dev="cuda"):
+def run_gpu_i8(inp, ref_sparsity=None, ref_keep_k=None, dev="cuda", split_chunks=0):
     import tile_sparse_video_amd as tsv
     wl = inp.wl
     att = tsv.TileSparseAttention(wl.prefix_segments, wl.grid, wl.tile, wl.heads, wl.head_dim,
                                   sparsity=wl.sparsity, keep_k=wl.keep_k, device=dev,
-                                  reference_sparsity=ref_sparsity, ref_keep_k=ref_keep_k, int8=True)
+                                  reference_sparsity=ref_sparsity, ref_keep_k=ref_keep_k, int8=True,
+                                  split_chunks=split_chunks)
     qd, kd, vd = (t.to(dev) for t in (inp.q, inp.k, inp.v))
     xd, wd = inp.x.to(dev), inp.w.to(dev)
     g = torch.empty((wl.tokens, wl.heads * wl.head_dim), dtype=torch.bfloat16, device=dev)
@@ -114,13 +115,9 @@ def test_i8_small_every_token(name, chunks):
     wl = CUSTOM[name]
     print(f"[gpu] int8 {name} chunks={chunks}", flush=True)
     inp = parity.make_inputs(wl)
-    tsv.vsa_set_split_chunks(chunks)
-    try:
-        run = run_gpu_i8(inp)
-        check_k_codes(inp, run, range(wl.heads))
-        check_layer_i8(inp, run, range(wl.heads), np.arange(wl.tokens))
-    finally:
-        tsv.vsa_set_split_chunks(0)
+    run = run_gpu_i8(inp, split_chunks=chunks)
+    check_k_codes(inp, run, range(wl.heads))
+    check_layer_i8(inp, run, range(wl.heads), np.arange(wl.tokens))
 
 
 @pytest.mark.parametrize("name,rs,rk", [("ragged64", None, 1), ("ragged128", 0.5, None),

@@ -289,9 +289,6 @@ def test_split_key_lists_every_token(name, chunks):
     wl = CUSTOM[name]
     print(f"[gpu] split {name} chunks={chunks}", flush=True)
     inp = parity.make_inputs(wl)
-    tsv.vsa_set_split_chunks(chunks)
-    try:
-        run = parity.run_gpu(inp)
-        check_layer(inp, run, range(wl.heads), np.arange(wl.tokens))
-    finally:
-        tsv.vsa_set_split_chunks(0)
+    run = parity.run_gpu(inp, split_chunks=chunks)
+    assert run.att.split_chunks == chunks
+    check_layer(inp, run, range(wl.heads), np.arange(wl.tokens))

@@ -80,12 +80,8 @@ def test_ref_small_every_token(name, rs, rk, chunks):
     wl = CUSTOM[name]
     print(f"[gpu] ref {name} rs={rs} rk={rk} chunks={chunks}", flush=True)
     inp = parity.make_inputs(wl)
-    tsv.vsa_set_split_chunks(chunks)
-    try:
-        run = parity.run_gpu_ref(inp, rs, rk)
-        check_layer_ref(inp, run, range(wl.heads), np.arange(wl.tokens), rs, rk)
-    finally:
-        tsv.vsa_set_split_chunks(0)
+    run = parity.run_gpu_ref(inp, rs, rk, split_chunks=chunks)
+    check_layer_ref(inp, run, range(wl.heads), np.arange(wl.tokens), rs, rk)
 
 
 def test_ref_tiny_and_mid():

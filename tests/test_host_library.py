@@ -134,16 +134,22 @@ def test_workspace_layout():
     # a 50 MiB head splits its key lists: room for 8 chunk partials per 64 query rows
     items = H * n_t
     assert lay.part_ml - lay.part_o >= items * 8 * 64 * D * 2
-    # an override changes the layout, and 0 restores the automatic choice
-    tsv.vsa_set_split_chunks(1)
-    try:
-        assert tsv.vsa_workspace_layout(pl.info, H, D).total_bytes < lay.total_bytes
-    finally:
-        tsv.vsa_set_split_chunks(0)
-    assert tsv.vsa_workspace_layout(pl.info, H, D).total_bytes == lay.total_bytes
-    with pytest.raises(tsv.VsaError) as e:
-        tsv.vsa_set_split_chunks(65)
-    assert e.value.status == tsv.VSA_ERR_ARG
+    assert lay.split_chunks == 8
+    # the split is an argument: layouts of different splits coexist, and only the
+    # partials (placed last) depend on it
+    one = tsv.vsa_workspace_layout(pl.info, H, D, 1)
+    sixteen = tsv.vsa_workspace_layout(pl.info, H, D, 16)
+    assert one.split_chunks == 1 and sixteen.split_chunks == 16
+    assert one.total_bytes == one.part_o < lay.total_bytes < sixteen.total_bytes
+    for name in ("k_tiled", "v_tiled", "q_mean", "k_mean", "v_mean", "scores", "k_i8", "k_scale",
+                 "part_o"):
+        assert getattr(one, name) == getattr(lay, name) == getattr(sixteen, name)
+    assert sixteen.part_ml - sixteen.part_o == 2 * (lay.part_ml - lay.part_o)
+    assert tsv.vsa_workspace_layout(pl.info, H, D, 0).total_bytes == lay.total_bytes
+    for bad in (-1, 65):
+        with pytest.raises(tsv.VsaError) as e:
+            tsv.vsa_workspace_layout(pl.info, H, D, bad)
+        assert e.value.status == tsv.VSA_ERR_ARG
 
 
 def test_workspace_layout_unsupported():
@@ -172,10 +178,10 @@ def _coarse(info, heads=2, head_dim=128, sparsity=float("nan"), keep_k=1, scale=
 
 
 def _fine(info, heads=2, head_dim=128, k=1, scale=0.0, ws_bytes=1 << 40, keep=FAKE,
-          q=FAKE, gate=FAKE, out=FAKE):
+          q=FAKE, gate=FAKE, out=FAKE, split=0):
     lib = tsv._lib
-    return lib.vsa_sparse_attn_fwd(ctypes.byref(info), FAKE, FAKE, heads, head_dim, k, scale, q,
-                                   FAKE * 2, ws_bytes, keep, FAKE, gate, out, None)
+    return lib.vsa_sparse_attn_fwd(ctypes.byref(info), FAKE, FAKE, heads, head_dim, k, scale, split,
+                                   q, FAKE * 2, ws_bytes, keep, FAKE, gate, out, None)
 
 
 def test_gpu_entry_points_reject_bad_arguments():
@@ -196,6 +202,8 @@ def test_gpu_entry_points_reject_bad_arguments():
         (_fine(info, q=0), E.VSA_ERR_ARG),
         (_fine(info, ws_bytes=1024), E.VSA_ERR_ARG),
         (_fine(info, keep=0), E.VSA_ERR_ARG),
+        (_fine(info, split=-1), E.VSA_ERR_ARG),
+        (_fine(info, split=65), E.VSA_ERR_ARG),
     ]
     for got, want in cases:
         assert got == want, (got, want, tsv._lib.vsa_last_error())
@@ -223,24 +231,31 @@ def test_status_strings():
 
 def test_kernel_timing_host_side():
     lib = tsv._lib
-    tsv.vsa_timing_enable(True)
+    s0, s1 = 0, 0x1234000   # stream handles as keys only: nothing is enqueued on them
+    tsv.vsa_timing_enable(True, stream=s0)
     try:
         for name in tsv.TIMED_KERNELS:
-            assert tsv.vsa_timing_read(name) == (0, 0.0)   # nothing launched since enable
+            assert tsv.vsa_timing_read(name, stream=s0) == (0, 0.0)   # nothing launched since enable
         with pytest.raises(tsv.VsaError) as e:
-            tsv.vsa_timing_read("not_a_kernel")
+            tsv.vsa_timing_read("not_a_kernel", stream=s0)
         assert e.value.status == tsv.VSA_ERR_ARG
-        assert lib.vsa_timing_read(b"fine_attn", None, None) == tsv.VSA_ERR_ARG
+        assert lib.vsa_timing_read(None, b"fine_attn", None, None) == tsv.VSA_ERR_ARG
+        # timing is per stream: a stream never enabled reads as empty, and enabling
+        # or disabling one stream leaves another's state alone
+        assert tsv.vsa_timing_read("fine_attn", stream=s1) == (0, 0.0)
+        tsv.vsa_timing_enable(True, stream=s1)
+        tsv.vsa_timing_enable(False, stream=s1)
+        assert tsv.vsa_timing_read("fine_attn", stream=s0) == (0, 0.0)
     finally:
-        tsv.vsa_timing_enable(False)
+        tsv.vsa_timing_enable(False, stream=s0)
     # failed launches (argument errors) record nothing
     pl = tsv.vsa_plan_tiles([20, 40], (4, 8, 8), (4, 4, 4))
-    tsv.vsa_timing_enable(True)
+    tsv.vsa_timing_enable(True, stream=s0)
     try:
         assert _fine(pl.info, head_dim=80) == tsv.VSA_ERR_UNSUPPORTED
-        assert tsv.vsa_timing_read("fine_attn") == (0, 0.0)
+        assert tsv.vsa_timing_read("fine_attn", stream=s0) == (0, 0.0)
     finally:
-        tsv.vsa_timing_enable(False)
+        tsv.vsa_timing_enable(False, stream=s0)
 
 
 # ---- reference-sparsity mode: host-side checks
@@ -285,7 +300,7 @@ def test_ref_entry_points_reject_bad_arguments():
 
     def fine(heads=2, head_dim=128, k_ref=1, k_gen=1, keep=FAKE, ws_bytes=1 << 40):
         return lib.vsa_sparse_attn_fwd_ref(ctypes.byref(info), FAKE, FAKE, heads, head_dim, k_ref,
-                                           k_gen, 0.0, FAKE, FAKE * 2, ws_bytes, keep, FAKE, FAKE,
+                                           k_gen, 0.0, 0, FAKE, FAKE * 2, ws_bytes, keep, FAKE, FAKE,
                                            FAKE, None)
 
     E = tsv
@@ -318,8 +333,8 @@ def test_i8_entry_point_rejects_bad_arguments():
     def fine(heads=2, head_dim=128, k_ref=-1, k_gen=1, keep=FAKE, ws_bytes=1 << 40, q=FAKE,
              scale=0.0):
         return lib.vsa_sparse_attn_fwd_i8(ctypes.byref(info), FAKE, FAKE, heads, head_dim, k_ref,
-                                          k_gen, scale, q, FAKE * 2, ws_bytes, keep, FAKE, FAKE,
-                                          FAKE, None)
+                                          k_gen, scale, 0, q, FAKE * 2, ws_bytes, keep, FAKE,
+                                          FAKE, FAKE, None)
 
     E = tsv
     cases = [
@@ -342,8 +357,8 @@ def test_i8_entry_point_rejects_bad_arguments():
     lay = tsv.vsa_workspace_layout(big.info, wl.heads, wl.head_dim)
     assert lay.k_i8 % 256 == 0 and lay.k_scale % 256 == 0
     assert lay.k_scale - lay.k_i8 >= wl.heads * big.S_pad * wl.head_dim
-    assert lay.total_bytes - lay.k_scale >= wl.heads * big.S_pad // 64 * 4
-    assert lay.k_i8 >= lay.part_ml
+    assert lay.part_o - lay.k_scale >= wl.heads * big.S_pad // 64 * 4
+    assert lay.k_i8 >= lay.scores and lay.part_o >= lay.k_scale
 
 
 def test_group_entry_point_rejects_bad_arguments():
@@ -353,13 +368,14 @@ def test_group_entry_point_rejects_bad_arguments():
     b = tsv.vsa_plan_tiles([20, 40], (4, 8, 8), (1, 8, 8))
     other = tsv.vsa_plan_tiles([20, 41], (4, 8, 8), (4, 4, 4))   # one token more
 
-    def group(pl, first, heads, keep_k=1, ws=FAKE, ref=0, ref_keep_k=-1):
+    def group(pl, first, heads, keep_k=1, ws=FAKE, ref=0, ref_keep_k=-1, split=0):
         g = tsv.vsa_head_group()
         g.info = ctypes.pointer(pl.info)
         g.row_src_dev = g.block_len_dev = FAKE
         g.head_first, g.heads = first, heads
         g.sparsity, g.keep_k = float("nan"), keep_k
         g.ref, g.int8, g.ref_sparsity, g.ref_keep_k = ref, 0, float("nan"), ref_keep_k
+        g.split_chunks = split
         g.workspace, g.workspace_bytes = ws, 1 << 40
         g.keep_idx_dev = g.o_coarse_dev = FAKE
         return g
@@ -385,6 +401,8 @@ def test_group_entry_point_rejects_bad_arguments():
     assert b"group 1" in lib.vsa_last_error()
     assert call([group(a, 0, 2), group(b, 2, 2, ws=FAKE + 8)]) == E.VSA_ERR_ARG   # misaligned
     assert call([group(a, 0, 2)], head_dim=96) == E.VSA_ERR_UNSUPPORTED
+    assert call([group(a, 0, 2), group(b, 2, 2, split=65)]) == E.VSA_ERR_ARG   # bad split
+    assert b"group 1" in lib.vsa_last_error()
 
 
 def test_heads_beyond_4gib_are_rejected():
@@ -397,17 +415,17 @@ def test_heads_beyond_4gib_are_rejected():
     info.rows_real = info.rows_padded = 256 ** 3      # 2^24 rows x 128 x 2 B = 4 GiB
     info.prefix_rows = 0
     lib = tsv._lib
-    rc = lib.vsa_sparse_attn_fwd(ctypes.byref(info), FAKE, FAKE, 1, 128, 1, 0.0, FAKE, FAKE * 2,
+    rc = lib.vsa_sparse_attn_fwd(ctypes.byref(info), FAKE, FAKE, 1, 128, 1, 0.0, 0, FAKE, FAKE * 2,
                                  1 << 50, FAKE, FAKE, FAKE, FAKE, None)
     assert rc == tsv.VSA_ERR_UNSUPPORTED, lib.vsa_last_error()
     assert b"4 GiB" in lib.vsa_last_error()
-    rc = lib.vsa_sparse_attn_bwd(ctypes.byref(info), FAKE, FAKE, 1, 128, -1, 1, 0.0, FAKE, FAKE,
+    rc = lib.vsa_sparse_attn_bwd(ctypes.byref(info), FAKE, FAKE, 1, 128, -1, 1, 0.0, 0, FAKE, FAKE,
                                  FAKE, FAKE, FAKE, FAKE * 2, 1 << 50, FAKE, FAKE, FAKE * 2, 1 << 50,
                                  FAKE, FAKE, FAKE, FAKE, 0, None)
     assert rc == tsv.VSA_ERR_UNSUPPORTED, lib.vsa_last_error()
     # head_dim 64 halves the bytes: the same plan passes this check (and fails later on the
     # fake workspace size, still before any device work)
-    rc = lib.vsa_sparse_attn_fwd(ctypes.byref(info), FAKE, FAKE, 1, 64, 1, 0.0, FAKE, FAKE * 2,
+    rc = lib.vsa_sparse_attn_fwd(ctypes.byref(info), FAKE, FAKE, 1, 64, 1, 0.0, 0, FAKE, FAKE * 2,
                                  1024, FAKE, FAKE, FAKE, FAKE, None)
     assert rc == tsv.VSA_ERR_ARG and b"workspace" in lib.vsa_last_error()
 
@@ -419,8 +437,8 @@ def test_training_forward_rejects_bad_arguments():
 
     def call(bw=FAKE * 4, bw_bytes=1 << 40, heads=2, head_dim=128, k_gen=1):
         return lib.vsa_sparse_attn_fwd_train(ctypes.byref(info), FAKE, FAKE, heads, head_dim, -1,
-                                             k_gen, 0.0, FAKE, FAKE * 2, 1 << 40, FAKE, FAKE, FAKE,
-                                             FAKE, bw, bw_bytes, None)
+                                             k_gen, 0.0, 0, FAKE, FAKE * 2, 1 << 40, FAKE, FAKE,
+                                             FAKE, FAKE, bw, bw_bytes, None)
 
     E = tsv
     assert call(bw=0) == E.VSA_ERR_ARG

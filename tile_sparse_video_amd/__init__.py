@@ -31,7 +31,7 @@ VSA_ERR_DEVICE = -4
 EXPORTED = (
     "vsa_status_string", "vsa_last_error", "vsa_plan_tiles", "vsa_plan_validate",
     "vsa_keep_count", "vsa_tile_pair_fraction", "vsa_workspace_layout", "vsa_coarse_topk",
-    "vsa_sparse_attn_fwd", "vsa_gate_proj", "vsa_set_split_chunks", "vsa_timing_enable",
+    "vsa_sparse_attn_fwd", "vsa_gate_proj", "vsa_timing_enable",
     "vsa_timing_read", "vsa_ref_keep_count", "vsa_tile_pair_fraction_ref", "vsa_coarse_topk_ref",
     "vsa_sparse_attn_fwd_ref", "vsa_bwd_workspace_layout", "vsa_sparse_attn_bwd",
     "vsa_sparse_attn_fwd_i8", "vsa_layer_fwd_groups", "vsa_sparse_attn_fwd_train",
@@ -58,8 +58,8 @@ class vsa_plan_info(ctypes.Structure):
 
 class vsa_ws_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("k_tiled", "v_tiled", "q_mean", "k_mean", "v_mean", "scores", "part_o",
-                 "part_ml", "k_i8", "k_scale", "total_bytes")]
+                ("k_tiled", "v_tiled", "q_mean", "k_mean", "v_mean", "scores", "k_i8",
+                 "k_scale", "part_o", "part_ml", "total_bytes")] + [("split_chunks", ctypes.c_int32)]
 
 
 class vsa_head_group(ctypes.Structure):
@@ -68,7 +68,7 @@ class vsa_head_group(ctypes.Structure):
         ("block_len_dev", ctypes.c_void_p), ("head_first", ctypes.c_int32),
         ("heads", ctypes.c_int32), ("sparsity", ctypes.c_double), ("keep_k", ctypes.c_int64),
         ("ref", ctypes.c_int32), ("int8", ctypes.c_int32), ("ref_sparsity", ctypes.c_double),
-        ("ref_keep_k", ctypes.c_int64), ("workspace", ctypes.c_void_p),
+        ("ref_keep_k", ctypes.c_int64), ("split_chunks", ctypes.c_int32), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t), ("keep_idx_dev", ctypes.c_void_p),
         ("o_coarse_dev", ctypes.c_void_p),
     ]
@@ -78,7 +78,7 @@ class vsa_bwd_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("vrow", "kcol", "qcol", "docol", "qrow", "dorow", "lse", "dt", "doc", "dqm", "dkm",
                  "dvm", "lsec", "dcc", "tlist", "tcount", "tbits", "part_dq", "part_dkv", "ofine",
-                 "total_bytes")]
+                 "total_bytes")] + [("split_chunks", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -96,30 +96,30 @@ def _load() -> ctypes.CDLL:
         "vsa_plan_validate": ([info_p, P, I32, P, P, P], ctypes.c_int),
         "vsa_keep_count": ([info_p, F64, I64, ctypes.POINTER(I32)], ctypes.c_int),
         "vsa_tile_pair_fraction": ([info_p, I32, ctypes.POINTER(F64)], ctypes.c_int),
-        "vsa_workspace_layout": ([info_p, I32, I32, ctypes.POINTER(vsa_ws_layout)], ctypes.c_int),
+        "vsa_workspace_layout": ([info_p, I32, I32, I32, ctypes.POINTER(vsa_ws_layout)], ctypes.c_int),
         "vsa_coarse_topk": ([info_p, P, P, I32, I32, F64, I64, F32, P, P, P, P, SZ, P, P, P],
                             ctypes.c_int),
-        "vsa_sparse_attn_fwd": ([info_p, P, P, I32, I32, I32, F32, P, P, SZ, P, P, P, P, P],
+        "vsa_sparse_attn_fwd": ([info_p, P, P, I32, I32, I32, F32, I32, P, P, SZ, P, P, P, P, P],
                                 ctypes.c_int),
         "vsa_gate_proj": ([P, P, I64, I32, I32, P, P], ctypes.c_int),
-        "vsa_set_split_chunks": ([I32], ctypes.c_int),
         "vsa_ref_keep_count": ([info_p, F64, I64, ctypes.POINTER(I32)], ctypes.c_int),
         "vsa_tile_pair_fraction_ref": ([info_p, I32, I32, ctypes.POINTER(F64)], ctypes.c_int),
         "vsa_coarse_topk_ref": ([info_p, P, P, I32, I32, F64, I64, F64, I64, F32, P, P, P, P, SZ,
                                  P, P, P], ctypes.c_int),
-        "vsa_sparse_attn_fwd_ref": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, SZ, P, P, P, P,
-                                     P], ctypes.c_int),
-        "vsa_sparse_attn_fwd_i8": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, SZ, P, P, P, P,
-                                    P], ctypes.c_int),
+        "vsa_sparse_attn_fwd_ref": ([info_p, P, P, I32, I32, I32, I32, F32, I32, P, P, SZ, P, P, P,
+                                     P, P], ctypes.c_int),
+        "vsa_sparse_attn_fwd_i8": ([info_p, P, P, I32, I32, I32, I32, F32, I32, P, P, SZ, P, P, P,
+                                    P, P], ctypes.c_int),
         "vsa_layer_fwd_groups": ([ctypes.POINTER(vsa_head_group), I32, I32, I32, F32, P, P, P, P,
                                   P, P], ctypes.c_int),
-        "vsa_bwd_workspace_layout": ([info_p, I32, I32, ctypes.POINTER(vsa_bwd_layout)], ctypes.c_int),
-        "vsa_sparse_attn_bwd": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, P, P, P, P, SZ, P, P,
-                                 P, SZ, P, P, P, P, I32, P], ctypes.c_int),
-        "vsa_sparse_attn_fwd_train": ([info_p, P, P, I32, I32, I32, I32, F32, P, P, SZ, P, P, P, P,
-                                       P, SZ, P], ctypes.c_int),
-        "vsa_timing_enable": ([I32], ctypes.c_int),
-        "vsa_timing_read": ([ctypes.c_char_p, ctypes.POINTER(I32), ctypes.POINTER(F64)],
+        "vsa_bwd_workspace_layout": ([info_p, I32, I32, I32, ctypes.POINTER(vsa_bwd_layout)],
+                                     ctypes.c_int),
+        "vsa_sparse_attn_bwd": ([info_p, P, P, I32, I32, I32, I32, F32, I32, P, P, P, P, P, P, SZ, P,
+                                 P, P, SZ, P, P, P, P, I32, P], ctypes.c_int),
+        "vsa_sparse_attn_fwd_train": ([info_p, P, P, I32, I32, I32, I32, F32, I32, P, P, SZ, P, P,
+                                       P, P, P, SZ, P], ctypes.c_int),
+        "vsa_timing_enable": ([P, I32], ctypes.c_int),
+        "vsa_timing_read": ([P, ctypes.c_char_p, ctypes.POINTER(I32), ctypes.POINTER(F64)],
                             ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -247,10 +247,12 @@ def vsa_tile_pair_fraction_ref(info: vsa_plan_info, k_ref: int, k_gen: int) -> f
     return float(f.value)
 
 
-def vsa_workspace_layout(info: vsa_plan_info, heads: int, head_dim: int) -> vsa_ws_layout:
+def vsa_workspace_layout(info: vsa_plan_info, heads: int, head_dim: int,
+                         split_chunks: int = 0) -> vsa_ws_layout:
+    """Workspace regions for `split_chunks` fine-pass key chunks (0 = automatic)."""
     lay = vsa_ws_layout()
-    _check(_lib.vsa_workspace_layout(ctypes.byref(info), int(heads), int(head_dim), ctypes.byref(lay)),
-           "vsa_workspace_layout")
+    _check(_lib.vsa_workspace_layout(ctypes.byref(info), int(heads), int(head_dim), int(split_chunks),
+                                     ctypes.byref(lay)), "vsa_workspace_layout")
     return lay
 
 
@@ -294,7 +296,8 @@ def vsa_coarse_topk(info: vsa_plan_info, row_src_dev: torch.Tensor, block_len_de
 def vsa_sparse_attn_fwd(info: vsa_plan_info, row_src_dev: torch.Tensor, block_len_dev: torch.Tensor,
                         heads: int, head_dim: int, k: int, q: torch.Tensor, workspace: torch.Tensor,
                         keep_idx: Optional[torch.Tensor], o_coarse: torch.Tensor, gate: torch.Tensor,
-                        out: torch.Tensor, scale: float = 0.0, stream=None) -> None:
+                        out: torch.Tensor, scale: float = 0.0, stream=None,
+                        split_chunks: int = 0) -> None:
     S = info.rows_real
     _need(q, "q", torch.bfloat16, (S, heads, head_dim))
     _need(gate, "gate", torch.bfloat16)
@@ -308,7 +311,8 @@ def vsa_sparse_attn_fwd(info: vsa_plan_info, row_src_dev: torch.Tensor, block_le
     if keep_idx is not None:
         _need(keep_idx, "keep_idx", torch.int32, (heads, info.n_video_tiles, k))
     _check(_lib.vsa_sparse_attn_fwd(ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev), heads,
-                                    head_dim, int(k), float(scale), _ptr(q), _ptr(workspace),
+                                    head_dim, int(k), float(scale), int(split_chunks), _ptr(q),
+                                    _ptr(workspace),
                                     workspace.numel(), _ptr(keep_idx), _ptr(o_coarse), _ptr(gate),
                                     _ptr(out), _stream(stream)),
            "vsa_sparse_attn_fwd")
@@ -346,7 +350,7 @@ def vsa_sparse_attn_fwd_ref(info: vsa_plan_info, row_src_dev: torch.Tensor,
                             k_gen: int, q: torch.Tensor, workspace: torch.Tensor,
                             keep_idx: Optional[torch.Tensor], o_coarse: torch.Tensor,
                             gate: torch.Tensor, out: torch.Tensor, scale: float = 0.0,
-                            stream=None) -> None:
+                            stream=None, split_chunks: int = 0) -> None:
     S = info.rows_real
     _need(q, "q", torch.bfloat16, (S, heads, head_dim))
     _need(gate, "gate", torch.bfloat16)
@@ -361,7 +365,8 @@ def vsa_sparse_attn_fwd_ref(info: vsa_plan_info, row_src_dev: torch.Tensor,
         _need(keep_idx, "keep_idx", torch.int32, (heads, info.n_tiles, k_ref + k_gen))
     _check(_lib.vsa_sparse_attn_fwd_ref(ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev),
                                         heads, head_dim, int(k_ref), int(k_gen), float(scale),
-                                        _ptr(q), _ptr(workspace), workspace.numel(), _ptr(keep_idx),
+                                        int(split_chunks), _ptr(q), _ptr(workspace),
+                                        workspace.numel(), _ptr(keep_idx),
                                         _ptr(o_coarse), _ptr(gate), _ptr(out), _stream(stream)),
            "vsa_sparse_attn_fwd_ref")
 
@@ -371,7 +376,7 @@ def vsa_sparse_attn_fwd_i8(info: vsa_plan_info, row_src_dev: torch.Tensor,
                            k_gen: int, q: torch.Tensor, workspace: torch.Tensor,
                            keep_idx: Optional[torch.Tensor], o_coarse: torch.Tensor,
                            gate: torch.Tensor, out: torch.Tensor, scale: float = 0.0,
-                           stream=None) -> None:
+                           stream=None, split_chunks: int = 0) -> None:
     """The fine pass with INT8 scores; k_ref < 0 selects the default mode
     (keep_idx [H][n_v][k_gen]), k_ref >= 0 the reference-sparsity mode."""
     S = info.rows_real
@@ -390,15 +395,18 @@ def vsa_sparse_attn_fwd_i8(info: vsa_plan_info, row_src_dev: torch.Tensor,
         _need(keep_idx, "keep_idx", torch.int32, shape)
     _check(_lib.vsa_sparse_attn_fwd_i8(ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev),
                                        heads, head_dim, int(k_ref), int(k_gen), float(scale),
-                                       _ptr(q), _ptr(workspace), workspace.numel(), _ptr(keep_idx),
+                                       int(split_chunks), _ptr(q), _ptr(workspace),
+                                       workspace.numel(), _ptr(keep_idx),
                                        _ptr(o_coarse), _ptr(gate), _ptr(out), _stream(stream)),
            "vsa_sparse_attn_fwd_i8")
 
 
-def vsa_bwd_workspace_layout(info: vsa_plan_info, heads: int, head_dim: int) -> vsa_bwd_layout:
+def vsa_bwd_workspace_layout(info: vsa_plan_info, heads: int, head_dim: int,
+                             split_chunks: int = 0) -> vsa_bwd_layout:
     lay = vsa_bwd_layout()
     _check(_lib.vsa_bwd_workspace_layout(ctypes.byref(info), int(heads), int(head_dim),
-                                         ctypes.byref(lay)), "vsa_bwd_workspace_layout")
+                                         int(split_chunks), ctypes.byref(lay)),
+           "vsa_bwd_workspace_layout")
     return lay
 
 
@@ -406,7 +414,8 @@ def vsa_sparse_attn_bwd(info: vsa_plan_info, row_src_dev: torch.Tensor, block_le
                         heads: int, head_dim: int, k_ref: int, k_gen: int, q, k, v, gate, dout,
                         workspace: torch.Tensor, keep_idx: Optional[torch.Tensor],
                         o_coarse: torch.Tensor, bwd_workspace: torch.Tensor, dq, dk, dv, dgate,
-                        scale: float = 0.0, stream=None, saved_stats: bool = False) -> None:
+                        scale: float = 0.0, stream=None, saved_stats: bool = False,
+                        split_chunks: int = 0) -> None:
     """Backward pass (k_ref < 0: default mode). Gradients are fp32. saved_stats: the
     bwd_workspace holds what vsa_sparse_attn_fwd_train saved for this forward."""
     S = info.rows_real
@@ -429,7 +438,7 @@ def vsa_sparse_attn_bwd(info: vsa_plan_info, row_src_dev: torch.Tensor, block_le
         _need(keep_idx, "keep_idx", torch.int32)
     _check(_lib.vsa_sparse_attn_bwd(
         ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev), heads, head_dim, int(k_ref),
-        int(k_gen), float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(dout),
+        int(k_gen), float(scale), int(split_chunks), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(dout),
         _ptr(workspace), workspace.numel(), _ptr(keep_idx), _ptr(o_coarse), _ptr(bwd_workspace),
         bwd_workspace.numel(), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate), int(bool(saved_stats)),
         _stream(stream)),
@@ -441,7 +450,7 @@ def vsa_sparse_attn_fwd_train(info: vsa_plan_info, row_src_dev: torch.Tensor,
                               k_gen: int, q: torch.Tensor, workspace: torch.Tensor,
                               keep_idx: Optional[torch.Tensor], o_coarse: torch.Tensor,
                               gate: torch.Tensor, out: torch.Tensor, bwd_workspace: torch.Tensor,
-                              scale: float = 0.0, stream=None) -> None:
+                              scale: float = 0.0, stream=None, split_chunks: int = 0) -> None:
     """The fine pass of a training step (k_ref < 0: default mode): the forward's
     output plus the lse and O_fine the backward needs, saved in bwd_workspace."""
     S = info.rows_real
@@ -461,7 +470,8 @@ def vsa_sparse_attn_fwd_train(info: vsa_plan_info, row_src_dev: torch.Tensor,
         _need(keep_idx, "keep_idx", torch.int32, shape)
     _check(_lib.vsa_sparse_attn_fwd_train(
         ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev), heads, head_dim, int(k_ref),
-        int(k_gen), float(scale), _ptr(q), _ptr(workspace), workspace.numel(), _ptr(keep_idx),
+        int(k_gen), float(scale), int(split_chunks), _ptr(q), _ptr(workspace), workspace.numel(),
+        _ptr(keep_idx),
         _ptr(o_coarse), _ptr(gate), _ptr(out), _ptr(bwd_workspace), bwd_workspace.numel(),
         _stream(stream)), "vsa_sparse_attn_fwd_train")
 
@@ -478,21 +488,18 @@ def vsa_gate_proj(x: torch.Tensor, w_gate: torch.Tensor, g: torch.Tensor, stream
            "vsa_gate_proj")
 
 
-def vsa_set_split_chunks(chunks: int) -> None:
-    """Tuning override for the fine pass key-list split (0 = automatic)."""
-    _check(_lib.vsa_set_split_chunks(int(chunks)), "vsa_set_split_chunks")
+def vsa_timing_enable(enable: bool, stream=None) -> None:
+    """Start (clearing earlier records) or stop per-kernel timing of the library's
+    launches on `stream` (default: torch's current stream)."""
+    _check(_lib.vsa_timing_enable(_stream(stream), 1 if enable else 0), "vsa_timing_enable")
 
 
-def vsa_timing_enable(enable: bool) -> None:
-    """Start (clearing earlier records) or stop per-kernel timing of library launches."""
-    _check(_lib.vsa_timing_enable(1 if enable else 0), "vsa_timing_enable")
-
-
-def vsa_timing_read(kernel: str) -> tuple:
-    """(launches, total ms) of `kernel` since timing was last enabled; waits for them."""
+def vsa_timing_read(kernel: str, stream=None) -> tuple:
+    """(launches, total ms) of `kernel` on `stream` since its timing was last enabled;
+    waits for them."""
     n = ctypes.c_int32()
     ms = ctypes.c_double()
-    _check(_lib.vsa_timing_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)),
+    _check(_lib.vsa_timing_read(_stream(stream), kernel.encode(), ctypes.byref(n), ctypes.byref(ms)),
            "vsa_timing_read")
     return n.value, ms.value
 
@@ -522,10 +529,11 @@ class TileSparseAttention:
     def __init__(self, prefix_segments, grid, tile, heads: int, head_dim: int,
                  sparsity: Optional[float] = None, keep_k: Optional[int] = None,
                  scale: float = 0.0, device="cuda", reference_sparsity: Optional[float] = None,
-                 ref_keep_k: Optional[int] = None, int8: bool = False):
+                 ref_keep_k: Optional[int] = None, int8: bool = False, split_chunks: int = 0):
         """reference_sparsity / ref_keep_k (either one) switch to the reference-sparsity
         mode: every query tile keeps k_ref prefix tiles and k video tiles. int8 runs
-        the fine pass with INT8 scores (vsa_sparse_attn_fwd_i8)."""
+        the fine pass with INT8 scores (vsa_sparse_attn_fwd_i8). split_chunks: the fine
+        pass's key-list split for this layer (0 = automatic)."""
         self.int8 = bool(int8)
         self.plan = cached_plan(prefix_segments, grid, tile)
         info = self.plan.info
@@ -535,7 +543,8 @@ class TileSparseAttention:
         self.ref = reference_sparsity is not None or ref_keep_k is not None
         self.reference_sparsity, self.ref_keep_k = reference_sparsity, ref_keep_k
         self.k_ref = vsa_ref_keep_count(info, reference_sparsity, ref_keep_k) if self.ref else 0
-        self.layout = vsa_workspace_layout(info, heads, head_dim)
+        self.layout = vsa_workspace_layout(info, heads, head_dim, split_chunks)
+        self.split_chunks = int(self.layout.split_chunks)
         dev = torch.device(device)
         self.row_src = torch.from_numpy(self.plan.row_src).to(dev)
         self.block_len = torch.from_numpy(self.plan.block_len).to(dev)
@@ -572,19 +581,22 @@ class TileSparseAttention:
             vsa_sparse_attn_fwd_i8(self.plan.info, self.row_src, self.block_len, self.heads,
                                    self.head_dim, self.k_ref if self.ref else -1, self.k, q,
                                    self.workspace, keep, self.o_coarse, gate, out,
-                                   scale=self.scale, stream=stream)
+                                   scale=self.scale, stream=stream, split_chunks=self.split_chunks)
         elif self.ref:
             vsa_sparse_attn_fwd_ref(self.plan.info, self.row_src, self.block_len, self.heads,
                                     self.head_dim, self.k_ref, self.k, q, self.workspace, keep,
-                                    self.o_coarse, gate, out, scale=self.scale, stream=stream)
+                                    self.o_coarse, gate, out, scale=self.scale, stream=stream,
+                                    split_chunks=self.split_chunks)
         else:
             vsa_sparse_attn_fwd(self.plan.info, self.row_src, self.block_len, self.heads,
                                 self.head_dim, self.k, q, self.workspace, keep, self.o_coarse,
-                                gate, out, scale=self.scale, stream=stream)
+                                gate, out, scale=self.scale, stream=stream,
+                                split_chunks=self.split_chunks)
 
     def _bwd_workspace(self, device):
         if not hasattr(self, "bwd_workspace"):
-            lay = vsa_bwd_workspace_layout(self.plan.info, self.heads, self.head_dim)
+            lay = vsa_bwd_workspace_layout(self.plan.info, self.heads, self.head_dim,
+                                           self.split_chunks)
             self.bwd_layout = lay
             self.bwd_workspace = torch.empty(lay.total_bytes, dtype=torch.uint8, device=device)
         return self.bwd_workspace
@@ -598,7 +610,8 @@ class TileSparseAttention:
         vsa_sparse_attn_fwd_train(self.plan.info, self.row_src, self.block_len, self.heads,
                                   self.head_dim, self.k_ref if self.ref else -1, self.k, q,
                                   self.workspace, keep, self.o_coarse, gate, out,
-                                  self._bwd_workspace(q.device), scale=self.scale, stream=stream)
+                                  self._bwd_workspace(q.device), scale=self.scale, stream=stream,
+                                  split_chunks=self.split_chunks)
         self._stats_saved = True
 
     def backward(self, q, k, v, gate, dout, stream=None):
@@ -614,7 +627,8 @@ class TileSparseAttention:
         vsa_sparse_attn_bwd(self.plan.info, self.row_src, self.block_len, self.heads, self.head_dim,
                             self.k_ref if self.ref else -1, self.k, q, k, v, gate, dout,
                             self.workspace, keep, self.o_coarse, self.bwd_workspace, dq, dk, dv,
-                            dgate, scale=self.scale, stream=stream, saved_stats=saved)
+                            dgate, scale=self.scale, stream=stream, saved_stats=saved,
+                            split_chunks=self.split_chunks)
         return dq, dk, dv, dgate
 
     def tile_pair_fraction(self) -> float:
@@ -642,7 +656,7 @@ class HeadGroupAttention:
     every group on the shared q, k, v, gate and out.
 
     groups: sequence of dicts with keys "tile" and "heads" (required) and optional
-    "sparsity", "keep_k", "reference_sparsity", "ref_keep_k", "int8"; the groups
+    "sparsity", "keep_k", "reference_sparsity", "ref_keep_k", "int8", "split_chunks"; the groups
     take the heads in order."""
 
     def __init__(self, prefix_segments, grid, groups, head_dim: int, scale: float = 0.0,
@@ -656,7 +670,8 @@ class HeadGroupAttention:
                                       sparsity=g.get("sparsity"), keep_k=g.get("keep_k"),
                                       scale=scale, device=device,
                                       reference_sparsity=g.get("reference_sparsity"),
-                                      ref_keep_k=g.get("ref_keep_k"), int8=g.get("int8", False))
+                                      ref_keep_k=g.get("ref_keep_k"), int8=g.get("int8", False),
+                                      split_chunks=g.get("split_chunks", 0))
             self.layers.append((first, att))
             first += int(g["heads"])
         self.heads_total = first if heads_total is None else int(heads_total)
@@ -672,6 +687,7 @@ class HeadGroupAttention:
             e.ref_sparsity = (float("nan") if att.reference_sparsity is None
                               else float(att.reference_sparsity))
             e.ref_keep_k = -1 if att.ref_keep_k is None else int(att.ref_keep_k)
+            e.split_chunks = att.split_chunks
             e.workspace, e.workspace_bytes = _ptr(att.workspace), att.workspace.numel()
             e.keep_idx_dev = _ptr(att.keep_idx) if att.list_len > 0 else None
             e.o_coarse_dev = _ptr(att.o_coarse)

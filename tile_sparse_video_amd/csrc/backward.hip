@@ -1349,13 +1349,13 @@ namespace vsa {
 
 // The dK/dV pass splits its query lists into 8 XCD-affine chunks when the
 // heads are large (as the forward) and the fp32 partials stay within 64 GiB.
-bool dkdv_split(const vsa_plan_info &info, int heads, int head_dim)
+bool dkdv_split(const vsa_plan_info &info, int heads, int head_dim, int chunks)
 {
     const double bytes = double(heads) * info.n_tiles * 8 * (info.tile_rows / 32) * 2 * 32 * head_dim * 4;
-    return split_chunks(info, head_dim) > 1 && info.n_tiles <= 4095 && bytes <= 64.0 * (1 << 30);
+    return chunks > 1 && info.n_tiles <= 4095 && bytes <= 64.0 * (1 << 30);
 }
 
-void compute_bwd_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_bwd_layout *L)
+void compute_bwd_layout(const vsa_plan_info &info, int heads, int head_dim, int chunks, vsa_bwd_layout *L)
 {
     const size_t H = size_t(heads), D = size_t(head_dim), n_t = size_t(info.n_tiles);
     const size_t S_pad = size_t(info.rows_padded);
@@ -1384,11 +1384,12 @@ void compute_bwd_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_
     L->tbits = take(H * n_t * size_t((n_t + 31) / 32) * 4);
     // Split dq partials, only when the forward splits its key lists.
     const size_t items = H * n_t * size_t(info.tile_rows / 64);
-    L->part_dq = take(split_chunks(info, head_dim) > 1 ? items * 8 * 64 * D * 4 : 0);
-    L->part_dkv = take(dkdv_split(info, heads, head_dim) ? H * n_t * 8 * size_t(info.tile_rows / 32) * 2 * 32 * D * 4 : 0);
+    L->part_dq = take(chunks > 1 ? items * 8 * 64 * D * 4 : 0);
+    L->part_dkv = take(dkdv_split(info, heads, head_dim, chunks) ? H * n_t * 8 * size_t(info.tile_rows / 32) * 2 * 32 * D * 4 : 0);
     // fp32 O_fine saved by a training forward, only when the key lists split.
-    L->ofine = take(split_chunks(info, head_dim) > 1 ? H * S_pad * D * 4 : 0);
+    L->ofine = take(chunks > 1 ? H * S_pad * D * 4 : 0);
     L->total_bytes = off;
+    L->split_chunks = int32_t(chunks);
 }
 
 namespace {
@@ -1432,7 +1433,7 @@ template <int D, int B>
 void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, const uint16_t *v,
                 const uint16_t *q, const uint16_t *dout, const uint16_t *gate,
                 const float *o_coarse, const float *qm, const float *km, const float *vm,
-                const vsa_bwd_layout &L, char *bw, float *dgate, bool split, hipStream_t st)
+                const vsa_bwd_layout &L, char *bw, float *dgate, bool split, bool ring, hipStream_t st)
 {
     constexpr int HPB = 256 / D;
     const int H = a.H, n_t = a.n_t;
@@ -1488,7 +1489,7 @@ void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, 
     }
     {
         KernelTimer t(K_BWD_DKDV, st);
-        if (dkdv_split(info, H, D)) {
+        if (ring) {
             hipLaunchKernelGGL((dkdv_ring_kernel<D, B>), dim3(H * n_t * 8), dim3(B * 2), (RingCfg<D, B>::LDS), st, a);
             const int units = H * n_t * (B / 32);
             hipLaunchKernelGGL((dkdv_merge_kernel<D, B>), dim3((units * 2 * (D / 32) + 3) / 4), dim3(256), 0, st, a, units);
@@ -1504,7 +1505,7 @@ void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, 
 using namespace vsa;
 
 extern "C" int vsa_bwd_workspace_layout(const vsa_plan_info *info, int32_t heads, int32_t head_dim,
-                                        vsa_bwd_layout *layout)
+                                        int32_t split_chunks, vsa_bwd_layout *layout)
 {
     clear_error();
     if (!layout) return fail(VSA_ERR_ARG, "layout is null");
@@ -1512,14 +1513,16 @@ extern "C" int vsa_bwd_workspace_layout(const vsa_plan_info *info, int32_t heads
     if (heads <= 0) return fail(VSA_ERR_ARG, "heads = %d", heads);
     if (head_dim != 64 && head_dim != 128)
         return fail(VSA_ERR_UNSUPPORTED, "head_dim = %d; supported: 64, 128", head_dim);
-    compute_bwd_layout(*info, heads, head_dim, layout);
+    int chunks = 0;
+    if (int st = resolve_split(*info, head_dim, split_chunks, &chunks)) return st;
+    compute_bwd_layout(*info, heads, head_dim, chunks, layout);
     return VSA_OK;
 }
 
 extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row_src_dev,
                                    const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
-                                   int32_t k_ref, int32_t k_gen, float scale, const void *q,
-                                   const void *k, const void *v, const void *gate,
+                                   int32_t k_ref, int32_t k_gen, float scale, int32_t split_chunks,
+                                   const void *q, const void *k, const void *v, const void *gate,
                                    const void *dout, const void *workspace, size_t workspace_bytes,
                                    const int32_t *keep_idx_dev, const float *o_coarse_dev,
                                    void *bwd_workspace, size_t bwd_workspace_bytes, float *dq,
@@ -1548,12 +1551,14 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
     if (int64_t(info->rows_padded) * head_dim * 2 >= (int64_t(1) << 32))
         return fail(VSA_ERR_UNSUPPORTED, "%s: %lld padded rows x head_dim %d exceed 4 GiB per head", name,
                     (long long)info->rows_padded, head_dim);
+    int chunks = 0;
+    if (int st = resolve_split(*info, head_dim, split_chunks, &chunks)) return st;
     vsa_ws_layout L;
-    compute_layout(*info, heads, head_dim, &L);
+    compute_layout(*info, heads, head_dim, chunks, &L);
     if (workspace_bytes < L.total_bytes)
         return fail(VSA_ERR_ARG, "%s: workspace has %zu bytes, needs %zu", name, workspace_bytes, L.total_bytes);
     vsa_bwd_layout BL;
-    compute_bwd_layout(*info, heads, head_dim, &BL);
+    compute_bwd_layout(*info, heads, head_dim, chunks, &BL);
     if (bwd_workspace_bytes < BL.total_bytes)
         return fail(VSA_ERR_ARG, "%s: backward workspace has %zu bytes, needs %zu", name,
                     bwd_workspace_bytes, BL.total_bytes);
@@ -1621,7 +1626,7 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
         if (lds != VSA_OK) return fail(VSA_ERR_DEVICE, "%s: cannot raise the LDS limit of the dK/dV kernel", name);
     }
     bool split = false;
-    if (split_chunks(*info, head_dim) > 1 && saved_stats) {
+    if (chunks > 1 && saved_stats) {
         // lse came with the training forward; D_t from its saved O_fine.
         const int64_t rows = int64_t(heads) * info->rows_padded;
         KernelTimer t(K_BWD_STATS, st);
@@ -1636,20 +1641,21 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
                                static_cast<const uint16_t *>(dout), ofp, row_src_dev, heads,
                                int64_t(info->rows_padded), dtp);
         split = true;
-    } else if (split_chunks(*info, head_dim) > 1) {
-        const int stv = fine_stats(*info, row_src_dev, block_len_dev, heads, head_dim, ref, k_gen,
+    } else if (chunks > 1) {
+        const int stv = fine_stats(*info, row_src_dev, block_len_dev, heads, head_dim, chunks, ref, k_gen,
                                    ref ? k_ref : 0, a.scale, q, workspace, keep_idx_dev, dout,
                                    reinterpret_cast<float *>(bw + BL.lse),
                                    reinterpret_cast<float *>(bw + BL.dt), st);
         split = stv == VSA_OK;
     }
     const int B = info->tile_rows;
+    const bool ring = dkdv_split(*info, heads, head_dim, chunks);
     if (head_dim == 128) {
-        if (B == 64) launch_bwd<128, 64>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, st);
-        else launch_bwd<128, 128>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, st);
+        if (B == 64) launch_bwd<128, 64>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, ring, st);
+        else launch_bwd<128, 128>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, ring, st);
     } else {
-        if (B == 64) launch_bwd<64, 64>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, st);
-        else launch_bwd<64, 128>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, st);
+        if (B == 64) launch_bwd<64, 64>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, ring, st);
+        else launch_bwd<64, 128>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, ring, st);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(VSA_ERR_DEVICE, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
@@ -1658,8 +1664,8 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
 
 extern "C" int vsa_sparse_attn_fwd_train(const vsa_plan_info *info, const int32_t *row_src_dev,
                                          const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
-                                         int32_t k_ref, int32_t k_gen, float scale, const void *q,
-                                         const void *workspace, size_t workspace_bytes,
+                                         int32_t k_ref, int32_t k_gen, float scale, int32_t split_chunks,
+                                         const void *q, const void *workspace, size_t workspace_bytes,
                                          const int32_t *keep_idx_dev, const float *o_coarse_dev,
                                          const void *gate, void *out, void *bwd_workspace,
                                          size_t bwd_workspace_bytes, void *stream)
@@ -1671,8 +1677,10 @@ extern "C" int vsa_sparse_attn_fwd_train(const vsa_plan_info *info, const int32_
     if (head_dim != 64 && head_dim != 128)
         return fail(VSA_ERR_UNSUPPORTED, "%s: head_dim = %d; supported: 64, 128", name, head_dim);
     if (!bwd_workspace) return fail(VSA_ERR_ARG, "%s: null device pointer", name);
+    int chunks = 0;
+    if (int st = resolve_split(*info, head_dim, split_chunks, &chunks)) return st;
     vsa_bwd_layout BL;
-    compute_bwd_layout(*info, heads, head_dim, &BL);
+    compute_bwd_layout(*info, heads, head_dim, chunks, &BL);
     if (bwd_workspace_bytes < BL.total_bytes)
         return fail(VSA_ERR_ARG, "%s: backward workspace has %zu bytes, needs %zu", name,
                     bwd_workspace_bytes, BL.total_bytes);
@@ -1680,7 +1688,7 @@ extern "C" int vsa_sparse_attn_fwd_train(const vsa_plan_info *info, const int32_
         return fail(VSA_ERR_ARG, "%s: workspaces must be 256-byte aligned", name);
     char *bw = static_cast<char *>(bwd_workspace);
     return fine_impl(name, info, row_src_dev, block_len_dev, heads, heads, head_dim, k_ref >= 0, false,
-                     k_gen, k_ref < 0 ? 0 : k_ref, scale, q, workspace, workspace_bytes, keep_idx_dev,
+                     k_gen, k_ref < 0 ? 0 : k_ref, scale, split_chunks, q, workspace, workspace_bytes, keep_idx_dev,
                      o_coarse_dev, gate, out, stream, reinterpret_cast<float *>(bw + BL.lse),
                      reinterpret_cast<float *>(bw + BL.ofine));
 }

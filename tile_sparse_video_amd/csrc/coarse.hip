@@ -1025,11 +1025,12 @@ int coarse_impl(const char *name, const vsa_plan_info *info, const int32_t *row_
         if (int st = vsa_ref_keep_count(info, ref_sparsity, ref_keep_k, &k_ref)) return st;
     if (k_gen + k_ref > 0 && !keep_idx_dev)
         return fail(VSA_ERR_ARG, "%s: keep_idx is null with %d kept tiles per row", name, k_gen + k_ref);
+    // The coarse stage writes only the regions ahead of the fine-pass partials,
+    // which do not depend on the split count.
     vsa_ws_layout L;
-    compute_layout(*info, heads, head_dim, &L);
-    if (workspace_bytes < L.total_bytes)
-        return fail(VSA_ERR_ARG, "%s: workspace has %zu bytes, needs %zu", name, workspace_bytes,
-                    L.total_bytes);
+    compute_layout(*info, heads, head_dim, 1, &L);
+    if (workspace_bytes < L.part_o)
+        return fail(VSA_ERR_ARG, "%s: workspace has %zu bytes, needs %zu", name, workspace_bytes, L.part_o);
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
         return fail(VSA_ERR_ARG, "%s: workspace must be 256-byte aligned", name);
     if (int st = check_device()) return st;

@@ -19,19 +19,26 @@ void clear_error();
 // consistent and supported on the device path (B in {64,128}, S_pad < 2^31).
 int check_info(const vsa_plan_info *info);
 
-// Fills `layout` for a checked plan (see vsa.h for the meaning of each region).
-void compute_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_ws_layout *layout);
-void compute_bwd_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_bwd_layout *layout);
+// Fills `layout` for a checked plan and a resolved split count (see vsa.h for
+// the meaning of each region).
+void compute_layout(const vsa_plan_info &info, int heads, int head_dim, int chunks, vsa_ws_layout *layout);
+void compute_bwd_layout(const vsa_plan_info &info, int heads, int head_dim, int chunks, vsa_bwd_layout *layout);
 
-// Number of key chunks the fine pass splits each key list into (1 = no split).
-int split_chunks(const vsa_plan_info &info, int head_dim);
+// The automatic number of key chunks the fine pass splits each key list into
+// (1 = no split): a function of the plan and head_dim only.
+int auto_split_chunks(const vsa_plan_info &info, int head_dim);
+
+// Resolves a caller's split request (0 = automatic, 1..kMaxSplit = that many
+// chunks) into *chunks; VSA_ERR_ARG for anything else.
+constexpr int kMaxSplit = 64;
+int resolve_split(const vsa_plan_info &info, int head_dim, int32_t requested, int *chunks);
 
 // Backward support: runs the fine pass with split key lists and a merge that
 // writes the per-row log-sum-exp (log2 domain) and D_t = dout . O_fine
 // ([H][S_pad], tile order). Returns VSA_ERR_UNSUPPORTED when the heads are
 // too small to split (the caller then recomputes the statistics itself).
 int fine_stats(const vsa_plan_info &info, const int32_t *row_src, const int32_t *block_len, int heads,
-               int head_dim, bool ref, int k, int k_ref, float scale, const void *q,
+               int head_dim, int chunks, bool ref, int k, int k_ref, float scale, const void *q,
                const void *workspace, const int32_t *keep_idx, const void *dout, float *lse_out,
                float *dt_out, hipStream_t st);
 
@@ -46,8 +53,10 @@ enum KernelId {
     K_COUNT
 };
 
-// Scope guard around one launch: while timing is enabled it records an event
-// before the launch and one after it on `stream`; otherwise it does nothing.
+// Scope guard around one launch: while timing is enabled for `stream` it
+// records an event before the launch and one after it on that stream;
+// otherwise it does nothing.
+struct StreamTiming;
 class KernelTimer {
   public:
     KernelTimer(KernelId id, hipStream_t stream);
@@ -57,6 +66,8 @@ class KernelTimer {
 
   private:
     hipStream_t stream_;
+    StreamTiming *timing_;
+    unsigned generation_;
     long slot_;
 };
 
@@ -73,7 +84,8 @@ int coarse_impl(const char *name, const vsa_plan_info *info, const int32_t *row_
                 int32_t *keep_idx_dev, float *o_coarse_dev, void *stream);
 int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_src_dev,
               const int32_t *block_len_dev, int heads, int ld, int head_dim, bool ref, bool i8, int k,
-              int k_ref, float scale, const void *q, const void *workspace, size_t workspace_bytes,
+              int k_ref, float scale, int32_t split_req, const void *q, const void *workspace,
+              size_t workspace_bytes,
               const int32_t *keep_idx_dev, const float *o_coarse_dev, const void *gate, void *out,
               void *stream, float *lse_out, float *ofine_out);
 

@@ -34,7 +34,6 @@
 //    in G phases per head.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 
 #include "common.h"
@@ -42,22 +41,26 @@
 
 namespace vsa {
 
-static std::atomic<int> g_split_override{0};
-
 // Number of key chunks for the fine pass. Split (8 chunks, one per XCD) when
 // the K and V of one head are large enough that L2 reuse across query tiles
 // matters; beyond 96 MiB per head use 8 * G chunks taken in G phases, so the
 // K/V touched by one phase stays within what the Infinity Cache serves at
 // full speed.
-int split_chunks(const vsa_plan_info &info, int head_dim)
+int auto_split_chunks(const vsa_plan_info &info, int head_dim)
 {
-    const int forced = g_split_override.load();
-    if (forced > 0) return forced;
     const double mib = 1024.0 * 1024.0;
     const double head_kv = 2.0 * double(info.rows_padded) * head_dim * 2.0;
     if (head_kv < 16.0 * mib) return 1;
     const int phases = int(std::ceil(head_kv / (96.0 * mib)));
     return 8 * std::min(phases, 8);
+}
+
+int resolve_split(const vsa_plan_info &info, int head_dim, int32_t requested, int *chunks)
+{
+    if (requested < 0 || requested > kMaxSplit)
+        return fail(VSA_ERR_ARG, "split_chunks = %d outside [0, %d] (0 = automatic)", requested, kMaxSplit);
+    *chunks = requested > 0 ? requested : auto_split_chunks(info, head_dim);
+    return VSA_OK;
 }
 
 namespace {
@@ -813,12 +816,12 @@ void launch_fine_stats(const FineArgs &a, hipStream_t st)
 }  // namespace
 
 int fine_stats(const vsa_plan_info &info, const int32_t *row_src, const int32_t *block_len, int heads,
-               int head_dim, bool ref, int k, int k_ref, float scale, const void *q,
+               int head_dim, int chunks, bool ref, int k, int k_ref, float scale, const void *q,
                const void *workspace, const int32_t *keep_idx, const void *dout, float *lse_out,
                float *dt_out, hipStream_t st)
 {
     vsa_ws_layout L;
-    compute_layout(info, heads, head_dim, &L);
+    compute_layout(info, heads, head_dim, chunks, &L);
     const char *ws = static_cast<const char *>(workspace);
     FineArgs a{};
     a.q = static_cast<const uint16_t *>(q);
@@ -835,7 +838,7 @@ int fine_stats(const vsa_plan_info &info, const int32_t *row_src, const int32_t 
     a.n_v = info.n_video_tiles;
     a.n_t = info.n_tiles;
     a.k = k;
-    a.chunks = split_chunks(info, head_dim);
+    a.chunks = chunks;
     a.ref = ref ? 1 : 0;
     a.list_len = ref ? k + k_ref : 0;
     a.scale_log2e = scale * 1.4426950408889634f;
@@ -854,26 +857,12 @@ int fine_stats(const vsa_plan_info &info, const int32_t *row_src, const int32_t 
     return VSA_OK;
 }
 
-}  // namespace vsa
-
-using namespace vsa;
-
-extern "C" int vsa_set_split_chunks(int32_t chunks)
-{
-    clear_error();
-    if (chunks < 0 || chunks > 64) return fail(VSA_ERR_ARG, "split chunks %d outside [0, 64]", chunks);
-    g_split_override.store(chunks);
-    return VSA_OK;
-}
-
-namespace vsa {
-
 // Shared body of the fine entry points (ref: reference-sparsity lists; i8:
 // INT8 scores). ld: heads per token row of q, gate and out (the pointers
 // address the first head).
 int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_src_dev,
               const int32_t *block_len_dev, int heads, int ld, int head_dim, bool ref, bool i8, int k, int k_ref,
-              float scale, const void *q, const void *workspace, size_t workspace_bytes,
+              float scale, int32_t split_req, const void *q, const void *workspace, size_t workspace_bytes,
               const int32_t *keep_idx_dev, const float *o_coarse_dev, const void *gate, void *out,
               void *stream, float *lse_out, float *ofine_out)
 {
@@ -894,8 +883,10 @@ int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_sr
     if ((ref ? k + k_ref : k) > 0 && !keep_idx_dev)
         return fail(VSA_ERR_ARG, "%s: keep_idx is null", name);
     if (!std::isfinite(scale)) return fail(VSA_ERR_ARG, "%s: scale is not finite", name);
+    int chunks = 0;
+    if (int st = resolve_split(*info, head_dim, split_req, &chunks)) return st;
     vsa_ws_layout L;
-    compute_layout(*info, heads, head_dim, &L);
+    compute_layout(*info, heads, head_dim, chunks, &L);
     if (workspace_bytes < L.total_bytes)
         return fail(VSA_ERR_ARG, "%s: workspace has %zu bytes, needs %zu", name, workspace_bytes,
                     L.total_bytes);
@@ -906,7 +897,6 @@ int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_sr
         return fail(VSA_ERR_UNSUPPORTED, "%s: %lld padded rows x head_dim %d exceed 4 GiB per head", name,
                     (long long)info->rows_padded, head_dim);
     const int64_t items = int64_t(heads) * info->n_tiles * (info->tile_rows / 64);
-    const int chunks = split_chunks(*info, head_dim);
     if (items * chunks >= (int64_t(1) << 31))
         return fail(VSA_ERR_UNSUPPORTED, "%s: too many work items (%lld)", name,
                     (long long)(items * chunks));
@@ -958,41 +948,45 @@ int fine_impl(const char *name, const vsa_plan_info *info, const int32_t *row_sr
 
 }  // namespace vsa
 
+using namespace vsa;
+
 extern "C" int vsa_sparse_attn_fwd(const vsa_plan_info *info, const int32_t *row_src_dev,
                                    const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
-                                   int32_t k, float scale, const void *q, const void *workspace,
-                                   size_t workspace_bytes, const int32_t *keep_idx_dev,
-                                   const float *o_coarse_dev, const void *gate, void *out,
-                                   void *stream)
+                                   int32_t k, float scale, int32_t split_chunks, const void *q,
+                                   const void *workspace, size_t workspace_bytes,
+                                   const int32_t *keep_idx_dev, const float *o_coarse_dev,
+                                   const void *gate, void *out, void *stream)
 {
     clear_error();
     return fine_impl("vsa_sparse_attn_fwd", info, row_src_dev, block_len_dev, heads, heads, head_dim, false,
-                     false, k, 0, scale, q, workspace, workspace_bytes, keep_idx_dev, o_coarse_dev, gate,
-                     out, stream, nullptr, nullptr);
+                     false, k, 0, scale, split_chunks, q, workspace, workspace_bytes, keep_idx_dev,
+                     o_coarse_dev, gate, out, stream, nullptr, nullptr);
 }
 
 extern "C" int vsa_sparse_attn_fwd_ref(const vsa_plan_info *info, const int32_t *row_src_dev,
                                        const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
-                                       int32_t k_ref, int32_t k_gen, float scale, const void *q,
+                                       int32_t k_ref, int32_t k_gen, float scale,
+                                       int32_t split_chunks, const void *q,
                                        const void *workspace, size_t workspace_bytes,
                                        const int32_t *keep_idx_dev, const float *o_coarse_dev,
                                        const void *gate, void *out, void *stream)
 {
     clear_error();
     return fine_impl("vsa_sparse_attn_fwd_ref", info, row_src_dev, block_len_dev, heads, heads, head_dim,
-                     true, false, k_gen, k_ref, scale, q, workspace, workspace_bytes, keep_idx_dev,
-                     o_coarse_dev, gate, out, stream, nullptr, nullptr);
+                     true, false, k_gen, k_ref, scale, split_chunks, q, workspace, workspace_bytes,
+                     keep_idx_dev, o_coarse_dev, gate, out, stream, nullptr, nullptr);
 }
 
 extern "C" int vsa_sparse_attn_fwd_i8(const vsa_plan_info *info, const int32_t *row_src_dev,
                                       const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
-                                      int32_t k_ref, int32_t k_gen, float scale, const void *q,
+                                      int32_t k_ref, int32_t k_gen, float scale,
+                                      int32_t split_chunks, const void *q,
                                       void *workspace, size_t workspace_bytes,
                                       const int32_t *keep_idx_dev, const float *o_coarse_dev,
                                       const void *gate, void *out, void *stream)
 {
     clear_error();
     return fine_impl("vsa_sparse_attn_fwd_i8", info, row_src_dev, block_len_dev, heads, heads, head_dim,
-                     k_ref >= 0, true, k_gen, k_ref < 0 ? 0 : k_ref, scale, q, workspace,
+                     k_ref >= 0, true, k_gen, k_ref < 0 ? 0 : k_ref, scale, split_chunks, q, workspace,
                      workspace_bytes, keep_idx_dev, o_coarse_dev, gate, out, stream, nullptr, nullptr);
 }

@@ -61,7 +61,7 @@ extern "C" int vsa_layer_fwd_groups(const vsa_head_group *groups, int32_t n_grou
             if (int st = vsa_ref_keep_count(g.info, g.ref_sparsity, g.ref_keep_k, &kr[size_t(i)]))
                 return wrap(st, i);
         vsa_ws_layout L;
-        if (int st = vsa_workspace_layout(g.info, g.heads, head_dim, &L)) return wrap(st, i);
+        if (int st = vsa_workspace_layout(g.info, g.heads, head_dim, g.split_chunks, &L)) return wrap(st, i);
         if (!g.row_src_dev || !g.block_len_dev || !g.workspace || !g.o_coarse_dev)
             return fail(VSA_ERR_ARG, "vsa_layer_fwd_groups: group %d: null device pointer", i);
         if ((g.ref ? kk[size_t(i)] + kr[size_t(i)] : kk[size_t(i)]) > 0 && !g.keep_idx_dev)
@@ -83,8 +83,8 @@ extern "C" int vsa_layer_fwd_groups(const vsa_head_group *groups, int32_t n_grou
                                  g.o_coarse_dev, stream))
             return st;
         if (int st = fine_impl(name, g.info, g.row_src_dev, g.block_len_dev, g.heads, heads_total, head_dim,
-                               g.ref != 0, g.int8 != 0, kk[size_t(i)], kr[size_t(i)], scale, at(q),
-                               g.workspace, g.workspace_bytes, g.keep_idx_dev, g.o_coarse_dev, at(gate),
+                               g.ref != 0, g.int8 != 0, kk[size_t(i)], kr[size_t(i)], scale,
+                               g.split_chunks, at(q), g.workspace, g.workspace_bytes, g.keep_idx_dev, g.o_coarse_dev, at(gate),
                                static_cast<char *>(out) + first, stream, nullptr, nullptr))
             return st;
     }

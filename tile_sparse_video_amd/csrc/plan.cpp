@@ -111,10 +111,10 @@ int check_info(const vsa_plan_info *info)
     return VSA_OK;
 }
 
-void compute_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_ws_layout *L)
+void compute_layout(const vsa_plan_info &info, int heads, int head_dim, int chunks, vsa_ws_layout *L)
 {
     const size_t H = size_t(heads), D = size_t(head_dim);
-    const size_t n_t = size_t(info.n_tiles), n_v = size_t(info.n_video_tiles);
+    const size_t n_t = size_t(info.n_tiles);
     const size_t S_pad = size_t(info.rows_padded);
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -129,17 +129,19 @@ void compute_layout(const vsa_plan_info &info, int heads, int head_dim, vsa_ws_l
     L->v_mean = take(H * n_t * D * 4);
     // Coarse scores: [H][n_v][n_v] on the default path, [H][n_t][n_t] with
     // reference sparsity (every query tile against every key tile).
-    (void)n_v;
     L->scores = take(H * n_t * n_t * 4);
     const size_t items = H * n_t * size_t(info.tile_rows / 64);
-    const size_t C = size_t(split_chunks(info, head_dim));
-    L->part_o = take(C > 1 ? items * C * 64 * D * 2 : 0);
-    L->part_ml = take(C > 1 ? items * C * 128 * 4 : 0);
     // INT8 fine pass: K codes in tile order (one byte per element) and one fp32
     // scale per 64-row block.
     L->k_i8 = take(H * S_pad * D);
     L->k_scale = take(items * 4);
+    // Fine-pass chunk partials last: everything before them is independent of
+    // the split count, so the coarse stage needs only that prefix.
+    const size_t C = size_t(chunks);
+    L->part_o = take(C > 1 ? items * C * 64 * D * 2 : 0);
+    L->part_ml = take(C > 1 ? items * C * 128 * 4 : 0);
     L->total_bytes = off;
+    L->split_chunks = int32_t(chunks);
 }
 
 }  // namespace vsa
@@ -335,7 +337,7 @@ int vsa_tile_pair_fraction(const vsa_plan_info *info, int32_t k, double *fractio
 }
 
 int vsa_workspace_layout(const vsa_plan_info *info, int32_t heads, int32_t head_dim,
-                         vsa_ws_layout *layout)
+                         int32_t split_chunks, vsa_ws_layout *layout)
 {
     clear_error();
     if (!layout) return fail(VSA_ERR_ARG, "layout is null");
@@ -343,7 +345,9 @@ int vsa_workspace_layout(const vsa_plan_info *info, int32_t heads, int32_t head_
     if (heads <= 0) return fail(VSA_ERR_ARG, "heads = %d", heads);
     if (head_dim != 64 && head_dim != 128)
         return fail(VSA_ERR_UNSUPPORTED, "head_dim = %d; supported: 64, 128", head_dim);
-    compute_layout(*info, heads, head_dim, layout);
+    int chunks = 0;
+    if (int st = resolve_split(*info, head_dim, split_chunks, &chunks)) return st;
+    compute_layout(*info, heads, head_dim, chunks, layout);
     return VSA_OK;
 }
 
