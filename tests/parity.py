@@ -22,6 +22,35 @@ MAX_ABS = 2e-2
 REL_L2 = 1e-2
 
 
+def bf16_ulp(x) -> np.ndarray:
+    """Spacing of bf16 numbers at |x|: 2^(e - 7) for |x| in [2^e, 2^(e + 1)) (8
+    significant bits), 2^-133 below the normal range."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
+def output_bar(got, ref) -> np.ndarray:
+    """Per-element bar for bf16 layer outputs against the oracle's bf16 result:
+    max-abs 2e-2, except where one bf16 step of the value is larger (|value| >= 4,
+    one step = 2^-5 or more): there the two roundings of nearly equal fp32 and fp64
+    results may land one step apart, so one step is the bar."""
+    return np.maximum(MAX_ABS, bf16_ulp(ref))
+
+
+def check_output(got, ref, what: str = "") -> tuple:
+    """Asserts the output bar element-wise and rel-L2 <= 1e-2; returns (max-abs, rel-L2)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    mx, rl = float(err.max()) if err.size else 0.0, rel_l2(got, ref)
+    bad = err > output_bar(got, ref)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements beyond the bar, worst "
+                           f"{float(err[bad].max())} at |ref| {float(np.abs(ref[bad]).max())}")
+    assert rl <= REL_L2, f"{what}: rel-L2 {rl}"
+    return mx, rl
+
+
 def rel_l2(a, b) -> float:
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)

@@ -99,7 +99,7 @@ def check_layer_i8(inp, run, heads, tokens, ref_mode=False, ref_sparsity=None, r
         mx, rl = float(np.abs(got - ref).max()), parity.rel_l2(got, ref)
         worst.append((mx, rl))
         dist.append(parity.rel_l2(got, ref_exact))
-        assert mx <= parity.MAX_ABS and rl <= parity.REL_L2, f"head {h}: max-abs {mx} rel-L2 {rl}"
+        parity.check_output(got, ref, f"head {h}")
         assert dist[-1] <= EXACT_REL_L2, f"head {h}: {dist[-1]} from the unquantised layer"
     print(f"[{wl.name} int8] worst max-abs {max(w[0] for w in worst):.3e} rel-L2 "
           f"{max(w[1] for w in worst):.3e}; vs unquantised rel-L2 {max(dist):.3e}", flush=True)

@@ -107,12 +107,14 @@ def test_tile_means_exact_cases(orc):
 
 def test_tile_means_sequential_order(orc):
     """Ascending-row fp32 summation, not pairwise or reversed: 2^24 + 1 + 1 ... cases."""
-    pl = orc.plan([3], (1, 1, 1), (1, 1, 4))  # one prefix tile of 3 rows (B = 4)
+    pl = orc.plan([3], (1, 1, 1), (1, 1, 4))  # one prefix tile of 3 rows (B = 4), one video token
+    assert pl.S == 4
     # rows: 2^24, 1, 1 -> ((2^24 + 1) + 1) = 2^24 in ascending fp32 order
-    # (reversed order would give 2^24 + 2)
-    vals = np.array([2.0 ** 24, 1.0, 1.0], dtype=np.float32).reshape(3, 1, 1)
+    # (reversed order would give 2^24 + 2); the video token is its own tile
+    vals = np.array([2.0 ** 24, 1.0, 1.0, 5.0], dtype=np.float32).reshape(4, 1, 1)
     m = orc.tile_means(bits_of(vals), 0, pl)
     assert m[0, 0] == np.float32(2.0 ** 24 / 3)
+    assert m[1, 0] == np.float32(5.0)
 
 
 # ------------------------------------------------------------------- scores --
@@ -322,3 +324,20 @@ def test_gate_proj_is_correctly_rounded_matmul(orc):
     assert (err <= np.abs(orc.bf16_value(hi.astype(np.uint16)) - exact) * (1 + 1e-12)).all()
     sub = orc.gate_proj(x, W, tokens=[5, 0, 36])
     assert np.array_equal(sub, g[[5, 0, 36]])
+
+
+def test_bf16_step_of_the_output_bar():
+    """The output bar's bf16 step: 2^(e-7) on [2^e, 2^(e+1)); the bar is 2e-2 up to
+    |value| < 4 and one step (2^-5, 2^-4, ...) from 4 on."""
+    from tests import parity
+    vals = np.array([1.0, 1.99, 2.0, 3.999, 4.0, -5.0, 8.0, 0.0, 1e-40])
+    want = np.array([2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -6, 2.0 ** -5, 2.0 ** -5, 2.0 ** -4,
+                     2.0 ** -133, 2.0 ** -133])
+    assert np.array_equal(parity.bf16_ulp(vals), want)
+    bar = parity.output_bar(vals, vals)
+    assert np.array_equal(bar, np.maximum(2e-2, want))
+    # consecutive bf16 numbers differ by exactly the step
+    for v in (1.0, 3.0, 4.0, 6.5, 100.0):
+        b = int(np.float32(v).view(np.uint32) >> 16)
+        nxt = np.uint32((b + 1) << 16).view(np.float32)
+        assert float(nxt) - v == parity.bf16_ulp(v)
