@@ -14,14 +14,19 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Iterable, Optional, Sequence
 
 import numpy as np
+from threadpoolctl import threadpool_limits
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIBRARY names another build of oracle.c (the host-sanitizer build of
+# build(sanitize=True)); by default the in-tree liboracle.so.
+_LIB_PATH = os.environ.get("ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
+_SANITIZED_LIB = os.path.join(_HERE, "liboracle_san.so")
 _lib = None
 
 _I32P = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
@@ -32,13 +37,24 @@ _F32P = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
 _F64P = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 
 
-def build() -> str:
-    """Compile liboracle.so with gcc (plain C, OpenMP, no FMA contraction)."""
-    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-fPIC", "-shared", _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+def build(sanitize: bool = False) -> str:
+    """Compile liboracle.so with gcc (plain C, OpenMP, no FMA contraction).
+    sanitize=True: the same source with clang and host AddressSanitizer +
+    UndefinedBehaviorSanitizer (the runtime the HIP library's sanitizer build
+    uses), into liboracle_san.so."""
+    if sanitize:
+        out = _SANITIZED_LIB
+        cmd = ["/opt/rocm/lib/llvm/bin/clang", "-std=c11", "-O1", "-fopenmp", "-ffp-contract=off",
+               "-fno-fast-math", "-fPIC", "-shared", "-fsanitize=address,undefined",
+               "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-shared-libsan", _SRC,
+               "-o", out + ".tmp", "-lm"]
+    else:
+        out = os.path.join(_HERE, "liboracle.so")
+        cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", _SRC, "-o", out + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
-    return _LIB_PATH
+    os.replace(out + ".tmp", out)
+    return out
 
 
 def _load():
@@ -442,6 +458,75 @@ def dq_tokens(Q, K, V, G, dOut, h: int, pl: Plan, csr, scale: float, tokens, mea
     if rc != 0:
         raise OracleError("dq: a query has an empty key list")
     return out
+
+
+def dkdv_tile(Q, K, V, G, dOut, h: int, pl: Plan, csr, scale: float, tile: int, means=None):
+    """dk, dv (fp64 [B][D], tile rows in order, padding rows 0) of the key rows of
+    one tile jt = `tile` of head h: the gradient orc_layer_bwd computes, restricted
+    to those rows, for element-wise checks at full size.
+
+    A key row u of tile jt receives gradient from the query tokens t whose tile's
+    key list holds jt, plus the mean's share of the coarse path:
+      dv[u] = dvm_jt / n_jt + sum_t p_tu dout_t,
+      dk[u] = dkm_jt / n_jt + sum_t scale p_tu (dout_t . v_u - D_t) q_t,
+    with p_tu the softmax of t over all of its keys, D_t = dout_t . O_fine[t], and
+    (dkm, dvm)_jt the column jt of the tile-level attention's gradient (every query
+    tile i contributes through P_c[i][jt], dO_c[i] = sum_{t in i} dout_t * g_t and
+    D_c[i] = dO_c[i] . O_c[i]). Written with fp64 numpy matrix products as steps."""
+    S, H, D = Q.shape
+    B, n_t = pl.B, pl.n_t
+    qm, km, vm = means if means is not None else (tile_means(X, h, pl) for X in (Q, K, V))
+    qm, km, vm = (np.asarray(m, dtype=np.float64) for m in (qm, km, vm))
+    x = lambda A: bf16_value(np.asarray(A)[:, h, :])                  # noqa: E731  fp64 [S][D]
+    q, k, v, go = x(Q), x(K), x(V), x(dOut)
+    g = bf16_value(np.asarray(G).reshape(S, H, D)[:, h, :])
+    rows = pl.row_src.reshape(n_t, B)
+    # coarse path: column jt of the tile attention's gradient
+    z = scale * (qm @ km.T)
+    pc = np.exp(z - z.max(axis=1, keepdims=True))
+    pc /= pc.sum(axis=1, keepdims=True)
+    oc = pc @ vm
+    doc = np.zeros((n_t, D))
+    real = pl.row_src >= 0
+    np.add.at(doc, np.nonzero(real)[0] // B, go[pl.row_src[real]] * g[pl.row_src[real]])
+    dc = (doc * oc).sum(axis=1)
+    dz = pc[:, tile] * (doc @ vm[tile] - dc)
+    dkm = scale * (dz @ qm)
+    dvm = pc[:, tile] @ doc
+    own = rows[tile]
+    ok = own >= 0
+    n_j = int(pl.block_len[tile])
+    dk = np.zeros((B, D))
+    dv = np.zeros((B, D))
+    dk[ok] = dkm / n_j
+    dv[ok] = dvm / n_j
+    # fine path: every query tile whose key list holds jt, in ascending order
+    off, ids = csr
+    vj = v[own[ok]]
+
+    def contribution(i):
+        lst = ids[off[i]:off[i + 1]]
+        blk = rows[lst]                                   # [tiles][B] key rows, -1 = padding
+        keys = blk[blk >= 0]
+        of_jt = np.repeat(lst, (blk >= 0).sum(axis=1)) == tile   # key columns of tile jt
+        qi = rows[i][rows[i] >= 0]
+        zi = scale * (q[qi] @ k[keys].T)
+        p = np.exp(zi - zi.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        dt = (go[qi] * (p @ v[keys])).sum(axis=1)
+        pj = p[:, of_jt]
+        ds = pj * (go[qi] @ vj.T - dt[:, None])
+        return scale * (ds.T @ q[qi]), pj.T @ go[qi]
+
+    # the query tiles whose key list holds jt; computed on a thread pool (numpy
+    # releases the interpreter lock), added in ascending order
+    tiles = [i for i in range(n_t) if tile in ids[off[i]:off[i + 1]]]
+    with threadpool_limits(1), ThreadPoolExecutor(len(os.sched_getaffinity(0))) as pool:
+        parts = list(pool.map(contribution, tiles))
+    for pk, pv in parts:
+        dk[ok] += pk
+        dv[ok] += pv
+    return dk, dv
 
 
 # ------------------------------------------------------- the layer, in order --

@@ -115,21 +115,27 @@ def test_bwd_mid_two_heads():
     run_case(wl, heads=[0, wl.heads - 1])
 
 
-@pytest.mark.parametrize("name,train", [("h3", False), ("veda", False), ("h3", True)])
-def test_bwd_full_size_sampled(name, train):
-    """Full-size layers: dq on sampled tokens against the oracle, dg = dout * O_coarse
+def host_gate(wl, seed=77):
+    """A seeded bf16 gate drawn on the host, fed as the same bytes to both sides."""
+    gen = torch.Generator().manual_seed(seed)
+    return (torch.randn(wl.tokens, wl.heads * wl.head_dim, generator=gen) * 0.5).to(torch.bfloat16)
+
+
+@pytest.mark.timeout(1500)
+@pytest.mark.parametrize("name,train,all_heads", [("h3", False, False), ("veda", False, True),
+                                                  ("h3", True, True)])
+def test_bwd_full_size(name, train, all_heads):
+    """Full-size layers, both sides fed the same host-drawn gate: dk and dv of one
+    sampled key tile per head element by element against the oracle (every head,
+    or 8 spread heads), dq of 128 sampled tokens on 8 heads, dg = dout * O_coarse
     on every token, and the identities sum(dv) = sum(dout * (1 + g)), sum(dk) = 0."""
     wl = workloads.WORKLOADS[name]
     print(f"[gpu] bwd full size {name}: inputs", flush=True)
     inp = parity.make_inputs(wl)
     pl = parity.oracle_plan(wl)
     dev = "cuda"
-    import tile_sparse_video_amd as tsv
-    xd, wd = inp.x.to(dev), inp.w.to(dev)
-    g = torch.empty((wl.tokens, wl.heads * wl.head_dim), dtype=torch.bfloat16, device=dev)
-    tsv.vsa_gate_proj(xd, wd, g)
-    del xd, wd
-    run = parity.run_gpu(inp, gate=g)
+    g_host = host_gate(wl)
+    run = parity.run_gpu(inp, gate=g_host)
     dout = make_dout(wl).to(dev)
     qd, kd, vd = (t.to(dev) for t in (inp.q, inp.k, inp.v))
     if train:
@@ -151,21 +157,50 @@ def test_bwd_full_size_sampled(name, train):
     assert parity.rel_l2(sdv.cpu().numpy(), want_sdv.cpu().numpy()) < 1e-3
     sdk = dk.double().sum(0).abs()
     assert (sdk <= 1e-2 * dk.double().abs().sum(0) + 1e-6).all()
+    keep_gpu = run.att.keep_idx.cpu().numpy()
     scale = wl.head_dim ** -0.5
     k = parity.oracle_k(wl, pl)
-    toks = parity.sample_tokens(pl, 48, 11)
-    g_bits = parity.bits(run.g.cpu())
+    H = wl.heads
+    spread = sorted({int(h) for h in np.linspace(0, H - 1, 8).round()})
+    dk_heads = list(range(H)) if all_heads else spread
+    # one key tile per head: a video tile, and a prefix tile (kept by every query
+    # tile) on the first and last head
+    rng = np.random.default_rng(13)
+    tiles = {h: (int(rng.integers(pl.P)) if h in (dk_heads[0], dk_heads[-1]) and pl.P
+                 else pl.P + int(rng.integers(pl.n_v))) for h in dk_heads}
+    dkdv_host = {}
+    for h, t in tiles.items():
+        rows = torch.from_numpy(np.maximum(pl.row_src[t * pl.B:(t + 1) * pl.B], 0).astype(np.int64)).to(dev)
+        dkdv_host[h] = (dk[rows, h].cpu().numpy(), dv[rows, h].cpu().numpy())
+    toks = parity.sample_tokens(pl, 128, 11)
     dq_host = dq[torch.from_numpy(toks).to(dev)].cpu().numpy()
     del run, dq, dk, dv, dg
     torch.cuda.empty_cache()
-    for h in sorted({0, wl.heads - 1}):
-        print(f"[gpu] bwd full size {name}: oracle head {h}", flush=True)
+    g_bits, d_bits = parity.bits(g_host), parity.bits(dout.cpu())
+    worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for h in dk_heads:
         hr = oracle.head(inp.qb, inp.kb, inp.vb, h, pl, k, scale)
+        assert np.array_equal(keep_gpu[h], hr.keep), f"keep-sets, head {h}"
         csr = oracle.key_lists_default(pl, hr.keep)
-        want = oracle.dq_tokens(inp.qb, inp.kb, inp.vb, g_bits, parity.bits(dout.cpu()), h, pl, csr,
-                                scale, toks, means=(hr.qm, hr.km, hr.vm))
-        got = dq_host[:, h, :].astype(np.float64)
-        rl = parity.rel_l2(got, want)
-        mx = float(np.abs(got - want).max() / np.abs(want).max())
-        print(f"[{name} bwd] head {h} dq rel-L2 {rl:.2e} max {mx:.2e}", flush=True)
-        assert rl <= GRAD_REL_L2 and mx <= GRAD_MAX_REL
+        means = (hr.qm, hr.km, hr.vm)
+        t = tiles[h]
+        real = pl.row_src[t * pl.B:(t + 1) * pl.B] >= 0
+        want_k, want_v = oracle.dkdv_tile(inp.qb, inp.kb, inp.vb, g_bits, d_bits, h, pl, csr, scale,
+                                          t, means=means)
+        for nm, got, want in (("dk", dkdv_host[h][0], want_k), ("dv", dkdv_host[h][1], want_v)):
+            got, want = got[real].astype(np.float64), want[real]
+            rl = parity.rel_l2(got, want)
+            mx = float(np.abs(got - want).max() / np.abs(want).max())
+            worst[nm] = max(worst[nm], rl)
+            assert rl <= GRAD_REL_L2 and mx <= GRAD_MAX_REL, f"{nm} head {h} tile {t}: {rl} {mx}"
+        if h in spread:
+            want = oracle.dq_tokens(inp.qb, inp.kb, inp.vb, g_bits, d_bits, h, pl, csr, scale, toks,
+                                    means=means)
+            got = dq_host[:, h, :].astype(np.float64)
+            rl = parity.rel_l2(got, want)
+            mx = float(np.abs(got - want).max() / np.abs(want).max())
+            worst["dq"] = max(worst["dq"], rl)
+            assert rl <= GRAD_REL_L2 and mx <= GRAD_MAX_REL, f"dq head {h}: {rl} {mx}"
+        print(f"[{name} bwd] head {h}: dk/dv of tile {t} "
+              f"({'prefix' if t < pl.P else 'video'}) ok", flush=True)
+    print(f"[{name} bwd] worst rel-L2 {worst}", flush=True)

@@ -129,3 +129,59 @@ def test_dq_tokens_matches_full_backward(orc):
         toks = np.array([0, 3, 11, pl.S - 1, pl.S // 2])
         got = orc.dq_tokens(Q, K, V, G, dO, h, pl, csr, D ** -0.5, toks)
         assert np.allclose(got, full["dq"][toks], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("segs,grid,tile,mode,kk", CASES)
+def test_dkdv_tile_matches_torch_autograd(orc, segs, grid, tile, mode, kk):
+    """dk and dv of one key tile at a time (the full-size check's oracle) against
+    torch autograd of the dense formulation, for every tile of the plan; padding
+    rows come back zero."""
+    pl = orc.plan(segs, grid, tile)
+    H, D = 2, 32
+    Q, K, V = (rand_bf16((pl.S, H, D), s) for s in (71, 72, 73))
+    G = rand_bf16((pl.S, H * D), 74, scale=0.5)
+    dO = rand_bf16((pl.S, H, D), 75)
+    scale = D ** -0.5
+    rng = np.random.default_rng(9)
+    h = 1
+    if mode == "default":
+        keep = np.sort(np.stack([rng.choice(pl.n_v, size=kk, replace=False)
+                                 for _ in range(pl.n_v)]), axis=1).astype(np.int32) + pl.P
+        csr = orc.key_lists_default(pl, keep)
+    else:
+        k_ref, k_gen = kk
+        lists = np.stack([np.concatenate([np.sort(rng.choice(pl.P, k_ref, replace=False)),
+                                          np.sort(rng.choice(pl.n_v, k_gen, replace=False)) + pl.P])
+                          for _ in range(pl.n_t)]).astype(np.int32)
+        csr = orc.key_lists_explicit(lists)
+    off, ids = csr
+    lists_py = [ids[off[i]:off[i + 1]] for i in range(pl.n_t)]
+    want = torch_layer_grads(orc, pl, segs, grid, tile, Q, K, V, G, dO, h, lists_py, scale)
+    for j in range(pl.n_t):
+        dk, dv = orc.dkdv_tile(Q, K, V, G, dO, h, pl, csr, scale, j)
+        rows = pl.row_src[j * pl.B:(j + 1) * pl.B]
+        real = rows >= 0
+        assert not dk[~real].any() and not dv[~real].any()
+        assert np.allclose(dk[real], want["dk"][rows[real]], rtol=1e-5, atol=1e-6), j
+        assert np.allclose(dv[real], want["dv"][rows[real]], rtol=1e-5, atol=1e-6), j
+
+
+def test_dkdv_tile_matches_full_backward(orc):
+    """The same gradient as the whole-layer oracle, tile by tile, to fp64 rounding."""
+    segs, grid, tile = (5, 70), (5, 6, 9), (4, 4, 4)
+    pl = orc.plan(segs, grid, tile)
+    H, D = 2, 32
+    Q, K, V = (rand_bf16((pl.S, H, D), s) for s in (81, 82, 83))
+    G = rand_bf16((pl.S, H * D), 84)
+    dO = rand_bf16((pl.S, H, D), 85)
+    for h in range(H):
+        hr = orc.head(Q, K, V, h, pl, 3, D ** -0.5)
+        csr = orc.key_lists_default(pl, hr.keep)
+        full = orc.layer_bwd(Q, K, V, G, dO, h, pl, csr, D ** -0.5)
+        for j in range(pl.n_t):
+            dk, dv = orc.dkdv_tile(Q, K, V, G, dO, h, pl, csr, D ** -0.5, j,
+                                   means=(hr.qm, hr.km, hr.vm))
+            rows = pl.row_src[j * pl.B:(j + 1) * pl.B]
+            real = rows >= 0
+            assert np.allclose(dk[real], full["dk"][rows[real]], rtol=1e-11, atol=1e-13), (h, j)
+            assert np.allclose(dv[real], full["dv"][rows[real]], rtol=1e-11, atol=1e-13), (h, j)
