@@ -20,7 +20,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libvsa.so")
+# VSA_LIBRARY names another build of the same library (the host-sanitizer build
+# of build.py --sanitize); by default the in-tree libvsa.so.
+LIB_PATH = os.environ.get("VSA_LIBRARY") or os.path.join(_HERE, "libvsa.so")
 
 VSA_OK = 0
 VSA_ERR_ARG = -1

@@ -52,22 +52,37 @@ def _run(cmd, verbose):
         print(msgs, file=sys.stderr)
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer (build(sanitize=True)):
+# each flag applies to the host compilation only, never to the gfx950 code.
+SANITIZE = ["-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=all",
+            "-fno-omit-frame-pointer"]
+SANITIZED_LIB = os.path.join(HERE, "_build_san", "libvsa.so")
+
+
+def build(verbose: bool = False, extra_flags=(), sanitize: bool = False) -> str:
+    """Compiles every source and links libvsa.so in-tree. sanitize=True builds the
+    host-sanitizer variant into _build_san/libvsa.so instead (load it with
+    VSA_LIBRARY=<path> and the clang ASan runtime preloaded; tests/run_sanitized.py
+    does both)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    objdir = os.path.join(HERE, "_build")
+    objdir = os.path.join(HERE, "_build_san" if sanitize else "_build")
     os.makedirs(objdir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    host_san = [x for f in SANITIZE for x in ("-Xarch_host", f)] if sanitize else []
     objs = [os.path.join(objdir, src + ".o") for src in SOURCES]
-    cmds = [[hipcc, *HIPCC_FLAGS, *PER_SOURCE.get(src, []), *extra_flags, *inc, "-c",
+    cmds = [[hipcc, *HIPCC_FLAGS, *PER_SOURCE.get(src, []), *host_san, *extra_flags, *inc, "-c",
              os.path.join(CSRC, src), "-o", obj] for src, obj in zip(SOURCES, objs)]
     with ThreadPoolExecutor(max_workers=len(cmds)) as pool:
         for f in [pool.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    lib = SANITIZED_LIB if sanitize else LIB
+    link_san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                "-Xarch_host", "-shared-libsan"] if sanitize else []
+    tmp = lib + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_san, *objs, "-o", tmp], verbose)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:]))

@@ -617,7 +617,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
                     cand[sel ? pos : kTopkCand1 + lane] = make_uint2(key[e], uint32_t(kWave * e + lane));
                     base += __popcll(msk);
                 }
-                // The wave reads back its own LDS stores: ordered by the LDS queue.
+                // The wave reads back slots other lanes stored: release the
+                // stores, keep the compiler from moving LDS accesses across
+                // this point, then acquire (no instruction cost on one wave).
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 if (m <= 4 * kWave)
                     topk_finish<4>(cand, m, k, tlo, lane, id_first, out);
                 else
