@@ -106,6 +106,40 @@ def compute_passes(wl, plan, kernels, k_ref=None):
     return out
 
 
+def selection_report(att, max_heads: int = 8) -> dict:
+    """How non-uniform and how spatially coherent the coarse selection is (the
+    default mode's video x video scores and keep lists), on up to max_heads spread
+    heads, computed after the timed region:
+      score_cv: per query tile, std / mean of its coarse softmax weights
+        exp(scale (s_ij - max_j s_ij)) over the video key tiles, averaged over rows
+        (0 for a uniform row);
+      kept_weight: share of those weights on the kept tiles (k / n_v if uniform);
+      adjacent_overlap: |keep(i) and keep(i+1)| / k for consecutive video query
+        tiles i, i+1 (w-neighbours except at row ends), averaged; a random choice
+        of k of n_v tiles gives k / n_v."""
+    plan = att.plan
+    n_v, P, k = plan.n_v, plan.P, att.k
+    if att.ref or k == 0 or n_v < 2:
+        return {}
+    H, D = att.heads, att.head_dim
+    scale = att.scale if att.scale > 0 else D ** -0.5
+    sc = att.workspace_view("scores", torch.float32, (H, n_v, n_v))
+    heads = sorted({int(h) for h in np.linspace(0, H - 1, min(H, max_heads)).round()})
+    cv, kept, ovl = [], [], []
+    for h in heads:
+        s = sc[h].double()
+        w = torch.exp(scale * (s - s.max(dim=1, keepdim=True).values))
+        cv.append((w.std(dim=1) / w.mean(dim=1)).mean().item())
+        keep = att.keep_idx[h].long() - P                       # [n_v][k] video tile ids
+        kept.append((w.gather(1, keep).sum(1) / w.sum(1)).mean().item())
+        mask = torch.zeros((n_v, n_v), dtype=torch.bool, device=s.device)
+        mask.scatter_(1, keep, True)
+        ovl.append(((mask[:-1] & mask[1:]).sum(1).double() / k).mean().item())
+    return {"heads": heads, "score_cv": round(float(np.mean(cv)), 4),
+            "kept_weight": round(float(np.mean(kept)), 4), "uniform_kept_weight": round(k / n_v, 4),
+            "adjacent_overlap": round(float(np.mean(ovl)), 4), "random_overlap": round(k / n_v, 4)}
+
+
 def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops, k_ref=None, int8=False):
     """The oracle, as it stands, on a bounded sample of this layer, scaled to one layer.
     k_ref is not None in the reference-sparsity mode; int8 times the INT8 fine pass."""
@@ -447,6 +481,7 @@ def main() -> int:
         "hbm_passes": hbm_passes(wl, att.plan, kernels, att.k, att.k_ref if att.ref else None),
         "compute_passes": compute_passes(wl, att.plan, kernels, att.k_ref if att.ref else None),
         "wall_s": round(wall, 3),
+        "selection": selection_report(att),
         "roofline": {
             "kernel": ("fine_attn_kernel, INT8 scores (vsa_sparse_attn_fwd_i8; peak mixes the "
                        "int8 and bf16 MFMA peaks per kept pair)" if args.int8 else
