@@ -468,6 +468,40 @@ int vsa_sparse_attn_fwd_train(const vsa_plan_info *info, const int32_t *row_src_
                               const void *gate, void *out, void *bwd_workspace,
                               size_t bwd_workspace_bytes, void *stream);
 
+/* ------------------------------------------- layer without allocation -- */
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the layer
+ * of vsa_coarse_topk followed by vsa_sparse_attn_fwd (default mode, key lists
+ * never split, i.e. split_chunks = 1), with the workspace taken from a static
+ * device array of VSA_STATIC_WORKSPACE_BYTES inside the library instead of
+ * from the caller. Each device the library runs on holds one such array until
+ * the process ends; its address is looked up on the first call on a device.
+ *
+ * The results are those of vsa_coarse_topk + vsa_sparse_attn_fwd(...,
+ * split_chunks = 1, ...) on the same arguments, bit for bit. The caller still
+ * owns and passes every input and output: q, k, v (bf16 [S][H][D]), gate
+ * (bf16 [S][H*D]), keep_idx_dev (out int32 [H][n_v][k]; NULL allowed when k
+ * is 0), o_coarse_dev (out fp32 [H][n_t][D]) and out (bf16 [S][H][D]).
+ * This call allocates nothing (no hipMalloc, no allocating library routine).
+ *
+ * All calls on one device share that device's array: calls that overlap in
+ * time on one device (other streams, other threads) race and give undefined
+ * results; serialise them. Every region the layer reads is written first in
+ * the same call, so a call never depends on what an earlier call left there.
+ * Errors: as vsa_coarse_topk / vsa_sparse_attn_fwd, plus VSA_ERR_ARG when the
+ * layer's workspace (vsa_workspace_layout(..., 1, ...).total_bytes) exceeds
+ * VSA_STATIC_WORKSPACE_BYTES (for example: 8 heads x 128 x 5,397 tokens
+ * needs about 30 MB and fits; a 42-head 100k-token layer does not).
+ */
+#define VSA_STATIC_WORKSPACE_BYTES (64u << 20)
+
+int vsa_layer_fwd_static(const vsa_plan_info *info, const int32_t *row_src_dev,
+                         const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                         double sparsity, int64_t keep_k, float scale, const void *q,
+                         const void *k, const void *v, const void *gate,
+                         int32_t *keep_idx_dev, float *o_coarse_dev, void *out, void *stream);
+
 /* -------------------------------------------------- gate projection -- */
 /*
  * vsa_gate_proj -- g = bf16_rne(x . W_gate^T), the bias-free gate projection

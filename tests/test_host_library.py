@@ -474,3 +474,34 @@ def test_bwd_layout_transposed_list_regions():
         assert lay.part_dq - lay.tbits < wl.heads * n_t * words * 4 + 256
         for off in (lay.tlist, lay.tcount, lay.tbits, lay.part_dq):
             assert off % 256 == 0
+
+
+def test_static_entry_point_rejects_before_device_work():
+    """vsa_layer_fwd_static: arguments and the static workspace's size are checked
+    before anything touches a device."""
+    lib = tsv._lib
+    wl = workloads.WORKLOADS["h3"]
+    big = tsv.cached_plan(wl.prefix_segments, wl.grid, wl.tile)
+    small = tsv.vsa_plan_tiles([20, 40], (4, 8, 8), (4, 4, 4))
+
+    def call(info, heads=2, head_dim=128, keep_k=1, gate=FAKE, keep=FAKE, scale=0.0):
+        return lib.vsa_layer_fwd_static(ctypes.byref(info), FAKE, FAKE, heads, head_dim,
+                                        float("nan"), keep_k, scale, FAKE, FAKE, FAKE, gate, keep,
+                                        FAKE, FAKE, None)
+
+    assert call(big.info, heads=wl.heads, keep_k=378) == tsv.VSA_ERR_ARG
+    assert b"static one holds" in lib.vsa_last_error()
+    need = tsv.vsa_workspace_layout(big.info, wl.heads, wl.head_dim, 1).total_bytes
+    assert need > tsv.STATIC_WORKSPACE_BYTES
+    mid = workloads.WORKLOADS["mid"]
+    mp = tsv.cached_plan(mid.prefix_segments, mid.grid, mid.tile)
+    assert tsv.vsa_workspace_layout(mp.info, mid.heads, mid.head_dim, 1).total_bytes \
+        <= tsv.STATIC_WORKSPACE_BYTES
+    assert call(small.info, head_dim=96) == tsv.VSA_ERR_UNSUPPORTED
+    assert call(small.info, gate=0) == tsv.VSA_ERR_ARG
+    assert call(small.info, keep=0) == tsv.VSA_ERR_ARG
+    assert call(small.info, keep_k=small.n_v + 1) == tsv.VSA_ERR_ARG
+    assert call(small.info, scale=float("inf")) == tsv.VSA_ERR_ARG
+    nopre = tsv.vsa_plan_tiles([], (4, 8, 8), (4, 4, 4))
+    assert call(nopre.info, keep_k=0, keep=0) == tsv.VSA_ERR_ARG
+    assert b"empty key set" in lib.vsa_last_error()

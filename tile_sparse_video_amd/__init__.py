@@ -37,7 +37,10 @@ EXPORTED = (
     "vsa_timing_read", "vsa_ref_keep_count", "vsa_tile_pair_fraction_ref", "vsa_coarse_topk_ref",
     "vsa_sparse_attn_fwd_ref", "vsa_bwd_workspace_layout", "vsa_sparse_attn_bwd",
     "vsa_sparse_attn_fwd_i8", "vsa_layer_fwd_groups", "vsa_sparse_attn_fwd_train",
+    "vsa_layer_fwd_static",
 )
+# Size of the library's static workspace (vsa_layer_fwd_static), as vsa.h defines it.
+STATIC_WORKSPACE_BYTES = 64 << 20
 TIMED_KERNELS = ("gate_gemm", "gather_pool", "video_scores", "coarse_attn", "topk", "fine_attn",
                  "merge", "bwd_gather", "bwd_prep", "bwd_coarse", "bwd_tlist", "bwd_dq", "bwd_dkdv",
                  "bwd_stats", "quant_k")
@@ -120,6 +123,8 @@ def _load() -> ctypes.CDLL:
                                  P, P, SZ, P, P, P, P, I32, P], ctypes.c_int),
         "vsa_sparse_attn_fwd_train": ([info_p, P, P, I32, I32, I32, I32, F32, I32, P, P, SZ, P, P,
                                        P, P, P, SZ, P], ctypes.c_int),
+        "vsa_layer_fwd_static": ([info_p, P, P, I32, I32, F64, I64, F32, P, P, P, P, P, P, P, P],
+                                 ctypes.c_int),
         "vsa_timing_enable": ([P, I32], ctypes.c_int),
         "vsa_timing_read": ([P, ctypes.c_char_p, ctypes.POINTER(I32), ctypes.POINTER(F64)],
                             ctypes.c_int),
@@ -476,6 +481,34 @@ def vsa_sparse_attn_fwd_train(info: vsa_plan_info, row_src_dev: torch.Tensor,
         _ptr(keep_idx),
         _ptr(o_coarse), _ptr(gate), _ptr(out), _ptr(bwd_workspace), bwd_workspace.numel(),
         _stream(stream)), "vsa_sparse_attn_fwd_train")
+
+
+def vsa_layer_fwd_static(info: vsa_plan_info, row_src_dev: torch.Tensor, block_len_dev: torch.Tensor,
+                         heads: int, head_dim: int, q: torch.Tensor, k: torch.Tensor,
+                         v: torch.Tensor, gate: torch.Tensor, keep_idx: Optional[torch.Tensor],
+                         o_coarse: torch.Tensor, out: torch.Tensor,
+                         sparsity: Optional[float] = None, keep_k: Optional[int] = None,
+                         scale: float = 0.0, stream=None) -> None:
+    """The whole layer (coarse stage, then the unsplit fine pass) with the library's
+    static workspace: no device allocation in the call."""
+    S = info.rows_real
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, n, torch.bfloat16, (S, heads, head_dim))
+    _need(gate, "gate", torch.bfloat16)
+    if gate.numel() != S * heads * head_dim:
+        raise ValueError("gate must hold [S][heads*head_dim] values")
+    _need(row_src_dev, "row_src", torch.int32, (info.rows_padded,))
+    _need(block_len_dev, "block_len", torch.int32, (info.n_tiles,))
+    _need(o_coarse, "o_coarse", torch.float32, (heads, info.n_tiles, head_dim))
+    if keep_idx is not None:
+        _need(keep_idx, "keep_idx", torch.int32)
+        if keep_idx.dim() != 3 or tuple(keep_idx.shape[:2]) != (heads, info.n_video_tiles):
+            raise ValueError("keep_idx must be [heads][n_v][k]")
+    _check(_lib.vsa_layer_fwd_static(
+        ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev), heads, head_dim,
+        float("nan") if sparsity is None else float(sparsity), -1 if keep_k is None else int(keep_k),
+        float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(keep_idx), _ptr(o_coarse),
+        _ptr(out), _stream(stream)), "vsa_layer_fwd_static")
 
 
 def vsa_gate_proj(x: torch.Tensor, w_gate: torch.Tensor, g: torch.Tensor, stream=None) -> None:

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvsa.so")
 SOURCES = ["plan.cpp", "timing.cpp", "groups.cpp", "coarse.hip", "fine.hip", "gemm.hip",
-           "backward.hip"]
+           "backward.hip", "static_ws.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
