@@ -21,8 +21,12 @@
 //    cross-half exchange), and the S accumulator already has the register
 //    layout of the P^T operand of the second product.
 //  - The key list is walked in 32-key halves; K of the next half is fetched
-//    as soon as S is formed and V once P.V is issued. 256 VGPRs per wave give
-//    two waves per SIMD, which cover each other's memory waits.
+//    once both S products are issued and V once P.V is issued. 256 VGPRs per
+//    wave give two waves per SIMD, which cover each other's memory waits. The
+//    bf16 step is scheduled by hand so that each query block's softmax runs
+//    on the vector unit while the matrix core works on the other block's
+//    products (scheduling barriers pin the interleaving); the kernel is
+//    power-limited, so the gain is small (1-5 %) but free.
 //  - With random keep-sets the kernel is bound by the traffic beyond L2, so
 //    for large heads the key list is split into C chunks by tile id modulo C,
 //    and chunk c is dispatched to XCD c (workgroups are spread round-robin
@@ -404,9 +408,9 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
     // rescale. With m = -inf every finite score moves it.
     float moff[2] = {0.f, 0.f}, thr[2] = {-INFINITY, -INFINITY};
 
-    // One 32-key half: S = K.Q^T, online softmax, O += V.P. K of the next half
-    // is fetched as soon as S is formed, V of the next half once P.V has been
-    // issued. The body is straight-line on purpose: halves with no real key are
+    // One 32-key half of the INT8 pass (the bf16 pass uses step_b below): S =
+    // K.Q^T, online softmax, O += V.P. K of the next half is fetched as soon as
+    // S is formed, V of the next half once P.V has been issued. The body is straight-line on purpose: halves with no real key are
     // masked rather than skipped, and the last refill re-reads a valid half, so
     // the K/V registers never merge values from different control paths.
     auto step = [&](int v, int n_half, uint32_t ecur, u32x4_t (&Kb)[KN], u32x4_t (&Vb)[2 * DB]) -> uint32_t {
@@ -521,6 +525,144 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
         return enext;
     };
 
+    // ---- bf16 step, scheduled by hand. Per 32-key half the matrix core runs
+    // 32 products (S of query blocks 0 and 1, then P.V of both) and the vector
+    // unit two softmaxes; in program order each softmax is spread over the
+    // products it does not depend on (scheduling barriers pin the order):
+    //   S0 (8)  |  S1 0-1 + max of S0  |  [rescale O0]  |  S1 2-7 + exp of S0
+    //   | P.V0 0-1 + max of S1  |  [rescale O1]  |  P.V0 2-7 + exp of S1  |  P.V1 (8)
+    // Q fragments are read from LDS two products ahead.
+    // The lane index goes through an empty asm once per step, so the Q reads
+    // are re-issued every step (not hoisted into registers) from one base.
+    const bf16x8_t *qbase = nullptr;
+    auto qread = [&](int qb, int c) -> bf16x8_t { return qbase[(qb * NC + c) * kWave]; };
+    auto row_max = [&](const f32x16_t &S) -> float {
+        float mx = fmaxf(fmaxf(S[0], S[1]), S[2]);
+#pragma unroll
+        for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, S[e]), S[e + 1]);
+        mx = fmaxf(mx, S[15]);
+        return xhalf_max(mx);
+    };
+    auto rescale = [&](float mx, int qb) {
+        if (__ballot(mx > thr[qb]) != 0) {
+            const float m_new = fmaxf(m[qb], mx);
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m[qb] - m_new) * c2);
+            l[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) O[db][qb][e] *= alpha;
+            m[qb] = m_new;
+            moff[qb] = m_new == -INFINITY ? 0.f : -m_new * c2;
+            thr[qb] = m_new == -INFINITY ? -INFINITY : m_new + kLazy / c2;
+        }
+    };
+    // Probabilities of elements 2p, 2p + 1 of S (16-key chunk p / 4), packed to
+    // bf16 into w[p / 4] and added to the row sum in the same bf16 values.
+    auto prob_pair = [&](const f32x16_t &S, int qb, int p, float &rs, u32x4_t (&w)[2]) {
+        const int cc = p >> 2, e = 2 * (p & 3);
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * cc + e], c2, moff[qb]));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * cc + e + 1], c2, moff[qb]));
+        const bf16x2_t pp = {(__bf16)p0, (__bf16)p1};
+        rs = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, rs, false);
+        w[cc][e / 2] = __builtin_bit_cast(uint32_t, pp);
+    };
+    auto mask_pad = [&](f32x16_t &S, int real) {
+        const int lim = real - 4 * half;  // key 8i + 4 half + j is padding iff 8i + j >= lim
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (8 * i + j >= lim) S[4 * i + j] = -INFINITY;
+    };
+    // pairs of softmax elements placed after product slot i of a 6-slot region
+    constexpr int kPairsAt[6] = {2, 2, 1, 1, 1, 1};
+    auto step_b = [&](int v, int n_half, uint32_t ecur, u32x4_t (&Kb)[KN], u32x4_t (&Vb)[2 * DB]) -> uint32_t {
+        const int real = min(32, int(ecur >> 25) + 1 - 32 * (v % HPU));
+        const int next = v + 1 < n_half ? v + 1 : v;
+        const uint32_t enext = entry(next);
+        {
+            int ql = lane;
+            asm volatile("" : "+v"(ql));
+            qbase = &q_lds[0][0][ql];
+        }
+        // ---- S0, with the first Q fragments of block 1 read at its end
+        bf16x8_t qa = qread(0, 0), qb_ = qread(0, 1), qc;
+        f32x16_t S0 = f32x16_t{}, S1 = f32x16_t{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            qc = c + 2 < NC ? qread(0, c + 2) : qread(1, c + 2 - NC);
+            S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Kb[c]), qa, S0, 0, 0, 0);
+            qa = qb_;
+            qb_ = qc;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- S1 products 0-1 with the max of S0
+        qc = qread(1, 2);
+        S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Kb[0]), qa, S1, 0, 0, 0);
+        qa = qb_;
+        qb_ = qc;
+        qc = qread(1, 3);
+        S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Kb[1]), qa, S1, 0, 0, 0);
+        qa = qb_;
+        qb_ = qc;
+        if (__builtin_expect(real < 32, 0)) mask_pad(S0, real);
+        const float mx0 = row_max(S0);
+        rescale(mx0, 0);
+        // ---- S1 products 2-7 with the exponentials of S0
+        float rs0 = 0.f;
+        u32x4_t w0[2];
+        {
+            int p = 0;
+#pragma unroll
+            for (int c = 2; c < NC; ++c) {
+                if (c + 2 < NC) qc = qread(1, c + 2);
+                S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Kb[c]), qa, S1, 0, 0, 0);
+                qa = qb_;
+                qb_ = qc;
+                const int np = NC == 8 ? kPairsAt[c - 2] : (c + 1 < NC ? 8 / (NC - 2) : 8 - (8 / (NC - 2)) * (NC - 3));
+#pragma unroll
+                for (int u = 0; u < np; ++u, ++p) prob_pair(S0, 0, p, rs0, w0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        l[0] += xhalf_sum(rs0);
+        const bf16x8_t P0[2] = {as_bf16x8(w0[0]), as_bf16x8(w0[1])};
+        load_k(next, enext, Kb);
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- P.V0 products 0-1 with the max of S1
+        O[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Vb[0]), P0[0], O[0][0], 0, 0, 0);
+        O[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Vb[1]), P0[1], O[0][0], 0, 0, 0);
+        if (__builtin_expect(real < 32, 0)) mask_pad(S1, real);
+        const float mx1 = row_max(S1);
+        rescale(mx1, 1);
+        // ---- P.V0 products 2-7 with the exponentials of S1
+        float rs1 = 0.f;
+        u32x4_t w1[2];
+        {
+            int p = 0;
+#pragma unroll
+            for (int i = 2; i < 2 * DB; ++i) {
+                const int db = i >> 1, cc = i & 1;
+                O[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Vb[2 * db + cc]), P0[cc], O[db][0], 0, 0, 0);
+                const int np = 2 * DB == 8 ? kPairsAt[i - 2] : (i + 1 < 2 * DB ? 8 / (2 * DB - 2) : 8 - (8 / (2 * DB - 2)) * (2 * DB - 3));
+#pragma unroll
+                for (int u = 0; u < np; ++u, ++p) prob_pair(S1, 1, p, rs1, w1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        l[1] += xhalf_sum(rs1);
+        const bf16x8_t P1[2] = {as_bf16x8(w1[0]), as_bf16x8(w1[1])};
+        // ---- P.V1
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+                O[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(Vb[2 * db + cc]), P1[cc], O[db][1], 0, 0, 0);
+        load_v(next, enext, Vb);
+        return enext;
+    };
+
     u32x4_t Kb[KN], Vb[2 * DB];
     while (true) {
         const int count = fill();
@@ -529,7 +671,10 @@ __global__ __launch_bounds__(64, 2) void fine_attn_kernel(FineArgs a)
             uint32_t e = entry(0);
             load_k(0, e, Kb);
             load_v(0, e, Vb);
-            for (int v = 0; v < n_half; ++v) e = step(v, n_half, e, Kb, Vb);
+            for (int v = 0; v < n_half; ++v) {
+                if constexpr (I8) e = step(v, n_half, e, Kb, Vb);
+                else e = step_b(v, n_half, e, Kb, Vb);
+            }
         }
         if (scan >= n_list) break;
         __syncthreads();  // every lane has read the list before it is refilled
