@@ -308,6 +308,88 @@ def bench_backward(args, wl, tsv, att, qd, kd, vd, xd, wd, g, out, stream, host_
     return 0
 
 
+def bench_producer(args, wl, tsv, att, xd, stream) -> int:
+    """The layer from its input x. Fused: vsa_qkv_gate_proj (q, gate natural; K/V tiled
+    with the tile means) + vsa_coarse_topk without the gather + the fine pass. Unfused:
+    four vsa_gate_proj calls (q, k, v, gate) + vsa_coarse_topk with its gather + the fine
+    pass. Same arithmetic, identical outputs (checked here on the last step)."""
+    dev = xd.device
+    S, H, D = wl.tokens, wl.heads, wl.head_dim
+    w4 = workloads.make_w_qkvg(wl).to(dev)
+    w_parts = [w4[i].contiguous() for i in range(4)]
+    qp = torch.empty((S, H, D), dtype=torch.bfloat16, device=dev)
+    gp = torch.empty((S, H * D), dtype=torch.bfloat16, device=dev)
+    out_f = torch.empty_like(qp)
+    out_u = torch.empty_like(qp)
+    proj = [torch.empty((S, H * D), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+
+    def fused(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        att.project(xd, w4, qp, gp, stream=stream)
+        att.coarse(None, None, None, stream=stream)
+        att.fine(qp, gp, out_f, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    def unfused(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        for i in range(4):
+            tsv.vsa_gate_proj(xd, w_parts[i], proj[i], stream=stream)
+        att.coarse(*(t.view(S, H, D) for t in proj[:3]), stream=stream)
+        att.fine(proj[0].view(S, H, D), proj[3], out_u, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    res = {}
+    for name, fn in (("fused", fused), ("unfused", unfused)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        tsv.vsa_timing_enable(True, stream)
+        for i in range(args.steps):
+            fn(evs[i])
+        torch.cuda.synchronize()
+        tsv.vsa_timing_enable(False, stream)
+        kernels = {}
+        for kname in tsv.TIMED_KERNELS:
+            n, ms = tsv.vsa_timing_read(kname, stream)
+            if n:
+                kernels[kname] = {"launches": n, "avg_ms": round(ms / n, 4)}
+        res[name] = {"ms_per_layer": round(float(np.mean([e[0].elapsed_time(e[1]) for e in evs])), 4),
+                     "kernels": kernels}
+    identical = bool(torch.equal(out_f.view(torch.int16), out_u.view(torch.int16)))
+    keep_host = att.keep_idx.cpu().numpy()
+    fine_flops = effective_fine_flops(att.plan, keep_host, H, D, att.ref)
+    proj_flops = 2.0 * S * wl.hidden * 4 * H * D
+    layer_ms = res["fused"]["ms_per_layer"]
+    qkv_ms = res["fused"]["kernels"]["qkv_proj"]["avg_ms"]
+    result = {
+        "metric": "ms/layer from the layer input (fused q/k/v/gate producer + coarse + fine)",
+        "value": round(layer_ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(layer_ms, 4), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.note}", "heads": H, "head_dim": D,
+                   "hidden": wl.hidden, "tokens": S, "keep_k": att.k, "mode": "from x (producer)",
+                   "split_chunks": att.split_chunks, "parallelism": "single GPU"},
+        "fused": res["fused"], "unfused": res["unfused"],
+        "outputs_identical": identical,
+        "saved_ms": round(res["unfused"]["ms_per_layer"] - layer_ms, 4),
+        "effective_fine_tflop": round(fine_flops / 1e12, 3),
+        "projection_tflop": round(proj_flops / 1e12, 3),
+        "roofline": {"kernel": "qkv_gemm_kernel (vsa_qkv_gate_proj)", "bound": "mfma",
+                     "achieved": round(proj_flops / (qkv_ms * 1e-3) / 1e12, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(proj_flops / (qkv_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "algorithmic_tflop_per_launch": round(proj_flops / 1e12, 4),
+                     "avg_launch_ms": qkv_ms, "traffic": None},
+    }
+    print(json.dumps(result), flush=True)
+    return 0 if identical else 1
+
+
 def cpu_baseline_backward(wl, host_inputs, att, dout, g, flops):
     """The oracle's backward on a bounded sample: dq of sampled tokens of head 0
     (each token's own keys plus its tile's coarse row), scaled by 3 (dk and dv
@@ -353,6 +435,12 @@ def main() -> int:
     ap.add_argument("--backward", action="store_true",
                     help="time the layer's training step instead: forward plus the backward "
                          "pass (gradients of q, k, v and the gate)")
+    ap.add_argument("--producer", action="store_true",
+                    help="run the layer from its input x: one chunked-producer GEMM for q, k, "
+                         "v and the gate (vsa_qkv_gate_proj, K/V written in tile order with the "
+                         "tile means), the coarse stage without its gather, the fine pass; "
+                         "timed beside the same layer with four vsa_gate_proj calls and the "
+                         "gather")
     ap.add_argument("--split-chunks", type=int, default=0,
                     help="fine-pass key-list split (0 = the library's automatic choice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -412,6 +500,8 @@ def main() -> int:
     if args.backward:
         return bench_backward(args, wl, tsv, att, qd, kd, vd, xd, wd, g, out, stream,
                               (q, k, v, x, w))
+    if args.producer:
+        return bench_producer(args, wl, tsv, att, xd, stream)
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

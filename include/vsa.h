@@ -211,7 +211,10 @@ int vsa_workspace_layout(const vsa_plan_info *info, int32_t heads, int32_t head_
  * row_src_dev, block_len_dev: device copies of the plan arrays.
  * heads (H), head_dim (D in {64,128}).
  * sparsity / keep_k: as vsa_keep_count. scale <= 0 means D^-1/2.
- * q, k, v: device bf16 [S][H][D].
+ * q, k, v: device bf16 [S][H][D]; or all three NULL when the workspace
+ *   already holds the tiled K/V and the three tile means of these tokens
+ *   (written by vsa_qkv_gate_proj for the same plan, heads and head_dim):
+ *   step 1 is then skipped and steps 2-4 read them.
  * workspace: device, >= vsa_workspace_layout().part_o bytes, 256-byte aligned.
  * keep_idx_dev: out device int32 [H][n_v][k] (may be NULL when k == 0).
  * o_coarse_dev: out device fp32 [H][n_t][D].
@@ -468,6 +471,37 @@ int vsa_sparse_attn_fwd_train(const vsa_plan_info *info, const int32_t *row_src_
                               const void *gate, void *out, void *bwd_workspace,
                               size_t bwd_workspace_bytes, void *stream);
 
+/* ------------------------------------------------- chunked producer -- */
+/*
+ * vsa_qkv_gate_proj -- the layer's four projections from its input x in one
+ * GEMM whose rows are taken in tile order, writing what the attention stages
+ * read directly ([SnackOnAI] "The Code, Annotated", snippet two: tile the
+ * hidden states before projecting, so no sequence-sized copies follow;
+ * "Why This Design Works": a chunked QKV producer that avoids the padded full
+ * projection). bf16 inputs, fp32 accumulation, one bf16 rounding per output
+ * (the arithmetic of vsa_gate_proj, so each projected value is the one
+ * vsa_gate_proj gives for the same weight rows, bit for bit):
+ *   q    = x . W_q^T   -> q, natural order, device bf16 [S][H][D];
+ *   g    = x . W_g^T   -> gate, natural order, device bf16 [S][H*D];
+ *   k, v = x . W_k^T, x . W_v^T -> the workspace's k_tiled / v_tiled, in the
+ *          fragment layout vsa_coarse_topk writes (padding rows zero);
+ *   and the tile means of q, k and v in the workspace's q_mean / k_mean /
+ *   v_mean, in the canonical order of vsa_coarse_topk step 1 over the bf16
+ *   values above.
+ * Follow it with vsa_coarse_topk(..., q = k = v = NULL, ...) and the fine pass
+ * (which reads q and gate). Only real rows are projected and stored.
+ * x: device bf16 [S][hidden]; w_qkvg: device bf16 [4][H*D][hidden], the
+ * stacked W_q, W_k, W_v, W_gate (nn.Linear weights, bias-free).
+ * workspace: >= vsa_workspace_layout().part_o bytes, 256-byte aligned.
+ * Errors: VSA_ERR_ARG (null pointers, small workspace), VSA_ERR_UNSUPPORTED
+ * (head_dim not 64 or 128, hidden not a multiple of 64, H*D not a multiple
+ * of 128, S*hidden*2 bytes of input beyond 4 GiB), VSA_ERR_DEVICE.
+ */
+int vsa_qkv_gate_proj(const vsa_plan_info *info, const int32_t *row_src_dev,
+                      const int32_t *block_len_dev, int32_t heads, int32_t head_dim,
+                      int32_t hidden, const void *x, const void *w_qkvg, void *q, void *gate,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------- layer without allocation -- */
 /*
  * For callers that cannot allocate device memory (code under HIP graph
@@ -532,7 +566,7 @@ int vsa_gate_proj(const void *x, const void *w_gate, int64_t rows, int32_t hidde
  * vsa_timing_read -- for the kernel named `kernel` (one of "gate_gemm",
  * "gather_pool", "video_scores", "coarse_attn", "topk", "fine_attn",
  * "merge", "bwd_gather", "bwd_prep", "bwd_coarse", "bwd_tlist", "bwd_dq",
- * "bwd_dkdv", "bwd_stats", "quant_k"), waits for the launches recorded on
+ * "bwd_dkdv", "bwd_stats", "quant_k", "qkv_proj"), waits for the launches recorded on
  * `stream` since its last enable (call it after those entry points have
  * returned) and returns their number in *launches and their summed duration
  * in *total_ms (host pointers); 0 and 0.0 for a stream never timed.

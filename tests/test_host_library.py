@@ -505,3 +505,24 @@ def test_static_entry_point_rejects_before_device_work():
     nopre = tsv.vsa_plan_tiles([], (4, 8, 8), (4, 4, 4))
     assert call(nopre.info, keep_k=0, keep=0) == tsv.VSA_ERR_ARG
     assert b"empty key set" in lib.vsa_last_error()
+
+
+def test_producer_rejects_before_device_work():
+    """vsa_qkv_gate_proj validates shapes, pointers and the workspace up front."""
+    pl = tsv.vsa_plan_tiles([5, 70, 1], (5, 6, 9), (4, 4, 4))
+    lib = tsv._lib
+
+    def call(heads=3, head_dim=128, hidden=128, ws_bytes=1 << 40, x=FAKE, ws=FAKE * 2):
+        return lib.vsa_qkv_gate_proj(ctypes.byref(pl.info), FAKE, FAKE, heads, head_dim, hidden, x,
+                                     FAKE, FAKE, FAKE, ws, ws_bytes, None)
+
+    assert call(head_dim=96) == tsv.VSA_ERR_UNSUPPORTED
+    assert call(hidden=100) == tsv.VSA_ERR_UNSUPPORTED
+    assert call(heads=1, head_dim=64) == tsv.VSA_ERR_UNSUPPORTED     # H*D = 64
+    assert call(heads=0) == tsv.VSA_ERR_ARG
+    assert call(x=0) == tsv.VSA_ERR_ARG
+    assert call(ws_bytes=1024) == tsv.VSA_ERR_ARG
+    assert call(ws=FAKE * 2 + 8) == tsv.VSA_ERR_ARG                   # misaligned
+    lay = tsv.vsa_workspace_layout(pl.info, 3, 128, 1)
+    assert call(ws_bytes=lay.part_o - 1) == tsv.VSA_ERR_ARG
+    assert b"workspace" in lib.vsa_last_error()

@@ -37,13 +37,13 @@ EXPORTED = (
     "vsa_timing_read", "vsa_ref_keep_count", "vsa_tile_pair_fraction_ref", "vsa_coarse_topk_ref",
     "vsa_sparse_attn_fwd_ref", "vsa_bwd_workspace_layout", "vsa_sparse_attn_bwd",
     "vsa_sparse_attn_fwd_i8", "vsa_layer_fwd_groups", "vsa_sparse_attn_fwd_train",
-    "vsa_layer_fwd_static",
+    "vsa_layer_fwd_static", "vsa_qkv_gate_proj",
 )
 # Size of the library's static workspace (vsa_layer_fwd_static), as vsa.h defines it.
 STATIC_WORKSPACE_BYTES = 64 << 20
 TIMED_KERNELS = ("gate_gemm", "gather_pool", "video_scores", "coarse_attn", "topk", "fine_attn",
                  "merge", "bwd_gather", "bwd_prep", "bwd_coarse", "bwd_tlist", "bwd_dq", "bwd_dkdv",
-                 "bwd_stats", "quant_k")
+                 "bwd_stats", "quant_k", "qkv_proj")
 
 
 class VsaError(RuntimeError):
@@ -125,6 +125,7 @@ def _load() -> ctypes.CDLL:
                                        P, P, P, SZ, P], ctypes.c_int),
         "vsa_layer_fwd_static": ([info_p, P, P, I32, I32, F64, I64, F32, P, P, P, P, P, P, P, P],
                                  ctypes.c_int),
+        "vsa_qkv_gate_proj": ([info_p, P, P, I32, I32, I32, P, P, P, P, P, SZ, P], ctypes.c_int),
         "vsa_timing_enable": ([P, I32], ctypes.c_int),
         "vsa_timing_read": ([P, ctypes.c_char_p, ctypes.POINTER(I32), ctypes.POINTER(F64)],
                             ctypes.c_int),
@@ -279,13 +280,19 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None) -> None:
 
 
 def vsa_coarse_topk(info: vsa_plan_info, row_src_dev: torch.Tensor, block_len_dev: torch.Tensor,
-                    heads: int, head_dim: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                    workspace: torch.Tensor, keep_idx: Optional[torch.Tensor], o_coarse: torch.Tensor,
+                    heads: int, head_dim: int, q: Optional[torch.Tensor], k: Optional[torch.Tensor],
+                    v: Optional[torch.Tensor], workspace: torch.Tensor,
+                    keep_idx: Optional[torch.Tensor], o_coarse: torch.Tensor,
                     sparsity: Optional[float] = None, keep_k: Optional[int] = None,
                     scale: float = 0.0, stream=None) -> None:
+    """q = k = v = None: the workspace already holds the tiled K/V and the tile means
+    (vsa_qkv_gate_proj), and the gather is skipped."""
     S = info.rows_real
+    if (q is None) != (k is None) or (q is None) != (v is None):
+        raise ValueError("pass q, k and v, or none of them")
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, torch.bfloat16, (S, heads, head_dim))
+        if t is not None:
+            _need(t, n, torch.bfloat16, (S, heads, head_dim))
     _need(row_src_dev, "row_src", torch.int32, (info.rows_padded,))
     _need(block_len_dev, "block_len", torch.int32, (info.n_tiles,))
     _need(workspace, "workspace", torch.uint8)
@@ -333,8 +340,11 @@ def vsa_coarse_topk_ref(info: vsa_plan_info, row_src_dev: torch.Tensor,
                         ref_sparsity: Optional[float] = None, ref_keep_k: Optional[int] = None,
                         scale: float = 0.0, stream=None) -> None:
     S = info.rows_real
+    if (q is None) != (k is None) or (q is None) != (v is None):
+        raise ValueError("pass q, k and v, or none of them")
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, torch.bfloat16, (S, heads, head_dim))
+        if t is not None:
+            _need(t, n, torch.bfloat16, (S, heads, head_dim))
     _need(row_src_dev, "row_src", torch.int32, (info.rows_padded,))
     _need(block_len_dev, "block_len", torch.int32, (info.n_tiles,))
     _need(workspace, "workspace", torch.uint8)
@@ -483,6 +493,33 @@ def vsa_sparse_attn_fwd_train(info: vsa_plan_info, row_src_dev: torch.Tensor,
         _stream(stream)), "vsa_sparse_attn_fwd_train")
 
 
+def vsa_qkv_gate_proj(info: vsa_plan_info, row_src_dev: torch.Tensor, block_len_dev: torch.Tensor,
+                      heads: int, head_dim: int, x: torch.Tensor, w_qkvg: torch.Tensor,
+                      q: torch.Tensor, gate: torch.Tensor, workspace: torch.Tensor,
+                      stream=None) -> None:
+    """The chunked producer: q and gate in natural order, tiled K/V and the tile means
+    in the workspace, from x and the stacked [W_q; W_k; W_v; W_gate]."""
+    S = info.rows_real
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.shape[0] != S:
+        raise ValueError("x must be [S][hidden]")
+    hidden = x.shape[1]
+    _need(w_qkvg, "w_qkvg", torch.bfloat16)
+    if w_qkvg.numel() != 4 * heads * head_dim * hidden:
+        raise ValueError("w_qkvg must be [4][heads*head_dim][hidden]")
+    _need(q, "q", torch.bfloat16, (S, heads, head_dim))
+    _need(gate, "gate", torch.bfloat16)
+    if gate.numel() != S * heads * head_dim:
+        raise ValueError("gate must hold [S][heads*head_dim] values")
+    _need(row_src_dev, "row_src", torch.int32, (info.rows_padded,))
+    _need(block_len_dev, "block_len", torch.int32, (info.n_tiles,))
+    _need(workspace, "workspace", torch.uint8)
+    _check(_lib.vsa_qkv_gate_proj(ctypes.byref(info), _ptr(row_src_dev), _ptr(block_len_dev), heads,
+                                  head_dim, int(hidden), _ptr(x), _ptr(w_qkvg), _ptr(q), _ptr(gate),
+                                  _ptr(workspace), workspace.numel(), _stream(stream)),
+           "vsa_qkv_gate_proj")
+
+
 def vsa_layer_fwd_static(info: vsa_plan_info, row_src_dev: torch.Tensor, block_len_dev: torch.Tensor,
                          heads: int, head_dim: int, q: torch.Tensor, k: torch.Tensor,
                          v: torch.Tensor, gate: torch.Tensor, keep_idx: Optional[torch.Tensor],
@@ -595,7 +632,14 @@ class TileSparseAttention:
     def list_len(self) -> int:
         return self.keep_idx.shape[2]
 
+    def project(self, x, w_qkvg, q, gate, stream=None) -> None:
+        """The chunked producer: q and gate (natural order) plus the tiled K/V and tile
+        means in this layer's workspace; follow with coarse(None, None, None)."""
+        vsa_qkv_gate_proj(self.plan.info, self.row_src, self.block_len, self.heads, self.head_dim,
+                          x, w_qkvg, q, gate, self.workspace, stream=stream)
+
     def coarse(self, q, k, v, stream=None) -> None:
+        """q = k = v = None after project(): the gather is skipped."""
         keep = self.keep_idx if self.list_len > 0 else None
         if self.ref:
             vsa_coarse_topk_ref(self.plan.info, self.row_src, self.block_len, self.heads,

@@ -1021,7 +1021,10 @@ int coarse_impl(const char *name, const vsa_plan_info *info, const int32_t *row_
     if (heads <= 0 || ld < heads) return fail(VSA_ERR_ARG, "%s: heads = %d (row stride %d)", name, heads, ld);
     if (head_dim != 64 && head_dim != 128)
         return fail(VSA_ERR_UNSUPPORTED, "%s: head_dim = %d; supported: 64, 128", name, head_dim);
-    if (!row_src_dev || !block_len_dev || !q || !k || !v || !workspace || !o_coarse_dev)
+    // q = k = v = null: the workspace already holds the tiled K/V and the tile
+    // means (written by the chunked producer), so the gather is skipped.
+    const bool pretiled = !q && !k && !v;
+    if (!row_src_dev || !block_len_dev || !workspace || !o_coarse_dev || (!pretiled && (!q || !k || !v)))
         return fail(VSA_ERR_ARG, "%s: null device pointer", name);
     if (!(std::isfinite(scale))) return fail(VSA_ERR_ARG, "%s: scale is not finite", name);
     int32_t k_gen = 0, k_ref = 0;
@@ -1058,11 +1061,13 @@ int coarse_impl(const char *name, const vsa_plan_info *info, const int32_t *row_
 
     (void)hipGetLastError();
     if (head_dim == 128) {
-        if (B == 64) launch_gather_pool<128, 64>(qq, kk_, vv, row_src_dev, block_len_dev, heads, ld, n_t, qm, km, vm, kt, vt, st);
+        if (pretiled) {
+        } else if (B == 64) launch_gather_pool<128, 64>(qq, kk_, vv, row_src_dev, block_len_dev, heads, ld, n_t, qm, km, vm, kt, vt, st);
         else launch_gather_pool<128, 128>(qq, kk_, vv, row_src_dev, block_len_dev, heads, ld, n_t, qm, km, vm, kt, vt, st);
         launch_coarse<128>(*info, heads, sc, qm, km, vm, first, n, sc_buf, o_coarse_dev, st);
     } else {
-        if (B == 64) launch_gather_pool<64, 64>(qq, kk_, vv, row_src_dev, block_len_dev, heads, ld, n_t, qm, km, vm, kt, vt, st);
+        if (pretiled) {
+        } else if (B == 64) launch_gather_pool<64, 64>(qq, kk_, vv, row_src_dev, block_len_dev, heads, ld, n_t, qm, km, vm, kt, vt, st);
         else launch_gather_pool<64, 128>(qq, kk_, vv, row_src_dev, block_len_dev, heads, ld, n_t, qm, km, vm, kt, vt, st);
         launch_coarse<64>(*info, heads, sc, qm, km, vm, first, n, sc_buf, o_coarse_dev, st);
     }

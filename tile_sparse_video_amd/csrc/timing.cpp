@@ -30,7 +30,7 @@ namespace {
 const char *const kNames[K_COUNT] = {"gate_gemm",  "gather_pool", "video_scores", "coarse_attn",
                                      "topk",       "fine_attn",   "merge",        "bwd_gather",
                                      "bwd_prep",   "bwd_coarse",  "bwd_tlist",    "bwd_dq",
-                                     "bwd_dkdv",   "bwd_stats",   "quant_k"};
+                                     "bwd_dkdv",   "bwd_stats",   "quant_k",      "qkv_proj"};
 
 std::mutex g_mu;
 // One entry per stream that ever had timing enabled; entries are never removed,

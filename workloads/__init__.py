@@ -9,7 +9,8 @@ Every tensor is drawn on the host with torch's CPU generator from a seed that
 is a pure function of (workload seed, stream id), sampled in fp32 and rounded
 once to bf16 (round-to-nearest-even, torch's own conversion). Stream ids:
 0 = Q, 1 = K, 2 = V, 3 = x, 4 = W_gate, 5 = per-head scales, 6 = low-rank
-fields, 7 = low-rank per-head bases.
+fields, 7 = low-rank per-head bases, 8-10 = W_q, W_k, W_v (for the layer run
+from its input x).
 
 The shapes follow the workloads these pages measure: MiniMax-H3-like layers
 (42 heads x 128, hidden 5376) with a segment-pure prefix of text, reference
@@ -28,6 +29,7 @@ import torch
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_X, STREAM_W = 0, 1, 2, 3, 4
 STREAM_HEAD_SCALE, STREAM_FIELDS, STREAM_LOWRANK_U = 5, 6, 7
+STREAM_WQ, STREAM_WK, STREAM_WV = 8, 9, 10
 
 
 @dataclass(frozen=True)
@@ -162,6 +164,16 @@ def make_w_gate(wl: Workload) -> torch.Tensor:
     """Bias-free gate weight W_gate ~ N(0, std^2), bf16 [H*D][hidden] (nn.Linear out x in)."""
     w = _normal((wl.heads * wl.head_dim, wl.hidden), wl.seed, STREAM_W)
     return (w * wl.w_gate_std).to(torch.bfloat16)
+
+
+def make_w_qkvg(wl: Workload) -> torch.Tensor:
+    """Stacked bias-free projection weights [W_q; W_k; W_v; W_gate], bf16
+    [4][H*D][hidden]: W_q, W_k, W_v ~ N(0, 1/hidden) (unit-variance projections of
+    a unit-variance x), W_gate as make_w_gate."""
+    HD = wl.heads * wl.head_dim
+    ws = [(_normal((HD, wl.hidden), wl.seed, st) * wl.hidden ** -0.5).to(torch.bfloat16)
+          for st in (STREAM_WQ, STREAM_WK, STREAM_WV)]
+    return torch.stack(ws + [make_w_gate(wl)])
 
 
 def bf16_bits(t: torch.Tensor):
