@@ -214,8 +214,9 @@ def kernel_source_hash() -> str:
 
 
 def recorded_traffic(workload: str):
-    """HBM-side bytes per fine-kernel launch from the committed PMC summary, or None
-    when it was taken on another workload or on a kernel source that has changed since."""
+    """HBM-side bytes per fine pass (fine kernel + merge) and the fine kernel's clock and
+    MFMA-busy share, from the committed PMC summary; None when it was taken on another
+    workload or on a kernel source that has changed since."""
     try:
         text = open(TRAFFIC_PROFILE).read()
     except OSError:
@@ -532,6 +533,11 @@ def main() -> int:
     tflops = fine_flops / (layer_ms * 1e-3) / 1e12
     fine_kernel_ms = kernels["fine_attn"]["avg_ms"]
     fine_tflops = fine_flops / (fine_kernel_ms * 1e-3) / 1e12
+    # The fine pass is the fine kernel plus, when the key lists are split, the merge
+    # of the chunk partials: both are vsa_sparse_attn_fwd's work.
+    merge_ms = kernels.get("merge", {}).get("avg_ms", 0.0)
+    pass_ms = fine_kernel_ms + merge_ms
+    pass_tflops = fine_flops / (pass_ms * 1e-3) / 1e12
     traffic = None if (att.ref or args.int8) else recorded_traffic(wl.name)
     peak = MIXED_PEAK_TOPS if args.int8 else BF16_PEAK_TFLOPS
     frac_pairs = att.tile_pair_fraction()
@@ -573,17 +579,22 @@ def main() -> int:
         "wall_s": round(wall, 3),
         "selection": selection_report(att),
         "roofline": {
-            "kernel": ("fine_attn_kernel, INT8 scores (vsa_sparse_attn_fwd_i8; peak mixes the "
-                       "int8 and bf16 MFMA peaks per kept pair)" if args.int8 else
-                       "fine_attn_kernel (vsa_sparse_attn_fwd; its merge kernel is timed apart)"),
+            "kernel": ("fine_attn_kernel + merge_kernel, INT8 scores (vsa_sparse_attn_fwd_i8; peak "
+                       "mixes the int8 and bf16 MFMA peaks per kept pair)" if args.int8 else
+                       "fine_attn_kernel + merge_kernel (the fine pass, vsa_sparse_attn_fwd)"),
             "bound": "mfma",
-            "achieved": round(fine_tflops, 2),
+            "achieved": round(pass_tflops, 2),
             "peak": round(peak, 1),
             "unit": "TOP/s" if args.int8 else "TFLOP/s",
-            "frac": round(fine_tflops / peak, 4),
+            "frac": round(pass_tflops / peak, 4),
             "algorithmic_tflop_per_launch": round(fine_flops / 1e12, 4),
-            "avg_launch_ms": fine_kernel_ms,
+            "avg_launch_ms": round(pass_ms, 4),
+            "fine_kernel_alone": {"avg_launch_ms": fine_kernel_ms, "achieved": round(fine_tflops, 2),
+                                  "frac": round(fine_tflops / peak, 4)},
+            "split_chunks": att.split_chunks,
             "traffic": None if traffic is None else traffic["bytes_per_launch"],
+            "mfma_busy": None if traffic is None else traffic.get("mfma_busy"),
+            "clock_ghz": None if traffic is None else traffic.get("clock_ghz"),
             "traffic_detail": traffic,
         },
     }

@@ -170,7 +170,8 @@ int vsa_tile_pair_fraction_ref(const vsa_plan_info *info, int32_t k_ref, int32_t
  *
  * split_chunks (here and in every fine / backward entry point): the C a call
  * uses; 0 = automatic (a function of the plan and head_dim only: 1 while one
- * head's K and V fit in 16 MiB, else 8 * ceil(K+V / 96 MiB), at most 64),
+ * head's K and V fit in 16 MiB, else 8 * ceil(K+V / 96 MiB), at least 16 for
+ * 64-row tiles beyond 32 MiB, at most 64),
  * 1 = never split, 2..64 = that many chunks. It is a tuning choice: the
  * result depends on it only through fp32 rounding. A workspace serves the
  * fine calls made with the split count it was laid out for (or a smaller

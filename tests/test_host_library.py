@@ -131,25 +131,36 @@ def test_workspace_layout():
         assert off % 256 == 0 and off >= end
         end = off + size
     assert lay.part_o >= end and lay.total_bytes >= lay.part_ml
-    # a 50 MiB head splits its key lists: room for 8 chunk partials per 64 query rows
+    # a 48 MiB head of 64-row tiles splits its key lists into two phases of 8 chunks:
+    # room for 16 chunk partials per 64 query rows
     items = H * n_t
-    assert lay.part_ml - lay.part_o >= items * 8 * 64 * D * 2
-    assert lay.split_chunks == 8
+    assert lay.part_ml - lay.part_o >= items * 16 * 64 * D * 2
+    assert lay.split_chunks == 16
     # the split is an argument: layouts of different splits coexist, and only the
     # partials (placed last) depend on it
     one = tsv.vsa_workspace_layout(pl.info, H, D, 1)
-    sixteen = tsv.vsa_workspace_layout(pl.info, H, D, 16)
-    assert one.split_chunks == 1 and sixteen.split_chunks == 16
-    assert one.total_bytes == one.part_o < lay.total_bytes < sixteen.total_bytes
+    eight = tsv.vsa_workspace_layout(pl.info, H, D, 8)
+    assert one.split_chunks == 1 and eight.split_chunks == 8
+    assert one.total_bytes == one.part_o < eight.total_bytes < lay.total_bytes
     for name in ("k_tiled", "v_tiled", "q_mean", "k_mean", "v_mean", "scores", "k_i8", "k_scale",
                  "part_o"):
-        assert getattr(one, name) == getattr(lay, name) == getattr(sixteen, name)
-    assert sixteen.part_ml - sixteen.part_o == 2 * (lay.part_ml - lay.part_o)
+        assert getattr(one, name) == getattr(lay, name) == getattr(eight, name)
+    assert lay.part_ml - lay.part_o == 2 * (eight.part_ml - eight.part_o)
     assert tsv.vsa_workspace_layout(pl.info, H, D, 0).total_bytes == lay.total_bytes
     for bad in (-1, 65):
         with pytest.raises(tsv.VsaError) as e:
             tsv.vsa_workspace_layout(pl.info, H, D, bad)
         assert e.value.status == tsv.VSA_ERR_ARG
+
+
+def test_automatic_split_rule():
+    """1 chunk up to 16 MiB of K+V per head; 8 beyond; at least 16 (two phases) for 64-row
+    tiles beyond 32 MiB; 8 per started 96 MiB beyond that."""
+    want = {"tiny": 1, "mid": 1, "page5": 8, "h3": 16, "veda": 8, "long": 16}
+    for name, c in want.items():
+        wl = workloads.WORKLOADS[name]
+        pl = tsv.cached_plan(wl.prefix_segments, wl.grid, wl.tile)
+        assert tsv.vsa_workspace_layout(pl.info, wl.heads, wl.head_dim).split_chunks == c, name
 
 
 def test_workspace_layout_unsupported():
