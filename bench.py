@@ -65,10 +65,12 @@ def effective_fine_flops(plan, keep_idx: np.ndarray, heads: int, head_dim: int,
     return 4.0 * head_dim * float(pairs)
 
 
-def hbm_passes(wl, plan, kernels, k, k_ref=None):
-    """Achieved HBM bandwidth of the memory-bound coarse passes from their algorithmic bytes:
+def hbm_passes(wl, plan, kernels, k, k_ref=None, chunks=1):
+    """Achieved HBM bandwidth of the memory-bound passes from their algorithmic bytes:
     gather_pool reads Q, K, V once and writes the tile-ordered K, V and the three tile-mean
-    arrays; top-k reads the coarse score rows and writes the keep lists."""
+    arrays; top-k reads the coarse score rows and writes the keep lists; the merge of a
+    split fine pass reads every chunk's partial of every (padded row, head) (D bf16 values
+    and the fp32 max and sum), the gate and the O_coarse rows once, and writes the output."""
     H, D, S = wl.heads, wl.head_dim, wl.tokens
     S_pad, n_t, n_v, P = plan.S_pad, plan.n_t, plan.n_v, plan.P
     gather = 3 * S * H * D * 2 + 2 * S_pad * H * D * 2 + 3 * H * n_t * D * 4
@@ -76,8 +78,11 @@ def hbm_passes(wl, plan, kernels, k, k_ref=None):
         topk = H * n_v * n_v * 4 + H * n_v * k * 4
     else:
         topk = H * n_t * n_t * 4 + H * n_t * (k + k_ref) * 4
+    merge = chunks * S_pad * H * (D * 2 + 8) + 2 * S * H * D * 2 + n_t * H * D * 4
     out = {}
-    for name, nbytes in (("gather_pool", gather), ("topk", topk)):
+    for name, nbytes in (("gather_pool", gather), ("topk", topk), ("merge", merge if chunks > 1 else 0)):
+        if nbytes == 0:
+            continue
         if name in kernels:
             gbs = nbytes / (kernels[name]["avg_ms"] * 1e-3) / 1e9
             out[name] = {"algorithmic_bytes": int(nbytes), "gb_s": round(gbs, 1),
@@ -574,7 +579,8 @@ def main() -> int:
         "ms_per_layer_attention_only": round(coarse_ms + fine_ms, 4),
         "tile_pair_fraction": round(frac_pairs, 4),
         "effective_fine_tflop": round(fine_flops / 1e12, 3),
-        "hbm_passes": hbm_passes(wl, att.plan, kernels, att.k, att.k_ref if att.ref else None),
+        "hbm_passes": hbm_passes(wl, att.plan, kernels, att.k, att.k_ref if att.ref else None,
+                                 att.split_chunks),
         "compute_passes": compute_passes(wl, att.plan, kernels, att.k_ref if att.ref else None),
         "wall_s": round(wall, 3),
         "selection": selection_report(att),

@@ -1,5 +1,5 @@
-"""GPU parity of the per-row top-k on long score rows (the one-wave sampled path,
-the multi-wave register path up to 16,384 columns, and the radix select beyond), with and without
+"""GPU parity of the per-row top-k on long score rows (the one-wave sampled and
+bracketed paths, the multi-wave register path up to 16,384 columns, and the radix select beyond), with and without
 massive ties. Keep-sets and the scores they come from are compared bit for bit
 with the oracle on sampled rows.
 
@@ -32,6 +32,11 @@ CASES = {
     # (1,024 columns, 16 keys per lane; 1,936 columns, 32 keys per lane).
     "o16": ((4, 128, 128), 60),
     "o32": ((4, 176, 176), 97),
+    # One wave per row, k a quarter of the row: the bracketed path (two
+    # sampled thresholds; 1,024 / 1,408 / 1,936 columns, 16 / 24 / 32 keys per lane).
+    "b16": ((4, 128, 128), 256),
+    "b24": ((4, 128, 176), 352),
+    "b32": ((4, 176, 176), 484),
     "w2": ((4, 160, 208), 520),
     "w3": ((4, 200, 280), 35),
     "w4": ((4, 264, 336), 277),
