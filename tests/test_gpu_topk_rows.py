@@ -37,6 +37,9 @@ CASES = {
     "b16": ((4, 128, 128), 256),
     "b24": ((4, 128, 176), 352),
     "b32": ((4, 176, 176), 484),
+    # ... half of the row, and all but one column
+    "b24h": ((4, 128, 176), 704),
+    "b24n1": ((4, 128, 176), 1407),
     "w2": ((4, 160, 208), 520),
     "w3": ((4, 200, 280), 35),
     "w4": ((4, 264, 336), 277),
@@ -70,20 +73,31 @@ def _tie_keys(inp, pl, classes: int):
 @pytest.mark.parametrize("ties", [False, True])
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_topk_long_rows(name, ties):
+    _check_rows(name, 7 if ties else 0)
+
+
+@pytest.mark.parametrize("name", ["b24", "o16"])
+def test_topk_constant_rows(name):
+    """Every video tile a copy of one tile: each score row is constant (no spread
+    for a histogram), and the first k columns are kept."""
+    _check_rows(name, 1)
+
+
+def _check_rows(name, classes):
     import tile_sparse_video_amd as tsv
     grid, keep_k = CASES[name]
     wl = workloads.custom(f"topk_{name}", seed=31, heads=1, head_dim=64, hidden=64,
                           prefix_segments=(70,), grid=grid, tile=(4, 4, 4), keep_k=keep_k)
-    print(f"[gpu] top-k rows {name} ties={ties}: inputs", flush=True)
+    print(f"[gpu] top-k rows {name} tie classes={classes}: inputs", flush=True)
     inp = parity.make_inputs(wl)
     pl = parity.oracle_plan(wl)
     assert all(g % 4 == 0 for g in grid)  # full video tiles, so tied tiles have identical means
-    if ties:
-        inp.k = _tie_keys(inp, pl, 7)
+    if classes:
+        inp.k = _tie_keys(inp, pl, classes)
     att = tsv.TileSparseAttention(wl.prefix_segments, wl.grid, wl.tile, wl.heads, wl.head_dim,
                                   keep_k=keep_k, device="cuda")
     assert att.k == keep_k
-    print(f"[gpu] top-k rows {name} ties={ties}: n_v={pl.n_v}, k={keep_k}", flush=True)
+    print(f"[gpu] top-k rows {name} tie classes={classes}: n_v={pl.n_v}, k={keep_k}", flush=True)
     att.coarse(inp.q.cuda(), inp.k.cuda(), inp.v.cuda())
     torch.cuda.synchronize()
     rng = np.random.default_rng(5)
@@ -95,7 +109,7 @@ def test_topk_long_rows(name, ties):
     keep_or = oracle.topk_rows(sc, keep_k, pl.P)
     got_sc = att.workspace_view("scores", torch.float32, (1, pl.n_v, pl.n_v))[0].cpu().numpy()[rows]
     assert np.array_equal(_u32(got_sc), _u32(sc))
-    if ties:
-        assert len(np.unique(sc[0])) <= 7 + 1
+    if classes:
+        assert len(np.unique(sc[0])) <= classes + 1
     keep = att.keep_idx[0].cpu().numpy()[rows]
     assert np.array_equal(keep, keep_or)

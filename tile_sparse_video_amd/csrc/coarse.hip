@@ -20,6 +20,8 @@
 // setting to the reference tokens).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -651,6 +653,198 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
     topk_select<PL>(key, 0, n_cols, lane, T, exact, k - n_gt, 0, 0, k, id_first, out);
 }
 
+// The score a key stands for (the inverse of score_key; both zeros map to +0).
+__device__ __forceinline__ float key_value(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// The wave's k-th largest key among its candidates ck (m of them, 0 past m; all
+// inside one histogram bin, so every key of the row outside the bin is either
+// above or below all of them), kk-th largest: T and whether exactly kk
+// candidates are >= T. With an early stop T is raised to the candidates'
+// minimum, so that "every key >= T" cannot reach below the bin.
+template <int CR>
+__device__ __forceinline__ void topk_bin_search(const uint32_t (&ck)[CR], int kk, uint32_t &T, bool &exact)
+{
+    uint32_t cmax = 0u, cmin = 0xffffffffu;
+#pragma unroll
+    for (int i = 0; i < CR; ++i) {
+        cmax = max(cmax, ck[i]);
+        cmin = min(cmin, ck[i] == 0u ? 0xffffffffu : ck[i]);
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        cmax = max(cmax, uint32_t(__shfl_xor(int(cmax), off)));
+        cmin = min(cmin, uint32_t(__shfl_xor(int(cmin), off)));
+    }
+    cmax = uint32_t(__builtin_amdgcn_readfirstlane(int(cmax)));
+    cmin = uint32_t(__builtin_amdgcn_readfirstlane(int(cmin)));
+    int top;
+    topk_start(cmax, cmin, T, top);
+    exact = false;
+    for (int b = top; b >= 0; --b) {
+        const uint32_t c_t = T | (1u << b);
+        const int c = topk_count_ge<CR>(ck, c_t);
+        if (c >= kk) T = c_t;
+        if (c == kk) {
+            exact = true;
+            break;
+        }
+    }
+    if (exact) T = max(T, cmin);
+}
+
+constexpr int kHistBins = 256;
+
+// Rows of up to 64 PL columns, one wavefront per row, when k is a large share of
+// the row (the sampled path would keep too many candidates): a histogram of
+// the row's scores over 256 bins of equal width between its minimum and
+// maximum (LDS atomics) finds the bin that holds the k-th largest score; bin(s)
+// never decreases as s grows, so every key of a higher bin is larger, and of a
+// lower bin smaller, than every key of that bin. The bin's keys are compacted
+// into the wave's LDS slots and the exact bitwise search runs on them alone;
+// the ordered selection over the row is the full search's, so the histogram
+// changes the work, never the result. Rows whose extremes are not finite, and
+// bins with more than 512 keys, take the full search.
+template <int PL>
+__global__ __launch_bounds__(256) void topk_hist_kernel(const float *__restrict__ scores, int n_rows,
+                                                        int row_len, int col_first, int n_cols, int k,
+                                                        int id_first, int32_t *__restrict__ keep,
+                                                        int keep_stride, int keep_first)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t hist_all[4][kHistBins + 4];  // + a bin for padding
+    __shared__ uint2 cand_all[4 * (kTopkCand1 + kWave)];  // per wave: candidates, then discards
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    const int row = blockIdx.x * 4 + wv;
+    if (row >= n_rows) return;  // wave-uniform; the block has no barrier
+    const float *s = scores + size_t(row) * row_len + col_first;
+    int32_t *out = keep + size_t(row) * keep_stride + keep_first;
+    if (k == n_cols) {
+        for (int j = lane; j < n_cols; j += kWave) out[j] = id_first + j;
+        return;
+    }
+    if (k == 0) return;
+    uint32_t key[PL];
+    float sc[PL];  // the scores themselves (clamped column past the row)
+#pragma unroll
+    for (int e = 0; e < PL; ++e) {
+        const int j = kWave * e + lane;
+        sc[e] = s[min(j, n_cols - 1)];
+        key[e] = j < n_cols ? score_key(sc[e]) : 0u;
+    }
+    uint32_t kmax, kmin, T;
+    int top;
+    topk_range<PL>(key, 0, n_cols, lane, kmax, kmin);
+    const float fmin = key_value(kmin), fmax = key_value(kmax);
+    const float span = fmax - fmin;
+    const float inv = float(kHistBins) / span;
+    // Finiteness from the exponent bits (the build does not honour NaNs in
+    // floating-point tests).
+    auto finite = [](float f) { return (__float_as_uint(f) & 0x7f800000u) != 0x7f800000u; };
+    if (kmax != kmin && finite(fmin) && finite(fmax) && finite(span) && finite(inv) && span > 0.f) {  // uniform
+        uint32_t *hist = hist_all[wv];
+        // (s - fmin) >= 0 and <= span, times inv, is finite and at most ~256:
+        // truncation gives a bin that never decreases as s grows.
+        // The bin of a real key's score (a zero of either sign reads as +0, as
+        // its key does: the key order ignores the sign of zero).
+        auto bin_of = [&](float v) -> int {
+            return min(kHistBins - 1, int(((v == 0.f ? 0.f : v) - fmin) * inv));
+        };
+        int bins[PL];
+#pragma unroll
+        for (int e = 0; e < PL; ++e) bins[e] = kWave * e + lane < n_cols ? bin_of(sc[e]) : kHistBins;
+        reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int e = 0; e < PL; ++e) atomicAdd(&hist[bins[e]], 1u);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // Lane l holds bins 4l .. 4l + 3; suf = keys in bins >= 4l (inclusive
+        // suffix over lanes). suf of lane 0 is the row's count, >= k.
+        const uint4 hv = reinterpret_cast<const uint4 *>(hist)[lane];
+        int suf = int(hv.x + hv.y + hv.z + hv.w);
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int v = __shfl_down(suf, off);
+            if (lane + off < kWave) suf += v;
+        }
+        const uint64_t ge = wave_mask(suf >= k);  // lanes 0 .. L, L the last with suf >= k
+        const int L = 63 - __builtin_clzll(ge);
+        const int h0 = __builtin_amdgcn_readlane(int(hv.x), L), h1 = __builtin_amdgcn_readlane(int(hv.y), L);
+        const int h2 = __builtin_amdgcn_readlane(int(hv.z), L), h3 = __builtin_amdgcn_readlane(int(hv.w), L);
+        int above = __builtin_amdgcn_readlane(suf, L) - (h0 + h1 + h2 + h3);  // keys in bins > 4L + 3
+        int bstar, m;
+        if (above + h3 >= k) {
+            bstar = 4 * L + 3;
+            m = h3;
+        } else if (above + h3 + h2 >= k) {
+            above += h3;
+            bstar = 4 * L + 2;
+            m = h2;
+        } else if (above + h3 + h2 + h1 >= k) {
+            above += h3 + h2;
+            bstar = 4 * L + 1;
+            m = h1;
+        } else {
+            above += h3 + h2 + h1;
+            bstar = 4 * L;
+            m = h0;
+        }
+        if (m <= kTopkCand1) {  // uniform
+            uint2 *cand = cand_all + wv * (kTopkCand1 + kWave);
+            int base = 0;
+#pragma unroll
+            for (int e = 0; e < PL; ++e) {
+                const bool sel = bins[e] == bstar;
+                const uint64_t msk = wave_mask(sel);
+                const int pos = below_count(msk, base);
+                cand[sel ? pos : kTopkCand1 + lane] = make_uint2(key[e], uint32_t(kWave * e + lane));
+                base += __popcll(msk);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int kk = k - above;  // 1 <= kk <= m
+            bool exact;
+            int n_gt;
+            auto finish = [&](auto cr_tag) {
+                constexpr int CR = decltype(cr_tag)::value;
+                uint32_t ck[CR];
+#pragma unroll
+                for (int i = 0; i < CR; ++i) {
+                    const int g = kWave * i + lane;
+                    const uint32_t v = cand[min(g, m - 1)].x;
+                    ck[i] = g < m ? v : 0u;
+                }
+                topk_bin_search<CR>(ck, kk, T, exact);
+                n_gt = exact ? k : above + topk_count_ge<CR>(ck, T + 1);
+            };
+            if (m <= kWave) finish(std::integral_constant<int, 1>{});
+            else if (m <= 4 * kWave) finish(std::integral_constant<int, 4>{});
+            else finish(std::integral_constant<int, 8>{});
+            topk_select<PL>(key, 0, n_cols, lane, T, exact, k - n_gt, 0, 0, k, id_first, out);
+            return;
+        }
+    }
+    topk_start(kmax, kmin, T, top);
+    bool exact = false;
+    for (int b = top; b >= 0; --b) {
+        const uint32_t cand = T | (1u << b);
+        const int c = topk_count_ge<PL>(key, cand);
+        if (c >= k) T = cand;
+        if (c == k) {
+            exact = true;
+            break;
+        }
+    }
+    const int n_gt = exact ? k : (T == 0xffffffffu ? 0 : topk_count_ge<PL>(key, T + 1));
+    topk_select<PL>(key, 0, n_cols, lane, T, exact, k - n_gt, 0, 0, k, id_first, out);
+}
+
 constexpr int kTopkMaxWaves = 8;
 constexpr int kTopkCand = 1024;  // candidate slots of the sampled path (16 per lane of one wave)
 
@@ -933,7 +1127,10 @@ void launch_topk(const float *scores, int n_rows, int row_len, int col_first, in
     KernelTimer t(K_TOPK, st);
     // The one-wave sampled path pays when the candidates it expects (the
     // sample rank it thresholds at, scaled to the row) fit its 512 slots with
-    // room to spare; otherwise the plain search runs.
+    // room to spare; otherwise rows of 8 or more keys per lane take the
+    // histogram path (0.155 -> 0.131 ms at the H3-shaped layer; at the
+    // Veda-style layer's k / n = 10 % it was 4 % slower than the sampled path),
+    // and shorter rows the plain search.
     const double mu = 64.0 * k / n_cols;
     const bool sampled = n_cols >= 8 * kWave && k < n_cols &&
                          (std::ceil(mu + 2.5 * std::sqrt(mu)) + 1.0) * n_cols / kWave <= 0.8 * kTopkCand1;
@@ -941,6 +1138,10 @@ void launch_topk(const float *scores, int n_rows, int row_len, int col_first, in
     do {                                                                                               \
         if (sampled && (PLV) % 4 == 0 && (PLV) >= 8)                                                   \
             hipLaunchKernelGGL((topk_kernel<PLV, (PLV) % 4 == 0 && (PLV) >= 8>), dim3((n_rows + 3) / 4), \
+                               dim3(256), 0, st, scores, n_rows, row_len, col_first, n_cols, k,        \
+                               id_first, keep, keep_stride, keep_first);                               \
+        else if ((PLV) % 4 == 0 && (PLV) >= 8)                                                        \
+            hipLaunchKernelGGL((topk_hist_kernel<((PLV) % 4 == 0 ? (PLV) : 8)>), dim3((n_rows + 3) / 4), \
                                dim3(256), 0, st, scores, n_rows, row_len, col_first, n_cols, k,        \
                                id_first, keep, keep_stride, keep_first);                               \
         else                                                                                           \
