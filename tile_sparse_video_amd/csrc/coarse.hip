@@ -5,11 +5,12 @@
 //                   range (video x video, or all x all with reference
 //                   sparsity) as an fp32 fused-multiply-add chain (VALU);
 //   coarse_attn  -- tile-level softmax attention over the pooled Q, K, V (fp32
-//                   matrix cores);
+//                   accumulation; products as split bf16 on the matrix cores);
 //   topk         -- per score row and column group, top-k: a bitwise search for
 //                   the k-th largest key over register-resident keys (a wave
-//                   per row up to 2,048 columns, a workgroup up to 16,384), an
-//                   8-bit radix select beyond; lowest index first on ties,
+//                   per row up to 2,048 columns, narrowed by a sample or a
+//                   score histogram; a workgroup up to 16,384), an 8-bit radix
+//                   select beyond; lowest index first on ties,
 //                   ascending output.
 //
 // Method: SnackOnAI analysis of ComfyUI-Ref2VA-VSA ("The Code, Annotated",
@@ -249,74 +250,127 @@ __global__ __launch_bounds__(256, 2) void tile_scores_kernel(const float *__rest
 // ------------------------------------------------------- coarse attention --
 //
 // O_coarse[h][i] = sum_j softmax_j(scale * qmean_i . kmean_j) vmean_j over all
-// n_t key tiles, for every tile i. fp32 throughout, on the fp32 matrix cores
-// (v_mfma_f32_32x32x2_f32). A workgroup of 4 waves covers 128 query tiles of a
-// head; blocks of 32 key tiles (means of K and V) are staged in LDS once and
-// used by all 4 waves. Each wave: S^T = K.Q^T for its 32 query tiles (lane =
-// one query column), an online softmax per lane, then O^T += V^T.P^T.
-// Reduction slots: in S, product m pairs d = m (lane half 0) with d = D/2 + m
-// (half 1); in P.V, product m pairs keys 8(m/4) + 4*half + m%4, which are
-// exactly the S accumulator elements the lane already holds.
+// n_t key tiles, for every tile i, accumulated in fp32. A workgroup of 4 waves
+// covers 128 query tiles of a head; blocks of 32 key tiles (means of K and V)
+// are staged in LDS once and used by all 4 waves. Each wave: S^T = K.Q^T for
+// its 32 query tiles (lane = one query column), an online softmax per lane in
+// fp32, then O^T += V^T.P^T.
+//
+// The products run on the bf16 matrix cores with split operands: every fp32
+// operand x is carried as hi = bf16(x) and lo = bf16(x - hi) (x - hi is exact
+// in fp32), and a product a.b as ahi.bhi + ahi.blo + alo.bhi, accumulated in
+// fp32 (the dropped alo.blo is below 2^-16 of |a b|). Three bf16 products cost
+// 3/16 of an fp32 product's matrix-core cycles (v_mfma_f32_32x32x2_f32 took
+// twice the time: 0.85 vs 0.43 ms at the H3-shaped layer, 7.98 vs 3.93 ms at
+// the long-video one). The key blocks are staged already split and in the
+// operand layouts:
+//   S^T = K.Q^T (A = K: lane (key, half) holds d = 16c + 8 half + 0..7);
+//   O^T += V^T.P^T (A = V^T: lane (d, half) holds the keys 16 kc + 8 (s / 4)
+//   + 4 half + s % 4 of slot s, which are the S accumulator elements 8 kc + s
+//   the lane holds for its query: P needs no exchange).
 template <int D>
 __global__ __launch_bounds__(256) void coarse_attn_kernel(const float *__restrict__ qmean,
                                                          const float *__restrict__ kmean,
                                                          const float *__restrict__ vmean, int n_t,
                                                          float scale_log2e, float *__restrict__ o_coarse)
 {
-    constexpr int KB = 32, ROW = D + 1, HD = D / 2, DB = D / 32;
-    __shared__ float ks[KB * ROW];
-    __shared__ float vs[KB * ROW];
+    constexpr int KB = 32, NCK = D / 16, DB = D / 32;
+    constexpr int KF = KB * NCK * 2 / 256;   // K fragments staged per thread
+    constexpr int VF = DB * 2 * kWave / 256; // V fragments staged per thread
+    static_assert(KF >= 1 && VF >= 1, "D = 64 or 128");
+    __shared__ bf16x8_t khl[NCK][2][kWave];   // [chunk][hi, lo][lane]
+    __shared__ bf16x8_t vhl[DB][2][2][kWave]; // [d block][key chunk][hi, lo][lane]
     const int h = blockIdx.y, wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int l32 = lane & 31, half = lane >> 5;
     const size_t hb = size_t(h) * n_t * D;
     const int qi = blockIdx.x * 128 + wave * 32 + l32;
     const bool qlive = qi < n_t;
 
-    float qv[HD];
+    auto split8 = [](const float (&x)[8], bf16x8_t &hi, bf16x8_t &lo) {
 #pragma unroll
-    for (int m = 0; m < HD; ++m) qv[m] = qlive ? qmean[hb + size_t(qi) * D + HD * half + m] : 0.f;
+        for (int e = 0; e < 8; ++e) {
+            hi[e] = (__bf16)x[e];
+            lo[e] = (__bf16)(x[e] - float(hi[e]));
+        }
+    };
+    // Q (B operand of S): lane (query, half), chunk c: d = 16c + 8 half + e.
+    bf16x8_t qhi[NCK], qlo[NCK];
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) {
+        float x[8];
+        const float *qrow = qmean + hb + size_t(qlive ? qi : 0) * D + 16 * c + 8 * half;
+        const float4 a0 = *reinterpret_cast<const float4 *>(qrow), a1 = *reinterpret_cast<const float4 *>(qrow + 4);
+        x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w; x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
+        if (!qlive)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        split8(x, qhi[c], qlo[c]);
+    }
 
     f32x16_t O[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) O[db] = f32x16_t{};
     float mrun = -INFINITY, lrun = 0.f;
 
-    // Key blocks are staged through registers: thread t holds float4 number
-    // t + 256 u (u < NT) of the block's K and V means. The next block's loads
-    // are issued right after the current block is in LDS, so they are in
-    // flight under its products; they read a clamped row (rows past the end
-    // are written to LDS as zeros), so no load sits behind a branch.
-    constexpr int C4 = D / 4, NT = KB * C4 / 256;
-    float4 kreg[NT], vreg[NT];
+    // Staging slots. K fragment f (< 2 NCK kWave... one per (chunk, lane)):
+    // key = lane % 32 of the block, d = 16 chunk + 8 (lane / 32) + 0..7.
+    // V fragment f: d = 32 db + f % 32, half = (f / 32) % 2, key chunk kc =
+    // (f / 64) % 2, db = f / 128; keys 16 kc + 8 (s / 4) + 4 half + s % 4.
+    // The next block's values are fetched into registers under the current
+    // block's products (clamped rows; rows past the end are staged as zero).
+    float kx[KF][8], vx[VF][8];
     auto fetch = [&](int j0) {
 #pragma unroll
-        for (int u = 0; u < NT; ++u) {
-            const int idx = threadIdx.x + 256 * u, r = idx / C4, c4 = idx % C4;
-            const size_t off = hb + size_t(min(j0 + r, n_t - 1)) * D + 4 * c4;
-            kreg[u] = *reinterpret_cast<const float4 *>(kmean + off);
-            vreg[u] = *reinterpret_cast<const float4 *>(vmean + off);
+        for (int u = 0; u < KF; ++u) {
+            const int f = threadIdx.x + 256 * u, c = f / kWave, ln = f % kWave;
+            const int key = ln % 32, d0 = 16 * c + 8 * (ln / 32);
+            const float *row = kmean + hb + size_t(min(j0 + key, n_t - 1)) * D + d0;
+            const float4 a0 = *reinterpret_cast<const float4 *>(row), a1 = *reinterpret_cast<const float4 *>(row + 4);
+            kx[u][0] = a0.x; kx[u][1] = a0.y; kx[u][2] = a0.z; kx[u][3] = a0.w;
+            kx[u][4] = a1.x; kx[u][5] = a1.y; kx[u][6] = a1.z; kx[u][7] = a1.w;
+        }
+#pragma unroll
+        for (int u = 0; u < VF; ++u) {
+            const int f = threadIdx.x + 256 * u;
+            const int d = 32 * (f / 128) + f % 32, hf = (f / 32) % 2, kc = (f / 64) % 2;
+#pragma unroll
+            for (int sl = 0; sl < 8; ++sl) {
+                const int key = 16 * kc + 8 * (sl / 4) + 4 * hf + sl % 4;
+                vx[u][sl] = vmean[hb + size_t(min(j0 + key, n_t - 1)) * D + d];
+            }
         }
     };
     fetch(0);
     for (int j0 = 0; j0 < n_t; j0 += KB) {
         __syncthreads();  // every wave is done with the previous block
 #pragma unroll
-        for (int u = 0; u < NT; ++u) {
-            const int idx = threadIdx.x + 256 * u, r = idx / C4, c4 = idx % C4;
-            const bool live = j0 + r < n_t;
-            const float4 k4 = live ? kreg[u] : make_float4(0.f, 0.f, 0.f, 0.f);
-            const float4 v4 = live ? vreg[u] : make_float4(0.f, 0.f, 0.f, 0.f);
-            float *kd = &ks[r * ROW + 4 * c4], *vd = &vs[r * ROW + 4 * c4];
-            kd[0] = k4.x; kd[1] = k4.y; kd[2] = k4.z; kd[3] = k4.w;
-            vd[0] = v4.x; vd[1] = v4.y; vd[2] = v4.z; vd[3] = v4.w;
+        for (int u = 0; u < KF; ++u) {
+            const int f = threadIdx.x + 256 * u, c = f / kWave, ln = f % kWave;
+            if (j0 + ln % 32 >= n_t)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kx[u][e] = 0.f;
+            split8(kx[u], khl[c][0][ln], khl[c][1][ln]);
+        }
+#pragma unroll
+        for (int u = 0; u < VF; ++u) {
+            const int f = threadIdx.x + 256 * u;
+            const int db = f / 128, hf = (f / 32) % 2, kc = (f / 64) % 2, ln = f % 32 + 32 * hf;
+#pragma unroll
+            for (int sl = 0; sl < 8; ++sl)
+                if (j0 + 16 * kc + 8 * (sl / 4) + 4 * hf + sl % 4 >= n_t) vx[u][sl] = 0.f;
+            split8(vx[u], vhl[db][kc][0][ln], vhl[db][kc][1][ln]);
         }
         __syncthreads();
         if (j0 + KB < n_t) fetch(j0 + KB);
 
         f32x16_t S = f32x16_t{};
 #pragma unroll
-        for (int m = 0; m < HD; ++m)
-            S = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[l32 * ROW + HD * half + m], qv[m], S, 0, 0, 0);
+        for (int c = 0; c < NCK; ++c) {
+            const bf16x8_t kh = khl[c][0][lane], kl = khl[c][1][lane];
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qhi[c], S, 0, 0, 0);
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qlo[c], S, 0, 0, 0);
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qhi[c], S, 0, 0, 0);
+        }
         if (j0 + KB > n_t) {  // key tiles past the end never score
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -339,17 +393,31 @@ __global__ __launch_bounds__(256) void coarse_attn_kernel(const float *__restric
         rs += __shfl_xor(rs, 32);
         lrun = lrun * alpha + rs;
         mrun = m_new;
+        bf16x8_t phi[2], plo[2];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            f32x16_t acc = O[db];
+        for (int kc = 0; kc < 2; ++kc) {
+            float x[8];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[e] *= alpha;
+            for (int sl = 0; sl < 8; ++sl) x[sl] = p[8 * kc + sl];
+            split8(x, phi[kc], plo[kc]);
+        }
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                const int key = 8 * (m / 4) + 4 * half + (m % 4);
-                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * ROW + 32 * db + l32], p[m], acc, 0, 0, 0);
-            }
-            O[db] = acc;
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) O[db][e] *= alpha;
+        // The small terms first (vlo.phi, vhi.plo), then vhi.phi; the d blocks
+        // interleaved, so consecutive products are independent.
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vhl[db][kc][1][lane], phi[kc], O[db], 0, 0, 0);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vhl[db][kc][0][lane], plo[kc], O[db], 0, 0, 0);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vhl[db][kc][0][lane], phi[kc], O[db], 0, 0, 0);
         }
     }
     if (!qlive) return;
