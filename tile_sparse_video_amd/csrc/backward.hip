@@ -780,7 +780,8 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
 
     if (SPLIT) {
         // partial dQ^T of this chunk, fp32: [item][8][DB][2][4][64][4], register
-        // group q4 of every lane in one lane-contiguous 1 KB run.
+        // group q4 of every lane in one lane-contiguous 1 KB run. Only the merge
+        // reads it: non-temporal stores keep it from displacing reused K/V in L2.
         float *pd = a.part_dq + (size_t(item) * 8 + chunk) * (DB * 2 * kWave * 16);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -789,8 +790,9 @@ __global__ __launch_bounds__(64, 1) void dq_kernel(BwdArgs a)
                 float4 *dst = reinterpret_cast<float4 *>(pd + (db * 2 + qb) * kWave * 16);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
-                    dst[q4 * kWave + lane] = make_float4(G[db][qb][4 * q4], G[db][qb][4 * q4 + 1], G[db][qb][4 * q4 + 2],
-                                          G[db][qb][4 * q4 + 3]);
+                    __builtin_nontemporal_store(f32x4_t{G[db][qb][4 * q4], G[db][qb][4 * q4 + 1], G[db][qb][4 * q4 + 2],
+                                                        G[db][qb][4 * q4 + 3]},
+                                                reinterpret_cast<f32x4_t *>(dst + q4 * kWave + lane));
             }
         return;
     }
@@ -845,11 +847,11 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdArgs a, int n_items)
             a.part_dq + (size_t(item) * 8 + c) * (DB * 2 * kWave * 16) + (db * 2 + qb) * kWave * 16);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 v = src[q4 * kWave + lane];
-            acc[4 * q4] += v.x;
-            acc[4 * q4 + 1] += v.y;
-            acc[4 * q4 + 2] += v.z;
-            acc[4 * q4 + 3] += v.w;
+            const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(src + q4 * kWave + lane));
+            acc[4 * q4] += v[0];
+            acc[4 * q4 + 1] += v[1];
+            acc[4 * q4 + 2] += v[2];
+            acc[4 * q4 + 3] += v[3];
         }
     }
     float4 mm[4];
@@ -1277,8 +1279,10 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
         float4 *dv4 = reinterpret_cast<float4 *>(pd + (DB + db) * kWave * 16);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            dk4[q4 * kWave + lane] = make_float4(GK[db][4 * q4], GK[db][4 * q4 + 1], GK[db][4 * q4 + 2], GK[db][4 * q4 + 3]);
-            dv4[q4 * kWave + lane] = make_float4(GV[db][4 * q4], GV[db][4 * q4 + 1], GV[db][4 * q4 + 2], GV[db][4 * q4 + 3]);
+            __builtin_nontemporal_store(f32x4_t{GK[db][4 * q4], GK[db][4 * q4 + 1], GK[db][4 * q4 + 2], GK[db][4 * q4 + 3]},
+                                        reinterpret_cast<f32x4_t *>(dk4 + q4 * kWave + lane));
+            __builtin_nontemporal_store(f32x4_t{GV[db][4 * q4], GV[db][4 * q4 + 1], GV[db][4 * q4 + 2], GV[db][4 * q4 + 3]},
+                                        reinterpret_cast<f32x4_t *>(dv4 + q4 * kWave + lane));
         }
     }
 }
@@ -1322,11 +1326,11 @@ __global__ __launch_bounds__(256) void dkdv_merge_kernel(BwdArgs a, int n_units)
             a.part_dkv + ((size_t(ht) * 8 + c) * KB + kb) * (2 * DB * kWave * 16) + (kv * DB + db) * kWave * 16);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 v = src[q4 * kWave + lane];
-            acc[4 * q4] += v.x;
-            acc[4 * q4 + 1] += v.y;
-            acc[4 * q4 + 2] += v.z;
-            acc[4 * q4 + 3] += v.w;
+            const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(src + q4 * kWave + lane));
+            acc[4 * q4] += v[0];
+            acc[4 * q4 + 1] += v[1];
+            acc[4 * q4 + 2] += v[2];
+            acc[4 * q4 + 3] += v[3];
         }
     }
     float4 mm[4];
