@@ -146,30 +146,38 @@ def selection_report(att, max_heads: int = 8) -> dict:
 
 
 def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops, k_ref=None, int8=False):
-    """The oracle, as it stands, on a bounded sample of this layer, scaled to one layer.
-    k_ref is not None in the reference-sparsity mode; int8 times the INT8 fine pass."""
+    """The oracle, as it stands, on a bounded sample of this layer, scaled to one layer;
+    when that estimate is at most FULL_CPU_LAYER_S the whole layer (every head and token)
+    is run and timed instead. k_ref is not None in the reference-sparsity mode; int8
+    times the INT8 fine pass."""
     import oracle
     Qb, Kb, Vb = (workloads.bf16_bits(t) for t in (q, k, v))
     xb, wb = workloads.bf16_bits(x), workloads.bf16_bits(w)
     pl = oracle.plan(wl.prefix_segments, wl.grid, wl.tile)
     scale = wl.head_dim ** -0.5
+
+    def head(h):
+        """Head h's coarse stage (pool, scores, top-k, O_coarse) and its fine pass."""
+        if k_ref is None:
+            hr = oracle.head(Qb, Kb, Vb, h, pl, kk, scale)
+
+            def fine(toks):
+                return oracle.fine_tokens(Qb, Kb, Vb, h, pl, hr.keep, kk, scale, toks)
+        else:
+            hr = oracle.head_ref(Qb, Kb, Vb, h, pl, k_ref, kk, scale)
+
+            def fine(toks):
+                return oracle.fine_tokens_lists(Qb, Kb, Vb, h, pl, hr.keep, scale, toks)
+        if int8:
+            csr = (oracle.key_lists_default(pl, hr.keep) if k_ref is None
+                   else oracle.key_lists_explicit(hr.keep))
+
+            def fine(toks):
+                return oracle.fine_tokens_i8(Qb, Kb, Vb, h, pl, csr, scale, toks)
+        return fine
+
     t0 = time.perf_counter()
-    if k_ref is None:
-        hr = oracle.head(Qb, Kb, Vb, 0, pl, kk, scale)      # pool, scores, top-k, O_coarse
-
-        def fine(toks):
-            return oracle.fine_tokens(Qb, Kb, Vb, 0, pl, hr.keep, kk, scale, toks)
-    else:
-        hr = oracle.head_ref(Qb, Kb, Vb, 0, pl, k_ref, kk, scale)
-
-        def fine(toks):
-            return oracle.fine_tokens_lists(Qb, Kb, Vb, 0, pl, hr.keep, scale, toks)
-    if int8:
-        csr = (oracle.key_lists_default(pl, hr.keep) if k_ref is None
-               else oracle.key_lists_explicit(hr.keep))
-
-        def fine(toks):
-            return oracle.fine_tokens_i8(Qb, Kb, Vb, 0, pl, csr, scale, toks)
+    fine = head(0)
     t_head = time.perf_counter() - t0
     rng = np.random.default_rng(0)
     vid_all = np.arange(pl.S)[pl.untile // pl.B >= pl.P]
@@ -191,6 +199,19 @@ def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops, k_ref=None, int8=False
     n_video_tok = pl.S - wl.prefix_tokens
     layer_s = (wl.heads * (t_head + n_video_tok * t_vid + wl.prefix_tokens * t_pre)
                + pl.S * t_gate)
+    sample = (f"head 0 of {wl.heads}: tile means, all coarse scores, top-k and O_coarse "
+              f"({t_head:.2f} s); fine attention of {len(vid)} video and {len(pre)} prefix "
+              f"query tokens; gate projection of {len(gt)} tokens; scaled to all heads "
+              f"and tokens of one layer")
+    if layer_s <= FULL_CPU_LAYER_S:
+        toks = np.arange(pl.S)
+        t0 = time.perf_counter()
+        for h in range(wl.heads):
+            head(h)(toks)
+        oracle.gate_proj(xb, wb, toks)
+        layer_s = time.perf_counter() - t0
+        sample = (f"the whole layer: all {wl.heads} heads (coarse stage and the fine pass of all "
+                  f"{pl.S} tokens) and the gate projection of every token")
     threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     return {
         "value": fine_flops / layer_s / 1e12,
@@ -198,12 +219,11 @@ def cpu_baseline(wl, q, k, v, x, w, plan, kk, fine_flops, k_ref=None, int8=False
         "ms_per_layer": layer_s * 1e3,
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"head 0 of {wl.heads}: tile means, all coarse scores, top-k and O_coarse "
-                   f"({t_head:.2f} s); fine attention of {len(vid)} video and {len(pre)} prefix "
-                   f"query tokens; gate projection of {len(gt)} tokens; scaled to all heads "
-                   f"and tokens of one layer"),
+        "sample": sample,
     }
 
+
+FULL_CPU_LAYER_S = 20.0  # the oracle runs the whole layer when the sample scales to at most this
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fine_attn_pmc_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "tile_sparse_video_amd", "csrc", f)
@@ -429,7 +449,7 @@ def cpu_baseline_backward(wl, host_inputs, att, dout, g, flops):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="h3", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -45,13 +45,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource word 3, 32-bit data (gfx9 family)
 
-__device__ __forceinline__ float wave_sum(float x)
-{
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
-}
-
 // Packs fp32 values a[8 cc .. 8 cc + 7] into the bf16 B operand of one 16-row
 // chunk (the accumulator-to-operand order the forward uses for P).
 __device__ __forceinline__ bf16x8_t pack8(const f32x16_t &a, int cc)
@@ -344,7 +337,7 @@ __global__ __launch_bounds__(256) void coarse_bwd_cols_kernel(const float *__res
             gs[r * ROW + c] = live ? doc[hb + size_t(i0 + r) * D + c] : 0.f;
         }
         if (threadIdx.x < QB) {
-            const bool live = i0 + threadIdx.x < n_t;
+            const bool live = i0 + int(threadIdx.x) < n_t;
             ls[threadIdx.x] = live ? lsec[size_t(h) * n_t + i0 + threadIdx.x] : INFINITY;  // P = 0
             cs[threadIdx.x] = live ? dcc[size_t(h) * n_t + i0 + threadIdx.x] : 0.f;
         }
@@ -1434,7 +1427,7 @@ __global__ __launch_bounds__(256) void dt_kernel(const uint16_t *__restrict__ do
 }
 
 template <int D, int B>
-void launch_bwd(const vsa_plan_info &info, const BwdArgs &a, const uint16_t *k, const uint16_t *v,
+void launch_bwd(const BwdArgs &a, const uint16_t *k, const uint16_t *v,
                 const uint16_t *q, const uint16_t *dout, const uint16_t *gate,
                 const float *o_coarse, const float *qm, const float *km, const float *vm,
                 const vsa_bwd_layout &L, char *bw, float *dgate, bool split, bool ring, hipStream_t st)
@@ -1655,11 +1648,11 @@ extern "C" int vsa_sparse_attn_bwd(const vsa_plan_info *info, const int32_t *row
     const int B = info->tile_rows;
     const bool ring = dkdv_split(*info, heads, head_dim, chunks);
     if (head_dim == 128) {
-        if (B == 64) launch_bwd<128, 64>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, ring, st);
-        else launch_bwd<128, 128>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, ring, st);
+        if (B == 64) launch_bwd<128, 64>(a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, ring, st);
+        else launch_bwd<128, 128>(a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, ring, st);
     } else {
-        if (B == 64) launch_bwd<64, 64>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, ring, st);
-        else launch_bwd<64, 128>(*info, a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, ring, st);
+        if (B == 64) launch_bwd<64, 64>(a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, ring, st);
+        else launch_bwd<64, 128>(a, kk, vv, qq, dd, gg, o_coarse_dev, qm, km, vm, BL, bw, dgate, split, ring, st);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(VSA_ERR_DEVICE, "%s: kernel launch failed: %s", name, hipGetErrorString(e));

@@ -941,6 +941,7 @@ __global__ __launch_bounds__(kWave * kTopkMaxWaves) void topk_wide_kernel(
     int id_first, int32_t *__restrict__ keep, int keep_stride, int keep_first)
 {
     static_assert(PL % 4 == 0, "the sample takes four registers per wave");
+    if (int(blockIdx.x) >= n_rows) return;  // one workgroup per row (the grid has n_rows)
     __shared__ int xs[2][kTopkMaxWaves];
     __shared__ uint32_t xmax[kTopkMaxWaves], xmin[kTopkMaxWaves];
     __shared__ uint32_t samp[kTopkMaxWaves * kWave];
