@@ -40,6 +40,9 @@ CASES = {
     # ... half of the row, and all but one column
     "b24h": ((4, 128, 176), 704),
     "b24n1": ((4, 128, 176), 1407),
+    # 512 / 768 columns (8 / 12 keys per lane) with k past the sampled path's reach
+    "b8": ((4, 64, 128), 300),
+    "b12": ((4, 96, 128), 400),
     "w2": ((4, 160, 208), 520),
     "w3": ((4, 200, 280), 35),
     "w4": ((4, 264, 336), 277),
