@@ -1168,16 +1168,26 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
             dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(NC + c), Vt[c], dP, 0, 0, 0);
         }
     };
-    // Phase 2 of block b: P, dS and the dV, dK products.
-    auto phase2 = [&](int b, const f32x16_t &S, const f32x16_t &dP) {
+    // One step of the loop: block b's softmax terms, each pair of elements
+    // placed between two of block b + 1's S and dP products (those only read
+    // the next stage, so the matrix core and the vector unit work side by
+    // side), then block b's dV and dK products. Past the list's end the S and dP
+    // products of the reloaded last block run and are never used.
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    auto step = [&](int b, const f32x16_t &S, const f32x16_t &dP, f32x16_t &Sn, f32x16_t &dPn) {
+        const int nb = b + NBUF - 1;
+        issue(nb < n_blocks ? nb : n_blocks - 1, nb % NBUF);  // into the stage freed by block b - 1
+        __builtin_amdgcn_s_waitcnt(VSA_VMCNT((NBUF - 2) * (LPW + 1)));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();     // every wave's part of stage (b + 1) % NBUF has landed
+        asm volatile("" ::: "memory");
         const char *stage = ring_lds + (b % NBUF) * STAGE;
-        // Row statistics of the block: lse at rows 8i + 4 half + j (i, j < 4) and
-        // D_t 256 bytes further. Read in one asm block that also waits for the
-        // reads, so the compiler sees no LDS load it would order after a wait
-        // for every buffer-to-LDS load in flight (the next stage's included).
-        // The outputs are early-clobber: the address must not share a register
-        // with a result, since the later reads still use it.
-        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        const char *nstage = ring_lds + ((b + 1) % NBUF) * STAGE;
+        // Row statistics of block b: lse at rows 8i + 4 half + j (i, j < 4) and
+        // D_t 256 bytes further, read in one asm block that also waits for them
+        // (the compiler sees no LDS load it would order after a wait for every
+        // buffer-to-LDS load in flight). Early-clobber outputs: the address is
+        // still read after the first result is written.
         f32x4_t L[4], Dv[4];
         const uint32_t st_addr = uint32_t(reinterpret_cast<uintptr_t>(stage)) + C::FRAGS * 1024 + 16 * half;
         asm volatile(
@@ -1194,19 +1204,13 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
               "=&v"(Dv[3])
             : "v"(st_addr)
             : "memory");
-        f32x16_t Pm, dS;
+        auto nfrag = [&](int j) { return *reinterpret_cast<const bf16x8_t *>(nstage + j * 1024 + lane * 16); };
+        bf16x8_t FQ[NC], FO[NC];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float l4[4] = {L[i].x, L[i].y, L[i].z, L[i].w}, d4[4] = {Dv[i].x, Dv[i].y, Dv[i].z, Dv[i].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[4 * i + j], c2, -l4[j]));
-                Pm[4 * i + j] = p;
-                dS[4 * i + j] = p * (dP[4 * i + j] - d4[j]);
-            }
+        for (int c = 0; c < NC; ++c) {
+            FQ[c] = nfrag(c);
+            FO[c] = nfrag(NC + c);
         }
-        const bf16x8_t p0 = pack8(Pm, 0), p1 = pack8(Pm, 1);
-        const bf16x8_t s0 = pack8(dS, 0), s1 = pack8(dS, 1);
         // Column fragment (db, cc) of the Q (first = 0) or dO (first = NC) chunks.
         auto col = [&](int first, int db, int cc) -> bf16x8_t {
             typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -1221,29 +1225,38 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
                                __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
             return as_bf16x8(w);
         };
+        Sn = f32x16_t{};
+        dPn = f32x16_t{};
+        f32x16_t Pm, dS;
+        bf16x8_t CO[DB][2], CQ[DB][2];  // block b's column fragments of dO and Q
+        constexpr int EPG = 16 / NC;  // softmax elements per pair of products
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int u = 0; u < EPG; ++u) {
+                const int e = EPG * c + u, i = e / 4, j = e % 4;
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], c2, -L[i][j]));
+                Pm[e] = p;
+                dS[e] = p * (dP[e] - Dv[i][j]);
+            }
+            Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FQ[c], Kt[c], Sn, 0, 0, 0);
+            dPn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FO[c], Vt[c], dPn, 0, 0, 0);
+#pragma unroll
+            for (int q = c * 2 * DB / NC; q < (c + 1) * 2 * DB / NC; ++q) {
+                CO[q / 2][q % 2] = col(NC, q / 2, q % 2);
+                CQ[q / 2][q % 2] = col(0, q / 2, q % 2);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const bf16x8_t p0 = pack8(Pm, 0), p1 = pack8(Pm, 1);
+        const bf16x8_t s0 = pack8(dS, 0), s1 = pack8(dS, 1);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col(NC, db, 0), p0, GV[db], 0, 0, 0);
-            GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col(NC, db, 1), p1, GV[db], 0, 0, 0);
-            GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col(0, db, 0), s0, GK[db], 0, 0, 0);
-            GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(col(0, db, 1), s1, GK[db], 0, 0, 0);
+            GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(CO[db][0], p0, GV[db], 0, 0, 0);
+            GV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(CO[db][1], p1, GV[db], 0, 0, 0);
+            GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(CQ[db][0], s0, GK[db], 0, 0, 0);
+            GK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(CQ[db][1], s1, GK[db], 0, 0, 0);
         }
-    };
-    // Software pipeline: block b + 1's S and dP products are issued before
-    // block b's softmax, so the matrix cores work while the VALU does. The
-    // empty asm statements keep the compiler from moving LDS accesses across
-    // the hand-placed waits and barriers (which carry no fence). Past the
-    // list's end the last block is reloaded into the free stage (never read),
-    // so every wait below is the same on every iteration.
-    auto step = [&](int b, const f32x16_t &S, const f32x16_t &dP, f32x16_t &Sn, f32x16_t &dPn) {
-        const int nb = b + NBUF - 1;
-        issue(nb < n_blocks ? nb : n_blocks - 1, nb % NBUF);  // into the stage freed by block b - 1
-        __builtin_amdgcn_s_waitcnt(VSA_VMCNT((NBUF - 2) * (LPW + 1)));
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();     // every wave's part of stage (b + 1) % NBUF has landed
-        asm volatile("" ::: "memory");
-        if (b + 1 < n_blocks) phase1(b + 1, Sn, dPn);
-        phase2(b, S, dP);
         __builtin_amdgcn_s_waitcnt(0xc07f);  // LDS reads of stage b % NBUF done (lgkmcnt 0)
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();     // stage b % NBUF may be refilled
