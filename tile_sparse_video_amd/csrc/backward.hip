@@ -1051,7 +1051,11 @@ struct RingCfg {
     static constexpr int FRAGS = 2 * NC;                // Qr, Or fragments per block
     static constexpr int LPW = FRAGS / KB;              // fragment loads per wave per block
     static constexpr int NBUF = 4;                      // stages (B = 64: two workgroups per CU)
-    static constexpr int STAGE = FRAGS * 1024 + KB * 256;  // + 64 lse, 64 D_t (+ spare areas)
+    // Fragments are staged 1024 + 64 bytes apart: the column reads of the dV and dK
+    // products take two neighbouring fragments at once, and the padding puts them
+    // on different LDS banks.
+    static constexpr int FST = 1024 + 64;
+    static constexpr int STAGE = FRAGS * FST + KB * 256;  // + 64 lse, 64 D_t (+ spare areas)
     static constexpr int LIST = 4096;                   // uint16 query-tile ids of the chunk
     static constexpr size_t LDS = size_t(NBUF) * STAGE + LIST * 2;
 };
@@ -1125,7 +1129,7 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
     // read adds 8 rows. The per-lane part of that address is fixed.
     const int tg = lane >> 4, ti = lane & 15;
     const int t_d0 = 16 * (tg & 1) + 4 * (ti & 3);                    // d - 32 db
-    const uint32_t t_base = uint32_t(((t_d0 >> 4) * 1024) +                   // chunk 2 db + g % 2
+    const uint32_t t_base = uint32_t(((t_d0 >> 4) * C::FST) +                 // chunk 2 db + g % 2
                                      ((4 * (tg >> 1) + (ti >> 2)) + 32 * ((t_d0 >> 3) & 1)) * 16 +
                                      2 * (t_d0 & 7));
     // Row statistics: wave 0 reads lse, the others D_t (only wave 1's copy is used).
@@ -1150,16 +1154,16 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
             const __amdgpu_buffer_rsrc_t r = j < NC ? rqr : ror;
             const uint32_t f = qb * NC + (j < NC ? j : j - NC);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (__attribute__((address_space(3))) void *)(stage + j * 1024), 16, lane * 16, fb + f * 1024u, 0, 0);
+                r, (__attribute__((address_space(3))) void *)(stage + j * C::FST), 16, lane * 16, fb + f * 1024u, 0, 0);
         }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rstat, (__attribute__((address_space(3))) void *)(stage + C::FRAGS * 1024 + kb * 256), 4, lane * 4,
+            rstat, (__attribute__((address_space(3))) void *)(stage + C::FRAGS * C::FST + kb * 256), 4, lane * 4,
             uint32_t(qt * B + 64 * sub + 32 * qb) * 4u, 0, 0);
     };
     // Phase 1 of block b: S = Q K^T and dP = dO V^T from the row fragments.
     auto phase1 = [&](int b, f32x16_t &S, f32x16_t &dP) {
         const char *stage = ring_lds + (b % NBUF) * STAGE;
-        auto frag = [&](int j) { return *reinterpret_cast<const bf16x8_t *>(stage + j * 1024 + lane * 16); };
+        auto frag = [&](int j) { return *reinterpret_cast<const bf16x8_t *>(stage + j * C::FST + lane * 16); };
         S = f32x16_t{};
         dP = f32x16_t{};
 #pragma unroll
@@ -1189,7 +1193,7 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
         // buffer-to-LDS load in flight). Early-clobber outputs: the address is
         // still read after the first result is written.
         f32x4_t L[4], Dv[4];
-        const uint32_t st_addr = uint32_t(reinterpret_cast<uintptr_t>(stage)) + C::FRAGS * 1024 + 16 * half;
+        const uint32_t st_addr = uint32_t(reinterpret_cast<uintptr_t>(stage)) + C::FRAGS * C::FST + 16 * half;
         asm volatile(
             "ds_read_b128 %0, %8\n\t"
             "ds_read_b128 %1, %8 offset:32\n\t"
@@ -1204,7 +1208,7 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
               "=&v"(Dv[3])
             : "v"(st_addr)
             : "memory");
-        auto nfrag = [&](int j) { return *reinterpret_cast<const bf16x8_t *>(nstage + j * 1024 + lane * 16); };
+        auto nfrag = [&](int j) { return *reinterpret_cast<const bf16x8_t *>(nstage + j * C::FST + lane * 16); };
         bf16x8_t FQ[NC], FO[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
@@ -1214,7 +1218,7 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_ring_kernel(BwdArgs a)
         // Column fragment (db, cc) of the Q (first = 0) or dO (first = NC) chunks.
         auto col = [&](int first, int db, int cc) -> bf16x8_t {
             typedef short s16x4_t __attribute__((ext_vector_type(4)));
-            const char *p = stage + first * 1024 + t_base + 2048 * db + 256 * cc;
+            const char *p = stage + first * C::FST + t_base + 2 * C::FST * db + 256 * cc;
             const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4_t *)(p));
             const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
