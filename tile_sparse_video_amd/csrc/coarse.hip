@@ -783,7 +783,9 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(const float *__restrict_
 {
     __shared__ __attribute__((aligned(16))) uint32_t hist_all[4][kHistBins + 4];  // + a bin for padding
     __shared__ uint2 cand_all[4 * (kTopkCand1 + kWave)];  // per wave: candidates, then discards
-    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    // The wave index through readfirstlane: the row, its base and its output
+    // are then scalar, and the loads take a 32-bit offset from a scalar base.
+    const int lane = threadIdx.x % kWave, wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int row = blockIdx.x * 4 + wv;
     if (row >= n_rows) return;  // wave-uniform; the block has no barrier
     const float *s = scores + size_t(row) * row_len + col_first;
@@ -797,9 +799,9 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(const float *__restrict_
     float sc[PL];  // the scores themselves (clamped column past the row)
 #pragma unroll
     for (int e = 0; e < PL; ++e) {
-        const int j = kWave * e + lane;
-        sc[e] = s[min(j, n_cols - 1)];
-        key[e] = j < n_cols ? score_key(sc[e]) : 0u;
+        const unsigned j = min(unsigned(kWave * e + lane), unsigned(n_cols - 1));
+        sc[e] = s[j];
+        key[e] = kWave * e + lane < n_cols ? score_key(sc[e]) : 0u;
     }
     uint32_t kmax, kmin, T;
     int top;
@@ -816,12 +818,13 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(const float *__restrict_
         // truncation gives a bin that never decreases as s grows.
         // The bin of a real key's score (a zero of either sign reads as +0, as
         // its key does: the key order ignores the sign of zero).
-        auto bin_of = [&](float v) -> int {
-            return min(kHistBins - 1, int(((v == 0.f ? 0.f : v) - fmin) * inv));
-        };
+        auto bin_of = [&](float v) -> int { return min(kHistBins - 1, int((v - fmin) * inv)); };
         int bins[PL];
 #pragma unroll
-        for (int e = 0; e < PL; ++e) bins[e] = kWave * e + lane < n_cols ? bin_of(sc[e]) : kHistBins;
+        for (int e = 0; e < PL; ++e) {
+            const int bn = bin_of(sc[e]);
+            bins[e] = kWave * e + lane < n_cols ? bn : kHistBins;
+        }
         reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
