@@ -1035,8 +1035,9 @@ __global__ __launch_bounds__(B * 2, 1) void dkdv_kernel(BwdArgs a)
 // stage holds the block's Q and dO row fragments (1 KB each, the tile-ordered
 // copies) and the lse and D_t of its rows; the column-layout operands of the
 // dV and dK products are read from the same row fragments with the LDS
-// transpose read (ds_read_b64_tr_b16), so Q and dO cross from L2 once. The waves fill a stage together with buffer-to-LDS loads (each wave a
-// fixed share of the fragments plus one row-statistics load: wave 0 the lse,
+// transpose read (ds_read_b64_tr_b16), so Q and dO cross from L2 once. The
+// waves fill a stage together with buffer-to-LDS loads (each wave a fixed
+// share of the fragments plus one row-statistics load: wave 0 the lse,
 // wave 1 the D_t, further waves a spare copy), so a fragment crosses from L2
 // once per workgroup and never occupies VGPRs in flight; a stage is refilled
 // NBUF - 1 blocks ahead of its use. Every wave issues the same number of
