@@ -238,6 +238,58 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def ceilings() -> int:
+    """What the box reaches with plain library operations, beside the vendor peaks used for
+    the roofline fractions: a 2 GiB device copy (read + write bytes), a read-only sum over 2 GiB,
+    and bf16 GEMMs through torch.matmul (hipBLASLt) on 8192^3 and on the H3-shaped gate
+    projection (98,432 x 5,376 by 5,376 x 5,376, the weight transposed once beforehand).
+    Each figure is the median of 5 timed repetitions after 3 warm-up ones."""
+    if not torch.cuda.is_available():
+        print("bench.py --ceilings needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def med_ms(fn, reps=5, warm=3):
+        for _ in range(warm):
+            fn()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return sorted(times)[len(times) // 2]
+
+    res = {"vendor_peaks": {"hbm_gb_s": HBM_PEAK_GBS, "bf16_mfma_tflop_s": BF16_PEAK_TFLOPS}}
+    n = 2 << 30
+    a = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    ms = med_ms(lambda: b.copy_(a))
+    res["copy"] = {"bytes": 2 * n, "ms": round(ms, 4), "gb_s": round(2 * n / ms / 1e6, 1)}
+    ms = med_ms(lambda: a.sum())
+    res["read_sum"] = {"bytes": n, "ms": round(ms, 4), "gb_s": round(n / ms / 1e6, 1)}
+    del a, b
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    m = 8192
+    A = torch.randn(m, m, generator=gen).to(torch.bfloat16).to(dev)
+    B = torch.randn(m, m, generator=gen).to(torch.bfloat16).to(dev)
+    ms = med_ms(lambda: torch.matmul(A, B))
+    res["gemm_8192"] = {"tflop": round(2 * m ** 3 / 1e12, 3), "ms": round(ms, 4),
+                        "tflop_s": round(2 * m ** 3 / ms / 1e9, 1)}
+    del A, B
+    S, hid, N = 98432, 5376, 5376
+    x = torch.randn(S, hid, generator=gen).to(torch.bfloat16).to(dev)
+    wt = torch.randn(N, hid, generator=gen).to(torch.bfloat16).to(dev).t().contiguous()
+    ms = med_ms(lambda: torch.matmul(x, wt))
+    res["gemm_gate_h3"] = {"tflop": round(2 * S * hid * N / 1e12, 3), "ms": round(ms, 4),
+                           "tflop_s": round(2 * S * hid * N / ms / 1e9, 1)}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def recorded_traffic(workload: str):
     """HBM-side bytes per fine pass (fine kernel + merge) and the fine kernel's clock and
     MFMA-busy share, from the committed PMC summary; None when it was taken on another
@@ -472,7 +524,13 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes (3 times), to scale "
                          "the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure what the box reaches with plain library operations (a "
+                         "device copy, a read-only reduction, bf16 GEMMs through torch.matmul) "
+                         "and print it as one JSON line, beside the vendor peaks the roofline uses")
     args = ap.parse_args()
+    if args.ceilings:
+        return ceilings()
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
