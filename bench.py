@@ -238,6 +238,31 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def _median_ms(fn, reps=5, warm=3):
+    for _ in range(warm):
+        fn()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return sorted(times)[len(times) // 2]
+
+
+def library_gemm_8192(dev) -> dict:
+    """hipBLASLt's rate (through torch.matmul) on a bf16 8192^3 GEMM on this machine: median of 5."""
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    m = 8192
+    A = torch.randn(m, m, generator=gen).to(torch.bfloat16).to(dev)
+    B = torch.randn(m, m, generator=gen).to(torch.bfloat16).to(dev)
+    ms = _median_ms(lambda: torch.matmul(A, B))
+    del A, B
+    return {"tflop": round(2 * m ** 3 / 1e12, 3), "ms": round(ms, 4), "tflop_s": round(2 * m ** 3 / ms / 1e9, 1)}
+
+
 def ceilings() -> int:
     """What the box reaches with plain library operations, beside the vendor peaks used for
     the roofline fractions: a 2 GiB device copy (read + write bytes), a read-only sum over 2 GiB,
@@ -249,19 +274,7 @@ def ceilings() -> int:
         return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    def med_ms(fn, reps=5, warm=3):
-        for _ in range(warm):
-            fn()
-        times = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        return sorted(times)[len(times) // 2]
+    med_ms = _median_ms
 
     res = {"vendor_peaks": {"hbm_gb_s": HBM_PEAK_GBS, "bf16_mfma_tflop_s": BF16_PEAK_TFLOPS}}
     n = 2 << 30
@@ -272,14 +285,8 @@ def ceilings() -> int:
     ms = med_ms(lambda: a.sum())
     res["read_sum"] = {"bytes": n, "ms": round(ms, 4), "gb_s": round(n / ms / 1e6, 1)}
     del a, b
+    res["gemm_8192"] = library_gemm_8192(dev)
     gen = torch.Generator(device="cpu").manual_seed(7)
-    m = 8192
-    A = torch.randn(m, m, generator=gen).to(torch.bfloat16).to(dev)
-    B = torch.randn(m, m, generator=gen).to(torch.bfloat16).to(dev)
-    ms = med_ms(lambda: torch.matmul(A, B))
-    res["gemm_8192"] = {"tflop": round(2 * m ** 3 / 1e12, 3), "ms": round(ms, 4),
-                        "tflop_s": round(2 * m ** 3 / ms / 1e9, 1)}
-    del A, B
     S, hid, N = 98432, 5376, 5376
     x = torch.randn(S, hid, generator=gen).to(torch.bfloat16).to(dev)
     wt = torch.randn(N, hid, generator=gen).to(torch.bfloat16).to(dev).t().contiguous()
@@ -682,6 +689,13 @@ def main() -> int:
             "traffic_detail": traffic,
         },
     }
+    if not args.int8:
+        # Context beside the vendor peak, measured after the timed region: what the vendor
+        # library reaches on a plain bf16 GEMM on this machine, and the fine kernel against it.
+        lib = library_gemm_8192(dev)
+        lib["what"] = "hipBLASLt bf16 GEMM 8192^3 through torch.matmul, median of 5, after the timed layers"
+        lib["fine_kernel_over_it"] = round(fine_tflops / lib["tflop_s"], 4)
+        result["roofline"]["library_gemm"] = lib
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, q, k, v, x, w, att.plan, att.k, fine_flops,
